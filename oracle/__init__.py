@@ -1,0 +1,206 @@
+"""CPU fp64 oracle for paged GQA attention -- TEST INFRASTRUCTURE.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package. The GPU library
+(``paged_gqa_attention_attn_amd``) never imports it, and it imports nothing
+from there: the two share no code.
+
+The arithmetic lives in ``oracle.c`` (plain C, fp64, OpenMP over output rows);
+this module only compiles it with gcc, loads it with ctypes and converts numpy
+arrays of stored bit patterns to pointers. Every function cites, in
+``oracle.c``, the page passage it follows.
+
+Arrays are passed as numpy arrays holding the exact stored values:
+``float32`` for fp32, and ``uint16`` bit patterns for bf16 and fp16.
+"""
+from __future__ import annotations
+
+import ctypes
+import subprocess
+from pathlib import Path
+
+import numpy as np
+
+_HERE = Path(__file__).resolve().parent
+SOURCE = _HERE / "oracle.c"
+LIB_PATH = _HERE / "liboracle.so"
+
+DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+
+
+def compile_library(source: Path = SOURCE, out: Path = LIB_PATH, extra_flags=()) -> Path:
+    """Compile ``source`` into a shared library with gcc (OpenMP on)."""
+    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+           *extra_flags, str(source), "-o", str(out), "-lm"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return out
+
+
+def build() -> Path:
+    """Always recompile the oracle library in-tree."""
+    return compile_library()
+
+
+def _ptr(a: np.ndarray | None):
+    if a is None:
+        return None
+    if not a.flags["C_CONTIGUOUS"]:
+        raise ValueError("oracle arrays must be C-contiguous")
+    return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _check_stored(a: np.ndarray, dtype: str, name: str) -> None:
+    want = np.float32 if dtype == "f32" else np.uint16
+    if a.dtype != want:
+        raise TypeError(f"{name}: dtype {dtype} is passed as {np.dtype(want).name}, got {a.dtype}")
+
+
+class Oracle:
+    """ctypes view of one compiled oracle library (the default one, or a test variant)."""
+
+    def __init__(self, lib_path: Path | str = LIB_PATH):
+        lib_path = Path(lib_path)
+        if not lib_path.exists():
+            raise FileNotFoundError(f"{lib_path} is not built; call oracle.build()")
+        self.lib = ctypes.CDLL(str(lib_path))
+        L = self.lib
+        vp, i32, i64, f64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_double
+        L.oracle_upcast.argtypes = [vp, ctypes.c_int, i64, vp]
+        L.oracle_upcast.restype = ctypes.c_int
+        L.oracle_kv_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp, vp]
+        L.oracle_kv_append.restype = i64
+        L.oracle_decode.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i64, i32,
+                                    vp, i32, vp, f64, vp, i64, vp, i32]
+        L.oracle_decode.restype = ctypes.c_int
+        L.oracle_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, f64,
+                                     vp, i64, vp, i32]
+        L.oracle_prefill.restype = ctypes.c_int
+        L.oracle_max_threads.argtypes = []
+        L.oracle_max_threads.restype = ctypes.c_int
+
+    def max_threads(self) -> int:
+        return int(self.lib.oracle_max_threads())
+
+    # -- exact widening ------------------------------------------------------
+    def upcast(self, a: np.ndarray, dtype: str) -> np.ndarray:
+        _check_stored(a, dtype, "a")
+        a = np.ascontiguousarray(a)
+        out = np.empty(a.shape, dtype=np.float64)
+        rc = self.lib.oracle_upcast(_ptr(a), DTYPE_CODES[dtype], a.size, _ptr(out))
+        if rc != 0:
+            raise ValueError("oracle_upcast rejected its arguments")
+        return out
+
+    # -- slot-mapped cache write (in place on the pools) ---------------------
+    def kv_append(self, k: np.ndarray, v: np.ndarray, slot_mapping: np.ndarray,
+                  k_pool: np.ndarray, v_pool: np.ndarray) -> int:
+        """k, v: [T][n_kv][d]; pools: [num_blocks][n_kv][bs][d]; slots int64 [T]."""
+        T, n_kv, d = k.shape
+        nb, n_kv2, bs, d2 = k_pool.shape
+        if v.shape != k.shape or v_pool.shape != k_pool.shape or n_kv2 != n_kv or d2 != d:
+            raise ValueError("shape mismatch")
+        if not (k.dtype == v.dtype == k_pool.dtype == v_pool.dtype):
+            raise TypeError("k, v and pools must share one dtype")
+        slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        if slots.shape != (T,):
+            raise ValueError("slot_mapping must have one entry per token")
+        n = self.lib.oracle_kv_append(_ptr(np.ascontiguousarray(k)), _ptr(np.ascontiguousarray(v)),
+                                      _ptr(slots), T, n_kv, d, k.dtype.itemsize, nb, bs,
+                                      _ptr(k_pool), _ptr(v_pool))
+        if n < 0:
+            raise ValueError("oracle_kv_append rejected its arguments (slot out of range?)")
+        return int(n)
+
+    # -- decode over the paged cache -------------------------------------------
+    def decode(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
+               block_table: np.ndarray, context_lens: np.ndarray, scale: float,
+               sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
+        """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d]."""
+        for name, a in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+            _check_stored(a, dtype, name)
+        B, n_q, d = q.shape
+        nb, n_kv, bs, d2 = k_pool.shape
+        if d2 != d or v_pool.shape != k_pool.shape:
+            raise ValueError("shape mismatch")
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        if bt.ndim != 2 or bt.shape[0] != B:
+            raise ValueError("block_table must be [B][max_blocks_per_seq]")
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
+        if ctx.shape != (B,):
+            raise ValueError("context_lens must be [B]")
+        if sel is not None:
+            sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
+            out = np.empty((sel.shape[0], d), dtype=np.float64)
+        else:
+            out = np.empty((B, n_q, d), dtype=np.float64)
+        rc = self.lib.oracle_decode(_ptr(np.ascontiguousarray(q)), _ptr(k_pool), _ptr(v_pool),
+                                    DTYPE_CODES[dtype], B, n_q, n_kv, d, nb, bs, _ptr(bt),
+                                    bt.shape[1], _ptr(ctx), float(scale), _ptr(sel),
+                                    0 if sel is None else sel.shape[0], _ptr(out), n_threads)
+        if rc != 0:
+            raise ValueError("oracle_decode rejected its arguments")
+        return out
+
+    # -- prefill over contiguous Q/K/V ---------------------------------------
+    def prefill(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, causal: bool,
+                scale: float, sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
+        """q [B][S][n_q][d], k/v [B][S][n_kv][d]; returns fp64 [B][S][n_q][d] or [len(sel)][d].
+
+        ``sel`` rows are (b, h, i) triples.
+        """
+        for name, a in (("q", q), ("k", k), ("v", v)):
+            _check_stored(a, dtype, name)
+        B, S, n_q, d = q.shape
+        n_kv = k.shape[2]
+        if k.shape != (B, S, n_kv, d) or v.shape != k.shape:
+            raise ValueError("shape mismatch")
+        if sel is not None:
+            sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+            out = np.empty((sel.shape[0], d), dtype=np.float64)
+        else:
+            out = np.empty((B, S, n_q, d), dtype=np.float64)
+        rc = self.lib.oracle_prefill(_ptr(np.ascontiguousarray(q)), _ptr(np.ascontiguousarray(k)),
+                                     _ptr(np.ascontiguousarray(v)), DTYPE_CODES[dtype], B, S, n_q,
+                                     n_kv, d, int(bool(causal)), float(scale), _ptr(sel),
+                                     0 if sel is None else sel.shape[0], _ptr(out), n_threads)
+        if rc != 0:
+            raise ValueError("oracle_prefill rejected its arguments")
+        return out
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The in-tree oracle library, compiled on first use if it is missing."""
+    global _default
+    if _default is None:
+        if not LIB_PATH.exists():
+            build()
+        _default = Oracle(LIB_PATH)
+    return _default
+
+
+def decode(*args, **kwargs):
+    return get().decode(*args, **kwargs)
+
+
+def prefill(*args, **kwargs):
+    return get().prefill(*args, **kwargs)
+
+
+def kv_append(*args, **kwargs):
+    return get().kv_append(*args, **kwargs)
+
+
+def upcast(*args, **kwargs):
+    return get().upcast(*args, **kwargs)
+
+
+def max_threads() -> int:
+    return get().max_threads()
+
+
+__all__ = ["Oracle", "build", "compile_library", "get", "decode", "prefill", "kv_append",
+           "upcast", "max_threads", "DTYPE_CODES", "ELEM_BYTES", "LIB_PATH", "SOURCE"]

@@ -1,0 +1,474 @@
+"""Pins for the CPU oracle: checks against what the pages and the mathematics fix.
+
+Each ``pin_*`` function takes an ``oracle.Oracle`` instance and raises
+``AssertionError`` when the oracle disagrees with the fixed value. They are
+run against the real oracle (test_oracle_pins.py) and against deliberately
+broken builds of it (test_oracle_mutants.py), which each pin set must catch.
+
+The expected values never come from the oracle's own formula retyped:
+  * library routines that compute the same textbook result independently
+    (torch's scaled_dot_product_attention in float64, torch's dtype casts);
+  * closed forms (one key -> its value; equal keys or zero scale -> mean of
+    the values; two keys -> logistic weights; hand-worked fixtures);
+  * invariants the definition implies (GQA equals MHA with the KV heads
+    repeated, causal row i equals decode over positions <= i, relabelling
+    physical blocks changes nothing, poisoned unread bytes change nothing,
+    affine maps of V commute, uniform score shifts cancel, duplicated tokens
+    cancel, outputs stay in the convex hull of V).
+
+Page sources: "注意力演进与推理流程" (jerryiiii.gitbook.io), section 3.1 GQA
+(g = floor(h/G)) and section 3.2 (repeat_interleave of KV heads); the vLLM
+concepts page (yyzxw.github.io), self-attention Steps 2-4, decode attention
+over K<=t, V<=t, and the block table / slot mapping paragraph; "LLM 推理全过程的
+维度变化与核心公式" (research.frankk.site), sections on decode shapes, the causal
+mask and Paged Attention's 16-token blocks.
+"""
+from __future__ import annotations
+
+import json
+import math
+from pathlib import Path
+
+import numpy as np
+import torch
+
+GOLDEN = Path(__file__).resolve().parent / "golden"
+
+
+# ---- test-side helpers (no oracle code) ---------------------------------------
+
+def stored(x: torch.Tensor, dtype: str) -> np.ndarray:
+    """Stored bit patterns of a float tensor in the oracle's calling convention."""
+    if dtype == "f32":
+        return x.to(torch.float32).contiguous().numpy()
+    t = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return x.to(t).contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def exact(x_stored: np.ndarray, dtype: str) -> torch.Tensor:
+    """float64 tensor of stored values, via torch's own casts."""
+    if dtype == "f32":
+        return torch.from_numpy(x_stored.astype(np.float64))
+    t = {"bf16": torch.bfloat16, "f16": torch.float16}[dtype]
+    return torch.from_numpy(x_stored.view(np.int16).copy()).view(t).to(torch.float64)
+
+
+def pack_pool(seqs, block_size: int, num_blocks: int, rng, fill):
+    """Scatter per-sequence rows [ctx][n_kv][d] into a [nb][n_kv][bs][d] pool.
+
+    Logical block j of sequence b goes to physical block ``bt[b][j]``; physical
+    ids are a seeded permutation. Unused block-table entries point at the
+    remaining (fill-valued) blocks, or at block 0 if none remain.
+    """
+    n_kv, d = seqs[0].shape[1], seqs[0].shape[2]
+    nblk = [-(-s.shape[0] // block_size) for s in seqs]
+    maxb = max(1, max(nblk))
+    perm = rng.permutation(num_blocks)
+    assert sum(nblk) <= num_blocks
+    pool = np.full((num_blocks, n_kv, block_size, d), fill, dtype=seqs[0].dtype)
+    bt = np.zeros((len(seqs), maxb), dtype=np.int32)
+    cur = 0
+    for b, s in enumerate(seqs):
+        for j in range(nblk[b]):
+            phys = perm[cur]
+            cur += 1
+            bt[b, j] = phys
+            rows = s[j * block_size:(j + 1) * block_size]            # [n][n_kv][d]
+            pool[phys, :, :rows.shape[0], :] = rows.transpose(1, 0, 2)
+    spare = perm[cur:]
+    for b in range(len(seqs)):
+        for j in range(nblk[b], maxb):
+            bt[b, j] = spare[(b + j) % len(spare)] if len(spare) else 0
+    return pool, bt
+
+
+def sdpa64(q, k, v, scale, causal=False):
+    """torch's scaled_dot_product_attention in float64 on the CPU; q [H][Lq][d], k/v [H][Lk][d]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), scale=scale, is_causal=causal)[0]
+
+
+def rand_seqs(rng_t: torch.Generator, ctxs, n_kv, d, dtype):
+    return [stored(torch.randn(c, n_kv, d, generator=rng_t), dtype) for c in ctxs]
+
+
+def decode_case(seed, ctxs, n_q, n_kv, d, dtype="f32", bs=4, extra_blocks=3, fill=np.nan):
+    """Random contiguous sequences plus their paged form; returns everything a pin needs."""
+    g = torch.Generator().manual_seed(seed)
+    rng = np.random.default_rng(seed)
+    ks = rand_seqs(g, ctxs, n_kv, d, dtype)
+    vs = rand_seqs(g, ctxs, n_kv, d, dtype)
+    q = stored(torch.randn(len(ctxs), n_q, d, generator=g), dtype)
+    nb = sum(-(-c // bs) for c in ctxs) + extra_blocks
+    fill_s = stored(torch.tensor([fill], dtype=torch.float64), dtype)[0]
+    kp, bt = pack_pool(ks, bs, nb, np.random.default_rng(seed + 1), fill_s)
+    vp, bt2 = pack_pool(vs, bs, nb, np.random.default_rng(seed + 1), fill_s)
+    assert (bt == bt2).all()
+    return dict(q=q, ks=ks, vs=vs, kp=kp, vp=vp, bt=bt, ctx=np.asarray(ctxs, np.int32),
+                scale=1.0 / math.sqrt(d), n_q=n_q, n_kv=n_kv, d=d, dtype=dtype, rng=rng)
+
+
+def run_decode(orc, c, **over):
+    args = dict(q=c["q"], k_pool=c["kp"], v_pool=c["vp"], dtype=c["dtype"],
+                block_table=c["bt"], context_lens=c["ctx"], scale=c["scale"])
+    args.update(over)
+    return orc.decode(**args)
+
+
+def close(a, b, tol, what):
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    assert a.shape == b.shape, f"{what}: shape {a.shape} vs {b.shape}"
+    assert np.isfinite(a).all(), f"{what}: non-finite oracle output"
+    err = float(np.max(np.abs(a - b))) if a.size else 0.0
+    assert err <= tol, f"{what}: max abs err {err:.3e} > {tol:.1e}"
+
+
+# ---- widening of stored values --------------------------------------------------
+
+def pin_upcast_bf16_every_pattern(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.upcast(bits, "bf16")
+    want = torch.from_numpy(bits.view(np.int16).copy()).view(torch.bfloat16).to(torch.float64).numpy()
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all(), "bf16 NaN patterns differ"
+    assert (got[~nan] == want[~nan]).all(), "bf16 widening differs from torch's cast"
+
+
+def pin_upcast_f16_every_pattern(orc):
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.upcast(bits, "f16")
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert (np.isnan(got) == nan).all(), "f16 NaN patterns differ"
+    assert (got[~nan] == want[~nan]).all(), "f16 widening differs from numpy's cast"
+
+
+# ---- decode: library routine ---------------------------------------------------------
+
+def _decode_vs_sdpa(orc, n_q, n_kv, dtype, seed):
+    ctxs = [1, 5, 9, 16, 23]
+    c = decode_case(seed, ctxs, n_q, n_kv, 8, dtype=dtype)
+    got = run_decode(orc, c)
+    G = n_q // n_kv
+    for b, L in enumerate(ctxs):
+        q = exact(c["q"][b], dtype).unsqueeze(1)                           # [n_q][1][d]
+        k = exact(c["ks"][b], dtype).permute(1, 0, 2).repeat_interleave(G, dim=0)  # [n_q][L][d]
+        v = exact(c["vs"][b], dtype).permute(1, 0, 2).repeat_interleave(G, dim=0)
+        want = sdpa64(q, k.contiguous(), v.contiguous(), c["scale"])[:, 0, :]
+        close(got[b], want.numpy(), 1e-12, f"decode vs sdpa b={b} ctx={L}")
+
+
+def pin_decode_gqa_matches_library_sdpa(orc):
+    _decode_vs_sdpa(orc, n_q=8, n_kv=2, dtype="f32", seed=11)
+
+
+def pin_decode_mha_matches_library_sdpa(orc):
+    _decode_vs_sdpa(orc, n_q=3, n_kv=3, dtype="f32", seed=12)
+
+
+def pin_decode_mqa_matches_library_sdpa(orc):
+    _decode_vs_sdpa(orc, n_q=4, n_kv=1, dtype="bf16", seed=13)
+
+
+def pin_decode_f16_matches_library_sdpa(orc):
+    _decode_vs_sdpa(orc, n_q=4, n_kv=2, dtype="f16", seed=14)
+
+
+# ---- decode: closed forms --------------------------------------------------------
+
+def pin_decode_single_key_returns_its_value(orc):
+    c = decode_case(21, [1, 1], 4, 2, 8)
+    got = run_decode(orc, c)
+    for b in range(2):
+        for h in range(4):
+            want = c["vs"][b][0, h // 2].astype(np.float64)
+            assert (got[b, h] == want).all(), "ctx=1 must return v exactly"
+
+
+def pin_decode_equal_keys_give_mean_value(orc):
+    c = decode_case(22, [7, 12], 4, 2, 8)
+    for b in range(2):
+        c["kp"][c["bt"][b]] = c["kp"][c["bt"][b][0], :, 0:1, :]   # every slot of b's blocks
+    got = run_decode(orc, c)
+    for b in range(2):
+        for h in range(4):
+            want = c["vs"][b][:, h // 2].astype(np.float64).mean(axis=0)
+            close(got[b, h], want, 1e-14, "equal keys -> mean(V)")
+
+
+def pin_decode_zero_scale_gives_mean_value(orc):
+    c = decode_case(23, [5, 13], 2, 1, 8)
+    got = run_decode(orc, c, scale=0.0)
+    for b in range(2):
+        want = c["vs"][b][:, 0].astype(np.float64).mean(axis=0)
+        close(got[b, 0], want, 1e-14, "scale=0 -> mean(V)")
+
+
+def pin_decode_two_keys_logistic(orc):
+    c = decode_case(24, [2], 2, 1, 8)
+    got = run_decode(orc, c)
+    k = c["ks"][0][:, 0].astype(np.float64)
+    v = c["vs"][0][:, 0].astype(np.float64)
+    for h in range(2):
+        q = c["q"][0, h].astype(np.float64)
+        delta = c["scale"] * float(q @ (k[1] - k[0]))       # s1 - s0
+        w1 = 1.0 / (1.0 + math.exp(-delta))
+        close(got[0, h], (1 - w1) * v[0] + w1 * v[1], 1e-14, "two keys -> logistic weights")
+
+
+def pin_decode_hand_worked_fixture(orc):
+    fx = json.loads((GOLDEN / "decode_hand_worked.json").read_text())
+    bs, d = fx["block_size"], fx["head_dim"]
+    k = np.zeros((1, 1, bs, d), np.float32)
+    v = np.zeros((1, 1, bs, d), np.float32)
+    k[0, 0, :2] = np.asarray(fx["k"], np.float32)
+    v[0, 0, :2] = np.asarray(fx["v"], np.float32)
+    q = np.asarray(fx["q"], np.float32).reshape(1, 1, d)
+    got = orc.decode(q, k, v, "f32", np.zeros((1, 1), np.int32), np.asarray([2], np.int32),
+                     fx["scale"])
+    close(got[0, 0], fx["expected"], fx["atol"], "hand-worked decode fixture")
+
+
+def pin_decode_dominant_key(orc):
+    c = decode_case(25, [9], 1, 1, 8)
+    q = c["q"][0, 0].astype(np.float64)
+    j = 5
+    c["kp"][c["bt"][0][j // 4], 0, j % 4] = (q * 400.0).astype(np.float32)  # score >> others
+    got = run_decode(orc, c)
+    close(got[0, 0], c["vs"][0][j, 0], 1e-9, "dominant key selects its value")
+
+
+def pin_decode_empty_context_is_zero(orc):
+    c = decode_case(26, [0, 6], 2, 1, 8)
+    got = run_decode(orc, c)
+    assert (got[0] == 0).all(), "ctx=0 must give a zero row"
+    assert np.isfinite(got[1]).all()
+
+
+# ---- decode: invariants --------------------------------------------------------------
+
+def pin_decode_gqa_equals_mha_with_repeated_heads(orc):
+    n_q, n_kv = 8, 2
+    G = n_q // n_kv
+    c = decode_case(31, [3, 17, 30], n_q, n_kv, 8)
+    got = run_decode(orc, c)
+    rep = {k2: np.ascontiguousarray(np.repeat(c[k2], G, axis=1)) for k2 in ("kp", "vp")}
+    mha = orc.decode(c["q"], rep["kp"], rep["vp"], "f32", c["bt"], c["ctx"], c["scale"])
+    close(got, mha, 1e-15, "GQA vs MHA with repeat_interleaved KV heads")
+
+
+def pin_decode_block_relabelling_is_bitwise_invariant(orc):
+    c = decode_case(32, [6, 21, 14], 4, 2, 8)
+    base = run_decode(orc, c)
+    nb = c["kp"].shape[0]
+    relabel = np.random.default_rng(99).permutation(nb)
+    kp = np.empty_like(c["kp"])
+    vp = np.empty_like(c["vp"])
+    kp[relabel] = c["kp"]
+    vp[relabel] = c["vp"]
+    got = orc.decode(c["q"], kp, vp, "f32", relabel[c["bt"]].astype(np.int32), c["ctx"],
+                     c["scale"])
+    assert (got.view(np.uint64) == base.view(np.uint64)).all(), "relabelling changed bits"
+
+
+def pin_decode_ignores_poisoned_unread_bytes(orc):
+    c_nan = decode_case(33, [6, 21, 14], 4, 2, 8, fill=np.nan)
+    c_zero = decode_case(33, [6, 21, 14], 4, 2, 8, fill=0.0)
+    a = run_decode(orc, c_nan)
+    b = run_decode(orc, c_zero)
+    assert np.isfinite(a).all(), "NaN in unread slots leaked into the output"
+    assert (a == b).all(), "output depends on bytes outside the context"
+
+
+def _short_mantissa(a: np.ndarray) -> np.ndarray:
+    """fp32 values rounded to 8 significant bits, so small affine maps stay exact in fp32."""
+    return torch.from_numpy(a).to(torch.bfloat16).to(torch.float32).numpy()
+
+
+def pin_decode_affine_in_values(orc):
+    c = decode_case(34, [11, 4], 4, 2, 8)
+    c["vp"] = _short_mantissa(c["vp"])
+    base = run_decode(orc, c)
+    c2 = dict(c)
+    c2["vp"] = (c["vp"].astype(np.float64) * 2.0 + 3.0).astype(np.float32)
+    got = run_decode(orc, c2)
+    close(got, base * 2.0 + 3.0, 1e-13, "out(2V+3) = 2 out(V) + 3")
+
+
+def pin_decode_uniform_score_shift_cancels(orc):
+    c = decode_case(35, [13], 2, 1, 8)
+    c["kp"] = _short_mantissa(c["kp"])
+    base = run_decode(orc, c)
+    c2 = dict(c)
+    c2["kp"] = (c["kp"].astype(np.float64) + 0.75).astype(np.float32)   # every key + u
+    got = run_decode(orc, c2)
+    close(got, base, 1e-13, "adding one vector to every key leaves softmax unchanged")
+
+
+def pin_decode_duplicated_tokens_cancel(orc):
+    c = decode_case(36, [9], 2, 1, 8)
+    base = run_decode(orc, c)
+    ks = [np.repeat(c["ks"][0], 2, axis=0)]
+    vs = [np.repeat(c["vs"][0], 2, axis=0)]
+    nb = 8
+    kp, bt = pack_pool(ks, 4, nb, np.random.default_rng(5), np.float32(np.nan))
+    vp, _ = pack_pool(vs, 4, nb, np.random.default_rng(5), np.float32(np.nan))
+    got = orc.decode(c["q"], kp, vp, "f32", bt, np.asarray([18], np.int32), c["scale"])
+    close(got, base, 1e-14, "every token twice leaves the output unchanged")
+
+
+def pin_decode_output_in_convex_hull(orc):
+    c = decode_case(37, [25, 8], 4, 2, 8)
+    got = run_decode(orc, c)
+    for b in range(2):
+        for h in range(4):
+            v = c["vs"][b][:, h // 2]
+            assert (got[b, h] >= v.min(axis=0) - 1e-12).all()
+            assert (got[b, h] <= v.max(axis=0) + 1e-12).all()
+
+
+def pin_decode_selected_rows_match_full(orc):
+    c = decode_case(38, [9, 14], 4, 2, 8)
+    full = run_decode(orc, c)
+    sel = np.asarray([[1, 3], [0, 0], [1, 0]], np.int32)
+    part = run_decode(orc, c, sel=sel)
+    for r, (b, h) in enumerate(sel):
+        assert (part[r] == full[b, h]).all()
+
+
+def pin_walkthrough_shapes(orc):
+    # Decode attention output [B, n_q, 1, d] = [2, 32, 1, 128] for the walk-through's
+    # B=2, n_q=32, n_kv=8, d=128 (here with cache_len 3).
+    c = decode_case(39, [3, 3], 32, 8, 128, extra_blocks=0)
+    assert run_decode(orc, c).shape == (2, 32, 128)
+    # Prefill attention output [B, n_q, S, d] for S=10 is stored [B][S][n_q][d].
+    g = torch.Generator().manual_seed(40)
+    q = stored(torch.randn(2, 10, 32, 128, generator=g), "bf16")
+    k = stored(torch.randn(2, 10, 8, 128, generator=g), "bf16")
+    out = orc.prefill(q, k, k.copy(), "bf16", True, 1 / math.sqrt(128))
+    assert out.shape == (2, 10, 32, 128)
+
+
+# ---- prefill -----------------------------------------------------------------------------
+
+def _prefill_inputs(seed, B, S, n_q, n_kv, d, dtype="f32"):
+    g = torch.Generator().manual_seed(seed)
+    q = stored(torch.randn(B, S, n_q, d, generator=g), dtype)
+    k = stored(torch.randn(B, S, n_kv, d, generator=g), dtype)
+    v = stored(torch.randn(B, S, n_kv, d, generator=g), dtype)
+    return q, k, v
+
+
+def _prefill_vs_sdpa(orc, causal):
+    B, S, n_q, n_kv, d = 2, 11, 6, 2, 8
+    q, k, v = _prefill_inputs(41 + causal, B, S, n_q, n_kv, d)
+    scale = 1 / math.sqrt(d)
+    got = orc.prefill(q, k, v, "f32", causal, scale)
+    G = n_q // n_kv
+    for b in range(B):
+        qq = exact(q[b], "f32").permute(1, 0, 2)
+        kk = exact(k[b], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        vv = exact(v[b], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        want = sdpa64(qq.contiguous(), kk, vv, scale, causal=causal).permute(1, 0, 2)
+        close(got[b], want.numpy(), 1e-12, f"prefill causal={causal} vs sdpa")
+
+
+def pin_prefill_causal_matches_library_sdpa(orc):
+    _prefill_vs_sdpa(orc, True)
+
+
+def pin_prefill_noncausal_matches_library_sdpa(orc):
+    _prefill_vs_sdpa(orc, False)
+
+
+def pin_prefill_first_row_is_first_value(orc):
+    q, k, v = _prefill_inputs(43, 1, 7, 4, 2, 8)
+    got = orc.prefill(q, k, v, "f32", True, 0.35)
+    for h in range(4):
+        assert (got[0, 0, h] == v[0, 0, h // 2].astype(np.float64)).all()
+
+
+def pin_prefill_row_equals_decode_over_prefix(orc):
+    B, S, n_q, n_kv, d = 2, 13, 4, 2, 8
+    q, k, v = _prefill_inputs(44, B, S, n_q, n_kv, d, "bf16")
+    scale = 1 / math.sqrt(d)
+    pre = orc.prefill(q, k, v, "bf16", True, scale)
+    kp, bt = pack_pool([k[b] for b in range(B)], 4, 12, np.random.default_rng(3), np.uint16(0x7FC0))
+    vp, _ = pack_pool([v[b] for b in range(B)], 4, 12, np.random.default_rng(3), np.uint16(0x7FC0))
+    for i in (0, 3, 7, 12):
+        dec = orc.decode(np.ascontiguousarray(q[:, i]), kp, vp, "bf16", bt,
+                         np.asarray([i + 1] * B, np.int32), scale)
+        close(pre[:, i], dec, 1e-15, f"prefill row {i} vs decode over positions <= {i}")
+
+
+def pin_prefill_noncausal_row_equals_decode_over_all(orc):
+    B, S, n_q, n_kv, d = 1, 9, 2, 1, 8
+    q, k, v = _prefill_inputs(45, B, S, n_q, n_kv, d)
+    pre = orc.prefill(q, k, v, "f32", False, 0.3)
+    kp, bt = pack_pool([k[0]], 4, 3, np.random.default_rng(4), np.float32(np.nan))
+    vp, _ = pack_pool([v[0]], 4, 3, np.random.default_rng(4), np.float32(np.nan))
+    for i in (0, 4, 8):
+        dec = orc.decode(np.ascontiguousarray(q[:, i]), kp, vp, "f32", bt,
+                         np.asarray([S], np.int32), 0.3)
+        close(pre[:, i], dec, 1e-15, f"non-causal row {i} vs decode over all keys")
+
+
+# ---- kv_append ---------------------------------------------------------------------------
+
+def pin_kv_append_hand_worked_fixture(orc):
+    fx = json.loads((GOLDEN / "kv_append_small.json").read_text())
+    nb, n_kv, bs, d = fx["num_blocks"], fx["n_kv"], fx["block_size"], fx["head_dim"]
+    kp = np.full((nb, n_kv, bs, d), fx["pool_fill"], np.float32)
+    vp = kp.copy()
+    k = np.asarray(fx["k"], np.float32)
+    v = np.asarray(fx["v"], np.float32)
+    n = orc.kv_append(k, v, np.asarray(fx["slot_mapping"], np.int64), kp, vp)
+    assert n == fx["expected_written"]
+    want_k = np.full_like(kp, fx["pool_fill"])
+    want_v = want_k.copy()
+    for blk, head, off, krow, vrow in fx["expected_rows"]:
+        want_k[blk, head, off] = krow
+        want_v[blk, head, off] = vrow
+    assert (kp == want_k).all(), "K pool differs from the hand-worked placement"
+    assert (vp == want_v).all(), "V pool differs from the hand-worked placement"
+
+
+def pin_kv_append_is_a_bitwise_copy(orc):
+    g = torch.Generator().manual_seed(51)
+    nb, n_kv, bs, d, T = 6, 3, 4, 8, 9
+    kp = stored(torch.randn(nb, n_kv, bs, d, generator=g), "bf16")
+    vp = stored(torch.randn(nb, n_kv, bs, d, generator=g), "bf16")
+    k = stored(torch.randn(T, n_kv, d, generator=g), "bf16")
+    v = stored(torch.randn(T, n_kv, d, generator=g), "bf16")
+    slots = np.random.default_rng(51).choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[2] = -1
+    kp0, vp0 = kp.copy(), vp.copy()
+    assert orc.kv_append(k, v, slots, kp, vp) == T - 1
+    # Independent view of the same placement: a [nb*bs] row index over a
+    # [nb][bs][n_kv][d] transpose of the pool.
+    kt = kp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+    vt = vp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+    kt0 = kp0.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+    keep = np.ones(nb * bs, bool)
+    for t, s in enumerate(slots):
+        if s < 0:
+            continue
+        keep[s] = False
+        assert (kt[s] == k[t]).all() and (vt[s] == v[t]).all(), f"token {t} not at slot {s}"
+    assert (kt[keep] == kt0[keep]).all(), "kv_append touched a slot it was not given"
+
+
+def pin_kv_append_rejects_out_of_range_slot(orc):
+    kp = np.zeros((2, 1, 4, 2), np.float32)
+    vp = kp.copy()
+    k = np.ones((1, 1, 2), np.float32)
+    try:
+        orc.kv_append(k, k.copy(), np.asarray([8], np.int64), kp, vp)
+    except ValueError:
+        assert (kp == 0).all(), "a rejected append must not write"
+        return
+    raise AssertionError("slot 8 in an 8-slot pool was accepted")
+
+
+ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

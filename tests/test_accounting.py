@@ -1,0 +1,56 @@
+"""Byte and FLOP accounting against the figures the pages print."""
+import json
+from pathlib import Path
+
+import pytest
+
+from paged_gqa_attention_attn_amd import accounting as acc
+
+FX = json.loads((Path(__file__).parent / "golden" / "kv_bytes_from_pages.json").read_text())
+
+
+@pytest.mark.parametrize("case", FX["cases"], ids=lambda c: c["what"])
+def test_kv_cache_bytes_matches_pages(case):
+    n = acc.kv_cache_bytes(case["layers"], case["tokens"], case["n_kv"], case["head_dim"],
+                           case["elem_bytes"])
+    if "bytes" in case:
+        assert n == case["bytes"]
+    if "mib" in case:
+        assert n == case["mib"] * 2**20
+    if "gib" in case:
+        assert n == case["gib"] * 2**30
+
+
+def test_decode_kv_read_matches_pages():
+    c = FX["decode_read"]
+    assert acc.decode_kv_bytes([c["ctx"]], c["n_kv"], c["head_dim"], c["elem_bytes"]) == c["mib"] * 2**20
+
+
+def test_decode_flops_matches_pages():
+    c = FX["decode_qk_flops"]
+    one = c["flops_one_matmul"]
+    assert round(one / 1e6, 1) == c["printed_mflops"]
+    assert acc.decode_flops([c["ctx"]], c["n_q"], c["head_dim"]) == 2 * one
+
+
+def test_prefill_full_square_flops_matches_pages():
+    c = FX["prefill_qk_flops"]
+    one = c["flops_one_matmul"]
+    assert round(one / 1e9, 1) == c["printed_gflops"]
+    assert acc.prefill_flops_full_square(c["batch"], c["seq_len"], c["n_q"], c["head_dim"]) == 2 * one
+
+
+def test_causal_flops_is_lower_triangle():
+    # S(S+1)/2 query-key pairs per head: for S=1 one pair, for S=2 three pairs.
+    assert acc.prefill_flops_causal(1, 1, 1, 1) == 4
+    assert acc.prefill_flops_causal(1, 2, 1, 1) == 12
+    assert acc.prefill_flops_causal(2, 4096, 32, 128) == 274_945_015_808
+
+
+def test_config_byte_totals():
+    # 8B-shaped decode: 32 sequences x 2048 tokens x 4096 B per token.
+    assert acc.decode_kv_bytes([2048] * 32, 8, 128, 2) == 268_435_456
+    # 70B-shaped long context: 1 GiB of KV.
+    assert acc.decode_kv_bytes([32768] * 8, 8, 128, 2) == 2**30
+    assert acc.decode_unique_kv_bytes([2000] * 4, 8, 128, 2, 1024, 4) == \
+        acc.decode_kv_bytes([2000] * 4, 8, 128, 2) - 3 * 1024 * 4096

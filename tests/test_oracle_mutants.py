@@ -1,0 +1,65 @@
+"""Planted mistakes in the oracle, on the CPU: every one must fail at least one pin.
+
+Each mutant is a textual edit of a private copy of oracle.c (the real source is
+never touched), compiled with gcc into a temporary directory. The edits are the
+plausible slips: a wrong head-to-group map, a dropped scale, a sign error, a
+missing normalisation, an off-by-one causal mask, wrong block or offset
+arithmetic, a transposed operand, a wrong widening of stored values. All
+mutants keep every memory access in bounds.
+"""
+from pathlib import Path
+
+import pytest
+
+import oracle
+from oracle_pins import ALL_PINS
+
+MUTANTS = {
+    "decode_group_map_mod": ("const int32_t g = h / group;                          /* [AE] 3.1",
+                             "const int32_t g = h % n_kv;                          /* [AE] 3.1"),
+    "prefill_group_map_mod": ("        const int32_t g = h / group;\n        const int32_t n_keys",
+                              "        const int32_t g = h % n_kv;\n        const int32_t n_keys"),
+    "dropped_scale": ("scores[t] = scale * dot;", "scores[t] = dot;"),
+    "exp_sign_flip": ("const double w = exp(scores[t] - m);", "const double w = exp(m - scores[t]);"),
+    "no_normalisation": ("out[c] /= den;", "out[c] /= 1.0;"),
+    "den_squares": ("den += w;", "den += w * w;"),
+    "causal_excludes_diagonal": ("causal ? i + 1 : seq_len", "causal ? (i > 0 ? i : 1) : seq_len"),
+    "block_offset_shift": ("const int64_t off = t % block_size;",
+                           "const int64_t off = (t + 1) % block_size;"),
+    "block_index_halved": ("block_table[(int64_t)b * max_blocks_per_seq + t / block_size]",
+                           "block_table[(int64_t)b * max_blocks_per_seq + t / block_size / 2]"),
+    "block_row_of_next_sequence": (
+        "block_table[(int64_t)b * max_blocks_per_seq + t / block_size]",
+        "block_table[(int64_t)((b + 1) % batch) * max_blocks_per_seq + t / block_size]"),
+    "append_offset_shift": ("const int64_t off = slot % block_size;",
+                            "const int64_t off = (slot + 1) % block_size;"),
+    "append_head_offset_transposed": (
+        "const size_t dst = (((size_t)blk * n_kv + g) * block_size + off) * row;",
+        "const size_t dst = (((size_t)blk * block_size + off) * n_kv + g) * row;"),
+    "query_index_transposed": ("load_elem(q, dtype, ((int64_t)b * n_q + h) * head_dim + c)",
+                               "load_elem(q, dtype, ((int64_t)h * batch + b) * head_dim + c)"),
+    "values_read_from_keys": ("out[c] += w * load_elem(keys->v_base",
+                              "out[c] += w * load_elem(keys->k_base"),
+    "bf16_widening_shift": ("((uint32_t)h) << 16", "((uint32_t)h) << 15"),
+    "f16_exponent_bias": ("ldexp((double)(1024 + frac), e - 25)",
+                          "ldexp((double)(1024 + frac), e - 24)"),
+    "max_tracks_minimum": ("if (scores[t] > m) m = scores[t];", "if (scores[t] < m) m = scores[t];"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = oracle.SOURCE.read_text()
+    assert src.count(old) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant_src = tmp_path / "oracle_mutant.c"
+    mutant_src.write_text(src.replace(old, new))
+    lib = oracle.compile_library(mutant_src, tmp_path / "liboracle_mutant.so")
+    orc = oracle.Oracle(lib)
+    caught = []
+    for pin_name, pin in ALL_PINS.items():
+        try:
+            pin(orc)
+        except Exception as e:  # AssertionError, or a rejection the real oracle never raises
+            caught.append((pin_name, type(e).__name__))
+    assert caught, f"no pin catches mutant {name}"
