@@ -1,0 +1,161 @@
+/*
+ * pagedattn.h -- C ABI of the MI355X (gfx950) paged GQA attention library.
+ *
+ * Scaled dot-product attention softmax(q K^T * scale + M) V over a key/value
+ * cache that is stored in fixed-size blocks reached through a block table.
+ *
+ * Sources (web pages):
+ *  [AE] "注意力演进与推理流程", jerryiiii.gitbook.io/llm-review/notes/attention/
+ *       attention-evolution-and-inference: section 1.1 (attention formula and
+ *       causal mask), section 3.1 (GQA: query head h reads KV group floor(h/G)),
+ *       "变革 1" (PagedAttention: fixed blocks such as 16 tokens).
+ *  [PD] xinc.fun/index.php/archives/233: section 2 (shapes, causal mask),
+ *       section 3 (KV cache append), section 6 (block table over scattered blocks).
+ *  [VC] yyzxw.github.io/acknowledge/research/vllm-concepts-deep-dive/section-1.html:
+ *       decode attention over K<=t, V<=t; attention kernels take a block table and
+ *       a slot mapping instead of contiguous pointers.
+ *  [IW] "LLM 推理全过程的维度变化与核心公式", research.frankk.site/notes/
+ *       llm-inference-walkthrough: "Decode 阶段维度流转" (append at cache_len, then
+ *       read the whole cache; no mask in decode), "Prefill 阶段维度流转",
+ *       "KV Cache 的形状与增长" (16-token blocks), "工程优化怎么嵌进公式"
+ *       (Flash Attention online softmax; Flash Decoding split + log-sum-exp).
+ *
+ * Conventions for every entry point
+ *  - All data pointers are device pointers owned by the caller (for example
+ *    torch allocations). The library keeps no reference after the call returns.
+ *  - Every call only enqueues work on `stream` (a hipStream_t passed as void*;
+ *    NULL is the null stream) and returns before the GPU finishes.
+ *  - Data pointers must be 16-byte aligned; rows are contiguous in the stated
+ *    layouts. Element offsets are computed in 64-bit arithmetic.
+ *  - Return value: PA_OK (0) or a negative pa_status. On failure nothing was
+ *    enqueued and pa_last_error() describes the problem.
+ *  - Device-resident metadata (block ids, slots, context lengths) is not read
+ *    by the host. Kernels bounds-check it: an out-of-range slot is skipped; a
+ *    sequence whose context length exceeds max_blocks_per_seq * block_size or
+ *    whose block table names a block outside the pool gets a NaN output row
+ *    instead of an out-of-bounds read.
+ */
+#ifndef PAGEDATTN_H
+#define PAGEDATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Element types. q/k/v and the cache share one type; outputs are f32 or that type. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+
+typedef enum {
+    PA_OK = 0,
+    PA_ERR_INVALID_ARG = -1, /* null pointer, bad size, misalignment, n_q % n_kv != 0 */
+    PA_ERR_UNSUPPORTED = -2, /* dtype / head_dim / block_size without a kernel        */
+    PA_ERR_HIP = -3          /* a HIP runtime call or launch failed                    */
+} pa_status;
+
+/*
+ * Paged cache description. Each of the two pools (K and V) is
+ *   [num_blocks][n_kv][block_size][head_dim], head_dim fastest,
+ * so element (block, kv_head, offset, c) sits at
+ *   ((block * n_kv + kv_head) * block_size + offset) * head_dim + c.
+ * Supported: block_size 16; head_dim 64 or 128; dtype f32, bf16 or f16.
+ */
+typedef struct {
+    int32_t num_blocks;
+    int32_t block_size;
+    int32_t n_kv;
+    int32_t head_dim;
+    pa_dtype dtype;
+} pa_cache_desc;
+
+/*
+ * kv_append -- write new K/V rows into the paged cache through slot_mapping.
+ * [VC] (slot mapping given to attention kernels); [IW] decode step: write the
+ * new K/V at position cache_len; prefill: write positions 0..S-1; [PD] section 3.
+ *
+ *   k, v          [num_tokens][n_kv][head_dim] in cache->dtype
+ *   slot_mapping  int64 [num_tokens]; token t goes to block slot / block_size,
+ *                 offset slot % block_size. slot < 0 marks a padding token
+ *                 (skipped); slot >= num_blocks * block_size is skipped too.
+ *   k_cache, v_cache  the pools described by `cache`, updated in place.
+ * The write is a bit-exact copy. Two tokens with the same slot race (which one
+ * lands is unspecified). num_tokens == 0 is a no-op.
+ */
+int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                 void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream);
+
+/*
+ * Bytes of scratch memory pa_paged_attn_decode needs for these arguments
+ * (partial results of a context split into partitions, [VC]/[IW] Flash Decoding).
+ * 0 when every sequence fits in one partition. Returns 0 as well for invalid
+ * arguments; the decode call then reports the error.
+ */
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc* cache);
+
+/*
+ * paged_attn_decode -- one query token per sequence attends to its cached
+ * context through the block table. [VC] decode attention over K<=t, V<=t;
+ * [AE] 3.1 GQA grouping; [IW] "Decode 阶段维度流转" (no causal mask in decode),
+ * Flash Attention's running max/sum and Flash Decoding's split + log-sum-exp.
+ *
+ *   q             [batch][n_q][head_dim] in cache->dtype
+ *   k_cache, v_cache  pools described by `cache`
+ *   block_table   int32 [batch][max_blocks_per_seq]; entry j = physical block of
+ *                 the sequence's logical block j (positions 16j .. 16j+15)
+ *   context_lens  int32 [batch]: number of positions attended, counting the
+ *                 token appended in the same step (positions 0..ctx-1)
+ *   scale         multiplies q.k (usually 1/sqrt(head_dim))
+ *   out           [batch][n_q][head_dim], out_dtype PA_F32 or cache->dtype
+ *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
+ *                 bytes for the same arguments; may be NULL when that is 0.
+ * Query head h reads KV head h / (n_q / n_kv). ctx == 0 gives a zero row.
+ * Results depend only on logical positions, so relabelling physical blocks
+ * leaves every output bit unchanged. Calls that share a workspace must not
+ * overlap on the GPU.
+ */
+int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * paged_attn_prefill -- attention of a whole prompt over itself.
+ * [AE] 1.1 / [PD] section 2: A = softmax(Q K^T / sqrt(d) + M), O = A V with the
+ * causal mask M_ij = 0 for j <= i and -inf otherwise; [AE] 3.1 GQA grouping;
+ * [IW] "Prefill 阶段维度流转".
+ *
+ *   q     [batch][seq_len][n_q][head_dim]   in dtype (bf16 or f16)
+ *   k, v  [batch][seq_len][n_kv][head_dim]  in dtype
+ *   causal  1: row i attends to keys 0..i; 0: to all seq_len keys
+ *   out   [batch][seq_len][n_q][head_dim], out_dtype PA_F32 or dtype
+ * Supported: head_dim 128 (and 64); dtype bf16 or f16.
+ */
+int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
+                          int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
+                          int32_t head_dim, int32_t causal, float scale, void* out,
+                          pa_dtype out_dtype, void* stream);
+
+/*
+ * Tuning override for the decode partition size, in tokens (a multiple of 16
+ * and of the work one workgroup takes per pass). 0 restores the built-in
+ * choice. Affects later pa_decode_workspace_bytes and pa_paged_attn_decode
+ * calls in this process; returns the previous value, or -1 (and leaves the
+ * setting unchanged) for an invalid value.
+ */
+int32_t pa_set_decode_partition_tokens(int32_t tokens);
+
+/* Thread-local, NUL-terminated description of the last failure on this thread. */
+const char* pa_last_error(void);
+
+/* Library ABI version (major * 100 + minor). */
+int32_t pa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PAGEDATTN_H */

@@ -1,0 +1,161 @@
+"""MI355X (gfx950) paged GQA attention: Python binding of the C-ABI library.
+
+The functions here have the names of the library's entry points and only
+marshal arguments: they check that tensors are contiguous device tensors of
+the right type, read sizes from shapes, and pass raw pointers and the current
+HIP stream to ``libpagedattn.so``. Every step of the computation runs in the
+library's HIP kernels; there is no fallback implementation.
+
+Layouts (see include/pagedattn.h):
+  q            [B][n_q][d]                 (decode)
+  k/v caches   [num_blocks][n_kv][16][d]
+  block_table  int32 [B][max_blocks_per_seq]
+  context_lens int32 [B]
+  slot_mapping int64 [T]
+  prefill q    [B][S][n_q][d], k/v [B][S][n_kv][d]
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import CacheDesc, LibraryNotBuilt
+
+__all__ = ["kv_append", "paged_attn_decode", "paged_attn_prefill", "decode_workspace_bytes",
+           "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
+
+_DTYPE = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
+
+
+class PagedAttnError(RuntimeError):
+    def __init__(self, fn: str, code: int):
+        super().__init__(f"{fn} failed ({code}): {_lib.last_error()}")
+        self.code = code
+
+
+def _check(fn: str, code: int) -> None:
+    if code != _lib.PA_OK:
+        raise PagedAttnError(fn, code)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be a device tensor (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype} (got {t.dtype})")
+    return t.data_ptr()
+
+
+def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
+    s = stream if stream is not None else torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _cache_desc(k_cache: torch.Tensor) -> CacheDesc:
+    if k_cache.dim() != 4:
+        raise ValueError("caches must be [num_blocks][n_kv][block_size][head_dim]")
+    if k_cache.dtype not in _DTYPE:
+        raise TypeError(f"unsupported cache dtype {k_cache.dtype}")
+    nb, n_kv, bs, d = k_cache.shape
+    return CacheDesc(nb, bs, n_kv, d, _DTYPE[k_cache.dtype])
+
+
+def library_version() -> int:
+    return int(_lib.load().pa_version())
+
+
+def set_decode_partition_tokens(tokens: int) -> int:
+    """Override the decode partition size (tokens); 0 restores the built-in choice."""
+    prev = _lib.load().pa_set_decode_partition_tokens(int(tokens))
+    if prev < 0:
+        raise ValueError(f"invalid partition size {tokens}")
+    return int(prev)
+
+
+def kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+              k_cache: torch.Tensor, v_cache: torch.Tensor, stream=None) -> None:
+    """Write k/v rows [T][n_kv][d] into the caches at ``slot_mapping`` (int64 [T])."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape or k.shape != v.shape:
+        raise ValueError("k/v or cache shapes differ")
+    if k.dim() != 3 or k.shape[1:] != k_cache.shape[1:2] + k_cache.shape[3:]:
+        raise ValueError("k and v must be [T][n_kv][head_dim] matching the cache")
+    T = k.shape[0]
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    dt = k_cache.dtype
+    _check("pa_kv_append", L.pa_kv_append(
+        _dev(k, "k", dt), _dev(v, "v", dt), _dev(slot_mapping, "slot_mapping", torch.int64), T,
+        _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), ctypes.byref(desc),
+        _stream(k_cache, stream)))
+
+
+def decode_workspace_bytes(batch: int, n_q: int, max_blocks_per_seq: int,
+                           k_cache: torch.Tensor) -> int:
+    desc = _cache_desc(k_cache)
+    return int(_lib.load().pa_decode_workspace_bytes(batch, n_q, max_blocks_per_seq,
+                                                     ctypes.byref(desc)))
+
+
+def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                      block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                      out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """Decode attention of q [B][n_q][d] over the paged caches; returns out [B][n_q][d]."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, n_q, d = q.shape
+    if d != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the cache")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][n_q][d] in a supported dtype")
+    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dt = k_cache.dtype
+    _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
+        _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
+                       scale: float, out: torch.Tensor | None = None,
+                       out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """Attention of a prompt over itself: q [B][S][n_q][d], k/v [B][S][n_kv][d]."""
+    L = _lib.load()
+    if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
+        raise ValueError("q must be [B][S][n_q][d] and k, v [B][S][n_kv][d]")
+    B, S, n_q, d = q.shape
+    if k.shape[0] != B or k.shape[1] != S or k.shape[3] != d:
+        raise ValueError("k/v batch, length or head_dim differ from q")
+    if q.dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {q.dtype}")
+    if out is None:
+        out = torch.empty((B, S, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][S][n_q][d] in a supported dtype")
+    dt = q.dtype
+    _check("pa_paged_attn_prefill", L.pa_paged_attn_prefill(
+        _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
+        d, int(bool(causal)), float(scale), _dev(out, "out"), _DTYPE[out.dtype],
+        _stream(q, stream)))
+    return out

@@ -1,0 +1,80 @@
+"""ctypes loader for ``libpagedattn.so`` (the gfx950 HIP library behind include/pagedattn.h).
+
+Loading fails loudly when the library has not been built: there is no
+fallback implementation of any entry point.
+"""
+from __future__ import annotations
+
+import ctypes
+from pathlib import Path
+
+LIB_PATH = Path(__file__).resolve().parent / "libpagedattn.so"
+
+PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
+
+EXPORTS = (
+    "pa_kv_append",
+    "pa_decode_workspace_bytes",
+    "pa_paged_attn_decode",
+    "pa_paged_attn_prefill",
+    "pa_set_decode_partition_tokens",
+    "pa_last_error",
+    "pa_version",
+)
+
+
+class CacheDesc(ctypes.Structure):
+    """Mirror of ``pa_cache_desc``."""
+
+    _fields_ = [
+        ("num_blocks", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("n_kv", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("dtype", ctypes.c_int),
+    ]
+
+
+class LibraryNotBuilt(RuntimeError):
+    pass
+
+
+_lib: ctypes.CDLL | None = None
+
+
+def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
+    """Load (once) and type the shared library."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = Path(path)
+    if not path.exists():
+        raise LibraryNotBuilt(
+            f"{path} does not exist: build the HIP library first "
+            "(python -c 'import __graft_entry__ as g; g.build()')")
+    L = ctypes.CDLL(str(path))
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    cd = ctypes.POINTER(CacheDesc)
+    L.pa_kv_append.argtypes = [vp, vp, vp, i32, vp, vp, cd, vp]
+    L.pa_kv_append.restype = ctypes.c_int
+    L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, cd]
+    L.pa_decode_workspace_bytes.restype = sz
+    L.pa_paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cd, vp, i32, vp, ctypes.c_float, vp,
+                                       ctypes.c_int, vp, sz, vp]
+    L.pa_paged_attn_decode.restype = ctypes.c_int
+    L.pa_paged_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_float, vp, ctypes.c_int, vp]
+    L.pa_paged_attn_prefill.restype = ctypes.c_int
+    L.pa_set_decode_partition_tokens.argtypes = [i32]
+    L.pa_set_decode_partition_tokens.restype = i32
+    L.pa_last_error.argtypes = []
+    L.pa_last_error.restype = ctypes.c_char_p
+    L.pa_version.argtypes = []
+    L.pa_version.restype = i32
+    _lib = L
+    return L
+
+
+def last_error() -> str:
+    return load().pa_last_error().decode(errors="replace")

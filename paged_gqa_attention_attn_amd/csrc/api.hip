@@ -1,0 +1,277 @@
+// api.hip -- C-ABI entry points: argument validation, launch planning, error reporting.
+//
+// No entry point reads device memory on the host or synchronises the stream;
+// every check here uses host-side arguments only. See include/pagedattn.h for
+// the contract of each call.
+#include <atomic>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "launch.h"
+#include "pagedattn.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(PA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int elem_bytes(pa_dtype d) {
+    switch (d) {
+    case PA_F32: return 4;
+    case PA_BF16: return 2;
+    case PA_F16: return 2;
+    }
+    return 0;
+}
+
+pa::Elem to_elem(pa_dtype d) { return static_cast<pa::Elem>(static_cast<int>(d)); }
+
+std::atomic<int32_t> g_partition_tokens{0};
+
+constexpr int kBlockSize = 16;
+constexpr int kMaxWaves = 8;
+
+int check_cache(const pa_cache_desc* c) {
+    if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
+    if (c->num_blocks <= 0 || c->n_kv <= 0 || c->head_dim <= 0 || c->block_size <= 0)
+        return fail(PA_ERR_INVALID_ARG,
+                    "cache sizes must be positive (num_blocks=%d n_kv=%d head_dim=%d block_size=%d)",
+                    c->num_blocks, c->n_kv, c->head_dim, c->block_size);
+    if (elem_bytes(c->dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)c->dtype);
+    if (c->block_size != kBlockSize)
+        return fail(PA_ERR_UNSUPPORTED, "block_size %d has no kernel (supported: 16)", c->block_size);
+    if (c->head_dim != 64 && c->head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "head_dim %d has no kernel (supported: 64, 128)", c->head_dim);
+    return PA_OK;
+}
+
+// Decode launch plan; a pure function of the host arguments so that
+// pa_decode_workspace_bytes and pa_paged_attn_decode always agree.
+struct Plan {
+    int32_t gw, hs_wg, hsg, waves_tok, blocks_per_wave, nparts_max;
+    size_t ws_floats_m, ws_floats_acc;  // floats in m (== l) and acc arrays
+};
+
+int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c, Plan* pl) {
+    const int32_t G = n_q / c->n_kv;
+    // Query heads per wave: 4 when the group allows it (keeps acc at 64 fp32
+    // registers for head_dim 128), else the largest power of two dividing G.
+    const int32_t gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    const int32_t hs = G / gw;
+    int32_t hs_wg = 1;
+    for (int32_t d = kMaxWaves; d >= 1; --d)
+        if (hs % d == 0) {
+            hs_wg = d;
+            break;
+        }
+    const int32_t waves_tok = kMaxWaves / hs_wg;
+    const int32_t unit = waves_tok * kBlockSize;  // tokens per pass of the workgroup
+
+    int32_t tokens = g_partition_tokens.load();
+    if (tokens <= 0) {
+        // Built-in choice: 1024-token partitions (8 blocks per wave at 8 token-waves).
+        tokens = 1024;
+    }
+    int32_t bpw = tokens / unit;
+    if (bpw < 1) bpw = 1;
+    if (bpw > 64) bpw = 64;
+    const int32_t bpp = bpw * waves_tok;
+    const int32_t nparts_max = (max_blocks + bpp - 1) / bpp;
+
+    pl->gw = gw;
+    pl->hs_wg = hs_wg;
+    pl->hsg = hs / hs_wg;
+    pl->waves_tok = waves_tok;
+    pl->blocks_per_wave = bpw;
+    pl->nparts_max = nparts_max < 1 ? 1 : nparts_max;
+    if (pl->nparts_max > 1) {
+        pl->ws_floats_m = (size_t)batch * n_q * pl->nparts_max;
+        pl->ws_floats_acc = pl->ws_floats_m * (size_t)c->head_dim;
+    } else {
+        pl->ws_floats_m = pl->ws_floats_acc = 0;
+    }
+    return PA_OK;
+}
+
+size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
+
+size_t plan_bytes(const Plan& pl) {
+    if (pl.ws_floats_m == 0) return 0;
+    return 2 * round16(pl.ws_floats_m * sizeof(float)) + pl.ws_floats_acc * sizeof(float);
+}
+
+int check_decode_args(int32_t batch, int32_t n_q, const pa_cache_desc* cache,
+                      int32_t max_blocks_per_seq) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch %d < 0", batch);
+    if (n_q <= 0) return fail(PA_ERR_INVALID_ARG, "n_q %d must be positive", n_q);
+    if (n_q % cache->n_kv != 0)
+        return fail(PA_ERR_INVALID_ARG, "n_q (%d) is not a multiple of n_kv (%d)", n_q, cache->n_kv);
+    if (max_blocks_per_seq <= 0)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d must be positive", max_blocks_per_seq);
+    if ((int64_t)max_blocks_per_seq * kBlockSize > INT32_MAX / 2)
+        return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d too large", max_blocks_per_seq);
+    return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pa_version(void) { return 100; }
+
+const char* pa_last_error(void) { return g_err; }
+
+int32_t pa_set_decode_partition_tokens(int32_t tokens) {
+    if (tokens < 0 || (tokens % kBlockSize) != 0) return -1;
+    return g_partition_tokens.exchange(tokens);
+}
+
+int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
+                 void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream) {
+    int rc = check_cache(cache);
+    if (rc) return rc;
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache)
+        return fail(PA_ERR_INVALID_ARG, "kv_append: a pointer argument is NULL");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache))
+        return fail(PA_ERR_INVALID_ARG, "kv_append: k, v and the caches must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+        return fail(PA_ERR_INVALID_ARG, "kv_append: slot_mapping must be 8-byte aligned");
+    const int32_t row = cache->head_dim * elem_bytes(cache->dtype);
+    const hipError_t e = pa::launch_kv_append(k, v, slot_mapping, num_tokens, cache->n_kv, row,
+                                              cache->block_size,
+                                              (int64_t)cache->num_blocks * cache->block_size,
+                                              k_cache, v_cache, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_append launch");
+    return PA_OK;
+}
+
+size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
+                                 const pa_cache_desc* cache) {
+    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK) return 0;
+    Plan pl;
+    make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
+    return plan_bytes(pl);
+}
+
+int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
+    if (rc) return rc;
+    if (out_dtype != PA_F32 && out_dtype != cache->dtype)
+        return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    if (batch == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "decode: a pointer argument is NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "decode: q, caches and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return fail(PA_ERR_INVALID_ARG, "decode: block_table and context_lens must be 4-byte aligned");
+
+    Plan pl;
+    make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
+    const size_t need = plan_bytes(pl);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(PA_ERR_INVALID_ARG, "decode: workspace of %zu bytes required (got %zu)", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "decode: workspace must be 16-byte aligned");
+    }
+
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    if (need > 0) {
+        char* w = static_cast<char*>(workspace);
+        a.ws_m = reinterpret_cast<float*>(w);
+        a.ws_l = reinterpret_cast<float*>(w + round16(pl.ws_floats_m * sizeof(float)));
+        a.ws_acc = reinterpret_cast<float*>(w + 2 * round16(pl.ws_floats_m * sizeof(float)));
+    }
+    a.batch = batch;
+    a.n_q = n_q;
+    a.n_kv = cache->n_kv;
+    a.num_blocks = cache->num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.group = n_q / cache->n_kv;
+    a.gw = pl.gw;
+    a.hs_wg = pl.hs_wg;
+    a.hsg = pl.hsg;
+    a.waves_tok = pl.waves_tok;
+    a.blocks_per_wave = pl.blocks_per_wave;
+    a.nparts_max = pl.nparts_max;
+    a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
+    a.out_f32 = out_dtype == PA_F32;
+    const hipError_t e = pa::launch_decode(a, to_elem(cache->dtype), cache->head_dim,
+                                           static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode launch");
+    return PA_OK;
+}
+
+int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
+                          int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
+                          int32_t head_dim, int32_t causal, float scale, void* out,
+                          pa_dtype out_dtype, void* stream) {
+    if (dtype != PA_BF16 && dtype != PA_F16)
+        return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and f16 inputs");
+    if (out_dtype != PA_F32 && out_dtype != dtype)
+        return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
+    if (head_dim != 64 && head_dim != 128)
+        return fail(PA_ERR_UNSUPPORTED, "prefill head_dim %d has no kernel (supported: 64, 128)", head_dim);
+    if (batch < 0 || seq_len < 0) return fail(PA_ERR_INVALID_ARG, "batch and seq_len must be >= 0");
+    if (n_q <= 0 || n_kv <= 0) return fail(PA_ERR_INVALID_ARG, "n_q and n_kv must be positive");
+    if (n_q % n_kv != 0)
+        return fail(PA_ERR_INVALID_ARG, "n_q (%d) is not a multiple of n_kv (%d)", n_q, n_kv);
+    if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    if (batch == 0 || seq_len == 0) return PA_OK;
+    if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
+    if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "prefill: q, k, v and out must be 16-byte aligned");
+
+    pa::PrefillArgs a{};
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.out = out;
+    a.batch = batch;
+    a.seq_len = seq_len;
+    a.n_q = n_q;
+    a.n_kv = n_kv;
+    a.group = n_q / n_kv;
+    a.causal = causal;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PA_F32;
+    const hipError_t e = pa::launch_prefill(a, to_elem(dtype), head_dim, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "prefill: no kernel for these arguments");
+    if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return PA_OK;
+}
+
+}  // extern "C"

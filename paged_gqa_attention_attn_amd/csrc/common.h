@@ -1,0 +1,163 @@
+// common.h -- device helpers shared by the gfx950 kernels of the paged attention library.
+//
+// Element types, 16-byte chunk dot products, widening of stored values, and
+// wavefront (64-lane) cross-lane reductions built from DPP and the gfx950
+// permlane swaps. Nothing here is specific to one kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Element type tags: storage type and the dot product of two packed 16-byte chunks.
+struct F32 {
+    using storage = float;
+};
+struct BF16 {
+    using storage = uint16_t;
+};
+struct F16 {
+    using storage = uint16_t;
+};
+
+__device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+// acc + sum over the chunk of a[i] * b[i], accumulated in fp32.
+template <class E> __device__ __forceinline__ float chunk_dot(uint4 a, uint4 b, float acc);
+
+template <> __device__ __forceinline__ float chunk_dot<BF16>(uint4 a, uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.x),
+                                          __builtin_bit_cast(bf16x2_t, b.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.y),
+                                          __builtin_bit_cast(bf16x2_t, b.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.z),
+                                          __builtin_bit_cast(bf16x2_t, b.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a.w),
+                                          __builtin_bit_cast(bf16x2_t, b.w), acc, false);
+    return acc;
+}
+
+template <> __device__ __forceinline__ float chunk_dot<F16>(uint4 a, uint4 b, float acc) {
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.x), __builtin_bit_cast(f16x2_t, b.x),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.y), __builtin_bit_cast(f16x2_t, b.y),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.z), __builtin_bit_cast(f16x2_t, b.z),
+                                 acc, false);
+    acc = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a.w), __builtin_bit_cast(f16x2_t, b.w),
+                                 acc, false);
+    return acc;
+}
+
+template <> __device__ __forceinline__ float chunk_dot<F32>(uint4 a, uint4 b, float acc) {
+    acc = fmaf(as_f32(a.x), as_f32(b.x), acc);
+    acc = fmaf(as_f32(a.y), as_f32(b.y), acc);
+    acc = fmaf(as_f32(a.z), as_f32(b.z), acc);
+    acc = fmaf(as_f32(a.w), as_f32(b.w), acc);
+    return acc;
+}
+
+// Number of elements in one 16-byte chunk.
+template <class E> struct chunk_elems {
+    static constexpr int value = 16 / (int)sizeof(typename E::storage);
+};
+
+// Widen the elements of a 16-byte chunk to fp32 (exact for every type).
+template <class E> __device__ __forceinline__ void widen(uint4 a, float* o);
+
+template <> __device__ __forceinline__ void widen<BF16>(uint4 a, float* o) {
+    // bf16 is the upper half of a binary32 pattern.
+    o[0] = as_f32(a.x << 16);
+    o[1] = as_f32(a.x & 0xffff0000u);
+    o[2] = as_f32(a.y << 16);
+    o[3] = as_f32(a.y & 0xffff0000u);
+    o[4] = as_f32(a.z << 16);
+    o[5] = as_f32(a.z & 0xffff0000u);
+    o[6] = as_f32(a.w << 16);
+    o[7] = as_f32(a.w & 0xffff0000u);
+}
+
+template <> __device__ __forceinline__ void widen<F16>(uint4 a, float* o) {
+    const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        f16x2_t h = __builtin_bit_cast(f16x2_t, w[i]);
+        o[2 * i] = (float)h[0];
+        o[2 * i + 1] = (float)h[1];
+    }
+}
+
+template <> __device__ __forceinline__ void widen<F32>(uint4 a, float* o) {
+    o[0] = as_f32(a.x);
+    o[1] = as_f32(a.y);
+    o[2] = as_f32(a.z);
+    o[3] = as_f32(a.w);
+}
+
+// Store one fp32 value as element type E (round to nearest even).
+template <class E> __device__ __forceinline__ typename E::storage narrow(float x);
+template <> __device__ __forceinline__ float narrow<F32>(float x) { return x; }
+template <> __device__ __forceinline__ uint16_t narrow<BF16>(float x) {
+    return __builtin_bit_cast(uint16_t, (__bf16)x);
+}
+template <> __device__ __forceinline__ uint16_t narrow<F16>(float x) {
+    return __builtin_bit_cast(uint16_t, (_Float16)x);
+}
+
+// ---- cross-lane exchange ----------------------------------------------------------
+
+// DPP move of a float within a 16-lane row. CTRL: 0xB1 quad [1,0,3,2], 0x4E quad
+// [2,3,0,1], 0x141 half-row mirror, 0x140 row mirror, 0x124 / 0x128 row rotate by 4 / 8.
+template <int CTRL> __device__ __forceinline__ float dpp(float x) {
+    return as_f32((uint32_t)__builtin_amdgcn_update_dpp(0, (int)as_u32(x), CTRL, 0xF, 0xF, false));
+}
+
+// The values of lanes l and l^16 (order unspecified) via v_permlane16_swap.
+__device__ __forceinline__ void pair16(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(as_u32(x), as_u32(x), false, false);
+    a = as_f32(r[0]);
+    b = as_f32(r[1]);
+}
+// The values of lanes l and l^32 (order unspecified) via v_permlane32_swap.
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(as_u32(x), as_u32(x), false, false);
+    a = as_f32(r[0]);
+    b = as_f32(r[1]);
+}
+
+// Sum over the N consecutive lanes of an aligned group (N = 4, 8 or 16). Every
+// lane of the group ends with the same bits: each step adds two partial sums
+// that both lanes of a pair hold, and IEEE addition is commutative.
+template <int N> __device__ __forceinline__ float group_sum(float x) {
+    static_assert(N == 4 || N == 8 || N == 16, "group of 4, 8 or 16 lanes");
+    x += dpp<0xB1>(x);
+    x += dpp<0x4E>(x);
+    if constexpr (N >= 8) x += dpp<0x141>(x);
+    if constexpr (N >= 16) x += dpp<0x140>(x);
+    return x;
+}
+
+// Reduce over the lanes that share lane % N (N = 4, 8, 16 or 32): the result in
+// each lane covers all 64 / N lanes of its residue class. Every lane of a class
+// holds the same bits for MAX, and for sums when N >= 8; for N == 4 the two
+// row-rotate steps associate the four row partials differently per lane.
+template <int N, bool MAX> __device__ __forceinline__ float stride_reduce(float x) {
+    static_assert(N == 4 || N == 8 || N == 16 || N == 32, "stride of 4, 8, 16 or 32 lanes");
+    auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : a + b; };
+    if constexpr (N == 4) x = op(x, dpp<0x124>(x));   // + lane (l+4) mod 16 within the row
+    if constexpr (N <= 8) x = op(x, dpp<0x128>(x));   // + lane (l+8) mod 16 within the row
+    float a, b;
+    if constexpr (N <= 16) {
+        pair16(x, a, b);
+        x = op(a, b);
+    }
+    pair32(x, a, b);
+    return op(a, b);
+}
+
+}  // namespace pa

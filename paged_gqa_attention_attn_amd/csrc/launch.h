@@ -1,0 +1,54 @@
+// launch.h -- internal interface between the C-ABI host layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace pa {
+
+enum class Elem { F32 = 0, BF16 = 1, F16 = 2 };
+
+// Everything a decode launch needs; filled by the host plan in api.hip.
+struct DecodeArgs {
+    const void* q;               // [B][n_q][D]
+    const void* k_cache;         // [num_blocks][n_kv][16][D]
+    const void* v_cache;
+    const int32_t* block_table;  // [B][max_blocks]
+    const int32_t* context_lens; // [B]
+    void* out;                   // [B][n_q][D]
+    float* ws_m;                 // [B][n_q][nparts_max]      partition running max (log2 units)
+    float* ws_l;                 // [B][n_q][nparts_max]      partition softmax denominator
+    float* ws_acc;               // [B][n_q][nparts_max][D]   partition numerator
+    int32_t batch, n_q, n_kv, num_blocks, max_blocks;
+    int32_t group;               // G = n_q / n_kv
+    int32_t gw;                  // query heads per wave (template parameter of the kernel)
+    int32_t hs_wg;               // head slices (of gw heads) per workgroup
+    int32_t hsg;                 // head-slice groups per KV head (grid.y = n_kv * hsg)
+    int32_t waves_tok;           // waves that split the partition's blocks
+    int32_t blocks_per_wave;     // 16-token blocks one wave takes per partition
+    int32_t nparts_max;          // grid.x
+    float scale_log2;            // scale * log2(e)
+    int32_t out_f32;             // 1: fp32 output, 0: output in the input type
+};
+
+hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
+
+hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
+                            int32_t n_kv, int32_t row_bytes, int32_t block_size,
+                            int64_t num_slots, void* k_cache, void* v_cache, hipStream_t s);
+
+struct PrefillArgs {
+    const void* q;  // [B][S][n_q][D]
+    const void* k;  // [B][S][n_kv][D]
+    const void* v;
+    void* out;      // [B][S][n_q][D]
+    int32_t batch, seq_len, n_q, n_kv;
+    int32_t group;
+    int32_t causal;
+    float scale_log2;
+    int32_t out_f32;
+};
+
+hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);
+
+}  // namespace pa

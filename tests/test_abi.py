@@ -1,0 +1,153 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, and
+rejects bad arguments with the documented codes before any HIP call.
+
+Only error paths and pure host queries are called here: fake device pointers
+are never dereferenced because validation fails first.
+"""
+import ctypes
+import re
+from pathlib import Path
+
+import pytest
+
+from paged_gqa_attention_attn_amd import _lib
+
+HEADER = Path(__file__).resolve().parent.parent / "include" / "pagedattn.h"
+
+PA_OK, INVALID, UNSUPPORTED = _lib.PA_OK, _lib.PA_ERR_INVALID_ARG, _lib.PA_ERR_UNSUPPORTED
+FAKE = 1 << 20          # a 16-byte aligned fake device address (never dereferenced)
+MISALIGNED = FAKE + 8
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not _lib.LIB_PATH.exists():
+        pytest.skip("libpagedattn.so not built")
+    return _lib.load()
+
+
+def desc(nb=64, bs=16, n_kv=2, d=128, dtype=_lib.PA_BF16):
+    return ctypes.byref(_lib.CacheDesc(nb, bs, n_kv, d, dtype))
+
+
+def declared_functions():
+    text = HEADER.read_text()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_and_exports_agree(L):
+    names = declared_functions()
+    assert set(names) == set(_lib.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), f"{n} declared in the header but not exported"
+
+
+def test_version(L):
+    assert L.pa_version() == 100
+
+
+def decode(L, **kw):
+    a = dict(q=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
+             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_decode(a["q"], a["batch"], a["n_q"], a["k"], a["v"], a["cache"],
+                                  a["bt"], a["maxb"], a["ctx"], a["scale"], a["out"],
+                                  a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=None), INVALID, "descriptor"),
+    (dict(cache=desc(bs=8)), UNSUPPORTED, "block_size"),
+    (dict(cache=desc(d=96)), UNSUPPORTED, "head_dim"),
+    (dict(cache=desc(dtype=7)), UNSUPPORTED, "dtype"),
+    (dict(cache=desc(nb=0)), INVALID, "positive"),
+    (dict(n_q=7), INVALID, "multiple"),
+    (dict(n_q=0), INVALID, "n_q"),
+    (dict(batch=-1), INVALID, "batch"),
+    (dict(maxb=0), INVALID, "max_blocks"),
+    (dict(q=None), INVALID, "NULL"),
+    (dict(out=MISALIGNED), INVALID, "aligned"),
+    (dict(bt=FAKE + 2), INVALID, "aligned"),
+    (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+    (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(maxb=4096), INVALID, "workspace"),
+])
+def test_decode_rejects(L, kw, code, msg):
+    assert decode(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_decode_empty_batch_is_a_noop(L):
+    assert decode(L, batch=0) == PA_OK
+
+
+def test_workspace_query(L):
+    # A single partition needs no workspace; 2048-token contexts at the default
+    # 1024-token partitions need (m, l, acc) for 2 partitions of every head.
+    assert L.pa_decode_workspace_bytes(32, 32, 16, desc(nb=4096, n_kv=8)) == 0
+    n = L.pa_decode_workspace_bytes(32, 32, 128, desc(nb=4096, n_kv=8))
+    rows = 32 * 32 * 2
+    assert n == 2 * rows * 4 + rows * 128 * 4
+    assert L.pa_decode_workspace_bytes(2, 7, 4, desc()) == 0      # invalid: 7 % 2 != 0
+
+
+def test_partition_override(L):
+    assert L.pa_set_decode_partition_tokens(17) == -1
+    assert L.pa_set_decode_partition_tokens(-16) == -1
+    prev = L.pa_set_decode_partition_tokens(256)
+    try:
+        assert L.pa_decode_workspace_bytes(1, 8, 64, desc()) > 0    # 1024 tokens / 256
+    finally:
+        assert L.pa_set_decode_partition_tokens(prev) == 256
+
+
+def append(L, **kw):
+    a = dict(k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE, cache=desc(), stream=None)
+    a.update(kw)
+    return L.pa_kv_append(a["k"], a["v"], a["slots"], a["T"], a["kc"], a["vc"], a["cache"],
+                          a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(cache=None), INVALID),
+    (dict(cache=desc(bs=32)), UNSUPPORTED),
+    (dict(T=-1), INVALID),
+    (dict(v=None), INVALID),
+    (dict(kc=MISALIGNED), INVALID),
+    (dict(slots=FAKE + 4), INVALID),
+])
+def test_append_rejects(L, kw, code):
+    assert append(L, **kw) == code
+
+
+def test_append_zero_tokens_is_a_noop(L):
+    assert append(L, T=0) == PA_OK
+
+
+def prefill(L, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=_lib.PA_BF16, B=1, S=64, n_q=8, n_kv=2, d=128,
+             causal=1, scale=0.1, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["S"], a["n_q"],
+                                   a["n_kv"], a["d"], a["causal"], a["scale"], a["out"],
+                                   a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype=_lib.PA_F32), UNSUPPORTED),
+    (dict(d=80), UNSUPPORTED),
+    (dict(n_q=6, n_kv=4), INVALID),
+    (dict(causal=2), INVALID),
+    (dict(S=-1), INVALID),
+    (dict(out=None), INVALID),
+    (dict(k=MISALIGNED), INVALID),
+    (dict(out_dtype=_lib.PA_F16), UNSUPPORTED),
+])
+def test_prefill_rejects(L, kw, code):
+    assert prefill(L, **kw) == code
+
+
+def test_prefill_empty_is_a_noop(L):
+    assert prefill(L, S=0) == PA_OK
+    assert prefill(L, B=0) == PA_OK
