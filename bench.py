@@ -1,0 +1,315 @@
+#!/usr/bin/env python3
+"""Benchmark of the paged GQA attention hot path on one MI355X.
+
+Default workload (the headline metric): the LLaMA-3-8B-shaped decode step --
+B=32 sequences, n_q=32, n_kv=8, d=128, every context 2048 tokens, bf16 cache
+in 16-token blocks scattered by a seeded permutation. One step = kv_append of
+the 32 new tokens + paged decode attention over the 2048-token contexts.
+
+Other workloads (``--workload``): the 70B-shaped long-context decode
+(B=8, n_q=64, ctx 32768), the variable-length batch with a shared prefix, the
+tiny fp32 case, and the causal prefill + cache write + first decode step.
+
+Timing: ``--warmup`` untimed steps, then exactly ``--steps`` timed steps between
+two ``torch.cuda.synchronize()`` calls. Steps rotate over ``--sets``
+independent input sets so the 256 MB Infinity Cache cannot keep one step's
+K/V for the next. The dominant kernel call is also bracketed with HIP events
+recorded on the stream it is launched on; its average duration gives the
+roofline figure.
+
+Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import sys
+import time
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+
+WORKLOADS = {
+    "decode_8b": 2,
+    "decode_varlen": 3,
+    "decode_70b_longctx": 4,
+    "decode_tiny_fp32": 1,
+    "prefill_then_decode": 5,
+}
+
+
+def parse_args(argv=None):
+    p = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=10)
+    p.add_argument("--workload", choices=sorted(WORKLOADS), default="decode_8b")
+    p.add_argument("--sets", type=int, default=4, help="independent input sets rotated per step")
+    p.add_argument("--cpu-seconds", type=float, default=12.0,
+                   help="target CPU time of the oracle baseline sample (0 disables it)")
+    p.add_argument("--partition-tokens", type=int, default=0,
+                   help="decode partition size override (0: library default)")
+    return p.parse_args(argv)
+
+
+def _stored(t):
+    import numpy as np
+    import torch
+    t = t.detach().to("cpu").contiguous()
+    return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
+
+
+def cpu_baseline_decode(case, target_s: float):
+    """Time the CPU oracle on whole sequences of one input set (all heads)."""
+    import numpy as np
+
+    import oracle
+    from paged_gqa_attention_attn_amd import accounting as acc
+
+    kp, vp = _stored(case.k_pool), _stored(case.v_pool)
+    q = _stored(case.q)
+    bt = case.block_table.cpu().numpy()
+    ctx = case.context_lens.cpu().numpy()
+    elem = acc.ELEM_BYTES[case.dtype]
+
+    def run(seqs):
+        sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
+        t0 = time.perf_counter()
+        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel)
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    n = int(min(case.batch, max(1, math.ceil(target_s / max(t1, 1e-6)))))
+    seqs = list(range(n))
+    t_all = run(seqs)
+    reps = max(1, int(target_s / max(t_all, 1e-6))) if n == case.batch else 1
+    dt = t_all + sum(run(seqs) for _ in range(reps - 1))
+    kv = reps * acc.decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim, elem)
+    return {
+        "value": round(kv / dt / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle decode of {n} of {case.batch} sequences (all {case.n_q} query "
+                  f"heads), {reps} pass(es), {kv} KV bytes in {dt:.2f} s",
+    }
+
+
+def cpu_baseline_prefill(case, target_s: float):
+    """Time the CPU oracle on sampled causal prefill rows, scaled to TFLOP/s."""
+    import numpy as np
+
+    import oracle
+
+    q, k, v = _stored(case.q), _stored(case.k), _stored(case.v)
+    rng = np.random.default_rng(0)
+
+    def run(n):
+        rows = np.stack([rng.integers(0, case.batch, n), rng.integers(0, case.n_q, n),
+                         rng.integers(0, case.seq_len, n)], axis=1).astype(np.int32)
+        t0 = time.perf_counter()
+        oracle.prefill(q, k, v, case.dtype, True, case.scale, sel=rows)
+        dt = time.perf_counter() - t0
+        flops = float(4 * case.head_dim * (rows[:, 2].astype(np.int64) + 1).sum())
+        return dt, flops
+
+    dt, _ = run(64)
+    n = int(max(64, min(1 << 16, 64 * target_s / max(dt, 1e-6))))
+    dt, flops = run(n)
+    return {
+        "value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": oracle.max_threads(),
+        "kind": "oracle",
+        "sample": f"fp64 oracle causal prefill of {n} random (b, h, i) rows ({flops:.3e} FLOP) "
+                  f"in {dt:.2f} s",
+    }
+
+
+def bench_decode(args, cfg: int):
+    import torch
+
+    import paged_gqa_attention_attn_amd as pa
+    from paged_gqa_attention_attn_amd import accounting as acc
+    from paged_gqa_attention_attn_amd import workloads as wl
+
+    seed0 = wl.CONFIG_SEEDS[cfg]
+    sets = [wl.make_config(cfg, device="cuda", seed=seed0 + 1000 * i) for i in range(args.sets)]
+    c0 = sets[0]
+    if args.partition_tokens:
+        pa.set_decode_partition_tokens(args.partition_tokens)
+    elem = acc.ELEM_BYTES[c0.dtype]
+    out = torch.empty((c0.batch, c0.n_q, c0.head_dim), dtype=torch.float32, device="cuda")
+    ws_bytes = max(pa.decode_workspace_bytes(s.batch, s.n_q, s.max_blocks_per_seq, s.k_pool)
+                   for s in sets)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def step(i, ev=None):
+        s = sets[i % len(sets)]
+        pa.kv_append(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool)
+        if ev is not None:
+            ev[0].record()
+        pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
+                             out=out, workspace=ws)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms = (t1 - t0) * 1e3 / args.steps
+
+    # Event-timed pass of the decode call on the launch stream.
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+
+    kv = sum(acc.decode_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim, elem)
+             for s in sets) / len(sets)
+    io = acc.decode_io_bytes(c0.batch, c0.n_q, c0.head_dim, elem, 4, c0.max_blocks_per_seq)
+    achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
+    rec = {
+        "metric": "paged GQA decode attention: KV GB/s (% HBM peak) and µs/step at 1 GPU",
+        "value": round(kv / (ms * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": c0.dtype,
+        "data": "synthetic",
+        "config": {
+            "workload": c0.name, "batch": c0.batch, "n_q": c0.n_q, "n_kv": c0.n_kv,
+            "head_dim": c0.head_dim, "block_size": c0.block_size,
+            "context_lens": "2048 each" if cfg == 2 else
+            ("32768 each" if cfg == 4 else ("U[128,8192], 16 sharers of a 1024-token prefix"
+                                            if cfg == 3 else "{7, 33}")),
+            "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
+            "step": "kv_append of one new token per sequence + paged decode",
+        },
+        "roofline": {
+            "kernel": "paged_attn_decode (partition kernel, plus the log-sum-exp reduce "
+                      "kernel when the context is split)",
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
+        },
+    }
+    if cfg == 3:
+        uniq = sum(acc.decode_unique_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim,
+                                              elem, s.shared_prefix_blocks * 16, len(s.sharers))
+                   for s in sets) / len(sets)
+        rec["unique_kv_gbs"] = round(uniq / (ms * 1e-3) / 1e9, 2)
+    flops = acc.decode_flops(c0.context_lens.cpu().tolist(), c0.n_q, c0.head_dim)
+    rec["tflops"] = round(flops / (dec_ms * 1e-3) / 1e12, 3)
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_decode(c0, args.cpu_seconds)
+    return rec
+
+
+def bench_prefill(args):
+    import torch
+
+    import paged_gqa_attention_attn_amd as pa
+    from paged_gqa_attention_attn_amd import accounting as acc
+    from paged_gqa_attention_attn_amd import workloads as wl
+
+    n_sets = max(1, min(args.sets, 2))
+    sets = [wl.make_config(5, device="cuda", seed=wl.CONFIG_SEEDS[5] + 1000 * i)
+            for i in range(n_sets)]
+    c0 = sets[0]
+    out = torch.empty_like(c0.q, dtype=torch.float32)
+    dout = torch.empty((c0.batch, c0.n_q, c0.head_dim), dtype=torch.float32, device="cuda")
+    ws_bytes = pa.decode_workspace_bytes(c0.batch, c0.n_q, c0.block_table.shape[1], c0.k_pool)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    kf = [s.k.reshape(-1, s.n_kv, s.head_dim) for s in sets]
+    vf = [s.v.reshape(-1, s.n_kv, s.head_dim) for s in sets]
+
+    def step(i, ev=None):
+        s = sets[i % n_sets]
+        if ev is not None:
+            ev[0].record()
+        pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out)
+        if ev is not None:
+            ev[1].record()
+        pa.kv_append(kf[i % n_sets], vf[i % n_sets], s.prompt_slots, s.k_pool, s.v_pool)
+        pa.kv_append(s.new_k, s.new_v, s.new_slots, s.k_pool, s.v_pool)
+        pa.paged_attn_decode(s.q_new, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
+                             out=dout, workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    for i in range(args.steps):
+        step(i, evs[i])
+    torch.cuda.synchronize()
+    pre_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    flops = acc.prefill_flops_causal(c0.batch, c0.seq_len, c0.n_q, c0.head_dim)
+    achieved = flops / (pre_ms * 1e-3) / 1e12
+    rec = {
+        "metric": "causal prefill attention TFLOP/s (+ cache write and first decode step) at 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c0.dtype, "data": "synthetic",
+        "config": {
+            "workload": c0.name, "batch": c0.batch, "seq_len": c0.seq_len, "n_q": c0.n_q,
+            "n_kv": c0.n_kv, "head_dim": c0.head_dim, "causal": True,
+            "causal_flops": flops,
+            "full_square_flops": acc.prefill_flops_full_square(c0.batch, c0.seq_len, c0.n_q,
+                                                              c0.head_dim),
+            "step": "causal prefill + kv_append of the prompt + kv_append of one token + "
+                    "decode at context 4097",
+        },
+        "roofline": {
+            "kernel": "paged_attn_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+            "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
+        },
+    }
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_prefill(c0, args.cpu_seconds)
+    return rec
+
+
+def main(argv=None) -> int:
+    args = parse_args(argv)
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no "
+              "multi-GPU path; see DESIGN.md for how the decode step would shard.",
+              file=sys.stderr)
+        return 2
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    cfg = WORKLOADS[args.workload]
+    rec = bench_prefill(args) if cfg == 5 else bench_decode(args, cfg)
+    rec["device"] = torch.cuda.get_device_name(0)
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 
 #include "launch.h"
@@ -45,6 +46,16 @@ std::atomic<int32_t> g_partition_tokens{0};
 
 constexpr int kBlockSize = 16;
 constexpr int kMaxWaves = 8;
+constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+
+// Integer tuning knob from the environment (for sweeps), or `dflt`.
+int env_int(const char* name, int dflt) {
+    const char* v = std::getenv(name);
+    if (!v || !*v) return dflt;
+    char* end = nullptr;
+    const long x = std::strtol(v, &end, 10);
+    return (end && *end == 0) ? (int)x : dflt;
+}
 
 int check_cache(const pa_cache_desc* c) {
     if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
@@ -63,7 +74,7 @@ int check_cache(const pa_cache_desc* c) {
 // Decode launch plan; a pure function of the host arguments so that
 // pa_decode_workspace_bytes and pa_paged_attn_decode always agree.
 struct Plan {
-    int32_t gw, hs_wg, hsg, waves_tok, blocks_per_wave, nparts_max;
+    int32_t gw, hs_wg, hsg, waves_tok, blocks_per_wave, nparts_max, ring;
     size_t ws_floats_m, ws_floats_acc;  // floats in m (== l) and acc arrays
 };
 
@@ -73,13 +84,21 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     // registers for head_dim 128), else the largest power of two dividing G.
     const int32_t gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
+    // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
+    // (PA_DECODE_RING: 1 or 2); PA_DECODE_WAVES caps the workgroup size.
+    int32_t ring = env_int("PA_DECODE_RING", 1);
+    if (ring != 1 && ring != 2) ring = 1;
+    int32_t max_waves = env_int("PA_DECODE_WAVES", kMaxWaves);
+    if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
+    const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
+    while (max_waves > 1 && max_waves * ring * 2 * tile > kLdsBytes) --max_waves;
     int32_t hs_wg = 1;
-    for (int32_t d = kMaxWaves; d >= 1; --d)
+    for (int32_t d = max_waves; d >= 1; --d)
         if (hs % d == 0) {
             hs_wg = d;
             break;
         }
-    const int32_t waves_tok = kMaxWaves / hs_wg;
+    const int32_t waves_tok = max_waves / hs_wg;
     const int32_t unit = waves_tok * kBlockSize;  // tokens per pass of the workgroup
 
     int32_t tokens = g_partition_tokens.load();
@@ -99,6 +118,7 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     pl->waves_tok = waves_tok;
     pl->blocks_per_wave = bpw;
     pl->nparts_max = nparts_max < 1 ? 1 : nparts_max;
+    pl->ring = ring;
     if (pl->nparts_max > 1) {
         pl->ws_floats_m = (size_t)batch * n_q * pl->nparts_max;
         pl->ws_floats_acc = pl->ws_floats_m * (size_t)c->head_dim;
@@ -225,6 +245,7 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
     a.waves_tok = pl.waves_tok;
     a.blocks_per_wave = pl.blocks_per_wave;
     a.nparts_max = pl.nparts_max;
+    a.ring = pl.ring;
     a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
     a.out_f32 = out_dtype == PA_F32;
     const hipError_t e = pa::launch_decode(a, to_elem(cache->dtype), cache->head_dim,

@@ -12,6 +12,8 @@ namespace pa {
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // Element type tags: storage type and the dot product of two packed 16-byte chunks.
 struct F32 {
@@ -109,6 +111,45 @@ template <> __device__ __forceinline__ uint16_t narrow<F16>(float x) {
     return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
 
+// ---- LDS staging ---------------------------------------------------------------------
+//
+// global_load_lds_dwordx4 copies 16 bytes per lane from global memory straight
+// into LDS (lane l's bytes land at M0 + 16 * l) without passing through VGPRs.
+// The copy is issued from inline asm so the compiler's wait-count pass does not
+// see an LDS write behind a vector-memory counter: if it did, it would put a
+// full vmcnt(0) wait in front of every LDS read, draining a multi-block ring.
+// The caller therefore orders the ring by hand:
+//   wait_vmcnt<N>()  before reading a slot (copies complete in issue order),
+//   lds_reads_done() before a copy overwrites a slot that was just read.
+// Both, and the copy itself, clobber "memory", so the compiler keeps every
+// ordinary LDS load of the ring between them.
+
+// 32-bit LDS byte address of a pointer into __shared__ memory.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+    return (uint32_t)(uintptr_t)(const lds_char_t*)p;
+}
+
+// Asynchronous copy of 16 bytes per lane from `src` to LDS at lds_dst + 16 * lane.
+// lds_dst must be wave-uniform.
+__device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(src)
+        : "memory", "m0");
+}
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory");
+}
+
+// Wait until every LDS read issued so far has returned.
+__device__ __forceinline__ void lds_reads_done() { asm volatile("s_waitcnt lgkmcnt(0)" : : : "memory"); }
+
 // ---- cross-lane exchange ----------------------------------------------------------
 
 // DPP move of a float within a 16-lane row. CTRL: 0xB1 quad [1,0,3,2], 0x4E quad
@@ -159,5 +200,77 @@ template <int N, bool MAX> __device__ __forceinline__ float stride_reduce(float 
     pair32(x, a, b);
     return op(a, b);
 }
+
+// ---- reduce-scatter across lane bits ---------------------------------------------------
+//
+// Sum N values per lane over the lanes that differ in lane bits [LO, 6), leaving
+// each lane with N / 2^(6-LO) fully reduced values. Bits are reduced from bit 5
+// down; at each step a lane keeps the half of its values selected by its own
+// lane bit and adds its partner's copy of that half. Afterwards lane l holds
+// values j*M .. j*M + M - 1 (M = N / 2^(6-LO)), where j = l >> LO.
+//
+//   bit 5: v_permlane32_swap(x[k], x[k+H]) gives both halves in one exchange.
+//   bit 4: v_permlane16_swap, the same within each 32-lane half.
+//   bit 3: DPP row_ror:8 reads lane l^8 inside its 16-lane row.
+//   bit 2: ds_bpermute (lane l^4).
+template <int N, int BIT> __device__ __forceinline__ void rs_step(const float (&x)[N], float (&y)[N / 2],
+                                                                  int lane) {
+    constexpr int H = N / 2;
+    if constexpr (BIT == 5 || BIT == 4) {
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            auto r = BIT == 5 ? __builtin_amdgcn_permlane32_swap(as_u32(x[k]), as_u32(x[k + H]), false, false)
+                              : __builtin_amdgcn_permlane16_swap(as_u32(x[k]), as_u32(x[k + H]), false, false);
+            y[k] = as_f32(r[0]) + as_f32(r[1]);
+        }
+    } else {
+        const bool hi = (lane >> BIT) & 1;
+#pragma unroll
+        for (int k = 0; k < H; ++k) {
+            const float keep = hi ? x[k + H] : x[k];
+            const float send = hi ? x[k] : x[k + H];
+            float other;
+            if constexpr (BIT == 3)
+                other = dpp<0x128>(send);
+            else
+                other = __shfl_xor(send, 1 << BIT);
+            y[k] = keep + other;
+        }
+    }
+}
+
+template <int N, int LO> struct ReduceScatter {
+    static constexpr int M = N >> (6 - LO);
+    static __device__ __forceinline__ void run(const float (&x)[N], float (&out)[M], int lane) {
+        if constexpr (LO == 6) {
+#pragma unroll
+            for (int k = 0; k < N; ++k) out[k] = x[k];
+        } else {
+            float y5[N / 2];
+            rs_step<N, 5>(x, y5, lane);
+            if constexpr (LO == 5) {
+#pragma unroll
+                for (int k = 0; k < M; ++k) out[k] = y5[k];
+            } else {
+                float y4[N / 4];
+                rs_step<N / 2, 4>(y5, y4, lane);
+                if constexpr (LO == 4) {
+#pragma unroll
+                    for (int k = 0; k < M; ++k) out[k] = y4[k];
+                } else {
+                    float y3[N / 8];
+                    rs_step<N / 4, 3>(y4, y3, lane);
+                    if constexpr (LO == 3) {
+#pragma unroll
+                        for (int k = 0; k < M; ++k) out[k] = y3[k];
+                    } else {
+                        static_assert(LO == 2, "reduce over lane bits 2..5 at most");
+                        rs_step<N / 8, 2>(y3, out, lane);
+                    }
+                }
+            }
+        }
+    }
+};
 
 }  // namespace pa

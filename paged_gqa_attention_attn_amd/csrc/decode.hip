@@ -12,20 +12,21 @@
 // Work decomposition
 //  * grid = (partitions, n_kv * head-slice groups, batch). A partition is a
 //    run of consecutive logical blocks; its waves split it further.
-//  * A wave owns `gw` query heads and a contiguous run of blocks. Per 16-token
-//    block it loads the 4 KB K tile and the 4 KB V tile straight into
-//    registers (two 16-byte loads per lane per token it owns), with the next
-//    block's loads issued before the current block is computed.
-//  * Lane layout inside a block: lane = slot * LPT + c. The LPT lanes of a
-//    token slot each hold 16-byte chunks c and c + LPT of the token row, so
-//    every load instruction of the wave reads whole 16-byte-aligned
-//    half-rows. Scores come from packed dot products (v_dot2 for bf16/f16)
-//    and a DPP sum over the LPT lanes.
+//  * A wave owns `gw` query heads and a contiguous run of blocks. Each 16-token
+//    block's 4 KB K tile and 4 KB V tile (bf16, d = 128) are copied into the
+//    wave's own LDS ring with global_load_lds_dwordx4: every copy instruction
+//    moves one contiguous 1 KB run, and the copies cost no registers, so a
+//    wave keeps R blocks in flight while it computes on the current one.
+//  * Lane layout for compute: lane = slot * LPT + c. The LPT lanes of a token
+//    slot read 16-byte chunks c and c + LPT of the token row from LDS. Scores
+//    come from packed dot products (v_dot2 for bf16/f16) and a DPP sum over
+//    the LPT lanes.
 //  * Softmax runs online (running max m and denominator l per head, the
 //    Flash Attention statistics of the walk-through page's "工程优化怎么嵌进公式"
-//    section) in log2 units. The running max only moves when a block's max
-//    exceeds it by more than TAU, so the accumulator is rarely rescaled; the
-//    result is exact either way because acc, l and m stay consistent.
+//    section) in log2 units. The running max only moves when some score of
+//    the block exceeds it by more than TAU (a one-instruction ballot test), so
+//    the wave-wide max and the accumulator rescale are rare; the result is
+//    exact either way because acc, l and m stay consistent.
 //  * The waves of a workgroup combine through LDS; a workgroup that covers the
 //    whole context writes the output, otherwise it writes (m, l, acc) partials
 //    and the reduce kernel merges them with log-sum-exp weights (Flash
@@ -42,13 +43,14 @@ namespace {
 constexpr int BS = 16;         // tokens per cache block
 constexpr float TAU = 8.0f;    // rescale threshold (log2 units): p <= 2^TAU between rescales
 constexpr int MAX_WAVES = 8;   // waves per workgroup
+constexpr int MIN_WAVES_PER_SIMD = 3;  // register budget: at most 168 VGPRs per lane
 
 template <int D, int GW> struct WaveSlot {
     static constexpr int floats = GW * D + 2 * GW;   // acc[GW][D], m[GW], l[GW]
 };
 
-template <class E, int D, int GW>
-__global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const DecodeArgs p) {
+template <class E, int D, int GW, int R>
+__global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_partition_kernel(const DecodeArgs p) {
     using S = typename E::storage;
     constexpr int EB = (int)sizeof(S);
     constexpr int ROW = D * EB;            // bytes per token row
@@ -58,10 +60,17 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
     constexpr int EPC = 16 / EB;           // elements per chunk
     constexpr int EPL = 2 * EPC;           // elements per lane per token
     constexpr int SLOT = WaveSlot<D, GW>::floats;
+    constexpr int TILE = BS * ROW;         // bytes of one (block, KV head) K or V tile
+    constexpr int NQ = TILE / 1024;        // 1 KB wave copies per tile
+    constexpr int OPS = 2 * NQ;            // vector-memory operations per block (K and V)
+    constexpr int RING = R * 2 * TILE;     // bytes of this wave's LDS ring
     static_assert(LPT == 4 || LPT == 8 || LPT == 16, "row must split into 4, 8 or 16 lanes");
     static_assert(NT >= 1 && NT * TPP == BS, "block must split evenly over token slots");
+    static_assert(TILE % 1024 == 0, "tiles move in whole 1 KB wave copies");
+    static_assert(OPS * (R - 1) < 64, "outstanding copies must fit the vmcnt counter");
+    static_assert(SLOT * 4 <= RING, "the merge slot reuses the wave's ring");
 
-    extern __shared__ float smem[];
+    extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int part = blockIdx.x;
     const int g = blockIdx.y / p.hsg;
@@ -77,7 +86,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
     // Context of this sequence. A length past the block table's reach cannot be
     // served without reading out of bounds: that sequence's rows become NaN.
     const int cap = p.max_blocks * BS;
-    const int ctx_in = p.context_lens[b];
+    const int ctx_in = __builtin_amdgcn_readfirstlane(p.context_lens[b]);
     const bool ctx_bad = ctx_in > cap;
     const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
@@ -90,11 +99,6 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
     const int hwg0 = g * p.group + hsgi * p.hs_wg * GW;  // first query head of the workgroup
     const int h0 = hwg0 + hs * GW;                        // first query head of this wave
 
-    // Lane k holds the physical id of logical block blk0 + k.
-    int my_phys = 0;
-    if (lane < nb) my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
-    const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
-
     uint4 qv[GW][2];
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
@@ -103,6 +107,11 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
         qv[hh][0] = qrow[c];
         qv[hh][1] = qrow[c + LPT];
     }
+
+    // Lane k holds the physical id of logical block blk0 + k.
+    int my_phys = 0;
+    if (lane < nb) my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
+    const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
     float m_run[GW], l_run[GW], acc[GW][EPL];
 #pragma unroll
@@ -113,31 +122,57 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
         for (int e = 0; e < EPL; ++e) acc[hh][e] = 0.f;
     }
 
-    const char* kbase = (const char*)p.k_cache;
-    const char* vbase = (const char*)p.v_cache;
-    const int64_t tile_bytes = (int64_t)BS * ROW;              // one (block, KV head) tile
-    const int64_t block_bytes = (int64_t)p.n_kv * tile_bytes;
-    const int64_t off0 = (int64_t)slot * ROW + c * 16;          // chunk c of token `slot`
-    const int64_t off1 = off0 + LPT * 16;                       // chunk c + LPT
+    char* ring = smem + wave * RING;
+    const int64_t block_bytes = (int64_t)p.n_kv * TILE;
+    const char* ksrc = (const char*)p.k_cache + (int64_t)g * TILE + lane * 16;
+    const char* vsrc = (const char*)p.v_cache + (int64_t)g * TILE + lane * 16;
+    const uint32_t off0 = slot * ROW + c * 16;          // chunk c of token `slot`
+    const uint32_t off1 = off0 + LPT * 16;              // chunk c + LPT
+
+    // Copy block i's K and V tiles into ring slot i % R (8 KB for bf16, d = 128).
+    const uint32_t ring_lds = lds_addr(ring);
+    auto issue = [&](int i) {
+        const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
+        const uint32_t dst = ring_lds + (i % R) * 2 * TILE;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(ksrc + phys * block_bytes + qq * 1024, dst + qq * 1024);
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq)
+            copy_to_lds16(vsrc + phys * block_bytes + qq * 1024, dst + TILE + qq * 1024);
+    };
+
+    // q and the block ids have landed before the ring copies start, so the
+    // compiler never needs a full vmcnt(0) wait (which would drain the ring)
+    // to reach them inside the loop.
+    wait_vmcnt<0>();
 
     if (!phys_bad && nb > 0) {
-        uint4 kc[NT][2], vc[NT][2], kn[NT][2], vn[NT][2];
-        auto load = [&](int i, uint4 (&kr)[NT][2], uint4 (&vr)[NT][2]) {
-            const int phys = __builtin_amdgcn_readlane(my_phys, i);
-            const int64_t tile = (int64_t)phys * block_bytes + (int64_t)g * tile_bytes;
+        const int pre = min(R, nb);
+        for (int i = 0; i < pre; ++i) issue(i);
+        for (int i = 0; i < nb; ++i) {
+            // Block i has landed once at most (blocks issued after it) * OPS copies are pending.
+            const int ahead = min(R - 1, nb - 1 - i);
+            if constexpr (R >= 4) {
+                if (ahead >= 3) wait_vmcnt<3 * OPS>();
+            }
+            if constexpr (R >= 3) {
+                if (ahead == 2) wait_vmcnt<2 * OPS>();
+            }
+            if (ahead == 1) wait_vmcnt<OPS>();
+            if (ahead == 0) wait_vmcnt<0>();
+
+            const char* base = ring + (i % R) * 2 * TILE;
+            uint4 kc[NT][2], vc[NT][2];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
-                const int64_t o = tile + (int64_t)t * TPP * ROW;
-                kr[t][0] = *reinterpret_cast<const uint4*>(kbase + o + off0);
-                kr[t][1] = *reinterpret_cast<const uint4*>(kbase + o + off1);
-                vr[t][0] = *reinterpret_cast<const uint4*>(vbase + o + off0);
-                vr[t][1] = *reinterpret_cast<const uint4*>(vbase + o + off1);
+                kc[t][0] = *reinterpret_cast<const uint4*>(base + t * TPP * ROW + off0);
+                kc[t][1] = *reinterpret_cast<const uint4*>(base + t * TPP * ROW + off1);
+                vc[t][0] = *reinterpret_cast<const uint4*>(base + TILE + t * TPP * ROW + off0);
+                vc[t][1] = *reinterpret_cast<const uint4*>(base + TILE + t * TPP * ROW + off1);
             }
-        };
-
-        load(0, kc, vc);
-        for (int i = 0; i < nb; ++i) {
-            if (i + 1 < nb) load(i + 1, kn, vn);
+            lds_reads_done();
+            // The slot is free again: start the copy R blocks ahead.
+            if (i + R < nb) issue(i + R);
 
             const int pos0 = (blk0 + i) * BS;
             float s[GW][NT];
@@ -174,8 +209,10 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
                 float bm = s[hh][0];
 #pragma unroll
                 for (int t = 1; t < NT; ++t) bm = fmaxf(bm, s[hh][t]);
-                bm = stride_reduce<LPT, true>(bm);
-                if (bm > m_run[hh] + TAU) {  // wave-uniform
+                // The running max moves only when some score in the wave passes it by
+                // more than TAU (log2 units); the wave-wide max is taken only then.
+                if (__any(bm > m_run[hh] + TAU)) {
+                    bm = stride_reduce<LPT, true>(bm);
                     const float alpha = __builtin_amdgcn_exp2f(m_run[hh] - bm);
                     l_run[hh] *= alpha;
 #pragma unroll
@@ -190,34 +227,34 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
                     for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[t][e], acc[hh][e]);
                 }
             }
-
-#pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                kc[t][0] = kn[t][0];
-                kc[t][1] = kn[t][1];
-                vc[t][0] = vn[t][0];
-                vc[t][1] = vn[t][1];
-            }
         }
     }
 
-    // Sum l and acc over the wave's token slots; lanes of slot 0 publish to LDS.
+    // Sum l over the wave's token slots, and reduce-scatter acc over them: each
+    // lane ends with M fully summed values (head, dimension pairs) to publish.
+    constexpr int LOG_LPT = LPT == 4 ? 2 : LPT == 8 ? 3 : 4;
+    constexpr int NV = GW * EPL;
+    using RS = ReduceScatter<NV, LOG_LPT>;
+    constexpr int M = RS::M;
+    static_assert(M >= 1, "at least one value per lane after the reduce-scatter");
 #pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-        l_run[hh] = stride_reduce<LPT, false>(l_run[hh]);
+    for (int hh = 0; hh < GW; ++hh) l_run[hh] = stride_reduce<LPT, false>(l_run[hh]);
+    float flat[NV];
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) acc[hh][e] = stride_reduce<LPT, false>(acc[hh][e]);
-    }
-    float* mine = smem + wave * SLOT;
-    if (lane < LPT) {
+    for (int hh = 0; hh < GW; ++hh)
 #pragma unroll
-        for (int hh = 0; hh < GW; ++hh) {
+        for (int e = 0; e < EPL; ++e) flat[hh * EPL + e] = acc[hh][e];
+    float mine_vals[M];
+    RS::run(flat, mine_vals, lane);
+
+    float* mine = reinterpret_cast<float*>(smem + wave * RING);
 #pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                mine[hh * D + c * EPC + e] = acc[hh][e];
-                mine[hh * D + (c + LPT) * EPC + e] = acc[hh][EPC + e];
-            }
-        }
+    for (int k = 0; k < M; ++k) {
+        const int kg = slot * M + k;       // index into flat[]
+        const int hh = kg / EPL;
+        const int e = kg % EPL;
+        const int dim = e < EPC ? c * EPC + e : D / 2 + c * EPC + (e - EPC);
+        mine[hh * D + dim] = mine_vals[k];
     }
     if (lane == 0) {
 #pragma unroll
@@ -236,12 +273,14 @@ __global__ __launch_bounds__(64 * MAX_WAVES) void decode_partition_kernel(const 
         const int hsl = hl / GW;
         const int hh = hl % GW;
         float M = -INFINITY;
+        const float* slots = reinterpret_cast<const float*>(smem);
+        constexpr int RING_F = RING / 4;
         for (int w = 0; w < p.waves_tok; ++w)
-            M = fmaxf(M, smem[(w * p.hs_wg + hsl) * SLOT + GW * D + hh]);
+            M = fmaxf(M, slots[(w * p.hs_wg + hsl) * RING_F + GW * D + hh]);
         float L = 0.f, A = 0.f;
         if (M != -INFINITY) {
             for (int w = 0; w < p.waves_tok; ++w) {
-                const float* ws = smem + (w * p.hs_wg + hsl) * SLOT;
+                const float* ws = slots + (w * p.hs_wg + hsl) * RING_F;
                 const float f = __builtin_amdgcn_exp2f(ws[GW * D + hh] - M);
                 L = fmaf(f, ws[GW * D + GW + hh], L);
                 A = fmaf(f, ws[hh * D + e], A);
@@ -304,30 +343,43 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs p) {
         reinterpret_cast<S*>(p.out)[row * D + e] = narrow<E>(o);
 }
 
-template <class E, int D, int GW> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+template <class E, int D, int GW, int R> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
     const int waves = a.hs_wg * a.waves_tok;
     const dim3 grid(a.nparts_max, a.n_kv * a.hsg, a.batch);
-    const size_t lds = (size_t)waves * WaveSlot<D, GW>::floats * sizeof(float);
-    hipLaunchKernelGGL((decode_partition_kernel<E, D, GW>), grid, dim3(64 * waves), lds, s, a);
+    const size_t lds = (size_t)waves * R * 2 * BS * D * sizeof(typename E::storage);
+    static bool lds_opt_in = [] {
+        return hipFuncSetAttribute(reinterpret_cast<const void*>(&decode_partition_kernel<E, D, GW, R>),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
+    }();
+    (void)lds_opt_in;
+    hipLaunchKernelGGL((decode_partition_kernel<E, D, GW, R>), grid, dim3(64 * waves), lds, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.nparts_max <= 1) return err;
     hipLaunchKernelGGL((decode_reduce_kernel<E, D>), dim3(a.n_q, a.batch), dim3(D), 0, s, a);
     return hipGetLastError();
 }
 
-template <class E, int D> hipError_t launch_gw(const DecodeArgs& a, hipStream_t s) {
+template <class E, int D, int R> hipError_t launch_gw(const DecodeArgs& a, hipStream_t s) {
     switch (a.gw) {
-    case 1: return launch_typed<E, D, 1>(a, s);
-    case 2: return launch_typed<E, D, 2>(a, s);
-    case 4: return launch_typed<E, D, 4>(a, s);
+    case 1: return launch_typed<E, D, 1, R>(a, s);
+    case 2: return launch_typed<E, D, 2, R>(a, s);
+    case 4: return launch_typed<E, D, 4, R>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class E, int D> hipError_t launch_ring(const DecodeArgs& a, hipStream_t s) {
+    switch (a.ring) {
+    case 1: return launch_gw<E, D, 1>(a, s);
+    case 2: return launch_gw<E, D, 2>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
 template <class E> hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t s) {
     switch (head_dim) {
-    case 64: return launch_gw<E, 64>(a, s);
-    case 128: return launch_gw<E, 128>(a, s);
+    case 64: return launch_ring<E, 64>(a, s);
+    case 128: return launch_ring<E, 128>(a, s);
     default: return hipErrorInvalidValue;
     }
 }

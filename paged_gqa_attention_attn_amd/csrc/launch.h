@@ -27,6 +27,7 @@ struct DecodeArgs {
     int32_t waves_tok;           // waves that split the partition's blocks
     int32_t blocks_per_wave;     // 16-token blocks one wave takes per partition
     int32_t nparts_max;          // grid.x
+    int32_t ring;                // blocks in flight per wave (LDS ring depth: 1 or 2)
     float scale_log2;            // scale * log2(e)
     int32_t out_f32;             // 1: fp32 output, 0: output in the input type
 };
