@@ -1,0 +1,135 @@
+"""GPU parity of the MFMA prefill kernel, and the prefill -> cache write -> decode flow.
+
+Prefill outputs are compared with the fp64 oracle row by row (every row for
+small shapes, sampled rows at the 2 x 4096 prompt size) within max-abs 2e-3
+and norm-wise relative 1e-2.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_parity, same_bits, say, stored_np
+from paged_gqa_attention_attn_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_gqa_attention_attn_amd as pa
+    pa._lib.load()
+    return pa
+
+
+def _inputs(B, S, n_q, n_kv, d, dtype, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    t = wl.TORCH_DTYPES[dtype]
+    q = torch.randn(B, S, n_q, d, generator=g, device="cuda").to(t)
+    k = torch.randn(B, S, n_kv, d, generator=g, device="cuda").to(t)
+    v = torch.randn(B, S, n_kv, d, generator=g, device="cuda").to(t)
+    return q, k, v
+
+
+SHAPES = {
+    # name: (B, S, n_q, n_kv, d, dtype, causal)
+    "gqa4_bf16_ragged_causal": (2, 200, 8, 2, 128, "bf16", True),
+    "gqa4_bf16_ragged_full": (2, 200, 8, 2, 128, "bf16", False),
+    "one_token": (1, 1, 4, 2, 128, "bf16", True),
+    "exact_tile": (1, 128, 4, 1, 128, "bf16", True),
+    "tile_plus_one": (1, 129, 4, 4, 128, "bf16", True),
+    "mqa_bf16": (1, 300, 8, 1, 128, "bf16", True),
+    "mha_f16": (2, 97, 2, 2, 128, "f16", True),
+    "d64_bf16": (2, 150, 4, 2, 64, "bf16", True),
+    "d64_f16_full": (1, 70, 4, 2, 64, "f16", False),
+    "long_causal": (1, 1000, 4, 2, 128, "bf16", True),
+}
+
+
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_prefill_all_rows(pa, name):
+    B, S, n_q, n_kv, d, dt, causal = SHAPES[name]
+    say(f"[prefill] {name}: B={B} S={S} n_q={n_q} n_kv={n_kv} d={d} {dt} causal={causal}")
+    q, k, v = _inputs(B, S, n_q, n_kv, d, dt, seed=len(name) * 31 + S)
+    scale = d ** -0.5
+    out = pa.paged_attn_prefill(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    want = oracle.prefill(stored_np(q), stored_np(k), stored_np(v), dt, causal, scale)
+    stats = assert_parity(out.cpu().numpy(), want, dt, name)
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+def test_prefill_bf16_output(pa):
+    q, k, v = _inputs(1, 150, 4, 2, 128, "bf16", seed=3)
+    out = pa.paged_attn_prefill(q, k, v, True, 128 ** -0.5, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    want = oracle.prefill(stored_np(q), stored_np(k), stored_np(v), "bf16", True, 128 ** -0.5)
+    err = np.abs(out.float().cpu().numpy() - want)
+    assert (err <= 2e-3 + 2.0**-8 * np.abs(want)).all(), float(err.max())
+
+
+def test_prefill_run_twice_bitwise(pa):
+    q, k, v = _inputs(2, 333, 8, 2, 128, "bf16", seed=4)
+    a = pa.paged_attn_prefill(q, k, v, True, 0.09)
+    b = pa.paged_attn_prefill(q, k, v, True, 0.09)
+    torch.cuda.synchronize()
+    assert same_bits(a, b)
+
+
+def test_prefill_row_matches_gpu_decode(pa):
+    """Causal prefill row i equals decode over positions <= i, both on the GPU."""
+    case = wl.make_prefill_case(batch=1, seq_len=300, n_q=8, n_kv=2, head_dim=128, seed=8,
+                                device="cuda")
+    pre = pa.paged_attn_prefill(case.q, case.k, case.v, True, case.scale)
+    kp, vp = case.k_pool.clone(), case.v_pool.clone()
+    pa.kv_append(case.k.reshape(-1, 2, 128), case.v.reshape(-1, 2, 128), case.prompt_slots, kp, vp)
+    for i in (0, 1, 63, 64, 150, 299):
+        dec = pa.paged_attn_decode(case.q[:, i].contiguous(), kp, vp, case.block_table,
+                                   torch.tensor([i + 1], dtype=torch.int32, device="cuda"),
+                                   case.scale)
+        torch.cuda.synchronize()
+        assert_parity(pre[:, i].cpu().numpy(), dec.cpu().numpy(), "bf16", f"row {i}",
+                      tol=(2e-3, 1e-2))
+
+
+def test_config5_prefill_append_decode(pa):
+    case = wl.make_config(5, device="cuda")
+    B, S, n_q, n_kv, d = case.batch, case.seq_len, case.n_q, case.n_kv, case.head_dim
+    say(f"[config5] prefill B={B} S={S} n_q={n_q} n_kv={n_kv}")
+    out = pa.paged_attn_prefill(case.q, case.k, case.v, True, case.scale)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(55)
+    rows = []
+    for b in range(B):
+        for h in range(n_q):
+            for i in sorted({0, 1, 2, 3, 17, 63, 64, 127, 128, 2047, S - 1,
+                             *rng.integers(0, S, 3).tolist()}):
+                rows.append((b, h, i))
+    sel = np.asarray(rows, np.int32)
+    want = oracle.prefill(stored_np(case.q), stored_np(case.k), stored_np(case.v), "bf16", True,
+                          case.scale, sel=sel)
+    got = out.cpu().numpy()[sel[:, 0], sel[:, 2], sel[:, 1]]
+    stats = assert_parity(got, want, "bf16", f"config5 prefill ({len(sel)} sampled rows)")
+    assert torch.isfinite(out).all()
+    say(f"    prefill sampled rows={len(sel)} max_abs={stats['max_abs']:.2e}")
+
+    # Cache write of the whole prompt, then of the first generated token.
+    kp, vp = case.k_pool.clone(), case.v_pool.clone()
+    kf = case.k.reshape(B * S, n_kv, d)
+    vf = case.v.reshape(B * S, n_kv, d)
+    pa.kv_append(kf, vf, case.prompt_slots, kp, vp)
+    pa.kv_append(case.new_k, case.new_v, case.new_slots, kp, vp)
+    dec = pa.paged_attn_decode(case.q_new, kp, vp, case.block_table, case.context_lens, case.scale)
+    torch.cuda.synchronize()
+    okp, ovp = stored_np(case.k_pool).copy(), stored_np(case.v_pool).copy()
+    oracle.kv_append(stored_np(kf), stored_np(vf), case.prompt_slots.cpu().numpy(), okp, ovp)
+    oracle.kv_append(stored_np(case.new_k), stored_np(case.new_v), case.new_slots.cpu().numpy(),
+                     okp, ovp)
+    assert same_bits(kp.cpu(), torch.from_numpy(okp).view(kp.dtype))
+    assert same_bits(vp.cpu(), torch.from_numpy(ovp).view(vp.dtype))
+    wd = oracle.decode(stored_np(case.q_new), okp, ovp, "bf16", case.block_table.cpu().numpy(),
+                       case.context_lens.cpu().numpy(), case.scale)
+    stats = assert_parity(dec.cpu().numpy(), wd, "bf16", "config5 decode at context 4097")
+    say(f"    decode ctx={S + 1} max_abs={stats['max_abs']:.2e}")
