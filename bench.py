@@ -22,10 +22,12 @@ Prints one JSON line.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import sys
 import time
+from pathlib import Path
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
@@ -36,7 +38,35 @@ WORKLOADS = {
     "decode_70b_longctx": 4,
     "decode_tiny_fp32": 1,
     "prefill_then_decode": 5,
+    "copy_calibration": 0,
 }
+
+ROOT = Path(__file__).resolve().parent
+CSRC = ROOT / "paged_gqa_attention_attn_amd" / "csrc"
+# Sources that determine each profiled kernel's code (their hash dates a counter summary).
+KERNEL_SOURCES = {
+    "decode": ["decode.hip", "common.h", "launch.h", "api.hip"],
+    "prefill": ["prefill.hip", "common.h", "launch.h", "api.hip"],
+}
+
+
+def source_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[kind]:
+        h.update((CSRC / name).read_bytes())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source; otherwise None."""
+    f = ROOT / "profiles" / f"{workload}_traffic.json"
+    if not f.exists():
+        return None
+    rec = json.loads(f.read_text())
+    if rec.get("source_hash") != source_hash(kind):
+        return None
+    return rec.get("hbm_bytes_per_launch")
 
 
 def parse_args(argv=None):
@@ -202,8 +232,10 @@ def bench_decode(args, cfg: int):
             "kernel": "paged_attn_decode (partition kernel, plus the log-sum-exp reduce "
                       "kernel when the context is split)",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": measured_traffic("decode", args.workload),
             "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
+            "source_hash": source_hash("decode"),
         },
     }
     if cfg == 3:
@@ -284,13 +316,38 @@ def bench_prefill(args):
         "roofline": {
             "kernel": "paged_attn_prefill", "bound": "mfma", "achieved": round(achieved, 2),
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+            "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("prefill", args.workload),
             "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
+            "source_hash": source_hash("prefill"),
         },
     }
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_prefill(c0, args.cpu_seconds)
     return rec
+
+
+def bench_copy(args):
+    """A plain device copy of a known size: the reference that scales the
+    FETCH_SIZE / WRITE_SIZE counters to bytes."""
+    import torch
+    n = 64 * 2**20                      # 64 Mi fp32 = 256 MiB each way
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(args.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    return {"metric": "plain device copy (counter calibration)", "value": round(2 * 4 * n / ms / 1e6, 1),
+            "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+            "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+            "config": {"workload": "copy_256MiB", "bytes_read_per_launch": 4 * n,
+                       "bytes_written_per_launch": 4 * n}}
 
 
 def main(argv=None) -> int:
@@ -305,7 +362,10 @@ def main(argv=None) -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
     cfg = WORKLOADS[args.workload]
-    rec = bench_prefill(args) if cfg == 5 else bench_decode(args, cfg)
+    if cfg == 0:
+        rec = bench_copy(args)
+    else:
+        rec = bench_prefill(args) if cfg == 5 else bench_decode(args, cfg)
     rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
     return 0

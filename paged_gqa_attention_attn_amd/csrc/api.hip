@@ -47,6 +47,7 @@ std::atomic<int32_t> g_partition_tokens{0};
 constexpr int kBlockSize = 16;
 constexpr int kMaxWaves = 8;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
+constexpr int kComputeUnits = 256;     // MI355X
 
 // Integer tuning knob from the environment (for sweeps), or `dflt`.
 int env_int(const char* name, int dflt) {
@@ -85,10 +86,14 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     const int32_t gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
     // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
-    // (PA_DECODE_RING: 1 or 2); PA_DECODE_WAVES caps the workgroup size.
+    // (PA_DECODE_RING: 1 or 2). Workgroup size: 8 waves when there are at least
+    // as many (sequence, KV head, head slice) units as compute units, else 4 so
+    // that long contexts split into more, smaller workgroups (PA_DECODE_WAVES
+    // overrides). Measured on MI355X with the 8B- and 70B-shaped workloads.
     int32_t ring = env_int("PA_DECODE_RING", 1);
     if (ring != 1 && ring != 2) ring = 1;
-    int32_t max_waves = env_int("PA_DECODE_WAVES", kMaxWaves);
+    const int64_t units = (int64_t)batch * c->n_kv * (G / gw);
+    int32_t max_waves = env_int("PA_DECODE_WAVES", units >= kComputeUnits ? kMaxWaves : 4);
     if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
     while (max_waves > 1 && max_waves * ring * 2 * tile > kLdsBytes) --max_waves;
@@ -101,11 +106,9 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     const int32_t waves_tok = max_waves / hs_wg;
     const int32_t unit = waves_tok * kBlockSize;  // tokens per pass of the workgroup
 
+    // Partition size: 2048 tokens unless overridden.
     int32_t tokens = g_partition_tokens.load();
-    if (tokens <= 0) {
-        // Built-in choice: 1024-token partitions (8 blocks per wave at 8 token-waves).
-        tokens = 1024;
-    }
+    if (tokens <= 0) tokens = 2048;
     int32_t bpw = tokens / unit;
     if (bpw < 1) bpw = 1;
     if (bpw > 64) bpw = 64;

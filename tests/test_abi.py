@@ -71,7 +71,7 @@ def decode(L, **kw):
     (dict(bt=FAKE + 2), INVALID, "aligned"),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
     (dict(scale=float("nan")), INVALID, "scale"),
-    (dict(maxb=4096), INVALID, "workspace"),
+    (dict(maxb=8192), INVALID, "workspace"),
 ])
 def test_decode_rejects(L, kw, code, msg):
     assert decode(L, **kw) == code
@@ -83,10 +83,11 @@ def test_decode_empty_batch_is_a_noop(L):
 
 
 def test_workspace_query(L):
-    # A single partition needs no workspace; 2048-token contexts at the default
-    # 1024-token partitions need (m, l, acc) for 2 partitions of every head.
-    assert L.pa_decode_workspace_bytes(32, 32, 16, desc(nb=4096, n_kv=8)) == 0
-    n = L.pa_decode_workspace_bytes(32, 32, 128, desc(nb=4096, n_kv=8))
+    # One partition per (sequence, KV head) needs no workspace; 4096-token
+    # contexts at the default 2048-token partitions need (m, l, acc) for 2
+    # partitions of every query head.
+    assert L.pa_decode_workspace_bytes(32, 32, 128, desc(nb=4096, n_kv=8)) == 0
+    n = L.pa_decode_workspace_bytes(32, 32, 256, desc(nb=8192, n_kv=8))
     rows = 32 * 32 * 2
     assert n == 2 * rows * 4 + rows * 128 * 4
     assert L.pa_decode_workspace_bytes(2, 7, 4, desc()) == 0      # invalid: 7 % 2 != 0
