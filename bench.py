@@ -80,6 +80,8 @@ def parse_args(argv=None):
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--partition-tokens", type=int, default=0,
                    help="decode partition size override (0: library default)")
+    p.add_argument("--unfused", action="store_true",
+                   help="decode step as two launches (kv_append, then decode) instead of one")
     return p.parse_args(argv)
 
 
@@ -173,11 +175,17 @@ def bench_decode(args, cfg: int):
 
     def step(i, ev=None):
         s = sets[i % len(sets)]
-        pa.kv_append(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool)
+        if args.unfused:
+            pa.kv_append(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool)
         if ev is not None:
             ev[0].record()
-        pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
-                             out=out, workspace=ws)
+        if args.unfused:
+            pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
+                                 out=out, workspace=ws)
+        else:
+            pa.paged_attn_decode_append(s.q, s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool,
+                                        s.block_table, s.context_lens, s.scale, out=out,
+                                        workspace=ws)
         if ev is not None:
             ev[1].record()
 
@@ -226,11 +234,13 @@ def bench_decode(args, cfg: int):
             ("32768 each" if cfg == 4 else ("U[128,8192], 16 sharers of a 1024-token prefix"
                                             if cfg == 3 else "{7, 33}")),
             "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
-            "step": "kv_append of one new token per sequence + paged decode",
+            "step": ("kv_append of one new token per sequence, then paged decode (two launches)"
+                     if args.unfused else
+                     "one launch: append of one new token per sequence + paged decode"),
         },
         "roofline": {
-            "kernel": "paged_attn_decode (partition kernel, plus the log-sum-exp reduce "
-                      "kernel when the context is split)",
+            "kernel": "decode partition kernel (with the fused append unless --unfused), plus "
+                      "the log-sum-exp reduce kernel when a context is split",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode", args.workload),

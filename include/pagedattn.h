@@ -123,6 +123,33 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
                          void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_append -- one decode step in a single launch: kv_append of
+ * one new token per sequence followed by paged_attn_decode. [IW] "Decode 阶段维度
+ * 流转": write the new K/V at position cache_len, increment it, then attend over
+ * the whole cache.
+ *
+ *   k_new, v_new  [batch][n_kv][head_dim] in cache->dtype: the new token of each sequence
+ *   slot_mapping  int64 [batch]: its slot (negative: sequence b appends nothing)
+ *   other arguments as for pa_paged_attn_decode; workspace size as reported by
+ *   pa_decode_workspace_bytes for the same arguments.
+ * The new token must sit at position context_lens[b] - 1, i.e. slot_mapping[b]
+ * must be the slot that sequence b's block table gives that position, and no
+ * other sequence may attend to that slot in the same call (the engine's
+ * copy-on-write rule for shared blocks). The attention then uses k_new/v_new at
+ * that position and every output bit equals the two-call sequence
+ * pa_kv_append + pa_paged_attn_decode. Otherwise the cache write still lands at
+ * slot_mapping[b] (or is skipped if out of range) but the attention result is
+ * unspecified; no access goes out of bounds.
+ */
+int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int32_t batch, int32_t n_q,
+                                void* k_cache, void* v_cache, const pa_cache_desc* cache,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, float scale, void* out,
+                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+/*
  * paged_attn_prefill -- attention of a whole prompt over itself.
  * [AE] 1.1 / [PD] section 2: A = softmax(Q K^T / sqrt(d) + M), O = A V with the
  * causal mask M_ij = 0 for j <= i and -inf otherwise; [AE] 3.1 GQA grouping;

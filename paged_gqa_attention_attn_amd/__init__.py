@@ -23,7 +23,8 @@ import torch
 from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
-__all__ = ["kv_append", "paged_attn_decode", "paged_attn_prefill", "decode_workspace_bytes",
+__all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
+           "decode_workspace_bytes",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
 _DTYPE = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -132,6 +133,49 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
         _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                             v_cache: torch.Tensor, block_table: torch.Tensor,
+                             context_lens: torch.Tensor, scale: float,
+                             out: torch.Tensor | None = None,
+                             out_dtype: torch.dtype = torch.float32,
+                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """One decode step in one launch: write k_new/v_new [B][n_kv][d] at slot_mapping [B],
+    then attend with q [B][n_q][d] over the caches; returns out [B][n_q][d]."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, n_q, d = q.shape
+    if d != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the cache")
+    if k_new.shape != (B, k_cache.shape[1], d) or v_new.shape != k_new.shape:
+        raise ValueError("k_new and v_new must be [B][n_kv][head_dim]")
+    if slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be [B]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][n_q][d] in a supported dtype")
+    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dt = k_cache.dtype
+    _check("pa_paged_attn_decode_append", L.pa_paged_attn_decode_append(
+        _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
+        _dev(slot_mapping, "slot_mapping", torch.int64), B, n_q, _dev(k_cache, "k_cache", dt),
+        _dev(v_cache, "v_cache", dt), ctypes.byref(desc),
+        _dev(block_table, "block_table", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out

@@ -195,11 +195,22 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
     return plan_bytes(pl);
 }
 
-int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
-                         const void* v_cache, const pa_cache_desc* cache,
-                         const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+struct FusedAppend {
+    const void* k_new;
+    const void* v_new;
+    const int64_t* slots;
+    void* k_cache_w;
+    void* v_cache_w;
+};
+
+int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, const void* v_cache,
+                const pa_cache_desc* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
+                const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                void* workspace, size_t workspace_bytes, void* stream, const FusedAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
@@ -212,6 +223,14 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
         return fail(PA_ERR_INVALID_ARG, "decode: q, caches and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return fail(PA_ERR_INVALID_ARG, "decode: block_table and context_lens must be 4-byte aligned");
+    if (fa) {
+        if (!fa->k_new || !fa->v_new || !fa->slots)
+            return fail(PA_ERR_INVALID_ARG, "decode_append: k_new, v_new and slot_mapping must not be NULL");
+        if (!aligned16(fa->k_new) || !aligned16(fa->v_new))
+            return fail(PA_ERR_INVALID_ARG, "decode_append: k_new and v_new must be 16-byte aligned");
+        if (reinterpret_cast<uintptr_t>(fa->slots) & 7u)
+            return fail(PA_ERR_INVALID_ARG, "decode_append: slot_mapping must be 8-byte aligned");
+    }
 
     Plan pl;
     make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
@@ -251,10 +270,43 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
     a.ring = pl.ring;
     a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
     a.out_f32 = out_dtype == PA_F32;
+    if (fa) {
+        a.k_new = fa->k_new;
+        a.v_new = fa->v_new;
+        a.new_slots = fa->slots;
+        a.k_cache_w = fa->k_cache_w;
+        a.v_cache_w = fa->v_cache_w;
+    }
     const hipError_t e = pa::launch_decode(a, to_elem(cache->dtype), cache->head_dim,
                                            static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode launch");
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
+                         const void* v_cache, const pa_cache_desc* cache,
+                         const int32_t* block_table, int32_t max_blocks_per_seq,
+                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
+                       context_lens, scale, out, out_dtype, workspace, workspace_bytes, stream,
+                       nullptr);
+}
+
+int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
+                                const int64_t* slot_mapping, int32_t batch, int32_t n_q,
+                                void* k_cache, void* v_cache, const pa_cache_desc* cache,
+                                const int32_t* block_table, int32_t max_blocks_per_seq,
+                                const int32_t* context_lens, float scale, void* out,
+                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                void* stream) {
+    const FusedAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache};
+    return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
+                       context_lens, scale, out, out_dtype, workspace, workspace_bytes, stream, &fa);
 }
 
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,

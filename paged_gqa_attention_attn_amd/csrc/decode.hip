@@ -113,6 +113,24 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
     if (lane < nb) my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
+    // Fused append: the wave that owns the block holding position ctx - 1 patches
+    // the new K/V row into its LDS copy of that tile, and one wave per
+    // (sequence, KV head) writes the row to the cache slot.
+    constexpr int CH = ROW / 16;   // 16-byte chunks per row: lanes [0, CH) K, [CH, 2 CH) V
+    static_assert(2 * CH <= 64, "a K row and a V row fit in one wave");
+    const bool fused = p.new_slots != nullptr;
+    const int64_t new_slot = fused ? p.new_slots[b] : -1;
+    const bool slot_ok = new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS;
+    const int last_blk = ctx > 0 ? (ctx - 1) / BS : -1;
+    const bool patch_here = fused && slot_ok && last_blk >= blk0 && last_blk < blk0 + nb;
+    const bool writer = fused && slot_ok && part == nparts - 1 && hsgi == 0 && wave == 0;
+    uint4 new_row = make_uint4(0, 0, 0, 0);
+    if ((patch_here || writer) && lane < 2 * CH) {
+        const char* src = (const char*)(lane < CH ? p.k_new : p.v_new) +
+                          ((int64_t)b * p.n_kv + g) * ROW + (lane % CH) * 16;
+        new_row = *reinterpret_cast<const uint4*>(src);
+    }
+
     float m_run[GW], l_run[GW], acc[GW][EPL];
 #pragma unroll
     for (int hh = 0; hh < GW; ++hh) {
@@ -162,6 +180,13 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
             if (ahead == 0) wait_vmcnt<0>();
 
             const char* base = ring + (i % R) * 2 * TILE;
+            if (patch_here && blk0 + i == last_blk) {  // uniform: the new token's block
+                if (lane < 2 * CH) {
+                    char* row = ring + (i % R) * 2 * TILE + (lane < CH ? 0 : TILE) +
+                                ((ctx - 1) % BS) * ROW + (lane % CH) * 16;
+                    *reinterpret_cast<uint4*>(row) = new_row;
+                }
+            }
             uint4 kc[NT][2], vc[NT][2];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -303,6 +328,14 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
             }
             p.ws_acc[pi * D + e] = A;
         }
+    }
+
+    // The fused append's cache write goes last: a store counts in vmcnt, so an
+    // earlier one would be waited on by the ring's first full wait.
+    if (writer && lane < 2 * CH) {
+        char* dst = (char*)(lane < CH ? p.k_cache_w : p.v_cache_w) +
+                    (((new_slot / BS) * p.n_kv + g) * BS + new_slot % BS) * ROW + (lane % CH) * 16;
+        *reinterpret_cast<uint4*>(dst) = new_row;
     }
 }
 

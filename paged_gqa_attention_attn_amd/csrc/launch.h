@@ -30,6 +30,12 @@ struct DecodeArgs {
     int32_t ring;                // blocks in flight per wave (LDS ring depth: 1 or 2)
     float scale_log2;            // scale * log2(e)
     int32_t out_f32;             // 1: fp32 output, 0: output in the input type
+    // Fused append (all null for a plain decode): new token of each sequence.
+    const void* k_new;           // [B][n_kv][D]
+    const void* v_new;
+    const int64_t* new_slots;    // [B]
+    void* k_cache_w;             // writable views of the pools for the append
+    void* v_cache_w;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);

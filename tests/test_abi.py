@@ -82,6 +82,30 @@ def test_decode_empty_batch_is_a_noop(L):
     assert decode(L, batch=0) == PA_OK
 
 
+def decode_append(L, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(),
+             bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None,
+             ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_decode_append(a["q"], a["kn"], a["vn"], a["slots"], a["batch"],
+                                         a["n_q"], a["k"], a["v"], a["cache"], a["bt"], a["maxb"],
+                                         a["ctx"], a["scale"], a["out"], a["out_dtype"], a["ws"],
+                                         a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(kn=None), INVALID, "k_new"),
+    (dict(slots=None), INVALID, "slot_mapping"),
+    (dict(vn=MISALIGNED), INVALID, "aligned"),
+    (dict(slots=FAKE + 4), INVALID, "aligned"),
+    (dict(cache=desc(bs=32)), UNSUPPORTED, "block_size"),
+    (dict(n_q=5), INVALID, "multiple"),
+])
+def test_decode_append_rejects(L, kw, code, msg):
+    assert decode_append(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
 def test_workspace_query(L):
     # One partition per (sequence, KV head) needs no workspace; 4096-token
     # contexts at the default 2048-token partitions need (m, l, acc) for 2

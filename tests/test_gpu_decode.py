@@ -224,3 +224,95 @@ def test_full_size_config_sampled(pa, cfg):
     stats = assert_parity(got, want, case.dtype, f"config {cfg} sampled ({len(sel)} rows)")
     assert torch.isfinite(out).all()
     say(f"    sampled rows={len(sel)} max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+# ---- fused append + decode ------------------------------------------------------------------
+
+def _two_call(pa, case, slots=None):
+    kp, vp = case.k_pool.clone(), case.v_pool.clone()
+    s = case.slot_mapping if slots is None else slots
+    pa.kv_append(case.new_k, case.new_v, s, kp, vp)
+    out = pa.paged_attn_decode(case.q, kp, vp, case.block_table, case.context_lens, case.scale)
+    torch.cuda.synchronize()
+    return kp, vp, out
+
+
+def _fused(pa, case, slots=None):
+    kp, vp = case.k_pool.clone(), case.v_pool.clone()
+    s = case.slot_mapping if slots is None else slots
+    out = pa.paged_attn_decode_append(case.q, case.new_k, case.new_v, s, kp, vp,
+                                      case.block_table, case.context_lens, case.scale)
+    torch.cuda.synchronize()
+    return kp, vp, out
+
+
+def check_fused(pa, case, what, slots=None):
+    say(f"[decode+append] {what}: B={case.batch} n_q={case.n_q} n_kv={case.n_kv} "
+        f"ctx={case.context_lens.tolist()[:8]}")
+    ka, va, oa = _two_call(pa, case, slots)
+    kb, vb, ob = _fused(pa, case, slots)
+    assert same_bits(ka, kb) and same_bits(va, vb), f"{what}: pools differ from kv_append"
+    assert same_bits(oa, ob), f"{what}: fused output differs from kv_append + decode"
+    return ob
+
+
+FUSED = {
+    "gqa4_bf16_d128_ragged": (8, 2, 128, [1, 15, 16, 17, 33, 300, 1000], "bf16"),
+    "gqa4_f32_d64": (8, 2, 64, [31, 1, 2], "f32"),
+    "gqa2_f32_d128": (4, 2, 128, [9, 77], "f32"),
+    "bf16_d64": (8, 2, 64, [5, 64, 130], "bf16"),
+    "mqa64_bf16": (64, 1, 128, [100, 17], "bf16"),
+    "gqa8_bf16": (64, 8, 128, [1500, 2100], "bf16"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(FUSED))
+def test_fused_equals_two_calls(pa, name):
+    n_q, n_kv, d, ctx, dt = FUSED[name]
+    case = wl.make_decode_case(batch=len(ctx), n_q=n_q, n_kv=n_kv, head_dim=d, context_lens=ctx,
+                               dtype=dt, free_fraction=0.25, seed=zlib.crc32(name.encode()) % 9999,
+                               device="cuda", name=name)
+    out = check_fused(pa, case, name)
+    _, _, want = oracle_step(case)
+    assert_parity(out.cpu().numpy(), want, dt, f"fused {name} vs oracle")
+
+
+@pytest.mark.parametrize("tokens", [128, 512, 0])
+def test_fused_with_split_contexts(pa, tokens):
+    prev = pa.set_decode_partition_tokens(tokens)
+    try:
+        check_fused(pa, _sweep_case(), f"partition={tokens}")
+    finally:
+        pa.set_decode_partition_tokens(prev)
+
+
+def test_fused_config1_and_shared_prefix(pa):
+    check_fused(pa, wl.make_config(1, device="cuda"), "config1")
+    case = wl.make_decode_case(batch=6, n_q=8, n_kv=2, head_dim=128,
+                               context_lens=[300, 500, 900, 400, 640, 129], dtype="bf16",
+                               free_fraction=0.2, shared_prefix_blocks=8, n_sharers=3, seed=9,
+                               device="cuda", name="shared")
+    check_fused(pa, case, "shared prefix")
+
+
+def test_fused_padding_and_empty_context(pa):
+    case = wl.make_decode_case(batch=4, n_q=8, n_kv=2, head_dim=128, context_lens=[0, 40, 33, 20],
+                               dtype="bf16", free_fraction=0.3, seed=12, device="cuda",
+                               name="pad")
+    # Put the real new tokens in the cache first, then mark sequence 2 as padding: both
+    # paths must read the cached row at its last position and write nothing for it.
+    pa.kv_append(case.new_k, case.new_v, case.slot_mapping, case.k_pool, case.v_pool)
+    slots = case.slot_mapping.clone()
+    slots[2] = -1
+    out = check_fused(pa, case, "padding + empty context", slots=slots)
+    assert (out[0].cpu() == 0).all()
+    assert torch.isfinite(out[1:]).all()
+
+
+def test_fused_full_size_config2(pa):
+    case = wl.make_config(2, device="cuda")
+    out = check_fused(pa, case, "config 2 full size")
+    sel = _sampled_pairs(case)
+    _, _, want = oracle_step(case, sel=sel)
+    got = out.cpu().numpy()[sel[:, 0], sel[:, 1]]
+    assert_parity(got, want, "bf16", "fused config 2 sampled")
