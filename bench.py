@@ -173,12 +173,13 @@ def bench_decode(args, cfg: int):
                    for s in sets)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
-    def step(i, ev=None):
+    def step(i):
         s = sets[i % len(sets)]
         if args.unfused:
             pa.kv_append(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool)
-        if ev is not None:
-            ev[0].record()
+        decode(s)
+
+    def decode(s):
         if args.unfused:
             pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
                                  out=out, workspace=ws)
@@ -186,8 +187,6 @@ def bench_decode(args, cfg: int):
             pa.paged_attn_decode_append(s.q, s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool,
                                         s.block_table, s.context_lens, s.scale, out=out,
                                         workspace=ws)
-        if ev is not None:
-            ev[1].record()
 
     for i in range(args.warmup):
         step(i)
@@ -199,14 +198,17 @@ def bench_decode(args, cfg: int):
     t1 = time.perf_counter()
     ms = (t1 - t0) * 1e3 / args.steps
 
-    # Event-timed pass of the decode call on the launch stream.
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The decode launches alone, back to back, between two events on the launch
+    # stream: elapsed / steps is the average duration of one decode launch.
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
+    e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        decode(sets[i % len(sets)])
+    e1.record(stream)
     torch.cuda.synchronize()
-    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    dec_ms = e0.elapsed_time(e1) / args.steps
 
     kv = sum(acc.decode_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim, elem)
              for s in sets) / len(sets)
@@ -278,13 +280,12 @@ def bench_prefill(args):
     kf = [s.k.reshape(-1, s.n_kv, s.head_dim) for s in sets]
     vf = [s.v.reshape(-1, s.n_kv, s.head_dim) for s in sets]
 
-    def step(i, ev=None):
-        s = sets[i % n_sets]
-        if ev is not None:
-            ev[0].record()
+    def prefill(s):
         pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out)
-        if ev is not None:
-            ev[1].record()
+
+    def step(i):
+        s = sets[i % n_sets]
+        prefill(s)
         pa.kv_append(kf[i % n_sets], vf[i % n_sets], s.prompt_slots, s.k_pool, s.v_pool)
         pa.kv_append(s.new_k, s.new_v, s.new_slots, s.k_pool, s.v_pool)
         pa.paged_attn_decode(s.q_new, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
@@ -298,12 +299,15 @@ def bench_prefill(args):
         step(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
+    # The prefill launches alone, back to back, between two events on the launch stream.
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
     for i in range(args.steps):
-        step(i, evs[i])
+        prefill(sets[i % n_sets])
+    e1.record(stream)
     torch.cuda.synchronize()
-    pre_ms = sum(a.elapsed_time(b) for a, b in evs) / len(evs)
+    pre_ms = e0.elapsed_time(e1) / args.steps
     flops = acc.prefill_flops_causal(c0.batch, c0.seq_len, c0.n_q, c0.head_dim)
     achieved = flops / (pre_ms * 1e-3) / 1e12
     rec = {

@@ -107,7 +107,7 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *                 the sequence's logical block j (positions 16j .. 16j+15)
  *   context_lens  int32 [batch]: number of positions attended, counting the
  *                 token appended in the same step (positions 0..ctx-1)
- *   scale         multiplies q.k (usually 1/sqrt(head_dim))
+ *   scale         multiplies q.k (usually 1/sqrt(head_dim)); must be positive
  *   out           [batch][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes for the same arguments; may be NULL when that is 0.

@@ -215,7 +215,8 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     if (rc) return rc;
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
-    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "decode: a pointer argument is NULL");

@@ -83,6 +83,39 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
     const int slot = lane / LPT;
     const int c = lane % LPT;
 
+    // Every load that does not need the context length is issued before it is
+    // known, so the start of the kernel waits for one memory latency, not a chain.
+    const int hwg0 = g * p.group + hsgi * p.hs_wg * GW;  // first query head of the workgroup
+    const int h0 = hwg0 + hs * GW;                        // first query head of this wave
+    const int blk0 = part * p.waves_tok * p.blocks_per_wave + wt * p.blocks_per_wave;
+    uint4 qv[GW][2];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) {
+        const uint4* qrow =
+            reinterpret_cast<const uint4*>((const char*)p.q + (int64_t)(b * p.n_q + h0 + hh) * ROW);
+        qv[hh][0] = qrow[c];
+        qv[hh][1] = qrow[c + LPT];
+    }
+    // Lane k holds the physical id of logical block blk0 + k (the table row is
+    // read up to the wave's share or the row's end, whatever the context).
+    int my_phys = 0;
+    if (lane < p.blocks_per_wave && blk0 + lane < p.max_blocks)
+        my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
+
+    // Fused append: the wave that owns the block holding position ctx - 1 patches
+    // the new K/V row into its LDS copy of that tile, and one wave per
+    // (sequence, KV head) writes the row to the cache slot.
+    constexpr int CH = ROW / 16;   // 16-byte chunks per row: lanes [0, CH) K, [CH, 2 CH) V
+    static_assert(2 * CH <= 64, "a K row and a V row fit in one wave");
+    const bool fused = p.new_slots != nullptr;
+    const int64_t new_slot = fused ? p.new_slots[b] : -1;
+    uint4 new_row = make_uint4(0, 0, 0, 0);
+    if (fused && lane < 2 * CH) {
+        const char* src = (const char*)(lane < CH ? p.k_new : p.v_new) +
+                          ((int64_t)b * p.n_kv + g) * ROW + (lane % CH) * 16;
+        new_row = *reinterpret_cast<const uint4*>(src);
+    }
+
     // Context of this sequence. A length past the block table's reach cannot be
     // served without reading out of bounds: that sequence's rows become NaN.
     const int cap = p.max_blocks * BS;
@@ -93,43 +126,13 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
     const int bpp = p.waves_tok * p.blocks_per_wave;
     const int nparts = nblk > 0 ? (nblk + bpp - 1) / bpp : 1;
     if (part >= nparts) return;  // uniform over the workgroup
-
-    const int blk0 = part * bpp + wt * p.blocks_per_wave;
     const int nb = max(0, min(nblk - blk0, p.blocks_per_wave));
-    const int hwg0 = g * p.group + hsgi * p.hs_wg * GW;  // first query head of the workgroup
-    const int h0 = hwg0 + hs * GW;                        // first query head of this wave
-
-    uint4 qv[GW][2];
-#pragma unroll
-    for (int hh = 0; hh < GW; ++hh) {
-        const uint4* qrow =
-            reinterpret_cast<const uint4*>((const char*)p.q + (int64_t)(b * p.n_q + h0 + hh) * ROW);
-        qv[hh][0] = qrow[c];
-        qv[hh][1] = qrow[c + LPT];
-    }
-
-    // Lane k holds the physical id of logical block blk0 + k.
-    int my_phys = 0;
-    if (lane < nb) my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
-    // Fused append: the wave that owns the block holding position ctx - 1 patches
-    // the new K/V row into its LDS copy of that tile, and one wave per
-    // (sequence, KV head) writes the row to the cache slot.
-    constexpr int CH = ROW / 16;   // 16-byte chunks per row: lanes [0, CH) K, [CH, 2 CH) V
-    static_assert(2 * CH <= 64, "a K row and a V row fit in one wave");
-    const bool fused = p.new_slots != nullptr;
-    const int64_t new_slot = fused ? p.new_slots[b] : -1;
     const bool slot_ok = new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS;
     const int last_blk = ctx > 0 ? (ctx - 1) / BS : -1;
     const bool patch_here = fused && slot_ok && last_blk >= blk0 && last_blk < blk0 + nb;
     const bool writer = fused && slot_ok && part == nparts - 1 && hsgi == 0 && wave == 0;
-    uint4 new_row = make_uint4(0, 0, 0, 0);
-    if ((patch_here || writer) && lane < 2 * CH) {
-        const char* src = (const char*)(lane < CH ? p.k_new : p.v_new) +
-                          ((int64_t)b * p.n_kv + g) * ROW + (lane % CH) * 16;
-        new_row = *reinterpret_cast<const uint4*>(src);
-    }
 
     float m_run[GW], l_run[GW], acc[GW][EPL];
 #pragma unroll
@@ -207,7 +210,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                 for (int hh = 0; hh < GW; ++hh) {
                     float d = chunk_dot<E>(kc[t][0], qv[hh][0], 0.f);
                     d = chunk_dot<E>(kc[t][1], qv[hh][1], d);
-                    s[hh][t] = group_sum<LPT>(d) * p.scale_log2;
+                    s[hh][t] = group_sum<LPT>(d);   // raw q.k; scaled inside exp2 below
                 }
             }
             if (pos0 + BS > ctx) {  // last block: positions >= ctx hold unrelated bytes
@@ -234,6 +237,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                 float bm = s[hh][0];
 #pragma unroll
                 for (int t = 1; t < NT; ++t) bm = fmaxf(bm, s[hh][t]);
+                bm *= p.scale_log2;   // scale > 0, so scaling commutes with the max
                 // The running max moves only when some score in the wave passes it by
                 // more than TAU (log2 units); the wave-wide max is taken only then.
                 if (__any(bm > m_run[hh] + TAU)) {
@@ -246,7 +250,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const float pr = __builtin_amdgcn_exp2f(s[hh][t] - m_run[hh]);
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(s[hh][t], p.scale_log2, -m_run[hh]));
                     l_run[hh] += pr;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[t][e], acc[hh][e]);
@@ -297,24 +301,35 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
         const int e = idx % D;
         const int hsl = hl / GW;
         const int hh = hl % GW;
-        float M = -INFINITY;
         const float* slots = reinterpret_cast<const float*>(smem);
         constexpr int RING_F = RING / 4;
-        for (int w = 0; w < p.waves_tok; ++w)
-            M = fmaxf(M, slots[(w * p.hs_wg + hsl) * RING_F + GW * D + hh]);
+        // All reads are issued before any use, so the merge costs one LDS
+        // round trip rather than one per wave.
+        float mw[MAX_WAVES], lw[MAX_WAVES], aw[MAX_WAVES];
+#pragma unroll
+        for (int w = 0; w < MAX_WAVES; ++w) {
+            const bool live = w < p.waves_tok;
+            const float* ws = slots + (live ? w * p.hs_wg + hsl : 0) * RING_F;
+            mw[w] = live ? ws[GW * D + hh] : -INFINITY;
+            lw[w] = live ? ws[GW * D + GW + hh] : 0.f;
+            aw[w] = live ? ws[hh * D + e] : 0.f;
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MAX_WAVES; ++w) M = fmaxf(M, mw[w]);
         float L = 0.f, A = 0.f;
         if (M != -INFINITY) {
-            for (int w = 0; w < p.waves_tok; ++w) {
-                const float* ws = slots + (w * p.hs_wg + hsl) * RING_F;
-                const float f = __builtin_amdgcn_exp2f(ws[GW * D + hh] - M);
-                L = fmaf(f, ws[GW * D + GW + hh], L);
-                A = fmaf(f, ws[hh * D + e], A);
+#pragma unroll
+            for (int w = 0; w < MAX_WAVES; ++w) {
+                const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+                L = fmaf(f, lw[w], L);
+                A = fmaf(f, aw[w], A);
             }
         }
         const int h = hwg0 + hl;
         const int64_t row = (int64_t)b * p.n_q + h;
         if (nparts == 1) {
-            float o = (L == 0.f) ? 0.f : A / L;
+            float o = (L == 0.f) ? 0.f : A * __builtin_amdgcn_rcpf(L);
             if (ctx_bad) o = NAN;
             if (p.out_f32)
                 reinterpret_cast<float*>(p.out)[row * D + e] = o;

@@ -71,6 +71,8 @@ def decode(L, **kw):
     (dict(bt=FAKE + 2), INVALID, "aligned"),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
     (dict(scale=float("nan")), INVALID, "scale"),
+    (dict(scale=0.0), INVALID, "positive"),
+    (dict(scale=-0.125), INVALID, "positive"),
     (dict(maxb=8192), INVALID, "workspace"),
 ])
 def test_decode_rejects(L, kw, code, msg):
