@@ -9,21 +9,32 @@
 // research.frankk.site, Flash Attention paragraph of "工程优化怎么嵌进公式").
 //
 // Tiling (per workgroup: 4 waves, 128 query rows of one head, 32 per wave)
-//  * Key/value tiles of 64 positions are double-buffered in LDS: K row-major
-//    (rows padded to 272 B), V transposed to [dim][key] (rows padded to 136 B)
-//    because the PV product needs 8 consecutive keys per lane for one dim.
+//  * Key/value tiles of 64 positions are double-buffered in LDS. Each wave
+//    copies its quarter of the next K and V tiles with global_load_lds_dwordx4
+//    while the current tile is consumed, so tile data never passes through
+//    registers. Rows are stored unpadded, with the 16-byte chunk c of row r at
+//    position c ^ swz(r) of the row, which keeps the operand reads below free
+//    of LDS bank conflicts (the copy picks its source chunk so that each lane's
+//    destination stays the contiguous 16 * lane the copy instruction writes).
 //  * S^T = K Q^T with v_mfma_f32_32x32x16 (M = keys, N = queries, K = dims):
 //    each lane then holds 16 keys of ONE query per 32-key half-tile, so the
 //    row max needs only one v_permlane32_swap.
-//  * O^T = V^T P^T (M = dims, N = queries, K = keys): each lane's output
-//    column also belongs to one query, so the online-softmax rescale is a
-//    lane-local multiply. P is split into bf16 (or f16) hi + lo parts and both
-//    are multiplied, which keeps the result within ~1e-5 of exact (P rounded
-//    to 8 bits alone errs by up to ~3e-3 on rows with few keys).
+//  * O^T = V^T P^T (M = dims, N = queries, K = keys): each lane's output column
+//    also belongs to one query, so the online-softmax rescale is lane-local.
+//    The V^T operand (8 keys of one dim per lane) is read from the row-major V
+//    tile with ds_read_b64_tr_b16, which hands lane j of a 16-lane group
+//    element j % 4 of the 8-byte chunk fetched by lane 4e + j / 4, for e = 0..3.
+//  * For bf16, P is split into bf16 hi + lo parts and both are multiplied,
+//    which keeps the result within ~1e-5 of exact (P rounded to 8 bits alone
+//    errs by up to ~3e-3 on rows with few keys); f16 keeps 11 bits and needs
+//    no split.
 //  * The K/V-position permutation inside one MFMA is shared by both operands
 //    (it only has to be the same on A and B): lane half h = lane/32 holds keys
 //    {16j + 8(i/4) + 4h + i%4 : i = 0..7} of 16-key group j, which is exactly
 //    where the S^T accumulator put them.
+//  * The running max only moves when a score passes it by more than TAU
+//    (log2 units, checked with one ballot per tile), so the output rescale is
+//    rare; p stays below 2^TAU and acc, l and m stay consistent either way.
 //  * Causal: a workgroup visits key tiles up to its last query; tiles past a
 //    wave's last query are skipped by that wave; the heavy (late) query tiles
 //    are launched first.
@@ -38,55 +49,64 @@ typedef float f32x16_t __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int WM = 32;    // query rows per wave
 constexpr int NWAVES = BM / WM;
+constexpr float TAU = 8.0f;        // rescale threshold (log2 units)
+constexpr float M_FLOOR = -1e30f;  // running-max start: finite, so 2^(s - m) of a masked s is 0
 
 template <class E> struct Mfma;
 template <> struct Mfma<BF16> {
+    static constexpr bool kSplit = true;
     static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                        __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
     }
-    // Pack two fp32 values as the element type (round to nearest even), low half first.
+    // Two fp32 values as the element type (round to nearest even), x in the low half.
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        return (uint32_t)narrow<BF16>(x) | ((uint32_t)narrow<BF16>(y) << 16);
+        const bf16x2_t v = {(__bf16)x, (__bf16)y};
+        return __builtin_bit_cast(uint32_t, v);
     }
     static __device__ __forceinline__ float lo_of(uint32_t w) { return as_f32(w << 16); }
     static __device__ __forceinline__ float hi_of(uint32_t w) { return as_f32(w & 0xffff0000u); }
 };
 template <> struct Mfma<F16> {
+    static constexpr bool kSplit = false;
     static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
                                                       __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
     }
     static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        return (uint32_t)narrow<F16>(x) | ((uint32_t)narrow<F16>(y) << 16);
+        const f16x2_t v = {(_Float16)x, (_Float16)y};
+        return __builtin_bit_cast(uint32_t, v);
     }
-    static __device__ __forceinline__ float lo_of(uint32_t w) {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
-    }
-    static __device__ __forceinline__ float hi_of(uint32_t w) {
-        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
-    }
+    static __device__ __forceinline__ float lo_of(uint32_t) { return 0.f; }
+    static __device__ __forceinline__ float hi_of(uint32_t) { return 0.f; }
 };
 
-template <int D> struct Layout {
-    static constexpr int KROW = D * 2 + 16;          // padded bytes per K row in LDS
-    static constexpr int VTROW = BN * 2 + 8;         // padded bytes per V^T row (one dim)
-    static constexpr int K_BYTES = BN * KROW;
-    static constexpr int VT_BYTES = D * VTROW;
-    static constexpr int BUF = K_BYTES + VT_BYTES;   // one tile buffer
-    static constexpr int CHUNKS = BN * D / 8;        // 16-byte chunks per K (or V) tile
-    static constexpr int PER_THREAD = CHUNKS / (64 * NWAVES);
-    static_assert(PER_THREAD * 64 * NWAVES == CHUNKS, "tile splits evenly over the workgroup");
+template <int D> struct Tile {
+    static constexpr int ROWB = D * 2;                  // bytes per K or V row
+    static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
+    static constexpr int BYTES = BN * ROWB;             // one K or V tile
+    static constexpr int COPIES = BYTES / (1024 * NWAVES);  // 1 KB copies per wave per tile
+    static constexpr int BUF = 2 * BYTES;               // K tile, then V tile
+    static_assert(COPIES * 1024 * NWAVES == BYTES, "a tile splits into whole 1 KB wave copies");
+    // Position of chunk c of row r within the LDS row: c ^ swz(r). For 16 consecutive
+    // rows the masks are distinct (the K operand reads: one chunk column of 16 rows),
+    // and for 4 aligned rows they differ in bits 2-3 (the V^T reads: 4 rows x 4
+    // chunks), so neither read pattern hits an LDS bank twice.
+    static __device__ __forceinline__ int swz(int r) {
+        return (((r & 3) << 2) | ((r >> 2) & 3)) & (CPR - 1);
+    }
 };
 
 template <class E, int D>
 __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillArgs p) {
-    using L = Layout<D>;
+    using T = Tile<D>;
     using S = typename E::storage;
     constexpr int KK = D / 16;     // MFMA k-steps over the head dimension
     constexpr int MT = D / 32;     // 32-dim output tiles
@@ -97,7 +117,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int h = blockIdx.y;
     const int b = blockIdx.z;
     const int g = h / p.group;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;    // 0 or 1
     const int l32 = lane & 31;
@@ -106,10 +126,10 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int S_len = p.seq_len;
 
     const int64_t q_stride = (int64_t)p.n_q * D;       // elements between query positions
-    const int64_t kv_stride = (int64_t)p.n_kv * D;     // elements between key positions
+    const int64_t kv_row = (int64_t)p.n_kv * D * 2;    // bytes between key positions
     const S* Qg = reinterpret_cast<const S*>(p.q) + (int64_t)b * S_len * q_stride + (int64_t)h * D;
-    const S* Kg = reinterpret_cast<const S*>(p.k) + (int64_t)b * S_len * kv_stride + (int64_t)g * D;
-    const S* Vg = reinterpret_cast<const S*>(p.v) + (int64_t)b * S_len * kv_stride + (int64_t)g * D;
+    const char* Kg = reinterpret_cast<const char*>(p.k) + (int64_t)b * S_len * kv_row + (int64_t)g * D * 2;
+    const char* Vg = reinterpret_cast<const char*>(p.v) + (int64_t)b * S_len * kv_row + (int64_t)g * D * 2;
 
     // Q^T operand: lane holds dims 16*kk + 8*half .. +8 of its query, for every kk.
     u32x4_t qreg[KK];
@@ -128,141 +148,146 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int n_tiles = p.causal ? q_last_wg / BN + 1 : (S_len + BN - 1) / BN;
     const int q_last_wave = min(q0 + WM, S_len) - 1;
 
-    // Tile loads: K chunk r of this thread covers (key row, 16-byte column) of the
-    // tile; V chunks are assigned so that one wave's 64 lanes hold 64 consecutive
-    // keys of the same 8 dims, which makes the transposed LDS stores contiguous.
-    uint4 kbuf[L::PER_THREAD], vbuf[L::PER_THREAD];
-    auto load_tile = [&](int j) {
+    // This wave's copies of tile j into buffer `buf`: copy c fills bytes
+    // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
+    // the 16 bytes at 16 l of that, which hold source chunk pos ^ swz(row).
+    // Rows past the prompt repeat its last row; their keys are masked.
+    const uint32_t lds0 = lds_addr(smem);
+    auto issue_tile = [&](int j, int buf) {
+        const int key0 = j * BN;
 #pragma unroll
-        for (int r = 0; r < L::PER_THREAD; ++r) {
-            const int id = threadIdx.x + 64 * NWAVES * r;
-            const int krow = id / (D / 8), kcol = id % (D / 8);
-            const int kpos = j * BN + krow;
-            kbuf[r] = kpos < S_len ? *reinterpret_cast<const uint4*>(Kg + (int64_t)kpos * kv_stride + kcol * 8)
-                                   : make_uint4(0, 0, 0, 0);
-            const int vkey = id % BN, vcol = id / BN;
-            const int vpos = j * BN + vkey;
-            vbuf[r] = vpos < S_len ? *reinterpret_cast<const uint4*>(Vg + (int64_t)vpos * kv_stride + vcol * 8)
-                                   : make_uint4(0, 0, 0, 0);
+        for (int c = 0; c < T::COPIES; ++c) {
+            const int off = (wave * T::COPIES + c) * 1024 + 16 * lane;
+            const int r = off / T::ROWB;
+            const int chunk = ((off % T::ROWB) / 16) ^ T::swz(r);
+            const int64_t src = (int64_t)min(key0 + r, S_len - 1) * kv_row + chunk * 16;
+            const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
+            copy_to_lds16(Kg + src, dst);
+            copy_to_lds16(Vg + src, dst + T::BYTES);
         }
     };
-    auto store_tile = [&](int buf) {
-        char* kl = smem + buf * L::BUF;
-        char* vl = kl + L::K_BYTES;
+
+    // The tile copies are invisible to the compiler's wait counting: make it
+    // wait for q here, before the first copy, rather than inside the loop where
+    // its wait would also drain the prefetch of the next tile.
 #pragma unroll
-        for (int r = 0; r < L::PER_THREAD; ++r) {
-            const int id = threadIdx.x + 64 * NWAVES * r;
-            const int krow = id / (D / 8), kcol = id % (D / 8);
-            *reinterpret_cast<uint4*>(kl + krow * L::KROW + kcol * 16) = kbuf[r];
-            const int vkey = id % BN, vcol = id / BN;
-            const uint32_t w[4] = {vbuf[r].x, vbuf[r].y, vbuf[r].z, vbuf[r].w};
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint16_t val = (uint16_t)(w[e / 2] >> (16 * (e % 2)));
-                *reinterpret_cast<uint16_t*>(vl + (vcol * 8 + e) * L::VTROW + vkey * 2) = val;
-            }
-        }
-    };
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : : "v"(qreg[kk]));
 
     f32x16_t o[MT];
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16_t{};
-    float m_run = -INFINITY;   // running max (log2 units) of this lane's query
+    float m_run = M_FLOOR;     // running max (log2 units) of this lane's query
     float l_run = 0.f;         // this lane's share of the softmax denominator
+    const float c2 = p.scale_log2;
 
-    load_tile(0);
-    store_tile(0);
-    __syncthreads();
+    // Lane-constant parts of the operand addresses.
+    const int ksw = T::swz(l32);                 // rows l32 and 32 + l32 share it
+    const int g16 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
+    const int vkey = 4 * half + r16 / 4;         // + 16 jg + 8 t + 32 st
+    const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
+    const int vbyte = 8 * (r16 & 1);
 
+    issue_tile(0, 0);
     for (int j = 0; j < n_tiles; ++j) {
-        if (j + 1 < n_tiles) load_tile(j + 1);
-        const char* kl = smem + (j & 1) * L::BUF;
-        const char* vl = kl + L::K_BYTES;
+        wait_vmcnt<0>();   // this wave's copies of tile j have landed
+        __syncthreads();   // so have the other waves'; all are done with tile j - 1
+        if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
         const int key0 = j * BN;
+        if (p.causal && key0 > q_last_wave) continue;   // uniform over the wave
 
-        if (!p.causal || key0 <= q_last_wave) {
-            // S^T for two 32-key halves of the tile.
-            f32x16_t sc[2];
+        const char* kl = smem + (j & 1) * T::BUF;
+        lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
+
+        // S^T for the two 32-key halves, interleaved so each MFMA hides the other's latency.
+        f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+        const char* k0 = kl + l32 * T::ROWB;
+        const char* k1 = k0 + 32 * T::ROWB;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
-                sc[st] = f32x16_t{};
-                const char* krow = kl + (st * 32 + l32) * L::KROW + half * 16;
+        for (int kk = 0; kk < KK; ++kk) {
+            const int pos = ((2 * kk + half) ^ ksw) * 16;
+            const uint4 a0 = *reinterpret_cast<const uint4*>(k0 + pos);
+            const uint4 a1 = *reinterpret_cast<const uint4*>(k1 + pos);
+            sc[0] = Mfma<E>::run(u32x4_t{a0.x, a0.y, a0.z, a0.w}, qreg[kk], sc[0]);
+            sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
+        }
+
+        // Mask keys past this lane's query (causal) or past the prompt.
+        if (key0 + BN > S_len || (p.causal && key0 + BN - 1 > q0)) {   // uniform
+            const int lim = (p.causal ? min(my_q, S_len - 1) : S_len - 1) - key0;
 #pragma unroll
-                for (int kk = 0; kk < KK; ++kk) {
-                    const uint4 a = *reinterpret_cast<const uint4*>(krow + kk * 32);
-                    sc[st] = Mfma<E>::run(u32x4_t{a.x, a.y, a.z, a.w}, qreg[kk], sc[st]);
-                }
-            }
-            // Scale, mask, and the tile max of this lane's query.
-            const bool need_mask = key0 + BN > S_len || (p.causal && key0 + BN - 1 > q0);
-            float tmax = -INFINITY;
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
+            for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
-                    float x = sc[st][i] * p.scale_log2;
-                    if (need_mask) {
-                        const int key = key0 + st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                        if (key >= S_len || (p.causal && key > my_q)) x = -INFINITY;
-                    }
-                    sc[st][i] = x;
-                    tmax = fmaxf(tmax, x);
+                    const int key = st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+                    sc[st][i] = key > lim ? -INFINITY : sc[st][i];
                 }
-            }
-            {
-                float a2, b2;
-                pair32(tmax, a2, b2);
-                tmax = fmaxf(a2, b2);
-            }
+        }
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int st = 0; st < 2; ++st)
+#pragma unroll
+            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[st][i]);
+        {
+            float a2, b2;
+            pair32(tmax, a2, b2);
+            tmax = fmaxf(a2, b2) * c2;   // scale > 0, so scaling commutes with the max
+        }
+        if (__any(tmax > m_run + TAU)) {
             const float m_new = fmaxf(m_run, tmax);
-            const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
             m_run = m_new;
             l_run *= alpha;
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+        }
 
-            // P = 2^(s - m), split as hi + lo in the element type; PV on both parts.
-            u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
+        // P = 2^(s scale - m) in the element type (bf16: hi + lo parts).
+        u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
+        float lsum = 0.f;
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < 2; ++st) {
 #pragma unroll
-                for (int jg = 0; jg < 2; ++jg) {
-                    uint32_t hw[4], lw[4];
+            for (int jg = 0; jg < 2; ++jg) {
+                uint32_t hw[4], lw[4];
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float x0 = sc[st][8 * jg + 2 * w], x1 = sc[st][8 * jg + 2 * w + 1];
-                        const float p0 = (x0 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x0 - m_new);
-                        const float p1 = (x1 == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(x1 - m_new);
-                        hw[w] = Mfma<E>::pack(p0, p1);
-                        const float r0 = p0 - Mfma<E>::lo_of(hw[w]);
-                        const float r1 = p1 - Mfma<E>::hi_of(hw[w]);
-                        lw[w] = Mfma<E>::pack(r0, r1);
-                        l_run += p0 + p1;
-                    }
-                    ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                    pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+                for (int w = 0; w < 4; ++w) {
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, -m_run));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, -m_run));
+                    hw[w] = Mfma<E>::pack(p0, p1);
+                    if constexpr (Mfma<E>::kSplit)
+                        lw[w] = Mfma<E>::pack(p0 - Mfma<E>::lo_of(hw[w]), p1 - Mfma<E>::hi_of(hw[w]));
+                    lsum += p0 + p1;
                 }
+                ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                if constexpr (Mfma<E>::kSplit) pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
             }
+        }
+        l_run += lsum;
+
+        // O^T += V^T P^T. Lane (group g16, r16) fetches 4 dims of key vkey + ...,
+        // and after the transpose holds 4 consecutive keys of one dim.
 #pragma unroll
-            for (int mt = 0; mt < MT; ++mt) {
-                const char* vrow = vl + (mt * 32 + l32) * L::VTROW;
+        for (int st = 0; st < 2; ++st) {
 #pragma unroll
-                for (int st = 0; st < 2; ++st) {
+            for (int jg = 0; jg < 2; ++jg) {
 #pragma unroll
-                    for (int jg = 0; jg < 2; ++jg) {
-                        const int kb = st * 32 + jg * 16 + half * 4;   // keys kb..kb+3 and kb+8..kb+11
-                        const uint2 a0 = *reinterpret_cast<const uint2*>(vrow + kb * 2);
-                        const uint2 a1 = *reinterpret_cast<const uint2*>(vrow + (kb + 8) * 2);
-                        const u32x4_t a = u32x4_t{a0.x, a0.y, a1.x, a1.y};
-                        o[mt] = Mfma<E>::run(a, ph[st][jg], o[mt]);
-                        o[mt] = Mfma<E>::run(a, pl[st][jg], o[mt]);
+                for (int mt = 0; mt < MT; ++mt) {
+                    uint32_t a[4];
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const int key = st * 32 + jg * 16 + 8 * t + vkey;
+                        const int pos = ((4 * mt + vchunk) ^ T::swz(key)) * 16 + vbyte;
+                        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                            (lds_i16x4_t*)(vl_lds + key * T::ROWB + pos));
+                        a[2 * t] = __builtin_bit_cast(uint2, v).x;
+                        a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
                     }
+                    const u32x4_t av = u32x4_t{a[0], a[1], a[2], a[3]};
+                    o[mt] = Mfma<E>::run(av, ph[st][jg], o[mt]);
+                    if constexpr (Mfma<E>::kSplit) o[mt] = Mfma<E>::run(av, pl[st][jg], o[mt]);
                 }
             }
         }
-
-        if (j + 1 < n_tiles) store_tile((j + 1) & 1);
-        __syncthreads();
     }
 
     // Denominator: this lane and its partner (lane ^ 32) covered complementary keys.
@@ -296,7 +321,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 }
 
 template <class E, int D> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
-    const size_t lds = 2 * (size_t)Layout<D>::BUF;
+    const size_t lds = 2 * (size_t)Tile<D>::BUF;
     static bool opt_in = [] {
         return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<E, D>),
                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
