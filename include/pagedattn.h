@@ -34,6 +34,14 @@
  *    sequence whose context length exceeds max_blocks_per_seq * block_size or
  *    whose block table names a block outside the pool gets a NaN output row
  *    instead of an out-of-bounds read.
+ *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append and the
+ *    decode calls also copy that metadata to the host (synchronising `stream`)
+ *    and return PA_ERR_INVALID_ARG, enqueuing nothing, for: a slot past the
+ *    pool or repeated within one call; a context length outside
+ *    [0, max_blocks_per_seq * block_size]; a block id outside the pool among a
+ *    sequence's first ceil(ctx / block_size) table entries; and, for
+ *    decode_append, a slot other than position ctx - 1 of its own sequence or in
+ *    a block another sequence of the call also reads.
  */
 #ifndef PAGEDATTN_H
 #define PAGEDATTN_H
@@ -110,11 +118,15 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *   scale         multiplies q.k (usually 1/sqrt(head_dim)); must be positive
  *   out           [batch][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
- *                 bytes for the same arguments; may be NULL when that is 0.
+ *                 bytes for the same arguments, or NULL: then the workspace
+ *                 given to pa_set_workspace if it is large enough, else one the
+ *                 library allocates on the current device at the first call
+ *                 that needs it (grown when a later call needs more, which
+ *                 synchronises the device; kept until the process ends).
  * Query head h reads KV head h / (n_q / n_kv). ctx == 0 gives a zero row.
  * Results depend only on logical positions, so relabelling physical blocks
- * leaves every output bit unchanged. Calls that share a workspace must not
- * overlap on the GPU.
+ * leaves every output bit unchanged. Calls that share a workspace (the library's
+ * own included) must not overlap on the GPU: concurrent streams pass their own.
  */
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
@@ -158,6 +170,7 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *   q     [batch][seq_len][n_q][head_dim]   in dtype (bf16 or f16)
  *   k, v  [batch][seq_len][n_kv][head_dim]  in dtype
  *   causal  1: row i attends to keys 0..i; 0: to all seq_len keys
+ *   scale   multiplies q.k (usually 1/sqrt(head_dim)); must be positive
  *   out   [batch][seq_len][n_q][head_dim], out_dtype PA_F32 or dtype
  * Supported: head_dim 128 (and 64); dtype bf16 or f16.
  */
@@ -174,6 +187,15 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  * setting unchanged) for an invalid value.
  */
 int32_t pa_set_decode_partition_tokens(int32_t tokens);
+
+/*
+ * Default decode workspace for calls that pass workspace == NULL ([VC]/[IW]
+ * Flash Decoding partials). `workspace` is caller-owned device memory of
+ * `bytes` bytes, 16-byte aligned, that must stay valid while such calls run;
+ * NULL (with bytes == 0) clears the setting. Process-wide; returns PA_OK or
+ * PA_ERR_INVALID_ARG.
+ */
+int pa_set_workspace(void* workspace, size_t bytes);
 
 /* Thread-local, NUL-terminated description of the last failure on this thread. */
 const char* pa_last_error(void);

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
-           "decode_workspace_bytes",
+           "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
 _DTYPE = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
@@ -96,6 +96,17 @@ def kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
         _dev(k, "k", dt), _dev(v, "v", dt), _dev(slot_mapping, "slot_mapping", torch.int64), T,
         _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt), ctypes.byref(desc),
         _stream(k_cache, stream)))
+
+
+def set_workspace(workspace: torch.Tensor | None) -> None:
+    """Default decode workspace for calls made with ``workspace=None`` at the C ABI
+    (the binding below always passes one it allocated); None clears it."""
+    L = _lib.load()
+    if workspace is None:
+        _check("pa_set_workspace", L.pa_set_workspace(None, 0))
+    else:
+        _check("pa_set_workspace", L.pa_set_workspace(_dev(workspace, "workspace"),
+                                                      workspace.numel() * workspace.element_size()))
 
 
 def decode_workspace_bytes(batch: int, n_q: int, max_blocks_per_seq: int,

@@ -20,6 +20,7 @@ EXPORTS = (
     "pa_paged_attn_decode_append",
     "pa_paged_attn_prefill",
     "pa_set_decode_partition_tokens",
+    "pa_set_workspace",
     "pa_last_error",
     "pa_version",
 )
@@ -72,6 +73,8 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_prefill.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
+    L.pa_set_workspace.argtypes = [vp, sz]
+    L.pa_set_workspace.restype = ctypes.c_int
     L.pa_last_error.argtypes = []
     L.pa_last_error.restype = ctypes.c_char_p
     L.pa_version.argtypes = []

@@ -1,14 +1,22 @@
-// api.hip -- C-ABI entry points: argument validation, launch planning, error reporting.
+// api.hip -- C-ABI entry points: argument validation, launch planning, error reporting,
+// the decode workspace.
 //
-// No entry point reads device memory on the host or synchronises the stream;
-// every check here uses host-side arguments only. See include/pagedattn.h for
-// the contract of each call.
+// By default no entry point reads device memory on the host or synchronises the
+// stream: every check uses host-side arguments only, and the kernels bounds-check
+// the device-resident metadata themselves. With PA_VALIDATE=1 in the environment,
+// the calls also copy that metadata to the host (synchronising the stream) and
+// reject what the kernels would only skip or turn into NaN rows. See
+// include/pagedattn.h for the contract of each call.
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <unordered_map>
+#include <unordered_set>
+#include <vector>
 
 #include "launch.h"
 #include "pagedattn.h"
@@ -153,6 +161,120 @@ int check_decode_args(int32_t batch, int32_t n_q, const pa_cache_desc* cache,
     return PA_OK;
 }
 
+// ---- PA_VALIDATE: host-side checks of device-resident metadata ----------------------
+
+bool validate_enabled() {
+    const char* v = std::getenv("PA_VALIDATE");
+    return v && v[0] == '1' && v[1] == 0;
+}
+
+template <class T>
+int fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s, const char* what) {
+    dst.resize(n);
+    if (n == 0) return PA_OK;
+    hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "PA_VALIDATE: copying %s: %s", what, hipGetErrorString(e));
+    return PA_OK;
+}
+
+int validate_slots(const int64_t* slots_dev, int32_t n, const pa_cache_desc* c, hipStream_t s,
+                   std::vector<int64_t>& slots) {
+    int rc = fetch(slots, slots_dev, (size_t)n, s, "slot_mapping");
+    if (rc) return rc;
+    const int64_t num_slots = (int64_t)c->num_blocks * c->block_size;
+    std::unordered_set<int64_t> seen;
+    for (int32_t t = 0; t < n; ++t) {
+        const int64_t x = slots[t];
+        if (x < 0) continue;
+        if (x >= num_slots)
+            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: slot_mapping[%d] = %lld is past the pool (%lld slots)",
+                        t, (long long)x, (long long)num_slots);
+        if (!seen.insert(x).second)
+            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: slot %lld appears twice in slot_mapping", (long long)x);
+    }
+    return PA_OK;
+}
+
+int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev, int32_t max_blocks,
+                    const int32_t* ctx_dev, const int64_t* new_slots_dev, hipStream_t s) {
+    std::vector<int32_t> ctx, bt;
+    int rc = fetch(ctx, ctx_dev, (size_t)batch, s, "context_lens");
+    if (!rc) rc = fetch(bt, bt_dev, (size_t)batch * max_blocks, s, "block_table");
+    if (rc) return rc;
+    const int64_t cap = (int64_t)max_blocks * c->block_size;
+    std::unordered_map<int32_t, int32_t> readers;   // physical block -> sequences attending it
+    for (int32_t b = 0; b < batch; ++b) {
+        if (ctx[b] < 0 || ctx[b] > cap)
+            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: context_lens[%d] = %d is outside [0, %lld]", b,
+                        ctx[b], (long long)cap);
+        const int32_t nblk = (ctx[b] + c->block_size - 1) / c->block_size;
+        for (int32_t j = 0; j < nblk; ++j) {
+            const int32_t phys = bt[(size_t)b * max_blocks + j];
+            if (phys < 0 || phys >= c->num_blocks)
+                return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: block_table[%d][%d] = %d is outside the pool (%d blocks)",
+                            b, j, phys, c->num_blocks);
+            ++readers[phys];
+        }
+    }
+    if (!new_slots_dev) return PA_OK;
+    std::vector<int64_t> slots;
+    rc = validate_slots(new_slots_dev, batch, c, s, slots);
+    if (rc) return rc;
+    for (int32_t b = 0; b < batch; ++b) {
+        if (slots[b] < 0) continue;
+        if (ctx[b] < 1)
+            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: sequence %d appends a token but its context is empty", b);
+        const int32_t pos = ctx[b] - 1;
+        const int64_t want = (int64_t)bt[(size_t)b * max_blocks + pos / c->block_size] * c->block_size +
+                             pos % c->block_size;
+        if (slots[b] != want)
+            return fail(PA_ERR_INVALID_ARG,
+                        "PA_VALIDATE: slot_mapping[%d] = %lld, but position %d of sequence %d is slot %lld",
+                        b, (long long)slots[b], pos, b, (long long)want);
+        const int32_t phys = (int32_t)(slots[b] / c->block_size);
+        if (readers[phys] > 1)
+            return fail(PA_ERR_INVALID_ARG,
+                        "PA_VALIDATE: sequence %d appends into block %d, which another sequence also reads", b, phys);
+    }
+    return PA_OK;
+}
+
+// ---- decode workspace ------------------------------------------------------------------
+
+std::mutex g_ws_mu;
+void* g_default_ws = nullptr;       // set by pa_set_workspace (caller-owned)
+size_t g_default_ws_bytes = 0;
+std::unordered_map<int, std::pair<void*, size_t>> g_lib_ws;   // device -> library-owned buffer
+
+// A workspace of at least `need` bytes when the call passed none: the one set by
+// pa_set_workspace if it is large enough, else the library's own for the current
+// device (allocated or grown here, kept until the process ends).
+int resolve_workspace(size_t need, void** ws) {
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    if (g_default_ws && g_default_ws_bytes >= need) {
+        *ws = g_default_ws;
+        return PA_OK;
+    }
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "decode workspace: hipGetDevice");
+    auto& slot = g_lib_ws[dev];
+    if (slot.second < need) {
+        if (slot.first) {
+            e = hipFree(slot.first);   // synchronises the device: earlier users are done
+            slot = {nullptr, 0};
+            if (e != hipSuccess) return hip_fail(e, "decode workspace: hipFree");
+        }
+        void* p = nullptr;
+        e = hipMalloc(&p, need);
+        if (e != hipSuccess) return hip_fail(e, "decode workspace: hipMalloc");
+        slot = {p, need};
+    }
+    *ws = slot.first;
+    return PA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,6 +286,16 @@ const char* pa_last_error(void) { return g_err; }
 int32_t pa_set_decode_partition_tokens(int32_t tokens) {
     if (tokens < 0 || (tokens % kBlockSize) != 0) return -1;
     return g_partition_tokens.exchange(tokens);
+}
+
+int pa_set_workspace(void* workspace, size_t bytes) {
+    if (!workspace && bytes != 0) return fail(PA_ERR_INVALID_ARG, "pa_set_workspace: NULL with a nonzero size");
+    if (workspace && !aligned16(workspace))
+        return fail(PA_ERR_INVALID_ARG, "pa_set_workspace: workspace must be 16-byte aligned");
+    std::lock_guard<std::mutex> lock(g_ws_mu);
+    g_default_ws = workspace;
+    g_default_ws_bytes = workspace ? bytes : 0;
+    return PA_OK;
 }
 
 int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int32_t num_tokens,
@@ -178,6 +310,11 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
         return fail(PA_ERR_INVALID_ARG, "kv_append: k, v and the caches must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
         return fail(PA_ERR_INVALID_ARG, "kv_append: slot_mapping must be 8-byte aligned");
+    if (validate_enabled()) {
+        std::vector<int64_t> slots;
+        rc = validate_slots(slot_mapping, num_tokens, cache, static_cast<hipStream_t>(stream), slots);
+        if (rc) return rc;
+    }
     const int32_t row = cache->head_dim * elem_bytes(cache->dtype);
     const hipError_t e = pa::launch_kv_append(k, v, slot_mapping, num_tokens, cache->n_kv, row,
                                               cache->block_size,
@@ -237,10 +374,19 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
     const size_t need = plan_bytes(pl);
     if (need > 0) {
-        if (!workspace || workspace_bytes < need)
+        if (!workspace) {
+            rc = resolve_workspace(need, &workspace);
+            if (rc) return rc;
+        } else if (workspace_bytes < need) {
             return fail(PA_ERR_INVALID_ARG, "decode: workspace of %zu bytes required (got %zu)", need,
-                        workspace ? workspace_bytes : (size_t)0);
+                        workspace_bytes);
+        }
         if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "decode: workspace must be 16-byte aligned");
+    }
+    if (validate_enabled()) {
+        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens,
+                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream));
+        if (rc) return rc;
     }
 
     pa::DecodeArgs a{};
@@ -325,7 +471,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (n_q % n_kv != 0)
         return fail(PA_ERR_INVALID_ARG, "n_q (%d) is not a multiple of n_kv (%d)", n_q, n_kv);
     if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (batch == 0 || seq_len == 0) return PA_OK;
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))

@@ -25,6 +25,7 @@ mask and Paged Attention's 16-token blocks.
 """
 from __future__ import annotations
 
+import decimal
 import json
 import math
 from pathlib import Path
@@ -215,6 +216,31 @@ def pin_decode_two_keys_logistic(orc):
         delta = c["scale"] * float(q @ (k[1] - k[0]))       # s1 - s0
         w1 = 1.0 / (1.0 + math.exp(-delta))
         close(got[0, h], (1 - w1) * v[0] + w1 * v[1], 1e-14, "two keys -> logistic weights")
+
+
+def _decimal_decode(q, ks, vs, scale):
+    """Softmax attention of one query over a few keys in 40-digit decimal arithmetic."""
+    with decimal.localcontext() as ctx:
+        ctx.prec = 40
+        D = decimal.Decimal
+        sc = D(float(scale))
+        s = [sc * sum((D(float(a)) * D(float(b)) for a, b in zip(q, k)), D(0)) for k in ks]
+        m = max(s)
+        w = [(x - m).exp() for x in s]
+        tot = sum(w, D(0))
+        return np.asarray([float(sum((wi * D(float(v[c])) for wi, v in zip(w, vs)), D(0)) / tot)
+                           for c in range(len(vs[0]))], np.float64)
+
+
+def pin_decode_matches_decimal_bruteforce(orc):
+    # Tiny inputs (d <= 4, ctx <= 5) against the definition in 40-digit decimals.
+    for seed, ctxs, d in ((41, [1, 3, 5], 4), (42, [2, 4], 3), (43, [5], 2)):
+        c = decode_case(seed, ctxs, 2, 1, d, bs=2)
+        got = run_decode(orc, c)
+        for b, L in enumerate(ctxs):
+            for h in range(2):
+                want = _decimal_decode(c["q"][b, h], c["ks"][b][:L, 0], c["vs"][b][:L, 0], c["scale"])
+                close(got[b, h], want, 1e-14, f"decimal brute force b={b} h={h}")
 
 
 def pin_decode_hand_worked_fixture(orc):

@@ -73,7 +73,7 @@ def decode(L, **kw):
     (dict(scale=float("nan")), INVALID, "scale"),
     (dict(scale=0.0), INVALID, "positive"),
     (dict(scale=-0.125), INVALID, "positive"),
-    (dict(maxb=8192), INVALID, "workspace"),
+    (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),   # too small (NULL: library's own)
 ])
 def test_decode_rejects(L, kw, code, msg):
     assert decode(L, **kw) == code
@@ -129,6 +129,14 @@ def test_partition_override(L):
         assert L.pa_set_decode_partition_tokens(prev) == 256
 
 
+def test_set_workspace_rejects(L):
+    assert L.pa_set_workspace(None, 16) == INVALID
+    assert "NULL" in _lib.last_error()
+    assert L.pa_set_workspace(MISALIGNED, 1 << 20) == INVALID
+    assert "aligned" in _lib.last_error()
+    assert L.pa_set_workspace(None, 0) == PA_OK
+
+
 def append(L, **kw):
     a = dict(k=FAKE, v=FAKE, slots=FAKE, T=4, kc=FAKE, vc=FAKE, cache=desc(), stream=None)
     a.update(kw)
@@ -170,6 +178,8 @@ def prefill(L, **kw):
     (dict(out=None), INVALID),
     (dict(k=MISALIGNED), INVALID),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED),
+    (dict(scale=0.0), INVALID),
+    (dict(scale=-1.0), INVALID),
 ])
 def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
