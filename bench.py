@@ -210,6 +210,18 @@ def bench_decode(args, cfg: int):
     torch.cuda.synchronize()
     dec_ms = e0.elapsed_time(e1) / args.steps
 
+    # Per-launch spread: an event pair around each decode launch (each pair adds
+    # its own overhead, so these sit above the back-to-back average).
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(args.steps)]
+    for i, (a, b) in enumerate(pairs):
+        a.record(stream)
+        decode(sets[i % len(sets)])
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
+    pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 2) for q in (10, 50, 90)}
+
     kv = sum(acc.decode_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim, elem)
              for s in sets) / len(sets)
     io = acc.decode_io_bytes(c0.batch, c0.n_q, c0.head_dim, elem, 4, c0.max_blocks_per_seq)
@@ -247,6 +259,8 @@ def bench_decode(args, cfg: int):
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode", args.workload),
             "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
+            "launch_us_event_pairs": pct,
+            "device_copy_gbs": device_copy_gbs(),
             "source_hash": source_hash("decode"),
         },
     }
@@ -339,6 +353,22 @@ def bench_prefill(args):
     if args.cpu_seconds > 0:
         rec["cpu_baseline"] = cpu_baseline_prefill(c0, args.cpu_seconds)
     return rec
+
+
+def device_copy_gbs(n_bytes: int = 256 * 2**20, reps: int = 20) -> float:
+    """Read + write GB/s of a plain device copy of n_bytes, for context beside the roofline."""
+    import torch
+    src = torch.ones(n_bytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    return round(2 * n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
 def bench_copy(args):
