@@ -38,6 +38,7 @@ WORKLOADS = {
     "decode_70b_longctx": 4,
     "decode_tiny_fp32": 1,
     "prefill_then_decode": 5,
+    "chunked_prefill": 6,
     "copy_calibration": 0,
 }
 
@@ -371,6 +372,69 @@ def device_copy_gbs(n_bytes: int = 256 * 2**20, reps: int = 20) -> float:
     return round(2 * n_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9, 1)
 
 
+def bench_chunked_prefill(args):
+    """A 1024-token prompt chunk of each of 2 sequences over a 3072-token paged prefix
+    (LLaMA-3-8B attention shape): kv_append of the chunk, then chunked prefill."""
+    import torch
+
+    import paged_gqa_attention_attn_amd as pa
+    from paged_gqa_attention_attn_amd import accounting as acc
+    from paged_gqa_attention_attn_amd import workloads as wl
+
+    B, C, P = 2, 1024, 3072
+    n_sets = max(1, min(args.sets, 2))
+    sets = [wl.make_chunk_case(batch=B, chunk_len=C, prefix_lens=[P] * B, n_q=32, n_kv=8,
+                               head_dim=128, dtype="bf16", seed=1006 + 1000 * i, device="cuda",
+                               name="chunked_prefill_b2_prefix3072_chunk1024")
+            for i in range(n_sets)]
+    c0 = sets[0]
+    out = torch.empty_like(c0.q, dtype=torch.float32)
+
+    def prefill(s):
+        pa.paged_attn_chunked_prefill(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens,
+                                      s.scale, out=out)
+
+    def step(i):
+        s = sets[i % n_sets]
+        pa.kv_append(s.chunk_k, s.chunk_v, s.chunk_slots, s.k_pool, s.v_pool)
+        prefill(s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        prefill(sets[i % n_sets])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    pre_ms = e0.elapsed_time(e1) / args.steps
+    flops = acc.chunked_prefill_flops(c0.context_lens.cpu().tolist(), C, c0.n_q, c0.head_dim)
+    achieved = flops / (pre_ms * 1e-3) / 1e12
+    return {
+        "metric": "chunked prefill attention over a paged prefix, TFLOP/s (+ the chunk's cache write) at 1 GPU",
+        "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c0.dtype, "data": "synthetic",
+        "config": {"workload": c0.name, "batch": B, "chunk_len": C, "prefix_len": P, "n_q": c0.n_q,
+                   "n_kv": c0.n_kv, "head_dim": c0.head_dim, "flops": flops,
+                   "step": "kv_append of the 2x1024 chunk tokens + chunked prefill"},
+        "roofline": {"kernel": "prefill kernel, paged keys", "bound": "mfma",
+                     "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
+                     "source_hash": source_hash("prefill")},
+    }
+
+
 def bench_copy(args):
     """A plain device copy of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -409,7 +473,8 @@ def main(argv=None) -> int:
     if cfg == 0:
         rec = bench_copy(args)
     else:
-        rec = bench_prefill(args) if cfg == 5 else bench_decode(args, cfg)
+        rec = (bench_prefill(args) if cfg == 5 else bench_chunked_prefill(args) if cfg == 6
+               else bench_decode(args, cfg))
     rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
     return 0

@@ -34,8 +34,8 @@
  *    sequence whose context length exceeds max_blocks_per_seq * block_size or
  *    whose block table names a block outside the pool gets a NaN output row
  *    instead of an out-of-bounds read.
- *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append and the
- *    decode calls also copy that metadata to the host (synchronising `stream`)
+ *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append, the decode
+ *    calls and chunked prefill also copy that metadata to the host (synchronising `stream`)
  *    and return PA_ERR_INVALID_ARG, enqueuing nothing, for: a slot past the
  *    pool or repeated within one call; a context length outside
  *    [0, max_blocks_per_seq * block_size]; a block id outside the pool among a
@@ -178,6 +178,34 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, void* out,
                           pa_dtype out_dtype, void* stream);
+
+/*
+ * paged_attn_chunked_prefill -- a chunk of a prompt attends to the cached prefix
+ * and causally to itself, all keys read through the block table. [IW]
+ * "工程优化怎么嵌进公式" (chunked prefill: the prompt goes in pieces, the formula
+ * is unchanged) and "Prefill 阶段维度流转"; [VC] (kernels take a block table);
+ * [AE] 1.1 causal mask, 3.1 GQA grouping.
+ *
+ *   q             [batch][chunk_len][n_q][head_dim] in cache->dtype (bf16 or f16)
+ *   k_cache, v_cache  pools described by `cache`, already holding the chunk's own
+ *                 K/V (pa_kv_append first)
+ *   block_table   int32 [batch][max_blocks_per_seq]
+ *   context_lens  int32 [batch]: keys of sequence b, prefix plus chunk; query row i
+ *                 sits at position context_lens[b] - chunk_len + i and attends to
+ *                 positions 0 .. that position (causal mask aligned at the bottom
+ *                 right; chunk_len == context_lens[b] is a plain causal prefill)
+ *   scale         multiplies q.k; must be positive
+ *   out           [batch][chunk_len][n_q][head_dim], out_dtype PA_F32 or cache->dtype
+ * Rows at negative positions (context_lens[b] < chunk_len) are zero. A context
+ * length past max_blocks_per_seq * block_size, or a block id outside the pool
+ * among the ones the sequence's rows read, turns every row of that sequence into
+ * NaN instead of an out-of-bounds read. Supported: head_dim 64 or 128.
+ */
+int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
+                                  const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, float scale, void* out,
+                                  pa_dtype out_dtype, void* stream);
 
 /*
  * Tuning override for the decode partition size, in tokens (a multiple of 16

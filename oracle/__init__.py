@@ -169,6 +169,32 @@ class Oracle:
         return out
 
 
+    # -- a prompt chunk over its paged prefix ---------------------------------
+    def chunked_prefill(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
+                        block_table: np.ndarray, context_lens: np.ndarray, scale: float,
+                        sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
+        """q [B][C][n_q][d]; row i of sequence b is position ctx_b - C + i and attends to
+        positions 0 .. that position (the causal mask of the prefill pages, aligned at the
+        bottom right as chunked prefill keeps the formula unchanged). Each row is the
+        decode definition over the first ctx_b - C + i + 1 positions, so this runs
+        oracle_decode with one pseudo-sequence per (b, i); rows at negative positions are
+        zero. Returns fp64 [B][C][n_q][d], or [len(sel)][d] for (b, i, h) triples."""
+        B, C, n_q, d = q.shape
+        bt = np.ascontiguousarray(block_table, dtype=np.int32)
+        ctx = np.ascontiguousarray(context_lens, dtype=np.int64)
+        rows_ctx = (ctx[:, None] - C + np.arange(C)[None, :] + 1).clip(min=0).astype(np.int32)
+        q2 = np.ascontiguousarray(q).reshape(B * C, n_q, d)
+        bt2 = np.repeat(bt, C, axis=0)
+        if sel is not None:
+            sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
+            sel2 = np.stack([sel[:, 0] * C + sel[:, 1], sel[:, 2]], axis=1)
+            return self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
+                               sel=sel2, n_threads=n_threads)
+        out = self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
+                          n_threads=n_threads)
+        return out.reshape(B, C, n_q, d)
+
+
 _default: Oracle | None = None
 
 
@@ -188,6 +214,10 @@ def decode(*args, **kwargs):
 
 def prefill(*args, **kwargs):
     return get().prefill(*args, **kwargs)
+
+
+def chunked_prefill(*args, **kwargs):
+    return get().chunked_prefill(*args, **kwargs)
 
 
 def kv_append(*args, **kwargs):

@@ -24,6 +24,7 @@ from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
+           "paged_attn_chunked_prefill",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
@@ -213,4 +214,32 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
         d, int(bool(causal)), float(scale), _dev(out, "out"), _DTYPE[out.dtype],
         _stream(q, stream)))
+    return out
+
+
+def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                               block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                               out: torch.Tensor | None = None,
+                               out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+    """A prompt chunk q [B][C][n_q][d] attends to its paged prefix and causally to itself;
+    row i of sequence b is position context_lens[b] - C + i. Returns out [B][C][n_q][d]."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if q.dim() != 4 or q.shape[3] != k_cache.shape[3]:
+        raise ValueError("q must be [B][chunk_len][n_q][head_dim] matching the cache")
+    B, C, n_q, d = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    if out is None:
+        out = torch.empty((B, C, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][chunk_len][n_q][d] in a supported dtype")
+    dt = k_cache.dtype
+    _check("pa_paged_attn_chunked_prefill", L.pa_paged_attn_chunked_prefill(
+        _dev(q, "q", dt), B, C, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _DTYPE[out.dtype], _stream(q, stream)))
     return out

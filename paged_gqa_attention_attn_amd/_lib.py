@@ -19,6 +19,7 @@ EXPORTS = (
     "pa_paged_attn_decode",
     "pa_paged_attn_decode_append",
     "pa_paged_attn_prefill",
+    "pa_paged_attn_chunked_prefill",
     "pa_set_decode_partition_tokens",
     "pa_set_workspace",
     "pa_last_error",
@@ -71,6 +72,9 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, vp, ctypes.c_int, vp]
     L.pa_paged_attn_prefill.restype = ctypes.c_int
+    L.pa_paged_attn_chunked_prefill.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
+                                                ctypes.c_float, vp, ctypes.c_int, vp]
+    L.pa_paged_attn_chunked_prefill.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
     L.pa_set_workspace.argtypes = [vp, sz]

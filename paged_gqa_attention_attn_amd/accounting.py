@@ -56,6 +56,17 @@ def prefill_flops_causal(batch: int, seq_len: int, n_q: int, head_dim: int) -> i
     return 4 * batch * n_q * head_dim * (seq_len * (seq_len + 1) // 2)
 
 
+def chunked_prefill_flops(context_lens, chunk_len: int, n_q: int, head_dim: int) -> int:
+    """QK^T plus PV for a chunk of C rows at positions ctx-C .. ctx-1: row at position p sees p+1 keys."""
+    total = 0
+    for ctx in context_lens:
+        ctx = int(ctx)
+        first = max(0, ctx - chunk_len)                  # keys seen by the first row, minus one
+        rows = ctx - first
+        total += rows * (first + 1) + rows * (rows - 1) // 2
+    return 4 * n_q * head_dim * total
+
+
 def prefill_flops_full_square(batch: int, seq_len: int, n_q: int, head_dim: int) -> int:
     """The pages' convention: 2 * B * n_q * S * S * d per matmul, both matmuls."""
     return 2 * 2 * batch * n_q * seq_len * seq_len * head_dim

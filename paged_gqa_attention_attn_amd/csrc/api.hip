@@ -498,4 +498,56 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     return PA_OK;
 }
 
+int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
+                                  const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                                  const int32_t* context_lens, float scale, void* out,
+                                  pa_dtype out_dtype, void* stream) {
+    int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
+    if (rc) return rc;
+    if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill supports bf16 and f16 caches");
+    if (out_dtype != PA_F32 && out_dtype != cache->dtype)
+        return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
+    if (chunk_len < 0) return fail(PA_ERR_INVALID_ARG, "chunk_len %d < 0", chunk_len);
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (batch == 0 || chunk_len == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "chunked prefill: q, caches and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return fail(PA_ERR_INVALID_ARG, "chunked prefill: block_table and context_lens must be 4-byte aligned");
+    if (validate_enabled()) {
+        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
+                             static_cast<hipStream_t>(stream));
+        if (rc) return rc;
+    }
+
+    pa::PrefillArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.batch = batch;
+    a.seq_len = chunk_len;
+    a.n_q = n_q;
+    a.n_kv = cache->n_kv;
+    a.group = n_q / cache->n_kv;
+    a.causal = 1;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PA_F32;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks_per_seq;
+    a.num_blocks = cache->num_blocks;
+    const hipError_t e = pa::launch_prefill(a, to_elem(cache->dtype), cache->head_dim,
+                                            static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill: no kernel for these arguments");
+    if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
+    return PA_OK;
+}
+
 }  // extern "C"

@@ -45,8 +45,8 @@ hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, 
                             int64_t num_slots, void* k_cache, void* v_cache, hipStream_t s);
 
 struct PrefillArgs {
-    const void* q;  // [B][S][n_q][D]
-    const void* k;  // [B][S][n_kv][D]
+    const void* q;  // [B][S][n_q][D]: S = seq_len query rows per sequence
+    const void* k;  // contiguous: [B][S][n_kv][D]; paged: the K pool [num_blocks][n_kv][16][D]
     const void* v;
     void* out;      // [B][S][n_q][D]
     int32_t batch, seq_len, n_q, n_kv;
@@ -54,6 +54,11 @@ struct PrefillArgs {
     int32_t causal;
     float scale_log2;
     int32_t out_f32;
+    // Paged keys (block_table != nullptr): sequence b has context_lens[b] keys in the
+    // pools and its S query rows are its last S positions.
+    const int32_t* block_table;   // [B][max_blocks]
+    const int32_t* context_lens;  // [B]
+    int32_t max_blocks, num_blocks;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);

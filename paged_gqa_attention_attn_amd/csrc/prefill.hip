@@ -104,7 +104,7 @@ template <int D> struct Tile {
     }
 };
 
-template <class E, int D>
+template <class E, int D, bool PAGED>
 __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillArgs p) {
     using T = Tile<D>;
     using S = typename E::storage;
@@ -122,14 +122,34 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int half = lane >> 5;    // 0 or 1
     const int l32 = lane & 31;
     const int q0 = qt * BM + wave * WM;           // first query row of this wave
-    const int my_q = q0 + l32;                    // the query this lane's columns belong to
-    const int S_len = p.seq_len;
+    const int my_q = q0 + l32;                    // the query row this lane's columns belong to
+    const int S_len = p.seq_len;                  // query rows per sequence
+
+    // Keys: contiguous K/V hold exactly the S_len positions of the rows; paged
+    // K/V hold ctx positions reached through the block table, and the rows are
+    // the last S_len of them (causal, aligned at the bottom right). A context
+    // past the block table's reach or a block id outside the pool makes every
+    // row of the sequence NaN instead of reading out of bounds.
+    int ctx = S_len;
+    bool bad = false;
+    if constexpr (PAGED) {
+        ctx = p.context_lens[b];
+        if (ctx < 0 || ctx > p.max_blocks * 16) {
+            bad = ctx > 0;
+            ctx = 0;
+        }
+    }
+    const int qbase = ctx - S_len;                // position of query row 0
+    const int pos0 = qbase + q0;                  // position of this wave's first row
+    const int my_pos = qbase + my_q;              // position of this lane's query
 
     const int64_t q_stride = (int64_t)p.n_q * D;       // elements between query positions
     const int64_t kv_row = (int64_t)p.n_kv * D * 2;    // bytes between key positions
     const S* Qg = reinterpret_cast<const S*>(p.q) + (int64_t)b * S_len * q_stride + (int64_t)h * D;
-    const char* Kg = reinterpret_cast<const char*>(p.k) + (int64_t)b * S_len * kv_row + (int64_t)g * D * 2;
-    const char* Vg = reinterpret_cast<const char*>(p.v) + (int64_t)b * S_len * kv_row + (int64_t)g * D * 2;
+    // Contiguous rows interleave the KV heads; a pool block holds one 16-row tile per KV head.
+    const int64_t head_off = PAGED ? (int64_t)g * 16 * D * 2 : (int64_t)g * D * 2 + (int64_t)b * S_len * kv_row;
+    const char* Kg = reinterpret_cast<const char*>(p.k) + head_off;
+    const char* Vg = reinterpret_cast<const char*>(p.v) + head_off;
 
     // Q^T operand: lane holds dims 16*kk + 8*half .. +8 of its query, for every kk.
     u32x4_t qreg[KK];
@@ -143,24 +163,43 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
         }
     }
 
-    // Key tiles this workgroup visits.
-    const int q_last_wg = min(qt * BM + BM, S_len) - 1;
-    const int n_tiles = p.causal ? q_last_wg / BN + 1 : (S_len + BN - 1) / BN;
-    const int q_last_wave = min(q0 + WM, S_len) - 1;
+    // Key tiles this workgroup visits (none when its last query sees no key).
+    const int pos_last_wg = qbase + min(qt * BM + BM, S_len) - 1;
+    const int n_tiles = ctx == 0 ? 0
+                        : p.causal ? (pos_last_wg < 0 ? 0 : min(pos_last_wg, ctx - 1) / BN + 1)
+                                   : (ctx + BN - 1) / BN;
+    const int pos_last_wave = qbase + min(q0 + WM, S_len) - 1;
 
     // This wave's copies of tile j into buffer `buf`: copy c fills bytes
     // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
     // the 16 bytes at 16 l of that, which hold source chunk pos ^ swz(row).
-    // Rows past the prompt repeat its last row; their keys are masked.
+    // A wave's copies cover rows 16 wave .. 16 wave + 15 of the tile, i.e. one
+    // whole 16-token cache block when the keys are paged. Rows past the context
+    // read its last row instead (which is in the block the clamped block index
+    // names): their keys are masked, and their V rows must be finite because
+    // the P V product multiplies them by exactly 0.
+    static_assert(T::COPIES * 1024 == 16 * T::ROWB, "a wave copies one 16-row block per tile");
     const uint32_t lds0 = lds_addr(smem);
     auto issue_tile = [&](int j, int buf) {
         const int key0 = j * BN;
+        int64_t block_src = 0;
+        if constexpr (PAGED) {
+            const int jb = min(key0 / 16 + wave, (ctx - 1) / 16);   // uniform over the wave
+            int phys = p.block_table[(int64_t)b * p.max_blocks + jb];
+            if (phys < 0 || phys >= p.num_blocks) {
+                bad = true;
+                phys = 0;
+            }
+            block_src = (int64_t)phys * p.n_kv * 16 * T::ROWB;
+        }
 #pragma unroll
         for (int c = 0; c < T::COPIES; ++c) {
             const int off = (wave * T::COPIES + c) * 1024 + 16 * lane;
             const int r = off / T::ROWB;
             const int chunk = ((off % T::ROWB) / 16) ^ T::swz(r);
-            const int64_t src = (int64_t)min(key0 + r, S_len - 1) * kv_row + chunk * 16;
+            const int t = min(key0 + r, ctx - 1);   // the key this lane's row holds
+            const int64_t src = PAGED ? block_src + (int64_t)(t % 16) * T::ROWB + chunk * 16
+                                      : (int64_t)t * kv_row + chunk * 16;
             const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
             copy_to_lds16(Kg + src, dst);
             copy_to_lds16(Vg + src, dst + T::BYTES);
@@ -187,13 +226,13 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
 
-    issue_tile(0, 0);
+    if (n_tiles > 0) issue_tile(0, 0);
     for (int j = 0; j < n_tiles; ++j) {
         wait_vmcnt<0>();   // this wave's copies of tile j have landed
         __syncthreads();   // so have the other waves'; all are done with tile j - 1
         if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
         const int key0 = j * BN;
-        if (p.causal && key0 > q_last_wave) continue;   // uniform over the wave
+        if (p.causal && key0 > pos_last_wave) continue;   // uniform over the wave
 
         const char* kl = smem + (j & 1) * T::BUF;
         lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
@@ -212,8 +251,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
         }
 
         // Mask keys past this lane's query (causal) or past the prompt.
-        if (key0 + BN > S_len || (p.causal && key0 + BN - 1 > q0)) {   // uniform
-            const int lim = (p.causal ? min(my_q, S_len - 1) : S_len - 1) - key0;
+        if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0)) {   // uniform
+            const int lim = (p.causal ? min(my_pos, ctx - 1) : ctx - 1) - key0;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
@@ -296,8 +335,9 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
         pair32(l_run, a2, b2);
         l_run = a2 + b2;
     }
+    if constexpr (PAGED) bad = __syncthreads_or(bad);   // a bad block anywhere spoils the tiles
     if (my_q >= S_len) return;
-    const float inv = l_run > 0.f ? 1.f / l_run : 0.f;
+    const float inv = bad ? NAN : l_run > 0.f ? 1.f / l_run : 0.f;
     const int64_t orow = ((int64_t)b * S_len + my_q) * p.n_q + h;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
@@ -320,25 +360,30 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     }
 }
 
-template <class E, int D> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
+template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
     const size_t lds = 2 * (size_t)Tile<D>::BUF;
-    static bool opt_in = [] {
-        return hipFuncSetAttribute(reinterpret_cast<const void*>(&prefill_kernel<E, D>),
-                                   hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) == hipSuccess;
-    }();
-    (void)opt_in;
+    // Opt in to exactly the dynamic LDS used (static LDS, e.g. the one word
+    // __syncthreads_or needs, counts against the same 160 KB).
+    static const hipError_t opt_in = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&prefill_kernel<E, D, PAGED>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (opt_in != hipSuccess) return opt_in;
     const dim3 grid((a.seq_len + BM - 1) / BM, a.n_q, a.batch);
-    hipLaunchKernelGGL((prefill_kernel<E, D>), grid, dim3(64 * NWAVES), lds, s, a);
+    hipLaunchKernelGGL((prefill_kernel<E, D, PAGED>), grid, dim3(64 * NWAVES), lds, s, a);
     return hipGetLastError();
+}
+
+template <class E, int D> hipError_t launch_kv(const PrefillArgs& a, hipStream_t s) {
+    return a.block_table ? launch_typed<E, D, true>(a, s) : launch_typed<E, D, false>(a, s);
 }
 
 }  // namespace
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s) {
-    if (e == Elem::BF16 && head_dim == 128) return launch_typed<BF16, 128>(a, s);
-    if (e == Elem::BF16 && head_dim == 64) return launch_typed<BF16, 64>(a, s);
-    if (e == Elem::F16 && head_dim == 128) return launch_typed<F16, 128>(a, s);
-    if (e == Elem::F16 && head_dim == 64) return launch_typed<F16, 64>(a, s);
+    if (e == Elem::BF16 && head_dim == 128) return launch_kv<BF16, 128>(a, s);
+    if (e == Elem::BF16 && head_dim == 64) return launch_kv<BF16, 64>(a, s);
+    if (e == Elem::F16 && head_dim == 128) return launch_kv<F16, 128>(a, s);
+    if (e == Elem::F16 && head_dim == 64) return launch_kv<F16, 64>(a, s);
     return hipErrorNotSupported;
 }
 

@@ -244,6 +244,96 @@ def make_prefill_case(*, batch: int, seq_len: int, n_q: int, n_kv: int, head_dim
         context_lens=torch.full((batch,), seq_len + 1, dtype=torch.int32, device=device))
 
 
+@dataclass
+class ChunkCase:
+    """A prompt chunk against a paged prefix: append the chunk's K/V, then attend."""
+
+    name: str
+    dtype: str
+    batch: int
+    chunk_len: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    q: torch.Tensor             # [B][C][n_q][d]
+    k_pool: torch.Tensor        # [num_blocks][n_kv][bs][d], prefixes written, the rest NaN
+    v_pool: torch.Tensor
+    block_table: torch.Tensor   # int32 [B][max_blocks_per_seq]
+    context_lens: torch.Tensor  # int32 [B] = prefix + C
+    chunk_k: torch.Tensor       # [B*C][n_kv][d]  K/V of chunk token (b, i) at row b*C + i
+    chunk_v: torch.Tensor
+    chunk_slots: torch.Tensor   # int64 [B*C]     its slot (position prefix_b + i)
+
+    @property
+    def max_blocks_per_seq(self) -> int:
+        return int(self.block_table.shape[1])
+
+
+def make_chunk_case(*, batch: int, chunk_len: int, prefix_lens, n_q: int, n_kv: int,
+                    head_dim: int, dtype: str = "bf16", block_size: int = 16,
+                    free_fraction: float = 0.0, seed: int = 0, device="cpu",
+                    name: str = "chunk") -> ChunkCase:
+    """Paged prefixes of the given lengths plus one chunk of ``chunk_len`` new tokens each.
+
+    Blocks are a seeded permutation of the pool; every slot from a sequence's
+    prefix length on, and every free block, holds NaN until the chunk is appended.
+    """
+    rng = np.random.default_rng(seed)
+    pre = np.asarray(prefix_lens, dtype=np.int64).reshape(-1)
+    if pre.shape[0] != batch:
+        raise ValueError("prefix_lens must have one entry per sequence")
+    ctx = pre + chunk_len
+    nblk = (ctx + block_size - 1) // block_size
+    maxb = max(1, int(nblk.max(initial=0)))
+    used = int(nblk.sum())
+    num_blocks = max(1, math.ceil(used / (1.0 - free_fraction)))
+    perm = rng.permutation(num_blocks).astype(np.int32)
+    bt = np.zeros((batch, maxb), dtype=np.int32)
+    cursor = 0
+    for b in range(batch):
+        bt[b, :nblk[b]] = perm[cursor:cursor + nblk[b]]
+        cursor += int(nblk[b])
+    free = perm[cursor:]
+    for b in range(batch):
+        if maxb > nblk[b]:
+            bt[b, nblk[b]:] = rng.choice(free, size=maxb - nblk[b]) if free.size else 0
+
+    gen = _gen(device, seed)
+    shape = (num_blocks, n_kv, block_size, head_dim)
+    k_pool = _randn(shape, dtype, gen, device)
+    v_pool = _randn(shape, dtype, gen, device)
+    q = _randn((batch, chunk_len, n_q, head_dim), dtype, gen, device)
+    chunk_k = _randn((batch * chunk_len, n_kv, head_dim), dtype, gen, device)
+    chunk_v = _randn((batch * chunk_len, n_kv, head_dim), dtype, gen, device)
+    nan = float("nan")
+    if free.size:
+        idx = torch.as_tensor(free.astype(np.int64), device=device)
+        k_pool[idx] = nan
+        v_pool[idx] = nan
+    slots = np.zeros(batch * chunk_len, dtype=np.int64)
+    for b in range(batch):
+        for t in range(int(pre[b]), int(ctx[b])):
+            blk = int(bt[b, t // block_size])
+            k_pool[blk, :, t % block_size, :] = nan
+            v_pool[blk, :, t % block_size, :] = nan
+            slots[b * chunk_len + t - int(pre[b])] = blk * block_size + t % block_size
+        last = int(ctx[b]) - 1 if ctx[b] > 0 else -1
+        if last >= 0 and (last + 1) % block_size:
+            blk = int(bt[b, last // block_size])
+            k_pool[blk, :, (last + 1) % block_size:, :] = nan
+            v_pool[blk, :, (last + 1) % block_size:, :] = nan
+    return ChunkCase(
+        name=name, dtype=dtype, batch=batch, chunk_len=chunk_len, n_q=n_q, n_kv=n_kv,
+        head_dim=head_dim, block_size=block_size, num_blocks=num_blocks,
+        scale=1.0 / math.sqrt(head_dim), q=q, k_pool=k_pool, v_pool=v_pool,
+        block_table=torch.as_tensor(bt, device=device),
+        context_lens=torch.as_tensor(ctx.astype(np.int32), device=device),
+        chunk_k=chunk_k, chunk_v=chunk_v, chunk_slots=torch.as_tensor(slots, device=device))
+
+
 # ---- the five named workloads -------------------------------------------------
 
 CONFIG_SEEDS = {1: 1001, 2: 1002, 3: 1003, 4: 1004, 5: 1005}

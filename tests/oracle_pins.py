@@ -440,6 +440,56 @@ def pin_prefill_noncausal_row_equals_decode_over_all(orc):
         close(pre[:, i], dec, 1e-15, f"non-causal row {i} vs decode over all keys")
 
 
+# ---- chunked prefill over a paged prefix ---------------------------------------------------
+
+def pin_chunked_prefill_without_prefix_equals_causal_prefill(orc):
+    B, S, n_q, n_kv, d = 2, 11, 4, 2, 8
+    q, k, v = _prefill_inputs(46, B, S, n_q, n_kv, d)
+    want = orc.prefill(q, k, v, "f32", True, 0.3)
+    kp, bt = pack_pool([k[b] for b in range(B)], 4, 8, np.random.default_rng(6), np.float32(np.nan))
+    vp, _ = pack_pool([v[b] for b in range(B)], 4, 8, np.random.default_rng(6), np.float32(np.nan))
+    got = orc.chunked_prefill(q, kp, vp, "f32", bt, np.asarray([S, S], np.int32), 0.3)
+    close(got, want, 1e-14, "chunk == whole prompt: causal prefill")
+
+
+def pin_chunked_prefill_matches_library_sdpa_bottom_right(orc):
+    # Sequences of 13 and 21 keys; the last C = 6 are the chunk. Reference: torch's
+    # float64 SDPA with an explicit mask (row i sees keys <= prefix + i) and the KV heads
+    # repeated G times.
+    n_q, n_kv, d, C = 4, 2, 8, 6
+    g = torch.Generator().manual_seed(47)
+    lens = [13, 21]
+    ks = [stored(torch.randn(L, n_kv, d, generator=g), "f32") for L in lens]
+    vs = [stored(torch.randn(L, n_kv, d, generator=g), "f32") for L in lens]
+    q = stored(torch.randn(len(lens), C, n_q, d, generator=g), "f32")
+    kp, bt = pack_pool(ks, 4, 12, np.random.default_rng(7), np.float32(np.nan))
+    vp, _ = pack_pool(vs, 4, 12, np.random.default_rng(7), np.float32(np.nan))
+    got = orc.chunked_prefill(q, kp, vp, "f32", bt, np.asarray(lens, np.int32), 0.25)
+    G = n_q // n_kv
+    for b, L in enumerate(lens):
+        P = L - C
+        mask = torch.arange(L)[None, :] <= (P + torch.arange(C))[:, None]          # [C][L]
+        qq = torch.from_numpy(q[b].astype(np.float64)).transpose(0, 1)             # [n_q][C][d]
+        kk = torch.from_numpy(ks[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        vv = torch.from_numpy(vs[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qq.unsqueeze(0), kk.unsqueeze(0), vv.unsqueeze(0), attn_mask=mask, scale=0.25)[0]
+        close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"chunked prefill b={b} vs sdpa")
+
+
+def pin_chunked_prefill_rows_before_the_sequence_are_zero(orc):
+    n_q, n_kv, d, C = 2, 1, 8, 5
+    g = torch.Generator().manual_seed(48)
+    ks = [stored(torch.randn(3, n_kv, d, generator=g), "f32")]
+    vs = [stored(torch.randn(3, n_kv, d, generator=g), "f32")]
+    q = stored(torch.randn(1, C, n_q, d, generator=g), "f32")
+    kp, bt = pack_pool(ks, 4, 2, np.random.default_rng(8), np.float32(np.nan))
+    vp, _ = pack_pool(vs, 4, 2, np.random.default_rng(8), np.float32(np.nan))
+    got = orc.chunked_prefill(q, kp, vp, "f32", bt, np.asarray([3], np.int32), 0.3)
+    assert (got[0, :2] == 0).all(), "rows at positions -2 and -1 must be zero"
+    close(got[0, 2, 0], vs[0][0, 0], 1e-15, "row at position 0 returns v_0")
+
+
 # ---- kv_append ---------------------------------------------------------------------------
 
 def pin_kv_append_hand_worked_fixture(orc):

@@ -188,3 +188,34 @@ def test_prefill_rejects(L, kw, code):
 def test_prefill_empty_is_a_noop(L):
     assert prefill(L, S=0) == PA_OK
     assert prefill(L, B=0) == PA_OK
+
+
+def chunked(L, **kw):
+    a = dict(q=FAKE, B=2, C=16, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
+             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_chunked_prefill(a["q"], a["B"], a["C"], a["n_q"], a["k"], a["v"],
+                                           a["cache"], a["bt"], a["maxb"], a["ctx"], a["scale"],
+                                           a["out"], a["out_dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=None), INVALID, "descriptor"),
+    (dict(cache=desc(dtype=_lib.PA_F32)), UNSUPPORTED, "bf16 and f16"),
+    (dict(cache=desc(d=96)), UNSUPPORTED, "head_dim"),
+    (dict(C=-1), INVALID, "chunk_len"),
+    (dict(n_q=7), INVALID, "multiple"),
+    (dict(scale=0.0), INVALID, "positive"),
+    (dict(q=None), INVALID, "NULL"),
+    (dict(out=MISALIGNED), INVALID, "aligned"),
+    (dict(ctx=FAKE + 2), INVALID, "aligned"),
+    (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+])
+def test_chunked_prefill_rejects(L, kw, code, msg):
+    assert chunked(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_chunked_prefill_empty_is_a_noop(L):
+    assert chunked(L, C=0) == PA_OK
+    assert chunked(L, B=0) == PA_OK

@@ -54,3 +54,12 @@ def test_config_byte_totals():
     assert acc.decode_kv_bytes([32768] * 8, 8, 128, 2) == 2**30
     assert acc.decode_unique_kv_bytes([2000] * 4, 8, 128, 2, 1024, 4) == \
         acc.decode_kv_bytes([2000] * 4, 8, 128, 2) - 3 * 1024 * 4096
+
+
+def test_chunked_prefill_flops():
+    # A chunk that is the whole prompt is a causal prefill.
+    assert acc.chunked_prefill_flops([4096, 4096], 4096, 32, 128) == acc.prefill_flops_causal(2, 4096, 32, 128)
+    # ctx 5, chunk 2: rows at positions 3 and 4 see 4 and 5 keys -> 9 (q, k) pairs.
+    assert acc.chunked_prefill_flops([5], 2, 1, 1) == 4 * 9
+    # ctx 2, chunk 4: rows at positions -2, -1 see nothing; 0 and 1 see 1 and 2 keys.
+    assert acc.chunked_prefill_flops([2], 4, 1, 1) == 4 * 3
