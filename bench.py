@@ -39,6 +39,7 @@ WORKLOADS = {
     "decode_tiny_fp32": 1,
     "prefill_then_decode": 5,
     "chunked_prefill": 6,
+    "decode_multi_8b": 7,
     "copy_calibration": 0,
 }
 
@@ -47,7 +48,8 @@ CSRC = ROOT / "paged_gqa_attention_attn_amd" / "csrc"
 # Sources that determine each profiled kernel's code (their hash dates a counter summary).
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "common.h", "launch.h", "api.hip"],
-    "prefill": ["prefill.hip", "common.h", "launch.h", "api.hip"],
+    "prefill": ["prefill.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
+    "decode_multi": ["decode_multi.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
 }
 
 
@@ -435,6 +437,73 @@ def bench_chunked_prefill(args):
     }
 
 
+def bench_decode_multi(args):
+    """Speculative verification on the 8B decode shape: 4 new tokens per sequence (B=32,
+    n_q=32, n_kv=8, d=128, contexts of 2048 including them): kv_append of the 128 new
+    tokens, then one multi-row decode launch."""
+    import torch
+
+    import paged_gqa_attention_attn_amd as pa
+    from paged_gqa_attention_attn_amd import accounting as acc
+    from paged_gqa_attention_attn_amd import workloads as wl
+
+    B, R, ctx = 32, 4, 2048
+    sets = [wl.make_chunk_case(batch=B, chunk_len=R, prefix_lens=[ctx - R] * B, n_q=32, n_kv=8,
+                               head_dim=128, dtype="bf16", seed=1007 + 1000 * i, device="cuda",
+                               name="llama3_8b_decode_b32_ctx2048_4_rows")
+            for i in range(args.sets)]
+    c0 = sets[0]
+    out = torch.empty_like(c0.q, dtype=torch.float32)
+
+    def decode(s):
+        pa.paged_attn_decode_multi(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
+                                   out=out)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        pa.kv_append(s.chunk_k, s.chunk_v, s.chunk_slots, s.k_pool, s.v_pool)
+        decode(s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(args.steps):
+        decode(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / args.steps
+    kv = acc.decode_kv_bytes([ctx] * B, c0.n_kv, c0.head_dim, 2)
+    io = acc.decode_io_bytes(B * R, c0.n_q, c0.head_dim, 2, 4, c0.max_blocks_per_seq)
+    achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
+    return {
+        "metric": "multi-row paged decode (4 new tokens per sequence): KV GB/s (% HBM peak) at 1 GPU",
+        "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": c0.dtype, "data": "synthetic",
+        "config": {"workload": c0.name, "batch": B, "q_rows": R, "n_q": c0.n_q, "n_kv": c0.n_kv,
+                   "head_dim": c0.head_dim, "context_lens": "2048 each (including the 4 new tokens)",
+                   "kv_bytes_per_step": int(kv),
+                   "step": "kv_append of 4 new tokens per sequence + one multi-row decode launch"},
+        "roofline": {"kernel": "multi-row decode kernel (matrix cores)", "bound": "hbm",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
+                     "source_hash": source_hash("decode_multi")},
+        "tflops": round(4 * R * c0.n_q * c0.head_dim * ctx * B / (dec_ms * 1e-3) / 1e12, 3),
+    }
+
+
 def bench_copy(args):
     """A plain device copy of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -474,7 +543,7 @@ def main(argv=None) -> int:
         rec = bench_copy(args)
     else:
         rec = (bench_prefill(args) if cfg == 5 else bench_chunked_prefill(args) if cfg == 6
-               else bench_decode(args, cfg))
+               else bench_decode_multi(args) if cfg == 7 else bench_decode(args, cfg))
     rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
     return 0

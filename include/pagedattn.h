@@ -35,7 +35,7 @@
  *    whose block table names a block outside the pool gets a NaN output row
  *    instead of an out-of-bounds read.
  *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append, the decode
- *    calls and chunked prefill also copy that metadata to the host (synchronising `stream`)
+ *    calls (single- and multi-row) and chunked prefill also copy that metadata to the host (synchronising `stream`)
  *    and return PA_ERR_INVALID_ARG, enqueuing nothing, for: a slot past the
  *    pool or repeated within one call; a context length outside
  *    [0, max_blocks_per_seq * block_size]; a block id outside the pool among a
@@ -178,6 +178,34 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, void* out,
                           pa_dtype out_dtype, void* stream);
+
+/*
+ * paged_attn_decode_multi -- q_rows new query rows per sequence (speculative
+ * verification of drafted tokens) attend to the paged cache in one step. Row r
+ * of sequence b sits at position context_lens[b] - q_rows + r and attends to
+ * positions 0 .. that position: [AE] 1.1 causal mask, 3.1 GQA grouping; [VC]
+ * block table; [IW] "工程优化怎么嵌进公式" (verifying several drafted tokens at
+ * once turns decode's vector products into small matrix products).
+ *
+ *   q             [batch][q_rows][n_q][head_dim] in cache->dtype (bf16 or f16)
+ *   k_cache, v_cache  pools described by `cache`, already holding the rows' own
+ *                 K/V (pa_kv_append of the q_rows new tokens first)
+ *   block_table, context_lens, scale  as for pa_paged_attn_decode
+ *   out           [batch][q_rows][n_q][head_dim], out_dtype PA_F32 or cache->dtype
+ *   workspace     as for pa_paged_attn_decode, sized by pa_decode_multi_workspace_bytes
+ * The (query head, row) pairs of one KV head are the N side of matrix-core
+ * products, so each K/V byte is read once per step. Rows at negative positions
+ * (context_lens[b] < q_rows) are zero; a context past the block table's reach or
+ * an out-of-pool block id gives NaN rows. Results equal pa_paged_attn_chunked_prefill
+ * with chunk_len = q_rows up to rounding. Supported: head_dim 64 or 128.
+ */
+size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
+                                       int32_t max_blocks_per_seq, const pa_cache_desc* cache);
+int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
+                               const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_chunked_prefill -- a chunk of a prompt attends to the cached prefix

@@ -24,7 +24,7 @@ from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
-           "paged_attn_chunked_prefill",
+           "paged_attn_chunked_prefill", "paged_attn_decode_multi",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
@@ -242,4 +242,38 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
         _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
         _DTYPE[out.dtype], _stream(q, stream)))
+    return out
+
+
+def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                            out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """q_rows new rows per sequence, q [B][q_rows][n_q][d]; row r of sequence b is position
+    context_lens[b] - q_rows + r. Returns out [B][q_rows][n_q][d]."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    if q.dim() != 4 or q.shape[3] != k_cache.shape[3]:
+        raise ValueError("q must be [B][q_rows][n_q][head_dim] matching the cache")
+    B, R, n_q, d = q.shape
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, R, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != q.shape or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][q_rows][n_q][d] in a supported dtype")
+    need = int(L.pa_decode_multi_workspace_bytes(B, R, n_q, maxb, ctypes.byref(desc)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    dt = k_cache.dtype
+    _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
+        _dev(q, "q", dt), B, R, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out

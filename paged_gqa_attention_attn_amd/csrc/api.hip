@@ -7,6 +7,7 @@
 // the calls also copy that metadata to the host (synchronising the stream) and
 // reject what the kernels would only skip or turn into NaN rows. See
 // include/pagedattn.h for the contract of each call.
+#include <algorithm>
 #include <atomic>
 #include <cmath>
 #include <cstdarg>
@@ -159,6 +160,34 @@ int check_decode_args(int32_t batch, int32_t n_q, const pa_cache_desc* cache,
     if ((int64_t)max_blocks_per_seq * kBlockSize > INT32_MAX / 2)
         return fail(PA_ERR_INVALID_ARG, "max_blocks_per_seq %d too large", max_blocks_per_seq);
     return PA_OK;
+}
+
+// Multi-row decode plan: 4 waves per workgroup, each a contiguous run of blocks of
+// the partition (2048 tokens unless overridden), groups of 32 (row, head) pairs.
+constexpr int kMultiWaves = 4;
+constexpr int kMultiRows = 32;
+
+struct MultiPlan {
+    int32_t blocks_per_wave, nparts_max, row_groups;
+    size_t m_floats, bytes;
+};
+
+MultiPlan multi_plan(int32_t batch, int32_t q_rows, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c) {
+    MultiPlan pl{};
+    const int64_t rows_per_kv = (int64_t)(n_q / c->n_kv) * q_rows;
+    pl.row_groups = (int32_t)((rows_per_kv + kMultiRows - 1) / kMultiRows);
+    int32_t tokens = g_partition_tokens.load();
+    if (tokens <= 0) tokens = 2048;
+    int32_t bpw = tokens / (kBlockSize * kMultiWaves);
+    bpw = std::max(2, std::min(64, bpw & ~1));
+    pl.blocks_per_wave = bpw;
+    const int32_t bpp = bpw * kMultiWaves;
+    pl.nparts_max = std::max(1, (max_blocks + bpp - 1) / bpp);
+    if (pl.nparts_max > 1) {
+        pl.m_floats = (size_t)batch * q_rows * n_q * pl.nparts_max;
+        pl.bytes = 2 * round16(pl.m_floats * sizeof(float)) + pl.m_floats * c->head_dim * sizeof(float);
+    }
+    return pl;
 }
 
 // ---- PA_VALIDATE: host-side checks of device-resident metadata ----------------------
@@ -495,6 +524,84 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (e == hipErrorNotSupported)
         return fail(PA_ERR_UNSUPPORTED, "prefill: no kernel for these arguments");
     if (e != hipSuccess) return hip_fail(e, "prefill launch");
+    return PA_OK;
+}
+
+size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
+                                       int32_t max_blocks_per_seq, const pa_cache_desc* cache) {
+    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK || q_rows < 1) return 0;
+    return multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache).bytes;
+}
+
+int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
+                               const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
+    if (rc) return rc;
+    if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
+        return fail(PA_ERR_UNSUPPORTED, "multi-row decode supports bf16 and f16 caches");
+    if (out_dtype != PA_F32 && out_dtype != cache->dtype)
+        return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
+    if (q_rows < 1) return fail(PA_ERR_INVALID_ARG, "q_rows %d must be positive", q_rows);
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (batch == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "multi-row decode: a pointer argument is NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "multi-row decode: q, caches and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return fail(PA_ERR_INVALID_ARG, "multi-row decode: block_table and context_lens must be 4-byte aligned");
+    const MultiPlan pl = multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache);
+    if (pl.bytes > 0) {
+        if (!workspace) {
+            rc = resolve_workspace(pl.bytes, &workspace);
+            if (rc) return rc;
+        } else if (workspace_bytes < pl.bytes) {
+            return fail(PA_ERR_INVALID_ARG, "multi-row decode: workspace of %zu bytes required (got %zu)",
+                        pl.bytes, workspace_bytes);
+        }
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "multi-row decode: workspace must be 16-byte aligned");
+    }
+    if (validate_enabled()) {
+        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
+                             static_cast<hipStream_t>(stream));
+        if (rc) return rc;
+    }
+
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    if (pl.bytes > 0) {
+        char* w = static_cast<char*>(workspace);
+        a.ws_m = reinterpret_cast<float*>(w);
+        a.ws_l = reinterpret_cast<float*>(w + round16(pl.m_floats * sizeof(float)));
+        a.ws_acc = reinterpret_cast<float*>(w + 2 * round16(pl.m_floats * sizeof(float)));
+    }
+    a.batch = batch;
+    a.n_q = n_q;
+    a.n_kv = cache->n_kv;
+    a.num_blocks = cache->num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.group = n_q / cache->n_kv;
+    a.waves_tok = kMultiWaves;
+    a.blocks_per_wave = pl.blocks_per_wave;
+    a.nparts_max = pl.nparts_max;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PA_F32;
+    a.q_rows = q_rows;
+    a.row_groups = pl.row_groups;
+    const hipError_t e = pa::launch_decode_multi(a, to_elem(cache->dtype), cache->head_dim,
+                                                 static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "multi-row decode: no kernel for these arguments");
+    if (e != hipSuccess) return hip_fail(e, "multi-row decode launch");
     return PA_OK;
 }
 

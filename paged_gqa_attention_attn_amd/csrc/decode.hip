@@ -434,6 +434,16 @@ template <class E> hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipS
 
 }  // namespace
 
+hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s) {
+    const dim3 grid(a.n_q, a.batch);
+    if (e == Elem::BF16 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<BF16, 128>), grid, dim3(128), 0, s, a);
+    else if (e == Elem::BF16 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<BF16, 64>), grid, dim3(64), 0, s, a);
+    else if (e == Elem::F16 && head_dim == 128) hipLaunchKernelGGL((decode_reduce_kernel<F16, 128>), grid, dim3(128), 0, s, a);
+    else if (e == Elem::F16 && head_dim == 64) hipLaunchKernelGGL((decode_reduce_kernel<F16, 64>), grid, dim3(64), 0, s, a);
+    else return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s) {
     if (a.hs_wg * a.waves_tok > MAX_WAVES || a.hs_wg < 1 || a.waves_tok < 1) return hipErrorInvalidValue;
     switch (e) {

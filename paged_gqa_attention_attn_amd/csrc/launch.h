@@ -36,9 +36,17 @@ struct DecodeArgs {
     const int64_t* new_slots;    // [B]
     void* k_cache_w;             // writable views of the pools for the append
     void* v_cache_w;
+    // Multi-row decode: q_rows new query rows per sequence ([B][q_rows][n_q][D]),
+    // served in groups of 32 (query head, row) pairs per KV head (grid.y = n_kv * row_groups).
+    int32_t q_rows;
+    int32_t row_groups;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
+// The log-sum-exp merge of partition partials alone (rows = batch * n_q of `a`).
+hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
+// Multi-row decode on the matrix cores (bf16/f16), plus the merge when contexts split.
+hipError_t launch_decode_multi(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
 
 hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
                             int32_t n_kv, int32_t row_bytes, int32_t block_size,

@@ -38,19 +38,12 @@
 //  * Causal: a workgroup visits key tiles up to its last query; tiles past a
 //    wave's last query are skipped by that wave; the heavy (late) query tiles
 //    are launched first.
-#include "common.h"
 #include "launch.h"
+#include "mfma.h"
 
 namespace pa {
 
 namespace {
-
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
-typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
-typedef short i16x4_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4_t lds_i16x4_t;
 
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
@@ -59,35 +52,6 @@ constexpr int NWAVES = BM / WM;
 constexpr float TAU = 8.0f;        // rescale threshold (log2 units)
 constexpr float M_FLOOR = -1e30f;  // running-max start: finite, so 2^(s - m) of a masked s is 0
 
-template <class E> struct Mfma;
-template <> struct Mfma<BF16> {
-    static constexpr bool kSplit = true;
-    static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
-                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
-    }
-    // Two fp32 values as the element type (round to nearest even), x in the low half.
-    static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        const bf16x2_t v = {(__bf16)x, (__bf16)y};
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    static __device__ __forceinline__ float lo_of(uint32_t w) { return as_f32(w << 16); }
-    static __device__ __forceinline__ float hi_of(uint32_t w) { return as_f32(w & 0xffff0000u); }
-};
-template <> struct Mfma<F16> {
-    static constexpr bool kSplit = false;
-    static __device__ __forceinline__ f32x16_t run(u32x4_t a, u32x4_t b, f32x16_t c) {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a),
-                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
-    }
-    static __device__ __forceinline__ uint32_t pack(float x, float y) {
-        const f16x2_t v = {(_Float16)x, (_Float16)y};
-        return __builtin_bit_cast(uint32_t, v);
-    }
-    static __device__ __forceinline__ float lo_of(uint32_t) { return 0.f; }
-    static __device__ __forceinline__ float hi_of(uint32_t) { return 0.f; }
-};
-
 template <int D> struct Tile {
     static constexpr int ROWB = D * 2;                  // bytes per K or V row
     static constexpr int CPR = ROWB / 16;               // 16-byte chunks per row
@@ -95,13 +59,7 @@ template <int D> struct Tile {
     static constexpr int COPIES = BYTES / (1024 * NWAVES);  // 1 KB copies per wave per tile
     static constexpr int BUF = 2 * BYTES;               // K tile, then V tile
     static_assert(COPIES * 1024 * NWAVES == BYTES, "a tile splits into whole 1 KB wave copies");
-    // Position of chunk c of row r within the LDS row: c ^ swz(r). For 16 consecutive
-    // rows the masks are distinct (the K operand reads: one chunk column of 16 rows),
-    // and for 4 aligned rows they differ in bits 2-3 (the V^T reads: 4 rows x 4
-    // chunks), so neither read pattern hits an LDS bank twice.
-    static __device__ __forceinline__ int swz(int r) {
-        return (((r & 3) << 2) | ((r >> 2) & 3)) & (CPR - 1);
-    }
+    static __device__ __forceinline__ int swz(int r) { return chunk_swizzle<CPR>(r); }
 };
 
 template <class E, int D, bool PAGED>

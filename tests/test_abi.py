@@ -219,3 +219,37 @@ def test_chunked_prefill_rejects(L, kw, code, msg):
 def test_chunked_prefill_empty_is_a_noop(L):
     assert chunked(L, C=0) == PA_OK
     assert chunked(L, B=0) == PA_OK
+
+
+def multi(L, **kw):
+    a = dict(q=FAKE, B=2, R=4, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
+             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_decode_multi(a["q"], a["B"], a["R"], a["n_q"], a["k"], a["v"], a["cache"],
+                                        a["bt"], a["maxb"], a["ctx"], a["scale"], a["out"],
+                                        a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=None), INVALID, "descriptor"),
+    (dict(cache=desc(dtype=_lib.PA_F32)), UNSUPPORTED, "bf16 and f16"),
+    (dict(R=0), INVALID, "q_rows"),
+    (dict(n_q=7), INVALID, "multiple"),
+    (dict(scale=-1.0), INVALID, "positive"),
+    (dict(v=None), INVALID, "NULL"),
+    (dict(q=MISALIGNED), INVALID, "aligned"),
+    (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
+])
+def test_decode_multi_rejects(L, kw, code, msg):
+    assert multi(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_decode_multi_workspace_query(L):
+    # 2048-token partitions: 4096-token contexts need (m, l, acc) for 2 partitions of
+    # every (sequence, row, query head).
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 128, desc(nb=4096, n_kv=8)) == 0
+    rows = 4 * 4 * 32 * 2
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 256, desc(nb=4096, n_kv=8)) == 2 * rows * 4 + rows * 128 * 4
+    assert L.pa_decode_multi_workspace_bytes(4, 0, 32, 256, desc(nb=4096, n_kv=8)) == 0
+    assert multi(L, B=0) == PA_OK
