@@ -71,10 +71,10 @@ class Oracle:
         L.oracle_kv_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp, vp]
         L.oracle_kv_append.restype = i64
         L.oracle_decode.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i64, i32,
-                                    vp, i32, vp, f64, vp, i64, vp, i32]
+                                    vp, i32, vp, f64, i32, vp, i64, vp, i32]
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, f64,
-                                     vp, i64, vp, i32]
+                                     i32, vp, i64, vp, i32]
         L.oracle_prefill.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = ctypes.c_int
@@ -115,8 +115,10 @@ class Oracle:
     # -- decode over the paged cache -------------------------------------------
     def decode(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
                block_table: np.ndarray, context_lens: np.ndarray, scale: float,
-               sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
-        """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d]."""
+               sel: np.ndarray | None = None, n_threads: int = 0, window: int = 0) -> np.ndarray:
+        """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d].
+
+        ``window`` W > 0 keeps only the last W positions of each context."""
         for name, a in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
             _check_stored(a, dtype, name)
         B, n_q, d = q.shape
@@ -136,7 +138,7 @@ class Oracle:
             out = np.empty((B, n_q, d), dtype=np.float64)
         rc = self.lib.oracle_decode(_ptr(np.ascontiguousarray(q)), _ptr(k_pool), _ptr(v_pool),
                                     DTYPE_CODES[dtype], B, n_q, n_kv, d, nb, bs, _ptr(bt),
-                                    bt.shape[1], _ptr(ctx), float(scale), _ptr(sel),
+                                    bt.shape[1], _ptr(ctx), float(scale), int(window), _ptr(sel),
                                     0 if sel is None else sel.shape[0], _ptr(out), n_threads)
         if rc != 0:
             raise ValueError("oracle_decode rejected its arguments")
@@ -144,7 +146,8 @@ class Oracle:
 
     # -- prefill over contiguous Q/K/V ---------------------------------------
     def prefill(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, causal: bool,
-                scale: float, sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
+                scale: float, sel: np.ndarray | None = None, n_threads: int = 0,
+                window: int = 0) -> np.ndarray:
         """q [B][S][n_q][d], k/v [B][S][n_kv][d]; returns fp64 [B][S][n_q][d] or [len(sel)][d].
 
         ``sel`` rows are (b, h, i) triples.
@@ -162,7 +165,7 @@ class Oracle:
             out = np.empty((B, S, n_q, d), dtype=np.float64)
         rc = self.lib.oracle_prefill(_ptr(np.ascontiguousarray(q)), _ptr(np.ascontiguousarray(k)),
                                      _ptr(np.ascontiguousarray(v)), DTYPE_CODES[dtype], B, S, n_q,
-                                     n_kv, d, int(bool(causal)), float(scale), _ptr(sel),
+                                     n_kv, d, int(bool(causal)), float(scale), int(window), _ptr(sel),
                                      0 if sel is None else sel.shape[0], _ptr(out), n_threads)
         if rc != 0:
             raise ValueError("oracle_prefill rejected its arguments")
@@ -172,13 +175,15 @@ class Oracle:
     # -- a prompt chunk over its paged prefix ---------------------------------
     def chunked_prefill(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
                         block_table: np.ndarray, context_lens: np.ndarray, scale: float,
-                        sel: np.ndarray | None = None, n_threads: int = 0) -> np.ndarray:
+                        sel: np.ndarray | None = None, n_threads: int = 0,
+                        window: int = 0) -> np.ndarray:
         """q [B][C][n_q][d]; row i of sequence b is position ctx_b - C + i and attends to
         positions 0 .. that position (the causal mask of the prefill pages, aligned at the
         bottom right as chunked prefill keeps the formula unchanged). Each row is the
         decode definition over the first ctx_b - C + i + 1 positions, so this runs
         oracle_decode with one pseudo-sequence per (b, i); rows at negative positions are
-        zero. Returns fp64 [B][C][n_q][d], or [len(sel)][d] for (b, i, h) triples."""
+        zero. With ``window`` W > 0 a row sees only the last W of its positions (the sliding
+        window applies per row). Returns fp64 [B][C][n_q][d], or [len(sel)][d] for (b, i, h)."""
         B, C, n_q, d = q.shape
         bt = np.ascontiguousarray(block_table, dtype=np.int32)
         ctx = np.ascontiguousarray(context_lens, dtype=np.int64)
@@ -189,9 +194,9 @@ class Oracle:
             sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
             sel2 = np.stack([sel[:, 0] * C + sel[:, 1], sel[:, 2]], axis=1)
             return self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
-                               sel=sel2, n_threads=n_threads)
+                               sel=sel2, n_threads=n_threads, window=window)
         out = self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
-                          n_threads=n_threads)
+                          n_threads=n_threads, window=window)
         return out.reshape(B, C, n_q, d)
 
 

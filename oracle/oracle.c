@@ -198,6 +198,9 @@ static int set_threads(int32_t n_threads) {
  * k_pool/v_pool[num_blocks][n_kv][block_size][head_dim]    (dtype)
  * block_table  [batch][max_blocks_per_seq] int32
  * context_lens [batch] int32, tokens attended (0 <= ctx <= max_blocks*bs)
+ * window       0: all ctx positions; W > 0: only the last W of them, positions
+ *              max(0, ctx - W) .. ctx - 1 (sliding-window attention, [IW]
+ *              "KV Cache 的形状与增长": only the most recent W tokens' K, V are kept)
  * sel          optional list of n_sel (b, h) pairs; NULL means every (b, h)
  * out          [batch][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
  * Returns 0, or -1 for invalid arguments or a block id outside the pool.
@@ -206,9 +209,10 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
                   int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
                   int64_t num_blocks, int32_t block_size,
                   const int32_t* block_table, int32_t max_blocks_per_seq,
-                  const int32_t* context_lens, double scale,
+                  const int32_t* context_lens, double scale, int32_t window,
                   const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return -1;
+    if (window < 0) return -1;
     if (elem_bytes_of(dtype) == 0 || batch < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 ||
         num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
         return -1;
@@ -245,13 +249,14 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
         } else {
             for (int32_t c = 0; c < head_dim; ++c)
                 qv[c] = load_elem(q, dtype, ((int64_t)b * n_q + h) * head_dim + c);
-            for (int32_t t = 0; t < ctx; ++t) {
+            const int32_t first = (window > 0 && ctx > window) ? ctx - window : 0;
+            for (int32_t t = first; t < ctx; ++t) {
                 /* block-table translation: logical t -> (physical block, offset) */
                 const int64_t phys = block_table[(int64_t)b * max_blocks_per_seq + t / block_size];
                 const int64_t off = t % block_size;
-                offs[t] = ((phys * n_kv + g) * block_size + off) * head_dim;
+                offs[t - first] = ((phys * n_kv + g) * block_size + off) * head_dim;
             }
-            key_list keys = {k_pool, v_pool, dtype, offs, ctx};
+            key_list keys = {k_pool, v_pool, dtype, offs, ctx - first};
             attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
         }
         free(qv);
@@ -267,13 +272,15 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
  * q   [batch][seq_len][n_q][head_dim], k/v [batch][seq_len][n_kv][head_dim]
  * sel optional list of n_sel (b, h, i) triples; NULL means every (b, i, h)
  * out [batch][seq_len][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
- * Row i attends to keys j <= i when causal, else to all seq_len keys.
+ * Row i attends to keys j <= i when causal, else to all seq_len keys; with
+ * window W > 0 (causal only) to keys max(0, i - W + 1) .. i.
  */
 int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                    int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
-                   int32_t head_dim, int32_t causal, double scale,
+                   int32_t head_dim, int32_t causal, double scale, int32_t window,
                    const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k || !v || !out) return -1;
+    if (window < 0 || (window > 0 && !causal)) return -1;
     if (elem_bytes_of(dtype) == 0 || batch < 0 || seq_len < 0 || n_q <= 0 || n_kv <= 0 ||
         head_dim <= 0)
         return -1;
@@ -301,6 +308,7 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
         }
         const int32_t g = h / group;
         const int32_t n_keys = causal ? i + 1 : seq_len;     /* M_ij = -inf for j > i */
+        const int32_t first = (window > 0 && i + 1 > window) ? i + 1 - window : 0;
 
         double* qv = (double*)malloc(sizeof(double) * (size_t)head_dim);
         double* scores = (double*)malloc(sizeof(double) * (size_t)(n_keys > 0 ? n_keys : 1));
@@ -310,9 +318,9 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
         } else {
             for (int32_t c = 0; c < head_dim; ++c)
                 qv[c] = load_elem(q, dtype, (((int64_t)b * seq_len + i) * n_q + h) * head_dim + c);
-            for (int32_t j = 0; j < n_keys; ++j)
-                offs[j] = (((int64_t)b * seq_len + j) * n_kv + g) * head_dim;
-            key_list keys = {k, v, dtype, offs, n_keys};
+            for (int32_t j = first; j < n_keys; ++j)
+                offs[j - first] = (((int64_t)b * seq_len + j) * n_kv + g) * head_dim;
+            key_list keys = {k, v, dtype, offs, n_keys - first};
             attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
         }
         free(qv);

@@ -490,6 +490,77 @@ def pin_chunked_prefill_rows_before_the_sequence_are_zero(orc):
     close(got[0, 2, 0], vs[0][0, 0], 1e-15, "row at position 0 returns v_0")
 
 
+# ---- sliding window ----------------------------------------------------------------------
+
+def pin_decode_window_equals_decode_over_the_last_w(orc):
+    # The window W keeps positions ctx-W .. ctx-1: the same as an unwindowed decode of
+    # sequences that hold only those rows, packed into a different pool.
+    c = decode_case(50, [21, 9, 40], 4, 2, 8)
+    W = 7
+    got = run_decode(orc, c, window=W)
+    tails = [ks[-W:] for ks in c["ks"]], [vs[-W:] for vs in c["vs"]]
+    kp, bt = pack_pool(tails[0], 4, 12, np.random.default_rng(51), np.float32(np.nan))
+    vp, _ = pack_pool(tails[1], 4, 12, np.random.default_rng(51), np.float32(np.nan))
+    want = orc.decode(c["q"], kp, vp, "f32", bt, np.asarray([min(W, L) for L in (21, 9, 40)], np.int32),
+                      c["scale"])
+    close(got, want, 1e-14, "window W vs decode over the last W rows")
+
+
+def pin_decode_window_one_returns_the_newest_value(orc):
+    c = decode_case(52, [13, 5], 2, 1, 8)
+    got = run_decode(orc, c, window=1)
+    for b, L in enumerate((13, 5)):
+        for h in range(2):
+            assert (got[b, h] == c["vs"][b][L - 1, 0].astype(np.float64)).all()
+
+
+def pin_decode_window_covering_the_context_changes_nothing(orc):
+    c = decode_case(53, [10, 17], 4, 2, 8)
+    assert (run_decode(orc, c, window=17) == run_decode(orc, c)).all()
+    assert (run_decode(orc, c, window=1000) == run_decode(orc, c)).all()
+
+
+def _band(n_rows, n_keys, first_pos, W):
+    pos = first_pos + torch.arange(n_rows)[:, None]
+    j = torch.arange(n_keys)[None, :]
+    return (j <= pos) & (j > pos - W)
+
+
+def pin_prefill_window_matches_library_sdpa_band(orc):
+    B, S, n_q, n_kv, d, W = 2, 23, 4, 2, 8, 6
+    q, k, v = _prefill_inputs(54, B, S, n_q, n_kv, d)
+    got = orc.prefill(q, k, v, "f32", True, 0.3, window=W)
+    G = n_q // n_kv
+    for b in range(B):
+        qq = torch.from_numpy(q[b].astype(np.float64)).transpose(0, 1)
+        kk = torch.from_numpy(k[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        vv = torch.from_numpy(v[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qq.unsqueeze(0), kk.unsqueeze(0), vv.unsqueeze(0), attn_mask=_band(S, S, 0, W), scale=0.3)[0]
+        close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"windowed prefill b={b} vs sdpa band")
+
+
+def pin_chunked_prefill_window_matches_library_sdpa_band(orc):
+    n_q, n_kv, d, C, W = 4, 2, 8, 5, 9
+    g = torch.Generator().manual_seed(55)
+    lens = [14, 30]
+    ks = [stored(torch.randn(L, n_kv, d, generator=g), "f32") for L in lens]
+    vs = [stored(torch.randn(L, n_kv, d, generator=g), "f32") for L in lens]
+    q = stored(torch.randn(len(lens), C, n_q, d, generator=g), "f32")
+    kp, bt = pack_pool(ks, 4, 14, np.random.default_rng(56), np.float32(np.nan))
+    vp, _ = pack_pool(vs, 4, 14, np.random.default_rng(56), np.float32(np.nan))
+    got = orc.chunked_prefill(q, kp, vp, "f32", bt, np.asarray(lens, np.int32), 0.25, window=W)
+    G = n_q // n_kv
+    for b, L in enumerate(lens):
+        qq = torch.from_numpy(q[b].astype(np.float64)).transpose(0, 1)
+        kk = torch.from_numpy(ks[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        vv = torch.from_numpy(vs[b].astype(np.float64)).transpose(0, 1).repeat_interleave(G, 0)
+        want = torch.nn.functional.scaled_dot_product_attention(
+            qq.unsqueeze(0), kk.unsqueeze(0), vv.unsqueeze(0), attn_mask=_band(C, L, L - C, W),
+            scale=0.25)[0]
+        close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"windowed chunk b={b} vs sdpa band")
+
+
 # ---- kv_append ---------------------------------------------------------------------------
 
 def pin_kv_append_hand_worked_fixture(orc):

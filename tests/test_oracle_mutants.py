@@ -44,6 +44,10 @@ MUTANTS = {
     "f16_exponent_bias": ("ldexp((double)(1024 + frac), e - 25)",
                           "ldexp((double)(1024 + frac), e - 24)"),
     "max_tracks_minimum": ("if (scores[t] > m) m = scores[t];", "if (scores[t] < m) m = scores[t];"),
+    "decode_window_one_too_wide": ("(window > 0 && ctx > window) ? ctx - window : 0",
+                                   "(window > 0 && ctx > window) ? ctx - window - 1 : 0"),
+    "prefill_window_one_too_narrow": ("(window > 0 && i + 1 > window) ? i + 1 - window : 0",
+                                      "(window > 0 && i + 1 > window) ? i + 2 - window : 0"),
 }
 
 
