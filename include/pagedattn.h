@@ -17,7 +17,8 @@
  *  [IW] "LLM 推理全过程的维度变化与核心公式", research.frankk.site/notes/
  *       llm-inference-walkthrough: "Decode 阶段维度流转" (append at cache_len, then
  *       read the whole cache; no mask in decode), "Prefill 阶段维度流转",
- *       "KV Cache 的形状与增长" (16-token blocks), "工程优化怎么嵌进公式"
+ *       "KV Cache 的形状与增长" (16-token blocks; sliding window bounding the
+ *       cache at W recent positions), "工程优化怎么嵌进公式"
  *       (Flash Attention online softmax; Flash Decoding split + log-sum-exp).
  *
  * Conventions for every entry point
@@ -32,14 +33,15 @@
  *  - Device-resident metadata (block ids, slots, context lengths) is not read
  *    by the host. Kernels bounds-check it: an out-of-range slot is skipped; a
  *    sequence whose context length exceeds max_blocks_per_seq * block_size or
- *    whose block table names a block outside the pool gets a NaN output row
- *    instead of an out-of-bounds read.
+ *    whose block table names a block outside the pool, among the blocks the
+ *    call reads, gets a NaN output row instead of an out-of-bounds read.
  *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append, the decode
  *    calls (single- and multi-row) and chunked prefill also copy that metadata to the host (synchronising `stream`)
  *    and return PA_ERR_INVALID_ARG, enqueuing nothing, for: a slot past the
  *    pool or repeated within one call; a context length outside
- *    [0, max_blocks_per_seq * block_size]; a block id outside the pool among a
- *    sequence's first ceil(ctx / block_size) table entries; and, for
+ *    [0, max_blocks_per_seq * block_size]; a block id outside the pool among the
+ *    table entries the call reads (a sequence's first ceil(ctx / block_size),
+ *    less those wholly before a sliding window); and, for
  *    decode_append, a slot other than position ctx - 1 of its own sequence or in
  *    a block another sequence of the call also reads.
  */
@@ -98,7 +100,8 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
  * Bytes of scratch memory pa_paged_attn_decode needs for these arguments
  * (partial results of a context split into partitions, [VC]/[IW] Flash Decoding).
  * 0 when every sequence fits in one partition. Returns 0 as well for invalid
- * arguments; the decode call then reports the error.
+ * arguments; the decode call then reports the error. The size covers any
+ * window; a windowed call may need less.
  */
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
                                  const pa_cache_desc* cache);
@@ -116,6 +119,11 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *   context_lens  int32 [batch]: number of positions attended, counting the
  *                 token appended in the same step (positions 0..ctx-1)
  *   scale         multiplies q.k (usually 1/sqrt(head_dim)); must be positive
+ *   window        sliding window ([IW] "KV Cache 的形状与增长", sliding-window item):
+ *                 0 attends to all ctx positions; W > 0 to the last W of them,
+ *                 positions max(0, ctx - W) .. ctx - 1. Block-table entries of
+ *                 blocks wholly before that range are never read, so an engine
+ *                 may recycle them. Negative: PA_ERR_INVALID_ARG.
  *   out           [batch][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes for the same arguments, or NULL: then the workspace
@@ -131,8 +139,8 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                         void* workspace, size_t workspace_bytes, void* stream);
+                         const int32_t* context_lens, float scale, int32_t window, void* out,
+                         pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_decode_append -- one decode step in a single launch: kv_append of
@@ -157,9 +165,9 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
                                 const int64_t* slot_mapping, int32_t batch, int32_t n_q,
                                 void* k_cache, void* v_cache, const pa_cache_desc* cache,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, float scale, void* out,
-                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                const int32_t* context_lens, float scale, int32_t window,
+                                void* out, pa_dtype out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_prefill -- attention of a whole prompt over itself.
@@ -171,13 +179,16 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *   k, v  [batch][seq_len][n_kv][head_dim]  in dtype
  *   causal  1: row i attends to keys 0..i; 0: to all seq_len keys
  *   scale   multiplies q.k (usually 1/sqrt(head_dim)); must be positive
+ *   window  0: no window; W > 0 (causal only) narrows row i to keys
+ *           max(0, i - W + 1) .. i ([IW] sliding-window item). Negative, or
+ *           positive with causal == 0: PA_ERR_INVALID_ARG.
  *   out   [batch][seq_len][n_q][head_dim], out_dtype PA_F32 or dtype
  * Supported: head_dim 128 (and 64); dtype bf16 or f16.
  */
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
-                          int32_t head_dim, int32_t causal, float scale, void* out,
-                          pa_dtype out_dtype, void* stream);
+                          int32_t head_dim, int32_t causal, float scale, int32_t window,
+                          void* out, pa_dtype out_dtype, void* stream);
 
 /*
  * paged_attn_decode_multi -- q_rows new query rows per sequence (speculative
@@ -191,21 +202,25 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  *   k_cache, v_cache  pools described by `cache`, already holding the rows' own
  *                 K/V (pa_kv_append of the q_rows new tokens first)
  *   block_table, context_lens, scale  as for pa_paged_attn_decode
+ *   window        0: none; W > 0: the row at position p attends to positions
+ *                 max(0, p - W + 1) .. p only ([IW] sliding-window item); entries
+ *                 of blocks wholly before the first row's window are never read
  *   out           [batch][q_rows][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  *   workspace     as for pa_paged_attn_decode, sized by pa_decode_multi_workspace_bytes
  * The (query head, row) pairs of one KV head are the N side of matrix-core
  * products, so each K/V byte is read once per step. Rows at negative positions
  * (context_lens[b] < q_rows) are zero; a context past the block table's reach or
- * an out-of-pool block id gives NaN rows. Results equal pa_paged_attn_chunked_prefill
- * with chunk_len = q_rows up to rounding. Supported: head_dim 64 or 128.
+ * an out-of-pool block id among those read gives NaN rows. Results equal
+ * pa_paged_attn_chunked_prefill with chunk_len = q_rows up to rounding. The
+ * workspace size covers any window. Supported: head_dim 64 or 128.
  */
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache);
 int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
                                const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                               void* workspace, size_t workspace_bytes, void* stream);
+                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * paged_attn_chunked_prefill -- a chunk of a prompt attends to the cached prefix
@@ -223,6 +238,9 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  *                 positions 0 .. that position (causal mask aligned at the bottom
  *                 right; chunk_len == context_lens[b] is a plain causal prefill)
  *   scale         multiplies q.k; must be positive
+ *   window        0: none; W > 0: the row at position p attends to positions
+ *                 max(0, p - W + 1) .. p only ([IW] sliding-window item); entries
+ *                 of blocks wholly before the first row's window are never read
  *   out           [batch][chunk_len][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  * Rows at negative positions (context_lens[b] < chunk_len) are zero. A context
  * length past max_blocks_per_seq * block_size, or a block id outside the pool
@@ -232,8 +250,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
-                                  const int32_t* context_lens, float scale, void* out,
-                                  pa_dtype out_dtype, void* stream);
+                                  const int32_t* context_lens, float scale, int32_t window,
+                                  void* out, pa_dtype out_dtype, void* stream);
 
 /*
  * Tuning override for the decode partition size, in tokens (a multiple of 16

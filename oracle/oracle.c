@@ -200,7 +200,8 @@ static int set_threads(int32_t n_threads) {
  * context_lens [batch] int32, tokens attended (0 <= ctx <= max_blocks*bs)
  * window       0: all ctx positions; W > 0: only the last W of them, positions
  *              max(0, ctx - W) .. ctx - 1 (sliding-window attention, [IW]
- *              "KV Cache 的形状与增长": only the most recent W tokens' K, V are kept)
+ *              "KV Cache 的形状与增长", sliding-window item: the cache is bounded at
+ *              W recent positions)
  * sel          optional list of n_sel (b, h) pairs; NULL means every (b, h)
  * out          [batch][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
  * Returns 0, or -1 for invalid arguments or a block id outside the pool.

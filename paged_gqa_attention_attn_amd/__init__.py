@@ -120,8 +120,10 @@ def decode_workspace_bytes(batch: int, n_q: int, max_blocks_per_seq: int,
 def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                       block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                      workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
-    """Decode attention of q [B][n_q][d] over the paged caches; returns out [B][n_q][d]."""
+                      workspace: torch.Tensor | None = None, stream=None,
+                      window: int = 0) -> torch.Tensor:
+    """Decode attention of q [B][n_q][d] over the paged caches; returns out [B][n_q][d].
+    window W > 0 restricts each sequence to its last W positions."""
     L = _lib.load()
     desc = _cache_desc(k_cache)
     if v_cache.shape != k_cache.shape:
@@ -145,7 +147,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
         _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
@@ -156,9 +158,11 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
                              context_lens: torch.Tensor, scale: float,
                              out: torch.Tensor | None = None,
                              out_dtype: torch.dtype = torch.float32,
-                             workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                             workspace: torch.Tensor | None = None, stream=None,
+                             window: int = 0) -> torch.Tensor:
     """One decode step in one launch: write k_new/v_new [B][n_kv][d] at slot_mapping [B],
-    then attend with q [B][n_q][d] over the caches; returns out [B][n_q][d]."""
+    then attend with q [B][n_q][d] over the caches; returns out [B][n_q][d].
+    window W > 0 restricts each sequence to its last W positions."""
     L = _lib.load()
     desc = _cache_desc(k_cache)
     if v_cache.shape != k_cache.shape:
@@ -188,15 +192,17 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
         _dev(slot_mapping, "slot_mapping", torch.int64), B, n_q, _dev(k_cache, "k_cache", dt),
         _dev(v_cache, "v_cache", dt), ctypes.byref(desc),
         _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
 
 def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
                        scale: float, out: torch.Tensor | None = None,
-                       out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
-    """Attention of a prompt over itself: q [B][S][n_q][d], k/v [B][S][n_kv][d]."""
+                       out_dtype: torch.dtype = torch.float32, stream=None,
+                       window: int = 0) -> torch.Tensor:
+    """Attention of a prompt over itself: q [B][S][n_q][d], k/v [B][S][n_kv][d].
+    window W > 0 (causal only) restricts row i to keys i - W + 1 .. i."""
     L = _lib.load()
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("q must be [B][S][n_q][d] and k, v [B][S][n_kv][d]")
@@ -212,7 +218,7 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     dt = q.dtype
     _check("pa_paged_attn_prefill", L.pa_paged_attn_prefill(
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
-        d, int(bool(causal)), float(scale), _dev(out, "out"), _DTYPE[out.dtype],
+        d, int(bool(causal)), float(scale), int(window), _dev(out, "out"), _DTYPE[out.dtype],
         _stream(q, stream)))
     return out
 
@@ -220,9 +226,11 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
 def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                                out: torch.Tensor | None = None,
-                               out_dtype: torch.dtype = torch.float32, stream=None) -> torch.Tensor:
+                               out_dtype: torch.dtype = torch.float32, stream=None,
+                               window: int = 0) -> torch.Tensor:
     """A prompt chunk q [B][C][n_q][d] attends to its paged prefix and causally to itself;
-    row i of sequence b is position context_lens[b] - C + i. Returns out [B][C][n_q][d]."""
+    row i of sequence b is position context_lens[b] - C + i. Returns out [B][C][n_q][d].
+    window W > 0 restricts the row at position p to positions p - W + 1 .. p."""
     L = _lib.load()
     desc = _cache_desc(k_cache)
     if v_cache.shape != k_cache.shape:
@@ -240,7 +248,7 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     _check("pa_paged_attn_chunked_prefill", L.pa_paged_attn_chunked_prefill(
         _dev(q, "q", dt), B, C, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
-        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], _stream(q, stream)))
     return out
 
@@ -248,9 +256,11 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
 def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                             out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
-                            workspace: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+                            workspace: torch.Tensor | None = None, stream=None,
+                            window: int = 0) -> torch.Tensor:
     """q_rows new rows per sequence, q [B][q_rows][n_q][d]; row r of sequence b is position
-    context_lens[b] - q_rows + r. Returns out [B][q_rows][n_q][d]."""
+    context_lens[b] - q_rows + r. Returns out [B][q_rows][n_q][d]. window W > 0 restricts
+    the row at position p to positions p - W + 1 .. p."""
     L = _lib.load()
     desc = _cache_desc(k_cache)
     if v_cache.shape != k_cache.shape:
@@ -274,6 +284,6 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
         _dev(q, "q", dt), B, R, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out

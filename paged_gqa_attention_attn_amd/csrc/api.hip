@@ -142,6 +142,16 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
 
 size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 
+// Blocks one sequence's call can read: all of max_blocks without a window; with
+// window W and `rows` query rows, the W + rows - 1 positions from the first
+// row's window start to the last row, which touch at most (W + rows + 29) / 16
+// blocks of 16 wherever they start. Partition counts and workspaces follow it.
+int32_t span_blocks(int32_t max_blocks, int32_t rows, int32_t window) {
+    if (window <= 0) return max_blocks;
+    const int64_t span = ((int64_t)window + rows - 1 + 2 * (kBlockSize - 1)) / kBlockSize;
+    return (int32_t)std::min<int64_t>(max_blocks, span);
+}
+
 size_t plan_bytes(const Plan& pl) {
     if (pl.ws_floats_m == 0) return 0;
     return 2 * round16(pl.ws_floats_m * sizeof(float)) + pl.ws_floats_acc * sizeof(float);
@@ -225,8 +235,12 @@ int validate_slots(const int64_t* slots_dev, int32_t n, const pa_cache_desc* c, 
     return PA_OK;
 }
 
+// Entries checked per sequence: the blocks the kernels read, i.e. those holding
+// positions first .. ctx - 1, where first is the earliest of `rows` query rows'
+// window start (0 without a window).
 int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev, int32_t max_blocks,
-                    const int32_t* ctx_dev, const int64_t* new_slots_dev, hipStream_t s) {
+                    const int32_t* ctx_dev, const int64_t* new_slots_dev, hipStream_t s,
+                    int32_t rows, int32_t window) {
     std::vector<int32_t> ctx, bt;
     int rc = fetch(ctx, ctx_dev, (size_t)batch, s, "context_lens");
     if (!rc) rc = fetch(bt, bt_dev, (size_t)batch * max_blocks, s, "block_table");
@@ -238,7 +252,8 @@ int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev
             return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: context_lens[%d] = %d is outside [0, %lld]", b,
                         ctx[b], (long long)cap);
         const int32_t nblk = (ctx[b] + c->block_size - 1) / c->block_size;
-        for (int32_t j = 0; j < nblk; ++j) {
+        const int32_t first = window > 0 ? std::max(0, ctx[b] - rows + 1 - window) : 0;
+        for (int32_t j = first / c->block_size; j < nblk; ++j) {
             const int32_t phys = bt[(size_t)b * max_blocks + j];
             if (phys < 0 || phys >= c->num_blocks)
                 return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: block_table[%d][%d] = %d is outside the pool (%d blocks)",
@@ -308,7 +323,7 @@ int resolve_workspace(size_t need, void** ws) {
 
 extern "C" {
 
-int32_t pa_version(void) { return 100; }
+int32_t pa_version(void) { return 200; }
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -375,14 +390,16 @@ struct FusedAppend {
 
 int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, const void* v_cache,
                 const pa_cache_desc* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
-                const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                void* workspace, size_t workspace_bytes, void* stream, const FusedAppend* fa) {
+                const int32_t* context_lens, float scale, int32_t window, void* out,
+                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                const FusedAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "decode: a pointer argument is NULL");
@@ -400,7 +417,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     }
 
     Plan pl;
-    make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
+    make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
     const size_t need = plan_bytes(pl);
     if (need > 0) {
         if (!workspace) {
@@ -414,7 +431,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     }
     if (validate_enabled()) {
         rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens,
-                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream));
+                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream), 1, window);
         if (rc) return rc;
     }
 
@@ -446,6 +463,8 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     a.ring = pl.ring;
     a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
     a.out_f32 = out_dtype == PA_F32;
+    a.q_rows = 1;
+    a.window = window;
     if (fa) {
         a.k_new = fa->k_new;
         a.v_new = fa->v_new;
@@ -466,29 +485,30 @@ extern "C" {
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                         void* workspace, size_t workspace_bytes, void* stream) {
+                         const int32_t* context_lens, float scale, int32_t window, void* out,
+                         pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
-                       context_lens, scale, out, out_dtype, workspace, workspace_bytes, stream,
-                       nullptr);
+                       context_lens, scale, window, out, out_dtype, workspace, workspace_bytes,
+                       stream, nullptr);
 }
 
 int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
                                 const int64_t* slot_mapping, int32_t batch, int32_t n_q,
                                 void* k_cache, void* v_cache, const pa_cache_desc* cache,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,
-                                const int32_t* context_lens, float scale, void* out,
-                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                                void* stream) {
+                                const int32_t* context_lens, float scale, int32_t window,
+                                void* out, pa_dtype out_dtype, void* workspace,
+                                size_t workspace_bytes, void* stream) {
     const FusedAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache};
     return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
-                       context_lens, scale, out, out_dtype, workspace, workspace_bytes, stream, &fa);
+                       context_lens, scale, window, out, out_dtype, workspace, workspace_bytes,
+                       stream, &fa);
 }
 
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
-                          int32_t head_dim, int32_t causal, float scale, void* out,
-                          pa_dtype out_dtype, void* stream) {
+                          int32_t head_dim, int32_t causal, float scale, int32_t window,
+                          void* out, pa_dtype out_dtype, void* stream) {
     if (dtype != PA_BF16 && dtype != PA_F16)
         return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and f16 inputs");
     if (out_dtype != PA_F32 && out_dtype != dtype)
@@ -502,6 +522,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (window > 0 && !causal) return fail(PA_ERR_INVALID_ARG, "a sliding window needs causal == 1");
     if (batch == 0 || seq_len == 0) return PA_OK;
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -520,6 +542,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.causal = causal;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PA_F32;
+    a.window = window;
     const hipError_t e = pa::launch_prefill(a, to_elem(dtype), head_dim, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
         return fail(PA_ERR_UNSUPPORTED, "prefill: no kernel for these arguments");
@@ -536,8 +559,8 @@ size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_
 int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
                                const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, void* out, pa_dtype out_dtype,
-                               void* workspace, size_t workspace_bytes, void* stream) {
+                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
@@ -547,6 +570,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     if (q_rows < 1) return fail(PA_ERR_INVALID_ARG, "q_rows %d must be positive", q_rows);
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: a pointer argument is NULL");
@@ -554,7 +578,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: q, caches and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: block_table and context_lens must be 4-byte aligned");
-    const MultiPlan pl = multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache);
+    const MultiPlan pl = multi_plan(batch, q_rows, n_q, span_blocks(max_blocks_per_seq, q_rows, window), cache);
     if (pl.bytes > 0) {
         if (!workspace) {
             rc = resolve_workspace(pl.bytes, &workspace);
@@ -567,7 +591,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     }
     if (validate_enabled()) {
         rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), q_rows, window);
         if (rc) return rc;
     }
 
@@ -597,6 +621,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = q_rows;
     a.row_groups = pl.row_groups;
+    a.window = window;
     const hipError_t e = pa::launch_decode_multi(a, to_elem(cache->dtype), cache->head_dim,
                                                  static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
@@ -608,8 +633,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
-                                  const int32_t* context_lens, float scale, void* out,
-                                  pa_dtype out_dtype, void* stream) {
+                                  const int32_t* context_lens, float scale, int32_t window,
+                                  void* out, pa_dtype out_dtype, void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
@@ -619,6 +644,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (chunk_len < 0) return fail(PA_ERR_INVALID_ARG, "chunk_len %d < 0", chunk_len);
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (batch == 0 || chunk_len == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
@@ -628,7 +654,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: block_table and context_lens must be 4-byte aligned");
     if (validate_enabled()) {
         rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
-                             static_cast<hipStream_t>(stream));
+                             static_cast<hipStream_t>(stream), chunk_len, window);
         if (rc) return rc;
     }
 
@@ -649,6 +675,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     a.context_lens = context_lens;
     a.max_blocks = max_blocks_per_seq;
     a.num_blocks = cache->num_blocks;
+    a.window = window;
     const hipError_t e = pa::launch_prefill(a, to_elem(cache->dtype), cache->head_dim,
                                             static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)

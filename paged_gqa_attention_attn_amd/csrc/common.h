@@ -26,6 +26,14 @@ struct F16 {
     using storage = uint16_t;
 };
 
+// Sliding window over a paged context of ctx positions whose last `rows` are
+// query rows: the first position any of them attends to (0 without a window).
+// The query at position p sees p - window + 1 .. p, so the earliest row,
+// at ctx - rows, reaches back to ctx - rows - window + 1.
+__device__ __forceinline__ int window_first(int ctx, int rows, int window) {
+    return window > 0 ? max(0, ctx - rows + 1 - window) : 0;
+}
+
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 

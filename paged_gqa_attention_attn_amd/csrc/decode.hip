@@ -31,6 +31,10 @@
 //    whole context writes the output, otherwise it writes (m, l, acc) partials
 //    and the reduce kernel merges them with log-sum-exp weights (Flash
 //    Decoding, same section).
+//  * Sliding window (the walk-through's KV-cache section, sliding-window item,
+//    which bounds the cache at W recent positions): the query at ctx - 1 sees
+//    ctx - W .. ctx - 1. Partitions start at the block holding ctx - W, and
+//    positions of that block before it are masked like those past ctx.
 // Every reduction order depends only on logical positions, never on physical
 // block ids, so relabelling the pool leaves every output bit unchanged.
 #include "common.h"
@@ -123,15 +127,25 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
     const bool ctx_bad = ctx_in > cap;
     const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
+    // Sliding window: the partitions start at the block holding the first
+    // attended position; the table entries of earlier blocks are never read.
+    const int first = window_first(ctx, 1, p.window);
+    const int fb = first / BS;
     const int bpp = p.waves_tok * p.blocks_per_wave;
-    const int nparts = nblk > 0 ? (nblk + bpp - 1) / bpp : 1;
+    const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
     if (part >= nparts) return;  // uniform over the workgroup
-    const int nb = max(0, min(nblk - blk0, p.blocks_per_wave));
+    const int wb0 = blk0 + fb;   // first logical block of this wave
+    if (fb > 0) {                // uniform: the hoisted table read was for blocks from 0
+        my_phys = 0;
+        if (lane < p.blocks_per_wave && wb0 + lane < p.max_blocks)
+            my_phys = p.block_table[(int64_t)b * p.max_blocks + wb0 + lane];
+    }
+    const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
     const bool slot_ok = new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS;
     const int last_blk = ctx > 0 ? (ctx - 1) / BS : -1;
-    const bool patch_here = fused && slot_ok && last_blk >= blk0 && last_blk < blk0 + nb;
+    const bool patch_here = fused && slot_ok && last_blk >= wb0 && last_blk < wb0 + nb;
     const bool writer = fused && slot_ok && part == nparts - 1 && hsgi == 0 && wave == 0;
 
     float m_run[GW], l_run[GW], acc[GW][EPL];
@@ -183,7 +197,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
             if (ahead == 0) wait_vmcnt<0>();
 
             const char* base = ring + (i % R) * 2 * TILE;
-            if (patch_here && blk0 + i == last_blk) {  // uniform: the new token's block
+            if (patch_here && wb0 + i == last_blk) {  // uniform: the new token's block
                 if (lane < 2 * CH) {
                     char* row = ring + (i % R) * 2 * TILE + (lane < CH ? 0 : TILE) +
                                 ((ctx - 1) % BS) * ROW + (lane % CH) * 16;
@@ -202,7 +216,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
             // The slot is free again: start the copy R blocks ahead.
             if (i + R < nb) issue(i + R);
 
-            const int pos0 = (blk0 + i) * BS;
+            const int pos0 = (wb0 + i) * BS;
             float s[GW][NT];
 #pragma unroll
             for (int t = 0; t < NT; ++t) {
@@ -213,10 +227,13 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                     s[hh][t] = group_sum<LPT>(d);   // raw q.k; scaled inside exp2 below
                 }
             }
-            if (pos0 + BS > ctx) {  // last block: positions >= ctx hold unrelated bytes
+            // Last block: positions >= ctx hold unrelated bytes. First block under a
+            // window: positions before `first` are outside it.
+            if (pos0 + BS > ctx || pos0 < first) {
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    if (pos0 + slot + t * TPP >= ctx) {
+                    const int pos = pos0 + slot + t * TPP;
+                    if (pos >= ctx || pos < first) {
 #pragma unroll
                         for (int hh = 0; hh < GW; ++hh) s[hh][t] = -INFINITY;
                         vc[t][0] = make_uint4(0, 0, 0, 0);
@@ -365,8 +382,9 @@ __global__ __launch_bounds__(D) void decode_reduce_kernel(const DecodeArgs p) {
     const int ctx_in = p.context_lens[b];
     const int ctx = (ctx_in < 0 || ctx_in > cap) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
+    const int fb = window_first(ctx, p.q_rows, p.window) / BS;   // as in the partition kernels
     const int bpp = p.waves_tok * p.blocks_per_wave;
-    const int nparts = nblk > 0 ? (nblk + bpp - 1) / bpp : 1;
+    const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
     if (nparts <= 1) return;  // the partition kernel wrote the output itself
 
     const int64_t row = (int64_t)b * p.n_q + h;
@@ -446,6 +464,7 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipSt
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s) {
     if (a.hs_wg * a.waves_tok > MAX_WAVES || a.hs_wg < 1 || a.waves_tok < 1) return hipErrorInvalidValue;
+    if (a.q_rows != 1 || a.window < 0) return hipErrorInvalidValue;   // the reduce kernel reads q_rows
     switch (e) {
     case Elem::F32: return launch_dim<F32>(a, head_dim, s);
     case Elem::BF16: return launch_dim<BF16>(a, head_dim, s);

@@ -26,6 +26,8 @@
 //  * The waves merge (m, l, O) through LDS; a workgroup that covers the whole
 //    context writes the output, otherwise it writes the partition partials that
 //    the decode reduce kernel merges with log-sum-exp weights.
+//  * Sliding window: row r sees positions my_pos - W + 1 .. my_pos; the
+//    partitions start at the block holding the earliest row's window start.
 // Reductions depend only on logical positions, so relabelling physical blocks
 // leaves every output bit unchanged.
 #include "launch.h"
@@ -104,11 +106,21 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     const bool ctx_bad = ctx_in > cap;
     const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
+    // Sliding window: partitions start at the block holding the first position
+    // any row attends to; earlier table entries are never read.
+    const int first = window_first(ctx, R, p.window);
+    const int fb = first / BS;
     const int bpp = WAVES * p.blocks_per_wave;
-    const int nparts = nblk > 0 ? (nblk + bpp - 1) / bpp : 1;
+    const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
     if (part >= nparts) return;  // uniform over the workgroup
-    const int nb = max(0, min(nblk - blk0, p.blocks_per_wave));
-    const int wave_end = min((blk0 + nb) * BS, ctx);   // keys of this wave: [blk0 * 16, wave_end)
+    const int wb0 = blk0 + fb;   // first logical block of this wave
+    if (fb > 0) {                // uniform: the hoisted table read was for blocks from 0
+        my_phys = 0;
+        if (lane < p.blocks_per_wave && wb0 + lane < p.max_blocks)
+            my_phys = p.block_table[(int64_t)b * p.max_blocks + wb0 + lane];
+    }
+    const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
+    const int wave_end = min((wb0 + nb) * BS, ctx);    // keys of this wave: [wb0 * 16, wave_end)
     const int my_pos = ctx - R + r;                      // this row sees keys <= my_pos
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
     // The copies below are invisible to the compiler's wait counting: have it
@@ -126,9 +138,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     const int64_t block_bytes = (int64_t)p.n_kv * BS * T::ROWB;
     const char* kbase = reinterpret_cast<const char*>(p.k_cache) + (int64_t)g * BS * T::ROWB;
     const char* vbase = reinterpret_cast<const char*>(p.v_cache) + (int64_t)g * BS * T::ROWB;
-    const int last_local = (wave_end - 1) / BS - blk0;   // last block of the run holding a key
+    const int last_local = (wave_end - 1) / BS - wb0;    // last block of the run holding a key
 
-    // Tile t of the run (keys blk0 * 16 + 32 t ..) into ring slot t % RING. Copy c
+    // Tile t of the run (keys wb0 * 16 + 32 t ..) into ring slot t % RING. Copy c
     // holds rows c * ROWS_PER_COPY .. of the tile; a row past the run reads the
     // run's last key instead (its score is masked and its V row stays finite).
     auto issue = [&](int t) {
@@ -141,7 +153,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
             const int off = c * 1024 + 16 * lane;
             const int row = off / T::ROWB;
             const int chunk = ((off % T::ROWB) / 16) ^ T::swz(row);
-            const int key = min(blk0 * BS + 32 * t + row, wave_end - 1);
+            const int key = min(wb0 * BS + 32 * t + row, wave_end - 1);
             const int64_t src = phys * block_bytes + (int64_t)(key % BS) * T::ROWB + chunk * 16;
             copy_to_lds16(kbase + src, dst + c * 1024);
             copy_to_lds16(vbase + src, dst + T::BYTES + c * 1024);
@@ -160,6 +172,9 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
     const int row_lim = min(my_pos, wave_end - 1);     // last key this row may use in this run
+    // First key this row may use: its window start (no lower limit without a window).
+    const int row_lo = p.window > 0 ? my_pos - p.window + 1 : 0;
+    const int lo_max = p.window > 0 ? ctx - p.window : 0;   // the last row's window start
 
     if (!phys_bad && ntile > 0) {
         const int pre = min(RING, ntile);
@@ -169,7 +184,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
             else wait_vmcnt<0>();
             const char* kl = ring + (t % RING) * T::SLOT;
             lds_char_t* vl = (lds_char_t*)(kl + T::BYTES);
-            const int key0 = blk0 * BS + 32 * t;
+            const int key0 = wb0 * BS + 32 * t;
 
             f32x16_t sc = f32x16_t{};
             const char* krow = kl + l32 * T::ROWB;
@@ -178,13 +193,14 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
                 const uint4 a = *reinterpret_cast<const uint4*>(krow + ((2 * kk + half) ^ ksw) * 16);
                 sc = Mfma<E>::run(u32x4_t{a.x, a.y, a.z, a.w}, qreg[kk], sc);
             }
-            // Mask keys past the run or past this row's position.
-            if (key0 + BN > wave_end || key0 + BN - 1 > ctx - R) {   // uniform
+            // Mask keys past the run, past this row's position or before its window.
+            if (key0 + BN > wave_end || key0 + BN - 1 > ctx - R || key0 < lo_max) {   // uniform
                 const int lim = row_lim - key0;
+                const int lo = row_lo - key0;
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = (i / 4) * 8 + half * 4 + (i % 4);
-                    sc[i] = key > lim ? -INFINITY : sc[i];
+                    sc[i] = (key > lim || key < lo) ? -INFINITY : sc[i];
                 }
             }
             float tmax = -INFINITY;

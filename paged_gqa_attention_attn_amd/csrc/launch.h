@@ -40,6 +40,9 @@ struct DecodeArgs {
     // served in groups of 32 (query head, row) pairs per KV head (grid.y = n_kv * row_groups).
     int32_t q_rows;
     int32_t row_groups;
+    // Sliding window: 0 attends to the whole context; W > 0 lets the query at
+    // position p see positions max(0, p - W + 1) .. p only.
+    int32_t window;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
@@ -67,6 +70,7 @@ struct PrefillArgs {
     const int32_t* block_table;   // [B][max_blocks]
     const int32_t* context_lens;  // [B]
     int32_t max_blocks, num_blocks;
+    int32_t window;   // sliding window (causal only); 0: none
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);

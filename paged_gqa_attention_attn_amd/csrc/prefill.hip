@@ -38,6 +38,10 @@
 //  * Causal: a workgroup visits key tiles up to its last query; tiles past a
 //    wave's last query are skipped by that wave; the heavy (late) query tiles
 //    are launched first.
+//  * Sliding window (the walk-through's KV-cache section, sliding-window item,
+//    which bounds the cache at W recent positions): the row at position p sees
+//    p - W + 1 .. p. A workgroup starts at the tile holding its first row's
+//    window start, and a wave skips tiles wholly before its first row's.
 #include "launch.h"
 #include "mfma.h"
 
@@ -127,13 +131,23 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                         : p.causal ? (pos_last_wg < 0 ? 0 : min(pos_last_wg, ctx - 1) / BN + 1)
                                    : (ctx + BN - 1) / BN;
     const int pos_last_wave = qbase + min(q0 + WM, S_len) - 1;
+    // Sliding window (causal): row at position p sees p - W + 1 .. p. Tiles wholly
+    // before the workgroup's first row's window are skipped, and no block before
+    // it is read (their table entries may be stale).
+    const int W = p.window;
+    const int wg_lo = W > 0 ? max(0, qbase + qt * BM - W + 1) : 0;
+    const int j0 = min(wg_lo / BN, n_tiles);
+    const int lo_blk = wg_lo / 16;
+    const int wave_lo = pos0 - W + 1;             // window start of this wave's first row
+    const int wave_lo_max = pos_last_wave - W + 1; // ... and of its last row
 
     // This wave's copies of tile j into buffer `buf`: copy c fills bytes
     // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
     // the 16 bytes at 16 l of that, which hold source chunk pos ^ swz(row).
     // A wave's copies cover rows 16 wave .. 16 wave + 15 of the tile, i.e. one
     // whole 16-token cache block when the keys are paged. Rows past the context
-    // read its last row instead (which is in the block the clamped block index
+    // read its last row instead, and rows of blocks wholly before the window
+    // read the window's first row (each in the block the clamped block index
     // names): their keys are masked, and their V rows must be finite because
     // the P V product multiplies them by exactly 0.
     static_assert(T::COPIES * 1024 == 16 * T::ROWB, "a wave copies one 16-row block per tile");
@@ -142,7 +156,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
         const int key0 = j * BN;
         int64_t block_src = 0;
         if constexpr (PAGED) {
-            const int jb = min(key0 / 16 + wave, (ctx - 1) / 16);   // uniform over the wave
+            const int jb = max(min(key0 / 16 + wave, (ctx - 1) / 16), lo_blk);   // uniform over the wave
             int phys = p.block_table[(int64_t)b * p.max_blocks + jb];
             if (phys < 0 || phys >= p.num_blocks) {
                 bad = true;
@@ -155,7 +169,9 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
             const int off = (wave * T::COPIES + c) * 1024 + 16 * lane;
             const int r = off / T::ROWB;
             const int chunk = ((off % T::ROWB) / 16) ^ T::swz(r);
-            const int t = min(key0 + r, ctx - 1);   // the key this lane's row holds
+            // The key this lane's row holds: rows past the context read its last
+            // key, rows before the window its first (both masked, both finite).
+            const int t = max(min(key0 + r, ctx - 1), wg_lo);
             const int64_t src = PAGED ? block_src + (int64_t)(t % 16) * T::ROWB + chunk * 16
                                       : (int64_t)t * kv_row + chunk * 16;
             const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
@@ -184,13 +200,14 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
 
-    if (n_tiles > 0) issue_tile(0, 0);
-    for (int j = 0; j < n_tiles; ++j) {
+    if (n_tiles > j0) issue_tile(j0, j0 & 1);
+    for (int j = j0; j < n_tiles; ++j) {
         wait_vmcnt<0>();   // this wave's copies of tile j have landed
         __syncthreads();   // so have the other waves'; all are done with tile j - 1
         if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
         const int key0 = j * BN;
         if (p.causal && key0 > pos_last_wave) continue;   // uniform over the wave
+        if (W > 0 && key0 + BN - 1 < wave_lo) continue;   // wholly before every row's window
 
         const char* kl = smem + (j & 1) * T::BUF;
         lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
@@ -208,15 +225,17 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
             sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
         }
 
-        // Mask keys past this lane's query (causal) or past the prompt.
-        if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0)) {   // uniform
+        // Mask keys past this lane's query (causal), past the prompt, or before
+        // this lane's window.
+        if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0) || (W > 0 && key0 < wave_lo_max)) {   // uniform
             const int lim = (p.causal ? min(my_pos, ctx - 1) : ctx - 1) - key0;
+            const int lo = (W > 0 ? my_pos - W + 1 : 0) - key0;
 #pragma unroll
             for (int st = 0; st < 2; ++st)
 #pragma unroll
                 for (int i = 0; i < 16; ++i) {
                     const int key = st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                    sc[st][i] = key > lim ? -INFINITY : sc[st][i];
+                    sc[st][i] = (key > lim || key < lo) ? -INFINITY : sc[st][i];
                 }
         }
         float tmax = -INFINITY;

@@ -44,15 +44,15 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 100
+    assert L.pa_version() == 200
 
 
 def decode(L, **kw):
     a = dict(q=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode(a["q"], a["batch"], a["n_q"], a["k"], a["v"], a["cache"],
-                                  a["bt"], a["maxb"], a["ctx"], a["scale"], a["out"],
+                                  a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
                                   a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -73,7 +73,9 @@ def decode(L, **kw):
     (dict(scale=float("nan")), INVALID, "scale"),
     (dict(scale=0.0), INVALID, "positive"),
     (dict(scale=-0.125), INVALID, "positive"),
+    (dict(window=-1), INVALID, "window"),
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),   # too small (NULL: library's own)
+    (dict(maxb=8192, window=4096, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
 ])
 def test_decode_rejects(L, kw, code, msg):
     assert decode(L, **kw) == code
@@ -86,12 +88,12 @@ def test_decode_empty_batch_is_a_noop(L):
 
 def decode_append(L, **kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(),
-             bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None,
-             ws_bytes=0, stream=None)
+             bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32,
+             ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode_append(a["q"], a["kn"], a["vn"], a["slots"], a["batch"],
                                          a["n_q"], a["k"], a["v"], a["cache"], a["bt"], a["maxb"],
-                                         a["ctx"], a["scale"], a["out"], a["out_dtype"], a["ws"],
+                                         a["ctx"], a["scale"], a["window"], a["out"], a["out_dtype"], a["ws"],
                                          a["ws_bytes"], a["stream"])
 
 
@@ -102,6 +104,7 @@ def decode_append(L, **kw):
     (dict(slots=FAKE + 4), INVALID, "aligned"),
     (dict(cache=desc(bs=32)), UNSUPPORTED, "block_size"),
     (dict(n_q=5), INVALID, "multiple"),
+    (dict(window=-3), INVALID, "window"),
 ])
 def test_decode_append_rejects(L, kw, code, msg):
     assert decode_append(L, **kw) == code
@@ -162,10 +165,10 @@ def test_append_zero_tokens_is_a_noop(L):
 
 def prefill(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=_lib.PA_BF16, B=1, S=64, n_q=8, n_kv=2, d=128,
-             causal=1, scale=0.1, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+             causal=1, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
     a.update(kw)
     return L.pa_paged_attn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["S"], a["n_q"],
-                                   a["n_kv"], a["d"], a["causal"], a["scale"], a["out"],
+                                   a["n_kv"], a["d"], a["causal"], a["scale"], a["window"], a["out"],
                                    a["out_dtype"], a["stream"])
 
 
@@ -180,6 +183,8 @@ def prefill(L, **kw):
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED),
     (dict(scale=0.0), INVALID),
     (dict(scale=-1.0), INVALID),
+    (dict(window=-1), INVALID),
+    (dict(window=8, causal=0), INVALID),    # a window is a causal band
 ])
 def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
@@ -192,11 +197,11 @@ def test_prefill_empty_is_a_noop(L):
 
 def chunked(L, **kw):
     a = dict(q=FAKE, B=2, C=16, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
     a.update(kw)
     return L.pa_paged_attn_chunked_prefill(a["q"], a["B"], a["C"], a["n_q"], a["k"], a["v"],
                                            a["cache"], a["bt"], a["maxb"], a["ctx"], a["scale"],
-                                           a["out"], a["out_dtype"], a["stream"])
+                                           a["window"], a["out"], a["out_dtype"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -210,6 +215,7 @@ def chunked(L, **kw):
     (dict(out=MISALIGNED), INVALID, "aligned"),
     (dict(ctx=FAKE + 2), INVALID, "aligned"),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+    (dict(window=-1), INVALID, "window"),
 ])
 def test_chunked_prefill_rejects(L, kw, code, msg):
     assert chunked(L, **kw) == code
@@ -223,10 +229,10 @@ def test_chunked_prefill_empty_is_a_noop(L):
 
 def multi(L, **kw):
     a = dict(q=FAKE, B=2, R=4, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode_multi(a["q"], a["B"], a["R"], a["n_q"], a["k"], a["v"], a["cache"],
-                                        a["bt"], a["maxb"], a["ctx"], a["scale"], a["out"],
+                                        a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
                                         a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -239,6 +245,8 @@ def multi(L, **kw):
     (dict(v=None), INVALID, "NULL"),
     (dict(q=MISALIGNED), INVALID, "aligned"),
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
+    (dict(maxb=8192, window=4096, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
+    (dict(window=-1), INVALID, "window"),
 ])
 def test_decode_multi_rejects(L, kw, code, msg):
     assert multi(L, **kw) == code
