@@ -8,7 +8,9 @@ the 32 new tokens + paged decode attention over the 2048-token contexts.
 
 Other workloads (``--workload``): the 70B-shaped long-context decode
 (B=8, n_q=64, ctx 32768), the variable-length batch with a shared prefix, the
-tiny fp32 case, and the causal prefill + cache write + first decode step.
+tiny fp32 case, the causal prefill + cache write + first decode step, chunked
+prefill over a paged prefix, multi-row (speculative) decode, and sliding-window
+decode (the 8B shape over 16384-token contexts, window 4096).
 
 Timing: ``--warmup`` untimed steps, then exactly ``--steps`` timed steps between
 two ``torch.cuda.synchronize()`` calls. Steps rotate over ``--sets``
@@ -40,6 +42,7 @@ WORKLOADS = {
     "prefill_then_decode": 5,
     "chunked_prefill": 6,
     "decode_multi_8b": 7,
+    "decode_window_8b": 8,
     "copy_calibration": 0,
 }
 
@@ -95,7 +98,7 @@ def _stored(t):
     return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
 
 
-def cpu_baseline_decode(case, target_s: float):
+def cpu_baseline_decode(case, target_s: float, window: int = 0):
     """Time the CPU oracle on whole sequences of one input set (all heads)."""
     import numpy as np
 
@@ -111,7 +114,7 @@ def cpu_baseline_decode(case, target_s: float):
     def run(seqs):
         sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
         t0 = time.perf_counter()
-        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel)
+        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel, window=window)
         return time.perf_counter() - t0
 
     t1 = run([0])
@@ -120,7 +123,7 @@ def cpu_baseline_decode(case, target_s: float):
     t_all = run(seqs)
     reps = max(1, int(target_s / max(t_all, 1e-6))) if n == case.batch else 1
     dt = t_all + sum(run(seqs) for _ in range(reps - 1))
-    kv = reps * acc.decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim, elem)
+    kv = reps * acc.decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim, elem, window)
     return {
         "value": round(kv / dt / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
         "kind": "oracle",
@@ -165,8 +168,14 @@ def bench_decode(args, cfg: int):
     from paged_gqa_attention_attn_amd import accounting as acc
     from paged_gqa_attention_attn_amd import workloads as wl
 
-    seed0 = wl.CONFIG_SEEDS[cfg]
-    sets = [wl.make_config(cfg, device="cuda", seed=seed0 + 1000 * i) for i in range(args.sets)]
+    if cfg == 8:
+        win = wl.WINDOW_TOKENS
+        sets = [wl.make_window_decode_case(device="cuda", seed=wl.WINDOW_CASE_SEED + 1000 * i)
+                for i in range(args.sets)]
+    else:
+        win = 0
+        seed0 = wl.CONFIG_SEEDS[cfg]
+        sets = [wl.make_config(cfg, device="cuda", seed=seed0 + 1000 * i) for i in range(args.sets)]
     c0 = sets[0]
     if args.partition_tokens:
         pa.set_decode_partition_tokens(args.partition_tokens)
@@ -185,11 +194,11 @@ def bench_decode(args, cfg: int):
     def decode(s):
         if args.unfused:
             pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
-                                 out=out, workspace=ws)
+                                 out=out, workspace=ws, window=win)
         else:
             pa.paged_attn_decode_append(s.q, s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool,
                                         s.block_table, s.context_lens, s.scale, out=out,
-                                        workspace=ws)
+                                        workspace=ws, window=win)
 
     for i in range(args.warmup):
         step(i)
@@ -225,7 +234,7 @@ def bench_decode(args, cfg: int):
     per = sorted(a.elapsed_time(b) * 1e3 for a, b in pairs)
     pct = {f"p{q}": round(per[min(len(per) - 1, int(q / 100 * len(per)))], 2) for q in (10, 50, 90)}
 
-    kv = sum(acc.decode_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim, elem)
+    kv = sum(acc.decode_kv_bytes(s.context_lens.cpu().tolist(), s.n_kv, s.head_dim, elem, win)
              for s in sets) / len(sets)
     io = acc.decode_io_bytes(c0.batch, c0.n_q, c0.head_dim, elem, 4, c0.max_blocks_per_seq)
     achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
@@ -249,7 +258,9 @@ def bench_decode(args, cfg: int):
             "head_dim": c0.head_dim, "block_size": c0.block_size,
             "context_lens": "2048 each" if cfg == 2 else
             ("32768 each" if cfg == 4 else ("U[128,8192], 16 sharers of a 1024-token prefix"
-                                            if cfg == 3 else "{7, 33}")),
+                                            if cfg == 3 else
+                                            ("16384 each" if cfg == 8 else "{7, 33}"))),
+            "window": win,
             "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
             "step": ("kv_append of one new token per sequence, then paged decode (two launches)"
                      if args.unfused else
@@ -272,10 +283,10 @@ def bench_decode(args, cfg: int):
                                               elem, s.shared_prefix_blocks * 16, len(s.sharers))
                    for s in sets) / len(sets)
         rec["unique_kv_gbs"] = round(uniq / (ms * 1e-3) / 1e9, 2)
-    flops = acc.decode_flops(c0.context_lens.cpu().tolist(), c0.n_q, c0.head_dim)
+    flops = acc.decode_flops(c0.context_lens.cpu().tolist(), c0.n_q, c0.head_dim, win)
     rec["tflops"] = round(flops / (dec_ms * 1e-3) / 1e12, 3)
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline_decode(c0, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline_decode(c0, args.cpu_seconds, win)
     return rec
 
 

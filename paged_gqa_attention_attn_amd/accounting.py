@@ -25,9 +25,16 @@ def kv_cache_bytes(layers: int, tokens: int, n_kv: int, head_dim: int, elem_byte
     return 2 * layers * tokens * n_kv * head_dim * elem_bytes
 
 
-def decode_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int, elem_bytes: int) -> int:
+def attended(ctx: int, window: int = 0) -> int:
+    """Positions one decode query attends to: all ctx, or the last ``window`` of them."""
+    return min(int(ctx), window) if window > 0 else int(ctx)
+
+
+def decode_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int, elem_bytes: int,
+                    window: int = 0) -> int:
     """K/V bytes one decode step must read: every attended position, every KV head, once."""
-    return sum(kv_cache_bytes(1, int(c), n_kv, head_dim, elem_bytes) for c in context_lens)
+    return sum(kv_cache_bytes(1, attended(c, window), n_kv, head_dim, elem_bytes)
+               for c in context_lens)
 
 
 def decode_unique_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int,
@@ -46,9 +53,9 @@ def decode_io_bytes(batch: int, n_q: int, head_dim: int, elem_bytes: int, out_by
             + batch * 4)
 
 
-def decode_flops(context_lens: Iterable[int], n_q: int, head_dim: int) -> int:
+def decode_flops(context_lens: Iterable[int], n_q: int, head_dim: int, window: int = 0) -> int:
     """QK^T plus PV: 2 * 2 * n_q * ctx * d per sequence (one query row)."""
-    return sum(4 * n_q * int(c) * head_dim for c in context_lens)
+    return sum(4 * n_q * attended(c, window) * head_dim for c in context_lens)
 
 
 def prefill_flops_causal(batch: int, seq_len: int, n_q: int, head_dim: int) -> int:

@@ -347,6 +347,20 @@ CONFIG_NAMES = {
 }
 
 
+# Sliding-window decode: the decode_8b shape over 16384-token contexts, each query
+# restricted to its last WINDOW_TOKENS positions.
+WINDOW_TOKENS = 4096
+WINDOW_CASE_NAME = "sliding_window_decode_b32_ctx16384_w4096"
+WINDOW_CASE_SEED = 1008
+
+
+def make_window_decode_case(device="cpu", seed: int | None = None, values: bool = True):
+    """B=32, n_q=32, n_kv=8, d=128, bf16, every context 16384; attend with window=WINDOW_TOKENS."""
+    return make_decode_case(batch=32, n_q=32, n_kv=8, head_dim=128, context_lens=[16384] * 32,
+                            dtype="bf16", seed=WINDOW_CASE_SEED if seed is None else seed,
+                            device=device, name=WINDOW_CASE_NAME, values=values)
+
+
 def varlen_context_lens(seed: int, batch: int = 64, lo: int = 128, hi: int = 8192) -> np.ndarray:
     """Context lengths drawn uniformly from the integers [lo, hi]."""
     return np.random.default_rng(seed + 7).integers(lo, hi + 1, size=batch)

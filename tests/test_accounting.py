@@ -63,3 +63,12 @@ def test_chunked_prefill_flops():
     assert acc.chunked_prefill_flops([5], 2, 1, 1) == 4 * 9
     # ctx 2, chunk 4: rows at positions -2, -1 see nothing; 0 and 1 see 1 and 2 keys.
     assert acc.chunked_prefill_flops([2], 4, 1, 1) == 4 * 3
+
+
+def test_windowed_decode_bytes_and_flops():
+    # Window 4096 over 16384-token contexts reads a quarter of the cache; a window wider
+    # than the context changes nothing.
+    assert acc.decode_kv_bytes([16384] * 32, 8, 128, 2, window=4096) == 32 * 4096 * 4096   # 512 MiB
+    assert acc.decode_kv_bytes([100, 5000], 8, 128, 2, window=4096) == (100 + 4096) * 4096
+    assert acc.decode_flops([16384], 32, 128, window=4096) == acc.decode_flops([4096], 32, 128)
+    assert acc.decode_flops([10], 1, 1, window=0) == 40
