@@ -11,7 +11,9 @@ arrays of stored bit patterns to pointers. Every function cites, in
 ``oracle.c``, the page passage it follows.
 
 Arrays are passed as numpy arrays holding the exact stored values:
-``float32`` for fp32, and ``uint16`` bit patterns for bf16 and fp16.
+``float32`` for fp32, ``uint16`` bit patterns for bf16 and fp16, and one-byte
+codes for a quantised cache (``uint8`` for FP8 E4M3, ``int8`` for INT8) with
+its ``float32`` per-row scales.
 """
 from __future__ import annotations
 
@@ -25,13 +27,15 @@ _HERE = Path(__file__).resolve().parent
 SOURCE = _HERE / "oracle.c"
 LIB_PATH = _HERE / "liboracle.so"
 
-DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2}
-ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2}
+DTYPE_CODES = {"f32": 0, "bf16": 1, "f16": 2, "fp8": 3, "int8": 4}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int8": 1}
+QUANTISED = ("fp8", "int8")
+_STORED = {"f32": np.float32, "bf16": np.uint16, "f16": np.uint16, "fp8": np.uint8, "int8": np.int8}
 
 
 def compile_library(source: Path = SOURCE, out: Path = LIB_PATH, extra_flags=()) -> Path:
     """Compile ``source`` into a shared library with gcc (OpenMP on)."""
-    cmd = ["gcc", "-O2", "-std=c99", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
+    cmd = ["gcc", "-O2", "-std=c99", "-ffp-contract=off", "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wextra",
            *extra_flags, str(source), "-o", str(out), "-lm"]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     return out
@@ -51,7 +55,7 @@ def _ptr(a: np.ndarray | None):
 
 
 def _check_stored(a: np.ndarray, dtype: str, name: str) -> None:
-    want = np.float32 if dtype == "f32" else np.uint16
+    want = _STORED[dtype]
     if a.dtype != want:
         raise TypeError(f"{name}: dtype {dtype} is passed as {np.dtype(want).name}, got {a.dtype}")
 
@@ -73,6 +77,16 @@ class Oracle:
         L.oracle_decode.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i64, i32,
                                     vp, i32, vp, f64, i32, vp, i64, vp, i32]
         L.oracle_decode.restype = ctypes.c_int
+        L.oracle_decode_ex.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, i32, i32, i32,
+                                       i32, i64, i32, vp, i32, vp, f64, i32, vp, i64, vp, i32]
+        L.oracle_decode_ex.restype = ctypes.c_int
+        L.oracle_encode_fp8_e4m3.argtypes = [vp, i64, vp]
+        L.oracle_encode_fp8_e4m3.restype = ctypes.c_int
+        L.oracle_quantize_rows.argtypes = [vp, ctypes.c_int, i64, i32, ctypes.c_int, vp, vp]
+        L.oracle_quantize_rows.restype = ctypes.c_int
+        L.oracle_kv_append_quant.argtypes = [vp, vp, ctypes.c_int, vp, i64, i32, i32, ctypes.c_int,
+                                             i64, i32, vp, vp, vp, vp]
+        L.oracle_kv_append_quant.restype = i64
         L.oracle_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, f64,
                                      i32, vp, i64, vp, i32]
         L.oracle_prefill.restype = ctypes.c_int
@@ -112,15 +126,74 @@ class Oracle:
             raise ValueError("oracle_kv_append rejected its arguments (slot out of range?)")
         return int(n)
 
+    # -- per-token quantisation (fp32 steps) -----------------------------------
+    def encode_fp8(self, y: np.ndarray) -> np.ndarray:
+        """Nearest OCP E4M3 code (ties to even) of each float32 y, |y| <= 448."""
+        y = np.ascontiguousarray(y, dtype=np.float32)
+        out = np.empty(y.shape, dtype=np.uint8)
+        if self.lib.oracle_encode_fp8_e4m3(_ptr(y), y.size, _ptr(out)) != 0:
+            raise ValueError("oracle_encode_fp8_e4m3: values must be finite with |y| <= 448")
+        return out
+
+    def quantize_rows(self, x: np.ndarray, src_dtype: str, fmt: str):
+        """Rows x [..., d] (stored values of src_dtype) -> (codes [..., d], scales [...])."""
+        _check_stored(x, src_dtype, "x")
+        x = np.ascontiguousarray(x)
+        d = x.shape[-1]
+        codes = np.empty(x.shape, dtype=_STORED[fmt])
+        scales = np.empty(x.shape[:-1], dtype=np.float32)
+        rc = self.lib.oracle_quantize_rows(_ptr(x), DTYPE_CODES[src_dtype], x.size // d, d,
+                                           DTYPE_CODES[fmt], _ptr(codes), _ptr(scales))
+        if rc != 0:
+            raise ValueError("oracle_quantize_rows rejected its arguments")
+        return codes, scales
+
+    def kv_append_quant(self, k: np.ndarray, v: np.ndarray, src_dtype: str,
+                        slot_mapping: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
+                        k_scale: np.ndarray, v_scale: np.ndarray, fmt: str) -> int:
+        """Quantise k, v [T][n_kv][d] per row into code pools [nb][n_kv][bs][d] and scale
+        pools [nb][n_kv][bs] (in place) at slot_mapping [T]."""
+        _check_stored(k, src_dtype, "k")
+        _check_stored(v, src_dtype, "v")
+        for name, a in (("k_pool", k_pool), ("v_pool", v_pool)):
+            _check_stored(a, fmt, name)
+        T, n_kv, d = k.shape
+        nb, n_kv2, bs, d2 = k_pool.shape
+        if (v.shape != k.shape or v_pool.shape != k_pool.shape or n_kv2 != n_kv or d2 != d
+                or k_scale.shape != (nb, n_kv, bs) or v_scale.shape != k_scale.shape):
+            raise ValueError("shape mismatch")
+        if k_scale.dtype != np.float32 or v_scale.dtype != np.float32:
+            raise TypeError("scales are float32")
+        slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        if slots.shape != (T,):
+            raise ValueError("slot_mapping must have one entry per token")
+        n = self.lib.oracle_kv_append_quant(_ptr(np.ascontiguousarray(k)), _ptr(np.ascontiguousarray(v)),
+                                            DTYPE_CODES[src_dtype], _ptr(slots), T, n_kv, d,
+                                            DTYPE_CODES[fmt], nb, bs, _ptr(k_pool), _ptr(v_pool),
+                                            _ptr(k_scale), _ptr(v_scale))
+        if n < 0:
+            raise ValueError("oracle_kv_append_quant rejected its arguments (slot out of range?)")
+        return int(n)
+
     # -- decode over the paged cache -------------------------------------------
     def decode(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
                block_table: np.ndarray, context_lens: np.ndarray, scale: float,
-               sel: np.ndarray | None = None, n_threads: int = 0, window: int = 0) -> np.ndarray:
+               sel: np.ndarray | None = None, n_threads: int = 0, window: int = 0,
+               q_dtype: str | None = None, k_scale: np.ndarray | None = None,
+               v_scale: np.ndarray | None = None) -> np.ndarray:
         """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d].
 
-        ``window`` W > 0 keeps only the last W positions of each context."""
-        for name, a in (("q", q), ("k_pool", k_pool), ("v_pool", v_pool)):
+        ``window`` W > 0 keeps only the last W positions of each context. For a quantised
+        cache (``dtype`` "fp8" or "int8") pass ``q_dtype`` and the [nb][n_kv][bs] scales."""
+        q_dtype = q_dtype or dtype
+        _check_stored(q, q_dtype, "q")
+        for name, a in (("k_pool", k_pool), ("v_pool", v_pool)):
             _check_stored(a, dtype, name)
+        if dtype in QUANTISED:
+            for name, a in (("k_scale", k_scale), ("v_scale", v_scale)):
+                if a is None or a.dtype != np.float32 or a.shape != k_pool.shape[:3]:
+                    raise ValueError(f"{name} must be float32 [nb][n_kv][bs]")
+            k_scale, v_scale = np.ascontiguousarray(k_scale), np.ascontiguousarray(v_scale)
         B, n_q, d = q.shape
         nb, n_kv, bs, d2 = k_pool.shape
         if d2 != d or v_pool.shape != k_pool.shape:
@@ -136,10 +209,13 @@ class Oracle:
             out = np.empty((sel.shape[0], d), dtype=np.float64)
         else:
             out = np.empty((B, n_q, d), dtype=np.float64)
-        rc = self.lib.oracle_decode(_ptr(np.ascontiguousarray(q)), _ptr(k_pool), _ptr(v_pool),
-                                    DTYPE_CODES[dtype], B, n_q, n_kv, d, nb, bs, _ptr(bt),
-                                    bt.shape[1], _ptr(ctx), float(scale), int(window), _ptr(sel),
-                                    0 if sel is None else sel.shape[0], _ptr(out), n_threads)
+        rc = self.lib.oracle_decode_ex(_ptr(np.ascontiguousarray(q)), DTYPE_CODES[q_dtype],
+                                       _ptr(np.ascontiguousarray(k_pool)),
+                                       _ptr(np.ascontiguousarray(v_pool)), DTYPE_CODES[dtype],
+                                       _ptr(k_scale), _ptr(v_scale), B, n_q, n_kv, d, nb, bs,
+                                       _ptr(bt), bt.shape[1], _ptr(ctx), float(scale), int(window),
+                                       _ptr(sel), 0 if sel is None else sel.shape[0], _ptr(out),
+                                       n_threads)
         if rc != 0:
             raise ValueError("oracle_decode rejected its arguments")
         return out
@@ -176,7 +252,7 @@ class Oracle:
     def chunked_prefill(self, q: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray, dtype: str,
                         block_table: np.ndarray, context_lens: np.ndarray, scale: float,
                         sel: np.ndarray | None = None, n_threads: int = 0,
-                        window: int = 0) -> np.ndarray:
+                        window: int = 0, **quant) -> np.ndarray:
         """q [B][C][n_q][d]; row i of sequence b is position ctx_b - C + i and attends to
         positions 0 .. that position (the causal mask of the prefill pages, aligned at the
         bottom right as chunked prefill keeps the formula unchanged). Each row is the
@@ -194,9 +270,9 @@ class Oracle:
             sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
             sel2 = np.stack([sel[:, 0] * C + sel[:, 1], sel[:, 2]], axis=1)
             return self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
-                               sel=sel2, n_threads=n_threads, window=window)
+                               sel=sel2, n_threads=n_threads, window=window, **quant)
         out = self.decode(q2, k_pool, v_pool, dtype, bt2, rows_ctx.reshape(-1), scale,
-                          n_threads=n_threads, window=window)
+                          n_threads=n_threads, window=window, **quant)
         return out.reshape(B, C, n_q, d)
 
 
@@ -233,9 +309,22 @@ def upcast(*args, **kwargs):
     return get().upcast(*args, **kwargs)
 
 
+def encode_fp8(*args, **kwargs):
+    return get().encode_fp8(*args, **kwargs)
+
+
+def quantize_rows(*args, **kwargs):
+    return get().quantize_rows(*args, **kwargs)
+
+
+def kv_append_quant(*args, **kwargs):
+    return get().kv_append_quant(*args, **kwargs)
+
+
 def max_threads() -> int:
     return get().max_threads()
 
 
 __all__ = ["Oracle", "build", "compile_library", "get", "decode", "prefill", "kv_append",
-           "upcast", "max_threads", "DTYPE_CODES", "ELEM_BYTES", "LIB_PATH", "SOURCE"]
+           "upcast", "encode_fp8", "quantize_rows", "kv_append_quant", "max_threads",
+           "DTYPE_CODES", "ELEM_BYTES", "QUANTISED", "LIB_PATH", "SOURCE"]

@@ -41,9 +41,19 @@
  * block table and a slot mapping; [IW] decode step "write the KV cache at the
  * next position").
  *
+ * Quantised cache ([IW] "KV Cache 的形状与增长", INT8 / FP8 item: the fp16
+ * cache is quantised to int8 or fp8 per channel or per token; the
+ * dimension-walkthrough page's KV-size formula counts FP8 as one byte):
+ * each (token, KV head) row of K and of V is stored as one-byte codes and one
+ * fp32 scale, value = code * scale. The quantiser is per token (one scale per
+ * row, symmetric, absolute maximum); its fp32 steps are spelled out at
+ * oracle_quantize_rows. FP8 is the OCP E4M3 ("fn") format: 1 sign bit, 4
+ * exponent bits with bias 7, 3 fraction bits, no infinities, one NaN
+ * pattern per sign, largest finite value 448.
+ *
  * Inputs arrive as the exact stored values (fp32, bf16 or fp16 bit
- * patterns) and are widened to fp64 exactly, so input rounding is not
- * counted as error.
+ * patterns, or one-byte codes) and are widened to fp64 exactly, so input
+ * rounding is not counted as error.
  */
 #include <math.h>
 #include <stdint.h>
@@ -54,7 +64,7 @@
 #endif
 
 /* element type codes understood by this file */
-enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2 };
+enum { ORACLE_F32 = 0, ORACLE_BF16 = 1, ORACLE_F16 = 2, ORACLE_FP8E4M3 = 3, ORACLE_INT8 = 4 };
 
 /* ---- exact widening of stored values to fp64 ---------------------------- */
 
@@ -82,19 +92,121 @@ static double widen_f16(uint16_t h) {
     return sign ? -mag : mag;
 }
 
+/* OCP FP8 E4M3: sign, exponent e (bias 7), fraction m. e = 0 is subnormal
+ * (m * 2^-9); e = 15 with m = 7 is NaN; otherwise (8 + m) * 2^(e - 10). */
+static double widen_fp8_e4m3(uint8_t c) {
+    const int sign = c >> 7;
+    const int e = (c >> 3) & 15;
+    const int m = c & 7;
+    double mag;
+    if (e == 15 && m == 7) return NAN;
+    if (e == 0) mag = ldexp((double)m, -9);
+    else mag = ldexp((double)(8 + m), e - 10);
+    return sign ? -mag : mag;
+}
+
 static int elem_bytes_of(int dtype) {
     switch (dtype) {
     case ORACLE_F32: return 4;
     case ORACLE_BF16: return 2;
     case ORACLE_F16: return 2;
+    case ORACLE_FP8E4M3: return 1;
+    case ORACLE_INT8: return 1;
     default: return 0;
     }
 }
 
+static int is_quantised(int dtype) { return dtype == ORACLE_FP8E4M3 || dtype == ORACLE_INT8; }
+
 static double load_elem(const void* base, int dtype, int64_t idx) {
-    if (dtype == ORACLE_F32) return (double)((const float*)base)[idx];
-    if (dtype == ORACLE_BF16) return widen_bf16(((const uint16_t*)base)[idx]);
-    return widen_f16(((const uint16_t*)base)[idx]);
+    switch (dtype) {
+    case ORACLE_F32: return (double)((const float*)base)[idx];
+    case ORACLE_BF16: return widen_bf16(((const uint16_t*)base)[idx]);
+    case ORACLE_FP8E4M3: return widen_fp8_e4m3(((const uint8_t*)base)[idx]);
+    case ORACLE_INT8: return (double)((const int8_t*)base)[idx];
+    default: return widen_f16(((const uint16_t*)base)[idx]);
+    }
+}
+
+/* ---- per-token quantisation (fp32 steps, as stored) ---------------------- */
+
+/* Nearest E4M3 code of a finite y with |y| <= 448, ties to the even code. */
+static uint8_t encode_fp8_e4m3(float y) {
+    const uint8_t sign = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: a = m * 2^-9; m = 8 is the smallest normal, code 8 */
+        return sign | (uint8_t)nearbyint(ldexp(a, 9));
+    }
+    int e2;
+    const double fr = frexp(a, &e2);          /* a = fr * 2^e2, fr in [0.5, 1) */
+    int e = e2 - 1;                           /* a = (2 fr) * 2^e, 2 fr in [1, 2) */
+    double q = nearbyint((2.0 * fr - 1.0) * 8.0);   /* fraction in eighths */
+    if (q == 8.0) {
+        q = 0.0;
+        ++e;
+    }
+    return sign | (uint8_t)(((e + 7) << 3) | (int)q);
+}
+
+int oracle_encode_fp8_e4m3(const float* y, int64_t n, uint8_t* out) {
+    if (!y || !out || n < 0) return -1;
+    for (int64_t i = 0; i < n; ++i) {
+        if (!(fabsf(y[i]) <= 448.0f)) return -1;
+        out[i] = encode_fp8_e4m3(y[i]);
+    }
+    return 0;
+}
+
+/*
+ * One row x[0..d) of the source type to codes and a scale, all in fp32:
+ *   amax  = max_i |x_i|
+ *   scale = amax / QMAX                (QMAX = 448 for E4M3, 127 for INT8)
+ *   scale below the smallest normal float (amax = 0 included): scale = 0,
+ *         every code 0
+ *   inv   = 1 / scale,  y_i = x_i * inv
+ *   E4M3: code_i = nearest E4M3 value of y_i clamped to [-448, 448]
+ *   INT8: code_i = y_i rounded to the nearest integer (ties to even),
+ *         clamped to [-127, 127]
+ * Every step is one correctly rounded fp32 operation, so the result is a
+ * function of the stored inputs alone. Rows must be finite.
+ */
+static void quantise_row(const void* x, int src_dtype, int64_t row0, int32_t d, int fmt,
+                         uint8_t* codes, float* scale_out) {
+    float amax = 0.0f;
+    for (int32_t i = 0; i < d; ++i) {
+        const float a = fabsf((float)load_elem(x, src_dtype, row0 + i));
+        if (a > amax) amax = a;
+    }
+    const float qmax = fmt == ORACLE_FP8E4M3 ? 448.0f : 127.0f;
+    volatile float scale = amax / qmax;
+    if (!(scale >= 0x1p-126f)) {
+        for (int32_t i = 0; i < d; ++i) codes[i] = 0;
+        *scale_out = 0.0f;
+        return;
+    }
+    volatile float inv = 1.0f / scale;
+    for (int32_t i = 0; i < d; ++i) {
+        volatile float y = (float)load_elem(x, src_dtype, row0 + i) * inv;
+        if (fmt == ORACLE_FP8E4M3) {
+            const float c = fminf(fmaxf(y, -448.0f), 448.0f);
+            codes[i] = encode_fp8_e4m3(c);
+        } else {
+            const float r = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+            codes[i] = (uint8_t)(int8_t)r;
+        }
+    }
+    *scale_out = scale;
+}
+
+/* x [n_rows][d] in src_dtype -> codes [n_rows][d], scales [n_rows]. */
+int oracle_quantize_rows(const void* x, int src_dtype, int64_t n_rows, int32_t d, int fmt,
+                         uint8_t* codes, float* scales) {
+    if (!x || !codes || !scales || n_rows < 0 || d <= 0) return -1;
+    if (is_quantised(src_dtype) || elem_bytes_of(src_dtype) == 0 || !is_quantised(fmt)) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        quantise_row(x, src_dtype, r * d, d, fmt, codes + r * d, scales + r);
+    return 0;
 }
 
 int oracle_upcast(const void* src, int dtype, int64_t n, double* dst) {
@@ -143,6 +255,44 @@ int64_t oracle_kv_append(const void* k, const void* v, const int64_t* slot_mappi
     return written;
 }
 
+/*
+ * kv_append into a quantised cache: every (token, KV head) row of k and v
+ * (src_dtype, [num_tokens][n_kv][head_dim]) is quantised per token as in
+ * oracle_quantize_rows; codes go to the pools [num_blocks][n_kv][block_size]
+ * [head_dim] (one byte each) and scales to k_scale / v_scale
+ * [num_blocks][n_kv][block_size], both at block slot / bs, offset slot % bs.
+ * Slot rules and the return value are those of oracle_kv_append.
+ */
+int64_t oracle_kv_append_quant(const void* k, const void* v, int src_dtype,
+                               const int64_t* slot_mapping, int64_t num_tokens, int32_t n_kv,
+                               int32_t head_dim, int fmt, int64_t num_blocks, int32_t block_size,
+                               uint8_t* k_pool, uint8_t* v_pool, float* k_scale, float* v_scale) {
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool || !k_scale || !v_scale) return -1;
+    if (is_quantised(src_dtype) || elem_bytes_of(src_dtype) == 0 || !is_quantised(fmt)) return -1;
+    if (num_tokens < 0 || n_kv <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return -1;
+    const int64_t n_slots = num_blocks * (int64_t)block_size;
+    for (int64_t t = 0; t < num_tokens; ++t)
+        if (slot_mapping[t] >= n_slots) return -1;
+    int64_t written = 0;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        const int64_t blk = slot / block_size;
+        const int64_t off = slot % block_size;
+        for (int32_t g = 0; g < n_kv; ++g) {
+            const int64_t src_row = (t * n_kv + g) * (int64_t)head_dim;
+            const int64_t dst_row = (blk * n_kv + g) * block_size + off;
+            quantise_row(k, src_dtype, src_row, head_dim, fmt, k_pool + dst_row * head_dim,
+                         k_scale + dst_row);
+            quantise_row(v, src_dtype, src_row, head_dim, fmt, v_pool + dst_row * head_dim,
+                         v_scale + dst_row);
+        }
+        ++written;
+    }
+    return written;
+}
+
 /* ---- softmax-weighted average over a list of key positions -------------- */
 
 /*
@@ -157,7 +307,17 @@ typedef struct {
     int dtype;
     int64_t* key_off;     /* element offset of row t, length n_keys */
     int64_t n_keys;
+    const float* k_scale; /* quantised cache: scale of row key_off / head_dim; else NULL */
+    const float* v_scale;
 } key_list;
+
+/* Element c of row t of K (or V): the stored value, times the row's scale in a quantised cache. */
+static double key_elem(const key_list* keys, int is_v, int64_t t, int32_t c, int32_t d) {
+    const int64_t base = keys->key_off[t];
+    const double x = load_elem(is_v ? keys->v_base : keys->k_base, keys->dtype, base + c);
+    const float* sc = is_v ? keys->v_scale : keys->k_scale;
+    return sc ? x * (double)sc[base / d] : x;
+}
 
 static void attend(const double* q, int32_t d, double scale, const key_list* keys,
                    double* scores, double* out) {
@@ -167,8 +327,7 @@ static void attend(const double* q, int32_t d, double scale, const key_list* key
     double m = -INFINITY;
     for (int64_t t = 0; t < keys->n_keys; ++t) {
         double dot = 0.0;
-        const int64_t base = keys->key_off[t];
-        for (int32_t c = 0; c < d; ++c) dot += q[c] * load_elem(keys->k_base, keys->dtype, base + c);
+        for (int32_t c = 0; c < d; ++c) dot += q[c] * key_elem(keys, 0, t, c, d);
         scores[t] = scale * dot;
         if (scores[t] > m) m = scores[t];
     }
@@ -176,8 +335,7 @@ static void attend(const double* q, int32_t d, double scale, const key_list* key
     for (int64_t t = 0; t < keys->n_keys; ++t) {
         const double w = exp(scores[t] - m);
         den += w;
-        const int64_t base = keys->key_off[t];
-        for (int32_t c = 0; c < d; ++c) out[c] += w * load_elem(keys->v_base, keys->dtype, base + c);
+        for (int32_t c = 0; c < d; ++c) out[c] += w * key_elem(keys, 1, t, c, d);
     }
     for (int32_t c = 0; c < d; ++c) out[c] /= den;
 }
@@ -204,17 +362,25 @@ static int set_threads(int32_t n_threads) {
  *              W recent positions)
  * sel          optional list of n_sel (b, h) pairs; NULL means every (b, h)
  * out          [batch][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
+ * Quantised pools (kv_dtype E4M3 or INT8) come with k_scale / v_scale
+ * [num_blocks][n_kv][block_size] fp32: element = code * the row's scale; q
+ * then has its own type q_dtype. Unquantised pools take no scales and
+ * q_dtype == kv_dtype.
  * Returns 0, or -1 for invalid arguments or a block id outside the pool.
  */
-int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dtype,
-                  int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
-                  int64_t num_blocks, int32_t block_size,
-                  const int32_t* block_table, int32_t max_blocks_per_seq,
-                  const int32_t* context_lens, double scale, int32_t window,
-                  const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
+int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                     const float* k_scale, const float* v_scale,
+                     int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                     int64_t num_blocks, int32_t block_size,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, double scale, int32_t window,
+                     const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return -1;
     if (window < 0) return -1;
-    if (elem_bytes_of(dtype) == 0 || batch < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 ||
+    if (elem_bytes_of(q_dtype) == 0 || is_quantised(q_dtype)) return -1;
+    if (is_quantised(kv_dtype) ? (!k_scale || !v_scale) : (k_scale || v_scale || q_dtype != kv_dtype))
+        return -1;
+    if (elem_bytes_of(kv_dtype) == 0 || batch < 0 || n_q <= 0 || n_kv <= 0 || head_dim <= 0 ||
         num_blocks <= 0 || block_size <= 0 || max_blocks_per_seq < 0)
         return -1;
     if (n_q % n_kv != 0) return -1;
@@ -249,7 +415,7 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
             bad |= 1;
         } else {
             for (int32_t c = 0; c < head_dim; ++c)
-                qv[c] = load_elem(q, dtype, ((int64_t)b * n_q + h) * head_dim + c);
+                qv[c] = load_elem(q, q_dtype, ((int64_t)b * n_q + h) * head_dim + c);
             const int32_t first = (window > 0 && ctx > window) ? ctx - window : 0;
             for (int32_t t = first; t < ctx; ++t) {
                 /* block-table translation: logical t -> (physical block, offset) */
@@ -257,7 +423,7 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
                 const int64_t off = t % block_size;
                 offs[t - first] = ((phys * n_kv + g) * block_size + off) * head_dim;
             }
-            key_list keys = {k_pool, v_pool, dtype, offs, ctx - first};
+            key_list keys = {k_pool, v_pool, kv_dtype, offs, ctx - first, k_scale, v_scale};
             attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
         }
         free(qv);
@@ -265,6 +431,19 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
         free(offs);
     }
     return bad ? -1 : 0;
+}
+
+/* Decode over an unquantised cache: q and the pools share one type. */
+int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dtype,
+                  int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                  int64_t num_blocks, int32_t block_size,
+                  const int32_t* block_table, int32_t max_blocks_per_seq,
+                  const int32_t* context_lens, double scale, int32_t window,
+                  const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
+    if (is_quantised(dtype)) return -1;
+    return oracle_decode_ex(q, dtype, k_pool, v_pool, dtype, NULL, NULL, batch, n_q, n_kv, head_dim,
+                            num_blocks, block_size, block_table, max_blocks_per_seq, context_lens,
+                            scale, window, sel, n_sel, out, n_threads);
 }
 
 /* ---- prefill over contiguous Q/K/V --------------------------------------- */
@@ -282,6 +461,7 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                    const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k || !v || !out) return -1;
     if (window < 0 || (window > 0 && !causal)) return -1;
+    if (is_quantised(dtype)) return -1;
     if (elem_bytes_of(dtype) == 0 || batch < 0 || seq_len < 0 || n_q <= 0 || n_kv <= 0 ||
         head_dim <= 0)
         return -1;
@@ -321,7 +501,7 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                 qv[c] = load_elem(q, dtype, (((int64_t)b * seq_len + i) * n_q + h) * head_dim + c);
             for (int32_t j = first; j < n_keys; ++j)
                 offs[j - first] = (((int64_t)b * seq_len + j) * n_kv + g) * head_dim;
-            key_list keys = {k, v, dtype, offs, n_keys - first};
+            key_list keys = {k, v, dtype, offs, n_keys - first, NULL, NULL};
             attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
         }
         free(qv);

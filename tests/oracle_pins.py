@@ -561,6 +561,172 @@ def pin_chunked_prefill_window_matches_library_sdpa_band(orc):
         close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"windowed chunk b={b} vs sdpa band")
 
 
+# ---- quantised cache: codes, quantiser, attention over codes * scales -------------------
+#
+# Quantised cache: the walk-through's KV-cache section, INT8 / FP8 item (per channel or per
+# token); read here as per-token symmetric absolute-maximum scaling, FP8 = OCP E4M3.
+
+def _fp8_values(codes: np.ndarray) -> np.ndarray:
+    """float64 values of E4M3 codes through torch's own float8_e4m3fn dtype."""
+    return torch.from_numpy(codes.astype(np.uint8)).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def _code_values(codes: np.ndarray, fmt: str) -> np.ndarray:
+    return _fp8_values(codes) if fmt == "fp8" else codes.astype(np.float64)
+
+
+def pin_upcast_fp8_every_pattern(orc):
+    codes = np.arange(256, dtype=np.uint8)
+    got = orc.upcast(codes, "fp8")
+    want = _fp8_values(codes)
+    nan = np.isnan(want)
+    assert nan.sum() == 2 and (np.isnan(got) == nan).all(), "E4M3 NaN patterns differ"
+    assert (got[~nan] == want[~nan]).all(), "E4M3 widening differs from torch's float8_e4m3fn"
+    assert got[0x7E] == 448.0 and got[0x01] == 2.0 ** -9
+
+
+def pin_upcast_int8_every_pattern(orc):
+    codes = np.arange(-128, 128, dtype=np.int8)
+    assert (orc.upcast(codes, "int8") == codes.astype(np.float64)).all()
+
+
+def pin_encode_fp8_matches_library_cast(orc):
+    vals = _fp8_values(np.arange(256, dtype=np.uint8))
+    vals = np.unique(vals[np.isfinite(vals)]).astype(np.float32)          # every finite value
+    mids = ((vals[1:].astype(np.float64) + vals[:-1]) / 2).astype(np.float32)   # exact in fp32
+    y = np.concatenate([vals, mids, np.nextafter(mids, np.float32(np.inf)),
+                        np.nextafter(mids, np.float32(-np.inf)),
+                        np.random.default_rng(60).normal(0, 60, 20000).astype(np.float32),
+                        np.random.default_rng(61).normal(0, 0.01, 5000).astype(np.float32)])
+    y = y[np.abs(y) <= 448].astype(np.float32)
+    got = orc.encode_fp8(y)
+    want = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"E4M3 encoding differs from torch at y={y[bad[:5]]}: {got[bad[:5]]} vs {want[bad[:5]]}"
+
+
+def pin_quantize_hand_worked_fixture(orc):
+    fx = json.loads((GOLDEN / "quantize_hand_worked.json").read_text())
+    for row in fx["rows"]:
+        x = np.asarray(row["x"], np.float32)[None, :]
+        codes, scales = orc.quantize_rows(x, "f32", row["fmt"])
+        assert scales[0] == np.float32(row["scale"]), f"{row['fmt']}: scale {scales[0]} vs {row['scale']}"
+        want = np.asarray(row["codes"], np.uint8 if row["fmt"] == "fp8" else np.int8)
+        assert (codes[0] == want).all(), f"{row['fmt']}: codes {codes[0]} vs {want}"
+
+
+def pin_quantize_exact_rows_round_trip(orc):
+    # Rows whose values are codes times a power of two, with a largest-magnitude element at
+    # QMAX times that power: the scale is exactly the power and the codes are the values.
+    rng = np.random.default_rng(62)
+    fp8_vals = _fp8_values(np.arange(256, dtype=np.uint8))
+    finite = np.nonzero(np.isfinite(fp8_vals))[0].astype(np.uint8)
+    for fmt, qmax in (("fp8", 448.0), ("int8", 127.0)):
+        for p in (0, -5, 7):
+            if fmt == "fp8":
+                c = rng.choice(finite, size=(6, 16))
+                c[:, 3] = 0x7E if p != 7 else 0xFE                        # +-448
+            else:
+                c = rng.integers(-127, 128, size=(6, 16)).astype(np.int8)
+                c[:, 5] = 127 if p != 7 else -127
+            x = (_code_values(c, fmt) * 2.0 ** p).astype(np.float32)
+            codes, scales = orc.quantize_rows(x, "f32", fmt)
+            assert (scales == np.float32(2.0 ** p)).all(), f"{fmt} p={p}: scales {scales}"
+            assert (_code_values(codes, fmt) == _code_values(c, fmt)).all(), f"{fmt} p={p}: codes differ"
+
+
+def pin_quantize_error_bound_and_extremes(orc):
+    g = torch.Generator().manual_seed(63)
+    x = stored(torch.randn(200, 64, generator=g) * torch.rand(200, 1, generator=g) * 10, "bf16")
+    xv = exact(x, "bf16").numpy()
+    amax = np.abs(xv).max(axis=1)
+    for fmt, qmax in (("fp8", 448.0), ("int8", 127.0)):
+        codes, scales = orc.quantize_rows(x, "bf16", fmt)
+        s = scales.astype(np.float64)
+        assert np.allclose(s, amax / qmax, rtol=2.0 ** -23, atol=0), f"{fmt}: scale is not amax / QMAX"
+        deq = _code_values(codes, fmt) * s[:, None]
+        err = np.abs(deq - xv)
+        if fmt == "int8":   # half a step, plus the fp32 rounding of 1/scale and of x * (1/scale)
+            bound = s[:, None] * (0.5 + 128 * 2.0 ** -22)
+        else:   # half a unit in the last place of y: 2^-4 |y|, or 2^-10 in the subnormal range
+            bound = np.maximum(np.abs(xv) * 2.0 ** -4, 2.0 ** -10 * s[:, None]) * (1 + 2.0 ** -20)
+        assert (err <= bound).all(), f"{fmt}: round-trip error {float((err - bound).max()):.3e} over the bound"
+        top = np.abs(xv) == amax[:, None]
+        assert (np.abs(_code_values(codes, fmt))[top] == qmax).all(), f"{fmt}: the largest element must map to QMAX"
+
+
+def pin_quantize_zero_and_tiny_rows(orc):
+    x = np.zeros((3, 8), np.float32)
+    x[1, 2] = 1e-38            # amax / 448 is below the smallest normal float: stored as zero
+    x[2, 5] = -3.0
+    for fmt in ("fp8", "int8"):
+        codes, scales = orc.quantize_rows(x, "f32", fmt)
+        assert scales[0] == 0 and scales[1] == 0 and (_code_values(codes[:2], fmt) == 0).all()
+        assert abs(_code_values(codes[2:], fmt)[0, 5] * scales[2] + 3.0) < 1e-6
+
+
+def pin_kv_append_quant_places_quantised_rows(orc):
+    g = torch.Generator().manual_seed(64)
+    nb, n_kv, bs, d, T = 5, 2, 4, 16, 7
+    k = stored(torch.randn(T, n_kv, d, generator=g), "bf16")
+    v = stored(torch.randn(T, n_kv, d, generator=g) * 3, "bf16")
+    slots = np.random.default_rng(64).choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[4] = -1
+    for fmt in ("fp8", "int8"):
+        cdt = np.uint8 if fmt == "fp8" else np.int8
+        kp = np.full((nb, n_kv, bs, d), 0x11, cdt)
+        vp = kp.copy()
+        ks = np.full((nb, n_kv, bs), -7.0, np.float32)
+        vs = ks.copy()
+        assert orc.kv_append_quant(k, v, "bf16", slots, kp, vp, ks, vs, fmt) == T - 1
+        kc, kscale = orc.quantize_rows(k, "bf16", fmt)
+        vc, vscale = orc.quantize_rows(v, "bf16", fmt)
+        # Independent placement view: slot s is row s of a [nb*bs][n_kv] transpose.
+        kt = kp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+        vt = vp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+        kst = ks.transpose(0, 2, 1).reshape(nb * bs, n_kv)
+        vst = vs.transpose(0, 2, 1).reshape(nb * bs, n_kv)
+        keep = np.ones(nb * bs, bool)
+        for t, s in enumerate(slots):
+            if s < 0:
+                continue
+            keep[s] = False
+            assert (kt[s] == kc[t]).all() and (vt[s] == vc[t]).all(), f"{fmt}: codes of token {t}"
+            assert (kst[s] == kscale[t]).all() and (vst[s] == vscale[t]).all(), f"{fmt}: scales of token {t}"
+        assert (kt[keep] == 0x11).all() and (kst[keep] == -7.0).all(), f"{fmt}: untouched slots changed"
+
+
+def pin_decode_quantised_matches_library_sdpa(orc):
+    ctxs, n_q, n_kv, d, bs = [1, 6, 13, 20], 8, 2, 16, 4
+    G = n_q // n_kv
+    g = torch.Generator().manual_seed(65)
+    q = stored(torch.randn(len(ctxs), n_q, d, generator=g), "bf16")
+    for fmt in ("fp8", "int8"):
+        kc, vc, ksc, vsc = [], [], [], []
+        for L in ctxs:
+            krow = stored(torch.randn(L, n_kv, d, generator=g), "bf16")
+            vrow = stored(torch.randn(L, n_kv, d, generator=g) * 2, "bf16")
+            a, sa = orc.quantize_rows(krow, "bf16", fmt)
+            b_, sb = orc.quantize_rows(vrow, "bf16", fmt)
+            kc.append(a); vc.append(b_); ksc.append(sa); vsc.append(sb)
+        nb = sum(-(-L // bs) for L in ctxs) + 2
+        fill = np.array(0x7F if fmt == "fp8" else 99).astype(kc[0].dtype)   # NaN code / junk
+        kp, bt = pack_pool(kc, bs, nb, np.random.default_rng(66), fill)
+        vp, _ = pack_pool(vc, bs, nb, np.random.default_rng(66), fill)
+        ksp, _ = pack_pool([s[..., None] for s in ksc], bs, nb, np.random.default_rng(66), np.float32(np.nan))
+        vsp, _ = pack_pool([s[..., None] for s in vsc], bs, nb, np.random.default_rng(66), np.float32(np.nan))
+        got = orc.decode(q, kp, vp, fmt, bt, np.asarray(ctxs, np.int32), 0.3, q_dtype="bf16",
+                         k_scale=np.ascontiguousarray(ksp[..., 0]), v_scale=np.ascontiguousarray(vsp[..., 0]))
+        for b, L in enumerate(ctxs):
+            kk = _code_values(kc[b], fmt) * ksc[b][..., None].astype(np.float64)     # [L][n_kv][d]
+            vv = _code_values(vc[b], fmt) * vsc[b][..., None].astype(np.float64)
+            qq = exact(q[b], "bf16").unsqueeze(1)
+            k_t = torch.from_numpy(kk).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+            v_t = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+            want = sdpa64(qq, k_t, v_t, 0.3)[:, 0, :]
+            close(got[b], want.numpy(), 1e-12, f"{fmt} decode vs sdpa over codes * scales, b={b}")
+
+
 # ---- kv_append ---------------------------------------------------------------------------
 
 def pin_kv_append_hand_worked_fixture(orc):

@@ -4,8 +4,11 @@ Each mutant is a textual edit of a private copy of oracle.c (the real source is
 never touched), compiled with gcc into a temporary directory. The edits are the
 plausible slips: a wrong head-to-group map, a dropped scale, a sign error, a
 missing normalisation, an off-by-one causal mask, wrong block or offset
-arithmetic, a transposed operand, a wrong widening of stored values. All
-mutants keep every memory access in bounds.
+arithmetic, a transposed operand, a wrong widening of stored values, a
+window off by one, and in the quantised cache a wrong largest code, wrong
+rounding, a wrong FP8 exponent bias or subnormal step, V scaled by K's scale,
+signed codes read as unsigned, scales stored at the wrong slot. All mutants
+keep every memory access in bounds.
 """
 from pathlib import Path
 
@@ -31,19 +34,33 @@ MUTANTS = {
     "block_row_of_next_sequence": (
         "block_table[(int64_t)b * max_blocks_per_seq + t / block_size]",
         "block_table[(int64_t)((b + 1) % batch) * max_blocks_per_seq + t / block_size]"),
-    "append_offset_shift": ("const int64_t off = slot % block_size;",
-                            "const int64_t off = (slot + 1) % block_size;"),
+    "append_offset_shift": ("const int64_t off = slot % block_size;\n        for (int32_t g = 0; g < n_kv; ++g) {\n            const size_t src",
+                            "const int64_t off = (slot + 1) % block_size;\n        for (int32_t g = 0; g < n_kv; ++g) {\n            const size_t src"),
     "append_head_offset_transposed": (
         "const size_t dst = (((size_t)blk * n_kv + g) * block_size + off) * row;",
         "const size_t dst = (((size_t)blk * block_size + off) * n_kv + g) * row;"),
-    "query_index_transposed": ("load_elem(q, dtype, ((int64_t)b * n_q + h) * head_dim + c)",
-                               "load_elem(q, dtype, ((int64_t)h * batch + b) * head_dim + c)"),
-    "values_read_from_keys": ("out[c] += w * load_elem(keys->v_base",
-                              "out[c] += w * load_elem(keys->k_base"),
+    "query_index_transposed": ("load_elem(q, q_dtype, ((int64_t)b * n_q + h) * head_dim + c)",
+                               "load_elem(q, q_dtype, ((int64_t)h * batch + b) * head_dim + c)"),
+    "values_read_from_keys": ("out[c] += w * key_elem(keys, 1, t, c, d)",
+                              "out[c] += w * key_elem(keys, 0, t, c, d)"),
     "bf16_widening_shift": ("((uint32_t)h) << 16", "((uint32_t)h) << 15"),
     "f16_exponent_bias": ("ldexp((double)(1024 + frac), e - 25)",
                           "ldexp((double)(1024 + frac), e - 24)"),
     "max_tracks_minimum": ("if (scores[t] > m) m = scores[t];", "if (scores[t] < m) m = scores[t];"),
+    "fp8_qmax_of_the_fnuz_format": ("fmt == ORACLE_FP8E4M3 ? 448.0f : 127.0f",
+                                    "fmt == ORACLE_FP8E4M3 ? 240.0f : 127.0f"),
+    "int8_truncates": ("fmaxf(rintf(y), -127.0f)", "fmaxf(truncf(y), -127.0f)"),
+    "fp8_exponent_bias": ("ldexp((double)(8 + m), e - 10)", "ldexp((double)(8 + m), e - 11)"),
+    "fp8_encode_ties_away": ("double q = nearbyint((2.0 * fr - 1.0) * 8.0);",
+                             "double q = round((2.0 * fr - 1.0) * 8.0);"),
+    "fp8_subnormal_step": ("return sign | (uint8_t)nearbyint(ldexp(a, 9));",
+                           "return sign | (uint8_t)nearbyint(ldexp(a, 8));"),
+    "v_scaled_by_k_scale": ("const float* sc = is_v ? keys->v_scale : keys->k_scale;",
+                            "const float* sc = is_v ? keys->k_scale : keys->k_scale;"),
+    "int8_read_unsigned": ("case ORACLE_INT8: return (double)((const int8_t*)base)[idx];",
+                           "case ORACLE_INT8: return (double)((const uint8_t*)base)[idx];"),
+    "quant_append_scale_row_offset": ("const int64_t dst_row = (blk * n_kv + g) * block_size + off;",
+                                      "const int64_t dst_row = (blk * n_kv + g) * block_size + (off + 1) % block_size;"),
     "decode_window_one_too_wide": ("(window > 0 && ctx > window) ? ctx - window : 0",
                                    "(window > 0 && ctx > window) ? ctx - window - 1 : 0"),
     "prefill_window_one_too_narrow": ("(window > 0 && i + 1 > window) ? i + 1 - window : 0",
