@@ -84,15 +84,34 @@ int check_cache(const pa_cache_desc* c) {
 // Decode launch plan; a pure function of the host arguments so that
 // pa_decode_workspace_bytes and pa_paged_attn_decode always agree.
 struct Plan {
-    int32_t gw, hs_wg, hsg, waves_tok, blocks_per_wave, nparts_max, ring;
+    int32_t gw, hs_wg, hsg, waves_tok, blocks_per_wave, nparts_max, ring, mfma;
     size_t ws_floats_m, ws_floats_acc;  // floats in m (== l) and acc arrays
 };
 
+// Decode on the matrix cores (decode_mfma.hip) for bf16/f16 caches whose group
+// size fills 4, 8 or 16 MFMA columns; PA_DECODE_MFMA=0 selects the VALU kernel.
+bool decode_uses_mfma(int32_t G, const pa_cache_desc* c) {
+    if (c->dtype != PA_BF16 && c->dtype != PA_F16) return false;
+    if (G % 4 != 0) return false;
+    return env_int("PA_DECODE_MFMA", 1) != 0;
+}
+
+// LDS bytes one wave of the matrix-core decode kernel takes: its ring, or the
+// merge slot of `hw` heads (acc rows padded by 4 floats, then m and l) if larger.
+int32_t mfma_wave_bytes(int32_t ring, int32_t tile, int32_t hw, int32_t head_dim) {
+    const int32_t slot = (hw * (head_dim + 4) + 2 * hw) * 4;
+    const int32_t r = ring * 2 * tile;
+    return ((r > slot ? r : slot) + 15) / 16 * 16;
+}
+
 int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c, Plan* pl) {
     const int32_t G = n_q / c->n_kv;
-    // Query heads per wave: 4 when the group allows it (keeps acc at 64 fp32
-    // registers for head_dim 128), else the largest power of two dividing G.
-    const int32_t gw = (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
+    const bool mfma = decode_uses_mfma(G, c);
+    // Query heads per wave. VALU kernel: 4 when the group allows it (keeps acc at
+    // 64 fp32 registers for head_dim 128), else the largest power of two dividing
+    // G. Matrix-core kernel: one workgroup slice of 16, 8 or 4 heads (MFMA columns).
+    const int32_t gw = mfma ? (G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : 4)
+                            : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
     // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
     // (PA_DECODE_RING: 1 or 2). Workgroup size: 8 waves when there are at least
@@ -105,13 +124,16 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     int32_t max_waves = env_int("PA_DECODE_WAVES", units >= kComputeUnits ? kMaxWaves : 4);
     if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
-    while (max_waves > 1 && max_waves * ring * 2 * tile > kLdsBytes) --max_waves;
+    const int32_t wave_lds = mfma ? mfma_wave_bytes(ring, tile, gw, c->head_dim) : ring * 2 * tile;
+    while (max_waves > 1 && max_waves * wave_lds > kLdsBytes) --max_waves;
     int32_t hs_wg = 1;
-    for (int32_t d = max_waves; d >= 1; --d)
-        if (hs % d == 0) {
-            hs_wg = d;
-            break;
-        }
+    if (!mfma) {   // the VALU kernel may also split a workgroup's waves over head slices
+        for (int32_t d = max_waves; d >= 1; --d)
+            if (hs % d == 0) {
+                hs_wg = d;
+                break;
+            }
+    }
     const int32_t waves_tok = max_waves / hs_wg;
     const int32_t unit = waves_tok * kBlockSize;  // tokens per pass of the workgroup
 
@@ -131,6 +153,7 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     pl->blocks_per_wave = bpw;
     pl->nparts_max = nparts_max < 1 ? 1 : nparts_max;
     pl->ring = ring;
+    pl->mfma = mfma ? 1 : 0;
     if (pl->nparts_max > 1) {
         pl->ws_floats_m = (size_t)batch * n_q * pl->nparts_max;
         pl->ws_floats_acc = pl->ws_floats_m * (size_t)c->head_dim;
@@ -461,6 +484,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     a.blocks_per_wave = pl.blocks_per_wave;
     a.nparts_max = pl.nparts_max;
     a.ring = pl.ring;
+    a.mfma = pl.mfma;
     a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;

@@ -465,6 +465,7 @@ hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipSt
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s) {
     if (a.hs_wg * a.waves_tok > MAX_WAVES || a.hs_wg < 1 || a.waves_tok < 1) return hipErrorInvalidValue;
     if (a.q_rows != 1 || a.window < 0) return hipErrorInvalidValue;   // the reduce kernel reads q_rows
+    if (a.mfma) return launch_decode_mfma(a, e, head_dim, s);
     switch (e) {
     case Elem::F32: return launch_dim<F32>(a, head_dim, s);
     case Elem::BF16: return launch_dim<BF16>(a, head_dim, s);

@@ -43,9 +43,14 @@ struct DecodeArgs {
     // Sliding window: 0 attends to the whole context; W > 0 lets the query at
     // position p see positions max(0, p - W + 1) .. p only.
     int32_t window;
+    // Single-row decode on the matrix cores (decode_mfma.hip): gw query heads
+    // (4, 8 or 16) per workgroup fill the MFMA columns; hs_wg must be 1.
+    int32_t mfma;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
+// Single-row decode with the per-block products on the matrix cores (bf16/f16).
+hipError_t launch_decode_mfma(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
 // The log-sum-exp merge of partition partials alone (rows = batch * n_q of `a`).
 hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
 // Multi-row decode on the matrix cores (bf16/f16), plus the merge when contexts split.

@@ -3,6 +3,10 @@
 Every case runs the library's HIP kernels through the C ABI and compares with
 the oracle on the same seeded inputs: kv_append bit-exact, decode within
 max-abs 2e-3 and norm-wise relative 1e-2 for bf16/fp16 (1e-5 for fp32).
+
+Each test runs twice: with the default kernel choice (the matrix-core decode for
+bf16/f16 caches whose group size is a multiple of 4, the VALU kernel otherwise)
+and with PA_DECODE_MFMA=0, which forces the VALU kernel everywhere.
 """
 import zlib
 
@@ -15,6 +19,12 @@ from gpu_helpers import assert_parity, gpu_step, oracle_step, same_bits, say, st
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(params=["default", "valu"], autouse=True)
+def decode_kernel(request, monkeypatch):
+    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+    return request.param
 
 
 @pytest.fixture(scope="module")
@@ -49,6 +59,10 @@ SMALL = {
     "gqa4_bf16_d128_ragged": (8, 2, 128, [1, 15, 16, 17, 33, 300, 1000], "bf16"),
     "gqa4_bf16_d64": (8, 2, 64, [5, 64, 130], "bf16"),
     "gqa2_f16_d128": (4, 2, 128, [7, 200, 513], "f16"),
+    "gqa4_f16_d128": (8, 2, 128, [2, 19, 250, 1100], "f16"),
+    "gqa8_f16_d64": (16, 2, 64, [1, 47, 600], "f16"),
+    "gqa8_bf16_d64": (32, 4, 64, [16, 31, 800], "bf16"),
+    "gqa16_bf16": (32, 2, 128, [5, 900], "bf16"),
     "gqa2_f32_d128": (4, 2, 128, [9, 77], "f32"),
     "gqa4_f32_d64": (8, 2, 64, [31, 1], "f32"),
     "mqa16_bf16": (16, 1, 128, [40, 700], "bf16"),

@@ -19,6 +19,14 @@ from paged_gqa_attention_attn_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
+@pytest.fixture(params=["default", "valu"])
+def decode_kernel(request, monkeypatch):
+    """Single-row decode tests run with the default kernel choice (matrix cores for
+    bf16/f16 groups of 4, 8 or 16) and with the VALU kernel forced."""
+    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+    return request.param
+
+
 @pytest.fixture(scope="module")
 def pa():
     if not torch.cuda.is_available():
@@ -63,7 +71,7 @@ def _appended(pa, c):
 
 @pytest.mark.parametrize("window", [1, 16, 100, 4096])
 @pytest.mark.parametrize("name", sorted(DECODE))
-def test_decode_window_matches_oracle(pa, name, window):
+def test_decode_window_matches_oracle(pa, decode_kernel, name, window):
     c = _decode_case(name)
     say(f"[window] decode {name} W={window} ctx={c.context_lens.tolist()}")
     kp, vp = _appended(pa, c)
@@ -82,7 +90,7 @@ def test_decode_window_matches_oracle(pa, name, window):
 
 
 @pytest.mark.parametrize("tokens", [256, 1024])
-def test_decode_window_partition_sizes(pa, tokens):
+def test_decode_window_partition_sizes(pa, decode_kernel, tokens):
     c = _decode_case("gqa4_bf16_d128", seed_extra=1)
     say(f"[window] decode partitions of {tokens} tokens, W=3000")
     kp, vp = _appended(pa, c)
@@ -98,7 +106,7 @@ def test_decode_window_partition_sizes(pa, tokens):
     assert_parity(got.cpu().numpy(), want, c.dtype, f"partition {tokens}")
 
 
-def test_decode_append_window_equals_two_calls_bitwise(pa):
+def test_decode_append_window_equals_two_calls_bitwise(pa, decode_kernel):
     c = _decode_case("gqa4_bf16_d128", seed_extra=2)
     say("[window] fused decode + append vs kv_append + decode, W=500")
     kp, vp = _appended(pa, c)
@@ -111,7 +119,7 @@ def test_decode_append_window_equals_two_calls_bitwise(pa):
     assert same_bits(kf, kp) and same_bits(vf, vp)
 
 
-def test_decode_window_covering_the_context_is_the_plain_decode(pa):
+def test_decode_window_covering_the_context_is_the_plain_decode(pa, decode_kernel):
     c = _decode_case("gqa4_f16_d64", seed_extra=3)
     say("[window] W >= every context gives the unwindowed bits")
     kp, vp = _appended(pa, c)
