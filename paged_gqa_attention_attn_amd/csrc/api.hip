@@ -104,6 +104,32 @@ int32_t mfma_wave_bytes(int32_t ring, int32_t tile, int32_t hw, int32_t head_dim
     return ((r > slot ? r : slot) + 15) / 16 * 16;
 }
 
+// Matrix-core decode plan: a grid of about kTargetWaves waves (8 per compute
+// unit), each streaming as long a run of blocks as that allows (4 to 64 blocks),
+// with the partitions of a context balanced. Measured on MI355X: larger runs and
+// fewer resident waves stream faster (8B-, 70B-shaped, variable-length and
+// sliding-window workloads), as long as every compute unit has work.
+constexpr int kTargetWaves = 2048;
+
+void mfma_partitions(int64_t units, int32_t span, int32_t* waves, int32_t* bpw, int32_t* nparts) {
+    int32_t w = env_int("PA_DECODE_WAVES", 8);
+    if (w < 1 || w > kMaxWaves) w = kMaxWaves;
+    int32_t tokens = g_partition_tokens.load();
+    int32_t b;
+    if (tokens > 0) {   // explicit partition size (pa_set_decode_partition_tokens)
+        b = tokens / (w * kBlockSize);
+    } else {
+        const int64_t want = (span * units + kTargetWaves - 1) / kTargetWaves;
+        b = (int32_t)std::min<int64_t>(64, std::max<int64_t>(4, want));
+        const int32_t p = (span + w * b - 1) / (w * b);
+        b = (span + p * w - 1) / (p * w);   // balance the partitions
+    }
+    b = std::max(1, std::min(64, b));
+    *waves = w;
+    *bpw = b;
+    *nparts = std::max(1, (span + w * b - 1) / (w * b));
+}
+
 int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c, Plan* pl) {
     const int32_t G = n_q / c->n_kv;
     const bool mfma = decode_uses_mfma(G, c);
@@ -114,44 +140,42 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
                             : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
     // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
-    // (PA_DECODE_RING: 1 or 2). Workgroup size: 8 waves when there are at least
-    // as many (sequence, KV head, head slice) units as compute units, else 4 so
-    // that long contexts split into more, smaller workgroups (PA_DECODE_WAVES
-    // overrides). Measured on MI355X with the 8B- and 70B-shaped workloads.
+    // (PA_DECODE_RING: 1 or 2).
     int32_t ring = env_int("PA_DECODE_RING", 1);
     if (ring != 1 && ring != 2) ring = 1;
-    const int64_t units = (int64_t)batch * c->n_kv * (G / gw);
-    int32_t max_waves = env_int("PA_DECODE_WAVES", units >= kComputeUnits ? kMaxWaves : 4);
-    if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
+    const int64_t units = (int64_t)batch * c->n_kv * hs;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
-    const int32_t wave_lds = mfma ? mfma_wave_bytes(ring, tile, gw, c->head_dim) : ring * 2 * tile;
-    while (max_waves > 1 && max_waves * wave_lds > kLdsBytes) --max_waves;
-    int32_t hs_wg = 1;
-    if (!mfma) {   // the VALU kernel may also split a workgroup's waves over head slices
+    int32_t hs_wg = 1, waves_tok, bpw, nparts_max;
+    if (mfma) {
+        mfma_partitions(units, max_blocks, &waves_tok, &bpw, &nparts_max);
+        while (waves_tok > 1 && waves_tok * mfma_wave_bytes(ring, tile, gw, c->head_dim) > kLdsBytes) --waves_tok;
+        nparts_max = std::max(1, (max_blocks + waves_tok * bpw - 1) / (waves_tok * bpw));
+    } else {
+        // VALU kernel: 8 waves when there are at least as many (sequence, KV head,
+        // head slice) units as compute units, else 4 so that long contexts split
+        // into more, smaller workgroups (PA_DECODE_WAVES overrides); 2048-token
+        // partitions unless overridden. The waves may also split over head slices.
+        int32_t max_waves = env_int("PA_DECODE_WAVES", units >= kComputeUnits ? kMaxWaves : 4);
+        if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
+        while (max_waves > 1 && max_waves * ring * 2 * tile > kLdsBytes) --max_waves;
         for (int32_t d = max_waves; d >= 1; --d)
             if (hs % d == 0) {
                 hs_wg = d;
                 break;
             }
+        waves_tok = max_waves / hs_wg;
+        int32_t tokens = g_partition_tokens.load();
+        if (tokens <= 0) tokens = 2048;
+        bpw = std::max(1, std::min(64, tokens / (waves_tok * kBlockSize)));
+        nparts_max = std::max(1, (max_blocks + bpw * waves_tok - 1) / (bpw * waves_tok));
     }
-    const int32_t waves_tok = max_waves / hs_wg;
-    const int32_t unit = waves_tok * kBlockSize;  // tokens per pass of the workgroup
-
-    // Partition size: 2048 tokens unless overridden.
-    int32_t tokens = g_partition_tokens.load();
-    if (tokens <= 0) tokens = 2048;
-    int32_t bpw = tokens / unit;
-    if (bpw < 1) bpw = 1;
-    if (bpw > 64) bpw = 64;
-    const int32_t bpp = bpw * waves_tok;
-    const int32_t nparts_max = (max_blocks + bpp - 1) / bpp;
 
     pl->gw = gw;
     pl->hs_wg = hs_wg;
     pl->hsg = hs / hs_wg;
     pl->waves_tok = waves_tok;
     pl->blocks_per_wave = bpw;
-    pl->nparts_max = nparts_max < 1 ? 1 : nparts_max;
+    pl->nparts_max = nparts_max;
     pl->ring = ring;
     pl->mfma = mfma ? 1 : 0;
     if (pl->nparts_max > 1) {
@@ -394,9 +418,15 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
                                  const pa_cache_desc* cache) {
     if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK) return 0;
-    Plan pl;
-    make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
-    return plan_bytes(pl);
+    // A windowed call plans for a shorter span of blocks; the size returned covers
+    // the plan of every span up to max_blocks_per_seq.
+    size_t most = 0;
+    for (int32_t span = 1; span <= max_blocks_per_seq; ++span) {
+        Plan pl;
+        make_plan(batch, n_q, span, cache, &pl);
+        most = std::max(most, plan_bytes(pl));
+    }
+    return most;
 }
 
 }  // extern "C"

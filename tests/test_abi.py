@@ -112,12 +112,21 @@ def test_decode_append_rejects(L, kw, code, msg):
 
 
 def test_workspace_query(L):
-    # One partition per (sequence, KV head) needs no workspace; 4096-token
-    # contexts at the default 2048-token partitions need (m, l, acc) for 2
+    # VALU kernel (fp32 cache): 2048-token partitions, so a 2048-token context
+    # needs no workspace and 4096-token contexts need (m, l, acc) for 2
     # partitions of every query head.
-    assert L.pa_decode_workspace_bytes(32, 32, 128, desc(nb=4096, n_kv=8)) == 0
-    n = L.pa_decode_workspace_bytes(32, 32, 256, desc(nb=8192, n_kv=8))
+    f32 = _lib.PA_F32
+    assert L.pa_decode_workspace_bytes(32, 32, 128, desc(nb=4096, n_kv=8, dtype=f32)) == 0
+    n = L.pa_decode_workspace_bytes(32, 32, 256, desc(nb=8192, n_kv=8, dtype=f32))
     rows = 32 * 32 * 2
+    assert n == 2 * rows * 4 + rows * 128 * 4
+    # Matrix-core kernel (bf16, groups of 4/8/16): about 2048 waves of up to 64
+    # blocks each. 32 x 8 (sequence, KV head) units over 4096 tokens fit one
+    # partition of 8 waves x 32 blocks; 8 x 8 units over 32768 tokens take 4
+    # partitions of 8 waves x 64 blocks.
+    assert L.pa_decode_workspace_bytes(32, 32, 256, desc(nb=8192, n_kv=8)) == 0
+    n = L.pa_decode_workspace_bytes(8, 64, 2048, desc(nb=16384, n_kv=8))
+    rows = 8 * 64 * 4
     assert n == 2 * rows * 4 + rows * 128 * 4
     assert L.pa_decode_workspace_bytes(2, 7, 4, desc()) == 0      # invalid: 7 % 2 != 0
 
