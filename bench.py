@@ -50,7 +50,7 @@ ROOT = Path(__file__).resolve().parent
 CSRC = ROOT / "paged_gqa_attention_attn_amd" / "csrc"
 # Sources that determine each profiled kernel's code (their hash dates a counter summary).
 KERNEL_SOURCES = {
-    "decode": ["decode.hip", "common.h", "launch.h", "api.hip"],
+    "decode": ["decode.hip", "decode_mfma.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "prefill": ["prefill.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "decode_multi": ["decode_multi.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
 }
@@ -267,8 +267,9 @@ def bench_decode(args, cfg: int):
                      "one launch: append of one new token per sequence + paged decode"),
         },
         "roofline": {
-            "kernel": "decode partition kernel (with the fused append unless --unfused), plus "
-                      "the log-sum-exp reduce kernel when a context is split",
+            "kernel": "decode partition kernel (decode_mfma_kernel for bf16/f16 groups of 4, 8 "
+                      "or 16 heads, else decode_partition_kernel; with the fused append unless "
+                      "--unfused), plus the log-sum-exp reduce kernel when a context is split",
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic("decode", args.workload),
