@@ -55,8 +55,11 @@
 extern "C" {
 #endif
 
-/* Element types. q/k/v and the cache share one type; outputs are f32 or that type. */
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2 } pa_dtype;
+/* Element types. q/k/v and the cache share one type; outputs are f32 or that type.
+ * PA_FP8_E4M3 and PA_INT8 describe quantised caches only (one-byte codes plus one
+ * fp32 scale per token row, see pa_kv_append_quant); every other entry point
+ * rejects them with PA_ERR_UNSUPPORTED. */
+typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2, PA_FP8_E4M3 = 3, PA_INT8 = 4 } pa_dtype;
 
 typedef enum {
     PA_OK = 0,
@@ -70,7 +73,8 @@ typedef enum {
  *   [num_blocks][n_kv][block_size][head_dim], head_dim fastest,
  * so element (block, kv_head, offset, c) sits at
  *   ((block * n_kv + kv_head) * block_size + offset) * head_dim + c.
- * Supported: block_size 16; head_dim 64 or 128; dtype f32, bf16 or f16.
+ * Supported: block_size 16; head_dim 64 or 128; dtype f32, bf16 or f16 (and,
+ * for the quantised entry points, PA_FP8_E4M3 or PA_INT8, one byte per element).
  */
 typedef struct {
     int32_t num_blocks;
@@ -97,7 +101,8 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
                  void* k_cache, void* v_cache, const pa_cache_desc* cache, void* stream);
 
 /*
- * Bytes of scratch memory pa_paged_attn_decode needs for these arguments
+ * Bytes of scratch memory pa_paged_attn_decode (or, for a quantised cache
+ * description, pa_paged_attn_decode_quant) needs for these arguments
  * (partial results of a context split into partitions, [VC]/[IW] Flash Decoding).
  * 0 when every sequence fits in one partition. Returns 0 as well for invalid
  * arguments; the decode call then reports the error. The size covers any
@@ -252,6 +257,52 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* context_lens, float scale, int32_t window,
                                   void* out, pa_dtype out_dtype, void* stream);
+
+/*
+ * kv_append_quant -- quantise new K/V rows into a one-byte cache and write them
+ * through slot_mapping. [IW] "KV Cache 的形状与增长", INT8 / FP8 item (the fp16
+ * cache quantised to int8 or fp8 per channel or per token; one byte per element in
+ * the KV-size formula); [VC] slot mapping.
+ *
+ *   k, v          [num_tokens][n_kv][head_dim] in src_dtype (f32, bf16 or f16)
+ *   slot_mapping  int64 [num_tokens], as for pa_kv_append (negative or past the
+ *                 pool: skipped)
+ *   k_cache, v_cache  code pools [num_blocks][n_kv][block_size][head_dim], one
+ *                 byte per element: OCP FP8 E4M3 (cache->dtype PA_FP8_E4M3) or
+ *                 two's-complement INT8 (PA_INT8)
+ *   k_scale, v_scale  fp32 [num_blocks][n_kv][block_size]: one scale per row
+ * Every (token, KV head) row x of K and of V is quantised on its own, with every
+ * step one correctly rounded fp32 operation: amax = max |x_i|; scale = amax / QMAX
+ * (448 for E4M3, 127 for INT8); a scale below the smallest normal float (amax = 0
+ * included) is stored as 0 with all codes 0; otherwise y_i = x_i * (1 / scale) and
+ * the code is the nearest E4M3 value of y_i clamped to [-448, 448] (ties to the
+ * even code) or rint(y_i) clamped to [-127, 127]. The stored value of a code is
+ * code * scale. Rows must be finite. num_tokens == 0 is a no-op.
+ */
+int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const int64_t* slot_mapping,
+                       int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pa_cache_desc* cache, void* stream);
+
+/*
+ * paged_attn_decode_quant -- pa_paged_attn_decode over a quantised cache: K and V
+ * values are code * scale of their row ([IW] INT8 / FP8 item), the attention is
+ * the same softmax(q K^T * scale + M) V.
+ *
+ *   q             [batch][n_q][head_dim] in q_dtype (bf16 or f16)
+ *   k_cache, v_cache, k_scale, v_scale  as written by pa_kv_append_quant
+ *   cache->dtype  PA_FP8_E4M3 or PA_INT8
+ *   out           [batch][n_q][head_dim], out_dtype PA_F32 or q_dtype
+ *   other arguments as for pa_paged_attn_decode (window, workspace sized by
+ *   pa_decode_workspace_bytes with this cache description).
+ * Codes are widened exactly to q's type and multiplied on the matrix cores in
+ * fp32; unused slots (codes or scales, NaN included) never reach the output.
+ */
+int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const pa_cache_desc* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Tuning override for the decode partition size, in tokens (a multiple of 16

@@ -13,6 +13,9 @@ Layouts (see include/pagedattn.h):
   context_lens int32 [B]
   slot_mapping int64 [T]
   prefill q    [B][S][n_q][d], k/v [B][S][n_kv][d]
+  quantised caches: codes uint8 (FP8 E4M3 bit patterns; torch.float8_e4m3fn views
+  are accepted too) or int8 [num_blocks][n_kv][16][d], scales float32
+  [num_blocks][n_kv][16]
 """
 from __future__ import annotations
 
@@ -24,7 +27,8 @@ from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
-           "paged_attn_chunked_prefill", "paged_attn_decode_multi",
+           "paged_attn_chunked_prefill", "paged_attn_decode_multi", "kv_append_quant",
+           "paged_attn_decode_quant", "quant_decode_workspace_bytes",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
@@ -283,6 +287,99 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     dt = k_cache.dtype
     _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
         _dev(q, "q", dt), B, R, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+# ---- quantised cache (one-byte codes + one fp32 scale per row) ------------------------------
+
+_QFMT = {"fp8": _lib.PA_FP8_E4M3, "int8": _lib.PA_INT8}
+_QCODE = {"fp8": (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)), "int8": (torch.int8,)}
+
+
+def _quant_desc(k_cache: torch.Tensor, fmt: str) -> CacheDesc:
+    if fmt not in _QFMT:
+        raise ValueError(f"fmt must be 'fp8' or 'int8' (got {fmt!r})")
+    if k_cache.dim() != 4:
+        raise ValueError("code pools must be [num_blocks][n_kv][block_size][head_dim]")
+    if k_cache.dtype not in _QCODE[fmt]:
+        raise TypeError(f"{fmt} code pools must be {_QCODE[fmt]} (got {k_cache.dtype})")
+    nb, n_kv, bs, d = k_cache.shape
+    return CacheDesc(nb, bs, n_kv, d, _QFMT[fmt])
+
+
+def _check_scales(k_cache, k_scale, v_scale):
+    want = tuple(k_cache.shape[:3])
+    for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
+        if tuple(t.shape) != want:
+            raise ValueError(f"{name} must be [num_blocks][n_kv][block_size] = {list(want)}")
+
+
+def kv_append_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                    k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
+                    v_scale: torch.Tensor, fmt: str, stream=None) -> None:
+    """Quantise k/v rows [T][n_kv][d] (f32, bf16 or f16) per row into the code pools and
+    float32 scale pools at ``slot_mapping`` (int64 [T]); ``fmt`` is 'fp8' or 'int8'."""
+    L = _lib.load()
+    desc = _quant_desc(k_cache, fmt)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or k.shape != v.shape:
+        raise ValueError("k/v or cache shapes differ")
+    if k.dim() != 3 or k.shape[1:] != k_cache.shape[1:2] + k_cache.shape[3:]:
+        raise ValueError("k and v must be [T][n_kv][head_dim] matching the cache")
+    if k.dtype not in _DTYPE or v.dtype != k.dtype:
+        raise TypeError("k and v must share one of float32, bfloat16, float16")
+    _check_scales(k_cache, k_scale, v_scale)
+    T = k.shape[0]
+    if slot_mapping.shape != (T,):
+        raise ValueError("slot_mapping must be [T]")
+    _check("pa_kv_append_quant", L.pa_kv_append_quant(
+        _dev(k, "k"), _dev(v, "v"), _DTYPE[k.dtype], _dev(slot_mapping, "slot_mapping", torch.int64), T,
+        _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), ctypes.byref(desc), _stream(k_cache, stream)))
+
+
+def quant_decode_workspace_bytes(batch: int, n_q: int, max_blocks_per_seq: int,
+                                 k_cache: torch.Tensor, fmt: str) -> int:
+    desc = _quant_desc(k_cache, fmt)
+    return int(_lib.load().pa_decode_workspace_bytes(batch, n_q, max_blocks_per_seq,
+                                                     ctypes.byref(desc)))
+
+
+def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                            k_scale: torch.Tensor, v_scale: torch.Tensor, fmt: str,
+                            block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                            out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                            workspace: torch.Tensor | None = None, stream=None,
+                            window: int = 0) -> torch.Tensor:
+    """Decode attention of q [B][n_q][d] (bf16 or f16) over a quantised paged cache (codes
+    and per-row scales); returns out [B][n_q][d] (float32 or q's dtype)."""
+    L = _lib.load()
+    desc = _quant_desc(k_cache, fmt)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache differ")
+    _check_scales(k_cache, k_scale, v_scale)
+    B, n_q, d = q.shape
+    if d != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the cache")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][n_q][d] in a supported dtype")
+    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+    if need and workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("pa_paged_attn_decode_quant", L.pa_paged_attn_decode_quant(
+        _dev(q, "q"), _DTYPE[q.dtype], B, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))

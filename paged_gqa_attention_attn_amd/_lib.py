@@ -10,7 +10,7 @@ from pathlib import Path
 
 LIB_PATH = Path(__file__).resolve().parent / "libpagedattn.so"
 
-PA_F32, PA_BF16, PA_F16 = 0, 1, 2
+PA_F32, PA_BF16, PA_F16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
 
 EXPORTS = (
@@ -22,6 +22,8 @@ EXPORTS = (
     "pa_paged_attn_decode_multi",
     "pa_paged_attn_prefill",
     "pa_paged_attn_chunked_prefill",
+    "pa_kv_append_quant",
+    "pa_paged_attn_decode_quant",
     "pa_set_decode_partition_tokens",
     "pa_set_workspace",
     "pa_last_error",
@@ -82,6 +84,11 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_chunked_prefill.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
                                                 ctypes.c_float, i32, vp, ctypes.c_int, vp]
     L.pa_paged_attn_chunked_prefill.restype = ctypes.c_int
+    L.pa_kv_append_quant.argtypes = [vp, vp, ctypes.c_int, vp, i32, vp, vp, vp, vp, cd, vp]
+    L.pa_kv_append_quant.restype = ctypes.c_int
+    L.pa_paged_attn_decode_quant.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, vp, vp, cd, vp, i32, vp,
+                                             ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
+    L.pa_paged_attn_decode_quant.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
     L.pa_set_workspace.argtypes = [vp, sz]

@@ -45,9 +45,13 @@ int elem_bytes(pa_dtype d) {
     case PA_F32: return 4;
     case PA_BF16: return 2;
     case PA_F16: return 2;
+    case PA_FP8_E4M3: return 1;
+    case PA_INT8: return 1;
     }
     return 0;
 }
+
+bool is_quant(pa_dtype d) { return d == PA_FP8_E4M3 || d == PA_INT8; }
 
 pa::Elem to_elem(pa_dtype d) { return static_cast<pa::Elem>(static_cast<int>(d)); }
 
@@ -67,13 +71,19 @@ int env_int(const char* name, int dflt) {
     return (end && *end == 0) ? (int)x : dflt;
 }
 
-int check_cache(const pa_cache_desc* c) {
+// Sizes and types of a cache description. Quantised caches (one-byte codes plus
+// per-row scales) are accepted only by the entry points that take the scales.
+int check_cache(const pa_cache_desc* c, bool allow_quant = false) {
     if (!c) return fail(PA_ERR_INVALID_ARG, "cache descriptor is NULL");
     if (c->num_blocks <= 0 || c->n_kv <= 0 || c->head_dim <= 0 || c->block_size <= 0)
         return fail(PA_ERR_INVALID_ARG,
                     "cache sizes must be positive (num_blocks=%d n_kv=%d head_dim=%d block_size=%d)",
                     c->num_blocks, c->n_kv, c->head_dim, c->block_size);
     if (elem_bytes(c->dtype) == 0) return fail(PA_ERR_UNSUPPORTED, "unknown cache dtype %d", (int)c->dtype);
+    if (is_quant(c->dtype) && !allow_quant)
+        return fail(PA_ERR_UNSUPPORTED,
+                    "a quantised cache (dtype %d) needs pa_kv_append_quant / pa_paged_attn_decode_quant",
+                    (int)c->dtype);
     if (c->block_size != kBlockSize)
         return fail(PA_ERR_UNSUPPORTED, "block_size %d has no kernel (supported: 16)", c->block_size);
     if (c->head_dim != 64 && c->head_dim != 128)
@@ -132,23 +142,28 @@ void mfma_partitions(int64_t units, int32_t span, int32_t* waves, int32_t* bpw, 
 
 int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c, Plan* pl) {
     const int32_t G = n_q / c->n_kv;
-    const bool mfma = decode_uses_mfma(G, c);
+    const bool quant = is_quant(c->dtype);
+    const bool mfma = quant || decode_uses_mfma(G, c);
     // Query heads per wave. VALU kernel: 4 when the group allows it (keeps acc at
     // 64 fp32 registers for head_dim 128), else the largest power of two dividing
-    // G. Matrix-core kernel: one workgroup slice of 16, 8 or 4 heads (MFMA columns).
-    const int32_t gw = mfma ? (G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : 4)
+    // G. Matrix-core kernels: one workgroup slice of 16, 8 or 4 heads (MFMA
+    // columns); the quantised-cache kernel also takes slices of 2 or 1.
+    const int32_t gw = mfma ? (G % 16 == 0 ? 16 : G % 8 == 0 ? 8 : G % 4 == 0 ? 4 : G % 2 == 0 ? 2 : 1)
                             : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
     // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
     // (PA_DECODE_RING: 1 or 2).
     int32_t ring = env_int("PA_DECODE_RING", 1);
     if (ring != 1 && ring != 2) ring = 1;
+    if (quant) ring = 1;   // the quantised-cache kernel keeps one block in flight per wave
     const int64_t units = (int64_t)batch * c->n_kv * hs;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
     int32_t hs_wg = 1, waves_tok, bpw, nparts_max;
     if (mfma) {
         mfma_partitions(units, max_blocks, &waves_tok, &bpw, &nparts_max);
-        while (waves_tok > 1 && waves_tok * mfma_wave_bytes(ring, tile, gw, c->head_dim) > kLdsBytes) --waves_tok;
+        const int32_t wave_lds = quant ? pa::quant_wave_bytes(c->head_dim, gw)
+                                       : mfma_wave_bytes(ring, tile, gw, c->head_dim);
+        while (waves_tok > 1 && waves_tok * wave_lds > kLdsBytes) --waves_tok;
         nparts_max = std::max(1, (max_blocks + waves_tok * bpw - 1) / (waves_tok * bpw));
     } else {
         // VALU kernel: 8 waves when there are at least as many (sequence, KV head,
@@ -205,8 +220,8 @@ size_t plan_bytes(const Plan& pl) {
 }
 
 int check_decode_args(int32_t batch, int32_t n_q, const pa_cache_desc* cache,
-                      int32_t max_blocks_per_seq) {
-    int rc = check_cache(cache);
+                      int32_t max_blocks_per_seq, bool allow_quant = false) {
+    int rc = check_cache(cache, allow_quant);
     if (rc) return rc;
     if (batch < 0) return fail(PA_ERR_INVALID_ARG, "batch %d < 0", batch);
     if (n_q <= 0) return fail(PA_ERR_INVALID_ARG, "n_q %d must be positive", n_q);
@@ -370,7 +385,7 @@ int resolve_workspace(size_t need, void** ws) {
 
 extern "C" {
 
-int32_t pa_version(void) { return 200; }
+int32_t pa_version(void) { return 201; }
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -417,7 +432,7 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
 
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
                                  const pa_cache_desc* cache) {
-    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK) return 0;
+    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq, true) != PA_OK) return 0;
     // A windowed call plans for a shorter span of blocks; the size returned covers
     // the plan of every span up to max_blocks_per_seq.
     size_t most = 0;
@@ -735,6 +750,123 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (e == hipErrorNotSupported)
         return fail(PA_ERR_UNSUPPORTED, "chunked prefill: no kernel for these arguments");
     if (e != hipSuccess) return hip_fail(e, "chunked prefill launch");
+    return PA_OK;
+}
+
+
+int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const int64_t* slot_mapping,
+                       int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                       const pa_cache_desc* cache, void* stream) {
+    int rc = check_cache(cache, true);
+    if (rc) return rc;
+    if (!is_quant(cache->dtype))
+        return fail(PA_ERR_INVALID_ARG, "kv_append_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8");
+    if (src_dtype != PA_F32 && src_dtype != PA_BF16 && src_dtype != PA_F16)
+        return fail(PA_ERR_UNSUPPORTED, "kv_append_quant: k and v must be f32, bf16 or f16");
+    if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
+    if (num_tokens == 0) return PA_OK;
+    if (!k || !v || !slot_mapping || !k_cache || !v_cache || !k_scale || !v_scale)
+        return fail(PA_ERR_INVALID_ARG, "kv_append_quant: a pointer argument is NULL");
+    if (!aligned16(k) || !aligned16(v) || !aligned16(k_cache) || !aligned16(v_cache) ||
+        !aligned16(k_scale) || !aligned16(v_scale))
+        return fail(PA_ERR_INVALID_ARG, "kv_append_quant: k, v, the caches and the scales must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(slot_mapping) & 7u) != 0)
+        return fail(PA_ERR_INVALID_ARG, "kv_append_quant: slot_mapping must be 8-byte aligned");
+    if (validate_enabled()) {
+        std::vector<int64_t> slots;
+        rc = validate_slots(slot_mapping, num_tokens, cache, static_cast<hipStream_t>(stream), slots);
+        if (rc) return rc;
+    }
+    const hipError_t e = pa::launch_kv_append_quant(
+        k, v, to_elem(src_dtype), static_cast<pa::QuantFmt>(static_cast<int>(cache->dtype)), slot_mapping,
+        num_tokens, cache->n_kv, cache->head_dim, (int64_t)cache->num_blocks * cache->block_size, k_cache,
+        v_cache, k_scale, v_scale, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "kv_append_quant launch");
+    return PA_OK;
+}
+
+int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const pa_cache_desc* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq, true);
+    if (rc) return rc;
+    if (!is_quant(cache->dtype))
+        return fail(PA_ERR_INVALID_ARG, "decode_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8");
+    if (q_dtype != PA_BF16 && q_dtype != PA_F16)
+        return fail(PA_ERR_UNSUPPORTED, "decode_quant: q must be bf16 or f16");
+    if (out_dtype != PA_F32 && out_dtype != q_dtype)
+        return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or q_dtype");
+    if (!(scale > 0.f) || !std::isfinite(scale))
+        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (batch == 0) return PA_OK;
+    if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out)
+        return fail(PA_ERR_INVALID_ARG, "decode_quant: a pointer argument is NULL");
+    if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(k_scale) ||
+        !aligned16(v_scale) || !aligned16(out))
+        return fail(PA_ERR_INVALID_ARG, "decode_quant: q, caches, scales and out must be 16-byte aligned");
+    if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
+        return fail(PA_ERR_INVALID_ARG, "decode_quant: block_table and context_lens must be 4-byte aligned");
+
+    Plan pl;
+    make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
+    const size_t need = plan_bytes(pl);
+    if (need > 0) {
+        if (!workspace) {
+            rc = resolve_workspace(need, &workspace);
+            if (rc) return rc;
+        } else if (workspace_bytes < need) {
+            return fail(PA_ERR_INVALID_ARG, "decode_quant: workspace of %zu bytes required (got %zu)", need,
+                        workspace_bytes);
+        }
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "decode_quant: workspace must be 16-byte aligned");
+    }
+    if (validate_enabled()) {
+        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
+                             static_cast<hipStream_t>(stream), 1, window);
+        if (rc) return rc;
+    }
+
+    pa::DecodeArgs a{};
+    a.q = q;
+    a.k_cache = k_cache;
+    a.v_cache = v_cache;
+    a.k_scale = k_scale;
+    a.v_scale = v_scale;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    if (need > 0) {
+        char* w = static_cast<char*>(workspace);
+        a.ws_m = reinterpret_cast<float*>(w);
+        a.ws_l = reinterpret_cast<float*>(w + round16(pl.ws_floats_m * sizeof(float)));
+        a.ws_acc = reinterpret_cast<float*>(w + 2 * round16(pl.ws_floats_m * sizeof(float)));
+    }
+    a.batch = batch;
+    a.n_q = n_q;
+    a.n_kv = cache->n_kv;
+    a.num_blocks = cache->num_blocks;
+    a.max_blocks = max_blocks_per_seq;
+    a.group = n_q / cache->n_kv;
+    a.gw = pl.gw;
+    a.hs_wg = pl.hs_wg;
+    a.hsg = pl.hsg;
+    a.waves_tok = pl.waves_tok;
+    a.blocks_per_wave = pl.blocks_per_wave;
+    a.nparts_max = pl.nparts_max;
+    a.ring = pl.ring;
+    a.mfma = 1;
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.out_f32 = out_dtype == PA_F32;
+    a.q_rows = 1;
+    a.window = window;
+    const hipError_t e = pa::launch_decode_quant(a, to_elem(q_dtype),
+                                                 static_cast<pa::QuantFmt>(static_cast<int>(cache->dtype)),
+                                                 cache->head_dim, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "decode_quant launch");
     return PA_OK;
 }
 

@@ -149,6 +149,17 @@ __device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds_dst)
         : "memory", "m0");
 }
 
+// Asynchronous copy of 4 bytes per lane from `src` to LDS at lds_dst + 4 * lane.
+__device__ __forceinline__ void copy_to_lds4(const void* src, uint32_t lds_dst) {
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(src)
+        : "memory", "m0");
+}
+
 // Wait until at most N vector-memory operations of this wave are outstanding.
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
     static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");

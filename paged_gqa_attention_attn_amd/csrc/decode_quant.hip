@@ -1,0 +1,411 @@
+// decode_quant.hip -- paged GQA decode over a quantised (FP8 E4M3 or INT8) KV cache,
+// on the gfx950 matrix cores.
+//
+// The cache keeps every (token, KV head) row of K and of V as one-byte codes and
+// one fp32 scale, value = code * scale ("LLM 推理全过程的维度变化与核心公式",
+// research.frankk.site, "KV Cache 的形状与增长": the fp16 cache quantised to
+// int8 / fp8 per token; the dimension-walkthrough page counts FP8 as one byte
+// per element). Decode reads half the bytes of a bf16 cache for the same
+// context. The work decomposition is that of decode_mfma.hip (one workgroup per
+// head slice of a KV head and partition, each wave a contiguous run of 16-token
+// blocks through its own LDS ring, cross-wave merge in LDS, partials for the
+// log-sum-exp reduce kernel when a context is split); what changes per block:
+//
+//  * Each block brings a D-byte-per-row K tile, a V tile and the two 16-float
+//    scale vectors, all by global_load_lds (the scales with one dword copy whose
+//    lanes 0-15 fetch K scales and 16-31 V scales).
+//  * The K operand of S^T = K q^T is 8 codes per lane widened in registers to
+//    the query's type (FP8: v_cvt_scalef32_pk_{bf16,f16}_fp8 with scale 1, an
+//    exact conversion; INT8: through fp32, exact), so the product runs on the
+//    bf16/f16 matrix cores; the K scale multiplies the 4 scores each lane holds.
+//  * The V scale folds into P (P' = P * v_scale per key; the softmax
+//    denominator keeps P), and V^T is gathered from the row-major code tile with
+//    byte reads (4 keys of one dim per lane) and widened the same way.
+//  * Codes of rows outside [first, ctx) are zeroed in LDS and their P' is
+//    selected to 0: an unused slot may hold a NaN code or a NaN scale.
+// Rows are stored with their 16-byte chunk c at position c ^ swz(row), swz
+// chosen for one-byte rows so that both operand reads stay conflict-free.
+#include <type_traits>
+
+#include "common.h"
+#include "launch.h"
+#include "mfma.h"
+
+namespace pa {
+
+namespace {
+
+constexpr int BS = 16;
+constexpr float TAU = 8.0f;
+constexpr int MAX_WAVES = 8;
+
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+
+struct QFp8 {};
+struct QInt8 {};
+
+// Four one-byte codes (bytes 0..3 of w) as four elements of a 16-bit operand of type E.
+template <class Q, class E> __device__ __forceinline__ uint2 widen4(uint32_t w);
+template <> __device__ __forceinline__ uint2 widen4<QFp8, BF16>(uint32_t w) {
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, 1.0f, true)));
+}
+template <> __device__ __forceinline__ uint2 widen4<QFp8, F16>(uint32_t w) {
+    return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
+                      __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
+}
+// A signed byte is exact in fp32, and its fp32 value has at most 7 significant
+// bits, so the upper half of the fp32 pattern is the exact bf16.
+template <> __device__ __forceinline__ uint2 widen4<QInt8, BF16>(uint32_t w) {
+    uint32_t h[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) h[i] = as_u32((float)(int8_t)(w >> (8 * i))) >> 16;
+    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+}
+template <> __device__ __forceinline__ uint2 widen4<QInt8, F16>(uint32_t w) {
+    f16x2_t a, b;
+    a[0] = (_Float16)(float)(int8_t)w;
+    a[1] = (_Float16)(float)(int8_t)(w >> 8);
+    b[0] = (_Float16)(float)(int8_t)(w >> 16);
+    b[1] = (_Float16)(float)(int8_t)(w >> 24);
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
+}
+
+template <class E> struct Mfma16;
+template <> struct Mfma16<BF16> {
+    static __device__ __forceinline__ f32x4_t qk(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                       __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(i16x4_t, a),
+                                                         __builtin_bit_cast(i16x4_t, b), c, 0, 0, 0);
+    }
+};
+template <> struct Mfma16<F16> {
+    static __device__ __forceinline__ f32x4_t qk(u32x4_t a, u32x4_t b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a),
+                                                      __builtin_bit_cast(f16x8_t, b), c, 0, 0, 0);
+    }
+    static __device__ __forceinline__ f32x4_t pv(uint2 a, uint2 b, f32x4_t c) {
+        return __builtin_amdgcn_mfma_f32_16x16x16f16(__builtin_bit_cast(f16x4_t, a),
+                                                     __builtin_bit_cast(f16x4_t, b), c, 0, 0, 0);
+    }
+};
+
+template <int D, int HW> struct QLayout {
+    static constexpr int ROW = D;                     // bytes per token row (one-byte codes)
+    static constexpr int CPR = ROW / 16;              // 16-byte chunks per row: 8 or 4
+    static constexpr int TILE = BS * ROW;             // one (block, KV head) code tile
+    static constexpr int NQ = TILE / 1024;            // 1 KB wave copies per tile
+    static constexpr int SC = 256;                    // scale copy: K scales, V scales, repeat
+    static constexpr int SLOTB = 2 * TILE + SC;       // one ring slot
+    static constexpr int OPS = 2 * NQ + 1;            // vector-memory operations per block
+    static constexpr int PITCH = D + 4;
+    static constexpr int SLOT = HW * PITCH + 2 * HW;  // merge slot floats
+    static constexpr int WAVE_BYTES = ((SLOTB > SLOT * 4 ? SLOTB : SLOT * 4) + 15) / 16 * 16;
+    // Rows of the 16 keys share 256-byte bank lines 256 / ROW at a time; rows of one
+    // line get distinct chunk masks and rows of the same line position distinct ones.
+    static __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
+};
+
+template <class Q, class E, int D, int HW>
+__global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const DecodeArgs p) {
+    using L = QLayout<D, HW>;
+    using S = typename E::storage;
+    constexpr int ROW = L::ROW, TILE = L::TILE, NQ = L::NQ, OPS = L::OPS;
+    constexpr int KK = D / 32;    // S^T k-steps
+    constexpr int MT = D / 16;    // O^T tiles
+    static_assert(HW == 1 || HW == 2 || HW == 4 || HW == 8 || HW == 16, "1 to 16 MFMA columns");
+    static_assert(TILE % 1024 == 0, "tiles move in whole 1 KB copies");
+    static_assert(OPS < 64, "one block's copies fit the vmcnt counter");
+
+    extern __shared__ __attribute__((aligned(16))) char smem[];
+
+    const int part = blockIdx.x;
+    const int g = blockIdx.y / p.hsg;
+    const int hsgi = blockIdx.y % p.hsg;
+    const int b = blockIdx.z;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15;
+    const int grp = lane >> 4;
+
+    const int h0 = g * p.group + hsgi * HW;
+    const int blk0 = part * p.waves_tok * p.blocks_per_wave + wave * p.blocks_per_wave;
+    u32x4_t qreg[KK];
+    {
+        const char* qrow = (const char*)p.q + (int64_t)(b * p.n_q + h0 + (col < HW ? col : 0)) * (D * 2);
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) {
+            uint4 v = make_uint4(0, 0, 0, 0);
+            if (col < HW) v = *reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2);
+            qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
+        }
+    }
+    int my_phys = 0;
+    if (lane < p.blocks_per_wave && blk0 + lane < p.max_blocks)
+        my_phys = p.block_table[(int64_t)b * p.max_blocks + blk0 + lane];
+
+    const int cap = p.max_blocks * BS;
+    const int ctx_in = __builtin_amdgcn_readfirstlane(p.context_lens[b]);
+    const bool ctx_bad = ctx_in > cap;
+    const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
+    const int nblk = (ctx + BS - 1) / BS;
+    const int first = window_first(ctx, 1, p.window);
+    const int fb = first / BS;
+    const int bpp = p.waves_tok * p.blocks_per_wave;
+    const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
+    if (part >= nparts) return;
+    const int wb0 = blk0 + fb;
+    if (fb > 0) {
+        my_phys = 0;
+        if (lane < p.blocks_per_wave && wb0 + lane < p.max_blocks)
+            my_phys = p.block_table[(int64_t)b * p.max_blocks + wb0 + lane];
+    }
+    const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
+    const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
+
+    char* ring = smem + wave * L::WAVE_BYTES;
+    const uint32_t ring_lds = lds_addr(ring);
+    const int64_t block_bytes = (int64_t)p.n_kv * TILE;
+    uint32_t src_off[NQ];
+#pragma unroll
+    for (int qq = 0; qq < NQ; ++qq) {
+        const int off = qq * 1024 + 16 * lane;
+        const int r = off / ROW;
+        src_off[qq] = r * ROW + (((off % ROW) / 16) ^ L::swz(r)) * 16;
+    }
+    const char* kbase = (const char*)p.k_cache + (int64_t)g * TILE;
+    const char* vbase = (const char*)p.v_cache + (int64_t)g * TILE;
+    // Scale copy: lanes 0-15 the K scales of the block's 16 rows, 16-31 the V
+    // scales, 32-63 the same again (landing in the unused half of the slot).
+    const float* sbase = ((lane >> 4) & 1 ? p.v_scale : p.k_scale) + (int64_t)g * BS + (lane & 15);
+    auto issue = [&](int i) {
+        const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
+        const uint32_t dst = ring_lds;   // one block in flight per wave
+        const char* kb = kbase + phys * block_bytes;
+        const char* vb = vbase + phys * block_bytes;
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024);
+#pragma unroll
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024);
+        copy_to_lds4(sbase + phys * p.n_kv * BS, dst + 2 * TILE);
+    };
+
+    uint32_t k_off[KK];   // K operand: row col, bytes 32 kk + 8 grp .. +8
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) {
+        const int c = 2 * kk + (grp >> 1);
+        k_off[kk] = col * ROW + ((c ^ L::swz(col)) * 16) + 8 * (grp & 1);
+    }
+    uint32_t v_off[4];    // V^T gather: byte col of row 4 grp + e, chunk t (t added below)
+    int v_sw[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        v_off[e] = TILE + (4 * grp + e) * ROW + col;
+        v_sw[e] = L::swz(4 * grp + e);
+    }
+
+    f32x4_t o[MT];
+#pragma unroll
+    for (int t = 0; t < MT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float m_run = -INFINITY;
+    float l_run = 0.f;
+
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) asm volatile("" : : "v"(qreg[kk]));
+
+    if (!phys_bad && nb > 0) {
+        issue(0);
+        for (int i = 0; i < nb; ++i) {
+            wait_vmcnt<0>();
+            char* base = ring;
+            const int pos0 = (wb0 + i) * BS;
+            const bool edge = pos0 + BS > ctx || pos0 < first;   // uniform
+            if (edge) {
+                // Zero the V code rows outside [first, ctx) (whole rows).
+#pragma unroll
+                for (int k = 0; k < BS * L::CPR / 64; ++k) {
+                    const int idx = k * 64 + lane;
+                    const int r = idx / L::CPR;
+                    const int pos = pos0 + r;
+                    if (pos >= ctx || pos < first)
+                        *reinterpret_cast<uint4*>(base + TILE + r * ROW + (idx % L::CPR) * 16) = make_uint4(0, 0, 0, 0);
+                }
+            }
+            u32x4_t ka[KK];
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const uint2 c8 = *reinterpret_cast<const uint2*>(base + k_off[kk]);
+                const uint2 lo = widen4<Q, E>(c8.x), hi = widen4<Q, E>(c8.y);
+                ka[kk] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+            }
+            uint2 va[MT];
+#pragma unroll
+            for (int t = 0; t < MT; ++t) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w |= (uint32_t)*reinterpret_cast<const uint8_t*>(base + v_off[e] + ((t ^ v_sw[e]) * 16)) << (8 * e);
+                va[t] = widen4<Q, E>(w);
+            }
+            const float4 ks = *reinterpret_cast<const float4*>(base + 2 * TILE + 16 * grp);
+            const float4 vs = *reinterpret_cast<const float4*>(base + 2 * TILE + 64 + 16 * grp);
+            lds_reads_done();
+            if (i + 1 < nb) issue(i + 1);
+
+            f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < KK; ++kk) s = Mfma16<E>::qk(ka[kk], qreg[kk], s);
+            s[0] *= ks.x;
+            s[1] *= ks.y;
+            s[2] *= ks.z;
+            s[3] *= ks.w;
+            bool live[4] = {true, true, true, true};
+            if (edge) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int pos = pos0 + 4 * grp + j;
+                    live[j] = pos < ctx && pos >= first;
+                    s[j] = live[j] ? s[j] : -INFINITY;
+                }
+            }
+            float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * p.scale_log2;
+            if (__any(bm > m_run + TAU)) {
+                const float m_new = fmaxf(m_run, stride_reduce<16, true>(bm));
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                l_run *= alpha;
+#pragma unroll
+                for (int t = 0; t < MT; ++t) o[t] *= alpha;
+                m_run = m_new;
+            }
+            const float vsc[4] = {vs.x, vs.y, vs.z, vs.w};
+            float pr[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -m_run));
+                l_run += pj;
+                pr[j] = live[j] ? pj * vsc[j] : 0.f;   // V scale folded into P
+            }
+            const uint2 ph = make_uint2(Mfma<E>::pack(pr[0], pr[1]), Mfma<E>::pack(pr[2], pr[3]));
+#pragma unroll
+            for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
+            if constexpr (Mfma<E>::kSplit) {
+                const uint2 pl = make_uint2(Mfma<E>::pack(pr[0] - Mfma<E>::lo_of(ph.x), pr[1] - Mfma<E>::hi_of(ph.x)),
+                                            Mfma<E>::pack(pr[2] - Mfma<E>::lo_of(ph.y), pr[3] - Mfma<E>::hi_of(ph.y)));
+#pragma unroll
+                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], pl, o[t]);
+            }
+        }
+    }
+
+    l_run = stride_reduce<16, false>(l_run);
+    float* mine = reinterpret_cast<float*>(ring);
+    if (col < HW) {
+#pragma unroll
+        for (int t = 0; t < MT; ++t)
+            *reinterpret_cast<f32x4_t*>(mine + col * L::PITCH + 16 * t + 4 * grp) = o[t];
+        if (grp == 0) {
+            mine[HW * L::PITCH + col] = phys_bad ? 0.f : m_run;
+            mine[HW * L::PITCH + HW + col] = phys_bad ? NAN : l_run;
+        }
+    }
+    __syncthreads();
+
+    for (int idx = threadIdx.x; idx < HW * D; idx += blockDim.x) {
+        const int hl = idx / D;
+        const int e = idx % D;
+        float mw[MAX_WAVES], lw[MAX_WAVES], aw[MAX_WAVES];
+#pragma unroll
+        for (int w = 0; w < MAX_WAVES; ++w) {
+            const bool live = w < p.waves_tok;
+            const float* ws = reinterpret_cast<const float*>(smem + (live ? w : 0) * L::WAVE_BYTES);
+            mw[w] = live ? ws[HW * L::PITCH + hl] : -INFINITY;
+            lw[w] = live ? ws[HW * L::PITCH + HW + hl] : 0.f;
+            aw[w] = live ? ws[hl * L::PITCH + e] : 0.f;
+        }
+        float M = -INFINITY;
+#pragma unroll
+        for (int w = 0; w < MAX_WAVES; ++w) M = fmaxf(M, mw[w]);
+        float Lsum = 0.f, A = 0.f;
+        if (M != -INFINITY) {
+#pragma unroll
+            for (int w = 0; w < MAX_WAVES; ++w) {
+                const float f = __builtin_amdgcn_exp2f(mw[w] - M);
+                Lsum = fmaf(f, lw[w], Lsum);
+                A = fmaf(f, aw[w], A);
+            }
+        }
+        const int64_t row = (int64_t)b * p.n_q + h0 + hl;
+        if (nparts == 1) {
+            float o1 = (Lsum == 0.f) ? 0.f : A * __builtin_amdgcn_rcpf(Lsum);
+            if (ctx_bad) o1 = NAN;
+            if (p.out_f32)
+                reinterpret_cast<float*>(p.out)[row * D + e] = o1;
+            else
+                reinterpret_cast<S*>(p.out)[row * D + e] = narrow<E>(o1);
+        } else {
+            const int64_t pi = row * p.nparts_max + part;
+            if (e == 0) {
+                p.ws_m[pi] = M;
+                p.ws_l[pi] = Lsum;
+            }
+            p.ws_acc[pi * D + e] = A;
+        }
+    }
+}
+
+template <class Q, class E, int D, int HW> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)a.waves_tok * QLayout<D, HW>::WAVE_BYTES;
+    if (lds > 160 * 1024) return hipErrorInvalidValue;
+    static const hipError_t opt_in = hipFuncSetAttribute(
+        reinterpret_cast<const void*>(&decode_quant_kernel<Q, E, D, HW>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
+    if (opt_in != hipSuccess) return opt_in;
+    const dim3 grid(a.nparts_max, a.n_kv * a.hsg, a.batch);
+    hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW>), grid, dim3(64 * a.waves_tok), lds, s, a);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || a.nparts_max <= 1) return err;
+    return launch_decode_reduce(a, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
+}
+
+template <class Q, class E, int D> hipError_t launch_hw(const DecodeArgs& a, hipStream_t s) {
+    switch (a.gw) {
+    case 1: return launch_typed<Q, E, D, 1>(a, s);
+    case 2: return launch_typed<Q, E, D, 2>(a, s);
+    case 4: return launch_typed<Q, E, D, 4>(a, s);
+    case 8: return launch_typed<Q, E, D, 8>(a, s);
+    case 16: return launch_typed<Q, E, D, 16>(a, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+template <class Q, class E> hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t s) {
+    if (head_dim == 128) return launch_hw<Q, E, 128>(a, s);
+    if (head_dim == 64) return launch_hw<Q, E, 64>(a, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+int quant_wave_bytes(int head_dim, int hw) {
+    const int tile = BS * head_dim;
+    const int slotb = 2 * tile + 256;
+    const int slot = (hw * (head_dim + 4) + 2 * hw) * 4;
+    return ((slotb > slot ? slotb : slot) + 15) / 16 * 16;
+}
+
+hipError_t launch_decode_quant(const DecodeArgs& a, Elem q_type, QuantFmt fmt, int head_dim, hipStream_t s) {
+    if (a.hs_wg != 1 || a.waves_tok < 1 || a.waves_tok > MAX_WAVES) return hipErrorInvalidValue;
+    if (a.q_rows != 1 || a.window < 0 || !a.k_scale || !a.v_scale) return hipErrorInvalidValue;
+    if (fmt == QuantFmt::FP8_E4M3 && q_type == Elem::BF16) return launch_dim<QFp8, BF16>(a, head_dim, s);
+    if (fmt == QuantFmt::FP8_E4M3 && q_type == Elem::F16) return launch_dim<QFp8, F16>(a, head_dim, s);
+    if (fmt == QuantFmt::INT8 && q_type == Elem::BF16) return launch_dim<QInt8, BF16>(a, head_dim, s);
+    if (fmt == QuantFmt::INT8 && q_type == Elem::F16) return launch_dim<QInt8, F16>(a, head_dim, s);
+    return hipErrorInvalidValue;
+}
+
+}  // namespace pa

@@ -7,6 +7,8 @@
 namespace pa {
 
 enum class Elem { F32 = 0, BF16 = 1, F16 = 2 };
+// One-byte cache formats (codes plus one fp32 scale per token row).
+enum class QuantFmt { FP8_E4M3 = 3, INT8 = 4 };
 
 // Everything a decode launch needs; filled by the host plan in api.hip.
 struct DecodeArgs {
@@ -46,6 +48,9 @@ struct DecodeArgs {
     // Single-row decode on the matrix cores (decode_mfma.hip): gw query heads
     // (4, 8 or 16) per workgroup fill the MFMA columns; hs_wg must be 1.
     int32_t mfma;
+    // Quantised cache (decode_quant.hip): per-row scales [num_blocks][n_kv][16].
+    const float* k_scale;
+    const float* v_scale;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
@@ -55,6 +60,15 @@ hipError_t launch_decode_mfma(const DecodeArgs& a, Elem e, int head_dim, hipStre
 hipError_t launch_decode_reduce(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
 // Multi-row decode on the matrix cores (bf16/f16), plus the merge when contexts split.
 hipError_t launch_decode_multi(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
+
+// Decode over a quantised cache (codes + per-row scales), q in q_type (bf16 or f16).
+hipError_t launch_decode_quant(const DecodeArgs& a, Elem q_type, QuantFmt fmt, int head_dim, hipStream_t s);
+// LDS bytes one wave of the quantised decode kernel takes for hw heads.
+int quant_wave_bytes(int head_dim, int hw);
+// Quantise k/v rows ([T][n_kv][D] in src) per row into codes + scales at slot_mapping.
+hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, const int64_t* slots,
+                                  int32_t num_tokens, int32_t n_kv, int32_t head_dim, int64_t num_slots,
+                                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, hipStream_t s);
 
 hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
                             int32_t n_kv, int32_t row_bytes, int32_t block_size,

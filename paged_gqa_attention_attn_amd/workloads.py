@@ -209,6 +209,104 @@ def make_decode_case(*, batch: int, n_q: int, n_kv: int, head_dim: int, context_
         shared_prefix_blocks=n_pref, sharers=sharers, free_blocks=free)
 
 
+@dataclass
+class QuantDecodeCase:
+    """A decode step over a quantised cache: one-byte codes and one fp32 scale per row."""
+
+    name: str
+    fmt: str                    # "fp8" (OCP E4M3 bit patterns, uint8) or "int8"
+    q_dtype: str                # "bf16" or "f16"
+    batch: int
+    n_q: int
+    n_kv: int
+    head_dim: int
+    block_size: int
+    num_blocks: int
+    scale: float
+    q: torch.Tensor             # [B][n_q][d] in q_dtype
+    k_pool: torch.Tensor        # codes [num_blocks][n_kv][bs][d]
+    v_pool: torch.Tensor
+    k_scale: torch.Tensor       # float32 [num_blocks][n_kv][bs]
+    v_scale: torch.Tensor
+    block_table: torch.Tensor
+    context_lens: torch.Tensor
+    new_k: torch.Tensor         # [B][n_kv][d] in q_dtype: the step's new token, unquantised
+    new_v: torch.Tensor
+    slot_mapping: torch.Tensor
+    free_blocks: np.ndarray
+    max_blocks_per_seq: int = 0
+
+
+QUANT_CODE_DTYPES = {"fp8": torch.uint8, "int8": torch.int8}
+QUANT_QMAX = {"fp8": 448.0, "int8": 127.0}
+
+
+def make_quant_decode_case(*, fmt: str, q_dtype: str = "bf16", batch: int, n_q: int, n_kv: int,
+                           head_dim: int, context_lens, free_fraction: float = 0.0,
+                           num_blocks: int | None = None, max_blocks_per_seq: int | None = None,
+                           seed: int = 0, device="cpu", name: str = "quant",
+                           row_amax: float = 3.5) -> QuantDecodeCase:
+    """Same table, slots and poisoned positions as make_decode_case, with the pools drawn
+    directly as codes and scales: codes uniform over the format's finite codes (FP8 E4M3
+    without its two NaN patterns, INT8 in [-127, 127]), scales row_amax / QMAX times
+    U[0.5, 1.5] (a row of N(0,1) values has |x| max around 3.5). Free blocks and the
+    slots past each context hold the FP8 NaN code 0x7F (INT8: -128) and a NaN scale.
+    q and the new rows are N(0,1)."""
+    if fmt not in QUANT_CODE_DTYPES:
+        raise ValueError("fmt must be 'fp8' or 'int8'")
+    base = make_decode_case(batch=batch, n_q=n_q, n_kv=n_kv, head_dim=head_dim,
+                            context_lens=context_lens, dtype=q_dtype, free_fraction=free_fraction,
+                            num_blocks=num_blocks, max_blocks_per_seq=max_blocks_per_seq,
+                            seed=seed, device=device, name=name, values=False)
+    gen = _gen(device, seed + 7919)
+    shape = (base.num_blocks, n_kv, base.block_size, head_dim)
+
+    def codes():
+        if fmt == "fp8":
+            c = torch.randint(0, 254, shape, generator=gen, device=device, dtype=torch.int32)
+            c = c + (c >= 0x7F).to(torch.int32)          # skip 0x7F; 0xFF is never drawn
+            return c.to(torch.uint8)
+        return torch.randint(-127, 128, shape, generator=gen, device=device, dtype=torch.int32).to(torch.int8)
+
+    def scales():
+        u = torch.rand(shape[:3], generator=gen, device=device, dtype=torch.float32)
+        return (row_amax / QUANT_QMAX[fmt]) * (0.5 + u)
+
+    k_pool, v_pool = codes(), codes()
+    k_scale, v_scale = scales(), scales()
+    # Poison the free blocks and, in each sequence's last block, the slots past its
+    # context. The new token's row (position ctx - 1) holds a valid code row, so the
+    # case decodes as it stands; an append of new_k / new_v overwrites it.
+    poison = 0x7F if fmt == "fp8" else -128
+    nan = float("nan")
+    if base.free_blocks.size:
+        idx = torch.as_tensor(base.free_blocks.astype(np.int64), device=device)
+        for t in (k_pool, v_pool):
+            t[idx] = poison
+        for t in (k_scale, v_scale):
+            t[idx] = nan
+    bs = base.block_size
+    for b, ctx in enumerate(base.context_lens.tolist()):
+        if ctx == 0:
+            continue
+        if ctx % bs == 0:
+            continue
+        last = int(base.block_table[b, (ctx - 1) // bs])
+        for t in (k_pool, v_pool):
+            t[last, :, ctx % bs:, :] = poison
+        for t in (k_scale, v_scale):
+            t[last, :, ctx % bs:] = nan
+    q = _randn((batch, n_q, head_dim), q_dtype, gen, device)
+    new_k = _randn((batch, n_kv, head_dim), q_dtype, gen, device)
+    new_v = _randn((batch, n_kv, head_dim), q_dtype, gen, device)
+    return QuantDecodeCase(
+        name=name, fmt=fmt, q_dtype=q_dtype, batch=batch, n_q=n_q, n_kv=n_kv, head_dim=head_dim,
+        block_size=bs, num_blocks=base.num_blocks, scale=base.scale, q=q, k_pool=k_pool,
+        v_pool=v_pool, k_scale=k_scale, v_scale=v_scale, block_table=base.block_table,
+        context_lens=base.context_lens, new_k=new_k, new_v=new_v, slot_mapping=base.slot_mapping,
+        free_blocks=base.free_blocks, max_blocks_per_seq=base.block_table.shape[1])
+
+
 def make_prefill_case(*, batch: int, seq_len: int, n_q: int, n_kv: int, head_dim: int,
                       dtype: str = "bf16", block_size: int = 16, seed: int = 0, device="cpu",
                       name: str = "custom") -> PrefillCase:

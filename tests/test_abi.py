@@ -44,7 +44,7 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 200
+    assert L.pa_version() == 201
 
 
 def decode(L, **kw):
@@ -270,3 +270,76 @@ def test_decode_multi_workspace_query(L):
     assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 256, desc(nb=4096, n_kv=8)) == 2 * rows * 4 + rows * 128 * 4
     assert L.pa_decode_multi_workspace_bytes(4, 0, 32, 256, desc(nb=4096, n_kv=8)) == 0
     assert multi(L, B=0) == PA_OK
+
+
+# ---- quantised cache entry points --------------------------------------------------------
+
+FP8, INT8 = _lib.PA_FP8_E4M3, _lib.PA_INT8
+
+
+def decode_quant(L, **kw):
+    a = dict(q=FAKE, q_dtype=_lib.PA_BF16, batch=2, n_q=8, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
+             cache=desc(dtype=FP8), bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, out=FAKE,
+             out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return L.pa_paged_attn_decode_quant(a["q"], a["q_dtype"], a["batch"], a["n_q"], a["k"], a["v"],
+                                        a["ks"], a["vs"], a["cache"], a["bt"], a["maxb"], a["ctx"],
+                                        a["scale"], a["window"], a["out"], a["out_dtype"], a["ws"],
+                                        a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=desc(dtype=_lib.PA_BF16)), INVALID, "PA_FP8_E4M3"),
+    (dict(q_dtype=_lib.PA_F32), UNSUPPORTED, "q must be"),
+    (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+    (dict(ks=None), INVALID, "NULL"),
+    (dict(vs=FAKE + 4), INVALID, "aligned"),
+    (dict(cache=desc(dtype=INT8, d=96)), UNSUPPORTED, "head_dim"),
+    (dict(n_q=7), INVALID, "multiple"),
+    (dict(scale=0.0), INVALID, "positive"),
+    (dict(window=-2), INVALID, "window"),
+])
+def test_decode_quant_rejects(L, kw, code, msg):
+    assert decode_quant(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_quantised_cache_refused_elsewhere(L):
+    # The bf16/f16 entry points do not take a quantised cache description.
+    assert decode(L, cache=desc(dtype=FP8)) == UNSUPPORTED
+    assert "quantised" in _lib.last_error()
+    assert L.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, desc(dtype=INT8), None) == UNSUPPORTED
+
+
+def append_quant(L, **kw):
+    a = dict(k=FAKE, v=FAKE, src=_lib.PA_BF16, slots=FAKE, T=4, kc=FAKE, vc=FAKE, ks=FAKE, vs=FAKE,
+             cache=desc(dtype=FP8), stream=None)
+    a.update(kw)
+    return L.pa_kv_append_quant(a["k"], a["v"], a["src"], a["slots"], a["T"], a["kc"], a["vc"],
+                                a["ks"], a["vs"], a["cache"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=desc(dtype=_lib.PA_F16)), INVALID, "PA_FP8_E4M3"),
+    (dict(src=FP8), UNSUPPORTED, "f32, bf16 or f16"),
+    (dict(T=-1), INVALID, "num_tokens"),
+    (dict(ks=None), INVALID, "NULL"),
+    (dict(slots=FAKE + 4), INVALID, "8-byte"),
+    (dict(kc=MISALIGNED), INVALID, "aligned"),
+])
+def test_append_quant_rejects(L, kw, code, msg):
+    assert append_quant(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_append_quant_no_tokens_is_a_noop(L):
+    assert append_quant(L, T=0) == PA_OK
+
+
+def test_quant_workspace_query(L):
+    # Same plan as the bf16 matrix-core decode: one partition for 32 x 8 units of
+    # 4096 tokens, four of 8 x 64 blocks for 8 x 8 units of 32768 tokens.
+    assert L.pa_decode_workspace_bytes(32, 32, 256, desc(nb=8192, n_kv=8, dtype=FP8)) == 0
+    rows = 8 * 64 * 4
+    assert L.pa_decode_workspace_bytes(8, 64, 2048, desc(nb=16384, n_kv=8, dtype=INT8)) == \
+        2 * rows * 4 + rows * 128 * 4

@@ -1,0 +1,217 @@
+"""GPU parity of the quantised KV cache (FP8 E4M3 / INT8 codes + one fp32 scale per row).
+
+kv_append_quant must give the oracle's codes and scales bit for bit (every step of
+the per-row quantiser is a correctly rounded fp32 operation). decode_quant over
+seeded code/scale pools must match the fp64 oracle, which attends over
+code * scale values, within max-abs 2e-3 and norm-wise relative 1e-2. Unused
+slots hold the FP8 NaN code (INT8: -128) and NaN scales and may not change any
+output bit; relabelling physical blocks may not either.
+"""
+import zlib
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_parity, same_bits, say, stored_np
+from paged_gqa_attention_attn_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_gqa_attention_attn_amd as pa
+    pa._lib.load()  # raises if the HIP library is missing: no fallback
+    return pa
+
+
+def _np(t):
+    return t.detach().cpu().contiguous().numpy()
+
+
+def _oracle_decode(c, k_pool=None, v_pool=None, k_scale=None, v_scale=None, window=0, sel=None):
+    return oracle.decode(stored_np(c.q), _np(c.k_pool if k_pool is None else k_pool),
+                         _np(c.v_pool if v_pool is None else v_pool), c.fmt,
+                         _np(c.block_table), _np(c.context_lens), c.scale, sel=sel, window=window,
+                         q_dtype=c.q_dtype, k_scale=_np(c.k_scale if k_scale is None else k_scale),
+                         v_scale=_np(c.v_scale if v_scale is None else v_scale))
+
+
+def _gpu_decode(pa, c, window=0, **kw):
+    out = pa.paged_attn_decode_quant(c.q, kw.get("k_pool", c.k_pool), kw.get("v_pool", c.v_pool),
+                                     kw.get("k_scale", c.k_scale), kw.get("v_scale", c.v_scale), c.fmt,
+                                     kw.get("block_table", c.block_table), c.context_lens, c.scale,
+                                     window=window, out_dtype=kw.get("out_dtype", torch.float32))
+    torch.cuda.synchronize()
+    return out
+
+
+# ---- kv_append_quant --------------------------------------------------------------------
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("src", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_quant_bit_exact(pa, fmt, src, d):
+    T, n_kv, nb = 300, 2, 40
+    g = torch.Generator(device="cuda").manual_seed(zlib.crc32(f"{fmt}{src}{d}".encode()))
+    dt = wl.TORCH_DTYPES[src]
+    k = (torch.randn((T, n_kv, d), generator=g, device="cuda") * 2.0).to(dt)
+    v = (torch.randn((T, n_kv, d), generator=g, device="cuda") * 0.01).to(dt)
+    k[3] = 0                      # an all-zero row: scale 0, codes 0
+    v[5, 1] = 0 if src == "f16" else 1e-38  # a row whose scale falls below the smallest normal
+    k[7, 0, :] = 448.0            # a row at the format's edge
+    slots = torch.as_tensor(np.random.default_rng(1).permutation(nb * 16)[:T], device="cuda")
+    slots[10] = -1                # padding
+    slots[11] = nb * 16 + 3       # past the pool: skipped
+    code_dt = wl.QUANT_CODE_DTYPES[fmt]
+    kc = torch.full((nb, n_kv, 16, d), 0x55, dtype=torch.uint8, device="cuda").view(code_dt)
+    vc = kc.clone()
+    ks = torch.full((nb, n_kv, 16), -7.0, dtype=torch.float32, device="cuda")
+    vs = ks.clone()
+    okc, ovc, oks, ovs = _np(kc).copy(), _np(vc).copy(), _np(ks).copy(), _np(vs).copy()
+    say(f"[quant append] {fmt} from {src}, d={d}, T={T}")
+    pa.kv_append_quant(k, v, slots, kc, vc, ks, vs, fmt)
+    torch.cuda.synchronize()
+    oslots = _np(slots).copy()
+    oslots[11] = -1               # the oracle rejects out-of-pool slots; the kernel skips them
+    oracle.kv_append_quant(stored_np(k), stored_np(v), src, oslots, okc, ovc, oks, ovs, fmt)
+    assert np.array_equal(_np(kc), okc), "K codes differ from the oracle"
+    assert np.array_equal(_np(vc), ovc), "V codes differ from the oracle"
+    assert np.array_equal(_np(ks).view(np.uint32), oks.view(np.uint32)), "K scales differ"
+    assert np.array_equal(_np(vs).view(np.uint32), ovs.view(np.uint32)), "V scales differ"
+
+
+# ---- decode over a quantised cache --------------------------------------------------------
+
+SHAPES = {
+    # name: (n_q, n_kv, head_dim, context lengths, q dtype)
+    "gqa4_d128": (8, 2, 128, [1, 15, 16, 17, 33, 300, 1000], "bf16"),
+    "gqa4_d64_f16": (8, 2, 64, [5, 64, 130], "f16"),
+    "gqa8_d128": (16, 2, 128, [2, 700, 2100], "bf16"),
+    "mha_d128": (4, 4, 128, [3, 90], "bf16"),
+    "gqa2_f16": (4, 2, 128, [7, 513], "f16"),
+    "mqa16_d128": (16, 1, 128, [40, 400], "bf16"),
+    "mqa32_d64": (32, 1, 64, [260], "bf16"),
+}
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("name", sorted(SHAPES))
+def test_decode_quant_matches_oracle(pa, fmt, name):
+    n_q, n_kv, d, ctx, qdt = SHAPES[name]
+    c = wl.make_quant_decode_case(fmt=fmt, q_dtype=qdt, batch=len(ctx), n_q=n_q, n_kv=n_kv,
+                                  head_dim=d, context_lens=ctx, free_fraction=0.25,
+                                  seed=zlib.crc32(f"{fmt}{name}".encode()) % 9973, device="cuda",
+                                  name=name)
+    say(f"[quant decode] {fmt} {name}: ctx={ctx}")
+    got = _gpu_decode(pa, c)
+    want = _oracle_decode(c)
+    stats = assert_parity(got.cpu().numpy(), want, qdt, f"{fmt} {name}")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+def _sweep_case(fmt):
+    return wl.make_quant_decode_case(fmt=fmt, batch=4, n_q=16, n_kv=4, head_dim=128,
+                                     context_lens=[3000, 1, 700, 2048], free_fraction=0.1,
+                                     seed=5, device="cuda", name="sweep")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("tokens", [256, 1024, 0])
+def test_decode_quant_partitions(pa, fmt, tokens):
+    c = _sweep_case(fmt)
+    prev = pa.set_decode_partition_tokens(tokens)
+    try:
+        say(f"[quant decode] {fmt} partition={tokens}")
+        got = _gpu_decode(pa, c)
+    finally:
+        pa.set_decode_partition_tokens(prev)
+    assert_parity(got.cpu().numpy(), _oracle_decode(c), "bf16", f"{fmt} partition={tokens}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("window", [1, 100, 2000])
+def test_decode_quant_window(pa, fmt, window):
+    c = _sweep_case(fmt)
+    say(f"[quant decode] {fmt} window={window}")
+    got = _gpu_decode(pa, c, window=window)
+    assert_parity(got.cpu().numpy(), _oracle_decode(c, window=window), "bf16", f"{fmt} W={window}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_decode_quant_unused_slots_and_relabelling(pa, fmt):
+    c = _sweep_case(fmt)
+    say(f"[quant decode] {fmt}: poison independence, relabelling, run twice")
+    base = _gpu_decode(pa, c)
+    assert torch.isfinite(base).all()
+    assert same_bits(base, _gpu_decode(pa, c)), "two runs differ"
+    # Unused slots: replace the poison (NaN codes / -128, NaN scales) with zeros.
+    nan_k = torch.isnan(c.k_scale)
+    zk, zv = c.k_pool.clone(), c.v_pool.clone()
+    zk[nan_k] = 0
+    zv[torch.isnan(c.v_scale)] = 0
+    zks = torch.nan_to_num(c.k_scale, nan=0.0)
+    zvs = torch.nan_to_num(c.v_scale, nan=0.0)
+    assert same_bits(base, _gpu_decode(pa, c, k_pool=zk, v_pool=zv, k_scale=zks, v_scale=zvs))
+    # Physical relabelling.
+    relabel = torch.as_tensor(np.random.default_rng(7).permutation(c.num_blocks), device="cuda")
+    moved = {}
+    for key in ("k_pool", "v_pool", "k_scale", "v_scale"):
+        t = getattr(c, key)
+        m = torch.empty_like(t)
+        m[relabel] = t
+        moved[key] = m
+    moved["block_table"] = relabel[c.block_table.long()].to(torch.int32)
+    assert same_bits(base, _gpu_decode(pa, c, **moved)), "relabelling changed output bits"
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_append_then_decode_end_to_end(pa, fmt):
+    """The step's new token quantised into the cache by each side, then attended."""
+    c = wl.make_quant_decode_case(fmt=fmt, batch=5, n_q=32, n_kv=8, head_dim=128,
+                                  context_lens=[1, 16, 17, 500, 1301], free_fraction=0.2, seed=31,
+                                  device="cuda", name="e2e")
+    say(f"[quant] {fmt}: append + decode vs oracle append + decode")
+    kc, vc, ks, vs = c.k_pool.clone(), c.v_pool.clone(), c.k_scale.clone(), c.v_scale.clone()
+    pa.kv_append_quant(c.new_k, c.new_v, c.slot_mapping, kc, vc, ks, vs, fmt)
+    got = _gpu_decode(pa, c, k_pool=kc, v_pool=vc, k_scale=ks, v_scale=vs)
+    okc, ovc, oks, ovs = _np(c.k_pool).copy(), _np(c.v_pool).copy(), _np(c.k_scale).copy(), _np(c.v_scale).copy()
+    oracle.kv_append_quant(stored_np(c.new_k), stored_np(c.new_v), c.q_dtype, _np(c.slot_mapping),
+                           okc, ovc, oks, ovs, fmt)
+    assert np.array_equal(_np(kc), okc) and np.array_equal(_np(vc), ovc)
+    assert np.array_equal(_np(ks).view(np.uint32), oks.view(np.uint32))
+    want = oracle.decode(stored_np(c.q), okc, ovc, fmt, _np(c.block_table), _np(c.context_lens), c.scale,
+                         q_dtype=c.q_dtype, k_scale=oks, v_scale=ovs)
+    assert_parity(got.cpu().numpy(), want, "bf16", f"{fmt} append + decode")
+
+
+def test_decode_quant_bf16_output_and_rejections(pa):
+    c = _sweep_case("fp8")
+    out = _gpu_decode(pa, c, out_dtype=torch.bfloat16)
+    want = _oracle_decode(c)
+    err = np.abs(out.float().cpu().numpy() - want)
+    assert (err <= 2e-3 + 2.0 ** -8 * np.abs(want)).all(), float(err.max())
+    # A quantised cache is refused by the bf16/f16 entry points, and q must be bf16/f16.
+    with pytest.raises(TypeError):
+        pa.paged_attn_decode(c.q, c.k_pool, c.v_pool, c.block_table, c.context_lens, c.scale)
+    with pytest.raises(TypeError):
+        pa.paged_attn_decode_quant(c.q.float(), c.k_pool, c.v_pool, c.k_scale, c.v_scale, "fp8",
+                                   c.block_table, c.context_lens, c.scale)
+
+
+def test_full_size_8b_fp8_sampled(pa):
+    ctx = [2048] * 32
+    c = wl.make_quant_decode_case(fmt="fp8", batch=32, n_q=32, n_kv=8, head_dim=128,
+                                  context_lens=ctx, seed=2002, device="cuda", name="8b_fp8")
+    say("[quant decode] 8B shape, fp8, full size (sampled rows)")
+    got = _gpu_decode(pa, c)
+    rng = np.random.default_rng(0)
+    sel = np.asarray([[b, h] for b in range(32) for h in sorted({0, 3, 4, 31, *rng.integers(0, 32, 3).tolist()})],
+                     np.int32)
+    want = _oracle_decode(c, sel=sel)
+    assert_parity(got.cpu().numpy()[sel[:, 0], sel[:, 1]], want, "bf16", "8B fp8 sampled")
+    assert torch.isfinite(got).all()
