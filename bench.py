@@ -10,7 +10,8 @@ Other workloads (``--workload``): the 70B-shaped long-context decode
 (B=8, n_q=64, ctx 32768), the variable-length batch with a shared prefix, the
 tiny fp32 case, the causal prefill + cache write + first decode step, chunked
 prefill over a paged prefix, multi-row (speculative) decode, and sliding-window
-decode (the 8B shape over 16384-token contexts, window 4096).
+decode (the 8B shape over 16384-token contexts, window 4096), and the 8B shape over an
+FP8 E4M3 or INT8 cache (codes + one fp32 scale per row).
 
 Timing: ``--warmup`` untimed steps, then exactly ``--steps`` timed steps between
 two ``torch.cuda.synchronize()`` calls. Steps rotate over ``--sets``
@@ -43,6 +44,8 @@ WORKLOADS = {
     "chunked_prefill": 6,
     "decode_multi_8b": 7,
     "decode_window_8b": 8,
+    "decode_8b_fp8": 9,
+    "decode_8b_int8": 10,
     "copy_calibration": 0,
 }
 
@@ -53,6 +56,7 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "decode_mfma.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "prefill": ["prefill.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "decode_multi": ["decode_multi.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
+    "decode_quant": ["decode_quant.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
 }
 
 
@@ -516,6 +520,111 @@ def bench_decode_multi(args):
     }
 
 
+def cpu_baseline_quant(case, target_s: float):
+    """Time the CPU oracle on whole sequences of one quantised input set (all heads)."""
+    import numpy as np
+
+    import oracle
+    from paged_gqa_attention_attn_amd import accounting as acc
+
+    def npy(t):
+        return t.detach().cpu().contiguous().numpy()
+
+    kp, vp, ks, vs = npy(case.k_pool), npy(case.v_pool), npy(case.k_scale), npy(case.v_scale)
+    q, bt, ctx = _stored(case.q), npy(case.block_table), npy(case.context_lens)
+
+    def run(seqs):
+        sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
+        t0 = time.perf_counter()
+        oracle.decode(q, kp, vp, case.fmt, bt, ctx, case.scale, sel=sel, q_dtype=case.q_dtype,
+                      k_scale=ks, v_scale=vs)
+        return time.perf_counter() - t0
+
+    t1 = run([0])
+    n = int(min(case.batch, max(1, math.ceil(target_s / max(t1, 1e-6)))))
+    dt = run(list(range(n)))
+    kv = acc.quant_decode_kv_bytes(ctx[:n], case.n_kv, case.head_dim)
+    return {"value": round(kv / dt / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
+            "kind": "oracle",
+            "sample": f"fp64 oracle decode over {case.fmt} codes of {n} of {case.batch} sequences "
+                      f"(all {case.n_q} query heads), {kv} bytes in {dt:.2f} s"}
+
+
+def bench_decode_quant(args, fmt: str):
+    """The 8B decode shape (B=32, n_q=32, n_kv=8, d=128, contexts 2048) over a one-byte
+    cache: kv_append_quant of the 32 new tokens, then decode_quant."""
+    import torch
+
+    import paged_gqa_attention_attn_amd as pa
+    from paged_gqa_attention_attn_amd import accounting as acc
+    from paged_gqa_attention_attn_amd import workloads as wl
+
+    B, ctx = 32, 2048
+    name = f"llama3_8b_decode_b32_ctx2048_{fmt}_cache"
+    sets = [wl.make_quant_decode_case(fmt=fmt, batch=B, n_q=32, n_kv=8, head_dim=128,
+                                      context_lens=[ctx] * B, seed=1009 + 1000 * i, device="cuda",
+                                      name=name) for i in range(args.sets)]
+    c0 = sets[0]
+    out = torch.empty((B, c0.n_q, c0.head_dim), dtype=torch.float32, device="cuda")
+    ws_bytes = pa.quant_decode_workspace_bytes(B, c0.n_q, c0.max_blocks_per_seq, c0.k_pool, fmt)
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+
+    def decode(s):
+        pa.paged_attn_decode_quant(s.q, s.k_pool, s.v_pool, s.k_scale, s.v_scale, fmt, s.block_table,
+                                   s.context_lens, s.scale, out=out, workspace=ws)
+
+    def step(i):
+        s = sets[i % len(sets)]
+        pa.kv_append_quant(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool, s.k_scale,
+                           s.v_scale, fmt)
+        decode(s)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(args.steps):
+        decode(sets[i % len(sets)])
+    e1.record(stream)
+    torch.cuda.synchronize()
+    dec_ms = e0.elapsed_time(e1) / args.steps
+    kv = acc.quant_decode_kv_bytes([ctx] * B, c0.n_kv, c0.head_dim)
+    io = acc.decode_io_bytes(B, c0.n_q, c0.head_dim, 2, 4, c0.max_blocks_per_seq)
+    achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
+    rec = {
+        "metric": f"paged GQA decode over an {fmt.upper()} KV cache: KV GB/s (% HBM peak) and "
+                  "µs/step at 1 GPU",
+        "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 5), "us_per_step": round(ms * 1e3, 2),
+        "pct_hbm_peak": round(100 * kv / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 2),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": f"{fmt} cache, bf16 q, fp32 accumulate", "data": "synthetic",
+        "config": {"workload": name, "batch": B, "n_q": c0.n_q, "n_kv": c0.n_kv,
+                   "head_dim": c0.head_dim, "block_size": 16, "context_lens": "2048 each",
+                   "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
+                   "step": "kv_append_quant of one new token per sequence, then decode_quant "
+                           "(two launches)"},
+        "roofline": {"kernel": "decode_quant_kernel", "bound": "hbm", "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_quant", args.workload),
+                     "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
+                     "source_hash": source_hash("decode_quant")},
+        "tflops": round(acc.decode_flops([ctx] * B, c0.n_q, c0.head_dim) / (dec_ms * 1e-3) / 1e12, 3),
+    }
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_quant(c0, args.cpu_seconds)
+    return rec
+
+
 def bench_copy(args):
     """A plain device copy of a known size: the reference that scales the
     FETCH_SIZE / WRITE_SIZE counters to bytes."""
@@ -555,7 +664,9 @@ def main(argv=None) -> int:
         rec = bench_copy(args)
     else:
         rec = (bench_prefill(args) if cfg == 5 else bench_chunked_prefill(args) if cfg == 6
-               else bench_decode_multi(args) if cfg == 7 else bench_decode(args, cfg))
+               else bench_decode_multi(args) if cfg == 7
+               else bench_decode_quant(args, "fp8") if cfg == 9
+               else bench_decode_quant(args, "int8") if cfg == 10 else bench_decode(args, cfg))
     rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
     return 0

@@ -17,7 +17,8 @@ from __future__ import annotations
 
 from typing import Iterable
 
-ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1}
+ELEM_BYTES = {"f32": 4, "bf16": 2, "f16": 2, "fp8": 1, "int8": 1}
+SCALE_BYTES = 4   # one fp32 scale per (token, KV head) row of a quantised cache
 
 
 def kv_cache_bytes(layers: int, tokens: int, n_kv: int, head_dim: int, elem_bytes: int) -> int:
@@ -35,6 +36,13 @@ def decode_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int, elem_
     """K/V bytes one decode step must read: every attended position, every KV head, once."""
     return sum(kv_cache_bytes(1, attended(c, window), n_kv, head_dim, elem_bytes)
                for c in context_lens)
+
+
+def quant_decode_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int,
+                          window: int = 0) -> int:
+    """Bytes one decode step reads from a one-byte (FP8 / INT8) cache: the codes of every
+    attended K and V row (the pages' one byte per element) plus each row's fp32 scale."""
+    return sum(2 * attended(c, window) * n_kv * (head_dim + SCALE_BYTES) for c in context_lens)
 
 
 def decode_unique_kv_bytes(context_lens: Iterable[int], n_kv: int, head_dim: int,

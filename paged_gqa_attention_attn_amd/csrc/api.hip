@@ -155,13 +155,12 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     // (PA_DECODE_RING: 1 or 2).
     int32_t ring = env_int("PA_DECODE_RING", 1);
     if (ring != 1 && ring != 2) ring = 1;
-    if (quant) ring = 1;   // the quantised-cache kernel keeps one block in flight per wave
     const int64_t units = (int64_t)batch * c->n_kv * hs;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
     int32_t hs_wg = 1, waves_tok, bpw, nparts_max;
     if (mfma) {
         mfma_partitions(units, max_blocks, &waves_tok, &bpw, &nparts_max);
-        const int32_t wave_lds = quant ? pa::quant_wave_bytes(c->head_dim, gw)
+        const int32_t wave_lds = quant ? pa::quant_wave_bytes(c->head_dim, gw, ring)
                                        : mfma_wave_bytes(ring, tile, gw, c->head_dim);
         while (waves_tok > 1 && waves_tok * wave_lds > kLdsBytes) --waves_tok;
         nparts_max = std::max(1, (max_blocks + waves_tok * bpw - 1) / (waves_tok * bpw));

@@ -94,7 +94,7 @@ template <> struct Mfma16<F16> {
     }
 };
 
-template <int D, int HW> struct QLayout {
+template <int D, int HW, int R> struct QLayout {
     static constexpr int ROW = D;                     // bytes per token row (one-byte codes)
     static constexpr int CPR = ROW / 16;              // 16-byte chunks per row: 8 or 4
     static constexpr int TILE = BS * ROW;             // one (block, KV head) code tile
@@ -102,24 +102,25 @@ template <int D, int HW> struct QLayout {
     static constexpr int SC = 256;                    // scale copy: K scales, V scales, repeat
     static constexpr int SLOTB = 2 * TILE + SC;       // one ring slot
     static constexpr int OPS = 2 * NQ + 1;            // vector-memory operations per block
+    static constexpr int RING = R * SLOTB;            // R blocks in flight per wave
     static constexpr int PITCH = D + 4;
     static constexpr int SLOT = HW * PITCH + 2 * HW;  // merge slot floats
-    static constexpr int WAVE_BYTES = ((SLOTB > SLOT * 4 ? SLOTB : SLOT * 4) + 15) / 16 * 16;
+    static constexpr int WAVE_BYTES = ((RING > SLOT * 4 ? RING : SLOT * 4) + 15) / 16 * 16;
     // Rows of the 16 keys share 256-byte bank lines 256 / ROW at a time; rows of one
     // line get distinct chunk masks and rows of the same line position distinct ones.
     static __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 };
 
-template <class Q, class E, int D, int HW>
+template <class Q, class E, int D, int HW, int R>
 __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const DecodeArgs p) {
-    using L = QLayout<D, HW>;
+    using L = QLayout<D, HW, R>;
     using S = typename E::storage;
     constexpr int ROW = L::ROW, TILE = L::TILE, NQ = L::NQ, OPS = L::OPS;
     constexpr int KK = D / 32;    // S^T k-steps
     constexpr int MT = D / 16;    // O^T tiles
     static_assert(HW == 1 || HW == 2 || HW == 4 || HW == 8 || HW == 16, "1 to 16 MFMA columns");
     static_assert(TILE % 1024 == 0, "tiles move in whole 1 KB copies");
-    static_assert(OPS < 64, "one block's copies fit the vmcnt counter");
+    static_assert(OPS * R < 64, "a ring's copies fit the vmcnt counter");
 
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -184,7 +185,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     const float* sbase = ((lane >> 4) & 1 ? p.v_scale : p.k_scale) + (int64_t)g * BS + (lane & 15);
     auto issue = [&](int i) {
         const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
-        const uint32_t dst = ring_lds;   // one block in flight per wave
+        const uint32_t dst = ring_lds + (i % R) * L::SLOTB;
         const char* kb = kbase + phys * block_bytes;
         const char* vb = vbase + phys * block_bytes;
 #pragma unroll
@@ -219,10 +220,16 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     for (int kk = 0; kk < KK; ++kk) asm volatile("" : : "v"(qreg[kk]));
 
     if (!phys_bad && nb > 0) {
-        issue(0);
+        const int pre = min(R, nb);
+        for (int i = 0; i < pre; ++i) issue(i);
         for (int i = 0; i < nb; ++i) {
-            wait_vmcnt<0>();
-            char* base = ring;
+            // Block i has landed once at most (blocks issued after it) * OPS copies are pending.
+            const int ahead = min(R - 1, nb - 1 - i);
+            if constexpr (R >= 2) {
+                if (ahead == 1) wait_vmcnt<OPS>();
+            }
+            if (ahead == 0) wait_vmcnt<0>();
+            char* base = ring + (i % R) * L::SLOTB;
             const int pos0 = (wb0 + i) * BS;
             const bool edge = pos0 + BS > ctx || pos0 < first;   // uniform
             if (edge) {
@@ -255,7 +262,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             const float4 ks = *reinterpret_cast<const float4*>(base + 2 * TILE + 16 * grp);
             const float4 vs = *reinterpret_cast<const float4*>(base + 2 * TILE + 64 + 16 * grp);
             lds_reads_done();
-            if (i + 1 < nb) issue(i + 1);
+            if (i + R < nb) issue(i + R);
 
             f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -358,42 +365,48 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     }
 }
 
-template <class Q, class E, int D, int HW> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    const size_t lds = (size_t)a.waves_tok * QLayout<D, HW>::WAVE_BYTES;
+template <class Q, class E, int D, int HW, int R> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)a.waves_tok * QLayout<D, HW, R>::WAVE_BYTES;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     static const hipError_t opt_in = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_quant_kernel<Q, E, D, HW>),
+        reinterpret_cast<const void*>(&decode_quant_kernel<Q, E, D, HW, R>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (opt_in != hipSuccess) return opt_in;
     const dim3 grid(a.nparts_max, a.n_kv * a.hsg, a.batch);
-    hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW>), grid, dim3(64 * a.waves_tok), lds, s, a);
+    hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW, R>), grid, dim3(64 * a.waves_tok), lds, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.nparts_max <= 1) return err;
     return launch_decode_reduce(a, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
 }
 
-template <class Q, class E, int D> hipError_t launch_hw(const DecodeArgs& a, hipStream_t s) {
+template <class Q, class E, int D, int R> hipError_t launch_hw(const DecodeArgs& a, hipStream_t s) {
     switch (a.gw) {
-    case 1: return launch_typed<Q, E, D, 1>(a, s);
-    case 2: return launch_typed<Q, E, D, 2>(a, s);
-    case 4: return launch_typed<Q, E, D, 4>(a, s);
-    case 8: return launch_typed<Q, E, D, 8>(a, s);
-    case 16: return launch_typed<Q, E, D, 16>(a, s);
+    case 1: return launch_typed<Q, E, D, 1, R>(a, s);
+    case 2: return launch_typed<Q, E, D, 2, R>(a, s);
+    case 4: return launch_typed<Q, E, D, 4, R>(a, s);
+    case 8: return launch_typed<Q, E, D, 8, R>(a, s);
+    case 16: return launch_typed<Q, E, D, 16, R>(a, s);
     default: return hipErrorInvalidValue;
     }
 }
 
+template <class Q, class E, int D> hipError_t launch_ring(const DecodeArgs& a, hipStream_t s) {
+    if (a.ring == 2) return launch_hw<Q, E, D, 2>(a, s);
+    if (a.ring == 1) return launch_hw<Q, E, D, 1>(a, s);
+    return hipErrorInvalidValue;
+}
+
 template <class Q, class E> hipError_t launch_dim(const DecodeArgs& a, int head_dim, hipStream_t s) {
-    if (head_dim == 128) return launch_hw<Q, E, 128>(a, s);
-    if (head_dim == 64) return launch_hw<Q, E, 64>(a, s);
+    if (head_dim == 128) return launch_ring<Q, E, 128>(a, s);
+    if (head_dim == 64) return launch_ring<Q, E, 64>(a, s);
     return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-int quant_wave_bytes(int head_dim, int hw) {
+int quant_wave_bytes(int head_dim, int hw, int ring) {
     const int tile = BS * head_dim;
-    const int slotb = 2 * tile + 256;
+    const int slotb = ring * (2 * tile + 256);
     const int slot = (hw * (head_dim + 4) + 2 * hw) * 4;
     return ((slotb > slot ? slotb : slot) + 15) / 16 * 16;
 }

@@ -63,8 +63,8 @@ hipError_t launch_decode_multi(const DecodeArgs& a, Elem e, int head_dim, hipStr
 
 // Decode over a quantised cache (codes + per-row scales), q in q_type (bf16 or f16).
 hipError_t launch_decode_quant(const DecodeArgs& a, Elem q_type, QuantFmt fmt, int head_dim, hipStream_t s);
-// LDS bytes one wave of the quantised decode kernel takes for hw heads.
-int quant_wave_bytes(int head_dim, int hw);
+// LDS bytes one wave of the quantised decode kernel takes for hw heads and a ring of `ring` blocks.
+int quant_wave_bytes(int head_dim, int hw, int ring);
 // Quantise k/v rows ([T][n_kv][D] in src) per row into codes + scales at slot_mapping.
 hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, const int64_t* slots,
                                   int32_t num_tokens, int32_t n_kv, int32_t head_dim, int64_t num_slots,

@@ -72,3 +72,12 @@ def test_windowed_decode_bytes_and_flops():
     assert acc.decode_kv_bytes([100, 5000], 8, 128, 2, window=4096) == (100 + 4096) * 4096
     assert acc.decode_flops([16384], 32, 128, window=4096) == acc.decode_flops([4096], 32, 128)
     assert acc.decode_flops([10], 1, 1, window=0) == 40
+
+
+def test_quant_bytes_are_one_byte_codes_plus_row_scales():
+    # The pages count FP8 as one byte per element; each row adds its fp32 scale.
+    ctx = [2048] * 32
+    codes = acc.decode_kv_bytes(ctx, 8, 128, acc.ELEM_BYTES["fp8"])
+    assert codes == 134_217_728
+    assert acc.quant_decode_kv_bytes(ctx, 8, 128) == codes + 2 * 32 * 2048 * 8 * 4
+    assert acc.quant_decode_kv_bytes([100, 5000], 2, 64, window=300) == 2 * (100 + 300) * 2 * (64 + 4)
