@@ -45,6 +45,10 @@ SHAPES = {
     "d64_bf16": (2, 150, 4, 2, 64, "bf16", True),
     "d64_f16_full": (1, 70, 4, 2, 64, "f16", False),
     "long_causal": (1, 1000, 4, 2, 128, "bf16", True),
+    "rows_257": (1, 257, 4, 2, 128, "bf16", True),
+    "full_600": (1, 600, 8, 2, 128, "bf16", False),
+    "d64_f16_513": (1, 513, 4, 2, 64, "f16", True),
+    "f16_causal_384": (2, 384, 4, 1, 128, "f16", True),
 }
 
 
