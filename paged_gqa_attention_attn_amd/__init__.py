@@ -142,9 +142,10 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
-    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dt = k_cache.dtype
@@ -185,9 +186,10 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
-    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     dt = k_cache.dtype
@@ -372,9 +374,10 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
-    need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
-    if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if workspace is None:
+        need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check("pa_paged_attn_decode_quant", L.pa_paged_attn_decode_quant(

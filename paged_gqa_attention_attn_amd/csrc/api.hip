@@ -121,9 +121,8 @@ int32_t mfma_wave_bytes(int32_t ring, int32_t tile, int32_t hw, int32_t head_dim
 // sliding-window workloads), as long as every compute unit has work.
 constexpr int kTargetWaves = 2048;
 
-void mfma_partitions(int64_t units, int32_t span, int32_t* waves, int32_t* bpw, int32_t* nparts) {
-    int32_t w = env_int("PA_DECODE_WAVES", 8);
-    if (w < 1 || w > kMaxWaves) w = kMaxWaves;
+// Runs of blocks per wave and partitions for `w` waves per workgroup.
+void mfma_partitions(int64_t units, int32_t span, int32_t w, int32_t* bpw, int32_t* nparts) {
     int32_t tokens = g_partition_tokens.load();
     int32_t b;
     if (tokens > 0) {   // explicit partition size (pa_set_decode_partition_tokens)
@@ -135,7 +134,6 @@ void mfma_partitions(int64_t units, int32_t span, int32_t* waves, int32_t* bpw, 
         b = (span + p * w - 1) / (p * w);   // balance the partitions
     }
     b = std::max(1, std::min(64, b));
-    *waves = w;
     *bpw = b;
     *nparts = std::max(1, (span + w * b - 1) / (w * b));
 }
@@ -159,11 +157,12 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
     int32_t hs_wg = 1, waves_tok, bpw, nparts_max;
     if (mfma) {
-        mfma_partitions(units, max_blocks, &waves_tok, &bpw, &nparts_max);
+        waves_tok = env_int("PA_DECODE_WAVES", kMaxWaves);
+        if (waves_tok < 1 || waves_tok > kMaxWaves) waves_tok = kMaxWaves;
         const int32_t wave_lds = quant ? pa::quant_wave_bytes(c->head_dim, gw, ring)
                                        : mfma_wave_bytes(ring, tile, gw, c->head_dim);
         while (waves_tok > 1 && waves_tok * wave_lds > kLdsBytes) --waves_tok;
-        nparts_max = std::max(1, (max_blocks + waves_tok * bpw - 1) / (waves_tok * bpw));
+        mfma_partitions(units, max_blocks, waves_tok, &bpw, &nparts_max);
     } else {
         // VALU kernel: 8 waves when there are at least as many (sequence, KV head,
         // head slice) units as compute units, else 4 so that long contexts split
@@ -432,15 +431,26 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
                                  const pa_cache_desc* cache) {
     if (check_decode_args(batch, n_q, cache, max_blocks_per_seq, true) != PA_OK) return 0;
-    // A windowed call plans for a shorter span of blocks; the size returned covers
-    // the plan of every span up to max_blocks_per_seq.
-    size_t most = 0;
-    for (int32_t span = 1; span <= max_blocks_per_seq; ++span) {
-        Plan pl;
-        make_plan(batch, n_q, span, cache, &pl);
-        most = std::max(most, plan_bytes(pl));
+    Plan pl;
+    make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
+    // A windowed call plans for a shorter span of blocks. With fixed runs of blocks
+    // per wave (the VALU plan, or an explicit partition size) the partition count
+    // grows with the span, so max_blocks_per_seq bounds it. The matrix-core plan
+    // gives each wave at least span * units / kTargetWaves blocks and at least 4,
+    // so below its 64-block cap a span takes at most
+    // min(ceil(kTargetWaves / (waves * units)), ceil(max_blocks / (4 * waves)))
+    // partitions, and at the cap the count again grows with the span.
+    int32_t np = pl.nparts_max;
+    if (pl.mfma && g_partition_tokens.load() <= 0) {
+        const int64_t units = (int64_t)batch * cache->n_kv * pl.hsg;
+        const int64_t w = pl.waves_tok;
+        const int64_t by_waves = (kTargetWaves + w * units - 1) / (w * units);
+        const int64_t by_min_run = (max_blocks_per_seq + 4 * w - 1) / (4 * w);
+        np = (int32_t)std::max<int64_t>(np, std::min(by_waves, by_min_run));
     }
-    return most;
+    if (np <= 1) return 0;
+    const size_t m_floats = (size_t)batch * n_q * np;
+    return 2 * round16(m_floats * sizeof(float)) + m_floats * cache->head_dim * sizeof(float);
 }
 
 }  // extern "C"
