@@ -20,7 +20,9 @@
 //    fetched by lane 4e + j / 4 (e = 0..3).
 //  * bf16 probabilities are split into bf16 hi + lo parts and both multiply V
 //    (P rounded to 8 bits alone errs by ~0.4% on contexts of a few tokens);
-//    f16 keeps 11 bits in one part.
+//    the two parts share one v_mfma_f32_16x16x32_bf16, stacked along k with V^T
+//    repeated, which issues at twice the rate of two 16x16x16 products. f16
+//    keeps 11 bits in one part.
 //  * Measured on the 8B-shaped step, the VALU form of these products costs
 //    about 7% of the step (its time grows linearly with the VALU instruction
 //    count, and the shader clock drops under it); here the VALU only runs the
@@ -298,13 +300,19 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
             }
             // P^T operand: keys 4 grp .. +4 of head h0 + col, exactly where S^T put them.
             const uint2 ph = make_uint2(Mfma<E>::pack(pr[0], pr[1]), Mfma<E>::pack(pr[2], pr[3]));
-#pragma unroll
-            for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
             if constexpr (Mfma<E>::kSplit) {
+                // hi and lo parts stacked along k of one 16x16x32 product (twice the
+                // rate of two 16x16x16 products): k slots 8 grp + j hold key 4 grp + j % 4,
+                // part j / 4, in both operands.
                 const uint2 pl = make_uint2(Mfma<E>::pack(pr[0] - Mfma<E>::lo_of(ph.x), pr[1] - Mfma<E>::hi_of(ph.x)),
                                             Mfma<E>::pack(pr[2] - Mfma<E>::lo_of(ph.y), pr[3] - Mfma<E>::hi_of(ph.y)));
+                const u32x4_t pb = u32x4_t{ph.x, ph.y, pl.x, pl.y};
 #pragma unroll
-                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], pl, o[t]);
+                for (int t = 0; t < MT; ++t)
+                    o[t] = Mfma16<E>::qk(u32x4_t{va[t].x, va[t].y, va[t].x, va[t].y}, pb, o[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
             }
         }
     }

@@ -298,13 +298,19 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                 pr[j] = live[j] ? pj * vsc[j] : 0.f;   // V scale folded into P
             }
             const uint2 ph = make_uint2(Mfma<E>::pack(pr[0], pr[1]), Mfma<E>::pack(pr[2], pr[3]));
-#pragma unroll
-            for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
             if constexpr (Mfma<E>::kSplit) {
+                // hi and lo parts stacked along k of one 16x16x32 product (twice the
+                // rate of two 16x16x16 products): k slots 8 grp + j hold key 4 grp + j % 4,
+                // part j / 4, in both operands.
                 const uint2 pl = make_uint2(Mfma<E>::pack(pr[0] - Mfma<E>::lo_of(ph.x), pr[1] - Mfma<E>::hi_of(ph.x)),
                                             Mfma<E>::pack(pr[2] - Mfma<E>::lo_of(ph.y), pr[3] - Mfma<E>::hi_of(ph.y)));
+                const u32x4_t pb = u32x4_t{ph.x, ph.y, pl.x, pl.y};
 #pragma unroll
-                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], pl, o[t]);
+                for (int t = 0; t < MT; ++t)
+                    o[t] = Mfma16<E>::qk(u32x4_t{va[t].x, va[t].y, va[t].x, va[t].y}, pb, o[t]);
+            } else {
+#pragma unroll
+                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
             }
         }
     }
