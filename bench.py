@@ -312,9 +312,11 @@ def bench_prefill(args):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
     kf = [s.k.reshape(-1, s.n_kv, s.head_dim) for s in sets]
     vf = [s.v.reshape(-1, s.n_kv, s.head_dim) for s in sets]
+    pws_bytes = pa.prefill_workspace_bytes(c0.q.dtype, c0.batch, c0.seq_len, c0.n_kv, c0.head_dim)
+    pws = torch.empty(max(pws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def prefill(s):
-        pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out)
+        pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out, workspace=pws)
 
     def step(i):
         s = sets[i % n_sets]
@@ -362,6 +364,10 @@ def bench_prefill(args):
         },
         "roofline": {
             "kernel": "paged_attn_prefill", "bound": "mfma", "achieved": round(achieved, 2),
+            # one call = the f16 staging of V (bf16 only) + the prefill kernel
+            "launches_per_call": 2 if pws_bytes else 1,
+            "pv_product": "f16 on an exact f16 copy of V, P in 11 bits" if pws_bytes
+                          else "input dtype (bf16: P in hi + lo parts)",
             "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
             "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
             "traffic": measured_traffic("prefill", args.workload),

@@ -188,12 +188,25 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *           max(0, i - W + 1) .. i ([IW] sliding-window item). Negative, or
  *           positive with causal == 0: PA_ERR_INVALID_ARG.
  *   out   [batch][seq_len][n_q][head_dim], out_dtype PA_F32 or dtype
+ *   workspace  device scratch of at least pa_prefill_workspace_bytes(...) bytes
+ *         (16-byte aligned), or NULL: then the workspace of pa_set_workspace if
+ *         large enough, else the library's own (as for pa_paged_attn_decode).
+ *         bf16 only: it receives an f16 copy of v, exact for every finite value
+ *         below 65520 in magnitude (f16 keeps 11 significant bits to bf16's 8;
+ *         values below 2^-14 move by at most 2^-25), so that P V runs with one
+ *         11-bit P part on the f16 matrix cores; 64-key tiles holding a larger
+ *         finite value keep the bf16 product for the rows that read them.
+ *         PA_PREFILL_STAGE_V=0 in the environment turns the staging off.
+ *         Calls that share a workspace must not overlap on the GPU.
  * Supported: head_dim 128 (and 64); dtype bf16 or f16.
  */
+size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len, int32_t n_kv,
+                                  int32_t head_dim);
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, int32_t window,
-                          void* out, pa_dtype out_dtype, void* stream);
+                          void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream);
 
 /*
  * paged_attn_decode_multi -- q_rows new query rows per sequence (speculative

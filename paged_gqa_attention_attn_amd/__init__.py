@@ -63,6 +63,13 @@ def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _workspace_args(workspace):
+    """(pointer, bytes) of an optional device workspace; (None, 0) for none."""
+    if workspace is None:
+        return None, 0
+    return _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+
+
 def _cache_desc(k_cache: torch.Tensor) -> CacheDesc:
     if k_cache.dim() != 4:
         raise ValueError("caches must be [num_blocks][n_kv][block_size][head_dim]")
@@ -146,8 +153,7 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
         _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
@@ -190,8 +196,7 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode_append", L.pa_paged_attn_decode_append(
         _dev(q, "q", dt), _dev(k_new, "k_new", dt), _dev(v_new, "v_new", dt),
@@ -203,12 +208,22 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
     return out
 
 
+def prefill_workspace_bytes(dtype: torch.dtype, batch: int, seq_len: int, n_kv: int,
+                            head_dim: int) -> int:
+    """Bytes of device workspace a prefill with these sizes uses (0: none)."""
+    if dtype not in _DTYPE:
+        raise TypeError(f"unsupported dtype {dtype}")
+    return int(_lib.load().pa_prefill_workspace_bytes(_DTYPE[dtype], batch, seq_len, n_kv, head_dim))
+
+
 def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
                        scale: float, out: torch.Tensor | None = None,
                        out_dtype: torch.dtype = torch.float32, stream=None,
-                       window: int = 0) -> torch.Tensor:
+                       window: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
     """Attention of a prompt over itself: q [B][S][n_q][d], k/v [B][S][n_kv][d].
-    window W > 0 (causal only) restricts row i to keys i - W + 1 .. i."""
+    window W > 0 (causal only) restricts row i to keys i - W + 1 .. i. workspace:
+    a device buffer of at least prefill_workspace_bytes(...) bytes, or None to
+    allocate one here."""
     L = _lib.load()
     if q.dim() != 4 or k.dim() != 4 or k.shape != v.shape:
         raise ValueError("q must be [B][S][n_q][d] and k, v [B][S][n_kv][d]")
@@ -222,10 +237,14 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     if out.shape != q.shape or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][S][n_q][d] in a supported dtype")
     dt = q.dtype
+    if workspace is None:
+        need = int(L.pa_prefill_workspace_bytes(_DTYPE[dt], B, S, k.shape[2], d))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("pa_paged_attn_prefill", L.pa_paged_attn_prefill(
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
         d, int(bool(causal)), float(scale), int(window), _dev(out, "out"), _DTYPE[out.dtype],
-        _stream(q, stream)))
+        *_workspace_args(workspace), _stream(q, stream)))
     return out
 
 
@@ -284,8 +303,7 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     need = int(L.pa_decode_multi_workspace_bytes(B, R, n_q, maxb, ctypes.byref(desc)))
     if need and workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
         _dev(q, "q", dt), B, R, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
@@ -378,8 +396,7 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-    ws_ptr = _dev(workspace, "workspace") if workspace is not None else None
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    ws_ptr, ws_bytes = _workspace_args(workspace)
     _check("pa_paged_attn_decode_quant", L.pa_paged_attn_decode_quant(
         _dev(q, "q"), _DTYPE[q.dtype], B, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),

@@ -20,6 +20,7 @@ EXPORTS = (
     "pa_paged_attn_decode_append",
     "pa_decode_multi_workspace_bytes",
     "pa_paged_attn_decode_multi",
+    "pa_prefill_workspace_bytes",
     "pa_paged_attn_prefill",
     "pa_paged_attn_chunked_prefill",
     "pa_kv_append_quant",
@@ -78,8 +79,10 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_decode_multi.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
                                              ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_multi.restype = ctypes.c_int
+    L.pa_prefill_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32]
+    L.pa_prefill_workspace_bytes.restype = sz
     L.pa_paged_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
-                                        ctypes.c_float, i32, vp, ctypes.c_int, vp]
+                                        ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_prefill.restype = ctypes.c_int
     L.pa_paged_attn_chunked_prefill.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
                                                 ctypes.c_float, i32, vp, ctypes.c_int, vp]

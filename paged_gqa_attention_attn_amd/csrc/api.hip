@@ -1,5 +1,5 @@
 // api.hip -- C-ABI entry points: argument validation, launch planning, error reporting,
-// the decode workspace.
+// the workspace (decode partials, prefill staging).
 //
 // By default no entry point reads device memory on the host or synchronises the
 // stream: every check uses host-side arguments only, and the kernels bounds-check
@@ -202,6 +202,18 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
 
 size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 
+// Workspace of a bf16 prefill over contiguous keys: the f16 copy of v, then one
+// flag byte per (sequence, KV head, 64-key tile). PA_PREFILL_STAGE_V=0 turns the
+// staging off (P V then stays in bf16 hi + lo parts).
+bool prefill_stages(pa_dtype dtype) { return dtype == PA_BF16 && env_int("PA_PREFILL_STAGE_V", 1) != 0; }
+size_t prefill_stage_v_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32_t head_dim) {
+    return round16((size_t)batch * seq_len * n_kv * head_dim * 2);
+}
+size_t prefill_stage_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32_t head_dim) {
+    const size_t tiles = (size_t)batch * n_kv * ((seq_len + 63) / 64);
+    return prefill_stage_v_bytes(batch, seq_len, n_kv, head_dim) + round16(tiles);
+}
+
 // Blocks one sequence's call can read: all of max_blocks without a window; with
 // window W and `rows` query rows, the W + rows - 1 positions from the first
 // row's window start to the last row, which touch at most (W + rows + 29) / 16
@@ -344,7 +356,7 @@ int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev
     return PA_OK;
 }
 
-// ---- decode workspace ------------------------------------------------------------------
+// ---- workspace (decode partials, prefill staging) ---------------------------------
 
 std::mutex g_ws_mu;
 void* g_default_ws = nullptr;       // set by pa_set_workspace (caller-owned)
@@ -362,17 +374,17 @@ int resolve_workspace(size_t need, void** ws) {
     }
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
-    if (e != hipSuccess) return hip_fail(e, "decode workspace: hipGetDevice");
+    if (e != hipSuccess) return hip_fail(e, "workspace: hipGetDevice");
     auto& slot = g_lib_ws[dev];
     if (slot.second < need) {
         if (slot.first) {
             e = hipFree(slot.first);   // synchronises the device: earlier users are done
             slot = {nullptr, 0};
-            if (e != hipSuccess) return hip_fail(e, "decode workspace: hipFree");
+            if (e != hipSuccess) return hip_fail(e, "workspace: hipFree");
         }
         void* p = nullptr;
         e = hipMalloc(&p, need);
-        if (e != hipSuccess) return hip_fail(e, "decode workspace: hipMalloc");
+        if (e != hipSuccess) return hip_fail(e, "workspace: hipMalloc");
         slot = {p, need};
     }
     *ws = slot.first;
@@ -583,10 +595,17 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
                        stream, &fa);
 }
 
+size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len, int32_t n_kv,
+                                  int32_t head_dim) {
+    if (!prefill_stages(dtype) || batch <= 0 || seq_len <= 0 || n_kv <= 0 || head_dim <= 0) return 0;
+    return prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
+}
+
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, int32_t window,
-                          void* out, pa_dtype out_dtype, void* stream) {
+                          void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                          void* stream) {
     if (dtype != PA_BF16 && dtype != PA_F16)
         return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and f16 inputs");
     if (out_dtype != PA_F32 && out_dtype != dtype)
@@ -621,6 +640,19 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PA_F32;
     a.window = window;
+    if (prefill_stages(dtype)) {
+        const size_t need = prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
+        if (!workspace) {
+            const int rc = resolve_workspace(need, &workspace);
+            if (rc != PA_OK) return rc;
+        } else if (workspace_bytes < need) {
+            return fail(PA_ERR_INVALID_ARG, "prefill: workspace of %zu bytes required (got %zu)", need,
+                        workspace_bytes);
+        }
+        if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "prefill: workspace must be 16-byte aligned");
+        a.v16 = workspace;
+        a.v16_ok = static_cast<uint8_t*>(workspace) + prefill_stage_v_bytes(batch, seq_len, n_kv, head_dim);
+    }
     const hipError_t e = pa::launch_prefill(a, to_elem(dtype), head_dim, static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
         return fail(PA_ERR_UNSUPPORTED, "prefill: no kernel for these arguments");

@@ -90,6 +90,11 @@ struct PrefillArgs {
     const int32_t* context_lens;  // [B]
     int32_t max_blocks, num_blocks;
     int32_t window;   // sliding window (causal only); 0: none
+    // Contiguous bf16 keys only: an f16 copy of v in v's layout, written by the
+    // staging kernel, and one byte per (sequence, KV head, 64-key tile) that is 1
+    // where the copy is exact. nullptr: P V stays in bf16 (hi + lo parts).
+    void* v16;
+    uint8_t* v16_ok;
 };
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);

@@ -42,6 +42,8 @@
 //    which bounds the cache at W recent positions): the row at position p sees
 //    p - W + 1 .. p. A workgroup starts at the tile holding its first row's
 //    window start, and a wave skips tiles wholly before its first row's.
+#include <type_traits>
+
 #include "launch.h"
 #include "mfma.h"
 
@@ -72,6 +74,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     using S = typename E::storage;
     constexpr int KK = D / 16;     // MFMA k-steps over the head dimension
     constexpr int MT = D / 32;     // 32-dim output tiles
+    constexpr bool kStage = std::is_same<E, BF16>::value && !PAGED;   // V may come staged as f16
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int nqt = (p.seq_len + BM - 1) / BM;
@@ -111,7 +114,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     // Contiguous rows interleave the KV heads; a pool block holds one 16-row tile per KV head.
     const int64_t head_off = PAGED ? (int64_t)g * 16 * D * 2 : (int64_t)g * D * 2 + (int64_t)b * S_len * kv_row;
     const char* Kg = reinterpret_cast<const char*>(p.k) + head_off;
-    const char* Vg = reinterpret_cast<const char*>(p.v) + head_off;
+    const char* Vg = reinterpret_cast<const char*>(p.v) + head_off;   // the f16 copy when staged (below)
 
     // Q^T operand: lane holds dims 16*kk + 8*half .. +8 of its query, for every kk.
     u32x4_t qreg[KK];
@@ -140,6 +143,21 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int lo_blk = wg_lo / 16;
     const int wave_lo = pos0 - W + 1;             // window start of this wave's first row
     const int wave_lo_max = pos_last_wave - W + 1; // ... and of its last row
+
+    // bf16 values staged as f16 (exact where this sequence's flags say so): the
+    // P V product then runs on the f16 matrix cores with one 11-bit P part
+    // instead of two bf16 parts. Every wave checks the same tiles, so the choice
+    // is uniform over the workgroup.
+    bool use16 = false;
+    if constexpr (kStage) {
+        if (p.v16 != nullptr) {
+            const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * ((S_len + BN - 1) / BN);
+            bool fits = true;
+            for (int j = j0 + lane; j < n_tiles; j += 64) fits = fits && ok[j] != 0;
+            use16 = __all(fits);
+        }
+    }
+    if (use16) Vg = reinterpret_cast<const char*>(p.v16) + head_off;
 
     // This wave's copies of tile j into buffer `buf`: copy c fills bytes
     // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
@@ -200,110 +218,122 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
 
-    if (n_tiles > j0) issue_tile(j0, j0 & 1);
-    for (int j = j0; j < n_tiles; ++j) {
-        wait_vmcnt<0>();   // this wave's copies of tile j have landed
-        __syncthreads();   // so have the other waves'; all are done with tile j - 1
-        if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
-        const int key0 = j * BN;
-        if (p.causal && key0 > pos_last_wave) continue;   // uniform over the wave
-        if (W > 0 && key0 + BN - 1 < wave_lo) continue;   // wholly before every row's window
+    // The tile loop, for P V in the input type (PE = E) or on the staged f16 V.
+    auto tile_loop = [&](auto staged) {
+        using PE = typename std::conditional<decltype(staged)::value, F16, E>::type;
+        if (n_tiles > j0) issue_tile(j0, j0 & 1);
+        for (int j = j0; j < n_tiles; ++j) {
+            wait_vmcnt<0>();   // this wave's copies of tile j have landed
+            __syncthreads();   // so have the other waves'; all are done with tile j - 1
+            if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
+            const int key0 = j * BN;
+            if (p.causal && key0 > pos_last_wave) continue;   // uniform over the wave
+            if (W > 0 && key0 + BN - 1 < wave_lo) continue;   // wholly before every row's window
 
-        const char* kl = smem + (j & 1) * T::BUF;
-        lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
+            const char* kl = smem + (j & 1) * T::BUF;
+            lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
 
-        // S^T for the two 32-key halves, interleaved so each MFMA hides the other's latency.
-        f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
-        const char* k0 = kl + l32 * T::ROWB;
-        const char* k1 = k0 + 32 * T::ROWB;
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-            const int pos = ((2 * kk + half) ^ ksw) * 16;
-            const uint4 a0 = *reinterpret_cast<const uint4*>(k0 + pos);
-            const uint4 a1 = *reinterpret_cast<const uint4*>(k1 + pos);
-            sc[0] = Mfma<E>::run(u32x4_t{a0.x, a0.y, a0.z, a0.w}, qreg[kk], sc[0]);
-            sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
-        }
-
-        // Mask keys past this lane's query (causal), past the prompt, or before
-        // this lane's window.
-        if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0) || (W > 0 && key0 < wave_lo_max)) {   // uniform
-            const int lim = (p.causal ? min(my_pos, ctx - 1) : ctx - 1) - key0;
-            const int lo = (W > 0 ? my_pos - W + 1 : 0) - key0;
-#pragma unroll
-            for (int st = 0; st < 2; ++st)
-#pragma unroll
-                for (int i = 0; i < 16; ++i) {
-                    const int key = st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
-                    sc[st][i] = (key > lim || key < lo) ? -INFINITY : sc[st][i];
-                }
-        }
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int st = 0; st < 2; ++st)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[st][i]);
-        {
-            float a2, b2;
-            pair32(tmax, a2, b2);
-            tmax = fmaxf(a2, b2) * c2;   // scale > 0, so scaling commutes with the max
-        }
-        if (__any(tmax > m_run + TAU)) {
-            const float m_new = fmaxf(m_run, tmax);
-            const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-            m_run = m_new;
-            l_run *= alpha;
-#pragma unroll
-            for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
-        }
-
-        // P = 2^(s scale - m) in the element type (bf16: hi + lo parts).
-        u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
-        float lsum = 0.f;
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int jg = 0; jg < 2; ++jg) {
-                uint32_t hw[4], lw[4];
-#pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, -m_run));
-                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, -m_run));
-                    hw[w] = Mfma<E>::pack(p0, p1);
-                    if constexpr (Mfma<E>::kSplit)
-                        lw[w] = Mfma<E>::pack(p0 - Mfma<E>::lo_of(hw[w]), p1 - Mfma<E>::hi_of(hw[w]));
-                    lsum += p0 + p1;
-                }
-                ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                if constexpr (Mfma<E>::kSplit) pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+            // S^T for the two 32-key halves, interleaved so each MFMA hides the other's latency.
+            f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+            const char* k0 = kl + l32 * T::ROWB;
+            const char* k1 = k0 + 32 * T::ROWB;
+    #pragma unroll
+            for (int kk = 0; kk < KK; ++kk) {
+                const int pos = ((2 * kk + half) ^ ksw) * 16;
+                const uint4 a0 = *reinterpret_cast<const uint4*>(k0 + pos);
+                const uint4 a1 = *reinterpret_cast<const uint4*>(k1 + pos);
+                sc[0] = Mfma<E>::run(u32x4_t{a0.x, a0.y, a0.z, a0.w}, qreg[kk], sc[0]);
+                sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
             }
-        }
-        l_run += lsum;
 
-        // O^T += V^T P^T. Lane (group g16, r16) fetches 4 dims of key vkey + ...,
-        // and after the transpose holds 4 consecutive keys of one dim.
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-#pragma unroll
-            for (int jg = 0; jg < 2; ++jg) {
-#pragma unroll
-                for (int mt = 0; mt < MT; ++mt) {
-                    uint32_t a[4];
-#pragma unroll
-                    for (int t = 0; t < 2; ++t) {
-                        const int key = st * 32 + jg * 16 + 8 * t + vkey;
-                        const int pos = ((4 * mt + vchunk) ^ T::swz(key)) * 16 + vbyte;
-                        const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                            (lds_i16x4_t*)(vl_lds + key * T::ROWB + pos));
-                        a[2 * t] = __builtin_bit_cast(uint2, v).x;
-                        a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
+            // Mask keys past this lane's query (causal), past the prompt, or before
+            // this lane's window.
+            if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0) || (W > 0 && key0 < wave_lo_max)) {   // uniform
+                const int lim = (p.causal ? min(my_pos, ctx - 1) : ctx - 1) - key0;
+                const int lo = (W > 0 ? my_pos - W + 1 : 0) - key0;
+    #pragma unroll
+                for (int st = 0; st < 2; ++st)
+    #pragma unroll
+                    for (int i = 0; i < 16; ++i) {
+                        const int key = st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
+                        sc[st][i] = (key > lim || key < lo) ? -INFINITY : sc[st][i];
                     }
-                    const u32x4_t av = u32x4_t{a[0], a[1], a[2], a[3]};
-                    o[mt] = Mfma<E>::run(av, ph[st][jg], o[mt]);
-                    if constexpr (Mfma<E>::kSplit) o[mt] = Mfma<E>::run(av, pl[st][jg], o[mt]);
+            }
+            float tmax = -INFINITY;
+    #pragma unroll
+            for (int st = 0; st < 2; ++st)
+    #pragma unroll
+                for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[st][i]);
+            {
+                float a2, b2;
+                pair32(tmax, a2, b2);
+                tmax = fmaxf(a2, b2) * c2;   // scale > 0, so scaling commutes with the max
+            }
+            if (__any(tmax > m_run + TAU)) {
+                const float m_new = fmaxf(m_run, tmax);
+                const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+                m_run = m_new;
+                l_run *= alpha;
+    #pragma unroll
+                for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+            }
+
+            // P = 2^(s scale - m) in the element type (bf16: hi + lo parts).
+            u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
+            float lsum = 0.f;
+    #pragma unroll
+            for (int st = 0; st < 2; ++st) {
+    #pragma unroll
+                for (int jg = 0; jg < 2; ++jg) {
+                    uint32_t hw[4], lw[4];
+    #pragma unroll
+                    for (int w = 0; w < 4; ++w) {
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, -m_run));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, -m_run));
+                        hw[w] = Mfma<PE>::pack(p0, p1);
+                        if constexpr (Mfma<PE>::kSplit)
+                            lw[w] = Mfma<PE>::pack(p0 - Mfma<PE>::lo_of(hw[w]), p1 - Mfma<PE>::hi_of(hw[w]));
+                        lsum += p0 + p1;
+                    }
+                    ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                    if constexpr (Mfma<PE>::kSplit) pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
+                }
+            }
+            l_run += lsum;
+
+            // O^T += V^T P^T. Lane (group g16, r16) fetches 4 dims of key vkey + ...,
+            // and after the transpose holds 4 consecutive keys of one dim.
+    #pragma unroll
+            for (int st = 0; st < 2; ++st) {
+    #pragma unroll
+                for (int jg = 0; jg < 2; ++jg) {
+    #pragma unroll
+                    for (int mt = 0; mt < MT; ++mt) {
+                        uint32_t a[4];
+    #pragma unroll
+                        for (int t = 0; t < 2; ++t) {
+                            const int key = st * 32 + jg * 16 + 8 * t + vkey;
+                            const int pos = ((4 * mt + vchunk) ^ T::swz(key)) * 16 + vbyte;
+                            const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                                (lds_i16x4_t*)(vl_lds + key * T::ROWB + pos));
+                            a[2 * t] = __builtin_bit_cast(uint2, v).x;
+                            a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
+                        }
+                        const u32x4_t av = u32x4_t{a[0], a[1], a[2], a[3]};
+                        o[mt] = Mfma<PE>::run(av, ph[st][jg], o[mt]);
+                        if constexpr (Mfma<PE>::kSplit) o[mt] = Mfma<PE>::run(av, pl[st][jg], o[mt]);
+                    }
                 }
             }
         }
+    };
+    if constexpr (kStage) {
+        if (use16)
+            tile_loop(std::true_type{});
+        else
+            tile_loop(std::false_type{});
+    } else {
+        tile_loop(std::false_type{});
     }
 
     // Denominator: this lane and its partner (lane ^ 32) covered complementary keys.
@@ -337,6 +367,38 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     }
 }
 
+// f16 copy of bf16 V for the staged P V product: f16 keeps 11 significant bits
+// to bf16's 8, so every finite bf16 value below 65520 in magnitude converts
+// exactly, except those below f16's normal range (2^-14), which move by at most
+// 2^-25. One workgroup per (64-key tile, KV head, sequence) also records whether
+// any finite value of its tile overflowed (flag 0: the prefill keeps bf16 there).
+template <int D> __global__ __launch_bounds__(256) void stage_v_f16_kernel(const PrefillArgs p) {
+    constexpr int CPR = D * 2 / 16;   // 16-byte chunks (8 values) per row
+    const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int S_len = p.seq_len;
+    bool bad = false;
+    for (int c = threadIdx.x; c < BN * CPR; c += blockDim.x) {
+        const int t = tile * BN + c / CPR;
+        if (t >= S_len) break;   // rows grow with c
+        const int64_t off = (((int64_t)b * S_len + t) * p.n_kv + g) * D + (c % CPR) * 8;
+        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + off);
+        const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+        uint32_t o16[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float x0 = as_f32(in[i] << 16), x1 = as_f32(in[i] & 0xffff0000u);
+            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+            bad = bad || (__builtin_isinf((float)h0) && !__builtin_isinf(x0)) ||
+                  (__builtin_isinf((float)h1) && !__builtin_isinf(x1));
+            const f16x2_t hv = {h0, h1};
+            o16[i] = __builtin_bit_cast(uint32_t, hv);
+        }
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.v16) + off) = make_uint4(o16[0], o16[1], o16[2], o16[3]);
+    }
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) p.v16_ok[((int64_t)b * p.n_kv + g) * gridDim.x + tile] = bad ? 0 : 1;
+}
+
 template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
     const size_t lds = 2 * (size_t)Tile<D>::BUF;
     // Opt in to exactly the dynamic LDS used (static LDS, e.g. the one word
@@ -345,6 +407,14 @@ template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs&
         reinterpret_cast<const void*>(&prefill_kernel<E, D, PAGED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (opt_in != hipSuccess) return opt_in;
+    if constexpr (std::is_same<E, BF16>::value && !PAGED) {
+        if (a.v16 != nullptr) {
+            const dim3 sgrid((a.seq_len + BN - 1) / BN, a.n_kv, a.batch);
+            hipLaunchKernelGGL((stage_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess) return e;
+        }
+    }
     const dim3 grid((a.seq_len + BM - 1) / BM, a.n_q, a.batch);
     hipLaunchKernelGGL((prefill_kernel<E, D, PAGED>), grid, dim3(64 * NWAVES), lds, s, a);
     return hipGetLastError();

@@ -174,11 +174,12 @@ def test_append_zero_tokens_is_a_noop(L):
 
 def prefill(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=_lib.PA_BF16, B=1, S=64, n_q=8, n_kv=2, d=128,
-             causal=1, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+             causal=1, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0,
+             stream=None)
     a.update(kw)
     return L.pa_paged_attn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["S"], a["n_q"],
                                    a["n_kv"], a["d"], a["causal"], a["scale"], a["window"], a["out"],
-                                   a["out_dtype"], a["stream"])
+                                   a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -197,6 +198,25 @@ def prefill(L, **kw):
 ])
 def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
+
+
+def test_prefill_workspace_bytes(L, monkeypatch):
+    # bf16: an f16 copy of v ([B][S][n_kv][d], 2 bytes each), then one flag byte per
+    # (sequence, KV head, 64-key tile), each part rounded up to 16 bytes.
+    assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 2, 4096, 8, 128) == 2 * 4096 * 8 * 128 * 2 + 1024
+    assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 1, 65, 1, 64) == 65 * 64 * 2 + 16
+    assert L.pa_prefill_workspace_bytes(_lib.PA_F16, 2, 4096, 8, 128) == 0
+    assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 0, 4096, 8, 128) == 0
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 2, 4096, 8, 128) == 0
+
+
+def test_prefill_rejects_small_or_misaligned_workspace(L):
+    need = L.pa_prefill_workspace_bytes(_lib.PA_BF16, 1, 64, 2, 128)
+    assert prefill(L, ws=FAKE, ws_bytes=need - 1) == INVALID
+    assert "workspace" in _lib.last_error()
+    assert prefill(L, ws=FAKE + 8, ws_bytes=need) == INVALID
+    assert "aligned" in _lib.last_error()
 
 
 def test_prefill_empty_is_a_noop(L):

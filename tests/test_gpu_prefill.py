@@ -137,3 +137,66 @@ def test_config5_prefill_append_decode(pa):
                        case.context_lens.cpu().numpy(), case.scale)
     stats = assert_parity(dec.cpu().numpy(), wd, "bf16", "config5 decode at context 4097")
     say(f"    decode ctx={S + 1} max_abs={stats['max_abs']:.2e}")
+
+
+SPLIT_SHAPES = ["gqa4_bf16_ragged_causal", "gqa4_bf16_ragged_full", "d64_bf16", "tile_plus_one"]
+
+
+@pytest.mark.parametrize("name", SPLIT_SHAPES)
+def test_prefill_bf16_without_staging(pa, monkeypatch, name):
+    """PA_PREFILL_STAGE_V=0 keeps P V in bf16 hi + lo parts; both forms meet the oracle."""
+    B, S, n_q, n_kv, d, dt, causal = SHAPES[name]
+    say(f"[prefill unstaged] {name}: B={B} S={S} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
+    q, k, v = _inputs(B, S, n_q, n_kv, d, dt, seed=len(name) * 31 + S)
+    scale = d ** -0.5
+    staged = pa.paged_attn_prefill(q, k, v, causal, scale)
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    assert pa.prefill_workspace_bytes(q.dtype, B, S, n_kv, d) == 0
+    plain = pa.paged_attn_prefill(q, k, v, causal, scale)
+    torch.cuda.synchronize()
+    want = oracle.prefill(stored_np(q), stored_np(k), stored_np(v), dt, causal, scale)
+    s1 = assert_parity(plain.cpu().numpy(), want, dt, f"{name} unstaged")
+    s2 = assert_parity(staged.cpu().numpy(), want, dt, f"{name} staged")
+    say(f"    unstaged max_abs={s1['max_abs']:.2e}  staged max_abs={s2['max_abs']:.2e}")
+
+
+def test_prefill_explicit_workspace(pa):
+    q, k, v = _inputs(1, 200, 8, 2, 128, "bf16", seed=12)
+    need = pa.prefill_workspace_bytes(q.dtype, 1, 200, 2, 128)
+    assert need == 200 * 2 * 128 * 2 + 16
+    ws = torch.full((need + 64,), 0xAB, dtype=torch.uint8, device="cuda")   # stale contents
+    a = pa.paged_attn_prefill(q, k, v, True, 0.09, workspace=ws)
+    b = pa.paged_attn_prefill(q, k, v, True, 0.09)
+    torch.cuda.synchronize()
+    assert same_bits(a, b)
+
+
+def test_prefill_v_beyond_f16_range(pa):
+    """A finite bf16 value above f16's range (70144) flags its 64-key tile: rows
+    whose keys reach it keep the bf16 product, the others run staged; a value
+    that f16 holds exactly (65280) stays staged. Outputs then scale with the
+    value, so the check is norm-wise relative per head plus the usual bound
+    on every other dimension."""
+    B, S, n_q, n_kv, d = 2, 330, 8, 2, 128
+    q, k, v = _inputs(B, S, n_q, n_kv, d, "bf16", seed=21)
+    v[0, 150, 1, 7] = 70144.0      # (sequence 0, KV head 1, tile 2): flagged
+    v[1, 40, 0, 100] = -65280.0    # (sequence 1, KV head 0, tile 0): exact in f16
+    v[1, 300, 1, 3] = 1.0e30       # (sequence 1, KV head 1, tile 4): flagged
+    assert float(v[0, 150, 1, 7]) == 70144.0 and float(v[1, 40, 0, 100]) == -65280.0
+    scale = d ** -0.5
+    out = pa.paged_attn_prefill(q, k, v, True, scale)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = oracle.prefill(stored_np(q), stored_np(k), stored_np(v), "bf16", True, scale)
+    assert np.isfinite(got).all()
+    big = np.zeros(got.shape, bool)
+    big[0, :, 4:8, 7] = True
+    big[1, :, 0:4, 100] = True
+    big[1, :, 4:8, 3] = True
+    assert_parity(got[~big], want[~big], "bf16", "dimensions without a large value")
+    for (b, h0, e) in ((0, 4, 7), (1, 0, 100), (1, 4, 3)):
+        g_ = got[b, :, h0:h0 + 4, e]
+        w_ = want[b, :, h0:h0 + 4, e]
+        rel = np.abs(g_ - w_).max() / np.abs(w_).max()
+        say(f"    sequence {b} heads {h0}..{h0 + 3} dim {e}: norm-wise rel {rel:.2e}")
+        assert rel <= 1e-3, rel
