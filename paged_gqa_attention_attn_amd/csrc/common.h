@@ -149,6 +149,21 @@ __device__ __forceinline__ void copy_to_lds16(const void* src, uint32_t lds_dst)
         : "memory", "m0");
 }
 
+// The same copy from the wave-uniform base `sbase` plus this lane's 32-bit byte
+// offset `voff` (the scalar-base form: no per-lane 64-bit address arithmetic).
+__device__ __forceinline__ void copy_to_lds16(const void* sbase, uint32_t voff, uint32_t lds_dst) {
+    const uint64_t b = (uint64_t)(uintptr_t)sbase;
+    const uint64_t ub = ((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(lds_dst)), "v"(voff), "s"(ub)
+        : "memory", "m0");
+}
+
 // Asynchronous copy of 4 bytes per lane from `src` to LDS at lds_dst + 4 * lane.
 __device__ __forceinline__ void copy_to_lds4(const void* src, uint32_t lds_dst) {
     asm volatile(

@@ -170,6 +170,19 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     // the P V product multiplies them by exactly 0.
     static_assert(T::COPIES * 1024 == 16 * T::ROWB, "a wave copies one 16-row block per tile");
     const uint32_t lds0 = lds_addr(smem);
+    // Tiles that need no row clamp (wholly inside [window start, ctx)) copy from a
+    // wave-uniform base plus lane offsets fixed for the whole kernel: row r of the
+    // tile is key key0 + r, at r * kv_row from the tile's first key (contiguous),
+    // or at (r % 16) * ROWB inside the wave's block (paged).
+    uint32_t lane_src[T::COPIES];
+#pragma unroll
+    for (int c = 0; c < T::COPIES; ++c) {
+        const int off = (wave * T::COPIES + c) * 1024 + 16 * lane;
+        const int r = off / T::ROWB;
+        const int chunk = ((off % T::ROWB) / 16) ^ T::swz(r);
+        lane_src[c] = PAGED ? (uint32_t)((r % 16) * T::ROWB + chunk * 16) : (uint32_t)(r * kv_row + chunk * 16);
+    }
+    const bool lane_src_fits = PAGED || (int64_t)BN * kv_row < ((int64_t)1 << 31);
     auto issue_tile = [&](int j, int buf) {
         const int key0 = j * BN;
         int64_t block_src = 0;
@@ -181,6 +194,16 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 phys = 0;
             }
             block_src = (int64_t)phys * p.n_kv * 16 * T::ROWB;
+        }
+        if (lane_src_fits && key0 >= wg_lo && key0 + BN <= ctx) {   // uniform
+            const int64_t base = PAGED ? block_src : (int64_t)key0 * kv_row;
+#pragma unroll
+            for (int c = 0; c < T::COPIES; ++c) {
+                const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
+                copy_to_lds16(Kg + base, lane_src[c], dst);
+                copy_to_lds16(Vg + base, lane_src[c], dst + T::BYTES);
+            }
+            return;
         }
 #pragma unroll
         for (int c = 0; c < T::COPIES; ++c) {
@@ -211,12 +234,22 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     float l_run = 0.f;         // this lane's share of the softmax denominator
     const float c2 = p.scale_log2;
 
-    // Lane-constant parts of the operand addresses.
+    // Lane-constant parts of the operand addresses (the swizzle of a row depends on
+    // its index mod 16 only, so key 32 st + 16 jg + 8 t + vkey shares it with 8 t + vkey).
     const int ksw = T::swz(l32);                 // rows l32 and 32 + l32 share it
     const int g16 = lane >> 4, r16 = lane & 15;  // 16-lane group and lane within it
     const int vkey = 4 * half + r16 / 4;         // + 16 jg + 8 t + 32 st
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
+    uint32_t k_off[KK];       // K operand: row l32, dims 16 kk + 8 half .. +8
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk) k_off[kk] = l32 * T::ROWB + (((2 * kk + half) ^ ksw) * 16);
+    uint32_t vt_off[2][MT];   // V^T operand: key 8 t + vkey, dims 32 mt + ... (transposing read)
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+            vt_off[t][mt] = (8 * t + vkey) * T::ROWB + (((4 * mt + vchunk) ^ T::swz(8 * t + vkey)) * 16) + vbyte;
 
     // The tile loop, for P V in the input type (PE = E) or on the staged f16 V.
     auto tile_loop = [&](auto staged) {
@@ -235,13 +268,11 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 
             // S^T for the two 32-key halves, interleaved so each MFMA hides the other's latency.
             f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
-            const char* k0 = kl + l32 * T::ROWB;
-            const char* k1 = k0 + 32 * T::ROWB;
-    #pragma unroll
+#pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const int pos = ((2 * kk + half) ^ ksw) * 16;
-                const uint4 a0 = *reinterpret_cast<const uint4*>(k0 + pos);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(k1 + pos);
+                const char* ka = kl + k_off[kk];
+                const uint4 a0 = *reinterpret_cast<const uint4*>(ka);
+                const uint4 a1 = *reinterpret_cast<const uint4*>(ka + 32 * T::ROWB);
                 sc[0] = Mfma<E>::run(u32x4_t{a0.x, a0.y, a0.z, a0.w}, qreg[kk], sc[0]);
                 sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
             }
@@ -251,18 +282,18 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
             if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0) || (W > 0 && key0 < wave_lo_max)) {   // uniform
                 const int lim = (p.causal ? min(my_pos, ctx - 1) : ctx - 1) - key0;
                 const int lo = (W > 0 ? my_pos - W + 1 : 0) - key0;
-    #pragma unroll
+#pragma unroll
                 for (int st = 0; st < 2; ++st)
-    #pragma unroll
+#pragma unroll
                     for (int i = 0; i < 16; ++i) {
                         const int key = st * 32 + (i / 4) * 8 + half * 4 + (i % 4);
                         sc[st][i] = (key > lim || key < lo) ? -INFINITY : sc[st][i];
                     }
             }
             float tmax = -INFINITY;
-    #pragma unroll
+#pragma unroll
             for (int st = 0; st < 2; ++st)
-    #pragma unroll
+#pragma unroll
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[st][i]);
             {
                 float a2, b2;
@@ -274,26 +305,31 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
                 m_run = m_new;
                 l_run *= alpha;
-    #pragma unroll
+#pragma unroll
                 for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
             }
 
             // P = 2^(s scale - m) in the element type (bf16: hi + lo parts).
             u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
             float lsum = 0.f;
-    #pragma unroll
+#pragma unroll
             for (int st = 0; st < 2; ++st) {
-    #pragma unroll
+#pragma unroll
                 for (int jg = 0; jg < 2; ++jg) {
                     uint32_t hw[4], lw[4];
-    #pragma unroll
+#pragma unroll
                     for (int w = 0; w < 4; ++w) {
                         const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, -m_run));
                         const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, -m_run));
                         hw[w] = Mfma<PE>::pack(p0, p1);
-                        if constexpr (Mfma<PE>::kSplit)
+                        if constexpr (Mfma<PE>::kSplit) {
                             lw[w] = Mfma<PE>::pack(p0 - Mfma<PE>::lo_of(hw[w]), p1 - Mfma<PE>::hi_of(hw[w]));
-                        lsum += p0 + p1;
+                            lsum += p0 + p1;
+                        } else {
+                            // the denominator of the rounded weights the product uses
+                            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[w]),
+                                                          f16x2_t{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+                        }
                     }
                     ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
                     if constexpr (Mfma<PE>::kSplit) pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
@@ -303,19 +339,17 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 
             // O^T += V^T P^T. Lane (group g16, r16) fetches 4 dims of key vkey + ...,
             // and after the transpose holds 4 consecutive keys of one dim.
-    #pragma unroll
+#pragma unroll
             for (int st = 0; st < 2; ++st) {
-    #pragma unroll
+#pragma unroll
                 for (int jg = 0; jg < 2; ++jg) {
-    #pragma unroll
+#pragma unroll
                     for (int mt = 0; mt < MT; ++mt) {
                         uint32_t a[4];
-    #pragma unroll
+#pragma unroll
                         for (int t = 0; t < 2; ++t) {
-                            const int key = st * 32 + jg * 16 + 8 * t + vkey;
-                            const int pos = ((4 * mt + vchunk) ^ T::swz(key)) * 16 + vbyte;
                             const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_i16x4_t*)(vl_lds + key * T::ROWB + pos));
+                                (lds_i16x4_t*)(vl_lds + (st * 32 + jg * 16) * T::ROWB + vt_off[t][mt]));
                             a[2 * t] = __builtin_bit_cast(uint2, v).x;
                             a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
                         }
