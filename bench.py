@@ -56,7 +56,7 @@ KERNEL_SOURCES = {
     "decode": ["decode.hip", "decode_mfma.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "prefill": ["prefill.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "decode_multi": ["decode_multi.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
-    "decode_quant": ["decode_quant.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
+    "decode_quant": ["decode_quant.hip", "decode.hip", "quant.h", "mfma.h", "common.h", "launch.h", "api.hip"],
 }
 
 
@@ -576,13 +576,20 @@ def bench_decode_quant(args, fmt: str):
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
 
     def decode(s):
-        pa.paged_attn_decode_quant(s.q, s.k_pool, s.v_pool, s.k_scale, s.v_scale, fmt, s.block_table,
-                                   s.context_lens, s.scale, out=out, workspace=ws)
+        # the attention launch of a step: the fused append + decode, or decode alone
+        if args.unfused:
+            pa.paged_attn_decode_quant(s.q, s.k_pool, s.v_pool, s.k_scale, s.v_scale, fmt, s.block_table,
+                                       s.context_lens, s.scale, out=out, workspace=ws)
+        else:
+            pa.paged_attn_decode_quant_append(s.q, s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool,
+                                              s.k_scale, s.v_scale, fmt, s.block_table, s.context_lens,
+                                              s.scale, out=out, workspace=ws)
 
     def step(i):
         s = sets[i % len(sets)]
-        pa.kv_append_quant(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool, s.k_scale,
-                           s.v_scale, fmt)
+        if args.unfused:
+            pa.kv_append_quant(s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool, s.k_scale,
+                               s.v_scale, fmt)
         decode(s)
 
     for i in range(args.warmup):
@@ -617,8 +624,10 @@ def bench_decode_quant(args, fmt: str):
         "config": {"workload": name, "batch": B, "n_q": c0.n_q, "n_kv": c0.n_kv,
                    "head_dim": c0.head_dim, "block_size": 16, "context_lens": "2048 each",
                    "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
-                   "step": "kv_append_quant of one new token per sequence, then decode_quant "
-                           "(two launches)"},
+                   "step": ("kv_append_quant of one new token per sequence, then decode_quant "
+                            "(two launches)") if args.unfused else
+                           "one decode_quant_append launch: the new token's quantising append fused "
+                           "into decode"},
         "roofline": {"kernel": "decode_quant_kernel", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic("decode_quant", args.workload),

@@ -318,6 +318,30 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_quant_append -- one decode step over a quantised cache in
+ * one launch: pa_kv_append_quant of each sequence's new token fused into
+ * pa_paged_attn_decode_quant ([IW] decode step: write the new K/V at position
+ * cache_len, then attend over the whole cache; [IW] INT8 / FP8 item).
+ *
+ *   k_new, v_new  [batch][n_kv][head_dim] in q_dtype: the new token of each sequence
+ *   slot_mapping  int64 [batch]: its slot (negative: sequence b appends nothing)
+ *   k_cache, v_cache, k_scale, v_scale  the pools and per-row scales (written)
+ *   other arguments as for pa_paged_attn_decode_quant.
+ * The new rows are quantised exactly as pa_kv_append_quant does, so codes,
+ * scales and outputs equal those of the two calls bit for bit, under the same
+ * conditions as pa_paged_attn_decode_append: each sequence's slot must be its
+ * position ctx - 1, in a block no other sequence of the call reads
+ * (PA_VALIDATE=1 checks both).
+ */
+int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const void* v_new, pa_dtype q_dtype,
+                                      const int64_t* slot_mapping, int32_t batch, int32_t n_q, void* k_cache,
+                                      void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* cache,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                                      pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream);
+
+/*
  * Tuning override for the decode partition size, in tokens (a multiple of 16
  * and of the work one workgroup takes per pass). 0 restores the built-in
  * choice. Affects later pa_decode_workspace_bytes and pa_paged_attn_decode

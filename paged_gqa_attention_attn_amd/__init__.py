@@ -28,7 +28,8 @@ from ._lib import CacheDesc, LibraryNotBuilt
 
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
            "paged_attn_chunked_prefill", "paged_attn_decode_multi", "kv_append_quant",
-           "paged_attn_decode_quant", "quant_decode_workspace_bytes",
+           "paged_attn_decode_quant", "paged_attn_decode_quant_append", "quant_decode_workspace_bytes",
+           "prefill_workspace_bytes",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
@@ -401,6 +402,56 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         _dev(q, "q"), _DTYPE[q.dtype], B, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                                   slot_mapping: torch.Tensor, k_cache: torch.Tensor,
+                                   v_cache: torch.Tensor, k_scale: torch.Tensor, v_scale: torch.Tensor,
+                                   fmt: str, block_table: torch.Tensor, context_lens: torch.Tensor,
+                                   scale: float, out: torch.Tensor | None = None,
+                                   out_dtype: torch.dtype = torch.float32,
+                                   workspace: torch.Tensor | None = None, stream=None,
+                                   window: int = 0) -> torch.Tensor:
+    """One decode step over a quantised cache in one launch: quantise and write
+    k_new/v_new [B][n_kv][d] (q's dtype) at slot_mapping [B], then attend with q
+    [B][n_q][d]; returns out [B][n_q][d]."""
+    L = _lib.load()
+    desc = _quant_desc(k_cache, fmt)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache differ")
+    _check_scales(k_cache, k_scale, v_scale)
+    B, n_q, d = q.shape
+    if d != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the cache")
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    n_kv = k_cache.shape[1]
+    for name, t in (("k_new", k_new), ("v_new", v_new)):
+        if t.shape != (B, n_kv, d) or t.dtype != q.dtype:
+            raise ValueError(f"{name} must be [B][n_kv][d] in q's dtype")
+    if slot_mapping.shape != (B,):
+        raise ValueError("slot_mapping must be [B]")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+    if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][n_q][d] in a supported dtype")
+    if workspace is None:
+        need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    ws_ptr, ws_bytes = _workspace_args(workspace)
+    _check("pa_paged_attn_decode_quant_append", L.pa_paged_attn_decode_quant_append(
+        _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _DTYPE[q.dtype],
+        _dev(slot_mapping, "slot_mapping", torch.int64), B, n_q, _dev(k_cache, "k_cache"),
+        _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
+        _dev(v_scale, "v_scale", torch.float32), ctypes.byref(desc),
+        _dev(block_table, "block_table", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out

@@ -25,6 +25,7 @@ EXPORTS = (
     "pa_paged_attn_chunked_prefill",
     "pa_kv_append_quant",
     "pa_paged_attn_decode_quant",
+    "pa_paged_attn_decode_quant_append",
     "pa_set_decode_partition_tokens",
     "pa_set_workspace",
     "pa_last_error",
@@ -92,6 +93,10 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_decode_quant.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, vp, vp, cd, vp, i32, vp,
                                              ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_quant.restype = ctypes.c_int
+    L.pa_paged_attn_decode_quant_append.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp, vp,
+                                                    cd, vp, i32, vp, ctypes.c_float, i32, vp, ctypes.c_int,
+                                                    vp, sz, vp]
+    L.pa_paged_attn_decode_quant_append.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
     L.pa_set_workspace.argtypes = [vp, sz]

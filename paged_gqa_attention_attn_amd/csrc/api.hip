@@ -395,7 +395,7 @@ int resolve_workspace(size_t need, void** ws) {
 
 extern "C" {
 
-int32_t pa_version(void) { return 201; }
+int32_t pa_version(void) { return 202; }
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -826,12 +826,28 @@ int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const i
     return PA_OK;
 }
 
-int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
-                               const void* k_cache, const void* v_cache, const float* k_scale,
-                               const float* v_scale, const pa_cache_desc* cache,
-                               const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, int32_t window, void* out,
-                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// The new rows of a fused quantising append, with the pools and scales it writes.
+struct FusedQuantAppend {
+    const void* k_new;
+    const void* v_new;
+    const int64_t* slots;
+    void* k_cache_w;
+    void* v_cache_w;
+    float* k_scale_w;
+    float* v_scale_w;
+};
+
+int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
+                      const void* k_cache, const void* v_cache, const float* k_scale,
+                      const float* v_scale, const pa_cache_desc* cache,
+                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                      pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
+                      const FusedQuantAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq, true);
     if (rc) return rc;
     if (!is_quant(cache->dtype))
@@ -851,6 +867,14 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
         return fail(PA_ERR_INVALID_ARG, "decode_quant: q, caches, scales and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return fail(PA_ERR_INVALID_ARG, "decode_quant: block_table and context_lens must be 4-byte aligned");
+    if (fa) {
+        if (!fa->k_new || !fa->v_new || !fa->slots)
+            return fail(PA_ERR_INVALID_ARG, "decode_quant_append: k_new, v_new and slot_mapping must not be NULL");
+        if (!aligned16(fa->k_new) || !aligned16(fa->v_new))
+            return fail(PA_ERR_INVALID_ARG, "decode_quant_append: k_new and v_new must be 16-byte aligned");
+        if (reinterpret_cast<uintptr_t>(fa->slots) & 7u)
+            return fail(PA_ERR_INVALID_ARG, "decode_quant_append: slot_mapping must be 8-byte aligned");
+    }
 
     Plan pl;
     make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
@@ -866,8 +890,8 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
         if (!aligned16(workspace)) return fail(PA_ERR_INVALID_ARG, "decode_quant: workspace must be 16-byte aligned");
     }
     if (validate_enabled()) {
-        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
-                             static_cast<hipStream_t>(stream), 1, window);
+        rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens,
+                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream), 1, window);
         if (rc) return rc;
     }
 
@@ -904,11 +928,48 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;
     a.window = window;
+    if (fa) {
+        a.k_new = fa->k_new;
+        a.v_new = fa->v_new;
+        a.new_slots = fa->slots;
+        a.k_cache_w = fa->k_cache_w;
+        a.v_cache_w = fa->v_cache_w;
+        a.k_scale_w = fa->k_scale_w;
+        a.v_scale_w = fa->v_scale_w;
+    }
     const hipError_t e = pa::launch_decode_quant(a, to_elem(q_dtype),
                                                  static_cast<pa::QuantFmt>(static_cast<int>(cache->dtype)),
                                                  cache->head_dim, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_quant launch");
     return PA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
+                               const void* k_cache, const void* v_cache, const float* k_scale,
+                               const float* v_scale, const pa_cache_desc* cache,
+                               const int32_t* block_table, int32_t max_blocks_per_seq,
+                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
+                             max_blocks_per_seq, context_lens, scale, window, out, out_dtype, workspace,
+                             workspace_bytes, stream, nullptr);
+}
+
+int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const void* v_new, pa_dtype q_dtype,
+                                      const int64_t* slot_mapping, int32_t batch, int32_t n_q, void* k_cache,
+                                      void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* cache,
+                                      const int32_t* block_table, int32_t max_blocks_per_seq,
+                                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                                      pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+    const FusedQuantAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale};
+    return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
+                             max_blocks_per_seq, context_lens, scale, window, out, out_dtype, workspace,
+                             workspace_bytes, stream, &fa);
 }
 
 }  // extern "C"

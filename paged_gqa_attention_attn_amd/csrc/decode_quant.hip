@@ -23,12 +23,17 @@
 //    byte reads (4 keys of one dim per lane) and widened the same way.
 //  * Codes of rows outside [first, ctx) are zeroed in LDS and their P' is
 //    selected to 0: an unused slot may hold a NaN code or a NaN scale.
+//  * A decode step may carry its own append: the new token's K and V rows are
+//    quantised in registers exactly as the quantising append does (quant.h),
+//    patched into the LDS copy of their block, and written to the cache by one
+//    wave at the end, so the step equals the append followed by the decode.
 // Rows are stored with their 16-byte chunk c at position c ^ swz(row), swz
 // chosen for one-byte rows so that both operand reads stay conflict-free.
 #include <type_traits>
 
 #include "common.h"
 #include "launch.h"
+#include "quant.h"
 #include "mfma.h"
 
 namespace pa {
@@ -42,8 +47,12 @@ constexpr int MAX_WAVES = 8;
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
 
-struct QFp8 {};
-struct QInt8 {};
+struct QFp8 {
+    static constexpr bool kFp8 = true;
+};
+struct QInt8 {
+    static constexpr bool kFp8 = false;
+};
 
 // Four one-byte codes (bytes 0..3 of w) as four elements of a 16-bit operand of type E.
 template <class Q, class E> __device__ __forceinline__ uint2 widen4(uint32_t w);
@@ -168,6 +177,31 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
+    // Fused append: the wave whose run holds position ctx - 1 patches the new
+    // token's codes and scales into its LDS copy of that block, and one wave of
+    // the sequence's last partition writes them to the cache at the end. Both
+    // quantise the new rows exactly as the quantising append does.
+    constexpr int EPL = D / 64;   // row bytes (codes) per lane
+    const bool fused = p.new_slots != nullptr;
+    const int64_t new_slot = fused ? p.new_slots[b] : -1;
+    const bool slot_ok = new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS;
+    const int last_blk = ctx > 0 ? (ctx - 1) / BS : -1;
+    const bool patch_here = fused && slot_ok && last_blk >= wb0 && last_blk < wb0 + nb;
+    const bool writer = fused && slot_ok && part == nparts - 1 && hsgi == 0 && wave == 0;
+    uint32_t new_kc = 0, new_vc = 0;
+    float new_ks = 0.f, new_vs = 0.f;
+    if (patch_here || writer) {   // uniform over the wave
+        float xk[EPL], xv[EPL];
+        const int64_t e0 = ((int64_t)b * p.n_kv + g) * D + lane * EPL;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) {
+            xk[i] = load_f32<E>(p.k_new, e0 + i);
+            xv[i] = load_f32<E>(p.v_new, e0 + i);
+        }
+        new_ks = quantize_row<Q::kFp8, EPL>(xk, new_kc);
+        new_vs = quantize_row<Q::kFp8, EPL>(xv, new_vc);
+    }
+
     char* ring = smem + wave * L::WAVE_BYTES;
     const uint32_t ring_lds = lds_addr(ring);
     const int64_t block_bytes = (int64_t)p.n_kv * TILE;
@@ -231,6 +265,21 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             if (ahead == 0) wait_vmcnt<0>();
             char* base = ring + (i % R) * L::SLOTB;
             const int pos0 = (wb0 + i) * BS;
+            if (patch_here && wb0 + i == last_blk) {   // uniform: the new token's block
+                const int r = (ctx - 1) % BS;
+                const int at = r * ROW + ((((lane * EPL) / 16) ^ L::swz(r)) * 16) + (lane * EPL) % 16;
+                if constexpr (EPL == 2) {
+                    *reinterpret_cast<uint16_t*>(base + at) = (uint16_t)new_kc;
+                    *reinterpret_cast<uint16_t*>(base + TILE + at) = (uint16_t)new_vc;
+                } else {
+                    *reinterpret_cast<uint8_t*>(base + at) = (uint8_t)new_kc;
+                    *reinterpret_cast<uint8_t*>(base + TILE + at) = (uint8_t)new_vc;
+                }
+                if (lane == 0) {
+                    *reinterpret_cast<float*>(base + 2 * TILE + 4 * r) = new_ks;
+                    *reinterpret_cast<float*>(base + 2 * TILE + 64 + 4 * r) = new_vs;
+                }
+            }
             const bool edge = pos0 + BS > ctx || pos0 < first;   // uniform
             if (edge) {
                 // Zero the V code rows outside [first, ctx) (whole rows).
@@ -367,6 +416,24 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                 p.ws_l[pi] = Lsum;
             }
             p.ws_acc[pi * D + e] = A;
+        }
+    }
+
+    // The fused append's cache write goes last (a store counts in vmcnt).
+    if (writer) {
+        const int64_t row = ((new_slot / BS) * p.n_kv + g) * BS + new_slot % BS;
+        uint8_t* kd = static_cast<uint8_t*>(p.k_cache_w) + row * D + lane * EPL;
+        uint8_t* vd = static_cast<uint8_t*>(p.v_cache_w) + row * D + lane * EPL;
+        if constexpr (EPL == 2) {
+            *reinterpret_cast<uint16_t*>(kd) = (uint16_t)new_kc;
+            *reinterpret_cast<uint16_t*>(vd) = (uint16_t)new_vc;
+        } else {
+            *kd = (uint8_t)new_kc;
+            *vd = (uint8_t)new_vc;
+        }
+        if (lane == 0) {
+            p.k_scale_w[row] = new_ks;
+            p.v_scale_w[row] = new_vs;
         }
     }
 }

@@ -48,9 +48,13 @@ struct DecodeArgs {
     // Single-row decode on the matrix cores (decode_mfma.hip): gw query heads
     // (4, 8 or 16) per workgroup fill the MFMA columns; hs_wg must be 1.
     int32_t mfma;
-    // Quantised cache (decode_quant.hip): per-row scales [num_blocks][n_kv][16].
+    // Quantised cache (decode_quant.hip): per-row scales [num_blocks][n_kv][16], and
+    // their writable views for a fused quantising append (k_new / v_new then hold
+    // the new rows in q's type, quantised as pa_kv_append_quant does).
     const float* k_scale;
     const float* v_scale;
+    float* k_scale_w;
+    float* v_scale_w;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);

@@ -34,7 +34,7 @@ def same_bits(a: torch.Tensor, b: torch.Tensor) -> bool:
     b = b.detach().to("cpu").contiguous()
     if a.dtype != b.dtype or a.shape != b.shape:
         return False
-    iv = {4: torch.int32, 2: torch.int16, 8: torch.int64}[a.element_size()]
+    iv = {4: torch.int32, 2: torch.int16, 8: torch.int64, 1: torch.uint8}[a.element_size()]
     return torch.equal(a.view(iv), b.view(iv))
 
 

@@ -44,7 +44,7 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 201
+    assert L.pa_version() == 202
 
 
 def decode(L, **kw):
@@ -322,6 +322,35 @@ def decode_quant(L, **kw):
 def test_decode_quant_rejects(L, kw, code, msg):
     assert decode_quant(L, **kw) == code
     assert msg in _lib.last_error()
+
+
+def decode_quant_append(L, **kw):
+    a = dict(q=FAKE, kn=FAKE, vn=FAKE, q_dtype=_lib.PA_BF16, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE,
+             ks=FAKE, vs=FAKE, cache=_lib.CacheDesc(64, 16, 2, 128, _lib.PA_FP8_E4M3), bt=FAKE, maxb=4,
+             ctx=FAKE, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=FAKE, ws_bytes=1 << 20)
+    a.update(kw)
+    return L.pa_paged_attn_decode_quant_append(
+        a["q"], a["kn"], a["vn"], a["q_dtype"], a["slots"], a["batch"], a["n_q"], a["k"], a["v"], a["ks"],
+        a["vs"], ctypes.byref(a["cache"]), a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
+        a["out_dtype"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(kn=None), INVALID, "k_new"),
+    (dict(slots=None), INVALID, "slot_mapping"),
+    (dict(vn=FAKE + 4), INVALID, "aligned"),
+    (dict(slots=FAKE + 4), INVALID, "8-byte"),
+    (dict(cache=_lib.CacheDesc(64, 16, 2, 128, _lib.PA_BF16)), INVALID, "PA_FP8_E4M3"),
+    (dict(q_dtype=_lib.PA_F32), UNSUPPORTED, "bf16 or f16"),
+    (dict(window=-1), INVALID, "window"),
+])
+def test_decode_quant_append_rejects(L, kw, code, msg):
+    assert decode_quant_append(L, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_decode_quant_append_empty_batch_is_a_noop(L):
+    assert decode_quant_append(L, batch=0) == PA_OK
 
 
 def test_quantised_cache_refused_elsewhere(L):

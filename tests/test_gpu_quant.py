@@ -215,3 +215,72 @@ def test_full_size_8b_fp8_sampled(pa):
     want = _oracle_decode(c, sel=sel)
     assert_parity(got.cpu().numpy()[sel[:, 0], sel[:, 1]], want, "bf16", "8B fp8 sampled")
     assert torch.isfinite(got).all()
+
+
+# ---- fused quantising append + decode ------------------------------------------------------
+
+FUSED_SHAPES = {
+    # name: (q_dtype, batch, n_q, n_kv, head_dim, context_lens)
+    "gqa4_bf16": ("bf16", 5, 32, 8, 128, [1, 16, 17, 500, 1301]),
+    "gqa4_f16_d64": ("f16", 3, 8, 2, 64, [33, 64, 700]),
+    "mqa_g16": ("bf16", 2, 16, 1, 128, [5, 2100]),
+    "g2": ("bf16", 3, 4, 2, 128, [15, 16, 300]),
+}
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("name", sorted(FUSED_SHAPES))
+@pytest.mark.parametrize("variant", ["plain", "split", "window", "padding"])
+def test_fused_quant_step_equals_two_calls(pa, fmt, name, variant):
+    """decode_quant_append gives the codes, scales and outputs of kv_append_quant
+    followed by decode_quant, bit for bit."""
+    qd, B, n_q, n_kv, d, ctx = FUSED_SHAPES[name]
+    c = wl.make_quant_decode_case(fmt=fmt, q_dtype=qd, batch=B, n_q=n_q, n_kv=n_kv, head_dim=d,
+                                  context_lens=ctx, free_fraction=0.2,
+                                  seed=zlib.crc32(f"{fmt}{name}{variant}".encode()) % 100000,
+                                  device="cuda", name="fused")
+    say(f"[quant fused] {fmt} {name} {variant}: B={B} n_q={n_q} n_kv={n_kv} d={d} ctx={ctx}")
+    slots = c.slot_mapping.clone()
+    if variant == "padding":
+        slots[1] = -1
+    window = 100 if variant == "window" else 0
+    old = pa.set_decode_partition_tokens(256 if variant == "split" else 0)
+    try:
+        kc, vc, ks, vs = c.k_pool.clone(), c.v_pool.clone(), c.k_scale.clone(), c.v_scale.clone()
+        pa.kv_append_quant(c.new_k, c.new_v, slots, kc, vc, ks, vs, fmt)
+        two = pa.paged_attn_decode_quant(c.q, kc, vc, ks, vs, fmt, c.block_table, c.context_lens, c.scale,
+                                         window=window)
+        fkc, fvc, fks, fvs = c.k_pool.clone(), c.v_pool.clone(), c.k_scale.clone(), c.v_scale.clone()
+        one = pa.paged_attn_decode_quant_append(c.q, c.new_k, c.new_v, slots, fkc, fvc, fks, fvs, fmt,
+                                                c.block_table, c.context_lens, c.scale, window=window)
+        torch.cuda.synchronize()
+    finally:
+        pa.set_decode_partition_tokens(old)
+    assert same_bits(fkc, kc) and same_bits(fvc, vc), "codes differ"
+    assert same_bits(fks, ks) and same_bits(fvs, vs), "scales differ"
+    assert same_bits(one, two), "outputs differ"
+
+
+def test_fused_quant_step_matches_oracle_full_size(pa):
+    """The 8B decode shape over an FP8 cache as one fused step, against the oracle's
+    append followed by its decode (sampled rows)."""
+    c = wl.make_quant_decode_case(fmt="fp8", batch=32, n_q=32, n_kv=8, head_dim=128,
+                                  context_lens=[2048] * 32, seed=2003, device="cuda", name="8b_fp8")
+    say("[quant fused] 8B shape, fp8, full size, fused step vs oracle (sampled rows)")
+    kc, vc, ks, vs = c.k_pool.clone(), c.v_pool.clone(), c.k_scale.clone(), c.v_scale.clone()
+    got = pa.paged_attn_decode_quant_append(c.q, c.new_k, c.new_v, c.slot_mapping, kc, vc, ks, vs, "fp8",
+                                            c.block_table, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    okc, ovc, oks, ovs = _np(c.k_pool).copy(), _np(c.v_pool).copy(), _np(c.k_scale).copy(), _np(c.v_scale).copy()
+    oracle.kv_append_quant(stored_np(c.new_k), stored_np(c.new_v), c.q_dtype, _np(c.slot_mapping),
+                           okc, ovc, oks, ovs, "fp8")
+    assert np.array_equal(_np(kc), okc) and np.array_equal(_np(vc), ovc)
+    assert np.array_equal(_np(ks).view(np.uint32), oks.view(np.uint32))
+    assert np.array_equal(_np(vs).view(np.uint32), ovs.view(np.uint32))
+    rng = np.random.default_rng(3)
+    sel = np.asarray([[b, h] for b in range(32) for h in sorted({0, 5, 31, *rng.integers(0, 32, 2).tolist()})],
+                     np.int32)
+    want = oracle.decode(stored_np(c.q), okc, ovc, "fp8", _np(c.block_table), _np(c.context_lens), c.scale,
+                         q_dtype=c.q_dtype, k_scale=oks, v_scale=ovs, sel=sel)
+    stats = assert_parity(got.cpu().numpy()[sel[:, 0], sel[:, 1]], want, "bf16", "fused fp8 step")
+    say(f"    sampled rows={len(sel)} max_abs={stats['max_abs']:.2e}")
