@@ -166,14 +166,18 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
 
     // Copy block i's K and V tiles into ring slot i % R (8 KB for bf16, d = 128).
     const uint32_t ring_lds = lds_addr(ring);
+    // Tiles no other wave or workgroup reads (one head slice per KV head) stream
+    // with the non-temporal hint.
+    const bool once = p.hsg == 1 && p.hs_wg == 1;
     auto issue = [&](int i) {
         const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
         const uint32_t dst = ring_lds + (i % R) * 2 * TILE;
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(ksrc + phys * block_bytes + qq * 1024, dst + qq * 1024);
+        for (int qq = 0; qq < NQ; ++qq)
+            copy_to_lds16(ksrc + phys * block_bytes + qq * 1024, dst + qq * 1024, once);
 #pragma unroll
         for (int qq = 0; qq < NQ; ++qq)
-            copy_to_lds16(vsrc + phys * block_bytes + qq * 1024, dst + TILE + qq * 1024);
+            copy_to_lds16(vsrc + phys * block_bytes + qq * 1024, dst + TILE + qq * 1024, once);
     };
 
     // q and the block ids have landed before the ring copies start, so the

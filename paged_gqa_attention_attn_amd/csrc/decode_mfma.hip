@@ -186,15 +186,18 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
     }
     const char* kbase = (const char*)p.k_cache + (int64_t)g * TILE;
     const char* vbase = (const char*)p.v_cache + (int64_t)g * TILE;
+    // With one head slice per KV head, no other workgroup reads this wave's tiles:
+    // they stream with the non-temporal hint.
+    const bool once = p.hsg == 1;
     auto issue = [&](int i) {
         const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
         const uint32_t dst = ring_lds + (i % R) * 2 * TILE;
         const char* kb = kbase + phys * block_bytes;
         const char* vb = vbase + phys * block_bytes;
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024);
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024, once);
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024);
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024, once);
     };
 
     // Lane-constant operand offsets inside a ring slot.

@@ -143,6 +143,7 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     // Tile t of the run (keys wb0 * 16 + 32 t ..) into ring slot t % RING. Copy c
     // holds rows c * ROWS_PER_COPY .. of the tile; a row past the run reads the
     // run's last key instead (its score is masked and its V row stays finite).
+    const bool once = p.row_groups == 1;   // no other workgroup reads these tiles: non-temporal
     auto issue = [&](int t) {
         const uint32_t dst = ring_lds + (t % RING) * T::SLOT;
 #pragma unroll
@@ -155,8 +156,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
             const int chunk = ((off % T::ROWB) / 16) ^ T::swz(row);
             const int key = min(wb0 * BS + 32 * t + row, wave_end - 1);
             const int64_t src = phys * block_bytes + (int64_t)(key % BS) * T::ROWB + chunk * 16;
-            copy_to_lds16(kbase + src, dst + c * 1024);
-            copy_to_lds16(vbase + src, dst + T::BYTES + c * 1024);
+            copy_to_lds16(kbase + src, dst + c * 1024, once);
+            copy_to_lds16(vbase + src, dst + T::BYTES + c * 1024, once);
         }
     };
 

@@ -217,16 +217,17 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     // Scale copy: lanes 0-15 the K scales of the block's 16 rows, 16-31 the V
     // scales, 32-63 the same again (landing in the unused half of the slot).
     const float* sbase = ((lane >> 4) & 1 ? p.v_scale : p.k_scale) + (int64_t)g * BS + (lane & 15);
+    const bool once = p.hsg == 1;   // no other workgroup reads these tiles: non-temporal
     auto issue = [&](int i) {
         const int64_t phys = __builtin_amdgcn_readlane(my_phys, i);
         const uint32_t dst = ring_lds + (i % R) * L::SLOTB;
         const char* kb = kbase + phys * block_bytes;
         const char* vb = vbase + phys * block_bytes;
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024);
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024, once);
 #pragma unroll
-        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024);
-        copy_to_lds4(sbase + phys * p.n_kv * BS, dst + 2 * TILE);
+        for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024, once);
+        copy_to_lds4(sbase + phys * p.n_kv * BS, dst + 2 * TILE, once);
     };
 
     uint32_t k_off[KK];   // K operand: row col, bytes 32 kk + 8 grp .. +8
