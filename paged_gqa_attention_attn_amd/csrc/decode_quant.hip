@@ -64,13 +64,12 @@ template <> __device__ __forceinline__ uint2 widen4<QFp8, F16>(uint32_t w) {
     return make_uint2(__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false)),
                       __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true)));
 }
-// A signed byte is exact in fp32, and its fp32 value has at most 7 significant
-// bits, so the upper half of the fp32 pattern is the exact bf16.
+// A signed byte is exact in fp32 and has at most 7 significant bits, so the
+// packed fp32 -> bf16 conversion (one instruction per pair) rounds nothing.
 template <> __device__ __forceinline__ uint2 widen4<QInt8, BF16>(uint32_t w) {
-    uint32_t h[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) h[i] = as_u32((float)(int8_t)(w >> (8 * i))) >> 16;
-    return make_uint2(h[0] | (h[1] << 16), h[2] | (h[3] << 16));
+    const bf16x2_t a = {(__bf16)(float)(int8_t)w, (__bf16)(float)(int8_t)(w >> 8)};
+    const bf16x2_t b = {(__bf16)(float)(int8_t)(w >> 16), (__bf16)(float)(int8_t)(w >> 24)};
+    return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 template <> __device__ __forceinline__ uint2 widen4<QInt8, F16>(uint32_t w) {
     f16x2_t a, b;
