@@ -252,10 +252,41 @@ constexpr int kMultiRows = 32;
 struct MultiPlan {
     int32_t blocks_per_wave, nparts_max, row_groups;
     size_t m_floats, bytes;
+    // Matrix-core decode kernel instead (G * q_rows a multiple of 4, at most 16):
+    // slices of gw (head, row) pairs as MFMA columns, hsg slices per KV head.
+    int32_t mfma, gw, hsg, waves_tok;
 };
+
+// (head, row) pairs of one KV head that the matrix-core decode kernel takes as
+// MFMA columns: a multiple of 4 up to 16, which one workgroup covers whole (so
+// every K/V tile has one reader); larger groups go to the multi-row kernel,
+// whose 32-pair tiles read each tile once for up to 32 pairs.
+bool multi_uses_mfma(int32_t G, int32_t q_rows, const pa_cache_desc* c) {
+    const int64_t pairs = (int64_t)G * q_rows;
+    return (c->dtype == PA_BF16 || c->dtype == PA_F16) && pairs % 4 == 0 && pairs <= 16 &&
+           env_int("PA_DECODE_MFMA", 1) != 0;
+}
 
 MultiPlan multi_plan(int32_t batch, int32_t q_rows, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c) {
     MultiPlan pl{};
+    const int32_t G = n_q / c->n_kv;
+    if (multi_uses_mfma(G, q_rows, c)) {
+        const int32_t pairs = G * q_rows;
+        pl.mfma = 1;
+        pl.gw = pairs % 16 == 0 ? 16 : pairs % 8 == 0 ? 8 : 4;
+        pl.hsg = pairs / pl.gw;
+        int32_t w = env_int("PA_DECODE_WAVES", kMaxWaves);
+        if (w < 1 || w > kMaxWaves) w = kMaxWaves;
+        const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
+        while (w > 1 && w * mfma_wave_bytes(1, tile, pl.gw, c->head_dim) > kLdsBytes) --w;
+        pl.waves_tok = w;
+        mfma_partitions((int64_t)batch * c->n_kv * pl.hsg, max_blocks, w, &pl.blocks_per_wave, &pl.nparts_max);
+        if (pl.nparts_max > 1) {
+            pl.m_floats = (size_t)batch * q_rows * n_q * pl.nparts_max;
+            pl.bytes = 2 * round16(pl.m_floats * sizeof(float)) + pl.m_floats * c->head_dim * sizeof(float);
+        }
+        return pl;
+    }
     const int64_t rows_per_kv = (int64_t)(n_q / c->n_kv) * q_rows;
     pl.row_groups = (int32_t)((rows_per_kv + kMultiRows - 1) / kMultiRows);
     int32_t tokens = g_partition_tokens.load();
@@ -440,29 +471,44 @@ int pa_kv_append(const void* k, const void* v, const int64_t* slot_mapping, int3
     return PA_OK;
 }
 
+}  // extern "C"
+
+namespace {
+
+// Partitions a matrix-core plan can take for any span up to max_blocks (a
+// windowed call plans for a shorter span). With fixed runs of blocks per wave
+// (an explicit partition size) the partition count grows with the span, so
+// max_blocks bounds it. Otherwise each wave gets at least span * units /
+// kTargetWaves blocks and at least 4, so below the 64-block cap a span takes at
+// most min(ceil(kTargetWaves / (waves * units)), ceil(max_blocks / (4 * waves)))
+// partitions, and at the cap the count again grows with the span.
+int32_t mfma_parts_bound(int32_t nparts_at_max, int64_t units, int32_t waves, int32_t max_blocks) {
+    if (g_partition_tokens.load() > 0) return nparts_at_max;
+    const int64_t w = waves;
+    const int64_t by_waves = (kTargetWaves + w * units - 1) / (w * units);
+    const int64_t by_min_run = (max_blocks + 4 * w - 1) / (4 * w);
+    return (int32_t)std::max<int64_t>(nparts_at_max, std::min(by_waves, by_min_run));
+}
+
+size_t partials_bytes(int64_t rows, int32_t nparts, int32_t head_dim) {
+    if (nparts <= 1) return 0;
+    const size_t m_floats = (size_t)rows * nparts;
+    return 2 * round16(m_floats * sizeof(float)) + m_floats * head_dim * sizeof(float);
+}
+
+}  // namespace
+
+extern "C" {
+
 size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_per_seq,
                                  const pa_cache_desc* cache) {
     if (check_decode_args(batch, n_q, cache, max_blocks_per_seq, true) != PA_OK) return 0;
     Plan pl;
     make_plan(batch, n_q, max_blocks_per_seq, cache, &pl);
-    // A windowed call plans for a shorter span of blocks. With fixed runs of blocks
-    // per wave (the VALU plan, or an explicit partition size) the partition count
-    // grows with the span, so max_blocks_per_seq bounds it. The matrix-core plan
-    // gives each wave at least span * units / kTargetWaves blocks and at least 4,
-    // so below its 64-block cap a span takes at most
-    // min(ceil(kTargetWaves / (waves * units)), ceil(max_blocks / (4 * waves)))
-    // partitions, and at the cap the count again grows with the span.
     int32_t np = pl.nparts_max;
-    if (pl.mfma && g_partition_tokens.load() <= 0) {
-        const int64_t units = (int64_t)batch * cache->n_kv * pl.hsg;
-        const int64_t w = pl.waves_tok;
-        const int64_t by_waves = (kTargetWaves + w * units - 1) / (w * units);
-        const int64_t by_min_run = (max_blocks_per_seq + 4 * w - 1) / (4 * w);
-        np = (int32_t)std::max<int64_t>(np, std::min(by_waves, by_min_run));
-    }
-    if (np <= 1) return 0;
-    const size_t m_floats = (size_t)batch * n_q * np;
-    return 2 * round16(m_floats * sizeof(float)) + m_floats * cache->head_dim * sizeof(float);
+    if (pl.mfma)
+        np = mfma_parts_bound(np, (int64_t)batch * cache->n_kv * pl.hsg, pl.waves_tok, max_blocks_per_seq);
+    return partials_bytes((int64_t)batch * n_q, np, cache->head_dim);
 }
 
 }  // extern "C"
@@ -663,7 +709,11 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache) {
     if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK || q_rows < 1) return 0;
-    return multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache).bytes;
+    const MultiPlan pl = multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache);
+    if (!pl.mfma) return pl.bytes;
+    const int32_t np = mfma_parts_bound(pl.nparts_max, (int64_t)batch * cache->n_kv * pl.hsg, pl.waves_tok,
+                                        max_blocks_per_seq);
+    return partials_bytes((int64_t)batch * q_rows * n_q, np, cache->head_dim);
 }
 
 int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
@@ -724,16 +774,26 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     a.num_blocks = cache->num_blocks;
     a.max_blocks = max_blocks_per_seq;
     a.group = n_q / cache->n_kv;
-    a.waves_tok = kMultiWaves;
     a.blocks_per_wave = pl.blocks_per_wave;
     a.nparts_max = pl.nparts_max;
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = q_rows;
-    a.row_groups = pl.row_groups;
     a.window = window;
-    const hipError_t e = pa::launch_decode_multi(a, to_elem(cache->dtype), cache->head_dim,
-                                                 static_cast<hipStream_t>(stream));
+    hipError_t e;
+    if (pl.mfma) {
+        a.gw = pl.gw;
+        a.hs_wg = 1;
+        a.hsg = pl.hsg;
+        a.waves_tok = pl.waves_tok;
+        a.ring = 1;
+        a.mfma = 1;
+        e = pa::launch_decode_mfma(a, to_elem(cache->dtype), cache->head_dim, static_cast<hipStream_t>(stream));
+    } else {
+        a.waves_tok = kMultiWaves;
+        a.row_groups = pl.row_groups;
+        e = pa::launch_decode_multi(a, to_elem(cache->dtype), cache->head_dim, static_cast<hipStream_t>(stream));
+    }
     if (e == hipErrorNotSupported)
         return fail(PA_ERR_UNSUPPORTED, "multi-row decode: no kernel for these arguments");
     if (e != hipSuccess) return hip_fail(e, "multi-row decode launch");

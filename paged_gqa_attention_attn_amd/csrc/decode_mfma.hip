@@ -28,6 +28,11 @@
 //    count, and the shader clock drops under it); here the VALU only runs the
 //    softmax.
 //
+// Multi-row decode (several new tokens per sequence, draft verification) runs
+// here too when the G * NR (head, row) pairs of a KV head are a multiple of 4 up
+// to 16: the pairs are the MFMA columns, the row at position ctx - NR + r sees
+// keys up to itself, so masks become per column on the blocks that need them.
+//
 // Tiles reach LDS by global_load_lds_dwordx4 as in decode.hip, each row stored
 // unpadded with its 16-byte chunk c at position c ^ swz(row) (the copy picks
 // each lane's source chunk so that its destination stays 16 * lane), which
@@ -53,6 +58,7 @@ namespace {
 constexpr int BS = 16;          // tokens per cache block
 constexpr float TAU = 8.0f;     // rescale threshold (log2 units)
 constexpr int MAX_WAVES = 8;    // waves per workgroup
+constexpr float M_FLOOR = -1e30f; // running-max start (finite)
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -113,21 +119,27 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
     const int b = blockIdx.z;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
-    const int col = lane & 15;    // MFMA column: query head h0 + col
+    const int col = lane & 15;    // MFMA column: (head, row) pair hsgi * HW + col
     const int grp = lane >> 4;    // 16-lane group
+
+    // MFMA column col holds (head, row) pair v = hsgi * HW + col of the KV head's
+    // G * NR pairs: new-token row v / G of the step's NR (1 outside multi-row
+    // decode), query head g * G + v % G. qo_row(v) is its row of q and of out.
+    const int G = p.group, NR = p.q_rows;
+    auto qo_row = [&](int v) { return ((int64_t)b * NR + v / G) * p.n_q + (int64_t)g * G + v % G; };
+    const int v_col = hsgi * HW + (col < HW ? col : 0);
 
     // Context-independent loads first (q, the table row, the new K/V row), so the
     // start waits for one memory latency rather than a chain.
-    const int h0 = g * p.group + hsgi * HW;
     const int blk0 = part * p.waves_tok * p.blocks_per_wave + wave * p.blocks_per_wave;
     u32x4_t qreg[KK];
     {
-        // Columns past the workgroup's HW heads stay zero (their scores are 0 and
+        // Columns past the workgroup's HW pairs stay zero (their scores are 0 and
         // their outputs are never stored).
-        const char* qrow = (const char*)p.q + (int64_t)(b * p.n_q + h0 + (col < HW ? col : 0)) * ROW;
+        const char* qrow = (const char*)p.q + qo_row(v_col) * ROW;
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-            // B operand of S^T: dims 32 kk + 8 grp .. +8 of head h0 + col (the same
+            // B operand of S^T: dims 32 kk + 8 grp .. +8 of column col's q row (the same
             // dims the K operand below takes, which is all the product needs).
             uint4 v = make_uint4(0, 0, 0, 0);
             if (col < HW) v = *reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2);
@@ -152,7 +164,10 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
     const bool ctx_bad = ctx_in > cap;
     const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
-    const int first = window_first(ctx, 1, p.window);
+    const int first = window_first(ctx, NR, p.window);   // the earliest position any row sees
+    // This column's row sees positions col_lo .. col_hi (causal among the new rows).
+    const int col_hi = ctx - NR + v_col / G;
+    const int col_lo = p.window > 0 ? col_hi - p.window + 1 : 0;
     const int fb = first / BS;
     const int bpp = p.waves_tok * p.blocks_per_wave;
     const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
@@ -212,7 +227,10 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
     f32x4_t o[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;   // running max (log2 units) of head h0 + col
+    // Running max (log2 units) of column col. It starts finite: with several rows a
+    // block can hold no key that some column attends, and 2^(s - m) of a masked s
+    // must then be 0, not 2^(-inf + inf).
+    float m_run = M_FLOOR;
     float l_run = 0.f;         // this lane's share of its denominator (keys 4 grp .. +4 of each block)
 
     // q and the new row have landed before the ring starts: were the compiler to
@@ -244,7 +262,8 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
                     *reinterpret_cast<uint4*>(dst) = new_row;
                 }
             }
-            const bool edge = pos0 + BS > ctx || pos0 < first;   // uniform
+            // Some key of the block is outside some column's range (uniform).
+            const bool edge = pos0 + BS - 1 > ctx - NR || (p.window > 0 && pos0 < ctx - p.window);
             if (edge) {
                 // Zero the V rows outside [first, ctx) (whole rows: the swizzle does not matter).
 #pragma unroll
@@ -273,7 +292,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
             lds_reads_done();
             if (i + R < nb) issue(i + R);
 
-            // S^T: s[j] = q_(h0 + col) . K[key 4 grp + j] (raw; scaled inside exp2).
+            // S^T: s[j] = q_col . K[key 4 grp + j] (raw; scaled inside exp2).
             f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) s = Mfma16<E>::qk(ka[kk], qreg[kk], s);
@@ -281,7 +300,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int pos = pos0 + 4 * grp + j;
-                    s[j] = (pos >= ctx || pos < first) ? -INFINITY : s[j];
+                    s[j] = (pos > col_hi || pos < col_lo) ? -INFINITY : s[j];
                 }
             }
             float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * p.scale_log2;   // scale > 0
@@ -301,7 +320,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
                 pr[j] = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -m_run));
                 l_run += pr[j];
             }
-            // P^T operand: keys 4 grp .. +4 of head h0 + col, exactly where S^T put them.
+            // P^T operand: keys 4 grp .. +4 of column col, exactly where S^T put them.
             const uint2 ph = make_uint2(Mfma<E>::pack(pr[0], pr[1]), Mfma<E>::pack(pr[2], pr[3]));
             if constexpr (Mfma<E>::kSplit) {
                 // hi and lo parts stacked along k of one 16x16x32 product (twice the
@@ -320,7 +339,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
         }
     }
 
-    // The denominator of head h0 + col is spread over the four 16-lane groups; o
+    // The denominator of column col is spread over the four 16-lane groups; o
     // holds dims 16 t + 4 grp + i of that head, each in exactly one lane.
     l_run = stride_reduce<16, false>(l_run);
     float* mine = reinterpret_cast<float*>(ring);
@@ -360,7 +379,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
                 A = fmaf(f, aw[w], A);
             }
         }
-        const int64_t row = (int64_t)b * p.n_q + h0 + hl;
+        const int64_t row = qo_row(hsgi * HW + hl);
         if (nparts == 1) {
             float o1 = (Lsum == 0.f) ? 0.f : A * __builtin_amdgcn_rcpf(Lsum);
             if (ctx_bad) o1 = NAN;
@@ -397,7 +416,9 @@ template <class E, int D, int HW, int R> hipError_t launch_typed(const DecodeArg
     hipLaunchKernelGGL((decode_mfma_kernel<E, D, HW, R>), grid, dim3(64 * a.waves_tok), lds, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.nparts_max <= 1) return err;
-    return launch_decode_reduce(a, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
+    DecodeArgs m = a;
+    m.n_q = a.n_q * a.q_rows;   // the reduce kernel's rows: (b, r, h) in [B][q_rows][n_q] order
+    return launch_decode_reduce(m, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
 }
 
 template <class E, int D, int R> hipError_t launch_hw(const DecodeArgs& a, hipStream_t s) {
@@ -421,7 +442,10 @@ template <class E, int D> hipError_t launch_ring(const DecodeArgs& a, hipStream_
 
 hipError_t launch_decode_mfma(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s) {
     if (a.hs_wg != 1 || a.waves_tok < 1 || a.waves_tok > MAX_WAVES) return hipErrorInvalidValue;
-    if (a.q_rows != 1 || a.window < 0) return hipErrorInvalidValue;
+    if (a.q_rows < 1 || a.window < 0) return hipErrorInvalidValue;
+    // Several new rows per sequence: their pairs must fill whole slices of gw
+    // columns, and the fused append serves single-row steps only.
+    if (a.q_rows > 1 && ((a.group * a.q_rows) % a.gw != 0 || a.new_slots != nullptr)) return hipErrorInvalidValue;
     if (e == Elem::BF16 && head_dim == 128) return launch_ring<BF16, 128>(a, s);
     if (e == Elem::BF16 && head_dim == 64) return launch_ring<BF16, 64>(a, s);
     if (e == Elem::F16 && head_dim == 128) return launch_ring<F16, 128>(a, s);

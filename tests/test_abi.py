@@ -282,12 +282,22 @@ def test_decode_multi_rejects(L, kw, code, msg):
     assert msg in _lib.last_error()
 
 
-def test_decode_multi_workspace_query(L):
-    # 2048-token partitions: 4096-token contexts need (m, l, acc) for 2 partitions of
-    # every (sequence, row, query head).
+def _partials(rows):
+    return 2 * rows * 4 + rows * 128 * 4   # m and l (fp32 each), then acc [rows][128]
+
+
+def test_decode_multi_workspace_query(L, monkeypatch):
+    # Multi-row kernel (G * q_rows = 8 * 4 = 32 (head, row) pairs): 2048-token partitions,
+    # so 4096-token contexts need (m, l, acc) for 2 partitions of every (sequence, row, head).
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 64, 128, desc(nb=4096, n_kv=8)) == 0
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 64, 256, desc(nb=4096, n_kv=8)) == _partials(4 * 4 * 64 * 2)
+    # 16 pairs go to the matrix-core decode kernel: 8-wave workgroups over 32
+    # (sequence, KV head) units take 4 partitions of a 128-block table ...
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 128, desc(nb=4096, n_kv=8)) == _partials(4 * 4 * 32 * 4)
+    # ... unless that kernel is turned off.
+    monkeypatch.setenv("PA_DECODE_MFMA", "0")
     assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 128, desc(nb=4096, n_kv=8)) == 0
-    rows = 4 * 4 * 32 * 2
-    assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 256, desc(nb=4096, n_kv=8)) == 2 * rows * 4 + rows * 128 * 4
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 256, desc(nb=4096, n_kv=8)) == _partials(4 * 4 * 32 * 2)
     assert L.pa_decode_multi_workspace_bytes(4, 0, 32, 256, desc(nb=4096, n_kv=8)) == 0
     assert multi(L, B=0) == PA_OK
 

@@ -82,6 +82,24 @@ def test_partition_sizes_agree(pa, tokens):
     assert_parity(got.cpu().numpy(), oracle_multi(c), "bf16", f"partition {tokens}")
 
 
+@pytest.mark.parametrize("kernel", ["mfma", "multi"])
+def test_blocks_past_the_first_rows_position(pa, monkeypatch, kernel):
+    """One block per wave: a wave whose only block lies past row 0's position (or
+    wholly before a later row's window) attends nothing for that row's columns,
+    which must give weights of 0, not NaN."""
+    if kernel == "multi":
+        monkeypatch.setenv("PA_DECODE_MFMA", "0")
+    c = wl.make_chunk_case(batch=4, chunk_len=4, prefix_lens=[93, 77, 12, 2000], n_q=32, n_kv=8,
+                           head_dim=128, dtype="bf16", seed=64, device="cuda")
+    say(f"[multi] {kernel}: contexts {[p + 4 for p in (93, 77, 12, 2000)]}, one block per wave")
+    prev = pa.set_decode_partition_tokens(128 if kernel == "mfma" else 256)
+    try:
+        got = gpu_multi(pa, c)
+    finally:
+        pa.set_decode_partition_tokens(prev)
+    assert_parity(got.cpu().numpy(), oracle_multi(c), "bf16", f"{kernel}: short runs")
+
+
 def test_agrees_with_chunked_prefill_and_is_reproducible(pa):
     c = wl.make_chunk_case(batch=3, chunk_len=6, prefix_lens=[50, 1500, 2600], n_q=32, n_kv=8,
                            head_dim=128, dtype="bf16", free_fraction=0.2, seed=62, device="cuda")
