@@ -60,6 +60,16 @@ def _check_stored(a: np.ndarray, dtype: str, name: str) -> None:
         raise TypeError(f"{name}: dtype {dtype} is passed as {np.dtype(want).name}, got {a.dtype}")
 
 
+def _slopes(alibi, n_q: int):
+    """ALiBi slopes as a contiguous float32 [n_q] array, or None."""
+    if alibi is None:
+        return None
+    a = np.ascontiguousarray(alibi, dtype=np.float32)
+    if a.shape != (n_q,):
+        raise ValueError("alibi slopes must be [n_q]")
+    return a
+
+
 class Oracle:
     """ctypes view of one compiled oracle library (the default one, or a test variant)."""
 
@@ -75,10 +85,10 @@ class Oracle:
         L.oracle_kv_append.argtypes = [vp, vp, vp, i64, i32, i32, i32, i64, i32, vp, vp]
         L.oracle_kv_append.restype = i64
         L.oracle_decode.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i64, i32,
-                                    vp, i32, vp, f64, i32, vp, i64, vp, i32]
+                                    vp, i32, vp, f64, i32, vp, vp, i64, vp, i32]
         L.oracle_decode.restype = ctypes.c_int
         L.oracle_decode_ex.argtypes = [vp, ctypes.c_int, vp, vp, ctypes.c_int, vp, vp, i32, i32, i32,
-                                       i32, i64, i32, vp, i32, vp, f64, i32, vp, i64, vp, i32]
+                                       i32, i64, i32, vp, i32, vp, f64, i32, vp, vp, i64, vp, i32]
         L.oracle_decode_ex.restype = ctypes.c_int
         L.oracle_encode_fp8_e4m3.argtypes = [vp, i64, vp]
         L.oracle_encode_fp8_e4m3.restype = ctypes.c_int
@@ -88,7 +98,7 @@ class Oracle:
                                              i64, i32, vp, vp, vp, vp]
         L.oracle_kv_append_quant.restype = i64
         L.oracle_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, f64,
-                                     i32, vp, i64, vp, i32]
+                                     i32, vp, vp, i64, vp, i32]
         L.oracle_prefill.restype = ctypes.c_int
         L.oracle_max_threads.argtypes = []
         L.oracle_max_threads.restype = ctypes.c_int
@@ -180,11 +190,12 @@ class Oracle:
                block_table: np.ndarray, context_lens: np.ndarray, scale: float,
                sel: np.ndarray | None = None, n_threads: int = 0, window: int = 0,
                q_dtype: str | None = None, k_scale: np.ndarray | None = None,
-               v_scale: np.ndarray | None = None) -> np.ndarray:
+               v_scale: np.ndarray | None = None, alibi: np.ndarray | None = None) -> np.ndarray:
         """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d].
 
         ``window`` W > 0 keeps only the last W positions of each context. For a quantised
-        cache (``dtype`` "fp8" or "int8") pass ``q_dtype`` and the [nb][n_kv][bs] scales."""
+        cache (``dtype`` "fp8" or "int8") pass ``q_dtype`` and the [nb][n_kv][bs] scales.
+        ``alibi``: float32 [n_q] slopes m_h; the score of position t gets -m_h (ctx - 1 - t)."""
         q_dtype = q_dtype or dtype
         _check_stored(q, q_dtype, "q")
         for name, a in (("k_pool", k_pool), ("v_pool", v_pool)):
@@ -204,6 +215,7 @@ class Oracle:
         ctx = np.ascontiguousarray(context_lens, dtype=np.int32)
         if ctx.shape != (B,):
             raise ValueError("context_lens must be [B]")
+        alibi = _slopes(alibi, n_q)
         if sel is not None:
             sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 2)
             out = np.empty((sel.shape[0], d), dtype=np.float64)
@@ -214,8 +226,8 @@ class Oracle:
                                        _ptr(np.ascontiguousarray(v_pool)), DTYPE_CODES[dtype],
                                        _ptr(k_scale), _ptr(v_scale), B, n_q, n_kv, d, nb, bs,
                                        _ptr(bt), bt.shape[1], _ptr(ctx), float(scale), int(window),
-                                       _ptr(sel), 0 if sel is None else sel.shape[0], _ptr(out),
-                                       n_threads)
+                                       _ptr(alibi), _ptr(sel), 0 if sel is None else sel.shape[0],
+                                       _ptr(out), n_threads)
         if rc != 0:
             raise ValueError("oracle_decode rejected its arguments")
         return out
@@ -223,10 +235,11 @@ class Oracle:
     # -- prefill over contiguous Q/K/V ---------------------------------------
     def prefill(self, q: np.ndarray, k: np.ndarray, v: np.ndarray, dtype: str, causal: bool,
                 scale: float, sel: np.ndarray | None = None, n_threads: int = 0,
-                window: int = 0) -> np.ndarray:
+                window: int = 0, alibi: np.ndarray | None = None) -> np.ndarray:
         """q [B][S][n_q][d], k/v [B][S][n_kv][d]; returns fp64 [B][S][n_q][d] or [len(sel)][d].
 
-        ``sel`` rows are (b, h, i) triples.
+        ``sel`` rows are (b, h, i) triples. ``alibi`` (causal only): float32 [n_q] slopes
+        m_h; the score of row i and key j gets -m_h (i - j).
         """
         for name, a in (("q", q), ("k", k), ("v", v)):
             _check_stored(a, dtype, name)
@@ -234,6 +247,7 @@ class Oracle:
         n_kv = k.shape[2]
         if k.shape != (B, S, n_kv, d) or v.shape != k.shape:
             raise ValueError("shape mismatch")
+        alibi = _slopes(alibi, n_q)
         if sel is not None:
             sel = np.ascontiguousarray(sel, dtype=np.int32).reshape(-1, 3)
             out = np.empty((sel.shape[0], d), dtype=np.float64)
@@ -241,8 +255,8 @@ class Oracle:
             out = np.empty((B, S, n_q, d), dtype=np.float64)
         rc = self.lib.oracle_prefill(_ptr(np.ascontiguousarray(q)), _ptr(np.ascontiguousarray(k)),
                                      _ptr(np.ascontiguousarray(v)), DTYPE_CODES[dtype], B, S, n_q,
-                                     n_kv, d, int(bool(causal)), float(scale), int(window), _ptr(sel),
-                                     0 if sel is None else sel.shape[0], _ptr(out), n_threads)
+                                     n_kv, d, int(bool(causal)), float(scale), int(window), _ptr(alibi),
+                                     _ptr(sel), 0 if sel is None else sel.shape[0], _ptr(out), n_threads)
         if rc != 0:
             raise ValueError("oracle_prefill rejected its arguments")
         return out
@@ -259,7 +273,8 @@ class Oracle:
         decode definition over the first ctx_b - C + i + 1 positions, so this runs
         oracle_decode with one pseudo-sequence per (b, i); rows at negative positions are
         zero. With ``window`` W > 0 a row sees only the last W of its positions (the sliding
-        window applies per row). Returns fp64 [B][C][n_q][d], or [len(sel)][d] for (b, i, h)."""
+        window applies per row); ``alibi`` slopes bias each row by its own position. Returns
+        fp64 [B][C][n_q][d], or [len(sel)][d] for (b, i, h)."""
         B, C, n_q, d = q.shape
         bt = np.ascontiguousarray(block_table, dtype=np.int32)
         ctx = np.ascontiguousarray(context_lens, dtype=np.int64)

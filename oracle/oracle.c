@@ -297,9 +297,13 @@ int64_t oracle_kv_append_quant(const void* k, const void* v, int src_dtype,
 
 /*
  * out[c] = sum_t w_t V[t][c] / sum_t w_t with w_t = exp(s_t - max s),
- * s_t = scale * <q, K[t]>. Key t is fetched through key_index(t), an element
- * offset of K[t][0] (and V[t][0]) in k_base / v_base. n_keys == 0 gives a
- * zero row (an empty context attends to nothing).
+ * s_t = scale * <q, K[t]> - slope * (qpos - kpos_t). Key t is fetched through
+ * key_off[t], an element offset of K[t][0] (and V[t][0]) in k_base / v_base, and
+ * sits at position kpos_t = kpos0 + t; the query sits at position qpos. The
+ * second term is ALiBi's linear bias ("LLM 推理全过程的维度变化与核心公式",
+ * research.frankk.site, position-encoding section: scores_ij = q_i.k_j / sqrt(d)
+ * - m_h (i - j), one slope m_h per head); slope 0 leaves plain attention.
+ * n_keys == 0 gives a zero row (an empty context attends to nothing).
  */
 typedef struct {
     const void* k_base;
@@ -309,6 +313,7 @@ typedef struct {
     int64_t n_keys;
     const float* k_scale; /* quantised cache: scale of row key_off / head_dim; else NULL */
     const float* v_scale;
+    int64_t kpos0;        /* position of key 0 */
 } key_list;
 
 /* Element c of row t of K (or V): the stored value, times the row's scale in a quantised cache. */
@@ -319,8 +324,8 @@ static double key_elem(const key_list* keys, int is_v, int64_t t, int32_t c, int
     return sc ? x * (double)sc[base / d] : x;
 }
 
-static void attend(const double* q, int32_t d, double scale, const key_list* keys,
-                   double* scores, double* out) {
+static void attend(const double* q, int32_t d, double scale, double slope, int64_t qpos,
+                   const key_list* keys, double* scores, double* out) {
     for (int32_t c = 0; c < d; ++c) out[c] = 0.0;
     if (keys->n_keys == 0) return;
 
@@ -328,7 +333,7 @@ static void attend(const double* q, int32_t d, double scale, const key_list* key
     for (int64_t t = 0; t < keys->n_keys; ++t) {
         double dot = 0.0;
         for (int32_t c = 0; c < d; ++c) dot += q[c] * key_elem(keys, 0, t, c, d);
-        scores[t] = scale * dot;
+        scores[t] = scale * dot - slope * (double)(qpos - (keys->kpos0 + t));
         if (scores[t] > m) m = scores[t];
     }
     double den = 0.0;
@@ -356,6 +361,9 @@ static int set_threads(int32_t n_threads) {
  * k_pool/v_pool[num_blocks][n_kv][block_size][head_dim]    (dtype)
  * block_table  [batch][max_blocks_per_seq] int32
  * context_lens [batch] int32, tokens attended (0 <= ctx <= max_blocks*bs)
+ * alibi_slopes optional fp32 [n_q]: ALiBi slope m_h of query head h, adding
+ *              -m_h (ctx - 1 - t) to the score of position t (the query is
+ *              position ctx - 1); NULL: no bias
  * window       0: all ctx positions; W > 0: only the last W of them, positions
  *              max(0, ctx - W) .. ctx - 1 (sliding-window attention, [IW]
  *              "KV Cache 的形状与增长", sliding-window item: the cache is bounded at
@@ -374,6 +382,7 @@ int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void*
                      int64_t num_blocks, int32_t block_size,
                      const int32_t* block_table, int32_t max_blocks_per_seq,
                      const int32_t* context_lens, double scale, int32_t window,
+                     const float* alibi_slopes,
                      const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return -1;
     if (window < 0) return -1;
@@ -423,8 +432,10 @@ int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void*
                 const int64_t off = t % block_size;
                 offs[t - first] = ((phys * n_kv + g) * block_size + off) * head_dim;
             }
-            key_list keys = {k_pool, v_pool, kv_dtype, offs, ctx - first, k_scale, v_scale};
-            attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
+            /* the query is the newest position, ctx - 1 */
+            key_list keys = {k_pool, v_pool, kv_dtype, offs, ctx - first, k_scale, v_scale, first};
+            const double slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;
+            attend(qv, head_dim, scale, slope, (int64_t)ctx - 1, &keys, scores, out + it * head_dim);
         }
         free(qv);
         free(scores);
@@ -439,11 +450,12 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
                   int64_t num_blocks, int32_t block_size,
                   const int32_t* block_table, int32_t max_blocks_per_seq,
                   const int32_t* context_lens, double scale, int32_t window,
+                  const float* alibi_slopes,
                   const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (is_quantised(dtype)) return -1;
     return oracle_decode_ex(q, dtype, k_pool, v_pool, dtype, NULL, NULL, batch, n_q, n_kv, head_dim,
                             num_blocks, block_size, block_table, max_blocks_per_seq, context_lens,
-                            scale, window, sel, n_sel, out, n_threads);
+                            scale, window, alibi_slopes, sel, n_sel, out, n_threads);
 }
 
 /* ---- prefill over contiguous Q/K/V --------------------------------------- */
@@ -453,14 +465,17 @@ int oracle_decode(const void* q, const void* k_pool, const void* v_pool, int dty
  * sel optional list of n_sel (b, h, i) triples; NULL means every (b, i, h)
  * out [batch][seq_len][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
  * Row i attends to keys j <= i when causal, else to all seq_len keys; with
- * window W > 0 (causal only) to keys max(0, i - W + 1) .. i.
+ * window W > 0 (causal only) to keys max(0, i - W + 1) .. i. alibi_slopes
+ * (causal only; NULL: none) adds -m_h (i - j) to the scores of head h.
  */
 int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                    int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                    int32_t head_dim, int32_t causal, double scale, int32_t window,
+                   const float* alibi_slopes,
                    const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k || !v || !out) return -1;
     if (window < 0 || (window > 0 && !causal)) return -1;
+    if (alibi_slopes && !causal) return -1;
     if (is_quantised(dtype)) return -1;
     if (elem_bytes_of(dtype) == 0 || batch < 0 || seq_len < 0 || n_q <= 0 || n_kv <= 0 ||
         head_dim <= 0)
@@ -501,8 +516,9 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                 qv[c] = load_elem(q, dtype, (((int64_t)b * seq_len + i) * n_q + h) * head_dim + c);
             for (int32_t j = first; j < n_keys; ++j)
                 offs[j - first] = (((int64_t)b * seq_len + j) * n_kv + g) * head_dim;
-            key_list keys = {k, v, dtype, offs, n_keys - first, NULL, NULL};
-            attend(qv, head_dim, scale, &keys, scores, out + it * head_dim);
+            key_list keys = {k, v, dtype, offs, n_keys - first, NULL, NULL, first};
+            const double slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;
+            attend(qv, head_dim, scale, slope, i, &keys, scores, out + it * head_dim);
         }
         free(qv);
         free(scores);

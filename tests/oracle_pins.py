@@ -784,4 +784,116 @@ def pin_kv_append_rejects_out_of_range_slot(orc):
     raise AssertionError("slot 8 in an 8-slot pool was accepted")
 
 
+# ---- ALiBi bias ("LLM 推理全过程的维度变化与核心公式", position-encoding section:
+# scores_ij = q_i.k_j / sqrt(d) - m_h (i - j), one slope m_h per head) -------------------
+
+def alibi_slopes(n_q: int) -> np.ndarray:
+    """Distinct per-head slopes (the geometric 2^(-8 (h+1) / n_q) family)."""
+    return (2.0 ** (-8.0 * (np.arange(n_q) + 1) / n_q)).astype(np.float32)
+
+
+def sdpa64_bias(q, k, v, scale, bias):
+    """torch's float64 SDPA with an additive float mask; q [H][Lq][d], k/v [H][Lk][d], bias [H][Lq][Lk]."""
+    return torch.nn.functional.scaled_dot_product_attention(
+        q.unsqueeze(0), k.unsqueeze(0), v.unsqueeze(0), attn_mask=bias.unsqueeze(0), scale=scale)[0]
+
+
+def _alibi_decode_vs_sdpa(orc, window):
+    n_q, n_kv, d = 8, 2, 8
+    ctxs = [1, 5, 9, 16, 23]
+    c = decode_case(71 + window, ctxs, n_q, n_kv, d)
+    slopes = alibi_slopes(n_q)
+    got = run_decode(orc, c, alibi=slopes, window=window)
+    G = n_q // n_kv
+    m = torch.from_numpy(slopes.astype(np.float64))
+    for b, L in enumerate(ctxs):
+        first = L - window if 0 < window < L else 0
+        q = exact(c["q"][b], "f32").unsqueeze(1)
+        k = exact(c["ks"][b][first:], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        v = exact(c["vs"][b][first:], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        pos = torch.arange(first, L, dtype=torch.float64)                 # key positions
+        bias = (-m[:, None] * ((L - 1) - pos)[None, :]).unsqueeze(1)      # query at L - 1
+        want = sdpa64_bias(q, k, v, c["scale"], bias)[:, 0, :]
+        close(got[b], want.numpy(), 1e-12, f"alibi decode vs sdpa b={b} ctx={L} window={window}")
+
+
+def pin_decode_alibi_matches_library_sdpa(orc):
+    _alibi_decode_vs_sdpa(orc, window=0)
+
+
+def pin_decode_alibi_with_window_matches_library_sdpa(orc):
+    _alibi_decode_vs_sdpa(orc, window=6)
+
+
+def pin_prefill_alibi_matches_library_sdpa(orc):
+    B, S, n_q, n_kv, d = 2, 11, 6, 2, 8
+    q, k, v = _prefill_inputs(72, B, S, n_q, n_kv, d)
+    scale = 1 / math.sqrt(d)
+    slopes = alibi_slopes(n_q)
+    got = orc.prefill(q, k, v, "f32", True, scale, alibi=slopes)
+    G = n_q // n_kv
+    i = torch.arange(S, dtype=torch.float64)
+    dist = i[:, None] - i[None, :]                                        # i - j
+    m = torch.from_numpy(slopes.astype(np.float64))
+    bias = -m[:, None, None] * dist[None]
+    bias = bias.masked_fill((dist < 0)[None], float("-inf"))             # causal
+    for b in range(B):
+        qq = exact(q[b], "f32").permute(1, 0, 2).contiguous()
+        kk = exact(k[b], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        vv = exact(v[b], "f32").permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        want = sdpa64_bias(qq, kk, vv, scale, bias).permute(1, 0, 2)
+        close(got[b], want.numpy(), 1e-12, "alibi prefill vs sdpa")
+
+
+def pin_chunked_prefill_alibi_matches_library_sdpa(orc):
+    # Sequences of 13 and 21 keys, the last C = 6 the chunk: row r is position L - C + r.
+    n_q, n_kv, d, C = 4, 2, 8, 6
+    g = torch.Generator().manual_seed(73)
+    lens = [13, 21]
+    ks = rand_seqs(g, lens, n_kv, d, "f32")
+    vs = rand_seqs(g, lens, n_kv, d, "f32")
+    q = stored(torch.randn(2, C, n_q, d, generator=g), "f32")
+    kp, bt = pack_pool(ks, 4, 12, np.random.default_rng(8), np.float32(np.nan))
+    vp, _ = pack_pool(vs, 4, 12, np.random.default_rng(8), np.float32(np.nan))
+    slopes = alibi_slopes(n_q)
+    got = orc.chunked_prefill(q, kp, vp, "f32", bt, np.asarray(lens, np.int32), 0.3, alibi=slopes)
+    m = torch.from_numpy(slopes.astype(np.float64))
+    for b, L in enumerate(lens):
+        rows = torch.arange(L - C, L, dtype=torch.float64)
+        keys = torch.arange(L, dtype=torch.float64)
+        dist = rows[:, None] - keys[None, :]
+        bias = (-m[:, None, None] * dist[None]).masked_fill((dist < 0)[None], float("-inf"))
+        qq = exact(q[b], "f32").permute(1, 0, 2).contiguous()
+        kk = exact(ks[b], "f32").permute(1, 0, 2).repeat_interleave(2, dim=0).contiguous()
+        vv = exact(vs[b], "f32").permute(1, 0, 2).repeat_interleave(2, dim=0).contiguous()
+        want = sdpa64_bias(qq, kk, vv, 0.3, bias).permute(1, 0, 2)
+        close(got[b], want.numpy(), 1e-12, f"alibi chunked prefill vs sdpa, length {L}")
+
+
+def pin_decode_alibi_closed_form(orc):
+    # q = 0 leaves only the bias: position t weighs r^(L-1-t), r = e^-m. With V[t] = t
+    # the output is (L - 1) - S1 / S0, S0 = sum_k r^k = (1 - r^L) / (1 - r) and
+    # S1 = sum_k k r^k = r (1 - L r^(L-1) + (L - 1) r^L) / (1 - r)^2, k = 0 .. L - 1.
+    d, L = 4, 37
+    pos = np.arange(L, dtype=np.float32)
+    rows = np.repeat(pos[:, None, None], d, axis=2)                      # [L][1][d], row t = t
+    kp, bt = pack_pool([np.ones((L, 1, d), np.float32)], 4, 12, np.random.default_rng(9), np.float32(np.nan))
+    vp, _ = pack_pool([rows], 4, 12, np.random.default_rng(9), np.float32(np.nan))
+    slopes = np.asarray([0.5, 0.125, 0.03125], np.float32)
+    q = np.zeros((1, 3, d), np.float32)
+    got = orc.decode(q, kp, vp, "f32", bt, np.asarray([L], np.int32), 1.0, alibi=slopes)
+    for h, m in enumerate(slopes.astype(np.float64)):
+        r = math.exp(-m)
+        s0 = (1 - r ** L) / (1 - r)
+        s1 = r * (1 - L * r ** (L - 1) + (L - 1) * r ** L) / (1 - r) ** 2
+        close(got[0, h], np.full(d, (L - 1) - s1 / s0), 1e-12, f"alibi closed form, slope {m}")
+
+
+def pin_decode_alibi_zero_slopes_change_nothing(orc):
+    c = decode_case(74, [3, 17, 30], 4, 2, 8, dtype="bf16")
+    plain = run_decode(orc, c)
+    zero = run_decode(orc, c, alibi=np.zeros(4, np.float32))
+    assert (plain == zero).all(), "zero ALiBi slopes changed the output"
+
+
 ALL_PINS = {name: fn for name, fn in sorted(globals().items()) if name.startswith("pin_")}

@@ -22,7 +22,7 @@ MUTANTS = {
                              "const int32_t g = h % n_kv;                          /* [AE] 3.1"),
     "prefill_group_map_mod": ("        const int32_t g = h / group;\n        const int32_t n_keys",
                               "        const int32_t g = h % n_kv;\n        const int32_t n_keys"),
-    "dropped_scale": ("scores[t] = scale * dot;", "scores[t] = dot;"),
+    "dropped_scale": ("scores[t] = scale * dot - slope", "scores[t] = dot - slope"),
     "exp_sign_flip": ("const double w = exp(scores[t] - m);", "const double w = exp(m - scores[t]);"),
     "no_normalisation": ("out[c] /= den;", "out[c] /= 1.0;"),
     "den_squares": ("den += w;", "den += w * w;"),
@@ -65,6 +65,13 @@ MUTANTS = {
                                    "(window > 0 && ctx > window) ? ctx - window - 1 : 0"),
     "prefill_window_one_too_narrow": ("(window > 0 && i + 1 > window) ? i + 1 - window : 0",
                                       "(window > 0 && i + 1 > window) ? i + 2 - window : 0"),
+    "alibi_bias_sign": ("scale * dot - slope * (double)(qpos - (keys->kpos0 + t))",
+                        "scale * dot + slope * (double)(qpos - (keys->kpos0 + t))"),
+    "alibi_physical_key_position": ("slope * (double)(qpos - (keys->kpos0 + t))",
+                                    "slope * (double)(qpos - keys->key_off[t] / d)"),
+    "alibi_slope_of_the_kv_group": (
+        "const double slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;\n            attend(qv, head_dim, scale, slope, (int64_t)ctx - 1",
+        "const double slope = alibi_slopes ? (double)alibi_slopes[g] : 0.0;\n            attend(qv, head_dim, scale, slope, (int64_t)ctx - 1"),
 }
 
 
