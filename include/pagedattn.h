@@ -129,6 +129,10 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *                 positions max(0, ctx - W) .. ctx - 1. Block-table entries of
  *                 blocks wholly before that range are never read, so an engine
  *                 may recycle them. Negative: PA_ERR_INVALID_ARG.
+ *   alibi_slopes  NULL, or device fp32 [n_q], 4-byte aligned: ALiBi's slope m_h of
+ *                 each query head ([IW] position-encoding section: scores_ij =
+ *                 q_i.k_j / sqrt(d) - m_h (i - j)); the score of position t gets
+ *                 -m_h (ctx - 1 - t), the query being the newest position ctx - 1.
  *   out           [batch][n_q][head_dim], out_dtype PA_F32 or cache->dtype
  *   workspace     device scratch of at least pa_decode_workspace_bytes(...)
  *                 bytes for the same arguments, or NULL: then the workspace
@@ -144,7 +148,8 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, float scale, int32_t window, void* out,
+                         const int32_t* context_lens, float scale, int32_t window,
+                         const float* alibi_slopes, void* out,
                          pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -171,6 +176,7 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
                                 void* k_cache, void* v_cache, const pa_cache_desc* cache,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, float scale, int32_t window,
+                                const float* alibi_slopes,
                                 void* out, pa_dtype out_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream);
 
@@ -187,6 +193,9 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *   window  0: no window; W > 0 (causal only) narrows row i to keys
  *           max(0, i - W + 1) .. i ([IW] sliding-window item). Negative, or
  *           positive with causal == 0: PA_ERR_INVALID_ARG.
+ *   alibi_slopes  NULL, or device fp32 [n_q] (causal only): row i's score for
+ *           key j gets -m_h (i - j) (as for pa_paged_attn_decode); with
+ *           causal == 0: PA_ERR_INVALID_ARG.
  *   out   [batch][seq_len][n_q][head_dim], out_dtype PA_F32 or dtype
  *   workspace  device scratch of at least pa_prefill_workspace_bytes(...) bytes
  *         (16-byte aligned), or NULL: then the workspace of pa_set_workspace if
@@ -205,6 +214,7 @@ size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, int32_t window,
+                          const float* alibi_slopes,
                           void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream);
 
@@ -220,6 +230,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  *   k_cache, v_cache  pools described by `cache`, already holding the rows' own
  *                 K/V (pa_kv_append of the q_rows new tokens first)
  *   block_table, context_lens, scale  as for pa_paged_attn_decode
+ *   alibi_slopes  NULL, or device fp32 [n_q]: the row at position p scores key
+ *                 position j with -m_h (p - j) added (as for pa_paged_attn_decode)
  *   window        0: none; W > 0: the row at position p attends to positions
  *                 max(0, p - W + 1) .. p only ([IW] sliding-window item); entries
  *                 of blocks wholly before the first row's window are never read
@@ -237,7 +249,8 @@ size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_
 int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
                                const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               const int32_t* context_lens, float scale, int32_t window,
+                         const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -256,6 +269,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  *                 positions 0 .. that position (causal mask aligned at the bottom
  *                 right; chunk_len == context_lens[b] is a plain causal prefill)
  *   scale         multiplies q.k; must be positive
+ *   alibi_slopes  NULL, or device fp32 [n_q]: the row at position p scores key
+ *                 position j with -m_h (p - j) added (as for pa_paged_attn_decode)
  *   window        0: none; W > 0: the row at position p attends to positions
  *                 max(0, p - W + 1) .. p only ([IW] sliding-window item); entries
  *                 of blocks wholly before the first row's window are never read
@@ -269,6 +284,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* context_lens, float scale, int32_t window,
+                                  const float* alibi_slopes,
                                   void* out, pa_dtype out_dtype, void* stream);
 
 /*
@@ -314,7 +330,8 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
                                const void* k_cache, const void* v_cache, const float* k_scale,
                                const float* v_scale, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               const int32_t* context_lens, float scale, int32_t window,
+                         const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -337,7 +354,8 @@ int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const vo
                                       const int64_t* slot_mapping, int32_t batch, int32_t n_q, void* k_cache,
                                       void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* cache,
                                       const int32_t* block_table, int32_t max_blocks_per_seq,
-                                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                                      const int32_t* context_lens, float scale, int32_t window,
+                         const float* alibi_slopes, void* out,
                                       pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream);
 

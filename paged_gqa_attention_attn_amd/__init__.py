@@ -16,6 +16,8 @@ Layouts (see include/pagedattn.h):
   quantised caches: codes uint8 (FP8 E4M3 bit patterns; torch.float8_e4m3fn views
   are accepted too) or int8 [num_blocks][n_kv][16][d], scales float32
   [num_blocks][n_kv][16]
+  alibi_slopes float32 [n_q], optional on every attention call: query head h adds
+  -alibi_slopes[h] * (query position - key position) to each score
 """
 from __future__ import annotations
 
@@ -62,6 +64,15 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
 def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
     s = stream if stream is not None else torch.cuda.current_stream(t.device)
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _alibi_arg(alibi_slopes, n_q: int):
+    """Device pointer of ALiBi slopes (float32 [n_q] on the GPU), or None for no bias."""
+    if alibi_slopes is None:
+        return None
+    if alibi_slopes.dtype != torch.float32 or tuple(alibi_slopes.shape) != (n_q,):
+        raise ValueError(f"alibi_slopes must be float32 [{n_q}]")
+    return _dev(alibi_slopes, "alibi_slopes", torch.float32)
 
 
 def _workspace_args(workspace):
@@ -133,7 +144,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
                       block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                       out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
                       workspace: torch.Tensor | None = None, stream=None,
-                      window: int = 0) -> torch.Tensor:
+                      window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention of q [B][n_q][d] over the paged caches; returns out [B][n_q][d].
     window W > 0 restricts each sequence to its last W positions."""
     L = _lib.load()
@@ -159,7 +171,8 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
     _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
         _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
@@ -171,7 +184,8 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
                              out: torch.Tensor | None = None,
                              out_dtype: torch.dtype = torch.float32,
                              workspace: torch.Tensor | None = None, stream=None,
-                             window: int = 0) -> torch.Tensor:
+                             window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step in one launch: write k_new/v_new [B][n_kv][d] at slot_mapping [B],
     then attend with q [B][n_q][d] over the caches; returns out [B][n_q][d].
     window W > 0 restricts each sequence to its last W positions."""
@@ -204,7 +218,8 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
         _dev(slot_mapping, "slot_mapping", torch.int64), B, n_q, _dev(k_cache, "k_cache", dt),
         _dev(v_cache, "v_cache", dt), ctypes.byref(desc),
         _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
@@ -220,7 +235,8 @@ def prefill_workspace_bytes(dtype: torch.dtype, batch: int, seq_len: int, n_kv: 
 def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal: bool,
                        scale: float, out: torch.Tensor | None = None,
                        out_dtype: torch.dtype = torch.float32, stream=None,
-                       window: int = 0, workspace: torch.Tensor | None = None) -> torch.Tensor:
+                       window: int = 0, workspace: torch.Tensor | None = None,
+                       alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """Attention of a prompt over itself: q [B][S][n_q][d], k/v [B][S][n_kv][d].
     window W > 0 (causal only) restricts row i to keys i - W + 1 .. i. workspace:
     a device buffer of at least prefill_workspace_bytes(...) bytes, or None to
@@ -244,7 +260,8 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     _check("pa_paged_attn_prefill", L.pa_paged_attn_prefill(
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
-        d, int(bool(causal)), float(scale), int(window), _dev(out, "out"), _DTYPE[out.dtype],
+        d, int(bool(causal)), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"), _DTYPE[out.dtype],
         *_workspace_args(workspace), _stream(q, stream)))
     return out
 
@@ -253,7 +270,8 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
                                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                                out: torch.Tensor | None = None,
                                out_dtype: torch.dtype = torch.float32, stream=None,
-                               window: int = 0) -> torch.Tensor:
+                               window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """A prompt chunk q [B][C][n_q][d] attends to its paged prefix and causally to itself;
     row i of sequence b is position context_lens[b] - C + i. Returns out [B][C][n_q][d].
     window W > 0 restricts the row at position p to positions p - W + 1 .. p."""
@@ -274,7 +292,8 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     _check("pa_paged_attn_chunked_prefill", L.pa_paged_attn_chunked_prefill(
         _dev(q, "q", dt), B, C, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], _stream(q, stream)))
     return out
 
@@ -283,7 +302,8 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                             out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
                             workspace: torch.Tensor | None = None, stream=None,
-                            window: int = 0) -> torch.Tensor:
+                            window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """q_rows new rows per sequence, q [B][q_rows][n_q][d]; row r of sequence b is position
     context_lens[b] - q_rows + r. Returns out [B][q_rows][n_q][d]. window W > 0 restricts
     the row at position p to positions p - W + 1 .. p."""
@@ -309,7 +329,8 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
         _dev(q, "q", dt), B, R, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
@@ -373,7 +394,8 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
                             block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                             out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
                             workspace: torch.Tensor | None = None, stream=None,
-                            window: int = 0) -> torch.Tensor:
+                            window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """Decode attention of q [B][n_q][d] (bf16 or f16) over a quantised paged cache (codes
     and per-row scales); returns out [B][n_q][d] (float32 or q's dtype)."""
     L = _lib.load()
@@ -402,7 +424,8 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         _dev(q, "q"), _DTYPE[q.dtype], B, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
         ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
 
@@ -414,7 +437,8 @@ def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: 
                                    scale: float, out: torch.Tensor | None = None,
                                    out_dtype: torch.dtype = torch.float32,
                                    workspace: torch.Tensor | None = None, stream=None,
-                                   window: int = 0) -> torch.Tensor:
+                                   window: int = 0,
+        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
     """One decode step over a quantised cache in one launch: quantise and write
     k_new/v_new [B][n_kv][d] (q's dtype) at slot_mapping [B], then attend with q
     [B][n_q][d]; returns out [B][n_q][d]."""
@@ -452,6 +476,7 @@ def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: 
         _dev(v_cache, "v_cache"), _dev(k_scale, "k_scale", torch.float32),
         _dev(v_scale, "v_scale", torch.float32), ctypes.byref(desc),
         _dev(block_table, "block_table", torch.int32), maxb,
-        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window), _dev(out, "out"),
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out

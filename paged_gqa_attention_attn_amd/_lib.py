@@ -69,33 +69,33 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_kv_append.restype = ctypes.c_int
     L.pa_decode_workspace_bytes.argtypes = [i32, i32, i32, cd]
     L.pa_decode_workspace_bytes.restype = sz
-    L.pa_paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cd, vp, i32, vp, ctypes.c_float, i32,
+    L.pa_paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cd, vp, i32, vp, ctypes.c_float, i32, vp,
                                        vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode.restype = ctypes.c_int
     L.pa_paged_attn_decode_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, cd, vp, i32, vp,
-                                              ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
+                                              ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_append.restype = ctypes.c_int
     L.pa_decode_multi_workspace_bytes.argtypes = [i32, i32, i32, i32, cd]
     L.pa_decode_multi_workspace_bytes.restype = sz
     L.pa_paged_attn_decode_multi.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
-                                             ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
+                                             ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_multi.restype = ctypes.c_int
     L.pa_prefill_workspace_bytes.argtypes = [ctypes.c_int, i32, i32, i32, i32]
     L.pa_prefill_workspace_bytes.restype = sz
     L.pa_paged_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
-                                        ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
+                                        ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_prefill.restype = ctypes.c_int
     L.pa_paged_attn_chunked_prefill.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
-                                                ctypes.c_float, i32, vp, ctypes.c_int, vp]
+                                                ctypes.c_float, i32, vp, vp, ctypes.c_int, vp]
     L.pa_paged_attn_chunked_prefill.restype = ctypes.c_int
     L.pa_kv_append_quant.argtypes = [vp, vp, ctypes.c_int, vp, i32, vp, vp, vp, vp, cd, vp]
     L.pa_kv_append_quant.restype = ctypes.c_int
     L.pa_paged_attn_decode_quant.argtypes = [vp, ctypes.c_int, i32, i32, vp, vp, vp, vp, cd, vp, i32, vp,
-                                             ctypes.c_float, i32, vp, ctypes.c_int, vp, sz, vp]
+                                             ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_quant.restype = ctypes.c_int
     L.pa_paged_attn_decode_quant_append.argtypes = [vp, vp, vp, ctypes.c_int, vp, i32, i32, vp, vp, vp, vp,
-                                                    cd, vp, i32, vp, ctypes.c_float, i32, vp, ctypes.c_int,
-                                                    vp, sz, vp]
+                                                    cd, vp, i32, vp, ctypes.c_float, i32, vp, vp,
+                                                    ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_quant_append.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32

@@ -426,7 +426,7 @@ int resolve_workspace(size_t need, void** ws) {
 
 extern "C" {
 
-int32_t pa_version(void) { return 202; }
+int32_t pa_version(void) { return 203; }
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -525,7 +525,8 @@ struct FusedAppend {
 
 int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, const void* v_cache,
                 const pa_cache_desc* cache, const int32_t* block_table, int32_t max_blocks_per_seq,
-                const int32_t* context_lens, float scale, int32_t window, void* out,
+                const int32_t* context_lens, float scale, int32_t window,
+                const float* alibi_slopes, void* out,
                 pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
                 const FusedAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
@@ -535,6 +536,8 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "decode: a pointer argument is NULL");
@@ -601,6 +604,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;
     a.window = window;
+    a.alibi = alibi_slopes;
     if (fa) {
         a.k_new = fa->k_new;
         a.v_new = fa->v_new;
@@ -621,10 +625,11 @@ extern "C" {
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
                          const int32_t* block_table, int32_t max_blocks_per_seq,
-                         const int32_t* context_lens, float scale, int32_t window, void* out,
+                         const int32_t* context_lens, float scale, int32_t window,
+                         const float* alibi_slopes, void* out,
                          pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
-                       context_lens, scale, window, out, out_dtype, workspace, workspace_bytes,
+                       context_lens, scale, window, alibi_slopes, out, out_dtype, workspace, workspace_bytes,
                        stream, nullptr);
 }
 
@@ -633,11 +638,12 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
                                 void* k_cache, void* v_cache, const pa_cache_desc* cache,
                                 const int32_t* block_table, int32_t max_blocks_per_seq,
                                 const int32_t* context_lens, float scale, int32_t window,
+                                const float* alibi_slopes,
                                 void* out, pa_dtype out_dtype, void* workspace,
                                 size_t workspace_bytes, void* stream) {
     const FusedAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache};
     return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
-                       context_lens, scale, window, out, out_dtype, workspace, workspace_bytes,
+                       context_lens, scale, window, alibi_slopes, out, out_dtype, workspace, workspace_bytes,
                        stream, &fa);
 }
 
@@ -650,6 +656,7 @@ size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len
 int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype dtype,
                           int32_t batch, int32_t seq_len, int32_t n_q, int32_t n_kv,
                           int32_t head_dim, int32_t causal, float scale, int32_t window,
+                          const float* alibi_slopes,
                           void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
     if (dtype != PA_BF16 && dtype != PA_F16)
@@ -666,7 +673,10 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (window > 0 && !causal) return fail(PA_ERR_INVALID_ARG, "a sliding window needs causal == 1");
+    if (alibi_slopes && !causal) return fail(PA_ERR_INVALID_ARG, "ALiBi slopes need causal == 1");
     if (batch == 0 || seq_len == 0) return PA_OK;
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -686,6 +696,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.scale_log2 = scale * 1.4426950408889634f;
     a.out_f32 = out_dtype == PA_F32;
     a.window = window;
+    a.alibi = alibi_slopes;
     if (prefill_stages(dtype)) {
         const size_t need = prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
         if (!workspace) {
@@ -719,7 +730,8 @@ size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_
 int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int32_t n_q,
                                const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               const int32_t* context_lens, float scale, int32_t window,
+                               const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
@@ -731,6 +743,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: a pointer argument is NULL");
@@ -780,6 +794,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = q_rows;
     a.window = window;
+    a.alibi = alibi_slopes;
     hipError_t e;
     if (pl.mfma) {
         a.gw = pl.gw;
@@ -804,6 +819,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* context_lens, float scale, int32_t window,
+                                  const float* alibi_slopes,
                                   void* out, pa_dtype out_dtype, void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
@@ -815,6 +831,8 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0 || chunk_len == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
@@ -846,6 +864,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     a.max_blocks = max_blocks_per_seq;
     a.num_blocks = cache->num_blocks;
     a.window = window;
+    a.alibi = alibi_slopes;
     const hipError_t e = pa::launch_prefill(a, to_elem(cache->dtype), cache->head_dim,
                                             static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)
@@ -905,7 +924,8 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
                       const void* k_cache, const void* v_cache, const float* k_scale,
                       const float* v_scale, const pa_cache_desc* cache,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
-                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                      const int32_t* context_lens, float scale, int32_t window,
+                      const float* alibi_slopes, void* out,
                       pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
                       const FusedQuantAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq, true);
@@ -919,6 +939,8 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     if (!(scale > 0.f) || !std::isfinite(scale))
         return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
+    if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
+        return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0) return PA_OK;
     if (!q || !k_cache || !v_cache || !k_scale || !v_scale || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "decode_quant: a pointer argument is NULL");
@@ -988,6 +1010,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;
     a.window = window;
+    a.alibi = alibi_slopes;
     if (fa) {
         a.k_new = fa->k_new;
         a.v_new = fa->v_new;
@@ -1012,10 +1035,11 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
                                const void* k_cache, const void* v_cache, const float* k_scale,
                                const float* v_scale, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
-                               const int32_t* context_lens, float scale, int32_t window, void* out,
+                               const int32_t* context_lens, float scale, int32_t window,
+                               const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
-                             max_blocks_per_seq, context_lens, scale, window, out, out_dtype, workspace,
+                             max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out, out_dtype, workspace,
                              workspace_bytes, stream, nullptr);
 }
 
@@ -1023,12 +1047,13 @@ int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const vo
                                       const int64_t* slot_mapping, int32_t batch, int32_t n_q, void* k_cache,
                                       void* v_cache, float* k_scale, float* v_scale, const pa_cache_desc* cache,
                                       const int32_t* block_table, int32_t max_blocks_per_seq,
-                                      const int32_t* context_lens, float scale, int32_t window, void* out,
+                                      const int32_t* context_lens, float scale, int32_t window,
+                                      const float* alibi_slopes, void* out,
                                       pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream) {
     const FusedQuantAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale};
     return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
-                             max_blocks_per_seq, context_lens, scale, window, out, out_dtype, workspace,
+                             max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out, out_dtype, workspace,
                              workspace_bytes, stream, &fa);
 }
 

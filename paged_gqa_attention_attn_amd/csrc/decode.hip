@@ -46,6 +46,7 @@ namespace {
 
 constexpr int BS = 16;         // tokens per cache block
 constexpr float TAU = 8.0f;    // rescale threshold (log2 units): p <= 2^TAU between rescales
+constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_WAVES = 8;   // waves per workgroup
 constexpr int MIN_WAVES_PER_SIMD = 3;  // register budget: at most 168 VGPRs per lane
 
@@ -141,6 +142,13 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
             my_phys = p.block_table[(int64_t)b * p.max_blocks + wb0 + lane];
     }
     const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
+    // ALiBi: each head's slope in log2 units; with it, scores are formed in log2
+    // units before the max (c2 = 1), else scaled inside it.
+    const bool alibi = p.alibi != nullptr;   // uniform
+    float al2[GW];
+#pragma unroll
+    for (int hh = 0; hh < GW; ++hh) al2[hh] = alibi ? p.alibi[h0 + hh] * LOG2E : 0.f;
+    const float c2 = alibi ? 1.f : p.scale_log2;
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
     const bool slot_ok = new_slot >= 0 && new_slot < (int64_t)p.num_blocks * BS;
@@ -231,6 +239,14 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                     s[hh][t] = group_sum<LPT>(d);   // raw q.k; scaled inside exp2 below
                 }
             }
+            if (alibi) {   // - m_h log2(e) (ctx - 1 - pos) for the key at pos
+#pragma unroll
+                for (int t = 0; t < NT; ++t) {
+                    const float dist = (float)(pos0 + slot + t * TPP - (ctx - 1));
+#pragma unroll
+                    for (int hh = 0; hh < GW; ++hh) s[hh][t] = fmaf(s[hh][t], p.scale_log2, al2[hh] * dist);
+                }
+            }
             // Last block: positions >= ctx hold unrelated bytes. First block under a
             // window: positions before `first` are outside it.
             if (pos0 + BS > ctx || pos0 < first) {
@@ -258,7 +274,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                 float bm = s[hh][0];
 #pragma unroll
                 for (int t = 1; t < NT; ++t) bm = fmaxf(bm, s[hh][t]);
-                bm *= p.scale_log2;   // scale > 0, so scaling commutes with the max
+                bm *= c2;   // c2 > 0, so scaling commutes with the max
                 // The running max moves only when some score in the wave passes it by
                 // more than TAU (log2 units); the wave-wide max is taken only then.
                 if (__any(bm > m_run[hh] + TAU)) {
@@ -271,7 +287,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
                 }
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
-                    const float pr = __builtin_amdgcn_exp2f(fmaf(s[hh][t], p.scale_log2, -m_run[hh]));
+                    const float pr = __builtin_amdgcn_exp2f(fmaf(s[hh][t], c2, -m_run[hh]));
                     l_run[hh] += pr;
 #pragma unroll
                     for (int e = 0; e < EPL; ++e) acc[hh][e] = fmaf(pr, vf[t][e], acc[hh][e]);

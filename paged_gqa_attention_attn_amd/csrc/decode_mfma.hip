@@ -59,6 +59,7 @@ constexpr int BS = 16;          // tokens per cache block
 constexpr float TAU = 8.0f;     // rescale threshold (log2 units)
 constexpr int MAX_WAVES = 8;    // waves per workgroup
 constexpr float M_FLOOR = -1e30f; // running-max start (finite)
+constexpr float LOG2E = 1.4426950408889634f;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
@@ -168,6 +169,11 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
     // This column's row sees positions col_lo .. col_hi (causal among the new rows).
     const int col_hi = ctx - NR + v_col / G;
     const int col_lo = p.window > 0 ? col_hi - p.window + 1 : 0;
+    // ALiBi: the column's head slope in log2 units; with it, scores are formed in
+    // log2 units before the max (c2 = 1), else scaled inside it.
+    const bool alibi = p.alibi != nullptr;   // uniform
+    const float al2 = alibi ? p.alibi[(int64_t)g * G + v_col % G] * LOG2E : 0.f;
+    const float c2 = alibi ? 1.f : p.scale_log2;
     const int fb = first / BS;
     const int bpp = p.waves_tok * p.blocks_per_wave;
     const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
@@ -296,6 +302,11 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
             f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) s = Mfma16<E>::qk(ka[kk], qreg[kk], s);
+            if (alibi) {   // s = q.k scale log2(e) - m_h log2(e) (i - j), key j = pos0 + 4 grp + j'
+                const float b0 = al2 * (float)(pos0 + 4 * grp - col_hi);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[j] = fmaf(s[j], p.scale_log2, fmaf(al2, (float)j, b0));
+            }
             if (edge) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
@@ -303,7 +314,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
                     s[j] = (pos > col_hi || pos < col_lo) ? -INFINITY : s[j];
                 }
             }
-            float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * p.scale_log2;   // scale > 0
+            float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * c2;   // c2 > 0
             // The running max moves only when some score passes it by more than TAU;
             // the column max over the four 16-lane groups is taken only then.
             if (__any(bm > m_run + TAU)) {
@@ -317,7 +328,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
             float pr[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                pr[j] = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -m_run));
+                pr[j] = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -m_run));
                 l_run += pr[j];
             }
             // P^T operand: keys 4 grp .. +4 of column col, exactly where S^T put them.

@@ -43,6 +43,7 @@ constexpr int BN = 32;            // keys per tile: two cache blocks
 constexpr int WAVES = 4;          // waves per workgroup, each streaming its own run of blocks
 constexpr int RING = 2;           // tiles in flight per wave
 constexpr float TAU = 8.0f;       // rescale threshold (log2 units)
+constexpr float LOG2E = 1.4426950408889634f;
 constexpr float M_FLOOR = -1e30f; // running-max start: finite, so 2^(s - m) of a masked s is 0
 
 template <int D> struct MTile {
@@ -166,7 +167,11 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16_t{};
     float m_run = M_FLOOR;
     float l_run = 0.f;
-    const float c2 = p.scale_log2;
+    // ALiBi: this row's head slope in log2 units; with it, scores are formed in log2
+    // units before the max (c2 = 1), else scaled inside it.
+    const bool alibi = p.alibi != nullptr;   // uniform
+    const float al2 = alibi ? p.alibi[(int64_t)g * G + jh] * LOG2E : 0.f;
+    const float c2 = alibi ? 1.f : p.scale_log2;
     const int ksw = T::swz(l32);
     const int g16 = lane >> 4, r16 = lane & 15;
     const int vkey = 4 * half + r16 / 4;               // + 16 jg + 8 tt
@@ -193,6 +198,12 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
             for (int kk = 0; kk < KK; ++kk) {
                 const uint4 a = *reinterpret_cast<const uint4*>(krow + ((2 * kk + half) ^ ksw) * 16);
                 sc = Mfma<E>::run(u32x4_t{a.x, a.y, a.z, a.w}, qreg[kk], sc);
+            }
+            if (alibi) {   // - m_h log2(e) (my_pos - key)
+                const float b0 = al2 * (float)(key0 + half * 4 - my_pos);
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    sc[i] = fmaf(sc[i], p.scale_log2, fmaf(al2, (float)((i / 4) * 8 + (i % 4)), b0));
             }
             // Mask keys past the run, past this row's position or before its window.
             if (key0 + BN > wave_end || key0 + BN - 1 > ctx - R || key0 < lo_max) {   // uniform

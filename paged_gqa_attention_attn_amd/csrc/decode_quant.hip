@@ -42,6 +42,7 @@ namespace {
 
 constexpr int BS = 16;
 constexpr float TAU = 8.0f;
+constexpr float LOG2E = 1.4426950408889634f;
 constexpr int MAX_WAVES = 8;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -174,6 +175,11 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             my_phys = p.block_table[(int64_t)b * p.max_blocks + wb0 + lane];
     }
     const int nb = max(0, min(nblk - wb0, p.blocks_per_wave));
+    // ALiBi: the column's head slope in log2 units; with it, scores are formed in
+    // log2 units before the max (c2 = 1), else scaled inside it.
+    const bool alibi = p.alibi != nullptr;   // uniform
+    const float al2 = alibi ? p.alibi[h0 + (col < HW ? col : 0)] * LOG2E : 0.f;
+    const float c2 = alibi ? 1.f : p.scale_log2;
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
     // Fused append: the wave whose run holds position ctx - 1 patches the new
@@ -320,6 +326,11 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             s[1] *= ks.y;
             s[2] *= ks.z;
             s[3] *= ks.w;
+            if (alibi) {   // - m_h log2(e) (ctx - 1 - j) for key j = pos0 + 4 grp + j'
+                const float b0 = al2 * (float)(pos0 + 4 * grp - (ctx - 1));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) s[j] = fmaf(s[j], p.scale_log2, fmaf(al2, (float)j, b0));
+            }
             bool live[4] = {true, true, true, true};
             if (edge) {
 #pragma unroll
@@ -329,7 +340,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                     s[j] = live[j] ? s[j] : -INFINITY;
                 }
             }
-            float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * p.scale_log2;
+            float bm = fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])) * c2;
             if (__any(bm > m_run + TAU)) {
                 const float m_new = fmaxf(m_run, stride_reduce<16, true>(bm));
                 const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
@@ -342,7 +353,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             float pr[4];
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], p.scale_log2, -m_run));
+                const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -m_run));
                 l_run += pj;
                 pr[j] = live[j] ? pj * vsc[j] : 0.f;   // V scale folded into P
             }

@@ -45,6 +45,9 @@ struct DecodeArgs {
     // Sliding window: 0 attends to the whole context; W > 0 lets the query at
     // position p see positions max(0, p - W + 1) .. p only.
     int32_t window;
+    // ALiBi: slope m_h per query head [n_q] (nullptr: none); the score of key
+    // position j for the query at position i gets -m_h (i - j).
+    const float* alibi;
     // Single-row decode on the matrix cores (decode_mfma.hip): gw query heads
     // (4, 8 or 16) per workgroup fill the MFMA columns; hs_wg must be 1.
     int32_t mfma;
@@ -94,6 +97,7 @@ struct PrefillArgs {
     const int32_t* context_lens;  // [B]
     int32_t max_blocks, num_blocks;
     int32_t window;   // sliding window (causal only); 0: none
+    const float* alibi;   // ALiBi slopes [n_q] (causal only); nullptr: none
     // Contiguous bf16 keys only: an f16 copy of v in v's layout, written by the
     // staging kernel, and one byte per (sequence, KV head, 64-key tile) that is 1
     // where the copy is exact. nullptr: P V stays in bf16 (hi + lo parts).

@@ -56,6 +56,7 @@ constexpr int BN = 64;    // keys per tile
 constexpr int WM = 32;    // query rows per wave
 constexpr int NWAVES = BM / WM;
 constexpr float TAU = 8.0f;        // rescale threshold (log2 units)
+constexpr float LOG2E = 1.4426950408889634f;
 constexpr float M_FLOOR = -1e30f;  // running-max start: finite, so 2^(s - m) of a masked s is 0
 
 template <int D> struct Tile {
@@ -232,7 +233,11 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16_t{};
     float m_run = M_FLOOR;     // running max (log2 units) of this lane's query
     float l_run = 0.f;         // this lane's share of the softmax denominator
-    const float c2 = p.scale_log2;
+    // ALiBi: the head's slope in log2 units; with it, scores are formed in log2
+    // units before the max (c2 = 1), else scaled inside it.
+    const bool alibi = p.alibi != nullptr;   // uniform
+    const float al2 = alibi ? p.alibi[h] * LOG2E : 0.f;
+    const float c2 = alibi ? 1.f : p.scale_log2;
 
     // Lane-constant parts of the operand addresses (the swizzle of a row depends on
     // its index mod 16 only, so key 32 st + 16 jg + 8 t + vkey shares it with 8 t + vkey).
@@ -277,6 +282,15 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
             }
 
+            if (alibi) {   // - m_h log2(e) (my_pos - key), key = key0 + 32 st + 8 (i / 4) + 4 half + i % 4
+                const float b0 = al2 * (float)(key0 + 4 * half - my_pos);
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int i = 0; i < 16; ++i)
+                        sc[st][i] = fmaf(sc[st][i], p.scale_log2,
+                                         fmaf(al2, (float)(32 * st + (i / 4) * 8 + (i % 4)), b0));
+            }
             // Mask keys past this lane's query (causal), past the prompt, or before
             // this lane's window.
             if (key0 + BN > ctx || (p.causal && key0 + BN - 1 > pos0) || (W > 0 && key0 < wave_lo_max)) {   // uniform

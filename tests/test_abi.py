@@ -44,15 +44,15 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 202
+    assert L.pa_version() == 203
 
 
 def decode(L, **kw):
     a = dict(q=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+             scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode(a["q"], a["batch"], a["n_q"], a["k"], a["v"], a["cache"],
-                                  a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
+                                  a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["alibi"], a["out"],
                                   a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -76,6 +76,7 @@ def decode(L, **kw):
     (dict(window=-1), INVALID, "window"),
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),   # too small (NULL: library's own)
     (dict(maxb=8192, window=4096, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_decode_rejects(L, kw, code, msg):
     assert decode(L, **kw) == code
@@ -88,12 +89,12 @@ def test_decode_empty_batch_is_a_noop(L):
 
 def decode_append(L, **kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE, cache=desc(),
-             bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32,
+             bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32,
              ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode_append(a["q"], a["kn"], a["vn"], a["slots"], a["batch"],
                                          a["n_q"], a["k"], a["v"], a["cache"], a["bt"], a["maxb"],
-                                         a["ctx"], a["scale"], a["window"], a["out"], a["out_dtype"], a["ws"],
+                                         a["ctx"], a["scale"], a["window"], a["alibi"], a["out"], a["out_dtype"], a["ws"],
                                          a["ws_bytes"], a["stream"])
 
 
@@ -105,6 +106,7 @@ def decode_append(L, **kw):
     (dict(cache=desc(bs=32)), UNSUPPORTED, "block_size"),
     (dict(n_q=5), INVALID, "multiple"),
     (dict(window=-3), INVALID, "window"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_decode_append_rejects(L, kw, code, msg):
     assert decode_append(L, **kw) == code
@@ -174,11 +176,11 @@ def test_append_zero_tokens_is_a_noop(L):
 
 def prefill(L, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, dtype=_lib.PA_BF16, B=1, S=64, n_q=8, n_kv=2, d=128,
-             causal=1, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0,
+             causal=1, scale=0.1, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0,
              stream=None)
     a.update(kw)
     return L.pa_paged_attn_prefill(a["q"], a["k"], a["v"], a["dtype"], a["B"], a["S"], a["n_q"],
-                                   a["n_kv"], a["d"], a["causal"], a["scale"], a["window"], a["out"],
+                                   a["n_kv"], a["d"], a["causal"], a["scale"], a["window"], a["alibi"], a["out"],
                                    a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -195,6 +197,8 @@ def prefill(L, **kw):
     (dict(scale=-1.0), INVALID),
     (dict(window=-1), INVALID),
     (dict(window=8, causal=0), INVALID),    # a window is a causal band
+    (dict(alibi=FAKE + 2), INVALID),
+    (dict(alibi=FAKE, causal=0), INVALID),  # the bias is defined for causal attention
 ])
 def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
@@ -226,11 +230,11 @@ def test_prefill_empty_is_a_noop(L):
 
 def chunked(L, **kw):
     a = dict(q=FAKE, B=2, C=16, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+             scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
     a.update(kw)
     return L.pa_paged_attn_chunked_prefill(a["q"], a["B"], a["C"], a["n_q"], a["k"], a["v"],
                                            a["cache"], a["bt"], a["maxb"], a["ctx"], a["scale"],
-                                           a["window"], a["out"], a["out_dtype"], a["stream"])
+                                           a["window"], a["alibi"], a["out"], a["out_dtype"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -245,6 +249,7 @@ def chunked(L, **kw):
     (dict(ctx=FAKE + 2), INVALID, "aligned"),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
     (dict(window=-1), INVALID, "window"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_chunked_prefill_rejects(L, kw, code, msg):
     assert chunked(L, **kw) == code
@@ -258,10 +263,10 @@ def test_chunked_prefill_empty_is_a_noop(L):
 
 def multi(L, **kw):
     a = dict(q=FAKE, B=2, R=4, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+             scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode_multi(a["q"], a["B"], a["R"], a["n_q"], a["k"], a["v"], a["cache"],
-                                        a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
+                                        a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["alibi"], a["out"],
                                         a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
 
 
@@ -276,6 +281,7 @@ def multi(L, **kw):
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
     (dict(maxb=8192, window=4096, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
     (dict(window=-1), INVALID, "window"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_decode_multi_rejects(L, kw, code, msg):
     assert multi(L, **kw) == code
@@ -309,12 +315,12 @@ FP8, INT8 = _lib.PA_FP8_E4M3, _lib.PA_INT8
 
 def decode_quant(L, **kw):
     a = dict(q=FAKE, q_dtype=_lib.PA_BF16, batch=2, n_q=8, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
-             cache=desc(dtype=FP8), bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, out=FAKE,
+             cache=desc(dtype=FP8), bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, alibi=None, out=FAKE,
              out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
     a.update(kw)
     return L.pa_paged_attn_decode_quant(a["q"], a["q_dtype"], a["batch"], a["n_q"], a["k"], a["v"],
                                         a["ks"], a["vs"], a["cache"], a["bt"], a["maxb"], a["ctx"],
-                                        a["scale"], a["window"], a["out"], a["out_dtype"], a["ws"],
+                                        a["scale"], a["window"], a["alibi"], a["out"], a["out_dtype"], a["ws"],
                                         a["ws_bytes"], a["stream"])
 
 
@@ -328,6 +334,7 @@ def decode_quant(L, **kw):
     (dict(n_q=7), INVALID, "multiple"),
     (dict(scale=0.0), INVALID, "positive"),
     (dict(window=-2), INVALID, "window"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_decode_quant_rejects(L, kw, code, msg):
     assert decode_quant(L, **kw) == code
@@ -337,11 +344,11 @@ def test_decode_quant_rejects(L, kw, code, msg):
 def decode_quant_append(L, **kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, q_dtype=_lib.PA_BF16, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE,
              ks=FAKE, vs=FAKE, cache=_lib.CacheDesc(64, 16, 2, 128, _lib.PA_FP8_E4M3), bt=FAKE, maxb=4,
-             ctx=FAKE, scale=0.1, window=0, out=FAKE, out_dtype=_lib.PA_F32, ws=FAKE, ws_bytes=1 << 20)
+             ctx=FAKE, scale=0.1, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=FAKE, ws_bytes=1 << 20)
     a.update(kw)
     return L.pa_paged_attn_decode_quant_append(
         a["q"], a["kn"], a["vn"], a["q_dtype"], a["slots"], a["batch"], a["n_q"], a["k"], a["v"], a["ks"],
-        a["vs"], ctypes.byref(a["cache"]), a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["out"],
+        a["vs"], ctypes.byref(a["cache"]), a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["alibi"], a["out"],
         a["out_dtype"], a["ws"], a["ws_bytes"], None)
 
 
@@ -353,6 +360,7 @@ def decode_quant_append(L, **kw):
     (dict(cache=_lib.CacheDesc(64, 16, 2, 128, _lib.PA_BF16)), INVALID, "PA_FP8_E4M3"),
     (dict(q_dtype=_lib.PA_F32), UNSUPPORTED, "bf16 or f16"),
     (dict(window=-1), INVALID, "window"),
+    (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
 def test_decode_quant_append_rejects(L, kw, code, msg):
     assert decode_quant_append(L, **kw) == code

@@ -54,7 +54,7 @@ def _raw_decode(case, bt, ctx, out, ws, ws_bytes):
     return L.pa_paged_attn_decode(
         case.q.data_ptr(), case.batch, case.n_q, case.k_pool.data_ptr(), case.v_pool.data_ptr(),
         ctypes.byref(desc), bt.data_ptr(), case.max_blocks_per_seq, ctx.data_ptr(), case.scale,
-        0, out.data_ptr(), _lib.PA_F32, ws, ws_bytes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+        0, None, out.data_ptr(), _lib.PA_F32, ws, ws_bytes, ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
 
 
 def test_null_workspace_uses_the_librarys_own(pa):
