@@ -55,9 +55,39 @@ CSRC = ROOT / "paged_gqa_attention_attn_amd" / "csrc"
 KERNEL_SOURCES = {
     "decode": ["decode.hip", "decode_mfma.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "prefill": ["prefill.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
-    "decode_multi": ["decode_multi.hip", "decode.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
+    "decode_multi": ["decode_multi.hip", "decode.hip", "decode_mfma.hip", "mfma.h", "common.h", "launch.h", "api.hip"],
     "decode_quant": ["decode_quant.hip", "decode.hip", "quant.h", "mfma.h", "common.h", "launch.h", "api.hip"],
 }
+
+
+_SPIN_CYCLES_PER_US = None
+
+
+def time_launches(launch, n: int) -> float:
+    """Average duration in ms of ``launch(i)`` for i < n, run back to back on the current
+    stream between two events. A spin kernel enqueued first keeps the GPU busy while the
+    host enqueues the n launches, so the events see the launches themselves and not the
+    host's enqueue latency."""
+    import torch
+    global _SPIN_CYCLES_PER_US
+    stream = torch.cuda.current_stream()
+    if _SPIN_CYCLES_PER_US is None:      # the spin's counter rate, measured once
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        torch.cuda._sleep(1_000_000)
+        b.record(stream)
+        torch.cuda.synchronize()
+        _SPIN_CYCLES_PER_US = 1_000_000 / max(a.elapsed_time(b) * 1e3, 1.0)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    torch.cuda._sleep(int((2000 + 200 * n) * _SPIN_CYCLES_PER_US))   # 200 us of host time per launch
+    e0.record(stream)
+    for i in range(n):
+        launch(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def source_hash(kind: str) -> str:
@@ -90,6 +120,8 @@ def parse_args(argv=None):
                    help="target CPU time of the oracle baseline sample (0 disables it)")
     p.add_argument("--partition-tokens", type=int, default=0,
                    help="decode partition size override (0: library default)")
+    p.add_argument("--alibi", action="store_true",
+                   help="decode and prefill workloads: add the ALiBi bias with geometric slopes")
     p.add_argument("--unfused", action="store_true",
                    help="decode step as two launches (kv_append, then decode) instead of one")
     return p.parse_args(argv)
@@ -102,7 +134,7 @@ def _stored(t):
     return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
 
 
-def cpu_baseline_decode(case, target_s: float, window: int = 0):
+def cpu_baseline_decode(case, target_s: float, window: int = 0, alibi=None):
     """Time the CPU oracle on whole sequences of one input set (all heads)."""
     import numpy as np
 
@@ -118,7 +150,8 @@ def cpu_baseline_decode(case, target_s: float, window: int = 0):
     def run(seqs):
         sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
         t0 = time.perf_counter()
-        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel, window=window)
+        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel, window=window,
+                      alibi=alibi)
         return time.perf_counter() - t0
 
     t1 = run([0])
@@ -136,7 +169,7 @@ def cpu_baseline_decode(case, target_s: float, window: int = 0):
     }
 
 
-def cpu_baseline_prefill(case, target_s: float):
+def cpu_baseline_prefill(case, target_s: float, alibi=None):
     """Time the CPU oracle on sampled causal prefill rows, scaled to TFLOP/s."""
     import numpy as np
 
@@ -149,7 +182,7 @@ def cpu_baseline_prefill(case, target_s: float):
         rows = np.stack([rng.integers(0, case.batch, n), rng.integers(0, case.n_q, n),
                          rng.integers(0, case.seq_len, n)], axis=1).astype(np.int32)
         t0 = time.perf_counter()
-        oracle.prefill(q, k, v, case.dtype, True, case.scale, sel=rows)
+        oracle.prefill(q, k, v, case.dtype, True, case.scale, sel=rows, alibi=alibi)
         dt = time.perf_counter() - t0
         flops = float(4 * case.head_dim * (rows[:, 2].astype(np.int64) + 1).sum())
         return dt, flops
@@ -188,6 +221,7 @@ def bench_decode(args, cfg: int):
     ws_bytes = max(pa.decode_workspace_bytes(s.batch, s.n_q, s.max_blocks_per_seq, s.k_pool)
                    for s in sets)
     ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device="cuda")
+    slopes = wl.geometric_alibi_slopes(c0.n_q, "cuda") if args.alibi else None
 
     def step(i):
         s = sets[i % len(sets)]
@@ -198,11 +232,11 @@ def bench_decode(args, cfg: int):
     def decode(s):
         if args.unfused:
             pa.paged_attn_decode(s.q, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
-                                 out=out, workspace=ws, window=win)
+                                 out=out, workspace=ws, window=win, alibi_slopes=slopes)
         else:
             pa.paged_attn_decode_append(s.q, s.new_k, s.new_v, s.slot_mapping, s.k_pool, s.v_pool,
                                         s.block_table, s.context_lens, s.scale, out=out,
-                                        workspace=ws, window=win)
+                                        workspace=ws, window=win, alibi_slopes=slopes)
 
     for i in range(args.warmup):
         step(i)
@@ -217,14 +251,7 @@ def bench_decode(args, cfg: int):
     # The decode launches alone, back to back, between two events on the launch
     # stream: elapsed / steps is the average duration of one decode launch.
     stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        decode(sets[i % len(sets)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / args.steps
+    dec_ms = time_launches(lambda i: decode(sets[i % len(sets)]), args.steps)
 
     # Per-launch spread: an event pair around each decode launch (each pair adds
     # its own overhead, so these sit above the back-to-back average).
@@ -264,7 +291,7 @@ def bench_decode(args, cfg: int):
             ("32768 each" if cfg == 4 else ("U[128,8192], 16 sharers of a 1024-token prefix"
                                             if cfg == 3 else
                                             ("16384 each" if cfg == 8 else "{7, 33}"))),
-            "window": win,
+            "window": win, "alibi": "geometric slopes" if args.alibi else None,
             "kv_bytes_per_step": int(kv), "input_sets_rotated": len(sets),
             "step": ("kv_append of one new token per sequence, then paged decode (two launches)"
                      if args.unfused else
@@ -291,7 +318,8 @@ def bench_decode(args, cfg: int):
     flops = acc.decode_flops(c0.context_lens.cpu().tolist(), c0.n_q, c0.head_dim, win)
     rec["tflops"] = round(flops / (dec_ms * 1e-3) / 1e12, 3)
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline_decode(c0, args.cpu_seconds, win)
+        rec["cpu_baseline"] = cpu_baseline_decode(c0, args.cpu_seconds, win,
+                                                  slopes.cpu().numpy() if args.alibi else None)
     return rec
 
 
@@ -315,8 +343,11 @@ def bench_prefill(args):
     pws_bytes = pa.prefill_workspace_bytes(c0.q.dtype, c0.batch, c0.seq_len, c0.n_kv, c0.head_dim)
     pws = torch.empty(max(pws_bytes, 16), dtype=torch.uint8, device="cuda")
 
+    slopes = wl.geometric_alibi_slopes(c0.n_q, "cuda") if args.alibi else None
+
     def prefill(s):
-        pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out, workspace=pws)
+        pa.paged_attn_prefill(s.q, s.k, s.v, True, s.scale, out=out, workspace=pws,
+                              alibi_slopes=slopes)
 
     def step(i):
         s = sets[i % n_sets]
@@ -324,7 +355,7 @@ def bench_prefill(args):
         pa.kv_append(kf[i % n_sets], vf[i % n_sets], s.prompt_slots, s.k_pool, s.v_pool)
         pa.kv_append(s.new_k, s.new_v, s.new_slots, s.k_pool, s.v_pool)
         pa.paged_attn_decode(s.q_new, s.k_pool, s.v_pool, s.block_table, s.context_lens, s.scale,
-                             out=dout, workspace=ws)
+                             out=dout, workspace=ws, alibi_slopes=slopes)
 
     for i in range(args.warmup):
         step(i)
@@ -335,14 +366,7 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
     # The prefill launches alone, back to back, between two events on the launch stream.
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        prefill(sets[i % n_sets])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    pre_ms = e0.elapsed_time(e1) / args.steps
+    pre_ms = time_launches(lambda i: prefill(sets[i % n_sets]), args.steps)
     flops = acc.prefill_flops_causal(c0.batch, c0.seq_len, c0.n_q, c0.head_dim)
     achieved = flops / (pre_ms * 1e-3) / 1e12
     rec = {
@@ -356,6 +380,7 @@ def bench_prefill(args):
         "config": {
             "workload": c0.name, "batch": c0.batch, "seq_len": c0.seq_len, "n_q": c0.n_q,
             "n_kv": c0.n_kv, "head_dim": c0.head_dim, "causal": True,
+            "alibi": "geometric slopes" if args.alibi else None,
             "causal_flops": flops,
             "full_square_flops": acc.prefill_flops_full_square(c0.batch, c0.seq_len, c0.n_q,
                                                               c0.head_dim),
@@ -376,7 +401,8 @@ def bench_prefill(args):
         },
     }
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline_prefill(c0, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline_prefill(c0, args.cpu_seconds,
+                                                   slopes.cpu().numpy() if args.alibi else None)
     return rec
 
 
@@ -431,14 +457,7 @@ def bench_chunked_prefill(args):
         step(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        prefill(sets[i % n_sets])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    pre_ms = e0.elapsed_time(e1) / args.steps
+    pre_ms = time_launches(lambda i: prefill(sets[i % n_sets]), args.steps)
     flops = acc.chunked_prefill_flops(c0.context_lens.cpu().tolist(), C, c0.n_q, c0.head_dim)
     achieved = flops / (pre_ms * 1e-3) / 1e12
     return {
@@ -494,14 +513,7 @@ def bench_decode_multi(args):
         step(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(args.steps):
-        decode(sets[i % len(sets)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / args.steps
+    dec_ms = time_launches(lambda i: decode(sets[i % len(sets)]), args.steps)
     kv = acc.decode_kv_bytes([ctx] * B, c0.n_kv, c0.head_dim, 2)
     io = acc.decode_io_bytes(B * R, c0.n_q, c0.head_dim, 2, 4, c0.max_blocks_per_seq)
     achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
@@ -600,15 +612,7 @@ def bench_decode_quant(args, fmt: str):
         step(i)
     torch.cuda.synchronize()
     ms = (time.perf_counter() - t0) * 1e3 / args.steps
-    stream = torch.cuda.current_stream()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for i in range(args.steps):
-        decode(sets[i % len(sets)])
-    e1.record(stream)
-    torch.cuda.synchronize()
-    dec_ms = e0.elapsed_time(e1) / args.steps
+    dec_ms = time_launches(lambda i: decode(sets[i % len(sets)]), args.steps)
     kv = acc.quant_decode_kv_bytes([ctx] * B, c0.n_kv, c0.head_dim)
     io = acc.decode_io_bytes(B, c0.n_q, c0.head_dim, 2, 4, c0.max_blocks_per_seq)
     achieved = (kv + io) / (dec_ms * 1e-3) / 1e9

@@ -233,11 +233,13 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     for (int mt = 0; mt < MT; ++mt) o[mt] = f32x16_t{};
     float m_run = M_FLOOR;     // running max (log2 units) of this lane's query
     float l_run = 0.f;         // this lane's share of the softmax denominator
-    // ALiBi: the head's slope in log2 units; with it, scores are formed in log2
-    // units before the max (c2 = 1), else scaled inside it.
+    // ALiBi: the bias -m_h (i - j) is a (j - i) in unscaled score units, a = m_h / scale.
+    // For the element at offset c of a lane's tile, j - i = (key0 + 4 half - my_pos) + c:
+    // the part a c (c a compile-time constant) is one multiply-add per score, and the
+    // lane's part a (key0 + 4 half - my_pos) shifts its tile max and exponent instead.
     const bool alibi = p.alibi != nullptr;   // uniform
-    const float al2 = alibi ? p.alibi[h] * LOG2E : 0.f;
-    const float c2 = alibi ? 1.f : p.scale_log2;
+    const float a_sl = alibi ? p.alibi[h] * LOG2E / p.scale_log2 : 0.f;
+    const float c2 = p.scale_log2;
 
     // Lane-constant parts of the operand addresses (the swizzle of a row depends on
     // its index mod 16 only, so key 32 st + 16 jg + 8 t + vkey shares it with 8 t + vkey).
@@ -282,14 +284,14 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
             }
 
-            if (alibi) {   // - m_h log2(e) (my_pos - key), key = key0 + 32 st + 8 (i / 4) + 4 half + i % 4
-                const float b0 = al2 * (float)(key0 + 4 * half - my_pos);
+            float lane_bias = 0.f;   // ALiBi bias shared by the lane's scores (unscaled units)
+            if (alibi) {   // key = key0 + 32 st + 8 (i / 4) + 4 half + i % 4
+                lane_bias = a_sl * (float)(key0 + 4 * half - my_pos);
 #pragma unroll
                 for (int st = 0; st < 2; ++st)
 #pragma unroll
                     for (int i = 0; i < 16; ++i)
-                        sc[st][i] = fmaf(sc[st][i], p.scale_log2,
-                                         fmaf(al2, (float)(32 * st + (i / 4) * 8 + (i % 4)), b0));
+                        sc[st][i] = fmaf(a_sl, (float)(32 * st + (i / 4) * 8 + (i % 4)), sc[st][i]);
             }
             // Mask keys past this lane's query (causal), past the prompt, or before
             // this lane's window.
@@ -311,7 +313,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 for (int i = 0; i < 16; ++i) tmax = fmaxf(tmax, sc[st][i]);
             {
                 float a2, b2;
-                pair32(tmax, a2, b2);
+                pair32(tmax + lane_bias, a2, b2);
                 tmax = fmaxf(a2, b2) * c2;   // scale > 0, so scaling commutes with the max
             }
             if (__any(tmax > m_run + TAU)) {
@@ -323,7 +325,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
             }
 
-            // P = 2^(s scale - m) in the element type (bf16: hi + lo parts).
+            // P = 2^((s + lane_bias) scale - m) in the element type (bf16: hi + lo parts).
+            const float nm = fmaf(lane_bias, c2, -m_run);
             u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
             float lsum = 0.f;
 #pragma unroll
@@ -333,8 +336,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                     uint32_t hw[4], lw[4];
 #pragma unroll
                     for (int w = 0; w < 4; ++w) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, -m_run));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, -m_run));
+                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, nm));
+                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, nm));
                         hw[w] = Mfma<PE>::pack(p0, p1);
                         if constexpr (Mfma<PE>::kSplit) {
                             lw[w] = Mfma<PE>::pack(p0 - Mfma<PE>::lo_of(hw[w]), p1 - Mfma<PE>::hi_of(hw[w]));

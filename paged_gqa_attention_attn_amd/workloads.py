@@ -115,6 +115,14 @@ def _randn(shape, dtype: str, gen: torch.Generator, device) -> torch.Tensor:
     return x.to(TORCH_DTYPES[dtype])
 
 
+def geometric_alibi_slopes(n_q: int, device="cpu") -> torch.Tensor:
+    """Per-query-head ALiBi slopes m_h = 2^(-8 (h+1) / n_q), float32 [n_q]: the family the
+    ALiBi paper uses (Press et al., ICLR 2022, cited by "LLM 推理全过程的维度变化与核心公式").
+    They are model constants that the attention calls take as an input."""
+    h = torch.arange(1, n_q + 1, dtype=torch.float64)
+    return (2.0 ** (-8.0 * h / n_q)).to(torch.float32).to(device)
+
+
 def make_decode_case(*, batch: int, n_q: int, n_kv: int, head_dim: int, context_lens,
                      dtype: str = "bf16", block_size: int = 16, free_fraction: float = 0.0,
                      num_blocks: int | None = None, max_blocks_per_seq: int | None = None,
