@@ -207,7 +207,9 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *         finite value keep the bf16 product for the rows that read them.
  *         PA_PREFILL_STAGE_V=0 in the environment turns the staging off.
  *         Calls that share a workspace must not overlap on the GPU.
- * Supported: head_dim 128 (and 64); dtype bf16 or f16.
+ * Supported: head_dim 128 (and 64); dtype bf16 or f16; seq_len at most
+ * 2^31 - 129 and ceil(seq_len / 128) * n_q * batch at most 2^31 - 1 (one
+ * workgroup per 128 query rows of one head), else PA_ERR_UNSUPPORTED.
  */
 size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len, int32_t n_kv,
                                   int32_t head_dim);
@@ -278,7 +280,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  * Rows at negative positions (context_lens[b] < chunk_len) are zero. A context
  * length past max_blocks_per_seq * block_size, or a block id outside the pool
  * among the ones the sequence's rows read, turns every row of that sequence into
- * NaN instead of an out-of-bounds read. Supported: head_dim 64 or 128.
+ * NaN instead of an out-of-bounds read. Supported: head_dim 64 or 128; the
+ * size limits of pa_paged_attn_prefill with chunk_len in place of seq_len.
  */
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,

@@ -210,7 +210,7 @@ size_t prefill_stage_v_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32
     return round16((size_t)batch * seq_len * n_kv * head_dim * 2);
 }
 size_t prefill_stage_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32_t head_dim) {
-    const size_t tiles = (size_t)batch * n_kv * ((seq_len + 63) / 64);
+    const size_t tiles = (size_t)batch * n_kv * (((size_t)seq_len + 63) / 64);
     return prefill_stage_v_bytes(batch, seq_len, n_kv, head_dim) + round16(tiles);
 }
 
@@ -678,6 +678,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (window > 0 && !causal) return fail(PA_ERR_INVALID_ARG, "a sliding window needs causal == 1");
     if (alibi_slopes && !causal) return fail(PA_ERR_INVALID_ARG, "ALiBi slopes need causal == 1");
     if (batch == 0 || seq_len == 0) return PA_OK;
+    if (!pa::prefill_grid_fits(seq_len, n_q, batch))
+        return fail(PA_ERR_UNSUPPORTED, "prefill: ceil(seq_len / 128) * n_q * batch exceeds one launch");
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(PA_ERR_INVALID_ARG, "prefill: q, k, v and out must be 16-byte aligned");
@@ -834,6 +836,8 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0 || chunk_len == 0) return PA_OK;
+    if (!pa::prefill_grid_fits(chunk_len, n_q, batch))
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill: ceil(chunk_len / 128) * n_q * batch exceeds one launch");
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))

@@ -105,6 +105,15 @@ struct PrefillArgs {
     uint8_t* v16_ok;
 };
 
+// Query rows per prefill workgroup. One launch has ceil(rows / 128) * n_q * batch
+// workgroups in a one-dimensional grid, so that count must fit in an int; rows stay
+// 128 below INT32_MAX so that the kernels' tile counts cannot overflow.
+constexpr int PREFILL_ROWS_PER_WG = 128;
+inline bool prefill_grid_fits(int rows, int n_q, int batch) {
+    return rows <= INT32_MAX - PREFILL_ROWS_PER_WG &&
+           ((int64_t)rows + PREFILL_ROWS_PER_WG - 1) / PREFILL_ROWS_PER_WG * n_q * batch <= INT32_MAX;
+}
+
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);
 
 }  // namespace pa

@@ -51,7 +51,7 @@ namespace pa {
 
 namespace {
 
-constexpr int BM = 128;   // query rows per workgroup
+constexpr int BM = PREFILL_ROWS_PER_WG;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int WM = 32;    // query rows per wave
 constexpr int NWAVES = BM / WM;
@@ -78,10 +78,22 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     constexpr bool kStage = std::is_same<E, BF16>::value && !PAGED;   // V may come staged as f16
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    const int nqt = (p.seq_len + BM - 1) / BM;
-    const int qt = p.causal ? nqt - 1 - (int)blockIdx.x : (int)blockIdx.x;  // heavy tiles first
-    const int h = blockIdx.y;
-    const int b = blockIdx.z;
+    // Work item of this workgroup: query tile qt of head h of sequence b. Workgroups go
+    // to the 8 XCDs in turn (XCD = id mod 8), so XCD k takes the k-th contiguous eighth
+    // of the items, ordered by (sequence, head), then query tile. Every XCD then gets
+    // whole heads, i.e. the same mix of causal tile costs, and the heads that share a
+    // KV head stay on one XCD's L2. Within a head the heaviest tiles (the last rows)
+    // go first. (Query tiles as the fastest grid index gave XCD k tiles 31-k, 23-k, ...
+    // of every head: 1.5x more causal work on XCD 0 than on XCD 7.)
+    const int nqt = p.seq_len / BM + (p.seq_len % BM != 0);
+    const int n_items = gridDim.x;
+    const int wg = blockIdx.x;
+    const int per_xcd = n_items / 8, extra = n_items % 8, xcd = wg % 8;
+    const int item = xcd * per_xcd + min(xcd, extra) + wg / 8;
+    const int hb = item / nqt, qr = item % nqt;
+    const int qt = p.causal ? nqt - 1 - qr : qr;
+    const int h = hb % p.n_q;
+    const int b = hb / p.n_q;
     const int g = h / p.group;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63;
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     bool use16 = false;
     if constexpr (kStage) {
         if (p.v16 != nullptr) {
-            const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * ((S_len + BN - 1) / BN);
+            const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * (S_len / BN + (S_len % BN != 0));
             bool fits = true;
             for (int j = j0 + lane; j < n_tiles; j += 64) fits = fits && ok[j] != 0;
             use16 = __all(fits);
@@ -460,13 +472,15 @@ template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs&
     if (opt_in != hipSuccess) return opt_in;
     if constexpr (std::is_same<E, BF16>::value && !PAGED) {
         if (a.v16 != nullptr) {
-            const dim3 sgrid((a.seq_len + BN - 1) / BN, a.n_kv, a.batch);
+            const dim3 sgrid(a.seq_len / BN + (a.seq_len % BN != 0), a.n_kv, a.batch);
             hipLaunchKernelGGL((stage_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }
     }
-    const dim3 grid((a.seq_len + BM - 1) / BM, a.n_q, a.batch);
+    const int64_t n_items = ((int64_t)a.seq_len + BM - 1) / BM * a.n_q * a.batch;
+    if (!prefill_grid_fits(a.seq_len, a.n_q, a.batch)) return hipErrorInvalidConfiguration;   // checked by the caller
+    const dim3 grid((unsigned)n_items);
     hipLaunchKernelGGL((prefill_kernel<E, D, PAGED>), grid, dim3(64 * NWAVES), lds, s, a);
     return hipGetLastError();
 }

@@ -199,6 +199,8 @@ def prefill(L, **kw):
     (dict(window=8, causal=0), INVALID),    # a window is a causal band
     (dict(alibi=FAKE + 2), INVALID),
     (dict(alibi=FAKE, causal=0), INVALID),  # the bias is defined for causal attention
+    (dict(S=2**31 - 1, n_q=64, n_kv=8, B=4), UNSUPPORTED),   # 2^32 workgroups in one grid
+    (dict(S=2**31 - 100), UNSUPPORTED),                       # rows too close to the int limit
 ])
 def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
@@ -250,6 +252,7 @@ def chunked(L, **kw):
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
     (dict(window=-1), INVALID, "window"),
     (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
+    (dict(C=2**31 - 1, n_q=64, cache=desc(n_kv=8), B=4), UNSUPPORTED, "exceeds one launch"),
 ])
 def test_chunked_prefill_rejects(L, kw, code, msg):
     assert chunked(L, **kw) == code
