@@ -49,6 +49,8 @@ SHAPES = [
     (2, 1, [50, 3], 8, 1, 128, "bf16"),
     (2, 300, [1000, 17], 16, 4, 128, "f16"),
     (1, 130, [64], 8, 2, 64, "bf16"),
+    (3, 150, [10, 400, 77], 6, 2, 128, "bf16"),   # 36 work items: not a multiple of 8 XCDs
+    (1, 257, [33], 3, 1, 64, "f16"),              # 9 work items
 ]
 
 

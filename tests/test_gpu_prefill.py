@@ -49,6 +49,10 @@ SHAPES = {
     "full_600": (1, 600, 8, 2, 128, "bf16", False),
     "d64_f16_513": (1, 513, 4, 2, 64, "f16", True),
     "f16_causal_384": (2, 384, 4, 1, 128, "f16", True),
+    # (query tiles x heads x sequences) not a multiple of the 8 XCDs the work is dealt over
+    "items_18": (1, 300, 6, 2, 128, "bf16", True),
+    "items_18_b3": (3, 129, 3, 1, 64, "f16", True),
+    "items_20_full": (2, 600, 2, 1, 128, "bf16", False),
 }
 
 
