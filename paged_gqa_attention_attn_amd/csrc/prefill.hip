@@ -78,19 +78,32 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     constexpr bool kStage = std::is_same<E, BF16>::value && !PAGED;   // V may come staged as f16
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    // Work item of this workgroup: query tile qt of head h of sequence b. Workgroups go
-    // to the 8 XCDs in turn (XCD = id mod 8), so XCD k takes the k-th contiguous eighth
-    // of the items, ordered by (sequence, head), then query tile. Every XCD then gets
-    // whole heads, i.e. the same mix of causal tile costs, and the heads that share a
-    // KV head stay on one XCD's L2. Within a head the heaviest tiles (the last rows)
-    // go first. (Query tiles as the fastest grid index gave XCD k tiles 31-k, 23-k, ...
-    // of every head: 1.5x more causal work on XCD 0 than on XCD 7.)
+    // Work item of this workgroup: query tile qt of head h of sequence b. Items are
+    // numbered hb * nqt + r (hb = b * n_q + h; rank r = 0 is the heaviest causal tile,
+    // the last rows). Workgroups go to the 8 XCDs in turn (XCD = id mod 8), so XCD k
+    // takes the k-th contiguous eighth [a, e) of the items: whole heads apart from the
+    // two ends, so every XCD gets the same mix of causal tile costs, and the heads that
+    // share a KV head stay on one XCD's L2. On its XCD, the j-th workgroup takes the
+    // j-th item of [a, e) in (rank, head) order: all heaviest tiles first, as in
+    // longest-first scheduling. C(r), the number of items of [a, e) with rank below r,
+    // is (e / nqt - a / nqt) r + min(r, e % nqt) - min(r, a % nqt); the rank is the
+    // largest r with C(r) <= j, and the heads holding rank r are consecutive from
+    // ceil((a - r) / nqt).
     const int nqt = p.seq_len / BM + (p.seq_len % BM != 0);
     const int n_items = gridDim.x;
     const int wg = blockIdx.x;
-    const int per_xcd = n_items / 8, extra = n_items % 8, xcd = wg % 8;
-    const int item = xcd * per_xcd + min(xcd, extra) + wg / 8;
-    const int hb = item / nqt, qr = item % nqt;
+    const int per_xcd = n_items / 8, xcd = wg % 8;
+    const int ia = xcd * per_xcd + min(xcd, n_items % 8);
+    const int ie = ia + per_xcd + (xcd < n_items % 8);
+    const int jx = wg / 8;
+    const int fa = ia / nqt, ra = ia % nqt, fe = ie / nqt, re = ie % nqt;
+    auto below = [&](int r) { return (fe - fa) * r + min(r, re) - min(r, ra); };
+    int qr = 0;
+    for (int hi = nqt - 1; qr < hi;) {   // uniform: a binary search on scalars
+        const int mid = (qr + hi + 1) / 2;
+        if (below(mid) <= jx) qr = mid; else hi = mid - 1;
+    }
+    const int hb = fa + (qr < ra ? 1 : 0) + (jx - below(qr));
     const int qt = p.causal ? nqt - 1 - qr : qr;
     const int h = hb % p.n_q;
     const int b = hb / p.n_q;
