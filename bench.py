@@ -28,6 +28,7 @@ import argparse
 import hashlib
 import json
 import math
+import re
 import sys
 import time
 from pathlib import Path
@@ -90,10 +91,19 @@ def time_launches(launch, n: int) -> float:
     return e0.elapsed_time(e1) / n
 
 
+def _code_only(text: str) -> str:
+    """Source text without comments and blank lines: what the compiler sees."""
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    return "\n".join(line.rstrip() for line in text.splitlines() if line.strip())
+
+
 def source_hash(kind: str) -> str:
+    """Hash of the code (comments and blank lines dropped) of the sources that make up a
+    profiled kernel: a counter summary carries it, and is used only while it matches."""
     h = hashlib.sha256()
     for name in KERNEL_SOURCES[kind]:
-        h.update((CSRC / name).read_bytes())
+        h.update(_code_only((CSRC / name).read_text()).encode())
     return h.hexdigest()[:16]
 
 

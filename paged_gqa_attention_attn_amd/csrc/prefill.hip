@@ -24,10 +24,12 @@
 //    The V^T operand (8 keys of one dim per lane) is read from the row-major V
 //    tile with ds_read_b64_tr_b16, which hands lane j of a 16-lane group
 //    element j % 4 of the 8-byte chunk fetched by lane 4e + j / 4, for e = 0..3.
-//  * For bf16, P is split into bf16 hi + lo parts and both are multiplied,
-//    which keeps the result within ~1e-5 of exact (P rounded to 8 bits alone
-//    errs by up to ~3e-3 on rows with few keys); f16 keeps 11 bits and needs
-//    no split.
+//  * P rounded to bf16's 8 bits errs by up to ~3e-3 on rows with few keys, so
+//    bf16 P V runs either on an f16 copy of V (written by stage_v_f16_kernel,
+//    exact for every finite bf16 value below 65520 in magnitude) with one
+//    11-bit f16 P, or, in tiles holding a larger value and for paged keys,
+//    with P split into bf16 hi + lo parts (within ~1e-5 of exact). f16 inputs
+//    keep one f16 P.
 //  * The K/V-position permutation inside one MFMA is shared by both operands
 //    (it only has to be the same on A and B): lane half h = lane/32 holds keys
 //    {16j + 8(i/4) + 4h + i%4 : i = 0..7} of 16-key group j, which is exactly
@@ -36,12 +38,16 @@
 //    (log2 units, checked with one ballot per tile), so the output rescale is
 //    rare; p stays below 2^TAU and acc, l and m stay consistent either way.
 //  * Causal: a workgroup visits key tiles up to its last query; tiles past a
-//    wave's last query are skipped by that wave; the heavy (late) query tiles
-//    are launched first.
+//    wave's last query are skipped by that wave. Each XCD gets an equal,
+//    contiguous share of the (head, query tile) items and starts the heaviest
+//    (latest) query tiles of its share first.
 //  * Sliding window (the walk-through's KV-cache section, sliding-window item,
 //    which bounds the cache at W recent positions): the row at position p sees
 //    p - W + 1 .. p. A workgroup starts at the tile holding its first row's
 //    window start, and a wave skips tiles wholly before its first row's.
+//  * ALiBi (the walk-through's position-encoding section): the score of row i
+//    and key j gets -m_h (i - j), added in unscaled units with one
+//    multiply-add per score.
 #include <type_traits>
 
 #include "launch.h"
