@@ -282,6 +282,13 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  * among the ones the sequence's rows read, turns every row of that sequence into
  * NaN instead of an out-of-bounds read. Supported: head_dim 64 or 128; the
  * size limits of pa_paged_attn_prefill with chunk_len in place of seq_len.
+ * bf16 caches: when batch * max_blocks_per_seq * n_kv * 16 * head_dim * 2 bytes
+ * (plus one byte per block) fit in 256 MiB, the call first copies the V rows it
+ * reads to f16 (exact below 65520 in magnitude, as for pa_paged_attn_prefill) in
+ * the workspace of pa_set_workspace if large enough, else the library's own, and
+ * P V then runs with one f16 P part; blocks holding a larger value keep the bf16
+ * hi + lo product. Calls that share that workspace must not overlap on the GPU.
+ * PA_PREFILL_STAGE_V=0 in the environment turns the copy off.
  */
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,

@@ -213,6 +213,18 @@ size_t prefill_stage_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32_t
     const size_t tiles = (size_t)batch * n_kv * (((size_t)seq_len + 63) / 64);
     return prefill_stage_v_bytes(batch, seq_len, n_kv, head_dim) + round16(tiles);
 }
+// The staging kernels take the sequence as grid z and the KV head as grid y.
+bool stage_grid_fits(int32_t batch, int32_t n_kv) { return batch <= 65535 && n_kv <= 65535; }
+// Chunked prefill over a bf16 cache: an f16 copy of the V blocks the call reads,
+// [batch][max_blocks][n_kv][16][head_dim], then one flag byte per block. Staged only
+// up to this size; beyond it P V keeps the bf16 hi + lo form.
+constexpr size_t kChunkStageCap = (size_t)256 << 20;
+size_t chunked_stage_v_bytes(int32_t batch, int32_t max_blocks, int32_t n_kv, int32_t head_dim) {
+    return round16((size_t)batch * max_blocks * n_kv * 16 * head_dim * 2);
+}
+size_t chunked_stage_bytes(int32_t batch, int32_t max_blocks, int32_t n_kv, int32_t head_dim) {
+    return chunked_stage_v_bytes(batch, max_blocks, n_kv, head_dim) + round16((size_t)batch * n_kv * max_blocks);
+}
 
 // Blocks one sequence's call can read: all of max_blocks without a window; with
 // window W and `rows` query rows, the W + rows - 1 positions from the first
@@ -699,7 +711,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.out_f32 = out_dtype == PA_F32;
     a.window = window;
     a.alibi = alibi_slopes;
-    if (prefill_stages(dtype)) {
+    if (prefill_stages(dtype) && stage_grid_fits(batch, n_kv)) {
         const size_t need = prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
         if (!workspace) {
             const int rc = resolve_workspace(need, &workspace);
@@ -869,6 +881,17 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     a.num_blocks = cache->num_blocks;
     a.window = window;
     a.alibi = alibi_slopes;
+    if (prefill_stages(cache->dtype) && stage_grid_fits(batch, cache->n_kv)) {
+        const size_t need = chunked_stage_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
+        if (need <= kChunkStageCap) {
+            void* ws = nullptr;
+            rc = resolve_workspace(need, &ws);
+            if (rc != PA_OK) return rc;
+            a.v16 = ws;
+            a.v16_ok = static_cast<uint8_t*>(ws) +
+                       chunked_stage_v_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
+        }
+    }
     const hipError_t e = pa::launch_prefill(a, to_elem(cache->dtype), cache->head_dim,
                                             static_cast<hipStream_t>(stream));
     if (e == hipErrorNotSupported)

@@ -81,7 +81,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     using S = typename E::storage;
     constexpr int KK = D / 16;     // MFMA k-steps over the head dimension
     constexpr int MT = D / 32;     // 32-dim output tiles
-    constexpr bool kStage = std::is_same<E, BF16>::value && !PAGED;   // V may come staged as f16
+    constexpr bool kStage = std::is_same<E, BF16>::value;   // V may come staged as f16
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     // Work item of this workgroup: query tile qt of head h of sequence b. Items are
@@ -180,16 +180,27 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     // P V product then runs on the f16 matrix cores with one 11-bit P part
     // instead of two bf16 parts. Every wave checks the same tiles, so the choice
     // is uniform over the workgroup.
+    // Paged keys: the copy holds the blocks this call reads, indexed by (sequence,
+    // logical block), with one flag per block; the blocks a workgroup reads are
+    // those from its first tile (or window block) to the context's last.
     bool use16 = false;
     if constexpr (kStage) {
         if (p.v16 != nullptr) {
-            const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * (S_len / BN + (S_len % BN != 0));
             bool fits = true;
-            for (int j = j0 + lane; j < n_tiles; j += 64) fits = fits && ok[j] != 0;
+            if constexpr (PAGED) {
+                const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * p.max_blocks;
+                const int blo = max(j0 * (BN / 16), lo_blk);
+                const int bhi = min(n_tiles * (BN / 16), (ctx + 15) / 16);
+                for (int jb = blo + lane; jb < bhi; jb += 64) fits = fits && ok[jb] != 0;
+            } else {
+                const uint8_t* ok = p.v16_ok + ((int64_t)b * p.n_kv + g) * (S_len / BN + (S_len % BN != 0));
+                for (int j = j0 + lane; j < n_tiles; j += 64) fits = fits && ok[j] != 0;
+            }
             use16 = __all(fits);
         }
     }
     if (use16) Vg = reinterpret_cast<const char*>(p.v16) + head_off;
+    const bool v_logical = PAGED && use16;   // V blocks addressed by logical index
 
     // This wave's copies of tile j into buffer `buf`: copy c fills bytes
     // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
@@ -217,7 +228,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const bool lane_src_fits = PAGED || (int64_t)BN * kv_row < ((int64_t)1 << 31);
     auto issue_tile = [&](int j, int buf) {
         const int key0 = j * BN;
-        int64_t block_src = 0;
+        int64_t block_src = 0, vblock_src = 0;
         if constexpr (PAGED) {
             const int jb = max(min(key0 / 16 + wave, (ctx - 1) / 16), lo_blk);   // uniform over the wave
             int phys = p.block_table[(int64_t)b * p.max_blocks + jb];
@@ -226,14 +237,16 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
                 phys = 0;
             }
             block_src = (int64_t)phys * p.n_kv * 16 * T::ROWB;
+            vblock_src = v_logical ? ((int64_t)b * p.max_blocks + jb) * p.n_kv * 16 * T::ROWB : block_src;
         }
         if (lane_src_fits && key0 >= wg_lo && key0 + BN <= ctx) {   // uniform
             const int64_t base = PAGED ? block_src : (int64_t)key0 * kv_row;
+            const int64_t vbase = PAGED ? vblock_src : base;
 #pragma unroll
             for (int c = 0; c < T::COPIES; ++c) {
                 const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
                 copy_to_lds16(Kg + base, lane_src[c], dst);
-                copy_to_lds16(Vg + base, lane_src[c], dst + T::BYTES);
+                copy_to_lds16(Vg + vbase, lane_src[c], dst + T::BYTES);
             }
             return;
         }
@@ -245,11 +258,12 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
             // The key this lane's row holds: rows past the context read its last
             // key, rows before the window its first (both masked, both finite).
             const int t = max(min(key0 + r, ctx - 1), wg_lo);
-            const int64_t src = PAGED ? block_src + (int64_t)(t % 16) * T::ROWB + chunk * 16
-                                      : (int64_t)t * kv_row + chunk * 16;
+            const int64_t in_blk = (int64_t)(t % 16) * T::ROWB + chunk * 16;
+            const int64_t src = PAGED ? block_src + in_blk : (int64_t)t * kv_row + chunk * 16;
+            const int64_t vsrc = PAGED ? vblock_src + in_blk : src;
             const uint32_t dst = lds0 + buf * T::BUF + (wave * T::COPIES + c) * 1024;
             copy_to_lds16(Kg + src, dst);
-            copy_to_lds16(Vg + src, dst + T::BYTES);
+            copy_to_lds16(Vg + vsrc, dst + T::BYTES);
         }
     };
 
@@ -454,6 +468,26 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 // exactly, except those below f16's normal range (2^-14), which move by at most
 // 2^-25. One workgroup per (64-key tile, KV head, sequence) also records whether
 // any finite value of its tile overflowed (flag 0: the prefill keeps bf16 there).
+// Eight bf16 values (one 16-byte chunk) as f16. `bad` is set when a finite value
+// overflows f16; every other finite bf16 value converts exactly (values below
+// 2^-14 move by at most 2^-25).
+__device__ __forceinline__ uint4 bf16x8_to_f16(const uint4 w, bool& bad) {
+    const uint32_t in[4] = {w.x, w.y, w.z, w.w};
+    uint32_t o16[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float x0 = as_f32(in[i] << 16), x1 = as_f32(in[i] & 0xffff0000u);
+        const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+        bad = bad || (__builtin_isinf((float)h0) && !__builtin_isinf(x0)) ||
+              (__builtin_isinf((float)h1) && !__builtin_isinf(x1));
+        const f16x2_t hv = {h0, h1};
+        o16[i] = __builtin_bit_cast(uint32_t, hv);
+    }
+    return make_uint4(o16[0], o16[1], o16[2], o16[3]);
+}
+
+// Contiguous bf16 V: one workgroup per (64-key tile, KV head, sequence) writes the
+// f16 copy of its tile in V's layout and flags whether the copy is exact.
 template <int D> __global__ __launch_bounds__(256) void stage_v_f16_kernel(const PrefillArgs p) {
     constexpr int CPR = D * 2 / 16;   // 16-byte chunks (8 values) per row
     const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
@@ -464,21 +498,36 @@ template <int D> __global__ __launch_bounds__(256) void stage_v_f16_kernel(const
         if (t >= S_len) break;   // rows grow with c
         const int64_t off = (((int64_t)b * S_len + t) * p.n_kv + g) * D + (c % CPR) * 8;
         const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + off);
-        const uint32_t in[4] = {w.x, w.y, w.z, w.w};
-        uint32_t o16[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float x0 = as_f32(in[i] << 16), x1 = as_f32(in[i] & 0xffff0000u);
-            const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
-            bad = bad || (__builtin_isinf((float)h0) && !__builtin_isinf(x0)) ||
-                  (__builtin_isinf((float)h1) && !__builtin_isinf(x1));
-            const f16x2_t hv = {h0, h1};
-            o16[i] = __builtin_bit_cast(uint32_t, hv);
-        }
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.v16) + off) = make_uint4(o16[0], o16[1], o16[2], o16[3]);
+        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.v16) + off) = bf16x8_to_f16(w, bad);
     }
     bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) p.v16_ok[((int64_t)b * p.n_kv + g) * gridDim.x + tile] = bad ? 0 : 1;
+}
+
+// Paged bf16 V (chunked prefill): one workgroup per (logical block, KV head,
+// sequence) copies the rows below the context length of that block to
+// v16[b][block][g][16][D] as f16 and flags it in v16_ok[b][g][block]. Blocks at or
+// past the context are never read and get no flag; a block id outside the pool
+// gets flag 0 and is not read (the prefill kernel reports that sequence as bad).
+template <int D> __global__ __launch_bounds__(256) void stage_paged_v_f16_kernel(const PrefillArgs p) {
+    constexpr int CPR = D * 2 / 16;
+    const int lb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    const int ctx = p.context_lens[b];
+    if (ctx <= 0 || ctx > p.max_blocks * 16 || lb * 16 >= ctx) return;   // uniform
+    uint8_t* flag = p.v16_ok + ((int64_t)b * p.n_kv + g) * p.max_blocks + lb;
+    const int phys = p.block_table[(int64_t)b * p.max_blocks + lb];
+    if (phys < 0 || phys >= p.num_blocks) {   // uniform
+        if (threadIdx.x == 0) *flag = 0;
+        return;
+    }
+    const int rows = min(16, ctx - lb * 16);
+    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.v) + ((int64_t)phys * p.n_kv + g) * 16 * D;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(p.v16) + (((int64_t)b * p.max_blocks + lb) * p.n_kv + g) * 16 * D;
+    bool bad = false;
+    for (int c = threadIdx.x; c < rows * CPR; c += blockDim.x)
+        *reinterpret_cast<uint4*>(dst + c * 8) = bf16x8_to_f16(*reinterpret_cast<const uint4*>(src + c * 8), bad);
+    bad = __syncthreads_or(bad);
+    if (threadIdx.x == 0) *flag = bad ? 0 : 1;
 }
 
 template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
@@ -489,10 +538,15 @@ template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs&
         reinterpret_cast<const void*>(&prefill_kernel<E, D, PAGED>),
         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (opt_in != hipSuccess) return opt_in;
-    if constexpr (std::is_same<E, BF16>::value && !PAGED) {
+    if constexpr (std::is_same<E, BF16>::value) {
         if (a.v16 != nullptr) {
-            const dim3 sgrid(a.seq_len / BN + (a.seq_len % BN != 0), a.n_kv, a.batch);
-            hipLaunchKernelGGL((stage_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
+            if constexpr (PAGED) {
+                const dim3 sgrid(a.max_blocks, a.n_kv, a.batch);
+                hipLaunchKernelGGL((stage_paged_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
+            } else {
+                const dim3 sgrid(a.seq_len / BN + (a.seq_len % BN != 0), a.n_kv, a.batch);
+                hipLaunchKernelGGL((stage_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
+            }
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess) return e;
         }

@@ -67,23 +67,56 @@ def test_chunked_prefill_matches_oracle(pa, shape):
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
 
 
-def test_whole_prompt_chunk_equals_contiguous_prefill_bitwise(pa, monkeypatch):
+@pytest.mark.parametrize("stage", ["1", "0"], ids=["staged", "unstaged"])
+def test_whole_prompt_chunk_equals_contiguous_prefill_bitwise(pa, monkeypatch, stage):
     # A chunk that is the whole prompt runs the same tile arithmetic as the
-    # contiguous prefill kernel: every output bit must agree.
+    # contiguous prefill kernel (both with V copied to f16, or both without):
+    # every output bit must agree.
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", stage)
     c = wl.make_prefill_case(batch=2, seq_len=300, n_q=8, n_kv=2, head_dim=128, dtype="bf16",
                              seed=77, device="cuda")
-    say("[chunk] whole-prompt chunk vs contiguous prefill, bitwise")
+    say(f"[chunk] whole-prompt chunk vs contiguous prefill, bitwise, PA_PREFILL_STAGE_V={stage}")
     kp, vp = c.k_pool.clone(), c.v_pool.clone()
     pa.kv_append(c.k.reshape(-1, c.n_kv, c.head_dim), c.v.reshape(-1, c.n_kv, c.head_dim),
                  c.prompt_slots, kp, vp)
     ctx = torch.full((c.batch,), c.seq_len, dtype=torch.int32, device="cuda")
     paged = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, ctx, c.scale)
-    # The contiguous kernel's unstaged form (bf16 P V, as the paged keys use);
-    # the staged form is checked against the oracle elsewhere.
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
     contig = pa.paged_attn_prefill(c.q, c.k, c.v, True, c.scale)
     torch.cuda.synchronize()
     assert same_bits(paged, contig)
+
+
+@pytest.mark.parametrize("where", ["prefix", "chunk"])
+def test_chunked_prefill_v_beyond_f16_matches_oracle(pa, where):
+    """A finite V value past f16's range (70144) in one block: workgroups whose rows
+    read that block keep the bf16 hi + lo product, the others use the f16 copy. The
+    dimension holding it scales with the value, so it is checked norm-wise relative;
+    every other dimension against the usual bound."""
+    c = wl.make_chunk_case(batch=2, chunk_len=200, prefix_lens=[300, 60], n_q=8, n_kv=2,
+                           head_dim=128, dtype="bf16", free_fraction=0.2, seed=401, device="cuda")
+    say(f"[chunk] one V value of 70144 in the {where}")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    cv = c.chunk_v.clone()
+    if where == "chunk":                    # sequence 0, chunk row 150 = position 450, KV head 1
+        cv[150, 1, 7] = 70144.0
+        e, h0 = 7, 4
+    pa.kv_append(c.chunk_k, cv, c.chunk_slots, kp, vp)
+    if where == "prefix":                   # sequence 0, position 83, KV head 0
+        vp[int(c.block_table[0, 5]), 0, 3, 11] = 70144.0
+        e, h0 = 11, 0
+    got = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    got = got.cpu().numpy()
+    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+                                  c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale)
+    assert np.isfinite(got).all()
+    big = np.zeros(got.shape, bool)
+    big[0, :, h0:h0 + 4, e] = True
+    assert_parity(got[~big], want[~big], "bf16", "dimensions without the large value")
+    g_, w_ = got[0, :, h0:h0 + 4, e], want[0, :, h0:h0 + 4, e]
+    rel = np.abs(g_ - w_).max() / np.abs(w_).max()
+    say(f"    heads {h0}..{h0 + 3} dim {e}: norm-wise rel {rel:.2e}")
+    assert rel <= 1e-3, rel
 
 
 def test_relabelled_blocks_give_identical_bits(pa):

@@ -215,18 +215,17 @@ def test_prefill_window_matches_oracle(pa, window):
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
 
 
-def test_whole_prompt_chunk_equals_contiguous_prefill_with_window_bitwise(pa, monkeypatch):
+@pytest.mark.parametrize("stage", ["1", "0"], ids=["staged", "unstaged"])
+def test_whole_prompt_chunk_equals_contiguous_prefill_with_window_bitwise(pa, monkeypatch, stage):
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", stage)
     c = wl.make_prefill_case(batch=2, seq_len=300, n_q=8, n_kv=2, head_dim=128, dtype="bf16",
                              seed=78, device="cuda")
-    say("[window] whole-prompt chunk vs contiguous prefill, W=90, bitwise")
+    say(f"[window] whole-prompt chunk vs contiguous prefill, W=90, bitwise, PA_PREFILL_STAGE_V={stage}")
     kp, vp = c.k_pool.clone(), c.v_pool.clone()
     pa.kv_append(c.k.reshape(-1, c.n_kv, c.head_dim), c.v.reshape(-1, c.n_kv, c.head_dim),
                  c.prompt_slots, kp, vp)
     ctx = torch.full((c.batch,), c.seq_len, dtype=torch.int32, device="cuda")
     paged = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, ctx, c.scale, window=90)
-    # The contiguous kernel's unstaged form (bf16 P V, as the paged keys use);
-    # the staged form is checked against the oracle elsewhere.
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
     contig = pa.paged_attn_prefill(c.q, c.k, c.v, True, c.scale, window=90)
     torch.cuda.synchronize()
     assert same_bits(paged, contig)
