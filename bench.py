@@ -480,7 +480,9 @@ def bench_chunked_prefill(args):
         "config": {"workload": c0.name, "batch": B, "chunk_len": C, "prefix_len": P, "n_q": c0.n_q,
                    "n_kv": c0.n_kv, "head_dim": c0.head_dim, "flops": flops,
                    "step": "kv_append of the 2x1024 chunk tokens + chunked prefill"},
-        "roofline": {"kernel": "prefill kernel, paged keys", "bound": "mfma",
+        "roofline": {"kernel": "chunked_prefill call: f16 copy of the V blocks read (bf16 caches) + "
+                               "prefill kernel with paged keys", "bound": "mfma",
+                     "launches_per_call": 2 if c0.dtype == "bf16" else 1,
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
