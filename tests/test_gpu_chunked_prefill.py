@@ -166,3 +166,26 @@ def test_bf16_output(pa):
     got = gpu_chunk(pa, c, out_dtype=torch.bfloat16).float().cpu().numpy()
     want = oracle_chunk(c)
     assert (np.abs(got - want) <= 2e-3 + 2.0**-8 * np.abs(want)).all()
+
+
+def test_chunked_prefill_past_the_copy_cap_keeps_the_bf16_product(pa, monkeypatch):
+    """A block table 9000 blocks wide over 8 KV heads would need a 295 MB f16 copy of V,
+    past the 256 MiB a call stages: P V then keeps the bf16 hi + lo product. The result
+    matches the oracle and, bit for bit, the same call on the narrow table with the copy
+    switched off."""
+    c = wl.make_chunk_case(batch=2, chunk_len=130, prefix_lens=[400, 33], n_q=16, n_kv=8,
+                           head_dim=128, dtype="bf16", free_fraction=0.2, seed=902, device="cuda")
+    say("[chunk] 9000-block table: past the f16 copy's size cap")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    wide = torch.full((c.batch, 9000), -1, dtype=torch.int32, device="cuda")   # unused entries
+    wide[:, :c.max_blocks_per_seq] = c.block_table
+    got = pa.paged_attn_chunked_prefill(c.q, kp, vp, wide, c.context_lens, c.scale)
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    unstaged = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+                                  c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale)
+    stats = assert_parity(got.cpu().numpy(), want, "bf16", "chunked prefill, 9000-block table")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+    assert same_bits(got, unstaged)
