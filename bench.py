@@ -484,7 +484,8 @@ def bench_chunked_prefill(args):
                                "prefill kernel with paged keys", "bound": "mfma",
                      "launches_per_call": 2 if c0.dtype == "bf16" else 1,
                      "achieved": round(achieved, 2), "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "frac": round(achieved / MFMA_BF16_PEAK_TFLOPS, 4),
+                     "traffic": measured_traffic("prefill", args.workload),
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
                      "source_hash": source_hash("prefill")},
     }
@@ -543,7 +544,8 @@ def bench_decode_multi(args):
                    "step": "kv_append of 4 new tokens per sequence + one multi-row decode launch"},
         "roofline": {"kernel": "multi-row decode kernel (matrix cores)", "bound": "hbm",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("decode_multi", args.workload),
                      "algorithmic_bytes_per_launch": int(kv + io), "avg_launch_us": round(dec_ms * 1e3, 2),
                      "source_hash": source_hash("decode_multi")},
         "tflops": round(4 * R * c0.n_q * c0.head_dim * ctx * B / (dec_ms * 1e-3) / 1e12, 3),
