@@ -26,10 +26,10 @@
 //    element j % 4 of the 8-byte chunk fetched by lane 4e + j / 4, for e = 0..3.
 //  * P rounded to bf16's 8 bits errs by up to ~3e-3 on rows with few keys, so
 //    bf16 P V runs either on an f16 copy of V (written by stage_v_f16_kernel,
-//    exact for every finite bf16 value below 65520 in magnitude) with one
-//    11-bit f16 P, or, in tiles holding a larger value and for paged keys,
-//    with P split into bf16 hi + lo parts (within ~1e-5 of exact). f16 inputs
-//    keep one f16 P.
+//    or by stage_paged_v_f16_kernel for paged keys; exact for every finite
+//    bf16 value below 65520 in magnitude) with one 11-bit f16 P, or, where a
+//    tile or block holds a larger value or no copy was made, with P split into
+//    bf16 hi + lo parts (within ~1e-5 of exact). f16 inputs keep one f16 P.
 //  * The K/V-position permutation inside one MFMA is shared by both operands
 //    (it only has to be the same on A and B): lane half h = lane/32 holds keys
 //    {16j + 8(i/4) + 4h + i%4 : i = 0..7} of 16-key group j, which is exactly
