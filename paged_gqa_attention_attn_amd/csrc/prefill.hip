@@ -487,47 +487,74 @@ __device__ __forceinline__ uint4 bf16x8_to_f16(const uint4 w, bool& bad) {
 }
 
 // Contiguous bf16 V: one workgroup per (64-key tile, KV head, sequence) writes the
-// f16 copy of its tile in V's layout and flags whether the copy is exact.
+// f16 copy of its tile in V's layout and flags whether the copy is exact. Each
+// thread loads all its chunks before it stores any, so the loads overlap.
 template <int D> __global__ __launch_bounds__(256) void stage_v_f16_kernel(const PrefillArgs p) {
-    constexpr int CPR = D * 2 / 16;   // 16-byte chunks (8 values) per row
+    constexpr int CPR = D * 2 / 16;                // 16-byte chunks (8 values) per row
+    constexpr int PER = BN * CPR / 256;            // chunks per thread
+    static_assert(PER * 256 == BN * CPR, "a tile splits evenly over 256 threads");
     const int tile = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
     const int S_len = p.seq_len;
-    bool bad = false;
-    for (int c = threadIdx.x; c < BN * CPR; c += blockDim.x) {
+    int64_t off[PER];
+    uint4 w[PER];
+#pragma unroll
+    for (int i = 0; i < PER; ++i) {
+        const int c = threadIdx.x + 256 * i;
         const int t = tile * BN + c / CPR;
-        if (t >= S_len) break;   // rows grow with c
-        const int64_t off = (((int64_t)b * S_len + t) * p.n_kv + g) * D + (c % CPR) * 8;
-        const uint4 w = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + off);
-        *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.v16) + off) = bf16x8_to_f16(w, bad);
+        off[i] = t < S_len ? (((int64_t)b * S_len + t) * p.n_kv + g) * D + (c % CPR) * 8 : -1;
+        if (off[i] >= 0) w[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) + off[i]);
     }
+    bool bad = false;
+#pragma unroll
+    for (int i = 0; i < PER; ++i)
+        if (off[i] >= 0)
+            *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(p.v16) + off[i]) = bf16x8_to_f16(w[i], bad);
     bad = __syncthreads_or(bad);
     if (threadIdx.x == 0) p.v16_ok[((int64_t)b * p.n_kv + g) * gridDim.x + tile] = bad ? 0 : 1;
 }
 
-// Paged bf16 V (chunked prefill): one workgroup per (logical block, KV head,
-// sequence) copies the rows below the context length of that block to
+// Paged bf16 V (chunked prefill): one workgroup per (4 logical blocks, KV head,
+// sequence) copies the rows below the context length of each block to
 // v16[b][block][g][16][D] as f16 and flags it in v16_ok[b][g][block]. Blocks at or
 // past the context are never read and get no flag; a block id outside the pool
 // gets flag 0 and is not read (the prefill kernel reports that sequence as bad).
+// Each thread loads its chunk of all 4 blocks before it stores any.
+constexpr int STAGE_BLOCKS = 4;   // logical blocks per staging workgroup
 template <int D> __global__ __launch_bounds__(256) void stage_paged_v_f16_kernel(const PrefillArgs p) {
     constexpr int CPR = D * 2 / 16;
-    const int lb = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+    static_assert(16 * CPR <= 256, "one chunk of a block per thread");
+    const int g = blockIdx.y, b = blockIdx.z;
     const int ctx = p.context_lens[b];
-    if (ctx <= 0 || ctx > p.max_blocks * 16 || lb * 16 >= ctx) return;   // uniform
-    uint8_t* flag = p.v16_ok + ((int64_t)b * p.n_kv + g) * p.max_blocks + lb;
-    const int phys = p.block_table[(int64_t)b * p.max_blocks + lb];
-    if (phys < 0 || phys >= p.num_blocks) {   // uniform
-        if (threadIdx.x == 0) *flag = 0;
-        return;
+    if (ctx <= 0 || ctx > p.max_blocks * 16) return;   // uniform
+    const int lb0 = blockIdx.x * STAGE_BLOCKS;
+    if (lb0 * 16 >= ctx) return;                        // uniform
+    const int c = threadIdx.x;
+    int rows[STAGE_BLOCKS];
+    bool live[STAGE_BLOCKS], ok[STAGE_BLOCKS];
+    uint4 w[STAGE_BLOCKS];
+#pragma unroll
+    for (int i = 0; i < STAGE_BLOCKS; ++i) {   // uniform per block
+        const int lb = lb0 + i;
+        live[i] = lb * 16 < ctx;               // then lb < max_blocks too
+        const int phys = live[i] ? p.block_table[(int64_t)b * p.max_blocks + lb] : -1;
+        ok[i] = live[i] && phys >= 0 && phys < p.num_blocks;
+        rows[i] = ok[i] ? min(16, ctx - lb * 16) : 0;
+        if (c < rows[i] * CPR)
+            w[i] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.v) +
+                                                  ((int64_t)phys * p.n_kv + g) * 16 * D + c * 8);
     }
-    const int rows = min(16, ctx - lb * 16);
-    const uint16_t* src = reinterpret_cast<const uint16_t*>(p.v) + ((int64_t)phys * p.n_kv + g) * 16 * D;
-    uint16_t* dst = reinterpret_cast<uint16_t*>(p.v16) + (((int64_t)b * p.max_blocks + lb) * p.n_kv + g) * 16 * D;
-    bool bad = false;
-    for (int c = threadIdx.x; c < rows * CPR; c += blockDim.x)
-        *reinterpret_cast<uint4*>(dst + c * 8) = bf16x8_to_f16(*reinterpret_cast<const uint4*>(src + c * 8), bad);
-    bad = __syncthreads_or(bad);
-    if (threadIdx.x == 0) *flag = bad ? 0 : 1;
+#pragma unroll
+    for (int i = 0; i < STAGE_BLOCKS; ++i) {
+        bool bad = false;
+        if (c < rows[i] * CPR) {
+            uint16_t* dst = reinterpret_cast<uint16_t*>(p.v16) +
+                            (((int64_t)b * p.max_blocks + lb0 + i) * p.n_kv + g) * 16 * D;
+            *reinterpret_cast<uint4*>(dst + c * 8) = bf16x8_to_f16(w[i], bad);
+        }
+        bad = __syncthreads_or(bad);           // every thread, every block: uniform trip count
+        if (threadIdx.x == 0 && live[i])
+            p.v16_ok[((int64_t)b * p.n_kv + g) * p.max_blocks + lb0 + i] = ok[i] && !bad ? 1 : 0;
+    }
 }
 
 template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
@@ -541,7 +568,7 @@ template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs&
     if constexpr (std::is_same<E, BF16>::value) {
         if (a.v16 != nullptr) {
             if constexpr (PAGED) {
-                const dim3 sgrid(a.max_blocks, a.n_kv, a.batch);
+                const dim3 sgrid((a.max_blocks + STAGE_BLOCKS - 1) / STAGE_BLOCKS, a.n_kv, a.batch);
                 hipLaunchKernelGGL((stage_paged_v_f16_kernel<D>), sgrid, dim3(256), 0, s, a);
             } else {
                 const dim3 sgrid(a.seq_len / BN + (a.seq_len % BN != 0), a.n_kv, a.batch);
