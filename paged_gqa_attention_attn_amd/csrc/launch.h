@@ -98,6 +98,7 @@ struct PrefillArgs {
     int32_t max_blocks, num_blocks;
     int32_t window;   // sliding window (causal only); 0: none
     const float* alibi;   // ALiBi slopes [n_q] (causal only); nullptr: none
+    int resident_wgs;     // prefill workgroups the GPU holds at once (set by the launcher)
     // Contiguous bf16 keys only: an f16 copy of v in v's layout, written by the
     // staging kernel, and one byte per (sequence, KV head, 64-key tile) that is 1
     // where the copy is exact. nullptr: P V stays in bf16 (hi + lo parts).

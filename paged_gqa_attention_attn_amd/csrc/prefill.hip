@@ -48,6 +48,7 @@
 //  * ALiBi (the walk-through's position-encoding section): the score of row i
 //    and key j gets -m_h (i - j), added in unscaled units with one
 //    multiply-add per score.
+#include <atomic>
 #include <type_traits>
 
 #include "launch.h"
@@ -101,7 +102,11 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int per_xcd = n_items / 8, xcd = wg % 8;
     const int ia = xcd * per_xcd + min(xcd, n_items % 8);
     const int ie = ia + per_xcd + (xcd < n_items % 8);
-    const int jx = wg / 8;
+    int jx = wg / 8;
+    // When the whole grid is resident at once (one round of two workgroups per CU),
+    // the second half of an XCD's share goes lightest first, so that a CU's two
+    // workgroups tend to pair a heavy tile with a light one.
+    if (n_items <= p.resident_wgs && jx >= (ie - ia) / 2) jx = (ie - ia) - 1 - (jx - (ie - ia) / 2);
     const int fa = ia / nqt, ra = ia % nqt, fe = ie / nqt, re = ie % nqt;
     auto below = [&](int r) { return (fe - fa) * r + min(r, re) - min(r, ra); };
     int qr = 0;
@@ -557,7 +562,20 @@ template <int D> __global__ __launch_bounds__(256) void stage_paged_v_f16_kernel
     }
 }
 
-template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& a, hipStream_t s) {
+// Compute units of the current device (cached per device).
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
+        cus[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
+template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& args, hipStream_t s) {
+    PrefillArgs a = args;
+    a.resident_wgs = 2 * device_cus();   // __launch_bounds__(256, 2) and 64 KB of LDS each
     const size_t lds = 2 * (size_t)Tile<D>::BUF;
     // Opt in to exactly the dynamic LDS used (static LDS, e.g. the one word
     // __syncthreads_or needs, counts against the same 160 KB).
