@@ -685,7 +685,8 @@ def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): this library has no "
-              "multi-GPU path; see DESIGN.md for how the decode step would shard.",
+              "multi-GPU path. Decode would shard by sequence or by KV head with no exchange "
+              "inside attention, or by context range with one log-sum-exp merge of the partials.",
               file=sys.stderr)
         return 2
     import torch
