@@ -69,12 +69,19 @@ def oracle_step(case, sel=None):
     return kp, vp, out
 
 
+def nan_out(shape, dtype=torch.float32, device="cuda") -> torch.Tensor:
+    """An output buffer filled with NaN, so that any element a kernel never writes
+    fails the parity check (torch.empty may hand back finite leftovers)."""
+    return torch.full(tuple(shape), float("nan"), dtype=dtype, device=device)
+
+
 def gpu_step(pa, case, out_dtype=torch.float32):
-    """The GPU path of one decode step on copies of the pools: kv_append then decode."""
+    """The GPU path of one decode step on copies of the pools: kv_append then decode,
+    into a NaN-filled output."""
     kp = case.k_pool.clone()
     vp = case.v_pool.clone()
     pa.kv_append(case.new_k, case.new_v, case.slot_mapping, kp, vp)
-    out = pa.paged_attn_decode(case.q, kp, vp, case.block_table, case.context_lens, case.scale,
-                               out_dtype=out_dtype)
+    out = nan_out((case.batch, case.n_q, case.head_dim), out_dtype)
+    pa.paged_attn_decode(case.q, kp, vp, case.block_table, case.context_lens, case.scale, out=out)
     torch.cuda.synchronize()
     return kp, vp, out

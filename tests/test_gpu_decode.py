@@ -15,7 +15,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, gpu_step, oracle_step, same_bits, say, stored_np
+from gpu_helpers import assert_parity, gpu_step, nan_out, oracle_step, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -209,20 +209,12 @@ def test_bf16_output(pa):
     assert (err <= 2e-3 + 2.0**-8 * np.abs(want)).all(), float(err.max())
 
 
-def _sampled_pairs(case, n_extra=4, seed=0):
-    G = case.n_q // case.n_kv
-    rng = np.random.default_rng(seed)
-    pairs = []
-    for b in range(case.batch):
-        heads = {0, G - 1, G, case.n_q - 1, *rng.integers(0, case.n_q, n_extra).tolist()}
-        pairs += [[b, h] for h in sorted(heads)]
-    return np.asarray(pairs, np.int32)
-
-
 @pytest.mark.parametrize("cfg", [2, 3, 4])
-def test_full_size_config_sampled(pa, cfg):
+def test_full_size_config_all_rows(pa, cfg):
+    """Every (sequence, query head) row of the full-size configuration against the
+    oracle, into a NaN-filled output: a row the kernels never write fails."""
     case = wl.make_config(cfg, device="cuda")
-    say(f"[decode] config {cfg} full size ({case.name}), B={case.batch}")
+    say(f"[decode] config {cfg} full size ({case.name}), B={case.batch}, all rows")
     kp, vp, out = gpu_step(pa, case)
     # kv_append: the pool after the append equals the oracle's appended pool.
     okp = stored_np(case.k_pool).copy()
@@ -231,13 +223,11 @@ def test_full_size_config_sampled(pa, cfg):
                      case.slot_mapping.cpu().numpy(), okp, ovp)
     assert same_bits(kp.cpu(), torch.from_numpy(okp).view(kp.dtype))
     assert same_bits(vp.cpu(), torch.from_numpy(ovp).view(vp.dtype))
-    sel = _sampled_pairs(case)
     want = oracle.decode(stored_np(case.q), okp, ovp, case.dtype, case.block_table.cpu().numpy(),
-                         case.context_lens.cpu().numpy(), case.scale, sel=sel)
-    got = out.cpu().numpy()[sel[:, 0], sel[:, 1]]
-    stats = assert_parity(got, want, case.dtype, f"config {cfg} sampled ({len(sel)} rows)")
-    assert torch.isfinite(out).all()
-    say(f"    sampled rows={len(sel)} max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+                         case.context_lens.cpu().numpy(), case.scale)
+    stats = assert_parity(out.cpu().numpy(), want, case.dtype,
+                          f"config {cfg} ({case.batch * case.n_q} rows)")
+    say(f"    rows={case.batch * case.n_q} max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
 
 
 # ---- fused append + decode ------------------------------------------------------------------
@@ -254,8 +244,9 @@ def _two_call(pa, case, slots=None):
 def _fused(pa, case, slots=None):
     kp, vp = case.k_pool.clone(), case.v_pool.clone()
     s = case.slot_mapping if slots is None else slots
-    out = pa.paged_attn_decode_append(case.q, case.new_k, case.new_v, s, kp, vp,
-                                      case.block_table, case.context_lens, case.scale)
+    out = nan_out((case.batch, case.n_q, case.head_dim))
+    pa.paged_attn_decode_append(case.q, case.new_k, case.new_v, s, kp, vp,
+                                case.block_table, case.context_lens, case.scale, out=out)
     torch.cuda.synchronize()
     return kp, vp, out
 
@@ -326,7 +317,5 @@ def test_fused_padding_and_empty_context(pa):
 def test_fused_full_size_config2(pa):
     case = wl.make_config(2, device="cuda")
     out = check_fused(pa, case, "config 2 full size")
-    sel = _sampled_pairs(case)
-    _, _, want = oracle_step(case, sel=sel)
-    got = out.cpu().numpy()[sel[:, 0], sel[:, 1]]
-    assert_parity(got, want, "bf16", "fused config 2 sampled")
+    _, _, want = oracle_step(case)
+    assert_parity(out.cpu().numpy(), want, "bf16", "fused config 2, all rows")

@@ -1,15 +1,14 @@
 """GPU parity of the MFMA prefill kernel, and the prefill -> cache write -> decode flow.
 
-Prefill outputs are compared with the fp64 oracle row by row (every row for
-small shapes, sampled rows at the 2 x 4096 prompt size) within max-abs 2e-3
-and norm-wise relative 1e-2.
+Prefill outputs are compared with the fp64 oracle on every row, the 2 x 4096
+prompt included, within max-abs 2e-3 and norm-wise relative 1e-2.
 """
 import numpy as np
 import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, same_bits, say, stored_np
+from gpu_helpers import assert_parity, nan_out, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -105,23 +104,15 @@ def test_prefill_row_matches_gpu_decode(pa):
 def test_config5_prefill_append_decode(pa):
     case = wl.make_config(5, device="cuda")
     B, S, n_q, n_kv, d = case.batch, case.seq_len, case.n_q, case.n_kv, case.head_dim
-    say(f"[config5] prefill B={B} S={S} n_q={n_q} n_kv={n_kv}")
-    out = pa.paged_attn_prefill(case.q, case.k, case.v, True, case.scale)
+    say(f"[config5] prefill B={B} S={S} n_q={n_q} n_kv={n_kv}, all rows")
+    out = nan_out(case.q.shape)
+    pa.paged_attn_prefill(case.q, case.k, case.v, True, case.scale, out=out)
     torch.cuda.synchronize()
-    rng = np.random.default_rng(55)
-    rows = []
-    for b in range(B):
-        for h in range(n_q):
-            for i in sorted({0, 1, 2, 3, 17, 63, 64, 127, 128, 2047, S - 1,
-                             *rng.integers(0, S, 3).tolist()}):
-                rows.append((b, h, i))
-    sel = np.asarray(rows, np.int32)
     want = oracle.prefill(stored_np(case.q), stored_np(case.k), stored_np(case.v), "bf16", True,
-                          case.scale, sel=sel)
-    got = out.cpu().numpy()[sel[:, 0], sel[:, 2], sel[:, 1]]
-    stats = assert_parity(got, want, "bf16", f"config5 prefill ({len(sel)} sampled rows)")
-    assert torch.isfinite(out).all()
-    say(f"    prefill sampled rows={len(sel)} max_abs={stats['max_abs']:.2e}")
+                          case.scale)
+    stats = assert_parity(out.cpu().numpy(), want, "bf16", f"config5 prefill ({B * S * n_q} rows)")
+    del want
+    say(f"    prefill rows={B * S * n_q} max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
 
     # Cache write of the whole prompt, then of the first generated token.
     kp, vp = case.k_pool.clone(), case.v_pool.clone()
@@ -129,7 +120,8 @@ def test_config5_prefill_append_decode(pa):
     vf = case.v.reshape(B * S, n_kv, d)
     pa.kv_append(kf, vf, case.prompt_slots, kp, vp)
     pa.kv_append(case.new_k, case.new_v, case.new_slots, kp, vp)
-    dec = pa.paged_attn_decode(case.q_new, kp, vp, case.block_table, case.context_lens, case.scale)
+    dec = nan_out((B, n_q, d))
+    pa.paged_attn_decode(case.q_new, kp, vp, case.block_table, case.context_lens, case.scale, out=dec)
     torch.cuda.synchronize()
     okp, ovp = stored_np(case.k_pool).copy(), stored_np(case.v_pool).copy()
     oracle.kv_append(stored_np(kf), stored_np(vf), case.prompt_slots.cpu().numpy(), okp, ovp)
