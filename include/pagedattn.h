@@ -123,7 +123,10 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *                 the sequence's logical block j (positions 16j .. 16j+15)
  *   context_lens  int32 [batch]: number of positions attended, counting the
  *                 token appended in the same step (positions 0..ctx-1)
- *   scale         multiplies q.k (usually 1/sqrt(head_dim)); must be positive
+ *   scale         multiplies q.k (usually 1/sqrt(head_dim)); any finite value. 0
+ *                 makes every score exactly 0 (with finite q and K), so a row is the
+ *                 mean of the V rows it attends to (plus the ALiBi bias, if any); a
+ *                 negative scale negates q.k exactly. Not finite: PA_ERR_INVALID_ARG.
  *   window        sliding window ([IW] "KV Cache 的形状与增长", sliding-window item):
  *                 0 attends to all ctx positions; W > 0 to the last W of them,
  *                 positions max(0, ctx - W) .. ctx - 1. Block-table entries of
@@ -138,12 +141,18 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
  *                 bytes for the same arguments, or NULL: then the workspace
  *                 given to pa_set_workspace if it is large enough, else one the
  *                 library allocates on the current device at the first call
- *                 that needs it (grown when a later call needs more, which
- *                 synchronises the device; kept until the process ends).
+ *                 that needs it. When a later call needs more, the library
+ *                 allocates a buffer at least twice as large and keeps the old
+ *                 one too (a call on another thread, or kernels still running,
+ *                 may use it), so every library buffer lives until the process
+ *                 ends; that call is then not capturable in a HIP graph.
  * Query head h reads KV head h / (n_q / n_kv). ctx == 0 gives a zero row.
  * Results depend only on logical positions, so relabelling physical blocks
  * leaves every output bit unchanged. Calls that share a workspace (the library's
  * own included) must not overlap on the GPU: concurrent streams pass their own.
+ * Calls from several host threads on one stream may share the library's own or
+ * the pa_set_workspace buffer: each call enqueues all its kernels while holding
+ * the library's workspace lock, so their kernels do not interleave.
  */
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
                          const void* v_cache, const pa_cache_desc* cache,
@@ -189,7 +198,8 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *   q     [batch][seq_len][n_q][head_dim]   in dtype (bf16 or f16)
  *   k, v  [batch][seq_len][n_kv][head_dim]  in dtype
  *   causal  1: row i attends to keys 0..i; 0: to all seq_len keys
- *   scale   multiplies q.k (usually 1/sqrt(head_dim)); must be positive
+ *   scale   multiplies q.k (usually 1/sqrt(head_dim)); any finite value, as
+ *           for pa_paged_attn_decode
  *   window  0: no window; W > 0 (causal only) narrows row i to keys
  *           max(0, i - W + 1) .. i ([IW] sliding-window item). Negative, or
  *           positive with causal == 0: PA_ERR_INVALID_ARG.
@@ -270,7 +280,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  *                 sits at position context_lens[b] - chunk_len + i and attends to
  *                 positions 0 .. that position (causal mask aligned at the bottom
  *                 right; chunk_len == context_lens[b] is a plain causal prefill)
- *   scale         multiplies q.k; must be positive
+ *   scale         multiplies q.k; any finite value, as for pa_paged_attn_decode
  *   alibi_slopes  NULL, or device fp32 [n_q]: the row at position p scores key
  *                 position j with -m_h (p - j) added (as for pa_paged_attn_decode)
  *   window        0: none; W > 0: the row at position p attends to positions
@@ -285,17 +295,25 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  * bf16 caches: when batch * max_blocks_per_seq * n_kv * 16 * head_dim * 2 bytes
  * (plus one byte per block) fit in 256 MiB, the call first copies the V rows it
  * reads to f16 (exact below 65520 in magnitude, as for pa_paged_attn_prefill) in
- * the workspace of pa_set_workspace if large enough, else the library's own, and
- * P V then runs with one f16 P part; blocks holding a larger value keep the bf16
- * hi + lo product. Calls that share that workspace must not overlap on the GPU.
+ * the workspace (below), and P V then runs with one f16 P part; blocks holding a
+ * larger value keep the bf16 hi + lo product. Calls that share that workspace
+ * must not overlap on the GPU.
  * PA_PREFILL_STAGE_V=0 in the environment turns the copy off.
+ *   workspace     device scratch of at least pa_chunked_prefill_workspace_bytes(...)
+ *                 bytes for the same batch, max_blocks_per_seq and cache (16-byte
+ *                 aligned; 0 bytes: none is used), or NULL: then the workspace of
+ *                 pa_set_workspace if large enough, else the library's own (as for
+ *                 pa_paged_attn_decode).
  */
+size_t pa_chunked_prefill_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq,
+                                          const pa_cache_desc* cache);
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* context_lens, float scale, int32_t window,
                                   const float* alibi_slopes,
-                                  void* out, pa_dtype out_dtype, void* stream);
+                                  void* out, pa_dtype out_dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
 
 /*
  * kv_append_quant -- quantise new K/V rows into a one-byte cache and write them

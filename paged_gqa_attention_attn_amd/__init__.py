@@ -31,7 +31,7 @@ from ._lib import CacheDesc, LibraryNotBuilt
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
            "paged_attn_chunked_prefill", "paged_attn_decode_multi", "kv_append_quant",
            "paged_attn_decode_quant", "paged_attn_decode_quant_append", "quant_decode_workspace_bytes",
-           "prefill_workspace_bytes",
+           "prefill_workspace_bytes", "chunked_prefill_workspace_bytes",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
@@ -61,9 +61,20 @@ def _dev(t: torch.Tensor, name: str, dtype=None) -> int:
     return t.data_ptr()
 
 
+def _torch_stream(t: torch.Tensor, stream):
+    """The stream a call enqueues on: ``stream``, else the current stream of t's device."""
+    return stream if stream is not None else torch.cuda.current_stream(t.device)
+
+
 def _stream(t: torch.Tensor, stream) -> ctypes.c_void_p:
-    s = stream if stream is not None else torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(s.cuda_stream)
+    return ctypes.c_void_p(_torch_stream(t, stream).cuda_stream)
+
+
+def _alloc(shape, dtype, like: torch.Tensor, stream) -> torch.Tensor:
+    """An output or scratch tensor owned by the stream the kernels run on, so that the
+    caching allocator does not hand its memory to other work before they finish."""
+    with torch.cuda.stream(_torch_stream(like, stream)):
+        return torch.empty(shape, dtype=dtype, device=like.device)
 
 
 def _alibi_arg(alibi_slopes, n_q: int):
@@ -159,13 +170,13 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
     maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, n_q, d), out_dtype, q, stream)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
     if workspace is None:
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc(need, torch.uint8, q, stream)
     ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode", L.pa_paged_attn_decode(
@@ -204,13 +215,13 @@ def paged_attn_decode_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
     maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, n_q, d), out_dtype, q, stream)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
     if workspace is None:
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc(need, torch.uint8, q, stream)
     ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode_append", L.pa_paged_attn_decode_append(
@@ -250,14 +261,14 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     if q.dtype not in _DTYPE:
         raise TypeError(f"unsupported dtype {q.dtype}")
     if out is None:
-        out = torch.empty((B, S, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, S, n_q, d), out_dtype, q, stream)
     if out.shape != q.shape or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][S][n_q][d] in a supported dtype")
     dt = q.dtype
     if workspace is None:
         need = int(L.pa_prefill_workspace_bytes(_DTYPE[dt], B, S, k.shape[2], d))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc(need, torch.uint8, q, stream)
     _check("pa_paged_attn_prefill", L.pa_paged_attn_prefill(
         _dev(q, "q", dt), _dev(k, "k", dt), _dev(v, "v", dt), _DTYPE[dt], B, S, n_q, k.shape[2],
         d, int(bool(causal)), float(scale), int(window),
@@ -266,15 +277,26 @@ def paged_attn_prefill(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, causal
     return out
 
 
+def chunked_prefill_workspace_bytes(batch: int, max_blocks_per_seq: int,
+                                    k_cache: torch.Tensor) -> int:
+    """Bytes of device workspace a chunked prefill with these sizes uses (0: none)."""
+    desc = _cache_desc(k_cache)
+    return int(_lib.load().pa_chunked_prefill_workspace_bytes(batch, max_blocks_per_seq,
+                                                              ctypes.byref(desc)))
+
+
 def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
                                block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
                                out: torch.Tensor | None = None,
                                out_dtype: torch.dtype = torch.float32, stream=None,
                                window: int = 0,
-        alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
+                               alibi_slopes: torch.Tensor | None = None,
+                               workspace: torch.Tensor | None = None) -> torch.Tensor:
     """A prompt chunk q [B][C][n_q][d] attends to its paged prefix and causally to itself;
     row i of sequence b is position context_lens[b] - C + i. Returns out [B][C][n_q][d].
-    window W > 0 restricts the row at position p to positions p - W + 1 .. p."""
+    window W > 0 restricts the row at position p to positions p - W + 1 .. p. workspace:
+    a device buffer of at least chunked_prefill_workspace_bytes(...) bytes, or None to
+    allocate one here."""
     L = _lib.load()
     desc = _cache_desc(k_cache)
     if v_cache.shape != k_cache.shape:
@@ -284,17 +306,22 @@ def paged_attn_chunked_prefill(q: torch.Tensor, k_cache: torch.Tensor, v_cache: 
     B, C, n_q, d = q.shape
     if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, C, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, C, n_q, d), out_dtype, q, stream)
     if out.shape != q.shape or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][chunk_len][n_q][d] in a supported dtype")
+    if workspace is None and B > 0 and C > 0:
+        need = int(L.pa_chunked_prefill_workspace_bytes(B, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = _alloc(need, torch.uint8, q, stream)
     dt = k_cache.dtype
     _check("pa_paged_attn_chunked_prefill", L.pa_paged_attn_chunked_prefill(
         _dev(q, "q", dt), B, C, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
-        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
         _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
         _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
-        _DTYPE[out.dtype], _stream(q, stream)))
+        _DTYPE[out.dtype], *_workspace_args(workspace), _stream(q, stream)))
     return out
 
 
@@ -318,12 +345,12 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
     maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, R, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, R, n_q, d), out_dtype, q, stream)
     if out.shape != q.shape or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][q_rows][n_q][d] in a supported dtype")
     need = int(L.pa_decode_multi_workspace_bytes(B, R, n_q, maxb, ctypes.byref(desc)))
     if need and workspace is None:
-        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        workspace = _alloc(need, torch.uint8, q, stream)
     ws_ptr, ws_bytes = _workspace_args(workspace)
     dt = k_cache.dtype
     _check("pa_paged_attn_decode_multi", L.pa_paged_attn_decode_multi(
@@ -412,13 +439,13 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
     maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, n_q, d), out_dtype, q, stream)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
     if workspace is None:
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc(need, torch.uint8, q, stream)
     ws_ptr, ws_bytes = _workspace_args(workspace)
     _check("pa_paged_attn_decode_quant", L.pa_paged_attn_decode_quant(
         _dev(q, "q"), _DTYPE[q.dtype], B, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
@@ -462,13 +489,13 @@ def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: 
         raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
     maxb = block_table.shape[1]
     if out is None:
-        out = torch.empty((B, n_q, d), dtype=out_dtype, device=q.device)
+        out = _alloc((B, n_q, d), out_dtype, q, stream)
     if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
         raise ValueError("out must be [B][n_q][d] in a supported dtype")
     if workspace is None:
         need = int(L.pa_decode_workspace_bytes(B, n_q, maxb, ctypes.byref(desc)))
         if need:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            workspace = _alloc(need, torch.uint8, q, stream)
     ws_ptr, ws_bytes = _workspace_args(workspace)
     _check("pa_paged_attn_decode_quant_append", L.pa_paged_attn_decode_quant_append(
         _dev(q, "q"), _dev(k_new, "k_new"), _dev(v_new, "v_new"), _DTYPE[q.dtype],

@@ -22,6 +22,7 @@ EXPORTS = (
     "pa_paged_attn_decode_multi",
     "pa_prefill_workspace_bytes",
     "pa_paged_attn_prefill",
+    "pa_chunked_prefill_workspace_bytes",
     "pa_paged_attn_chunked_prefill",
     "pa_kv_append_quant",
     "pa_paged_attn_decode_quant",
@@ -85,8 +86,10 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32,
                                         ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_prefill.restype = ctypes.c_int
+    L.pa_chunked_prefill_workspace_bytes.argtypes = [i32, i32, cd]
+    L.pa_chunked_prefill_workspace_bytes.restype = sz
     L.pa_paged_attn_chunked_prefill.argtypes = [vp, i32, i32, i32, vp, vp, cd, vp, i32, vp,
-                                                ctypes.c_float, i32, vp, vp, ctypes.c_int, vp]
+                                                ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_chunked_prefill.restype = ctypes.c_int
     L.pa_kv_append_quant.argtypes = [vp, vp, ctypes.c_int, vp, i32, vp, vp, vp, vp, cd, vp]
     L.pa_kv_append_quant.restype = ctypes.c_int

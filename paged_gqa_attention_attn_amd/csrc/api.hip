@@ -55,6 +55,22 @@ bool is_quant(pa_dtype d) { return d == PA_FP8_E4M3 || d == PA_INT8; }
 
 pa::Elem to_elem(pa_dtype d) { return static_cast<pa::Elem>(static_cast<int>(d)); }
 
+constexpr float kLog2e = 1.4426950408889634f;
+
+// The scale multiplying q.k, as the kernels take it: a positive factor |scale| log2(e)
+// and a fold of q's words ((word & q_and) ^ q_xor at load). A negative scale flips
+// the sign bits of q, which negates every q.k exactly; a zero scale zeroes q, so
+// every score is exactly 0 (the product of 0 and a finite q.k) and the factor is
+// an arbitrary positive one. Non-finite scales are rejected.
+template <class Args> int fold_scale(float scale, pa_dtype q_dtype, Args* a) {
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
+    const uint32_t sign = q_dtype == PA_F32 ? 0x80000000u : 0x80008000u;
+    a->q_and = scale == 0.f ? 0u : ~0u;
+    a->q_xor = scale < 0.f ? sign : 0u;
+    a->scale_log2 = scale == 0.f ? kLog2e : std::fabs(scale) * kLog2e;
+    return PA_OK;
+}
+
 std::atomic<int32_t> g_partition_tokens{0};
 
 constexpr int kBlockSize = 16;
@@ -405,14 +421,23 @@ std::mutex g_ws_mu;
 void* g_default_ws = nullptr;       // set by pa_set_workspace (caller-owned)
 size_t g_default_ws_bytes = 0;
 std::unordered_map<int, std::pair<void*, size_t>> g_lib_ws;   // device -> library-owned buffer
+std::vector<void*> g_retired_ws;    // superseded library buffers, kept until the process ends
 
 // A workspace of at least `need` bytes when the call passed none: the one set by
 // pa_set_workspace if it is large enough, else the library's own for the current
-// device (allocated or grown here, kept until the process ends).
-int resolve_workspace(size_t need, void** ws) {
-    std::lock_guard<std::mutex> lock(g_ws_mu);
+// device, allocated or grown here. A buffer that a larger one replaces is never
+// freed: a call on another thread may hold its address and not have enqueued its
+// kernels yet, and kernels enqueued earlier may still be running on it. Growth at
+// least doubles, so at most log2 of the largest size such buffers exist per device.
+// `lock` comes back holding the workspace mutex; the caller keeps it until it has
+// enqueued every kernel that uses the buffer, so that calls from several threads
+// on one stream cannot interleave their kernels on the shared buffer (a decode
+// call's partition kernel and merge kernel, for instance).
+int resolve_workspace(size_t need, void** ws, std::unique_lock<std::mutex>* lock) {
+    std::unique_lock<std::mutex> l(g_ws_mu);
     if (g_default_ws && g_default_ws_bytes >= need) {
         *ws = g_default_ws;
+        *lock = std::move(l);
         return PA_OK;
     }
     int dev = 0;
@@ -420,17 +445,15 @@ int resolve_workspace(size_t need, void** ws) {
     if (e != hipSuccess) return hip_fail(e, "workspace: hipGetDevice");
     auto& slot = g_lib_ws[dev];
     if (slot.second < need) {
-        if (slot.first) {
-            e = hipFree(slot.first);   // synchronises the device: earlier users are done
-            slot = {nullptr, 0};
-            if (e != hipSuccess) return hip_fail(e, "workspace: hipFree");
-        }
+        const size_t bytes = std::max(need, 2 * slot.second);
         void* p = nullptr;
-        e = hipMalloc(&p, need);
+        e = hipMalloc(&p, bytes);
         if (e != hipSuccess) return hip_fail(e, "workspace: hipMalloc");
-        slot = {p, need};
+        if (slot.first) g_retired_ws.push_back(slot.first);
+        slot = {p, bytes};
     }
     *ws = slot.first;
+    *lock = std::move(l);
     return PA_OK;
 }
 
@@ -438,7 +461,7 @@ int resolve_workspace(size_t need, void** ws) {
 
 extern "C" {
 
-int32_t pa_version(void) { return 203; }
+int32_t pa_version(void) { return 300; }
 
 const char* pa_last_error(void) { return g_err; }
 
@@ -545,8 +568,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     if (rc) return rc;
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
-    if (!(scale > 0.f) || !std::isfinite(scale))
-        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
@@ -569,9 +591,10 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     Plan pl;
     make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
     const size_t need = plan_bytes(pl);
+    std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (need > 0) {
         if (!workspace) {
-            rc = resolve_workspace(need, &workspace);
+            rc = resolve_workspace(need, &workspace, &ws_lock);
             if (rc) return rc;
         } else if (workspace_bytes < need) {
             return fail(PA_ERR_INVALID_ARG, "decode: workspace of %zu bytes required (got %zu)", need,
@@ -612,7 +635,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     a.nparts_max = pl.nparts_max;
     a.ring = pl.ring;
     a.mfma = pl.mfma;
-    a.scale_log2 = scale * 1.4426950408889634f;  // log2(e): exp(x) = 2^(x log2 e)
+    fold_scale(scale, cache->dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;
     a.window = window;
@@ -682,8 +705,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (n_q % n_kv != 0)
         return fail(PA_ERR_INVALID_ARG, "n_q (%d) is not a multiple of n_kv (%d)", n_q, n_kv);
     if (causal != 0 && causal != 1) return fail(PA_ERR_INVALID_ARG, "causal must be 0 or 1");
-    if (!(scale > 0.f) || !std::isfinite(scale))
-        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
@@ -707,14 +729,15 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.n_kv = n_kv;
     a.group = n_q / n_kv;
     a.causal = causal;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    fold_scale(scale, dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
     a.window = window;
     a.alibi = alibi_slopes;
+    std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (prefill_stages(dtype) && stage_grid_fits(batch, n_kv)) {
         const size_t need = prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
         if (!workspace) {
-            const int rc = resolve_workspace(need, &workspace);
+            const int rc = resolve_workspace(need, &workspace, &ws_lock);
             if (rc != PA_OK) return rc;
         } else if (workspace_bytes < need) {
             return fail(PA_ERR_INVALID_ARG, "prefill: workspace of %zu bytes required (got %zu)", need,
@@ -754,8 +777,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
     if (q_rows < 1) return fail(PA_ERR_INVALID_ARG, "q_rows %d must be positive", q_rows);
-    if (!(scale > 0.f) || !std::isfinite(scale))
-        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
@@ -767,9 +789,10 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: block_table and context_lens must be 4-byte aligned");
     const MultiPlan pl = multi_plan(batch, q_rows, n_q, span_blocks(max_blocks_per_seq, q_rows, window), cache);
+    std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (pl.bytes > 0) {
         if (!workspace) {
-            rc = resolve_workspace(pl.bytes, &workspace);
+            rc = resolve_workspace(pl.bytes, &workspace, &ws_lock);
             if (rc) return rc;
         } else if (workspace_bytes < pl.bytes) {
             return fail(PA_ERR_INVALID_ARG, "multi-row decode: workspace of %zu bytes required (got %zu)",
@@ -804,7 +827,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     a.group = n_q / cache->n_kv;
     a.blocks_per_wave = pl.blocks_per_wave;
     a.nparts_max = pl.nparts_max;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    fold_scale(scale, cache->dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = q_rows;
     a.window = window;
@@ -829,12 +852,21 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
     return PA_OK;
 }
 
+size_t pa_chunked_prefill_workspace_bytes(int32_t batch, int32_t max_blocks_per_seq,
+                                          const pa_cache_desc* cache) {
+    if (check_cache(cache) != PA_OK || batch <= 0 || max_blocks_per_seq <= 0) return 0;
+    if (!prefill_stages(cache->dtype) || !stage_grid_fits(batch, cache->n_kv)) return 0;
+    const size_t need = chunked_stage_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
+    return need <= kChunkStageCap ? need : 0;
+}
+
 int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_len, int32_t n_q,
                                   const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                   const int32_t* block_table, int32_t max_blocks_per_seq,
                                   const int32_t* context_lens, float scale, int32_t window,
                                   const float* alibi_slopes,
-                                  void* out, pa_dtype out_dtype, void* stream) {
+                                  void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
@@ -842,8 +874,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
     if (chunk_len < 0) return fail(PA_ERR_INVALID_ARG, "chunk_len %d < 0", chunk_len);
-    if (!(scale > 0.f) || !std::isfinite(scale))
-        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
@@ -873,7 +904,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     a.n_kv = cache->n_kv;
     a.group = n_q / cache->n_kv;
     a.causal = 1;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    fold_scale(scale, cache->dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
     a.block_table = block_table;
     a.context_lens = context_lens;
@@ -881,16 +912,21 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     a.num_blocks = cache->num_blocks;
     a.window = window;
     a.alibi = alibi_slopes;
-    if (prefill_stages(cache->dtype) && stage_grid_fits(batch, cache->n_kv)) {
-        const size_t need = chunked_stage_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
-        if (need <= kChunkStageCap) {
-            void* ws = nullptr;
-            rc = resolve_workspace(need, &ws);
+    const size_t need = pa_chunked_prefill_workspace_bytes(batch, max_blocks_per_seq, cache);
+    std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
+    if (need > 0) {
+        if (!workspace) {
+            rc = resolve_workspace(need, &workspace, &ws_lock);
             if (rc != PA_OK) return rc;
-            a.v16 = ws;
-            a.v16_ok = static_cast<uint8_t*>(ws) +
-                       chunked_stage_v_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
+        } else if (workspace_bytes < need) {
+            return fail(PA_ERR_INVALID_ARG, "chunked prefill: workspace of %zu bytes required (got %zu)", need,
+                        workspace_bytes);
         }
+        if (!aligned16(workspace))
+            return fail(PA_ERR_INVALID_ARG, "chunked prefill: workspace must be 16-byte aligned");
+        a.v16 = workspace;
+        a.v16_ok = static_cast<uint8_t*>(workspace) +
+                   chunked_stage_v_bytes(batch, max_blocks_per_seq, cache->n_kv, cache->head_dim);
     }
     const hipError_t e = pa::launch_prefill(a, to_elem(cache->dtype), cache->head_dim,
                                             static_cast<hipStream_t>(stream));
@@ -963,8 +999,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
         return fail(PA_ERR_UNSUPPORTED, "decode_quant: q must be bf16 or f16");
     if (out_dtype != PA_F32 && out_dtype != q_dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or q_dtype");
-    if (!(scale > 0.f) || !std::isfinite(scale))
-        return fail(PA_ERR_INVALID_ARG, "scale must be positive and finite");
+    if (!std::isfinite(scale)) return fail(PA_ERR_INVALID_ARG, "scale must be finite");
     if (window < 0) return fail(PA_ERR_INVALID_ARG, "window %d < 0", window);
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
@@ -988,9 +1023,10 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     Plan pl;
     make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
     const size_t need = plan_bytes(pl);
+    std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (need > 0) {
         if (!workspace) {
-            rc = resolve_workspace(need, &workspace);
+            rc = resolve_workspace(need, &workspace, &ws_lock);
             if (rc) return rc;
         } else if (workspace_bytes < need) {
             return fail(PA_ERR_INVALID_ARG, "decode_quant: workspace of %zu bytes required (got %zu)", need,
@@ -1033,7 +1069,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     a.nparts_max = pl.nparts_max;
     a.ring = pl.ring;
     a.mfma = 1;
-    a.scale_log2 = scale * 1.4426950408889634f;
+    fold_scale(scale, q_dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
     a.q_rows = 1;
     a.window = window;

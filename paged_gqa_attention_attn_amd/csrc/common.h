@@ -37,6 +37,15 @@ __device__ __forceinline__ int window_first(int ctx, int rows, int window) {
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// A 16-byte chunk of q with the scale's sign folded in: every word becomes
+// (word & q_and) ^ q_xor, which zeroes q for a zero scale (every score is then
+// exactly 0) or flips its sign bits for a negative one (q.k negated exactly), so
+// the kernels always multiply scores by a positive factor.
+__device__ __forceinline__ uint4 q_fold(uint4 v, uint32_t q_and, uint32_t q_xor) {
+    return make_uint4((v.x & q_and) ^ q_xor, (v.y & q_and) ^ q_xor, (v.z & q_and) ^ q_xor,
+                      (v.w & q_and) ^ q_xor);
+}
+
 // acc + sum over the chunk of a[i] * b[i], accumulated in fp32.
 template <class E> __device__ __forceinline__ float chunk_dot(uint4 a, uint4 b, float acc);
 

@@ -98,8 +98,8 @@ __global__ __launch_bounds__(64 * MAX_WAVES, MIN_WAVES_PER_SIMD) void decode_par
     for (int hh = 0; hh < GW; ++hh) {
         const uint4* qrow =
             reinterpret_cast<const uint4*>((const char*)p.q + (int64_t)(b * p.n_q + h0 + hh) * ROW);
-        qv[hh][0] = qrow[c];
-        qv[hh][1] = qrow[c + LPT];
+        qv[hh][0] = q_fold(qrow[c], p.q_and, p.q_xor);
+        qv[hh][1] = q_fold(qrow[c + LPT], p.q_and, p.q_xor);
     }
     // Lane k holds the physical id of logical block blk0 + k (the table row is
     // read up to the wave's share or the row's end, whatever the context).

@@ -143,7 +143,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_mfma_kernel(const De
             // B operand of S^T: dims 32 kk + 8 grp .. +8 of column col's q row (the same
             // dims the K operand below takes, which is all the product needs).
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < HW) v = *reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2);
+            if (col < HW) v = q_fold(*reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2), p.q_and, p.q_xor);
             qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
         }
     }

@@ -92,8 +92,8 @@ __global__ __launch_bounds__(64 * WAVES, 1) void decode_multi_kernel(const Decod
     u32x4_t qreg[KK];
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        const uint4 x = *reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.q) + qrow * D +
-                                                        16 * kk + 8 * half);
+        const uint4 x = q_fold(*reinterpret_cast<const uint4*>(reinterpret_cast<const S*>(p.q) + qrow * D +
+                                                               16 * kk + 8 * half), p.q_and, p.q_xor);
         qreg[kk] = u32x4_t{x.x, x.y, x.z, x.w};
     }
     // Lane k holds the physical id of logical block blk0 + k.

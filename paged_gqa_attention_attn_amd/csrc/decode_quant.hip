@@ -150,7 +150,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
-            if (col < HW) v = *reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2);
+            if (col < HW) v = q_fold(*reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2), p.q_and, p.q_xor);
             qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
         }
     }

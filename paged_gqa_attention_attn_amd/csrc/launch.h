@@ -30,7 +30,11 @@ struct DecodeArgs {
     int32_t blocks_per_wave;     // 16-token blocks one wave takes per partition
     int32_t nparts_max;          // grid.x
     int32_t ring;                // blocks in flight per wave (LDS ring depth: 1 or 2)
-    float scale_log2;            // scale * log2(e)
+    float scale_log2;            // |scale| * log2(e) (log2(e) when scale is 0)
+    // Every 32-bit word of q is taken as (word & q_and) ^ q_xor when it is loaded:
+    // all ones and 0 for a positive scale, 0 and 0 for scale 0 (every score is then
+    // exactly 0), the sign bits for a negative scale (q k negated exactly).
+    uint32_t q_and, q_xor;
     int32_t out_f32;             // 1: fp32 output, 0: output in the input type
     // Fused append (all null for a plain decode): new token of each sequence.
     const void* k_new;           // [B][n_kv][D]
@@ -89,7 +93,8 @@ struct PrefillArgs {
     int32_t batch, seq_len, n_q, n_kv;
     int32_t group;
     int32_t causal;
-    float scale_log2;
+    float scale_log2;             // as for DecodeArgs, with q_and / q_xor applied to q
+    uint32_t q_and, q_xor;
     int32_t out_f32;
     // Paged keys (block_table != nullptr): sequence b has context_lens[b] keys in the
     // pools and its S query rows are its last S positions.

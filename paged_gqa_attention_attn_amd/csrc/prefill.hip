@@ -158,7 +158,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
         if (my_q < S_len) {
-            const uint4 v = *reinterpret_cast<const uint4*>(Qg + (int64_t)my_q * q_stride + 16 * kk + 8 * half);
+            const uint4 v = q_fold(*reinterpret_cast<const uint4*>(Qg + (int64_t)my_q * q_stride + 16 * kk + 8 * half),
+                                   p.q_and, p.q_xor);
             qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
         } else {
             qreg[kk] = u32x4_t{0u, 0u, 0u, 0u};

@@ -44,7 +44,7 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 203
+    assert L.pa_version() == 300
 
 
 def decode(L, **kw):
@@ -70,9 +70,9 @@ def decode(L, **kw):
     (dict(out=MISALIGNED), INVALID, "aligned"),
     (dict(bt=FAKE + 2), INVALID, "aligned"),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
-    (dict(scale=float("nan")), INVALID, "scale"),
-    (dict(scale=0.0), INVALID, "positive"),
-    (dict(scale=-0.125), INVALID, "positive"),
+    (dict(scale=float("nan")), INVALID, "finite"),
+    (dict(scale=float("inf")), INVALID, "finite"),
+    (dict(scale=float("-inf")), INVALID, "finite"),
     (dict(window=-1), INVALID, "window"),
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),   # too small (NULL: library's own)
     (dict(maxb=8192, window=4096, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
@@ -193,8 +193,8 @@ def prefill(L, **kw):
     (dict(out=None), INVALID),
     (dict(k=MISALIGNED), INVALID),
     (dict(out_dtype=_lib.PA_F16), UNSUPPORTED),
-    (dict(scale=0.0), INVALID),
-    (dict(scale=-1.0), INVALID),
+    (dict(scale=float("nan")), INVALID),
+    (dict(scale=float("-inf")), INVALID),
     (dict(window=-1), INVALID),
     (dict(window=8, causal=0), INVALID),    # a window is a causal band
     (dict(alibi=FAKE + 2), INVALID),
@@ -232,11 +232,13 @@ def test_prefill_empty_is_a_noop(L):
 
 def chunked(L, **kw):
     a = dict(q=FAKE, B=2, C=16, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
-             scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, stream=None)
+             scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0,
+             stream=None)
     a.update(kw)
     return L.pa_paged_attn_chunked_prefill(a["q"], a["B"], a["C"], a["n_q"], a["k"], a["v"],
                                            a["cache"], a["bt"], a["maxb"], a["ctx"], a["scale"],
-                                           a["window"], a["alibi"], a["out"], a["out_dtype"], a["stream"])
+                                           a["window"], a["alibi"], a["out"], a["out_dtype"], a["ws"],
+                                           a["ws_bytes"], a["stream"])
 
 
 @pytest.mark.parametrize("kw,code,msg", [
@@ -245,7 +247,7 @@ def chunked(L, **kw):
     (dict(cache=desc(d=96)), UNSUPPORTED, "head_dim"),
     (dict(C=-1), INVALID, "chunk_len"),
     (dict(n_q=7), INVALID, "multiple"),
-    (dict(scale=0.0), INVALID, "positive"),
+    (dict(scale=float("inf")), INVALID, "finite"),
     (dict(q=None), INVALID, "NULL"),
     (dict(out=MISALIGNED), INVALID, "aligned"),
     (dict(ctx=FAKE + 2), INVALID, "aligned"),
@@ -264,6 +266,24 @@ def test_chunked_prefill_empty_is_a_noop(L):
     assert chunked(L, B=0) == PA_OK
 
 
+def test_chunked_prefill_workspace(L, monkeypatch):
+    # bf16: an f16 copy of the V blocks the call may read ([B][max_blocks][n_kv][16][d]),
+    # then one flag byte per (sequence, KV head, block), each part rounded up to 16 bytes;
+    # nothing past 256 MiB, nothing for f16 caches or with PA_PREFILL_STAGE_V=0.
+    assert L.pa_chunked_prefill_workspace_bytes(2, 256, desc(n_kv=8)) == 2 * 256 * 8 * 16 * 128 * 2 + 4096
+    assert L.pa_chunked_prefill_workspace_bytes(1, 3, desc(n_kv=1, d=64)) == 3 * 16 * 64 * 2 + 16
+    assert L.pa_chunked_prefill_workspace_bytes(64, 8192, desc(n_kv=8)) == 0
+    assert L.pa_chunked_prefill_workspace_bytes(2, 256, desc(n_kv=8, dtype=_lib.PA_F16)) == 0
+    assert L.pa_chunked_prefill_workspace_bytes(0, 256, desc()) == 0
+    need = L.pa_chunked_prefill_workspace_bytes(2, 4, desc())
+    assert chunked(L, ws=FAKE, ws_bytes=need - 1) == INVALID
+    assert "workspace" in _lib.last_error()
+    assert chunked(L, ws=FAKE + 8, ws_bytes=need) == INVALID
+    assert "aligned" in _lib.last_error()
+    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    assert L.pa_chunked_prefill_workspace_bytes(2, 256, desc(n_kv=8)) == 0
+
+
 def multi(L, **kw):
     a = dict(q=FAKE, B=2, R=4, n_q=8, k=FAKE, v=FAKE, cache=desc(), bt=FAKE, maxb=4, ctx=FAKE,
              scale=0.125, window=0, alibi=None, out=FAKE, out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
@@ -278,7 +298,7 @@ def multi(L, **kw):
     (dict(cache=desc(dtype=_lib.PA_F32)), UNSUPPORTED, "bf16 and f16"),
     (dict(R=0), INVALID, "q_rows"),
     (dict(n_q=7), INVALID, "multiple"),
-    (dict(scale=-1.0), INVALID, "positive"),
+    (dict(scale=float("nan")), INVALID, "finite"),
     (dict(v=None), INVALID, "NULL"),
     (dict(q=MISALIGNED), INVALID, "aligned"),
     (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
@@ -335,7 +355,7 @@ def decode_quant(L, **kw):
     (dict(vs=FAKE + 4), INVALID, "aligned"),
     (dict(cache=desc(dtype=INT8, d=96)), UNSUPPORTED, "head_dim"),
     (dict(n_q=7), INVALID, "multiple"),
-    (dict(scale=0.0), INVALID, "positive"),
+    (dict(scale=float("nan")), INVALID, "finite"),
     (dict(window=-2), INVALID, "window"),
     (dict(alibi=FAKE + 2), INVALID, "alibi_slopes"),
 ])
