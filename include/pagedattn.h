@@ -162,6 +162,30 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
                          pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * paged_attn_decode_noalloc -- pa_paged_attn_decode for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops and
+ * harnesses that forbid hipMalloc. Same arguments, kernels and results (bit for
+ * bit) as pa_paged_attn_decode, without the workspace arguments: when contexts
+ * are split into partitions, the partial results go to a fixed device array of
+ * PA_NOALLOC_SCRATCH_BYTES bytes inside the library, one per GPU, that each GPU
+ * holds from the library's first use there until the process ends. The call
+ * allocates nothing (no hipMalloc, hipFree or allocating library routine).
+ *   Returns PA_ERR_INVALID_ARG, enqueuing nothing, when the partials would exceed
+ * that size (pa_decode_workspace_bytes gives the need for the same arguments).
+ * Every call on one GPU shares that GPU's array: calls that overlap on the GPU
+ * (on different streams) race and their results are unspecified. Calls from
+ * several host threads on one stream are safe: each enqueues its kernels while
+ * holding the array's lock. The array keeps whatever the last call left; no part
+ * of it needs to start at zero (a merge reads only what its own call wrote).
+ */
+#define PA_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int pa_paged_attn_decode_noalloc(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
+                                 const void* v_cache, const pa_cache_desc* cache,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, float scale, int32_t window,
+                                 const float* alibi_slopes, void* out, pa_dtype out_dtype, void* stream);
+
+/*
  * paged_attn_decode_append -- one decode step in a single launch: kv_append of
  * one new token per sequence followed by paged_attn_decode. [IW] "Decode 阶段维度
  * 流转": write the new K/V at position cache_len, increment it, then attend over

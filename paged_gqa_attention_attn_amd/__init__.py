@@ -28,7 +28,7 @@ import torch
 from . import _lib
 from ._lib import CacheDesc, LibraryNotBuilt
 
-__all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_append", "paged_attn_prefill",
+__all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_append", "paged_attn_prefill",
            "paged_attn_chunked_prefill", "paged_attn_decode_multi", "kv_append_quant",
            "paged_attn_decode_quant", "paged_attn_decode_quant_append", "quant_decode_workspace_bytes",
            "prefill_workspace_bytes", "chunked_prefill_workspace_bytes",
@@ -185,6 +185,32 @@ def paged_attn_decode(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Ten
         _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
         _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def paged_attn_decode_noalloc(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                              block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                              out: torch.Tensor, stream=None, window: int = 0,
+                              alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
+    """paged_attn_decode into the caller's ``out`` [B][n_q][d] with no allocation at all:
+    split-context partials go to the library's fixed per-GPU scratch array."""
+    L = _lib.load()
+    desc = _cache_desc(k_cache)
+    if v_cache.shape != k_cache.shape:
+        raise ValueError("k_cache and v_cache shapes differ")
+    B, n_q, d = q.shape
+    if d != k_cache.shape[3]:
+        raise ValueError("q head_dim differs from the cache")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    if out.shape != (B, n_q, d) or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][n_q][d] in a supported dtype")
+    dt = k_cache.dtype
+    _check("pa_paged_attn_decode_noalloc", L.pa_paged_attn_decode_noalloc(
+        _dev(q, "q", dt), B, n_q, _dev(k_cache, "k_cache", dt), _dev(v_cache, "v_cache", dt),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), block_table.shape[1],
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"), _DTYPE[out.dtype], _stream(q, stream)))
     return out
 
 

@@ -17,6 +17,7 @@ EXPORTS = (
     "pa_kv_append",
     "pa_decode_workspace_bytes",
     "pa_paged_attn_decode",
+    "pa_paged_attn_decode_noalloc",
     "pa_paged_attn_decode_append",
     "pa_decode_multi_workspace_bytes",
     "pa_paged_attn_decode_multi",
@@ -73,6 +74,9 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_decode.argtypes = [vp, i32, i32, vp, vp, cd, vp, i32, vp, ctypes.c_float, i32, vp,
                                        vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode.restype = ctypes.c_int
+    L.pa_paged_attn_decode_noalloc.argtypes = [vp, i32, i32, vp, vp, cd, vp, i32, vp, ctypes.c_float, i32,
+                                               vp, vp, ctypes.c_int, vp]
+    L.pa_paged_attn_decode_noalloc.restype = ctypes.c_int
     L.pa_paged_attn_decode_append.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, cd, vp, i32, vp,
                                               ctypes.c_float, i32, vp, vp, ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_append.restype = ctypes.c_int

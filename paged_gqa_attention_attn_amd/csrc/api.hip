@@ -550,6 +550,38 @@ size_t pa_decode_workspace_bytes(int32_t batch, int32_t n_q, int32_t max_blocks_
 
 namespace {
 
+// ---- the no-allocation decode's scratch ---------------------------------------------
+// Split-context partials of pa_paged_attn_decode_noalloc live in this file-scope
+// device array instead of an allocated workspace. Each GPU the library runs on
+// holds its own copy from the moment the code object is loaded there until the
+// process ends. In host code `scratch` names a host-side stand-in, never the
+// device memory: the device address comes from hipGetSymbolAddress, once per
+// device with that device current, and only that address is handed to kernels.
+constexpr size_t kNoAllocScratchBytes = PA_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+std::mutex g_scratch_mu;                       // guards the map; held while a call enqueues
+std::unordered_map<int, void*> g_scratch_ptr;  // device -> its copy of `scratch`
+
+// Device address of the current device's `scratch`; caller holds g_scratch_mu.
+int scratch_address(void** ptr) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipGetDevice");
+    auto it = g_scratch_ptr.find(dev);
+    if (it != g_scratch_ptr.end()) {
+        *ptr = it->second;
+        return PA_OK;
+    }
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "decode_noalloc: hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(PA_ERR_HIP, "decode_noalloc: no device address for the scratch array");
+    g_scratch_ptr.emplace(dev, p);
+    *ptr = p;
+    return PA_OK;
+}
+
 struct FusedAppend {
     const void* k_new;
     const void* v_new;
@@ -563,7 +595,7 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
                 const int32_t* context_lens, float scale, int32_t window,
                 const float* alibi_slopes, void* out,
                 pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream,
-                const FusedAppend* fa) {
+                const FusedAppend* fa, bool noalloc = false) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
@@ -592,7 +624,17 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
     make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
     const size_t need = plan_bytes(pl);
     std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
-    if (need > 0) {
+    if (need > 0 && noalloc) {
+        // Partials go to this device's scratch array; nothing is allocated.
+        if (need > kNoAllocScratchBytes)
+            return fail(PA_ERR_INVALID_ARG,
+                        "decode_noalloc: %zu bytes of split-context partials needed, more than the "
+                        "%zu-byte scratch (pa_decode_workspace_bytes gives the need)",
+                        need, kNoAllocScratchBytes);
+        ws_lock = std::unique_lock<std::mutex>(g_scratch_mu);
+        rc = scratch_address(&workspace);
+        if (rc) return rc;
+    } else if (need > 0) {
         if (!workspace) {
             rc = resolve_workspace(need, &workspace, &ws_lock);
             if (rc) return rc;
@@ -666,6 +708,16 @@ int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* 
     return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
                        context_lens, scale, window, alibi_slopes, out, out_dtype, workspace, workspace_bytes,
                        stream, nullptr);
+}
+
+int pa_paged_attn_decode_noalloc(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
+                                 const void* v_cache, const pa_cache_desc* cache,
+                                 const int32_t* block_table, int32_t max_blocks_per_seq,
+                                 const int32_t* context_lens, float scale, int32_t window,
+                                 const float* alibi_slopes, void* out, pa_dtype out_dtype, void* stream) {
+    return decode_impl(q, batch, n_q, k_cache, v_cache, cache, block_table, max_blocks_per_seq,
+                       context_lens, scale, window, alibi_slopes, out, out_dtype, nullptr, 0, stream,
+                       nullptr, true);
 }
 
 int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_new,
