@@ -134,6 +134,10 @@ def parse_args(argv=None):
                    help="decode and prefill workloads: add the ALiBi bias with geometric slopes")
     p.add_argument("--unfused", action="store_true",
                    help="decode step as two launches (kv_append, then decode) instead of one")
+    p.add_argument("--no-sub-records", action="store_true",
+                   help="default workload only: skip the sub-records of the other workloads")
+    p.add_argument("--sub-cpu-seconds", type=float, default=3.0,
+                   help="target CPU time of each sub-record's oracle baseline")
     return p.parse_args(argv)
 
 
@@ -144,24 +148,57 @@ def _stored(t):
     return t.numpy() if t.dtype == torch.float32 else t.view(torch.int16).numpy().view(np.uint16)
 
 
-def cpu_baseline_decode(case, target_s: float, window: int = 0, alibi=None):
-    """Time the CPU oracle on whole sequences of one input set (all heads)."""
+def host_cpu_model() -> str:
+    """Model name of the host CPU, from /proc/cpuinfo."""
+    try:
+        for line in Path("/proc/cpuinfo").read_text().splitlines():
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _cpu_record(value, unit, sample, one_value, one_sample, digits=6):
+    import oracle
+    return {
+        "value": round(value, digits), "unit": unit, "cores": oracle.max_threads(), "kind": "oracle",
+        "sample": sample,
+        "one_thread": {"value": round(one_value, digits), "unit": unit, "cores": 1, "sample": one_sample},
+        "host_cpu": host_cpu_model(),
+    }
+
+
+def cpu_baseline_decode(case, target_s: float, window: int = 0, alibi=None, quant=None):
+    """Time the CPU oracle on whole sequences of one input set (all query heads), on
+    all host threads and on one. ``quant``: (codes fmt, q dtype, k_scale, v_scale)."""
     import numpy as np
 
     import oracle
     from paged_gqa_attention_attn_amd import accounting as acc
 
-    kp, vp = _stored(case.k_pool), _stored(case.v_pool)
+    if quant is None:
+        kp, vp = _stored(case.k_pool), _stored(case.v_pool)
+        kw = {}
+        dtype = case.dtype
+    else:
+        dtype, q_dtype, ks, vs = quant
+        kp, vp = case.k_pool.cpu().contiguous().numpy(), case.v_pool.cpu().contiguous().numpy()
+        kw = dict(q_dtype=q_dtype, k_scale=ks, v_scale=vs)
     q = _stored(case.q)
     bt = case.block_table.cpu().numpy()
     ctx = case.context_lens.cpu().numpy()
-    elem = acc.ELEM_BYTES[case.dtype]
 
-    def run(seqs):
+    def kv_bytes(seqs):
+        if quant is None:
+            return acc.decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim, acc.ELEM_BYTES[dtype], window)
+        return acc.quant_decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim)
+
+    def run(seqs, threads=0):
         sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
         t0 = time.perf_counter()
-        oracle.decode(q, kp, vp, case.dtype, bt, ctx, case.scale, sel=sel, window=window,
-                      alibi=alibi)
+        oracle.decode(q, kp, vp, dtype, bt, ctx, case.scale, sel=sel, window=window, alibi=alibi,
+                      n_threads=threads, **kw)
         return time.perf_counter() - t0
 
     t1 = run([0])
@@ -170,17 +207,24 @@ def cpu_baseline_decode(case, target_s: float, window: int = 0, alibi=None):
     t_all = run(seqs)
     reps = max(1, int(target_s / max(t_all, 1e-6))) if n == case.batch else 1
     dt = t_all + sum(run(seqs) for _ in range(reps - 1))
-    kv = reps * acc.decode_kv_bytes(ctx[seqs], case.n_kv, case.head_dim, elem, window)
-    return {
-        "value": round(kv / dt / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
-        "kind": "oracle",
-        "sample": f"fp64 oracle decode of {n} of {case.batch} sequences (all {case.n_q} query "
-                  f"heads), {reps} pass(es), {kv} KV bytes in {dt:.2f} s",
-    }
+    kv = reps * kv_bytes(seqs)
+    # One thread: whole sequences, about a quarter of the budget.
+    t1s = run([0], threads=1)
+    n1 = int(min(case.batch, max(1, (target_s / 4) // max(t1s, 1e-6))))
+    seqs1 = list(range(n1))
+    dt1 = t1s if n1 == 1 else run(seqs1, threads=1)
+    kv1 = kv_bytes(seqs1)
+    what = f"{dtype} codes" if quant is not None else dtype
+    return _cpu_record(
+        kv / dt / 1e9, "GB/s",
+        f"fp64 oracle decode over a {what} cache of {n} of {case.batch} sequences (all {case.n_q} query "
+        f"heads), {reps} pass(es), {kv} KV bytes in {dt:.2f} s",
+        kv1 / dt1 / 1e9, f"{n1} sequence(s), {kv1} KV bytes in {dt1:.2f} s")
 
 
 def cpu_baseline_prefill(case, target_s: float, alibi=None):
-    """Time the CPU oracle on sampled causal prefill rows, scaled to TFLOP/s."""
+    """Time the CPU oracle on random causal prefill rows, scaled to TFLOP/s, on all host
+    threads and on one."""
     import numpy as np
 
     import oracle
@@ -188,11 +232,11 @@ def cpu_baseline_prefill(case, target_s: float, alibi=None):
     q, k, v = _stored(case.q), _stored(case.k), _stored(case.v)
     rng = np.random.default_rng(0)
 
-    def run(n):
+    def run(n, threads=0):
         rows = np.stack([rng.integers(0, case.batch, n), rng.integers(0, case.n_q, n),
                          rng.integers(0, case.seq_len, n)], axis=1).astype(np.int32)
         t0 = time.perf_counter()
-        oracle.prefill(q, k, v, case.dtype, True, case.scale, sel=rows, alibi=alibi)
+        oracle.prefill(q, k, v, case.dtype, True, case.scale, sel=rows, alibi=alibi, n_threads=threads)
         dt = time.perf_counter() - t0
         flops = float(4 * case.head_dim * (rows[:, 2].astype(np.int64) + 1).sum())
         return dt, flops
@@ -200,12 +244,55 @@ def cpu_baseline_prefill(case, target_s: float, alibi=None):
     dt, _ = run(64)
     n = int(max(64, min(1 << 16, 64 * target_s / max(dt, 1e-6))))
     dt, flops = run(n)
-    return {
-        "value": round(flops / dt / 1e12, 9), "unit": "TFLOP/s", "cores": oracle.max_threads(),
-        "kind": "oracle",
-        "sample": f"fp64 oracle causal prefill of {n} random (b, h, i) rows ({flops:.3e} FLOP) "
-                  f"in {dt:.2f} s",
-    }
+    dt1, _ = run(16, threads=1)
+    n1 = int(max(16, min(1 << 14, 16 * (target_s / 4) / max(dt1, 1e-6))))
+    dt1, flops1 = run(n1, threads=1)
+    return _cpu_record(flops / dt / 1e12, "TFLOP/s",
+                       f"fp64 oracle causal prefill of {n} random (b, h, i) rows ({flops:.3e} FLOP) in {dt:.2f} s",
+                       flops1 / dt1 / 1e12, f"{n1} random rows ({flops1:.3e} FLOP) in {dt1:.2f} s", digits=9)
+
+
+def cpu_baseline_chunk(c, target_s: float, unit: str):
+    """Time the CPU oracle's chunked-prefill definition (each query row at its position over
+    the paged cache, the chunk appended), on all host threads and on one. "TFLOP/s": random
+    (b, i, h) rows, counting 4 d FLOP per key a row attends to. "GB/s": whole sequences (all
+    rows and heads), counting each sequence's K/V bytes once, as the GPU rate does."""
+    import numpy as np
+
+    import oracle
+    from paged_gqa_attention_attn_amd import accounting as acc
+
+    kp, vp = _stored(c.k_pool).copy(), _stored(c.v_pool).copy()
+    oracle.kv_append(_stored(c.chunk_k), _stored(c.chunk_v), c.chunk_slots.cpu().numpy(), kp, vp)
+    q, bt, ctx = _stored(c.q), c.block_table.cpu().numpy(), c.context_lens.cpu().numpy()
+    rng = np.random.default_rng(0)
+
+    def run(n, threads=0):
+        if unit == "TFLOP/s":
+            sel = np.stack([rng.integers(0, c.batch, n), rng.integers(0, c.chunk_len, n),
+                            rng.integers(0, c.n_q, n)], axis=1).astype(np.int32)
+            keys = (ctx[sel[:, 0]].astype(np.int64) - c.chunk_len + sel[:, 1] + 1).clip(min=0)
+            work = float(4 * c.head_dim * keys.sum())
+        else:
+            n = min(n, c.batch)
+            sel = np.asarray([[b, i, h] for b in range(n) for i in range(c.chunk_len) for h in range(c.n_q)],
+                             np.int32)
+            work = float(acc.decode_kv_bytes(ctx[:n], c.n_kv, c.head_dim, acc.ELEM_BYTES[c.dtype]))
+        t0 = time.perf_counter()
+        oracle.chunked_prefill(q, kp, vp, c.dtype, bt, ctx, c.scale, sel=sel, n_threads=threads)
+        return time.perf_counter() - t0, work, n
+
+    per = 1e12 if unit == "TFLOP/s" else 1e9
+    n0 = 32 if unit == "TFLOP/s" else 1
+    dt, _, _ = run(n0)
+    dt, work, n = run(int(max(n0, min(1 << 16, n0 * target_s / max(dt, 1e-6)))))
+    dt1, _, _ = run(max(1, n0 // 4), threads=1)
+    dt1, work1, n1 = run(int(max(1, min(1 << 14, max(1, n0 // 4) * (target_s / 4) / max(dt1, 1e-6)))), threads=1)
+    what = "random (b, i, h) rows" if unit == "TFLOP/s" else f"sequences of {c.batch} (all rows and heads)"
+    kind = "FLOP" if unit == "TFLOP/s" else "KV bytes"
+    return _cpu_record(work / dt / per, unit,
+                       f"fp64 oracle, chunk rows over the paged prefix: {n} {what} ({work:.3e} {kind}) in {dt:.2f} s",
+                       work1 / dt1 / per, f"{n1} {what} ({work1:.3e} {kind}) in {dt1:.2f} s", digits=9)
 
 
 def bench_decode(args, cfg: int):
@@ -470,7 +557,7 @@ def bench_chunked_prefill(args):
     pre_ms = time_launches(lambda i: prefill(sets[i % n_sets]), args.steps)
     flops = acc.chunked_prefill_flops(c0.context_lens.cpu().tolist(), C, c0.n_q, c0.head_dim)
     achieved = flops / (pre_ms * 1e-3) / 1e12
-    return {
+    rec = {
         "metric": "chunked prefill attention over a paged prefix, TFLOP/s (+ the chunk's cache write) at 1 GPU",
         "value": round(flops / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -489,6 +576,9 @@ def bench_chunked_prefill(args):
                      "algorithmic_flops_per_launch": flops, "avg_launch_us": round(pre_ms * 1e3, 2),
                      "source_hash": source_hash("prefill")},
     }
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_chunk(c0, args.cpu_seconds, "TFLOP/s")
+    return rec
 
 
 def bench_decode_multi(args):
@@ -530,7 +620,7 @@ def bench_decode_multi(args):
     kv = acc.decode_kv_bytes([ctx] * B, c0.n_kv, c0.head_dim, 2)
     io = acc.decode_io_bytes(B * R, c0.n_q, c0.head_dim, 2, 4, c0.max_blocks_per_seq)
     achieved = (kv + io) / (dec_ms * 1e-3) / 1e9
-    return {
+    rec = {
         "metric": "multi-row paged decode (4 new tokens per sequence): KV GB/s (% HBM peak) at 1 GPU",
         "value": round(kv / (ms * 1e-3) / 1e9, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
@@ -550,36 +640,9 @@ def bench_decode_multi(args):
                      "source_hash": source_hash("decode_multi")},
         "tflops": round(4 * R * c0.n_q * c0.head_dim * ctx * B / (dec_ms * 1e-3) / 1e12, 3),
     }
-
-
-def cpu_baseline_quant(case, target_s: float):
-    """Time the CPU oracle on whole sequences of one quantised input set (all heads)."""
-    import numpy as np
-
-    import oracle
-    from paged_gqa_attention_attn_amd import accounting as acc
-
-    def npy(t):
-        return t.detach().cpu().contiguous().numpy()
-
-    kp, vp, ks, vs = npy(case.k_pool), npy(case.v_pool), npy(case.k_scale), npy(case.v_scale)
-    q, bt, ctx = _stored(case.q), npy(case.block_table), npy(case.context_lens)
-
-    def run(seqs):
-        sel = np.asarray([[b, h] for b in seqs for h in range(case.n_q)], np.int32)
-        t0 = time.perf_counter()
-        oracle.decode(q, kp, vp, case.fmt, bt, ctx, case.scale, sel=sel, q_dtype=case.q_dtype,
-                      k_scale=ks, v_scale=vs)
-        return time.perf_counter() - t0
-
-    t1 = run([0])
-    n = int(min(case.batch, max(1, math.ceil(target_s / max(t1, 1e-6)))))
-    dt = run(list(range(n)))
-    kv = acc.quant_decode_kv_bytes(ctx[:n], case.n_kv, case.head_dim)
-    return {"value": round(kv / dt / 1e9, 6), "unit": "GB/s", "cores": oracle.max_threads(),
-            "kind": "oracle",
-            "sample": f"fp64 oracle decode over {case.fmt} codes of {n} of {case.batch} sequences "
-                      f"(all {case.n_q} query heads), {kv} bytes in {dt:.2f} s"}
+    if args.cpu_seconds > 0:
+        rec["cpu_baseline"] = cpu_baseline_chunk(c0, args.cpu_seconds, "GB/s")
+    return rec
 
 
 def bench_decode_quant(args, fmt: str):
@@ -654,7 +717,9 @@ def bench_decode_quant(args, fmt: str):
         "tflops": round(acc.decode_flops([ctx] * B, c0.n_q, c0.head_dim) / (dec_ms * 1e-3) / 1e12, 3),
     }
     if args.cpu_seconds > 0:
-        rec["cpu_baseline"] = cpu_baseline_quant(c0, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline_decode(
+            c0, args.cpu_seconds,
+            quant=(c0.fmt, c0.q_dtype, c0.k_scale.cpu().numpy(), c0.v_scale.cpu().numpy()))
     return rec
 
 
@@ -681,6 +746,53 @@ def bench_copy(args):
                        "bytes_written_per_launch": 4 * n}}
 
 
+# Workloads measured beside the default one (same steps and warm-up), each reported as a
+# compact sub-record of the default line: the 70B-shaped long-context decode, the
+# variable-length batch, the causal prefill + cache write + decode, and the 8B decode on
+# the VALU decode kernel (the design without matrix cores in decode).
+SUB_RECORDS = [("decode_70b_longctx", 4, None), ("decode_varlen", 3, None),
+               ("prefill_then_decode", 5, None), ("decode_8b_valu_kernel", 2, {"PA_DECODE_MFMA": "0"})]
+
+
+def compact(rec: dict) -> dict:
+    """The measured figures of a full bench record."""
+    out = {k: rec[k] for k in ("metric", "value", "unit", "us_per_step", "pct_hbm_peak", "tflops", "dtype")
+           if k in rec}
+    out["workload"] = rec["config"]["workload"]
+    r = rec["roofline"]
+    out["roofline"] = {k: r[k] for k in ("bound", "achieved", "peak", "unit", "frac", "traffic", "avg_launch_us")}
+    if "cpu_baseline" in rec:
+        out["cpu_baseline"] = rec["cpu_baseline"]
+    return out
+
+
+def sub_records(args) -> dict:
+    import os
+
+    import torch
+    sub = argparse.Namespace(**vars(args))
+    sub.cpu_seconds = args.sub_cpu_seconds
+    recs = {}
+    for name, cfg, env in SUB_RECORDS:
+        sub.workload = name   # names the counter summary of this workload (none for the VALU kernel)
+        saved = {k: os.environ.get(k) for k in (env or {})}
+        os.environ.update(env or {})
+        try:
+            rec = bench_prefill(sub) if cfg == 5 else bench_decode(sub, cfg)
+        finally:
+            for k, v in saved.items():
+                if v is None:
+                    os.environ.pop(k, None)
+                else:
+                    os.environ[k] = v
+        c = compact(rec)
+        if env:
+            c["env"] = env
+        recs[name] = c
+        torch.cuda.empty_cache()
+    return recs
+
+
 def main(argv=None) -> int:
     args = parse_args(argv)
     if args.gpus != 1:
@@ -701,6 +813,8 @@ def main(argv=None) -> int:
                else bench_decode_multi(args) if cfg == 7
                else bench_decode_quant(args, "fp8") if cfg == 9
                else bench_decode_quant(args, "int8") if cfg == 10 else bench_decode(args, cfg))
+    if args.workload == "decode_8b" and not args.no_sub_records and not args.unfused and not args.alibi:
+        rec["sub_records"] = sub_records(args)
     rec["device"] = torch.cuda.get_device_name(0)
     print(json.dumps(rec), flush=True)
     return 0
