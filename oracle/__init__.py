@@ -18,6 +18,7 @@ its ``float32`` per-row scales.
 from __future__ import annotations
 
 import ctypes
+import os
 import subprocess
 from pathlib import Path
 
@@ -295,12 +296,18 @@ _default: Oracle | None = None
 
 
 def get() -> Oracle:
-    """The in-tree oracle library, compiled on first use if it is missing."""
+    """The in-tree oracle library, compiled on first use if it is missing. PA_ORACLE_LIB in
+    the environment names another build of the same source to load instead (the
+    sanitizer test runs the pins against an AddressSanitizer build this way)."""
     global _default
     if _default is None:
-        if not LIB_PATH.exists():
-            build()
-        _default = Oracle(LIB_PATH)
+        override = os.environ.get("PA_ORACLE_LIB")
+        if override:
+            _default = Oracle(override)
+        else:
+            if not LIB_PATH.exists():
+                build()
+            _default = Oracle(LIB_PATH)
     return _default
 
 
