@@ -764,8 +764,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (window > 0 && !causal) return fail(PA_ERR_INVALID_ARG, "a sliding window needs causal == 1");
     if (alibi_slopes && !causal) return fail(PA_ERR_INVALID_ARG, "ALiBi slopes need causal == 1");
     if (batch == 0 || seq_len == 0) return PA_OK;
-    if (!pa::prefill_grid_fits(seq_len, n_q, batch))
-        return fail(PA_ERR_UNSUPPORTED, "prefill: ceil(seq_len / 128) * n_q * batch exceeds one launch");
+    if (!pa::prefill_grid_fits(seq_len, n_q, batch, n_q / n_kv))
+        return fail(PA_ERR_UNSUPPORTED, "prefill: the number of workgroups (ceil(seq_len / rows per workgroup) * n_q / heads per workgroup * batch) exceeds one launch");
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
         return fail(PA_ERR_INVALID_ARG, "prefill: q, k, v and out must be 16-byte aligned");
@@ -931,8 +931,8 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0 || chunk_len == 0) return PA_OK;
-    if (!pa::prefill_grid_fits(chunk_len, n_q, batch))
-        return fail(PA_ERR_UNSUPPORTED, "chunked prefill: ceil(chunk_len / 128) * n_q * batch exceeds one launch");
+    if (!pa::prefill_grid_fits(chunk_len, n_q, batch, n_q / cache->n_kv))
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill: the number of workgroups exceeds one launch");
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k_cache) || !aligned16(v_cache) || !aligned16(out))

@@ -37,6 +37,16 @@ __device__ __forceinline__ int window_first(int ctx, int rows, int window) {
 __device__ __forceinline__ float as_f32(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t as_u32(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// A read-only value at a wave-uniform address, loaded through the scalar cache
+// (s_load) rather than as a vector load: the compiler cannot prove that kernel
+// arguments such as a block table stay unwritten, so a plain load becomes a
+// vector load and its wait would also wait for every vector memory operation in
+// flight (the LDS copies of a prefetch ring). The data must not change during the
+// kernel; the scalar cache is invalidated at every launch.
+template <class T> __device__ __forceinline__ T load_uniform(const T* ptr) {
+    return *reinterpret_cast<const __attribute__((address_space(4))) T*>(reinterpret_cast<uintptr_t>(ptr));
+}
+
 // A 16-byte chunk of q with the scale's sign folded in: every word becomes
 // (word & q_and) ^ q_xor, which zeroes q for a zero scale (every score is then
 // exactly 0) or flips its sign bits for a negative one (q.k negated exactly), so

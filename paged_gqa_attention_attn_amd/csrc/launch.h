@@ -104,6 +104,7 @@ struct PrefillArgs {
     int32_t window;   // sliding window (causal only); 0: none
     const float* alibi;   // ALiBi slopes [n_q] (causal only); nullptr: none
     int resident_wgs;     // prefill workgroups the GPU holds at once (set by the launcher)
+    int hpw;              // query heads per workgroup (set by the launcher)
     // Contiguous bf16 keys only: an f16 copy of v in v's layout, written by the
     // staging kernel, and one byte per (sequence, KV head, 64-key tile) that is 1
     // where the copy is exact. nullptr: P V stays in bf16 (hi + lo parts).
@@ -111,13 +112,20 @@ struct PrefillArgs {
     uint8_t* v16_ok;
 };
 
-// Query rows per prefill workgroup. One launch has ceil(rows / 128) * n_q * batch
-// workgroups in a one-dimensional grid, so that count must fit in an int; rows stay
-// 128 below INT32_MAX so that the kernels' tile counts cannot overflow.
-constexpr int PREFILL_ROWS_PER_WG = 128;
-inline bool prefill_grid_fits(int rows, int n_q, int batch) {
-    return rows <= INT32_MAX - PREFILL_ROWS_PER_WG &&
-           ((int64_t)rows + PREFILL_ROWS_PER_WG - 1) / PREFILL_ROWS_PER_WG * n_q * batch <= INT32_MAX;
+// Prefill work items: a workgroup of 8 waves takes the query heads of one KV group
+// that share its K/V tiles, HPW of them (4, 2 or 1: the largest dividing the group
+// size), and 256 / HPW query rows of each (32 per wave). One launch has
+// ceil(rows / (256 / HPW)) * (n_q / HPW) * batch workgroups in a one-dimensional grid,
+// so that count must fit in an int; rows stay 256 below INT32_MAX so that the
+// kernels' tile counts cannot overflow.
+constexpr int PREFILL_WAVES = 8;
+constexpr int PREFILL_PAIRS_PER_WG = 32 * PREFILL_WAVES;   // (head, row) pairs
+inline int prefill_heads_per_wg(int group) { return group % 4 == 0 ? 4 : group % 2 == 0 ? 2 : 1; }
+inline bool prefill_grid_fits(int rows, int n_q, int batch, int group) {
+    const int hpw = prefill_heads_per_wg(group);
+    const int64_t rw = PREFILL_PAIRS_PER_WG / hpw;
+    return rows <= INT32_MAX - PREFILL_PAIRS_PER_WG &&
+           ((int64_t)rows + rw - 1) / rw * (n_q / hpw) * batch <= INT32_MAX;
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);

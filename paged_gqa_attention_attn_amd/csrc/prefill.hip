@@ -8,14 +8,20 @@
 // running max / sum rescales the output ("LLM 推理全过程的维度变化与核心公式",
 // research.frankk.site, Flash Attention paragraph of "工程优化怎么嵌进公式").
 //
-// Tiling (per workgroup: 4 waves, 128 query rows of one head, 32 per wave)
-//  * Key/value tiles of 64 positions are double-buffered in LDS. Each wave
-//    copies its quarter of the next K and V tiles with global_load_lds_dwordx4
-//    while the current tile is consumed, so tile data never passes through
-//    registers. Rows are stored unpadded, with the 16-byte chunk c of row r at
-//    position c ^ swz(r) of the row, which keeps the operand reads below free
-//    of LDS bank conflicts (the copy picks its source chunk so that each lane's
-//    destination stays the contiguous 16 * lane the copy instruction writes).
+// Tiling (per workgroup: 8 waves of 32 query rows, one KV head)
+//  * A workgroup takes the HPW query heads of one KV group that share its K/V tiles
+//    (4, 2 or 1: the largest dividing the group size) and 256 / HPW query rows of
+//    each, so every K/V tile staged in LDS feeds 256 (head, row) pairs. At HPW = 4
+//    the waves' rows (two runs of 32) end in the same 64-key tile, so all eight
+//    do the same causal work between barriers.
+//  * Key/value tiles of 64 positions stream through a ring of NBUF tiles in LDS
+//    (one workgroup per compute unit holds it), NBUF - 1 tiles ahead of the one in
+//    use. Each wave copies 8 rows of the next K and V tiles with
+//    global_load_lds_dwordx4, so tile data never passes through registers. Rows
+//    are stored unpadded, with the 16-byte chunk c of row r at position c ^ swz(r)
+//    of the row, which keeps the operand reads below free of LDS bank conflicts
+//    (the copy picks its source chunk so that each lane's destination stays the
+//    contiguous 16 * lane the copy instruction writes).
 //  * S^T = K Q^T with v_mfma_f32_32x32x16 (M = keys, N = queries, K = dims):
 //    each lane then holds 16 keys of ONE query per 32-key half-tile, so the
 //    row max needs only one v_permlane32_swap.
@@ -58,10 +64,10 @@ namespace pa {
 
 namespace {
 
-constexpr int BM = PREFILL_ROWS_PER_WG;   // query rows per workgroup
 constexpr int BN = 64;    // keys per tile
 constexpr int WM = 32;    // query rows per wave
-constexpr int NWAVES = BM / WM;
+constexpr int NWAVES = PREFILL_WAVES;
+constexpr int NBUF = 4;   // K/V tiles in the LDS ring
 constexpr float TAU = 8.0f;        // rescale threshold (log2 units)
 constexpr float LOG2E = 1.4426950408889634f;
 constexpr float M_FLOOR = -1e30f;  // running-max start: finite, so 2^(s - m) of a masked s is 0
@@ -72,12 +78,14 @@ template <int D> struct Tile {
     static constexpr int BYTES = BN * ROWB;             // one K or V tile
     static constexpr int COPIES = BYTES / (1024 * NWAVES);  // 1 KB copies per wave per tile
     static constexpr int BUF = 2 * BYTES;               // K tile, then V tile
+    static constexpr int LDS = NBUF * BUF;              // the ring
     static_assert(COPIES * 1024 * NWAVES == BYTES, "a tile splits into whole 1 KB wave copies");
+    static_assert(LDS <= 160 * 1024, "the ring fits one compute unit's LDS");
     static __device__ __forceinline__ int swz(int r) { return chunk_swizzle<CPR>(r); }
 };
 
 template <class E, int D, bool PAGED>
-__global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillArgs p) {
+__global__ __launch_bounds__(64 * NWAVES, 1) void prefill_kernel(const PrefillArgs p) {
     using T = Tile<D>;
     using S = typename E::storage;
     constexpr int KK = D / 16;     // MFMA k-steps over the head dimension
@@ -85,27 +93,30 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     constexpr bool kStage = std::is_same<E, BF16>::value;   // V may come staged as f16
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
-    // Work item of this workgroup: query tile qt of head h of sequence b. Items are
-    // numbered hb * nqt + r (hb = b * n_q + h; rank r = 0 is the heaviest causal tile,
-    // the last rows). Workgroups go to the 8 XCDs in turn (XCD = id mod 8), so XCD k
-    // takes the k-th contiguous eighth [a, e) of the items: whole heads apart from the
-    // two ends, so every XCD gets the same mix of causal tile costs, and the heads that
-    // share a KV head stay on one XCD's L2. On its XCD, the j-th workgroup takes the
-    // j-th item of [a, e) in (rank, head) order: all heaviest tiles first, as in
-    // longest-first scheduling. C(r), the number of items of [a, e) with rank below r,
-    // is (e / nqt - a / nqt) r + min(r, e % nqt) - min(r, a % nqt); the rank is the
-    // largest r with C(r) <= j, and the heads holding rank r are consecutive from
-    // ceil((a - r) / nqt).
-    const int nqt = p.seq_len / BM + (p.seq_len % BM != 0);
+    // Work item of this workgroup: query tile qt (RW = 256 / HPW rows) of head block hb
+    // (HPW heads of one KV group) of sequence b. Items are numbered hb * nqt + r
+    // (hb = b * n_q / HPW + head block; rank r = 0 is the heaviest causal tile, the last
+    // rows). Workgroups go to the 8 XCDs in turn (XCD = id mod 8), so XCD k takes the
+    // k-th contiguous eighth [a, e) of the items: whole head blocks apart from the two
+    // ends, so every XCD gets the same mix of causal tile costs, and a KV head's work
+    // stays on one XCD's L2. On its XCD, the j-th workgroup takes the j-th item of
+    // [a, e) in (rank, head block) order: all heaviest tiles first, as in longest-first
+    // scheduling. C(r), the number of items of [a, e) with rank below r, is
+    // (e / nqt - a / nqt) r + min(r, e % nqt) - min(r, a % nqt); the rank is the
+    // largest r with C(r) <= j, and the head blocks holding rank r are consecutive
+    // from ceil((a - r) / nqt).
+    const int HPW = p.hpw;
+    const int RW = NWAVES * WM / HPW;             // query rows per workgroup
+    const int nqt = p.seq_len / RW + (p.seq_len % RW != 0);
     const int n_items = gridDim.x;
     const int wg = blockIdx.x;
     const int per_xcd = n_items / 8, xcd = wg % 8;
     const int ia = xcd * per_xcd + min(xcd, n_items % 8);
     const int ie = ia + per_xcd + (xcd < n_items % 8);
     int jx = wg / 8;
-    // When the whole grid is resident at once (one round of two workgroups per CU),
-    // the second half of an XCD's share goes lightest first, so that a CU's two
-    // workgroups tend to pair a heavy tile with a light one.
+    // When the whole grid is resident at once, the second half of an XCD's share goes
+    // lightest first, so that workgroups that share the chip at the end pair heavy
+    // tiles with light ones.
     if (n_items <= p.resident_wgs && jx >= (ie - ia) / 2) jx = (ie - ia) - 1 - (jx - (ie - ia) / 2);
     const int fa = ia / nqt, ra = ia % nqt, fe = ie / nqt, re = ie % nqt;
     auto below = [&](int r) { return (fe - fa) * r + min(r, re) - min(r, ra); };
@@ -116,14 +127,15 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     }
     const int hb = fa + (qr < ra ? 1 : 0) + (jx - below(qr));
     const int qt = p.causal ? nqt - 1 - qr : qr;
-    const int h = hb % p.n_q;
-    const int b = hb / p.n_q;
-    const int g = h / p.group;
+    const int n_hb = p.n_q / HPW;                 // head blocks per sequence
+    const int b = hb / n_hb;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int h = (hb % n_hb) * HPW + wave % HPW;   // this wave's query head
+    const int g = (hb % n_hb) * HPW / p.group;      // the workgroup's KV head
     const int lane = threadIdx.x & 63;
     const int half = lane >> 5;    // 0 or 1
     const int l32 = lane & 31;
-    const int q0 = qt * BM + wave * WM;           // first query row of this wave
+    const int q0 = qt * RW + (wave / HPW) * WM;   // first query row of this wave
     const int my_q = q0 + l32;                    // the query row this lane's columns belong to
     const int S_len = p.seq_len;                  // query rows per sequence
 
@@ -135,7 +147,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     int ctx = S_len;
     bool bad = false;
     if constexpr (PAGED) {
-        ctx = p.context_lens[b];
+        ctx = load_uniform(p.context_lens + b);
         if (ctx < 0 || ctx > p.max_blocks * 16) {
             bad = ctx > 0;
             ctx = 0;
@@ -154,20 +166,21 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const char* Vg = reinterpret_cast<const char*>(p.v) + head_off;   // the f16 copy when staged (below)
 
     // Q^T operand: lane holds dims 16*kk + 8*half .. +8 of its query, for every kk.
+    // (Rows past the prompt load its last row, all loads in flight together, and are zeroed.)
     u32x4_t qreg[KK];
+    const int q_row = min(my_q, S_len - 1);
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
-        if (my_q < S_len) {
-            const uint4 v = q_fold(*reinterpret_cast<const uint4*>(Qg + (int64_t)my_q * q_stride + 16 * kk + 8 * half),
-                                   p.q_and, p.q_xor);
-            qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
-        } else {
-            qreg[kk] = u32x4_t{0u, 0u, 0u, 0u};
-        }
+        const uint4 v = q_fold(*reinterpret_cast<const uint4*>(Qg + (int64_t)q_row * q_stride + 16 * kk + 8 * half),
+                               p.q_and, p.q_xor);
+        qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
     }
+#pragma unroll
+    for (int kk = 0; kk < KK; ++kk)
+        if (my_q >= S_len) qreg[kk] = u32x4_t{0u, 0u, 0u, 0u};
 
     // Key tiles this workgroup visits (none when its last query sees no key).
-    const int pos_last_wg = qbase + min(qt * BM + BM, S_len) - 1;
+    const int pos_last_wg = qbase + min(qt * RW + RW, S_len) - 1;
     const int n_tiles = ctx == 0 ? 0
                         : p.causal ? (pos_last_wg < 0 ? 0 : min(pos_last_wg, ctx - 1) / BN + 1)
                                    : (ctx + BN - 1) / BN;
@@ -176,7 +189,7 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     // before the workgroup's first row's window are skipped, and no block before
     // it is read (their table entries may be stale).
     const int W = p.window;
-    const int wg_lo = W > 0 ? max(0, qbase + qt * BM - W + 1) : 0;
+    const int wg_lo = W > 0 ? max(0, qbase + qt * RW - W + 1) : 0;
     const int j0 = min(wg_lo / BN, n_tiles);
     const int lo_blk = wg_lo / 16;
     const int wave_lo = pos0 - W + 1;             // window start of this wave's first row
@@ -208,16 +221,16 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     if (use16) Vg = reinterpret_cast<const char*>(p.v16) + head_off;
     const bool v_logical = PAGED && use16;   // V blocks addressed by logical index
 
-    // This wave's copies of tile j into buffer `buf`: copy c fills bytes
+    // This wave's copies of tile j into ring slot `buf`: copy c fills bytes
     // [(wave * COPIES + c) KB, +1 KB) of the K tile and of the V tile, lane l
     // the 16 bytes at 16 l of that, which hold source chunk pos ^ swz(row).
-    // A wave's copies cover rows 16 wave .. 16 wave + 15 of the tile, i.e. one
-    // whole 16-token cache block when the keys are paged. Rows past the context
+    // A wave's copies cover rows 8 wave .. 8 wave + 7 of the tile, i.e. half of
+    // one 16-token cache block when the keys are paged. Rows past the context
     // read its last row instead, and rows of blocks wholly before the window
     // read the window's first row (each in the block the clamped block index
     // names): their keys are masked, and their V rows must be finite because
     // the P V product multiplies them by exactly 0.
-    static_assert(T::COPIES * 1024 == 16 * T::ROWB, "a wave copies one 16-row block per tile");
+    static_assert(T::COPIES * 1024 == 8 * T::ROWB, "a wave copies 8 rows of a tile");
     const uint32_t lds0 = lds_addr(smem);
     // Tiles that need no row clamp (wholly inside [window start, ctx)) copy from a
     // wave-uniform base plus lane offsets fixed for the whole kernel: row r of the
@@ -236,8 +249,8 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
         const int key0 = j * BN;
         int64_t block_src = 0, vblock_src = 0;
         if constexpr (PAGED) {
-            const int jb = max(min(key0 / 16 + wave, (ctx - 1) / 16), lo_blk);   // uniform over the wave
-            int phys = p.block_table[(int64_t)b * p.max_blocks + jb];
+            const int jb = max(min(key0 / 16 + wave / 2, (ctx - 1) / 16), lo_blk);   // uniform over the wave
+            int phys = load_uniform(p.block_table + (int64_t)b * p.max_blocks + jb);
             if (phys < 0 || phys >= p.num_blocks) {
                 bad = true;
                 phys = 0;
@@ -299,40 +312,62 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
     const int vkey = 4 * half + r16 / 4;         // + 16 jg + 8 t + 32 st
     const int vchunk = 2 * (g16 & 1) + (r16 & 3) / 2;  // + 4 mt
     const int vbyte = 8 * (r16 & 1);
-    uint32_t k_off[KK];       // K operand: row l32, dims 16 kk + 8 half .. +8
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) k_off[kk] = l32 * T::ROWB + (((2 * kk + half) ^ ksw) * 16);
-    uint32_t vt_off[2][MT];   // V^T operand: key 8 t + vkey, dims 32 mt + ... (transposing read)
+    // K operand: row l32, 16-byte chunk 2 kk + half, stored at chunk (2 kk + half) ^ ksw.
+    // As 2 kk + half = 2 kk ^ half, its byte offset is k_base ^ 32 kk (the XOR only
+    // touches bits 5..7, below the row's bits).
+    const uint32_t k_base = l32 * T::ROWB + ((half ^ ksw) * 16);
+    auto k_off = [&](int kk) { return k_base ^ (uint32_t)(32 * kk); };
+    // V^T operand: key 8 t + vkey, chunk 4 mt + vchunk (vchunk < 4, so that sum is an XOR),
+    // stored at chunk (4 mt + vchunk) ^ swz(8 t + vkey): byte offset vt_base[t] ^ 64 mt.
+    uint32_t vt_base[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t)
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt)
-            vt_off[t][mt] = (8 * t + vkey) * T::ROWB + (((4 * mt + vchunk) ^ T::swz(8 * t + vkey)) * 16) + vbyte;
+        vt_base[t] = (8 * t + vkey) * T::ROWB + ((vchunk ^ T::swz(8 * t + vkey)) * 16) + vbyte;
+    auto vt_off = [&](int t, int mt) { return vt_base[t] ^ (uint32_t)(64 * mt); };
 
     // The tile loop, for P V in the input type (PE = E) or on the staged f16 V.
     auto tile_loop = [&](auto staged) {
         using PE = typename std::conditional<decltype(staged)::value, F16, E>::type;
-        if (n_tiles > j0) issue_tile(j0, j0 & 1);
+        // Ring: tiles j0 .. j0 + NBUF - 2 are copied first; step j then waits for tile j,
+        // and once every wave is done with tile j - 1 copies tile j + NBUF - 1 into its
+        // slot. Copies complete in issue order, so tile j has landed when at most the
+        // copies of the tiles issued after it are outstanding.
+        for (int t = 0; t < NBUF - 1; ++t)
+            if (j0 + t < n_tiles) issue_tile(j0 + t, (j0 + t) % NBUF);
         for (int j = j0; j < n_tiles; ++j) {
-            wait_vmcnt<0>();   // this wave's copies of tile j have landed
-            __syncthreads();   // so have the other waves'; all are done with tile j - 1
-            if (j + 1 < n_tiles) issue_tile(j + 1, (j + 1) & 1);
+            const int ahead = min(n_tiles - 1, j + NBUF - 2) - j;   // tiles issued after j
+            static_assert(NBUF == 4, "the waits below cover up to two tiles in flight after j");
+            if (ahead >= 2) wait_vmcnt<4 * T::COPIES>();
+            else if (ahead == 1) wait_vmcnt<2 * T::COPIES>();
+            else wait_vmcnt<0>();
+            __syncthreads();   // the other waves' copies of tile j landed; all are done with tile j - 1
+            if (j + NBUF - 1 < n_tiles) issue_tile(j + NBUF - 1, (j + NBUF - 1) % NBUF);
             const int key0 = j * BN;
             if (p.causal && key0 > pos_last_wave) continue;   // uniform over the wave
             if (W > 0 && key0 + BN - 1 < wave_lo) continue;   // wholly before every row's window
 
-            const char* kl = smem + (j & 1) * T::BUF;
-            lds_char_t* vl_lds = (lds_char_t*)(smem + (j & 1) * T::BUF + T::BYTES);
+            const char* kl = smem + (j % NBUF) * T::BUF;
+            lds_char_t* vl_lds = (lds_char_t*)(smem + (j % NBUF) * T::BUF + T::BYTES);
 
             // S^T for the two 32-key halves, interleaved so each MFMA hides the other's latency.
+            // Operands of k-step kk + 2 are read before the products of k-step kk, so two
+            // steps of LDS reads are in flight behind the matrix cores.
             f32x16_t sc[2] = {f32x16_t{}, f32x16_t{}};
+            uint4 ka[3][2];
+            auto k_read = [&](int kk, uint4 (&a)[2]) {
+                a[0] = *reinterpret_cast<const uint4*>(kl + k_off(kk));
+                a[1] = *reinterpret_cast<const uint4*>(kl + k_off(kk) + 32 * T::ROWB);
+            };
+            k_read(0, ka[0]);
+            k_read(1, ka[1]);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
-                const char* ka = kl + k_off[kk];
-                const uint4 a0 = *reinterpret_cast<const uint4*>(ka);
-                const uint4 a1 = *reinterpret_cast<const uint4*>(ka + 32 * T::ROWB);
+                if (kk + 2 < KK) k_read(kk + 2, ka[(kk + 2) % 3]);
+                const uint4 a0 = ka[kk % 3][0], a1 = ka[kk % 3][1];
                 sc[0] = Mfma<E>::run(u32x4_t{a0.x, a0.y, a0.z, a0.w}, qreg[kk], sc[0]);
                 sc[1] = Mfma<E>::run(u32x4_t{a1.x, a1.y, a1.z, a1.w}, qreg[kk], sc[1]);
+                __builtin_amdgcn_sched_barrier(0);
             }
 
             float lane_bias = 0.f;   // ALiBi bias shared by the lane's scores (unscaled units)
@@ -378,54 +413,94 @@ __global__ __launch_bounds__(64 * NWAVES, 2) void prefill_kernel(const PrefillAr
 
             // P = 2^((s + lane_bias) scale - m) in the element type (bf16: hi + lo parts).
             const float nm = fmaf(lane_bias, c2, -m_run);
-            u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
-            float lsum = 0.f;
+            auto v_read = [&](int st, int jg, int mt) -> u32x4_t {   // V^T operand, see vt_off
+                uint32_t a[4];
 #pragma unroll
-            for (int st = 0; st < 2; ++st) {
+                for (int t = 0; t < 2; ++t) {
+                    const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                        (lds_i16x4_t*)(vl_lds + (st * 32 + jg * 16) * T::ROWB + vt_off(t, mt)));
+                    a[2 * t] = __builtin_bit_cast(uint2, v).x;
+                    a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
+                }
+                return u32x4_t{a[0], a[1], a[2], a[3]};
+            };
+            if constexpr (!Mfma<PE>::kSplit) {
+                // One f16 P part: group u = 2 st + jg of 16 keys; its P words are made on the
+                // VALU while the P V products of group u - 1 run, and each V^T operand is
+                // read two products ahead.
+                float lsum = 0.f;
+                auto p_word = [&](int u, int w) {
+                    const int st = u / 2, jg = u % 2;
+                    const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, nm));
+                    const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, nm));
+                    const uint32_t hw = Mfma<PE>::pack(p0, p1);
+                    // the denominator of the rounded weights the product uses
+                    lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw),
+                                                  f16x2_t{(_Float16)1.f, (_Float16)1.f}, lsum, false);
+                    return hw;
+                };
+                u32x4_t pw[2];
+                {
+                    uint32_t w4[4];
 #pragma unroll
-                for (int jg = 0; jg < 2; ++jg) {
-                    uint32_t hw[4], lw[4];
+                    for (int w = 0; w < 4; ++w) w4[w] = p_word(0, w);
+                    pw[0] = u32x4_t{w4[0], w4[1], w4[2], w4[3]};
+                }
+                constexpr int NU = 4 * MT;   // products: (group u, dims mt)
+                u32x4_t vv[3];
+                static_assert(MT >= 2, "the first two products are (group 0, dims 0) and (group 0, dims 32)");
+                vv[0] = v_read(0, 0, 0);
+                vv[1] = v_read(0, 0, 1);
+                __builtin_amdgcn_sched_barrier(0);
+                uint32_t nxt[4];
 #pragma unroll
-                    for (int w = 0; w < 4; ++w) {
-                        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, nm));
-                        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, nm));
-                        hw[w] = Mfma<PE>::pack(p0, p1);
-                        if constexpr (Mfma<PE>::kSplit) {
+                for (int i = 0; i < NU; ++i) {
+                    const int u = i / MT, mt = i % MT;
+                    if (i + 2 < NU) {
+                        const int i2 = i + 2, u2 = i2 / MT, m2 = i2 % MT;
+                        vv[i2 % 3] = v_read(u2 / 2, u2 % 2, m2);
+                    }
+                    o[mt] = Mfma<PE>::run(vv[i % 3], pw[u % 2], o[mt]);
+                    // P words of group u + 1, spread over group u's products
+                    if (u + 1 < 4) {
+#pragma unroll
+                        for (int w = mt * 4 / MT; w < (mt + 1) * 4 / MT; ++w) nxt[w] = p_word(u + 1, w);
+                        if (mt == MT - 1) pw[(u + 1) % 2] = u32x4_t{nxt[0], nxt[1], nxt[2], nxt[3]};
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+                l_run += lsum;
+            } else {
+                u32x4_t ph[2][2], pl[2][2];   // [half-tile][16-key group]
+                float lsum = 0.f;
+#pragma unroll
+                for (int st = 0; st < 2; ++st) {
+#pragma unroll
+                    for (int jg = 0; jg < 2; ++jg) {
+                        uint32_t hw[4], lw[4];
+#pragma unroll
+                        for (int w = 0; w < 4; ++w) {
+                            const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w], c2, nm));
+                            const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[st][8 * jg + 2 * w + 1], c2, nm));
+                            hw[w] = Mfma<PE>::pack(p0, p1);
                             lw[w] = Mfma<PE>::pack(p0 - Mfma<PE>::lo_of(hw[w]), p1 - Mfma<PE>::hi_of(hw[w]));
                             lsum += p0 + p1;
-                        } else {
-                            // the denominator of the rounded weights the product uses
-                            lsum = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, hw[w]),
-                                                          f16x2_t{(_Float16)1.f, (_Float16)1.f}, lsum, false);
                         }
-                    }
-                    ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
-                    if constexpr (Mfma<PE>::kSplit) pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
-                }
-            }
-            l_run += lsum;
-
-            // O^T += V^T P^T. Lane (group g16, r16) fetches 4 dims of key vkey + ...,
-            // and after the transpose holds 4 consecutive keys of one dim.
-#pragma unroll
-            for (int st = 0; st < 2; ++st) {
-#pragma unroll
-                for (int jg = 0; jg < 2; ++jg) {
-#pragma unroll
-                    for (int mt = 0; mt < MT; ++mt) {
-                        uint32_t a[4];
-#pragma unroll
-                        for (int t = 0; t < 2; ++t) {
-                            const i16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                                (lds_i16x4_t*)(vl_lds + (st * 32 + jg * 16) * T::ROWB + vt_off[t][mt]));
-                            a[2 * t] = __builtin_bit_cast(uint2, v).x;
-                            a[2 * t + 1] = __builtin_bit_cast(uint2, v).y;
-                        }
-                        const u32x4_t av = u32x4_t{a[0], a[1], a[2], a[3]};
-                        o[mt] = Mfma<PE>::run(av, ph[st][jg], o[mt]);
-                        if constexpr (Mfma<PE>::kSplit) o[mt] = Mfma<PE>::run(av, pl[st][jg], o[mt]);
+                        ph[st][jg] = u32x4_t{hw[0], hw[1], hw[2], hw[3]};
+                        pl[st][jg] = u32x4_t{lw[0], lw[1], lw[2], lw[3]};
                     }
                 }
+                l_run += lsum;
+#pragma unroll
+                for (int st = 0; st < 2; ++st)
+#pragma unroll
+                    for (int jg = 0; jg < 2; ++jg)
+#pragma unroll
+                        for (int mt = 0; mt < MT; ++mt) {
+                            const u32x4_t av = v_read(st, jg, mt);
+                            o[mt] = Mfma<PE>::run(av, ph[st][jg], o[mt]);
+                            o[mt] = Mfma<PE>::run(av, pl[st][jg], o[mt]);
+                        }
             }
         }
     };
@@ -576,8 +651,9 @@ int device_cus() {
 
 template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& args, hipStream_t s) {
     PrefillArgs a = args;
-    a.resident_wgs = 2 * device_cus();   // __launch_bounds__(256, 2) and 64 KB of LDS each
-    const size_t lds = 2 * (size_t)Tile<D>::BUF;
+    a.resident_wgs = device_cus();   // one 8-wave workgroup and its ring per compute unit
+    a.hpw = prefill_heads_per_wg(a.group);
+    const size_t lds = (size_t)Tile<D>::LDS;
     // Opt in to exactly the dynamic LDS used (static LDS, e.g. the one word
     // __syncthreads_or needs, counts against the same 160 KB).
     static const hipError_t opt_in = hipFuncSetAttribute(
@@ -597,8 +673,9 @@ template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs&
             if (e != hipSuccess) return e;
         }
     }
-    const int64_t n_items = ((int64_t)a.seq_len + BM - 1) / BM * a.n_q * a.batch;
-    if (!prefill_grid_fits(a.seq_len, a.n_q, a.batch)) return hipErrorInvalidConfiguration;   // checked by the caller
+    const int64_t rw = NWAVES * WM / a.hpw;
+    const int64_t n_items = ((int64_t)a.seq_len + rw - 1) / rw * (a.n_q / a.hpw) * a.batch;
+    if (!prefill_grid_fits(a.seq_len, a.n_q, a.batch, a.group)) return hipErrorInvalidConfiguration;   // checked by the caller
     const dim3 grid((unsigned)n_items);
     hipLaunchKernelGGL((prefill_kernel<E, D, PAGED>), grid, dim3(64 * NWAVES), lds, s, a);
     return hipGetLastError();
