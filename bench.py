@@ -751,7 +751,7 @@ def bench_copy(args):
 # variable-length batch, the causal prefill + cache write + decode, and the 8B decode on
 # the VALU decode kernel (the design without matrix cores in decode).
 SUB_RECORDS = [("decode_70b_longctx", 4, None), ("decode_varlen", 3, None),
-               ("prefill_then_decode", 5, None), ("decode_8b_valu_kernel", 2, {"PA_DECODE_MFMA": "0"})]
+               ("prefill_then_decode", 5, None), ("decode_8b_valu_kernel", 2, {"decode_matrix_cores": 0})]
 
 
 def compact(rec: dict) -> dict:
@@ -767,27 +767,23 @@ def compact(rec: dict) -> dict:
 
 
 def sub_records(args) -> dict:
-    import os
-
     import torch
+
+    import paged_gqa_attention_attn_amd as pa
     sub = argparse.Namespace(**vars(args))
     sub.cpu_seconds = args.sub_cpu_seconds
     recs = {}
-    for name, cfg, env in SUB_RECORDS:
+    for name, cfg, options in SUB_RECORDS:
         sub.workload = name   # names the counter summary of this workload (none for the VALU kernel)
-        saved = {k: os.environ.get(k) for k in (env or {})}
-        os.environ.update(env or {})
+        saved = {k: pa.set_option(k, v) for k, v in (options or {}).items()}
         try:
             rec = bench_prefill(sub) if cfg == 5 else bench_decode(sub, cfg)
         finally:
             for k, v in saved.items():
-                if v is None:
-                    os.environ.pop(k, None)
-                else:
-                    os.environ[k] = v
+                pa.set_option(k, v)
         c = compact(rec)
-        if env:
-            c["env"] = env
+        if options:
+            c["options"] = options
         recs[name] = c
         torch.cuda.empty_cache()
     return recs

@@ -35,7 +35,7 @@
  *    sequence whose context length exceeds max_blocks_per_seq * block_size or
  *    whose block table names a block outside the pool, among the blocks the
  *    call reads, gets a NaN output row instead of an out-of-bounds read.
- *  - Debug mode: with PA_VALIDATE=1 in the environment, kv_append, the decode
+ *  - Debug mode: with option PA_OPT_VALIDATE on (pa_set_option), kv_append, the decode
  *    calls (single- and multi-row) and chunked prefill also copy that metadata to the host (synchronising `stream`)
  *    and return PA_ERR_INVALID_ARG, enqueuing nothing, for: a slot past the
  *    pool or repeated within one call; a context length outside
@@ -239,7 +239,7 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *         values below 2^-14 move by at most 2^-25), so that P V runs with one
  *         11-bit P part on the f16 matrix cores; 64-key tiles holding a larger
  *         finite value keep the bf16 product for the rows that read them.
- *         PA_PREFILL_STAGE_V=0 in the environment turns the staging off.
+ *         Option PA_OPT_PREFILL_STAGE_V = 0 turns the staging off.
  *         Calls that share a workspace must not overlap on the GPU.
  * Supported: head_dim 128 (and 64); dtype bf16 or f16; seq_len at most
  * 2^31 - 129 and ceil(seq_len / 128) * n_q * batch at most 2^31 - 1 (one
@@ -322,7 +322,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  * the workspace (below), and P V then runs with one f16 P part; blocks holding a
  * larger value keep the bf16 hi + lo product. Calls that share that workspace
  * must not overlap on the GPU.
- * PA_PREFILL_STAGE_V=0 in the environment turns the copy off.
+ * Option PA_OPT_PREFILL_STAGE_V = 0 turns the copy off.
  *   workspace     device scratch of at least pa_chunked_prefill_workspace_bytes(...)
  *                 bytes for the same batch, max_blocks_per_seq and cache (16-byte
  *                 aligned; 0 bytes: none is used), or NULL: then the workspace of
@@ -400,7 +400,7 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
  * scales and outputs equal those of the two calls bit for bit, under the same
  * conditions as pa_paged_attn_decode_append: each sequence's slot must be its
  * position ctx - 1, in a block no other sequence of the call reads
- * (PA_VALIDATE=1 checks both).
+ * (option PA_OPT_VALIDATE checks both).
  */
 int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const void* v_new, pa_dtype q_dtype,
                                       const int64_t* slot_mapping, int32_t batch, int32_t n_q, void* k_cache,
@@ -419,6 +419,41 @@ int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const vo
  * setting unchanged) for an invalid value.
  */
 int32_t pa_set_decode_partition_tokens(int32_t tokens);
+
+/*
+ * Kernel-choice options. Each starts at the value of its environment variable
+ * (read once, when the library first needs an option; an unset, unparsable or
+ * out-of-range variable gives the default) and then changes only through
+ * pa_set_option. Process-wide, like the partition size: a call made while
+ * another thread changes an option sees the old or the new value, and the
+ * *_workspace_bytes queries must be made under the same options as the calls
+ * they size.
+ */
+typedef enum {
+    /* PA_DECODE_MFMA: 1 (default) runs bf16/f16 decode, and multi-row decode of
+     * at most 16 (head, row) pairs per KV head, on the matrix-core kernel when the
+     * pairs per KV head are a multiple of 4; 0 always takes the VALU kernel. */
+    PA_OPT_DECODE_MATRIX_CORES = 0,
+    /* PA_DECODE_RING: K/V blocks each decode wave keeps in flight, 1 (default) or 2. */
+    PA_OPT_DECODE_RING = 1,
+    /* PA_DECODE_WAVES: waves per decode workgroup, 1..8; 0 (default) lets the
+     * planner choose from the shape and the device's compute units. */
+    PA_OPT_DECODE_WAVES = 2,
+    /* PA_PREFILL_STAGE_V: 1 (default) stages a bf16 V as f16 for the P V product
+     * of prefill and chunked prefill; 0 keeps P V in bf16 hi + lo parts. */
+    PA_OPT_PREFILL_STAGE_V = 3,
+    /* PA_VALIDATE: 1 turns on the debug-mode checks of device metadata described
+     * at the top of this header; 0 (default) leaves them off. */
+    PA_OPT_VALIDATE = 4,
+    PA_OPT_COUNT = 5
+} pa_option;
+
+/* Sets `option` (a pa_option) to `value`; returns the previous value, or -1
+ * (changing nothing) for an unknown option or a value outside its range. */
+int32_t pa_set_option(int32_t option, int32_t value);
+
+/* Current value of `option`, or -1 for an unknown option. */
+int32_t pa_get_option(int32_t option);
 
 /*
  * Default decode workspace for calls that pass workspace == NULL ([VC]/[IW]

@@ -33,7 +33,7 @@ __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_noalloc", "paged
            "paged_attn_decode_quant", "paged_attn_decode_quant_append", "quant_decode_workspace_bytes",
            "prefill_workspace_bytes", "chunked_prefill_workspace_bytes",
            "decode_workspace_bytes", "set_workspace",
-           "set_decode_partition_tokens", "library_version", "LibraryNotBuilt", "PagedAttnError"]
+           "set_decode_partition_tokens", "set_option", "get_option", "library_version", "LibraryNotBuilt", "PagedAttnError"]
 
 _DTYPE = {torch.float32: _lib.PA_F32, torch.bfloat16: _lib.PA_BF16, torch.float16: _lib.PA_F16}
 
@@ -112,6 +112,28 @@ def set_decode_partition_tokens(tokens: int) -> int:
     if prev < 0:
         raise ValueError(f"invalid partition size {tokens}")
     return int(prev)
+
+
+def set_option(name: str, value: int) -> int:
+    """Set a kernel-choice option (``_lib.OPTIONS`` names them); returns the previous value.
+
+    decode_matrix_cores (0/1), decode_ring (1/2), decode_waves (0 = planner's
+    choice, 1..8), prefill_stage_v (0/1), validate (0/1). Each starts from its
+    environment variable, read once by the library.
+    """
+    if name not in _lib.OPTIONS:
+        raise ValueError(f"unknown option {name!r} (known: {sorted(_lib.OPTIONS)})")
+    prev = _lib.load().pa_set_option(_lib.OPTIONS[name][0], int(value))
+    if prev < 0:
+        raise ValueError(f"option {name}: value {value} out of range")
+    return int(prev)
+
+
+def get_option(name: str) -> int:
+    """Current value of a kernel-choice option."""
+    if name not in _lib.OPTIONS:
+        raise ValueError(f"unknown option {name!r} (known: {sorted(_lib.OPTIONS)})")
+    return int(_lib.load().pa_get_option(_lib.OPTIONS[name][0]))
 
 
 def kv_append(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,

@@ -13,6 +13,11 @@ LIB_PATH = Path(__file__).resolve().parent / "libpagedattn.so"
 PA_F32, PA_BF16, PA_F16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
 
+# pa_option: name -> (value, environment variable giving its initial value)
+OPTIONS = {"decode_matrix_cores": (0, "PA_DECODE_MFMA"), "decode_ring": (1, "PA_DECODE_RING"),
+           "decode_waves": (2, "PA_DECODE_WAVES"), "prefill_stage_v": (3, "PA_PREFILL_STAGE_V"),
+           "validate": (4, "PA_VALIDATE")}
+
 EXPORTS = (
     "pa_kv_append",
     "pa_decode_workspace_bytes",
@@ -29,6 +34,8 @@ EXPORTS = (
     "pa_paged_attn_decode_quant",
     "pa_paged_attn_decode_quant_append",
     "pa_set_decode_partition_tokens",
+    "pa_set_option",
+    "pa_get_option",
     "pa_set_workspace",
     "pa_last_error",
     "pa_version",
@@ -106,6 +113,10 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
     L.pa_paged_attn_decode_quant_append.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
+    L.pa_set_option.argtypes = [i32, i32]
+    L.pa_set_option.restype = i32
+    L.pa_get_option.argtypes = [i32]
+    L.pa_get_option.restype = i32
     L.pa_set_workspace.argtypes = [vp, sz]
     L.pa_set_workspace.restype = ctypes.c_int
     L.pa_last_error.argtypes = []

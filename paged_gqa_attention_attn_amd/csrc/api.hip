@@ -3,7 +3,7 @@
 //
 // By default no entry point reads device memory on the host or synchronises the
 // stream: every check uses host-side arguments only, and the kernels bounds-check
-// the device-resident metadata themselves. With PA_VALIDATE=1 in the environment,
+// the device-resident metadata themselves. With the PA_OPT_VALIDATE option on,
 // the calls also copy that metadata to the host (synchronising the stream) and
 // reject what the kernels would only skip or turn into NaN rows. See
 // include/pagedattn.h for the contract of each call.
@@ -21,6 +21,23 @@
 
 #include "launch.h"
 #include "pagedattn.h"
+
+namespace pa {
+
+int device_cus() {
+    static std::atomic<int> cus[64] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cus[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            return 256;
+        cus[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
+}  // namespace pa
 
 namespace {
 
@@ -76,16 +93,38 @@ std::atomic<int32_t> g_partition_tokens{0};
 constexpr int kBlockSize = 16;
 constexpr int kMaxWaves = 8;
 constexpr int kLdsBytes = 160 * 1024;  // LDS per workgroup on gfx950
-constexpr int kComputeUnits = 256;     // MI355X
 
-// Integer tuning knob from the environment (for sweeps), or `dflt`.
-int env_int(const char* name, int dflt) {
-    const char* v = std::getenv(name);
-    if (!v || !*v) return dflt;
-    char* end = nullptr;
-    const long x = std::strtol(v, &end, 10);
-    return (end && *end == 0) ? (int)x : dflt;
+// Kernel-choice options: each starts from its environment variable, read once
+// when an option is first needed (unset, unparsable or out of range: the
+// default), and afterwards changes only through pa_set_option.
+struct OptionSpec {
+    const char* env;
+    int32_t dflt, lo, hi;
+};
+constexpr OptionSpec kOptions[PA_OPT_COUNT] = {
+    {"PA_DECODE_MFMA", 1, 0, 1},     {"PA_DECODE_RING", 1, 1, 2}, {"PA_DECODE_WAVES", 0, 0, kMaxWaves},
+    {"PA_PREFILL_STAGE_V", 1, 0, 1}, {"PA_VALIDATE", 0, 0, 1},
+};
+
+std::atomic<int32_t>* option_values() {
+    static std::atomic<int32_t> v[PA_OPT_COUNT];
+    static std::once_flag once;
+    std::call_once(once, [] {
+        for (int i = 0; i < PA_OPT_COUNT; ++i) {
+            const OptionSpec& o = kOptions[i];
+            int32_t x = o.dflt;
+            if (const char* e = std::getenv(o.env); e && *e) {
+                char* end = nullptr;
+                const long y = std::strtol(e, &end, 10);
+                if (end && *end == 0 && y >= o.lo && y <= o.hi) x = (int32_t)y;
+            }
+            v[i].store(x, std::memory_order_relaxed);
+        }
+    });
+    return v;
 }
+
+int32_t option(pa_option o) { return option_values()[o].load(std::memory_order_relaxed); }
 
 // Sizes and types of a cache description. Quantised caches (one-byte codes plus
 // per-row scales) are accepted only by the entry points that take the scales.
@@ -115,11 +154,11 @@ struct Plan {
 };
 
 // Decode on the matrix cores (decode_mfma.hip) for bf16/f16 caches whose group
-// size fills 4, 8 or 16 MFMA columns; PA_DECODE_MFMA=0 selects the VALU kernel.
+// size fills 4, 8 or 16 MFMA columns, unless the option selects the VALU kernel.
 bool decode_uses_mfma(int32_t G, const pa_cache_desc* c) {
     if (c->dtype != PA_BF16 && c->dtype != PA_F16) return false;
     if (G % 4 != 0) return false;
-    return env_int("PA_DECODE_MFMA", 1) != 0;
+    return option(PA_OPT_DECODE_MATRIX_CORES) != 0;
 }
 
 // LDS bytes one wave of the matrix-core decode kernel takes: its ring, or the
@@ -130,12 +169,12 @@ int32_t mfma_wave_bytes(int32_t ring, int32_t tile, int32_t hw, int32_t head_dim
     return ((r > slot ? r : slot) + 15) / 16 * 16;
 }
 
-// Matrix-core decode plan: a grid of about kTargetWaves waves (8 per compute
-// unit), each streaming as long a run of blocks as that allows (4 to 64 blocks),
-// with the partitions of a context balanced. Measured on MI355X: larger runs and
-// fewer resident waves stream faster (8B-, 70B-shaped, variable-length and
+// Matrix-core decode plan: a grid of about 8 waves per compute unit, each
+// streaming as long a run of blocks as that allows (4 to 64 blocks), with the
+// partitions of a context balanced. Measured on MI355X: larger runs and fewer
+// resident waves stream faster (8B-, 70B-shaped, variable-length and
 // sliding-window workloads), as long as every compute unit has work.
-constexpr int kTargetWaves = 2048;
+int64_t target_waves() { return 8 * (int64_t)pa::device_cus(); }
 
 // Runs of blocks per wave and partitions for `w` waves per workgroup.
 void mfma_partitions(int64_t units, int32_t span, int32_t w, int32_t* bpw, int32_t* nparts) {
@@ -144,7 +183,8 @@ void mfma_partitions(int64_t units, int32_t span, int32_t w, int32_t* bpw, int32
     if (tokens > 0) {   // explicit partition size (pa_set_decode_partition_tokens)
         b = tokens / (w * kBlockSize);
     } else {
-        const int64_t want = (span * units + kTargetWaves - 1) / kTargetWaves;
+        const int64_t tw = target_waves();
+        const int64_t want = (span * units + tw - 1) / tw;
         b = (int32_t)std::min<int64_t>(64, std::max<int64_t>(4, want));
         const int32_t p = (span + w * b - 1) / (w * b);
         b = (span + p * w - 1) / (p * w);   // balance the partitions
@@ -166,15 +206,14 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
                             : (G % 4 == 0) ? 4 : (G % 2 == 0) ? 2 : 1;
     const int32_t hs = G / gw;
     // Each wave keeps `ring` blocks of K and V in flight in its own LDS ring
-    // (PA_DECODE_RING: 1 or 2).
-    int32_t ring = env_int("PA_DECODE_RING", 1);
-    if (ring != 1 && ring != 2) ring = 1;
+    // (option PA_OPT_DECODE_RING: 1 or 2).
+    const int32_t ring = option(PA_OPT_DECODE_RING);
     const int64_t units = (int64_t)batch * c->n_kv * hs;
     const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
     int32_t hs_wg = 1, waves_tok, bpw, nparts_max;
     if (mfma) {
-        waves_tok = env_int("PA_DECODE_WAVES", kMaxWaves);
-        if (waves_tok < 1 || waves_tok > kMaxWaves) waves_tok = kMaxWaves;
+        waves_tok = option(PA_OPT_DECODE_WAVES);
+        if (waves_tok == 0) waves_tok = kMaxWaves;
         const int32_t wave_lds = quant ? pa::quant_wave_bytes(c->head_dim, gw, ring)
                                        : mfma_wave_bytes(ring, tile, gw, c->head_dim);
         while (waves_tok > 1 && waves_tok * wave_lds > kLdsBytes) --waves_tok;
@@ -182,10 +221,11 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
     } else {
         // VALU kernel: 8 waves when there are at least as many (sequence, KV head,
         // head slice) units as compute units, else 4 so that long contexts split
-        // into more, smaller workgroups (PA_DECODE_WAVES overrides); 2048-token
-        // partitions unless overridden. The waves may also split over head slices.
-        int32_t max_waves = env_int("PA_DECODE_WAVES", units >= kComputeUnits ? kMaxWaves : 4);
-        if (max_waves < 1 || max_waves > kMaxWaves) max_waves = kMaxWaves;
+        // into more, smaller workgroups (option PA_OPT_DECODE_WAVES overrides);
+        // 2048-token partitions unless overridden. The waves may also split over
+        // head slices.
+        int32_t max_waves = option(PA_OPT_DECODE_WAVES);
+        if (max_waves == 0) max_waves = units >= pa::device_cus() ? kMaxWaves : 4;
         while (max_waves > 1 && max_waves * ring * 2 * tile > kLdsBytes) --max_waves;
         for (int32_t d = max_waves; d >= 1; --d)
             if (hs % d == 0) {
@@ -219,9 +259,9 @@ int make_plan(int32_t batch, int32_t n_q, int32_t max_blocks, const pa_cache_des
 size_t round16(size_t n) { return (n + 15) & ~(size_t)15; }
 
 // Workspace of a bf16 prefill over contiguous keys: the f16 copy of v, then one
-// flag byte per (sequence, KV head, 64-key tile). PA_PREFILL_STAGE_V=0 turns the
-// staging off (P V then stays in bf16 hi + lo parts).
-bool prefill_stages(pa_dtype dtype) { return dtype == PA_BF16 && env_int("PA_PREFILL_STAGE_V", 1) != 0; }
+// flag byte per (sequence, KV head, 64-key tile). Option PA_OPT_PREFILL_STAGE_V = 0
+// turns the staging off (P V then stays in bf16 hi + lo parts).
+bool prefill_stages(pa_dtype dtype) { return dtype == PA_BF16 && option(PA_OPT_PREFILL_STAGE_V) != 0; }
 size_t prefill_stage_v_bytes(int32_t batch, int32_t seq_len, int32_t n_kv, int32_t head_dim) {
     return round16((size_t)batch * seq_len * n_kv * head_dim * 2);
 }
@@ -292,7 +332,7 @@ struct MultiPlan {
 bool multi_uses_mfma(int32_t G, int32_t q_rows, const pa_cache_desc* c) {
     const int64_t pairs = (int64_t)G * q_rows;
     return (c->dtype == PA_BF16 || c->dtype == PA_F16) && pairs % 4 == 0 && pairs <= 16 &&
-           env_int("PA_DECODE_MFMA", 1) != 0;
+           option(PA_OPT_DECODE_MATRIX_CORES) != 0;
 }
 
 MultiPlan multi_plan(int32_t batch, int32_t q_rows, int32_t n_q, int32_t max_blocks, const pa_cache_desc* c) {
@@ -303,8 +343,8 @@ MultiPlan multi_plan(int32_t batch, int32_t q_rows, int32_t n_q, int32_t max_blo
         pl.mfma = 1;
         pl.gw = pairs % 16 == 0 ? 16 : pairs % 8 == 0 ? 8 : 4;
         pl.hsg = pairs / pl.gw;
-        int32_t w = env_int("PA_DECODE_WAVES", kMaxWaves);
-        if (w < 1 || w > kMaxWaves) w = kMaxWaves;
+        int32_t w = option(PA_OPT_DECODE_WAVES);
+        if (w == 0) w = kMaxWaves;
         const int32_t tile = kBlockSize * c->head_dim * elem_bytes(c->dtype);
         while (w > 1 && w * mfma_wave_bytes(1, tile, pl.gw, c->head_dim) > kLdsBytes) --w;
         pl.waves_tok = w;
@@ -331,12 +371,9 @@ MultiPlan multi_plan(int32_t batch, int32_t q_rows, int32_t n_q, int32_t max_blo
     return pl;
 }
 
-// ---- PA_VALIDATE: host-side checks of device-resident metadata ----------------------
+// ---- debug mode (option PA_OPT_VALIDATE): host-side checks of device-resident metadata
 
-bool validate_enabled() {
-    const char* v = std::getenv("PA_VALIDATE");
-    return v && v[0] == '1' && v[1] == 0;
-}
+bool validate_enabled() { return option(PA_OPT_VALIDATE) != 0; }
 
 template <class T>
 int fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s, const char* what) {
@@ -344,7 +381,7 @@ int fetch(std::vector<T>& dst, const T* src, size_t n, hipStream_t s, const char
     if (n == 0) return PA_OK;
     hipError_t e = hipMemcpyAsync(dst.data(), src, n * sizeof(T), hipMemcpyDeviceToHost, s);
     if (e == hipSuccess) e = hipStreamSynchronize(s);
-    if (e != hipSuccess) return fail(PA_ERR_HIP, "PA_VALIDATE: copying %s: %s", what, hipGetErrorString(e));
+    if (e != hipSuccess) return fail(PA_ERR_HIP, "validate: copying %s: %s", what, hipGetErrorString(e));
     return PA_OK;
 }
 
@@ -358,10 +395,10 @@ int validate_slots(const int64_t* slots_dev, int32_t n, const pa_cache_desc* c, 
         const int64_t x = slots[t];
         if (x < 0) continue;
         if (x >= num_slots)
-            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: slot_mapping[%d] = %lld is past the pool (%lld slots)",
+            return fail(PA_ERR_INVALID_ARG, "validate: slot_mapping[%d] = %lld is past the pool (%lld slots)",
                         t, (long long)x, (long long)num_slots);
         if (!seen.insert(x).second)
-            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: slot %lld appears twice in slot_mapping", (long long)x);
+            return fail(PA_ERR_INVALID_ARG, "validate: slot %lld appears twice in slot_mapping", (long long)x);
     }
     return PA_OK;
 }
@@ -380,14 +417,14 @@ int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev
     std::unordered_map<int32_t, int32_t> readers;   // physical block -> sequences attending it
     for (int32_t b = 0; b < batch; ++b) {
         if (ctx[b] < 0 || ctx[b] > cap)
-            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: context_lens[%d] = %d is outside [0, %lld]", b,
+            return fail(PA_ERR_INVALID_ARG, "validate: context_lens[%d] = %d is outside [0, %lld]", b,
                         ctx[b], (long long)cap);
         const int32_t nblk = (ctx[b] + c->block_size - 1) / c->block_size;
         const int32_t first = window > 0 ? std::max(0, ctx[b] - rows + 1 - window) : 0;
         for (int32_t j = first / c->block_size; j < nblk; ++j) {
             const int32_t phys = bt[(size_t)b * max_blocks + j];
             if (phys < 0 || phys >= c->num_blocks)
-                return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: block_table[%d][%d] = %d is outside the pool (%d blocks)",
+                return fail(PA_ERR_INVALID_ARG, "validate: block_table[%d][%d] = %d is outside the pool (%d blocks)",
                             b, j, phys, c->num_blocks);
             ++readers[phys];
         }
@@ -399,18 +436,18 @@ int validate_decode(int32_t batch, const pa_cache_desc* c, const int32_t* bt_dev
     for (int32_t b = 0; b < batch; ++b) {
         if (slots[b] < 0) continue;
         if (ctx[b] < 1)
-            return fail(PA_ERR_INVALID_ARG, "PA_VALIDATE: sequence %d appends a token but its context is empty", b);
+            return fail(PA_ERR_INVALID_ARG, "validate: sequence %d appends a token but its context is empty", b);
         const int32_t pos = ctx[b] - 1;
         const int64_t want = (int64_t)bt[(size_t)b * max_blocks + pos / c->block_size] * c->block_size +
                              pos % c->block_size;
         if (slots[b] != want)
             return fail(PA_ERR_INVALID_ARG,
-                        "PA_VALIDATE: slot_mapping[%d] = %lld, but position %d of sequence %d is slot %lld",
+                        "validate: slot_mapping[%d] = %lld, but position %d of sequence %d is slot %lld",
                         b, (long long)slots[b], pos, b, (long long)want);
         const int32_t phys = (int32_t)(slots[b] / c->block_size);
         if (readers[phys] > 1)
             return fail(PA_ERR_INVALID_ARG,
-                        "PA_VALIDATE: sequence %d appends into block %d, which another sequence also reads", b, phys);
+                        "validate: sequence %d appends into block %d, which another sequence also reads", b, phys);
     }
     return PA_OK;
 }
@@ -461,13 +498,23 @@ int resolve_workspace(size_t need, void** ws, std::unique_lock<std::mutex>* lock
 
 extern "C" {
 
-int32_t pa_version(void) { return 300; }
+int32_t pa_version(void) { return 301; }
 
 const char* pa_last_error(void) { return g_err; }
 
 int32_t pa_set_decode_partition_tokens(int32_t tokens) {
     if (tokens < 0 || (tokens % kBlockSize) != 0) return -1;
     return g_partition_tokens.exchange(tokens);
+}
+
+int32_t pa_set_option(int32_t o, int32_t value) {
+    if (o < 0 || o >= PA_OPT_COUNT || value < kOptions[o].lo || value > kOptions[o].hi) return -1;
+    return option_values()[o].exchange(value);
+}
+
+int32_t pa_get_option(int32_t o) {
+    if (o < 0 || o >= PA_OPT_COUNT) return -1;
+    return option(static_cast<pa_option>(o));
 }
 
 int pa_set_workspace(void* workspace, size_t bytes) {
@@ -514,13 +561,13 @@ namespace {
 // windowed call plans for a shorter span). With fixed runs of blocks per wave
 // (an explicit partition size) the partition count grows with the span, so
 // max_blocks bounds it. Otherwise each wave gets at least span * units /
-// kTargetWaves blocks and at least 4, so below the 64-block cap a span takes at
-// most min(ceil(kTargetWaves / (waves * units)), ceil(max_blocks / (4 * waves)))
+// target_waves() blocks and at least 4, so below the 64-block cap a span takes at
+// most min(ceil(target_waves() / (waves * units)), ceil(max_blocks / (4 * waves)))
 // partitions, and at the cap the count again grows with the span.
 int32_t mfma_parts_bound(int32_t nparts_at_max, int64_t units, int32_t waves, int32_t max_blocks) {
     if (g_partition_tokens.load() > 0) return nparts_at_max;
     const int64_t w = waves;
-    const int64_t by_waves = (kTargetWaves + w * units - 1) / (w * units);
+    const int64_t by_waves = (target_waves() + w * units - 1) / (w * units);
     const int64_t by_min_run = (max_blocks + 4 * w - 1) / (4 * w);
     return (int32_t)std::max<int64_t>(nparts_at_max, std::min(by_waves, by_min_run));
 }

@@ -130,4 +130,8 @@ inline bool prefill_grid_fits(int rows, int n_q, int batch, int group) {
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);
 
+// Compute units of the current device, queried once per device; 256 (MI355X)
+// when no device can be queried.
+int device_cus();
+
 }  // namespace pa

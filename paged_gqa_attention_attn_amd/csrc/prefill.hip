@@ -638,17 +638,6 @@ template <int D> __global__ __launch_bounds__(256) void stage_paged_v_f16_kernel
     }
 }
 
-// Compute units of the current device (cached per device).
-int device_cus() {
-    static std::atomic<int> cus[64] = {};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    int n = cus[dev].load(std::memory_order_relaxed);
-    if (n == 0 && hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess)
-        cus[dev].store(n, std::memory_order_relaxed);
-    return n;
-}
-
 template <class E, int D, bool PAGED> hipError_t launch_typed(const PrefillArgs& args, hipStream_t s) {
     PrefillArgs a = args;
     a.resident_wgs = device_cus();   // one 8-wave workgroup and its ring per compute unit

@@ -17,3 +17,18 @@ def pytest_configure(config):
 def orc():
     import oracle
     return oracle.get()
+
+
+@pytest.fixture
+def option():
+    """set(name, value) for the library's kernel-choice options, undone after the test."""
+    import paged_gqa_attention_attn_amd as pa
+    saved = {}
+
+    def set_(name, value):
+        prev = pa.set_option(name, int(value))
+        saved.setdefault(name, prev)
+
+    yield set_
+    for name, prev in saved.items():
+        pa.set_option(name, prev)

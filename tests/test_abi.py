@@ -44,7 +44,41 @@ def test_header_and_exports_agree(L):
 
 
 def test_version(L):
-    assert L.pa_version() == 300
+    assert L.pa_version() == 301
+
+
+def test_options_set_get_and_ranges(L):
+    ranges = {"decode_matrix_cores": (0, 1), "decode_ring": (1, 2), "decode_waves": (0, 8),
+              "prefill_stage_v": (0, 1), "validate": (0, 1)}
+    assert set(ranges) == set(_lib.OPTIONS)
+    assert L.pa_get_option(-1) == -1 and L.pa_get_option(len(ranges)) == -1
+    assert L.pa_set_option(len(ranges), 0) == -1
+    for name, (lo, hi) in ranges.items():
+        o = _lib.OPTIONS[name][0]
+        start = L.pa_get_option(o)
+        assert lo <= start <= hi
+        assert L.pa_set_option(o, lo - 1) == -1 and L.pa_set_option(o, hi + 1) == -1
+        assert L.pa_get_option(o) == start            # a rejected value changes nothing
+        assert L.pa_set_option(o, hi) == start
+        assert L.pa_set_option(o, lo) == hi
+        assert L.pa_get_option(o) == lo
+        assert L.pa_set_option(o, start) == lo
+
+
+def test_options_start_from_the_environment():
+    """Each option's first value comes from its variable; bad values give the default."""
+    import os
+    import subprocess
+    import sys
+    if not _lib.LIB_PATH.exists():
+        pytest.skip("libpagedattn.so not built")
+    env = dict(os.environ, PA_DECODE_MFMA="0", PA_DECODE_RING="2", PA_DECODE_WAVES="9",
+               PA_PREFILL_STAGE_V="x", PA_VALIDATE="1")
+    code = ("from paged_gqa_attention_attn_amd import _lib; L = _lib.load(); "
+            "print([L.pa_get_option(i) for i in range(5)])")
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True,
+                         cwd=Path(__file__).resolve().parent.parent).stdout.strip()
+    assert out == "[0, 2, 0, 1, 1]"
 
 
 def decode(L, **kw):
@@ -206,14 +240,14 @@ def test_prefill_rejects(L, kw, code):
     assert prefill(L, **kw) == code
 
 
-def test_prefill_workspace_bytes(L, monkeypatch):
+def test_prefill_workspace_bytes(L, option):
     # bf16: an f16 copy of v ([B][S][n_kv][d], 2 bytes each), then one flag byte per
     # (sequence, KV head, 64-key tile), each part rounded up to 16 bytes.
     assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 2, 4096, 8, 128) == 2 * 4096 * 8 * 128 * 2 + 1024
     assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 1, 65, 1, 64) == 65 * 64 * 2 + 16
     assert L.pa_prefill_workspace_bytes(_lib.PA_F16, 2, 4096, 8, 128) == 0
     assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 0, 4096, 8, 128) == 0
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    option("prefill_stage_v", 0)
     assert L.pa_prefill_workspace_bytes(_lib.PA_BF16, 2, 4096, 8, 128) == 0
 
 
@@ -266,7 +300,7 @@ def test_chunked_prefill_empty_is_a_noop(L):
     assert chunked(L, B=0) == PA_OK
 
 
-def test_chunked_prefill_workspace(L, monkeypatch):
+def test_chunked_prefill_workspace(L, option):
     # bf16: an f16 copy of the V blocks the call may read ([B][max_blocks][n_kv][16][d]),
     # then one flag byte per (sequence, KV head, block), each part rounded up to 16 bytes;
     # nothing past 256 MiB, nothing for f16 caches or with PA_PREFILL_STAGE_V=0.
@@ -280,7 +314,7 @@ def test_chunked_prefill_workspace(L, monkeypatch):
     assert "workspace" in _lib.last_error()
     assert chunked(L, ws=FAKE + 8, ws_bytes=need) == INVALID
     assert "aligned" in _lib.last_error()
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    option("prefill_stage_v", 0)
     assert L.pa_chunked_prefill_workspace_bytes(2, 256, desc(n_kv=8)) == 0
 
 
@@ -315,7 +349,7 @@ def _partials(rows):
     return 2 * rows * 4 + rows * 128 * 4   # m and l (fp32 each), then acc [rows][128]
 
 
-def test_decode_multi_workspace_query(L, monkeypatch):
+def test_decode_multi_workspace_query(L, option):
     # Multi-row kernel (G * q_rows = 8 * 4 = 32 (head, row) pairs): 2048-token partitions,
     # so 4096-token contexts need (m, l, acc) for 2 partitions of every (sequence, row, head).
     assert L.pa_decode_multi_workspace_bytes(4, 4, 64, 128, desc(nb=4096, n_kv=8)) == 0
@@ -324,7 +358,7 @@ def test_decode_multi_workspace_query(L, monkeypatch):
     # (sequence, KV head) units take 4 partitions of a 128-block table ...
     assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 128, desc(nb=4096, n_kv=8)) == _partials(4 * 4 * 32 * 4)
     # ... unless that kernel is turned off.
-    monkeypatch.setenv("PA_DECODE_MFMA", "0")
+    option("decode_matrix_cores", 0)
     assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 128, desc(nb=4096, n_kv=8)) == 0
     assert L.pa_decode_multi_workspace_bytes(4, 4, 32, 256, desc(nb=4096, n_kv=8)) == _partials(4 * 4 * 32 * 2)
     assert L.pa_decode_multi_workspace_bytes(4, 0, 32, 256, desc(nb=4096, n_kv=8)) == 0

@@ -35,10 +35,10 @@ def pa():
 
 
 @pytest.fixture(params=["default", "valu"])
-def decode_kernel(request, monkeypatch):
+def decode_kernel(request, option):
     """Decode runs with the default kernel choice (matrix cores where the group allows)
     and with the VALU kernels forced."""
-    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+    option("decode_matrix_cores", 0 if request.param == "valu" else 1)
     return request.param
 
 
@@ -231,9 +231,9 @@ PREFILL = {
 
 
 @pytest.fixture(params=["staged", "unstaged"])
-def stage_v(request, monkeypatch):
+def stage_v(request, option):
     """The prefill kernel with its f16 copy of V (the default) and with it switched off."""
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "1" if request.param == "staged" else "0")
+    option("prefill_stage_v", 1 if request.param == "staged" else 0)
     return request.param
 
 

@@ -1,12 +1,11 @@
-"""The C ABI's workspace options and its PA_VALIDATE debug mode, on the GPU.
+"""The C ABI's workspace options and its validate debug mode, on the GPU.
 
 Every call here goes through the C ABI with real device buffers. The results
 with a library-owned or a default workspace must equal, bit for bit, those with
-an explicit one; PA_VALIDATE=1 must reject bad device metadata before anything
+an explicit one; the validate option must reject bad device metadata before anything
 is enqueued, and leave valid calls' results unchanged.
 """
 import ctypes
-import os
 
 import pytest
 import torch
@@ -28,14 +27,9 @@ def pa():
 
 
 @pytest.fixture
-def validate():
-    old = os.environ.get("PA_VALIDATE")
-    os.environ["PA_VALIDATE"] = "1"
-    yield
-    if old is None:
-        del os.environ["PA_VALIDATE"]
-    else:
-        os.environ["PA_VALIDATE"] = old
+def validate(option):
+    option("validate", 1)
+    return option
 
 
 def _split_case():
@@ -92,11 +86,11 @@ def test_default_workspace(pa):
 
 def test_validate_passes_good_calls_unchanged(pa, validate):
     case = _split_case()
-    say("[boundary] PA_VALIDATE=1 on valid metadata")
+    say("[boundary] the validate option on valid metadata")
     kp, vp = case.k_pool.clone(), case.v_pool.clone()
     pa.kv_append(case.new_k, case.new_v, case.slot_mapping, kp, vp)
     got = pa.paged_attn_decode(case.q, kp, vp, case.block_table, case.context_lens, case.scale)
-    os.environ["PA_VALIDATE"] = "0"
+    validate("validate", 0)
     kp2, vp2 = case.k_pool.clone(), case.v_pool.clone()
     pa.kv_append(case.new_k, case.new_v, case.slot_mapping, kp2, vp2)
     want = pa.paged_attn_decode(case.q, kp2, vp2, case.block_table, case.context_lens, case.scale)
@@ -111,12 +105,12 @@ def test_validate_rejects_bad_decode_metadata(pa, validate):
                      dtype=torch.uint8, device="cuda")
     bt = case.block_table.clone()
     bt[1, 3] = case.num_blocks          # inside sequence 1's context, outside the pool
-    say("[boundary] PA_VALIDATE rejects an out-of-pool block id")
+    say("[boundary] validate rejects an out-of-pool block id")
     assert _raw_decode(case, bt, case.context_lens, out, ws.data_ptr(), ws.numel()) == _lib.PA_ERR_INVALID_ARG
     assert "block_table[1][3]" in _lib.last_error()
     ctx = case.context_lens.clone()
     ctx[2] = case.max_blocks_per_seq * 16 + 1
-    say("[boundary] PA_VALIDATE rejects a context past the block table")
+    say("[boundary] validate rejects a context past the block table")
     assert _raw_decode(case, case.block_table, ctx, out, ws.data_ptr(), ws.numel()) == _lib.PA_ERR_INVALID_ARG
     assert "context_lens[2]" in _lib.last_error()
     torch.cuda.synchronize()
@@ -126,7 +120,7 @@ def test_validate_rejects_bad_decode_metadata(pa, validate):
 def test_validate_rejects_bad_slots(pa, validate):
     case = wl.make_config(1, device="cuda")
     kp, vp = case.k_pool.clone(), case.v_pool.clone()
-    say("[boundary] PA_VALIDATE rejects repeated and out-of-pool slots")
+    say("[boundary] validate rejects repeated and out-of-pool slots")
     dup = torch.tensor([5, 5], dtype=torch.int64, device="cuda")
     with pytest.raises(pa.PagedAttnError, match="twice"):
         pa.kv_append(case.new_k, case.new_v, dup, kp, vp)
@@ -142,7 +136,7 @@ def test_validate_rejects_misplaced_fused_append(pa, validate):
     kp, vp = case.k_pool.clone(), case.v_pool.clone()
     slots = case.slot_mapping.clone()
     slots[0] += 1                          # not position ctx - 1 of sequence 0
-    say("[boundary] PA_VALIDATE rejects a fused append at the wrong slot")
+    say("[boundary] validate rejects a fused append at the wrong slot")
     with pytest.raises(pa.PagedAttnError, match="position"):
         pa.paged_attn_decode_append(case.q, case.new_k, case.new_v, slots, kp, vp, case.block_table,
                                     case.context_lens, case.scale)

@@ -68,11 +68,11 @@ def test_chunked_prefill_matches_oracle(pa, shape):
 
 
 @pytest.mark.parametrize("stage", ["1", "0"], ids=["staged", "unstaged"])
-def test_whole_prompt_chunk_equals_contiguous_prefill_bitwise(pa, monkeypatch, stage):
+def test_whole_prompt_chunk_equals_contiguous_prefill_bitwise(pa, option, stage):
     # A chunk that is the whole prompt runs the same tile arithmetic as the
     # contiguous prefill kernel (both with V copied to f16, or both without):
     # every output bit must agree.
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", stage)
+    option("prefill_stage_v", int(stage))
     c = wl.make_prefill_case(batch=2, seq_len=300, n_q=8, n_kv=2, head_dim=128, dtype="bf16",
                              seed=77, device="cuda")
     say(f"[chunk] whole-prompt chunk vs contiguous prefill, bitwise, PA_PREFILL_STAGE_V={stage}")
@@ -168,7 +168,7 @@ def test_bf16_output(pa):
     assert (np.abs(got - want) <= 2e-3 + 2.0**-8 * np.abs(want)).all()
 
 
-def test_chunked_prefill_past_the_copy_cap_keeps_the_bf16_product(pa, monkeypatch):
+def test_chunked_prefill_past_the_copy_cap_keeps_the_bf16_product(pa, option):
     """A block table 9000 blocks wide over 8 KV heads would need a 295 MB f16 copy of V,
     past the 256 MiB a call stages: P V then keeps the bf16 hi + lo product. The result
     matches the oracle and, bit for bit, the same call on the narrow table with the copy
@@ -181,7 +181,7 @@ def test_chunked_prefill_past_the_copy_cap_keeps_the_bf16_product(pa, monkeypatc
     wide = torch.full((c.batch, 9000), -1, dtype=torch.int32, device="cuda")   # unused entries
     wide[:, :c.max_blocks_per_seq] = c.block_table
     got = pa.paged_attn_chunked_prefill(c.q, kp, vp, wide, c.context_lens, c.scale)
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    option("prefill_stage_v", 0)
     unstaged = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
     torch.cuda.synchronize()
     want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",

@@ -22,8 +22,8 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(params=["default", "valu"], autouse=True)
-def decode_kernel(request, monkeypatch):
-    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+def decode_kernel(request, option):
+    option("decode_matrix_cores", 0 if request.param == "valu" else 1)
     return request.param
 
 

@@ -83,12 +83,12 @@ def test_partition_sizes_agree(pa, tokens):
 
 
 @pytest.mark.parametrize("kernel", ["mfma", "multi"])
-def test_blocks_past_the_first_rows_position(pa, monkeypatch, kernel):
+def test_blocks_past_the_first_rows_position(pa, option, kernel):
     """One block per wave: a wave whose only block lies past row 0's position (or
     wholly before a later row's window) attends nothing for that row's columns,
     which must give weights of 0, not NaN."""
     if kernel == "multi":
-        monkeypatch.setenv("PA_DECODE_MFMA", "0")
+        option("decode_matrix_cores", 0)
     c = wl.make_chunk_case(batch=4, chunk_len=4, prefix_lens=[93, 77, 12, 2000], n_q=32, n_kv=8,
                            head_dim=128, dtype="bf16", seed=64, device="cuda")
     say(f"[multi] {kernel}: contexts {[p + 4 for p in (93, 77, 12, 2000)]}, one block per wave")

@@ -139,14 +139,14 @@ SPLIT_SHAPES = ["gqa4_bf16_ragged_causal", "gqa4_bf16_ragged_full", "d64_bf16", 
 
 
 @pytest.mark.parametrize("name", SPLIT_SHAPES)
-def test_prefill_bf16_without_staging(pa, monkeypatch, name):
+def test_prefill_bf16_without_staging(pa, option, name):
     """PA_PREFILL_STAGE_V=0 keeps P V in bf16 hi + lo parts; both forms meet the oracle."""
     B, S, n_q, n_kv, d, dt, causal = SHAPES[name]
     say(f"[prefill unstaged] {name}: B={B} S={S} n_q={n_q} n_kv={n_kv} d={d} causal={causal}")
     q, k, v = _inputs(B, S, n_q, n_kv, d, dt, seed=len(name) * 31 + S)
     scale = d ** -0.5
     staged = pa.paged_attn_prefill(q, k, v, causal, scale)
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", "0")
+    option("prefill_stage_v", 0)
     assert pa.prefill_workspace_bytes(q.dtype, B, S, n_kv, d) == 0
     plain = pa.paged_attn_prefill(q, k, v, causal, scale)
     torch.cuda.synchronize()

@@ -34,8 +34,8 @@ def pa():
 
 
 @pytest.fixture(params=["default", "valu"])
-def decode_kernel(request, monkeypatch):
-    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+def decode_kernel(request, option):
+    option("decode_matrix_cores", 0 if request.param == "valu" else 1)
     return request.param
 
 
@@ -125,8 +125,8 @@ def test_decode_multi(pa, rows, n_q, scale):
 @pytest.mark.parametrize("scale", SCALES)
 @pytest.mark.parametrize("alibi", [False, True])
 @pytest.mark.parametrize("stage", ["1", "0"])
-def test_prefill(pa, monkeypatch, stage, alibi, scale):
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", stage)
+def test_prefill(pa, option, stage, alibi, scale):
+    option("prefill_stage_v", int(stage))
     B, S, n_q, n_kv, d = 2, 200, 8, 2, 128
     g = torch.Generator(device="cuda").manual_seed(5)
     q = torch.randn(B, S, n_q, d, generator=g, device="cuda").bfloat16()

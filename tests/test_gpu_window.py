@@ -20,10 +20,10 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.fixture(params=["default", "valu"])
-def decode_kernel(request, monkeypatch):
+def decode_kernel(request, option):
     """Single-row decode tests run with the default kernel choice (matrix cores for
     bf16/f16 groups of 4, 8 or 16) and with the VALU kernel forced."""
-    monkeypatch.setenv("PA_DECODE_MFMA", "0" if request.param == "valu" else "1")
+    option("decode_matrix_cores", 0 if request.param == "valu" else 1)
     return request.param
 
 
@@ -216,8 +216,8 @@ def test_prefill_window_matches_oracle(pa, window):
 
 
 @pytest.mark.parametrize("stage", ["1", "0"], ids=["staged", "unstaged"])
-def test_whole_prompt_chunk_equals_contiguous_prefill_with_window_bitwise(pa, monkeypatch, stage):
-    monkeypatch.setenv("PA_PREFILL_STAGE_V", stage)
+def test_whole_prompt_chunk_equals_contiguous_prefill_with_window_bitwise(pa, option, stage):
+    option("prefill_stage_v", int(stage))
     c = wl.make_prefill_case(batch=2, seq_len=300, n_q=8, n_kv=2, head_dim=128, dtype="bf16",
                              seed=78, device="cuda")
     say(f"[window] whole-prompt chunk vs contiguous prefill, W=90, bitwise, PA_PREFILL_STAGE_V={stage}")
