@@ -219,7 +219,7 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  * causal mask M_ij = 0 for j <= i and -inf otherwise; [AE] 3.1 GQA grouping;
  * [IW] "Prefill 阶段维度流转".
  *
- *   q     [batch][seq_len][n_q][head_dim]   in dtype (bf16 or f16)
+ *   q     [batch][seq_len][n_q][head_dim]   in dtype (f32, bf16 or f16)
  *   k, v  [batch][seq_len][n_kv][head_dim]  in dtype
  *   causal  1: row i attends to keys 0..i; 0: to all seq_len keys
  *   scale   multiplies q.k (usually 1/sqrt(head_dim)); any finite value, as
@@ -241,9 +241,13 @@ int pa_paged_attn_decode_append(const void* q, const void* k_new, const void* v_
  *         finite value keep the bf16 product for the rows that read them.
  *         Option PA_OPT_PREFILL_STAGE_V = 0 turns the staging off.
  *         Calls that share a workspace must not overlap on the GPU.
- * Supported: head_dim 128 (and 64); dtype bf16 or f16; seq_len at most
- * 2^31 - 129 and ceil(seq_len / 128) * n_q * batch at most 2^31 - 1 (one
- * workgroup per 128 query rows of one head), else PA_ERR_UNSUPPORTED.
+ * Supported: head_dim 128 (and 64); dtype f32, bf16 or f16. bf16/f16: seq_len
+ * at most 2^31 - 257 and the workgroup count, ceil(seq_len / (256 / H)) *
+ * (n_q / H) * batch with H = 4, 2 or 1 query heads per workgroup (the largest
+ * dividing n_q / n_kv), at most 2^31 - 1. f32 (fp32 matrix-core kernel, one
+ * workgroup per 64 (row, head) pairs of a KV head, no workspace): seq_len *
+ * n_q / n_kv at most 2^31 - 65, n_kv and batch at most 65535. Otherwise
+ * PA_ERR_UNSUPPORTED.
  */
 size_t pa_prefill_workspace_bytes(pa_dtype dtype, int32_t batch, int32_t seq_len, int32_t n_kv,
                                   int32_t head_dim);
@@ -262,7 +266,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  * block table; [IW] "工程优化怎么嵌进公式" (verifying several drafted tokens at
  * once turns decode's vector products into small matrix products).
  *
- *   q             [batch][q_rows][n_q][head_dim] in cache->dtype (bf16 or f16)
+ *   q             [batch][q_rows][n_q][head_dim] in cache->dtype (f32, bf16 or f16)
  *   k_cache, v_cache  pools described by `cache`, already holding the rows' own
  *                 K/V (pa_kv_append of the q_rows new tokens first)
  *   block_table, context_lens, scale  as for pa_paged_attn_decode
@@ -277,8 +281,10 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  * products, so each K/V byte is read once per step. Rows at negative positions
  * (context_lens[b] < q_rows) are zero; a context past the block table's reach or
  * an out-of-pool block id among those read gives NaN rows. Results equal
- * pa_paged_attn_chunked_prefill with chunk_len = q_rows up to rounding. The
- * workspace size covers any window. Supported: head_dim 64 or 128.
+ * pa_paged_attn_chunked_prefill with chunk_len = q_rows up to rounding (bit for
+ * bit for f32 caches, which both calls serve with the same fp32 kernel and no
+ * workspace). The workspace size covers any window. Supported: head_dim 64 or
+ * 128; f32 within the limits given for pa_paged_attn_prefill.
  */
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache);
@@ -296,7 +302,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
  * is unchanged) and "Prefill 阶段维度流转"; [VC] (kernels take a block table);
  * [AE] 1.1 causal mask, 3.1 GQA grouping.
  *
- *   q             [batch][chunk_len][n_q][head_dim] in cache->dtype (bf16 or f16)
+ *   q             [batch][chunk_len][n_q][head_dim] in cache->dtype (f32, bf16 or f16)
  *   k_cache, v_cache  pools described by `cache`, already holding the chunk's own
  *                 K/V (pa_kv_append first)
  *   block_table   int32 [batch][max_blocks_per_seq]

@@ -16,7 +16,7 @@ ROOT = PKG.parent
 CSRC = PKG / "csrc"
 BUILD_DIR = PKG / "_build"
 LIB_PATH = PKG / "libpagedattn.so"
-SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "decode_mfma.hip", "decode_quant.hip", "decode_multi.hip", "prefill.hip"]
+SOURCES = ["api.hip", "kv_append.hip", "decode.hip", "decode_mfma.hip", "decode_quant.hip", "decode_multi.hip", "prefill.hip", "attn_f32.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 

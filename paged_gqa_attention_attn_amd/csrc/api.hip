@@ -744,6 +744,46 @@ int decode_impl(const void* q, int32_t batch, int32_t n_q, const void* k_cache, 
 
 }  // namespace
 
+namespace {
+
+// Arguments of the fp32 kernel over the paged cache: `rows` query rows per
+// sequence at the end of its context (chunked prefill, multi-row decode).
+pa::PrefillArgs paged_f32_args(const void* q, int32_t batch, int32_t rows, int32_t n_q, const void* k_cache,
+                               const void* v_cache, const pa_cache_desc* cache, const int32_t* block_table,
+                               int32_t max_blocks, const int32_t* context_lens, float scale, int32_t window,
+                               const float* alibi_slopes, void* out) {
+    pa::PrefillArgs a{};
+    a.q = q;
+    a.k = k_cache;
+    a.v = v_cache;
+    a.out = out;
+    a.batch = batch;
+    a.seq_len = rows;
+    a.n_q = n_q;
+    a.n_kv = cache->n_kv;
+    a.group = n_q / cache->n_kv;
+    a.causal = 1;
+    fold_scale(scale, PA_F32, &a);
+    a.out_f32 = 1;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.max_blocks = max_blocks;
+    a.num_blocks = cache->num_blocks;
+    a.window = window;
+    a.alibi = alibi_slopes;
+    return a;
+}
+
+int launch_f32(const pa::PrefillArgs& a, int32_t head_dim, void* stream, const char* what) {
+    const hipError_t e = pa::launch_attn_f32(a, head_dim, static_cast<hipStream_t>(stream));
+    if (e == hipErrorNotSupported)
+        return fail(PA_ERR_UNSUPPORTED, "%s: f32 rows * group, n_kv or batch past the kernel's grid", what);
+    if (e != hipSuccess) return hip_fail(e, "f32 attention launch");
+    return PA_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int pa_paged_attn_decode(const void* q, int32_t batch, int32_t n_q, const void* k_cache,
@@ -793,8 +833,8 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
                           const float* alibi_slopes,
                           void* out, pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                           void* stream) {
-    if (dtype != PA_BF16 && dtype != PA_F16)
-        return fail(PA_ERR_UNSUPPORTED, "prefill supports bf16 and f16 inputs");
+    if (dtype != PA_BF16 && dtype != PA_F16 && dtype != PA_F32)
+        return fail(PA_ERR_UNSUPPORTED, "prefill supports f32, bf16 and f16 inputs");
     if (out_dtype != PA_F32 && out_dtype != dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the input dtype");
     if (head_dim != 64 && head_dim != 128)
@@ -811,7 +851,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     if (window > 0 && !causal) return fail(PA_ERR_INVALID_ARG, "a sliding window needs causal == 1");
     if (alibi_slopes && !causal) return fail(PA_ERR_INVALID_ARG, "ALiBi slopes need causal == 1");
     if (batch == 0 || seq_len == 0) return PA_OK;
-    if (!pa::prefill_grid_fits(seq_len, n_q, batch, n_q / n_kv))
+    if (dtype != PA_F32 && !pa::prefill_grid_fits(seq_len, n_q, batch, n_q / n_kv))
         return fail(PA_ERR_UNSUPPORTED, "prefill: the number of workgroups (ceil(seq_len / rows per workgroup) * n_q / heads per workgroup * batch) exceeds one launch");
     if (!q || !k || !v || !out) return fail(PA_ERR_INVALID_ARG, "prefill: a pointer argument is NULL");
     if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out))
@@ -832,6 +872,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
     a.out_f32 = out_dtype == PA_F32;
     a.window = window;
     a.alibi = alibi_slopes;
+    if (dtype == PA_F32) return launch_f32(a, head_dim, stream, "prefill");
     std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (prefill_stages(dtype) && stage_grid_fits(batch, n_kv)) {
         const size_t need = prefill_stage_bytes(batch, seq_len, n_kv, head_dim);
@@ -856,6 +897,7 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache) {
     if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK || q_rows < 1) return 0;
+    if (cache->dtype == PA_F32) return 0;   // the fp32 kernel keeps no partials
     const MultiPlan pl = multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache);
     if (!pl.mfma) return pl.bytes;
     const int32_t np = mfma_parts_bound(pl.nparts_max, (int64_t)batch * cache->n_kv * pl.hsg, pl.waves_tok,
@@ -871,8 +913,8 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
-    if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
-        return fail(PA_ERR_UNSUPPORTED, "multi-row decode supports bf16 and f16 caches");
+    if (is_quant(cache->dtype))
+        return fail(PA_ERR_UNSUPPORTED, "multi-row decode supports f32, bf16 and f16 caches");
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
     if (q_rows < 1) return fail(PA_ERR_INVALID_ARG, "q_rows %d must be positive", q_rows);
@@ -887,6 +929,16 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: q, caches and out must be 16-byte aligned");
     if ((reinterpret_cast<uintptr_t>(block_table) & 3u) || (reinterpret_cast<uintptr_t>(context_lens) & 3u))
         return fail(PA_ERR_INVALID_ARG, "multi-row decode: block_table and context_lens must be 4-byte aligned");
+    if (cache->dtype == PA_F32) {   // the fp32 kernel of chunked prefill, q_rows rows per sequence
+        if (validate_enabled()) {
+            rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
+                                 static_cast<hipStream_t>(stream), q_rows, window);
+            if (rc) return rc;
+        }
+        pa::PrefillArgs a = paged_f32_args(q, batch, q_rows, n_q, k_cache, v_cache, cache, block_table,
+                                           max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out);
+        return launch_f32(a, cache->head_dim, stream, "multi-row decode");
+    }
     const MultiPlan pl = multi_plan(batch, q_rows, n_q, span_blocks(max_blocks_per_seq, q_rows, window), cache);
     std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (pl.bytes > 0) {
@@ -968,8 +1020,8 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
                                   void* stream) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq);
     if (rc) return rc;
-    if (cache->dtype != PA_BF16 && cache->dtype != PA_F16)
-        return fail(PA_ERR_UNSUPPORTED, "chunked prefill supports bf16 and f16 caches");
+    if (is_quant(cache->dtype))
+        return fail(PA_ERR_UNSUPPORTED, "chunked prefill supports f32, bf16 and f16 caches");
     if (out_dtype != PA_F32 && out_dtype != cache->dtype)
         return fail(PA_ERR_UNSUPPORTED, "out_dtype must be PA_F32 or the cache dtype");
     if (chunk_len < 0) return fail(PA_ERR_INVALID_ARG, "chunk_len %d < 0", chunk_len);
@@ -978,7 +1030,7 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
     if (reinterpret_cast<uintptr_t>(alibi_slopes) & 3u)
         return fail(PA_ERR_INVALID_ARG, "alibi_slopes must be 4-byte aligned");
     if (batch == 0 || chunk_len == 0) return PA_OK;
-    if (!pa::prefill_grid_fits(chunk_len, n_q, batch, n_q / cache->n_kv))
+    if (cache->dtype != PA_F32 && !pa::prefill_grid_fits(chunk_len, n_q, batch, n_q / cache->n_kv))
         return fail(PA_ERR_UNSUPPORTED, "chunked prefill: the number of workgroups exceeds one launch");
     if (!q || !k_cache || !v_cache || !block_table || !context_lens || !out)
         return fail(PA_ERR_INVALID_ARG, "chunked prefill: a pointer argument is NULL");
@@ -990,6 +1042,11 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
         rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens, nullptr,
                              static_cast<hipStream_t>(stream), chunk_len, window);
         if (rc) return rc;
+    }
+    if (cache->dtype == PA_F32) {
+        pa::PrefillArgs a = paged_f32_args(q, batch, chunk_len, n_q, k_cache, v_cache, cache, block_table,
+                                           max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out);
+        return launch_f32(a, cache->head_dim, stream, "chunked prefill");
     }
 
     pa::PrefillArgs a{};

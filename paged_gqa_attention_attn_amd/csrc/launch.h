@@ -129,6 +129,11 @@ inline bool prefill_grid_fits(int rows, int n_q, int batch, int group) {
 }
 
 hipError_t launch_prefill(const PrefillArgs& a, Elem e, int head_dim, hipStream_t s);
+// fp32 attention of seq_len query rows per sequence (contiguous prefill, or paged
+// chunked prefill / multi-row decode when block_table is set) on the fp32 matrix
+// cores; hipErrorNotSupported past its grid limits (ceil(seq_len * group / 64)
+// workgroups per KV head and sequence at most 2^31 - 1, n_kv and batch at most 65535).
+hipError_t launch_attn_f32(const PrefillArgs& a, int head_dim, hipStream_t s);
 
 // Compute units of the current device, queried once per device; 256 (MI355X)
 // when no device can be queried.

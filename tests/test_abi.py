@@ -219,7 +219,11 @@ def prefill(L, **kw):
 
 
 @pytest.mark.parametrize("kw,code", [
-    (dict(dtype=_lib.PA_F32), UNSUPPORTED),
+    (dict(dtype=_lib.PA_FP8_E4M3), UNSUPPORTED),
+    (dict(dtype=_lib.PA_F32, d=80), UNSUPPORTED),
+    (dict(dtype=_lib.PA_F32, out_dtype=_lib.PA_BF16), UNSUPPORTED),
+    (dict(dtype=_lib.PA_F32, S=2**30), UNSUPPORTED),              # rows * group past an int
+    (dict(dtype=_lib.PA_F32, n_q=65536, n_kv=65536), UNSUPPORTED),  # KV heads past grid y
     (dict(d=80), UNSUPPORTED),
     (dict(n_q=6, n_kv=4), INVALID),
     (dict(causal=2), INVALID),
@@ -277,7 +281,9 @@ def chunked(L, **kw):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(cache=None), INVALID, "descriptor"),
-    (dict(cache=desc(dtype=_lib.PA_F32)), UNSUPPORTED, "bf16 and f16"),
+    (dict(cache=desc(dtype=_lib.PA_INT8)), UNSUPPORTED, "quantised"),
+    (dict(cache=desc(dtype=_lib.PA_F32), out_dtype=_lib.PA_BF16), UNSUPPORTED, "out_dtype"),
+    (dict(cache=desc(dtype=_lib.PA_F32, n_kv=8), C=2**30, n_q=64), UNSUPPORTED, "grid"),
     (dict(cache=desc(d=96)), UNSUPPORTED, "head_dim"),
     (dict(C=-1), INVALID, "chunk_len"),
     (dict(n_q=7), INVALID, "multiple"),
@@ -293,6 +299,13 @@ def chunked(L, **kw):
 def test_chunked_prefill_rejects(L, kw, code, msg):
     assert chunked(L, **kw) == code
     assert msg in _lib.last_error()
+
+
+def test_f32_paths_take_no_workspace(L):
+    f32 = desc(nb=4096, n_kv=8, dtype=_lib.PA_F32)
+    assert L.pa_prefill_workspace_bytes(_lib.PA_F32, 2, 4096, 8, 128) == 0
+    assert L.pa_chunked_prefill_workspace_bytes(2, 256, f32) == 0
+    assert L.pa_decode_multi_workspace_bytes(4, 4, 64, 256, f32) == 0
 
 
 def test_chunked_prefill_empty_is_a_noop(L):
@@ -329,7 +342,9 @@ def multi(L, **kw):
 
 @pytest.mark.parametrize("kw,code,msg", [
     (dict(cache=None), INVALID, "descriptor"),
-    (dict(cache=desc(dtype=_lib.PA_F32)), UNSUPPORTED, "bf16 and f16"),
+    (dict(cache=desc(dtype=_lib.PA_FP8_E4M3)), UNSUPPORTED, "quantised"),
+    (dict(cache=desc(dtype=_lib.PA_F32), out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+    (dict(cache=desc(dtype=_lib.PA_F32), R=2**29, n_q=64), UNSUPPORTED, "grid"),
     (dict(R=0), INVALID, "q_rows"),
     (dict(n_q=7), INVALID, "multiple"),
     (dict(scale=float("nan")), INVALID, "finite"),

@@ -1,0 +1,219 @@
+"""GPU parity of the fp32 paths of prefill, chunked prefill and multi-row decode.
+
+The attention formula ("注意力演进与推理流程", section 1.1) fixes no element type, and
+the cache may hold f32 rows. These calls run on the fp32 matrix-core kernel and are
+compared with the fp64 oracle on every output element, within max-abs 1e-5 and
+norm-wise relative 1e-5: causal and full prefill, ragged lengths that span several
+64-row tiles and 16-key tiles, head_dim 64 and 128, MHA, GQA and MQA groupings,
+sliding windows, ALiBi, zero and negative scales, contexts shorter than the rows,
+and the NaN rows of bad metadata.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_helpers import assert_parity, nan_out, same_bits, say, stored_np
+from paged_gqa_attention_attn_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def pa():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import paged_gqa_attention_attn_amd as pa
+    pa._lib.load()  # raises if the HIP library is missing: no fallback
+    return pa
+
+
+def _slopes(n_q):
+    return (2.0 ** (-8.0 * (np.arange(n_q) + 1) / n_q)).astype(np.float32)
+
+
+def _inputs(B, S, n_q, n_kv, d, seed):
+    g = torch.Generator(device="cuda").manual_seed(seed)
+    q = torch.randn(B, S, n_q, d, generator=g, device="cuda")
+    k = torch.randn(B, S, n_kv, d, generator=g, device="cuda")
+    v = torch.randn(B, S, n_kv, d, generator=g, device="cuda")
+    return q, k, v
+
+
+PREFILL = {
+    # name: (B, S, n_q, n_kv, d, causal, window, alibi, scale)
+    "gqa4_causal_ragged": (2, 200, 8, 2, 128, True, 0, False, None),
+    "gqa4_full_ragged": (2, 200, 8, 2, 128, False, 0, False, None),
+    "one_token": (1, 1, 4, 2, 128, True, 0, False, None),
+    "mha_d64": (2, 97, 2, 2, 64, True, 0, False, None),
+    "mqa_300": (1, 300, 8, 1, 128, True, 0, False, None),
+    "g3_d64_full": (1, 70, 6, 2, 64, False, 0, False, None),
+    "window_90": (2, 333, 8, 2, 128, True, 90, False, None),
+    "alibi": (1, 260, 8, 2, 128, True, 0, True, None),
+    "window_alibi_d64": (1, 180, 4, 1, 64, True, 33, True, None),
+    "scale_zero": (1, 150, 4, 2, 128, True, 0, False, 0.0),
+    "scale_negative_full": (1, 150, 4, 2, 128, False, 0, False, -0.2),
+    "long_1000": (1, 1000, 4, 2, 128, True, 0, False, None),
+}
+
+
+@pytest.mark.parametrize("name", sorted(PREFILL))
+def test_prefill_f32(pa, name):
+    B, S, n_q, n_kv, d, causal, window, alibi, scale = PREFILL[name]
+    scale = d ** -0.5 if scale is None else scale
+    m = _slopes(n_q) if alibi else None
+    say(f"[f32] prefill {name}: B={B} S={S} {n_q}x{n_kv} d={d} causal={causal} W={window} alibi={alibi} "
+        f"scale={scale}")
+    q, k, v = _inputs(B, S, n_q, n_kv, d, seed=len(name) * 131 + S)
+    out = nan_out(q.shape)
+    pa.paged_attn_prefill(q, k, v, causal, scale, out=out, window=window,
+                          alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
+    torch.cuda.synchronize()
+    want = oracle.prefill(stored_np(q), stored_np(k), stored_np(v), "f32", causal, scale, window=window, alibi=m)
+    stats = assert_parity(out.cpu().numpy(), want, "f32", name)
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+def test_prefill_f32_run_twice_bitwise(pa):
+    q, k, v = _inputs(2, 300, 8, 2, 128, seed=9)
+    say("[f32] prefill twice, bitwise")
+    a = pa.paged_attn_prefill(q, k, v, True, 0.09)
+    b = pa.paged_attn_prefill(q, k, v, True, 0.09)
+    torch.cuda.synchronize()
+    assert same_bits(a, b)
+
+
+CHUNK = [
+    # (batch, chunk_len, prefix lengths, n_q, n_kv, head_dim, window, alibi)
+    (2, 64, [0, 0], 8, 2, 128, 0, False),
+    (2, 17, [5, 40], 8, 2, 128, 0, False),
+    (3, 128, [100, 333, 0], 32, 8, 128, 0, False),
+    (1, 200, [700], 4, 4, 64, 0, False),
+    (2, 1, [50, 3], 8, 1, 128, 0, False),
+    (3, 150, [10, 400, 77], 6, 2, 128, 0, False),
+    (2, 100, [0, 333], 8, 2, 128, 0, True),
+    (2, 90, [500, 20], 8, 2, 128, 64, False),
+    (1, 70, [300], 4, 1, 64, 50, True),
+]
+
+
+@pytest.mark.parametrize("shape", CHUNK, ids=[f"B{s[0]}_C{s[1]}_P{'-'.join(map(str, s[2]))}_{s[3]}x{s[4]}_d{s[5]}"
+                                              f"_W{s[6]}{'_alibi' if s[7] else ''}" for s in CHUNK])
+def test_chunked_prefill_f32(pa, shape):
+    B, C, pre, n_q, n_kv, d, window, alibi = shape
+    c = wl.make_chunk_case(batch=B, chunk_len=C, prefix_lens=pre, n_q=n_q, n_kv=n_kv, head_dim=d,
+                           dtype="f32", free_fraction=0.2, seed=sum(pre) + 17 * C + d, device="cuda")
+    m = _slopes(n_q) if alibi else None
+    say(f"[f32] chunked prefill B={B} C={C} prefix={pre} {n_q}x{n_kv} d={d} W={window} alibi={alibi}")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    out = nan_out(c.q.shape)
+    pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out, window=window,
+                                  alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
+    torch.cuda.synchronize()
+    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+                                  c.context_lens.cpu().numpy(), c.scale, window=window, alibi=m)
+    stats = assert_parity(out.cpu().numpy(), want, "f32", "f32 chunked prefill")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+def test_chunked_prefill_f32_whole_prompt_equals_prefill(pa):
+    """A chunk that is the whole prompt is a causal prefill; both fp32 forms meet the oracle."""
+    c = wl.make_chunk_case(batch=2, chunk_len=150, prefix_lens=[0, 0], n_q=8, n_kv=2, head_dim=128,
+                           dtype="f32", free_fraction=0.2, seed=4, device="cuda")
+    say("[f32] whole-prompt chunk vs contiguous prefill")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    chunk = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
+    k = c.chunk_k.reshape(2, 150, 2, 128)
+    v = c.chunk_v.reshape(2, 150, 2, 128)
+    pre = pa.paged_attn_prefill(c.q, k, v, True, c.scale)
+    torch.cuda.synchronize()
+    # Same tiles, same order of operations: the two agree bit for bit.
+    assert same_bits(chunk, pre)
+
+
+def test_chunked_prefill_f32_short_context_and_bad_metadata(pa):
+    c = wl.make_chunk_case(batch=4, chunk_len=20, prefix_lens=[30, 30, 30, 30], n_q=8, n_kv=2,
+                           head_dim=128, dtype="f32", free_fraction=0.3, seed=12, device="cuda")
+    say("[f32] context shorter than the chunk, over-long context, out-of-pool block id")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    ctx = c.context_lens.clone()
+    ctx[0] = 7                                   # rows 0..12 sit before the sequence start
+    ctx[2] = c.max_blocks_per_seq * 16 + 1       # past the block table's reach
+    bt = c.block_table.clone()
+    bt[3, 1] = c.num_blocks + 3                  # a block the rows read, outside the pool
+    out = nan_out(c.q.shape)
+    pa.paged_attn_chunked_prefill(c.q, kp, vp, bt, ctx, c.scale, out=out)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert (out[0, :13] == 0).all(), "rows at negative positions must be zero"
+    assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
+    want = oracle.chunked_prefill(stored_np(c.q[:2]), stored_np(kp), stored_np(vp), "f32",
+                                  c.block_table[:2].cpu().numpy(), ctx[:2].cpu().numpy(), c.scale)
+    assert_parity(out[0, 13:].numpy(), want[0, 13:], "f32", "rows of the short sequence")
+    assert_parity(out[1].numpy(), want[1], "f32", "sequence next to bad metadata")
+
+
+MULTI = [
+    # (batch, q_rows, prefix lengths, n_q, n_kv, head_dim, window, alibi)
+    (2, 4, [40, 700], 8, 2, 128, 0, False),
+    (3, 2, [1, 100, 2000], 16, 2, 128, 0, False),
+    (2, 5, [33, 64], 4, 4, 64, 0, False),
+    (1, 8, [1500], 32, 8, 128, 0, True),
+    (2, 3, [300, 900], 8, 1, 128, 100, False),
+]
+
+
+@pytest.mark.parametrize("shape", MULTI, ids=[f"B{s[0]}_R{s[1]}_P{'-'.join(map(str, s[2]))}_{s[3]}x{s[4]}_d{s[5]}"
+                                              f"_W{s[6]}{'_alibi' if s[7] else ''}" for s in MULTI])
+def test_decode_multi_f32(pa, shape):
+    B, R, pre, n_q, n_kv, d, window, alibi = shape
+    c = wl.make_chunk_case(batch=B, chunk_len=R, prefix_lens=pre, n_q=n_q, n_kv=n_kv, head_dim=d,
+                           dtype="f32", free_fraction=0.2, seed=sum(pre) + 7 * R, device="cuda")
+    m = _slopes(n_q) if alibi else None
+    say(f"[f32] multi-row decode B={B} R={R} prefix={pre} {n_q}x{n_kv} d={d} W={window} alibi={alibi}")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    out = nan_out(c.q.shape)
+    pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out, window=window,
+                               alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
+    torch.cuda.synchronize()
+    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+                                  c.context_lens.cpu().numpy(), c.scale, window=window, alibi=m)
+    stats = assert_parity(out.cpu().numpy(), want, "f32", "f32 multi-row decode")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+def test_decode_multi_f32_one_row_matches_decode(pa):
+    """One row per sequence is plain decode; the fp32 multi-row path meets the same oracle."""
+    c = wl.make_decode_case(batch=3, n_q=8, n_kv=2, head_dim=128, context_lens=[1, 77, 1200], dtype="f32",
+                            free_fraction=0.2, seed=5, device="cuda", name="f32one")
+    say("[f32] multi-row decode with one row vs the decode oracle")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.new_k, c.new_v, c.slot_mapping, kp, vp)
+    q = c.q.reshape(3, 1, 8, 128)
+    out = nan_out(q.shape)
+    pa.paged_attn_decode_multi(q, kp, vp, c.block_table, c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+                         c.context_lens.cpu().numpy(), c.scale)
+    assert_parity(out.reshape(3, 8, 128).cpu().numpy(), want, "f32", "one-row f32 multi-row decode")
+
+
+def test_decode_multi_f32_relabelled_blocks_give_identical_bits(pa):
+    c = wl.make_chunk_case(batch=2, chunk_len=4, prefix_lens=[200, 37], n_q=8, n_kv=2, head_dim=128,
+                           dtype="f32", free_fraction=0.2, seed=21, device="cuda")
+    say("[f32] multi-row decode under a relabelling of physical blocks")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    a = pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
+    perm = torch.randperm(c.num_blocks, generator=torch.Generator().manual_seed(3)).to("cuda")
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(c.num_blocks, device="cuda")
+    kp2, vp2 = kp[inv], vp[inv]                    # block x moves to perm[x]
+    bt2 = perm[c.block_table.long()].to(torch.int32)
+    b = pa.paged_attn_decode_multi(c.q, kp2.contiguous(), vp2.contiguous(), bt2, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert same_bits(a, b)
