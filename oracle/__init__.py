@@ -98,6 +98,13 @@ class Oracle:
         L.oracle_kv_append_quant.argtypes = [vp, vp, ctypes.c_int, vp, i64, i32, i32, ctypes.c_int,
                                              i64, i32, vp, vp, vp, vp]
         L.oracle_kv_append_quant.restype = i64
+        L.oracle_decode_channel.argtypes = L.oracle_decode_ex.argtypes
+        L.oracle_decode_channel.restype = ctypes.c_int
+        L.oracle_quantize_channels.argtypes = [vp, ctypes.c_int, i64, i32, i32, ctypes.c_int, vp, vp]
+        L.oracle_quantize_channels.restype = ctypes.c_int
+        L.oracle_kv_append_quant_channel.argtypes = [vp, vp, ctypes.c_int, vp, i64, i32, i32, ctypes.c_int,
+                                                     i64, i32, vp, vp, vp, vp]
+        L.oracle_kv_append_quant_channel.restype = i64
         L.oracle_prefill.argtypes = [vp, vp, vp, ctypes.c_int, i32, i32, i32, i32, i32, i32, f64,
                                      i32, vp, vp, i64, vp, i32]
         L.oracle_prefill.restype = ctypes.c_int
@@ -159,6 +166,50 @@ class Oracle:
             raise ValueError("oracle_quantize_rows rejected its arguments")
         return codes, scales
 
+    def quantize_channels(self, x: np.ndarray, src_dtype: str, fmt: str, scales: np.ndarray) -> np.ndarray:
+        """Rows x [..., n_kv, d] (stored values of src_dtype) -> codes [..., n_kv, d] with the
+        fixed per-channel scales [n_kv][d] (float32)."""
+        _check_stored(x, src_dtype, "x")
+        x = np.ascontiguousarray(x)
+        n_kv, d = x.shape[-2:]
+        scales = np.ascontiguousarray(scales, dtype=np.float32)
+        if scales.shape != (n_kv, d):
+            raise ValueError("scales must be [n_kv][d]")
+        codes = np.empty(x.shape, dtype=_STORED[fmt])
+        rc = self.lib.oracle_quantize_channels(_ptr(x), DTYPE_CODES[src_dtype], x.size // (n_kv * d), n_kv, d,
+                                               DTYPE_CODES[fmt], _ptr(scales), _ptr(codes))
+        if rc != 0:
+            raise ValueError("oracle_quantize_channels rejected its arguments")
+        return codes
+
+    def kv_append_quant_channel(self, k: np.ndarray, v: np.ndarray, src_dtype: str, slot_mapping: np.ndarray,
+                                k_pool: np.ndarray, v_pool: np.ndarray, k_chan: np.ndarray, v_chan: np.ndarray,
+                                fmt: str) -> int:
+        """Quantise k, v [T][n_kv][d] with the fixed channel scales k_chan / v_chan [n_kv][d] into the
+        code pools [nb][n_kv][bs][d] (in place) at slot_mapping [T]."""
+        _check_stored(k, src_dtype, "k")
+        _check_stored(v, src_dtype, "v")
+        for name, a in (("k_pool", k_pool), ("v_pool", v_pool)):
+            _check_stored(a, fmt, name)
+        T, n_kv, d = k.shape
+        nb, n_kv2, bs, d2 = k_pool.shape
+        if v.shape != k.shape or v_pool.shape != k_pool.shape or n_kv2 != n_kv or d2 != d:
+            raise ValueError("shape mismatch")
+        kc = np.ascontiguousarray(k_chan, dtype=np.float32)
+        vc = np.ascontiguousarray(v_chan, dtype=np.float32)
+        if kc.shape != (n_kv, d) or vc.shape != (n_kv, d):
+            raise ValueError("channel scales must be [n_kv][d]")
+        slots = np.ascontiguousarray(slot_mapping, dtype=np.int64)
+        if slots.shape != (T,):
+            raise ValueError("slot_mapping must have one entry per token")
+        n = self.lib.oracle_kv_append_quant_channel(_ptr(np.ascontiguousarray(k)), _ptr(np.ascontiguousarray(v)),
+                                                    DTYPE_CODES[src_dtype], _ptr(slots), T, n_kv, d,
+                                                    DTYPE_CODES[fmt], nb, bs, _ptr(k_pool), _ptr(v_pool),
+                                                    _ptr(kc), _ptr(vc))
+        if n < 0:
+            raise ValueError("oracle_kv_append_quant_channel rejected its arguments (slot out of range?)")
+        return int(n)
+
     def kv_append_quant(self, k: np.ndarray, v: np.ndarray, src_dtype: str,
                         slot_mapping: np.ndarray, k_pool: np.ndarray, v_pool: np.ndarray,
                         k_scale: np.ndarray, v_scale: np.ndarray, fmt: str) -> int:
@@ -191,21 +242,29 @@ class Oracle:
                block_table: np.ndarray, context_lens: np.ndarray, scale: float,
                sel: np.ndarray | None = None, n_threads: int = 0, window: int = 0,
                q_dtype: str | None = None, k_scale: np.ndarray | None = None,
-               v_scale: np.ndarray | None = None, alibi: np.ndarray | None = None) -> np.ndarray:
+               v_scale: np.ndarray | None = None, alibi: np.ndarray | None = None,
+               scale_mode: str = "token") -> np.ndarray:
         """q [B][n_q][d]; pools [nb][n_kv][bs][d]; returns fp64 [B][n_q][d] or [len(sel)][d].
 
         ``window`` W > 0 keeps only the last W positions of each context. For a quantised
-        cache (``dtype`` "fp8" or "int8") pass ``q_dtype`` and the [nb][n_kv][bs] scales.
+        cache (``dtype`` "fp8" or "int8") pass ``q_dtype`` and the scales: [nb][n_kv][bs] per
+        token (``scale_mode`` "token"), or [n_kv][d] per channel (``scale_mode`` "channel").
         ``alibi``: float32 [n_q] slopes m_h; the score of position t gets -m_h (ctx - 1 - t)."""
         q_dtype = q_dtype or dtype
         _check_stored(q, q_dtype, "q")
         for name, a in (("k_pool", k_pool), ("v_pool", v_pool)):
             _check_stored(a, dtype, name)
+        if scale_mode not in ("token", "channel"):
+            raise ValueError("scale_mode is 'token' or 'channel'")
+        per_channel = scale_mode == "channel"
         if dtype in QUANTISED:
+            want = (k_pool.shape[1], k_pool.shape[3]) if per_channel else k_pool.shape[:3]
             for name, a in (("k_scale", k_scale), ("v_scale", v_scale)):
-                if a is None or a.dtype != np.float32 or a.shape != k_pool.shape[:3]:
-                    raise ValueError(f"{name} must be float32 [nb][n_kv][bs]")
+                if a is None or a.dtype != np.float32 or a.shape != want:
+                    raise ValueError(f"{name} must be float32 {'[n_kv][d]' if per_channel else '[nb][n_kv][bs]'}")
             k_scale, v_scale = np.ascontiguousarray(k_scale), np.ascontiguousarray(v_scale)
+        elif per_channel:
+            raise ValueError("per-channel scales need a quantised cache")
         B, n_q, d = q.shape
         nb, n_kv, bs, d2 = k_pool.shape
         if d2 != d or v_pool.shape != k_pool.shape:
@@ -222,7 +281,8 @@ class Oracle:
             out = np.empty((sel.shape[0], d), dtype=np.float64)
         else:
             out = np.empty((B, n_q, d), dtype=np.float64)
-        rc = self.lib.oracle_decode_ex(_ptr(np.ascontiguousarray(q)), DTYPE_CODES[q_dtype],
+        fn = self.lib.oracle_decode_channel if per_channel else self.lib.oracle_decode_ex
+        rc = fn(_ptr(np.ascontiguousarray(q)), DTYPE_CODES[q_dtype],
                                        _ptr(np.ascontiguousarray(k_pool)),
                                        _ptr(np.ascontiguousarray(v_pool)), DTYPE_CODES[dtype],
                                        _ptr(k_scale), _ptr(v_scale), B, n_q, n_kv, d, nb, bs,
@@ -343,10 +403,19 @@ def kv_append_quant(*args, **kwargs):
     return get().kv_append_quant(*args, **kwargs)
 
 
+def quantize_channels(*args, **kwargs):
+    return get().quantize_channels(*args, **kwargs)
+
+
+def kv_append_quant_channel(*args, **kwargs):
+    return get().kv_append_quant_channel(*args, **kwargs)
+
+
 def max_threads() -> int:
     return get().max_threads()
 
 
 __all__ = ["Oracle", "build", "compile_library", "get", "decode", "prefill", "kv_append",
-           "upcast", "encode_fp8", "quantize_rows", "kv_append_quant", "max_threads",
+           "upcast", "encode_fp8", "quantize_rows", "kv_append_quant", "quantize_channels",
+           "kv_append_quant_channel", "max_threads",
            "DTYPE_CODES", "ELEM_BYTES", "QUANTISED", "LIB_PATH", "SOURCE"]

@@ -44,10 +44,11 @@
  * Quantised cache ([IW] "KV Cache 的形状与增长", INT8 / FP8 item: the fp16
  * cache is quantised to int8 or fp8 per channel or per token; the
  * dimension-walkthrough page's KV-size formula counts FP8 as one byte):
- * each (token, KV head) row of K and of V is stored as one-byte codes and one
- * fp32 scale, value = code * scale. The quantiser is per token (one scale per
- * row, symmetric, absolute maximum); its fp32 steps are spelled out at
- * oracle_quantize_rows. FP8 is the OCP E4M3 ("fn") format: 1 sign bit, 4
+ * each (token, KV head) row of K and of V is stored as one-byte codes, value =
+ * code * scale, with the scale taken either per token (one fp32 scale per row,
+ * symmetric, absolute maximum; fp32 steps at oracle_quantize_rows) or per
+ * channel (one fixed fp32 scale per (KV head, channel), given by the caller;
+ * fp32 steps at oracle_quantize_channels). FP8 is the OCP E4M3 ("fn") format: 1 sign bit, 4
  * exponent bits with bias 7, 3 fraction bits, no infinities, one NaN
  * pattern per sign, largest finite value 448.
  *
@@ -158,6 +159,18 @@ int oracle_encode_fp8_e4m3(const float* y, int64_t n, uint8_t* out) {
     return 0;
 }
 
+/* The code of y = x / scale (an fp32 value): E4M3, the nearest code of y clamped
+ * to [-448, 448]; INT8, y rounded to the nearest integer (ties to even) and
+ * clamped to [-127, 127]. */
+static uint8_t code_of(float y, int fmt) {
+    if (fmt == ORACLE_FP8E4M3) {
+        const float c = fminf(fmaxf(y, -448.0f), 448.0f);
+        return encode_fp8_e4m3(c);
+    }
+    const float r = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
+    return (uint8_t)(int8_t)r;
+}
+
 /*
  * One row x[0..d) of the source type to codes and a scale, all in fp32:
  *   amax  = max_i |x_i|
@@ -188,13 +201,7 @@ static void quantise_row(const void* x, int src_dtype, int64_t row0, int32_t d, 
     volatile float inv = 1.0f / scale;
     for (int32_t i = 0; i < d; ++i) {
         volatile float y = (float)load_elem(x, src_dtype, row0 + i) * inv;
-        if (fmt == ORACLE_FP8E4M3) {
-            const float c = fminf(fmaxf(y, -448.0f), 448.0f);
-            codes[i] = encode_fp8_e4m3(c);
-        } else {
-            const float r = fminf(fmaxf(rintf(y), -127.0f), 127.0f);
-            codes[i] = (uint8_t)(int8_t)r;
-        }
+        codes[i] = code_of(y, fmt);
     }
     *scale_out = scale;
 }
@@ -206,6 +213,36 @@ int oracle_quantize_rows(const void* x, int src_dtype, int64_t n_rows, int32_t d
     if (is_quantised(src_dtype) || elem_bytes_of(src_dtype) == 0 || !is_quantised(fmt)) return -1;
     for (int64_t r = 0; r < n_rows; ++r)
         quantise_row(x, src_dtype, r * d, d, fmt, codes + r * d, scales + r);
+    return 0;
+}
+
+/*
+ * Per-channel quantisation (the "per channel" reading of the same item): channel
+ * c of KV head g has one fp32 scale s = scales[g * d + c], fixed in advance by
+ * the caller (a cache filled one token at a time cannot take a channel's range
+ * from tokens that have not arrived yet). Element c of a row of head g:
+ *   s below the smallest normal float (0 included): code 0
+ *   inv = 1 / s,  y = x * inv,  code = code_of(y): values past QMAX * s saturate
+ * each step one correctly rounded fp32 operation, as per token.
+ */
+static uint8_t quantise_channel_elem(float x, float s, int fmt) {
+    if (!(s >= 0x1p-126f)) return 0;
+    volatile float inv = 1.0f / s;
+    volatile float y = x * inv;
+    return code_of(y, fmt);
+}
+
+/* x [n_rows][n_kv][d] in src_dtype -> codes [n_rows][n_kv][d] with scales [n_kv][d]. */
+int oracle_quantize_channels(const void* x, int src_dtype, int64_t n_rows, int32_t n_kv, int32_t d, int fmt,
+                             const float* scales, uint8_t* codes) {
+    if (!x || !codes || !scales || n_rows < 0 || n_kv <= 0 || d <= 0) return -1;
+    if (is_quantised(src_dtype) || elem_bytes_of(src_dtype) == 0 || !is_quantised(fmt)) return -1;
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int32_t g = 0; g < n_kv; ++g)
+            for (int32_t c = 0; c < d; ++c) {
+                const int64_t i = (r * n_kv + g) * d + c;
+                codes[i] = quantise_channel_elem((float)load_elem(x, src_dtype, i), scales[(int64_t)g * d + c], fmt);
+            }
     return 0;
 }
 
@@ -293,6 +330,45 @@ int64_t oracle_kv_append_quant(const void* k, const void* v, int src_dtype,
     return written;
 }
 
+/*
+ * kv_append into a per-channel quantised cache: element c of every (token, KV
+ * head g) row of k and v is quantised with k_chan[g * d + c] / v_chan[g * d + c]
+ * as in oracle_quantize_channels, and the codes go to the pools at block
+ * slot / bs, offset slot % bs; nothing else is written. Slot rules and the
+ * return value are those of oracle_kv_append.
+ */
+int64_t oracle_kv_append_quant_channel(const void* k, const void* v, int src_dtype,
+                                       const int64_t* slot_mapping, int64_t num_tokens, int32_t n_kv,
+                                       int32_t head_dim, int fmt, int64_t num_blocks, int32_t block_size,
+                                       uint8_t* k_pool, uint8_t* v_pool, const float* k_chan,
+                                       const float* v_chan) {
+    if (!k || !v || !slot_mapping || !k_pool || !v_pool || !k_chan || !v_chan) return -1;
+    if (is_quantised(src_dtype) || elem_bytes_of(src_dtype) == 0 || !is_quantised(fmt)) return -1;
+    if (num_tokens < 0 || n_kv <= 0 || head_dim <= 0 || num_blocks <= 0 || block_size <= 0)
+        return -1;
+    const int64_t n_slots = num_blocks * (int64_t)block_size;
+    for (int64_t t = 0; t < num_tokens; ++t)
+        if (slot_mapping[t] >= n_slots) return -1;
+    int64_t written = 0;
+    for (int64_t t = 0; t < num_tokens; ++t) {
+        const int64_t slot = slot_mapping[t];
+        if (slot < 0) continue;
+        const int64_t blk = slot / block_size;
+        const int64_t off = slot % block_size;
+        for (int32_t g = 0; g < n_kv; ++g) {
+            const int64_t src = (t * n_kv + g) * (int64_t)head_dim;
+            const int64_t dst = ((blk * n_kv + g) * block_size + off) * head_dim;
+            for (int32_t c = 0; c < head_dim; ++c) {
+                const int64_t sc = (int64_t)g * head_dim + c;
+                k_pool[dst + c] = quantise_channel_elem((float)load_elem(k, src_dtype, src + c), k_chan[sc], fmt);
+                v_pool[dst + c] = quantise_channel_elem((float)load_elem(v, src_dtype, src + c), v_chan[sc], fmt);
+            }
+        }
+        ++written;
+    }
+    return written;
+}
+
 /* ---- softmax-weighted average over a list of key positions -------------- */
 
 /*
@@ -311,15 +387,20 @@ typedef struct {
     int dtype;
     int64_t* key_off;     /* element offset of row t, length n_keys */
     int64_t n_keys;
-    const float* k_scale; /* quantised cache: scale of row key_off / head_dim; else NULL */
+    const float* k_scale; /* per-token quantised cache: scale of row key_off / head_dim; else NULL */
     const float* v_scale;
     int64_t kpos0;        /* position of key 0 */
+    const float* k_chan;  /* per-channel quantised cache: the KV head's d channel scales; else NULL */
+    const float* v_chan;
 } key_list;
 
-/* Element c of row t of K (or V): the stored value, times the row's scale in a quantised cache. */
+/* Element c of row t of K (or V): the stored value, times its scale in a quantised
+ * cache (the row's scale per token, channel c's per channel). */
 static double key_elem(const key_list* keys, int is_v, int64_t t, int32_t c, int32_t d) {
     const int64_t base = keys->key_off[t];
     const double x = load_elem(is_v ? keys->v_base : keys->k_base, keys->dtype, base + c);
+    const float* ch = is_v ? keys->v_chan : keys->k_chan;
+    if (ch) return x * (double)ch[c];
     const float* sc = is_v ? keys->v_scale : keys->k_scale;
     return sc ? x * (double)sc[base / d] : x;
 }
@@ -370,20 +451,21 @@ static int set_threads(int32_t n_threads) {
  *              W recent positions)
  * sel          optional list of n_sel (b, h) pairs; NULL means every (b, h)
  * out          [batch][n_q][head_dim] fp64 (or [n_sel][head_dim] with sel)
- * Quantised pools (kv_dtype E4M3 or INT8) come with k_scale / v_scale
- * [num_blocks][n_kv][block_size] fp32: element = code * the row's scale; q
- * then has its own type q_dtype. Unquantised pools take no scales and
- * q_dtype == kv_dtype.
+ * Quantised pools (kv_dtype E4M3 or INT8) come with k_scale / v_scale fp32:
+ * per token (per_channel == 0) [num_blocks][n_kv][block_size], element = code *
+ * the row's scale; per channel (per_channel == 1) [n_kv][head_dim], element c
+ * of KV head g = code * scale[g][c]. q then has its own type q_dtype.
+ * Unquantised pools take no scales and q_dtype == kv_dtype.
  * Returns 0, or -1 for invalid arguments or a block id outside the pool.
  */
-int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
-                     const float* k_scale, const float* v_scale,
-                     int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
-                     int64_t num_blocks, int32_t block_size,
-                     const int32_t* block_table, int32_t max_blocks_per_seq,
-                     const int32_t* context_lens, double scale, int32_t window,
-                     const float* alibi_slopes,
-                     const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
+static int decode_core(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                       const float* k_scale, const float* v_scale, int per_channel,
+                       int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                       int64_t num_blocks, int32_t block_size,
+                       const int32_t* block_table, int32_t max_blocks_per_seq,
+                       const int32_t* context_lens, double scale, int32_t window,
+                       const float* alibi_slopes,
+                       const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
     if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return -1;
     if (window < 0) return -1;
     if (elem_bytes_of(q_dtype) == 0 || is_quantised(q_dtype)) return -1;
@@ -433,7 +515,12 @@ int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void*
                 offs[t - first] = ((phys * n_kv + g) * block_size + off) * head_dim;
             }
             /* the query is the newest position, ctx - 1 */
-            key_list keys = {k_pool, v_pool, kv_dtype, offs, ctx - first, k_scale, v_scale, first};
+            key_list keys = {k_pool, v_pool, kv_dtype, offs, ctx - first, k_scale, v_scale, first, NULL, NULL};
+            if (per_channel) {
+                keys.k_scale = keys.v_scale = NULL;
+                keys.k_chan = k_scale + (int64_t)g * head_dim;
+                keys.v_chan = v_scale + (int64_t)g * head_dim;
+            }
             const double slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;
             attend(qv, head_dim, scale, slope, (int64_t)ctx - 1, &keys, scores, out + it * head_dim);
         }
@@ -442,6 +529,35 @@ int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void*
         free(offs);
     }
     return bad ? -1 : 0;
+}
+
+/* Decode over an unquantised cache, or a quantised one with per-token scales. */
+int oracle_decode_ex(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                     const float* k_scale, const float* v_scale,
+                     int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                     int64_t num_blocks, int32_t block_size,
+                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                     const int32_t* context_lens, double scale, int32_t window,
+                     const float* alibi_slopes,
+                     const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
+    return decode_core(q, q_dtype, k_pool, v_pool, kv_dtype, k_scale, v_scale, 0, batch, n_q, n_kv, head_dim,
+                       num_blocks, block_size, block_table, max_blocks_per_seq, context_lens, scale, window,
+                       alibi_slopes, sel, n_sel, out, n_threads);
+}
+
+/* Decode over a quantised cache with per-channel scales k_chan / v_chan [n_kv][head_dim]. */
+int oracle_decode_channel(const void* q, int q_dtype, const void* k_pool, const void* v_pool, int kv_dtype,
+                          const float* k_chan, const float* v_chan,
+                          int32_t batch, int32_t n_q, int32_t n_kv, int32_t head_dim,
+                          int64_t num_blocks, int32_t block_size,
+                          const int32_t* block_table, int32_t max_blocks_per_seq,
+                          const int32_t* context_lens, double scale, int32_t window,
+                          const float* alibi_slopes,
+                          const int32_t* sel, int64_t n_sel, double* out, int32_t n_threads) {
+    if (!is_quantised(kv_dtype)) return -1;
+    return decode_core(q, q_dtype, k_pool, v_pool, kv_dtype, k_chan, v_chan, 1, batch, n_q, n_kv, head_dim,
+                       num_blocks, block_size, block_table, max_blocks_per_seq, context_lens, scale, window,
+                       alibi_slopes, sel, n_sel, out, n_threads);
 }
 
 /* Decode over an unquantised cache: q and the pools share one type. */
@@ -516,7 +632,7 @@ int oracle_prefill(const void* q, const void* k, const void* v, int dtype,
                 qv[c] = load_elem(q, dtype, (((int64_t)b * seq_len + i) * n_q + h) * head_dim + c);
             for (int32_t j = first; j < n_keys; ++j)
                 offs[j - first] = (((int64_t)b * seq_len + j) * n_kv + g) * head_dim;
-            key_list keys = {k, v, dtype, offs, n_keys - first, NULL, NULL, first};
+            key_list keys = {k, v, dtype, offs, n_keys - first, NULL, NULL, first, NULL, NULL};
             const double slope = alibi_slopes ? (double)alibi_slopes[h] : 0.0;
             attend(qv, head_dim, scale, slope, i, &keys, scores, out + it * head_dim);
         }

@@ -564,7 +564,7 @@ def pin_chunked_prefill_window_matches_library_sdpa_band(orc):
 # ---- quantised cache: codes, quantiser, attention over codes * scales -------------------
 #
 # Quantised cache: the walk-through's KV-cache section, INT8 / FP8 item (per channel or per
-# token); read here as per-token symmetric absolute-maximum scaling, FP8 = OCP E4M3.
+# token); per token read as symmetric absolute-maximum scaling of each row, FP8 = OCP E4M3.
 
 def _fp8_values(codes: np.ndarray) -> np.ndarray:
     """float64 values of E4M3 codes through torch's own float8_e4m3fn dtype."""
@@ -725,6 +725,194 @@ def pin_decode_quantised_matches_library_sdpa(orc):
             v_t = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
             want = sdpa64(qq, k_t, v_t, 0.3)[:, 0, :]
             close(got[b], want.numpy(), 1e-12, f"{fmt} decode vs sdpa over codes * scales, b={b}")
+
+
+def pin_chunked_prefill_quantised_matches_library_sdpa(orc):
+    # Chunk rows over a per-token quantised cache: torch's float64 SDPA with the bottom-right
+    # causal mask over K and V rebuilt as codes * row scales.
+    n_q, n_kv, d, bs, C = 4, 2, 8, 4, 5
+    G = n_q // n_kv
+    g = torch.Generator().manual_seed(67)
+    lens = [9, 14]
+    q = stored(torch.randn(len(lens), C, n_q, d, generator=g), "f16")
+    for fmt in ("fp8", "int8"):
+        kc, vc, ksc, vsc = [], [], [], []
+        for L in lens:
+            a, sa = orc.quantize_rows(stored(torch.randn(L, n_kv, d, generator=g), "f16"), "f16", fmt)
+            b_, sb = orc.quantize_rows(stored(torch.randn(L, n_kv, d, generator=g) * 3, "f16"), "f16", fmt)
+            kc.append(a); vc.append(b_); ksc.append(sa); vsc.append(sb)
+        fill = np.array(0x7F if fmt == "fp8" else 77).astype(kc[0].dtype)
+        kp, bt = pack_pool(kc, bs, 9, np.random.default_rng(68), fill)
+        vp, _ = pack_pool(vc, bs, 9, np.random.default_rng(68), fill)
+        ksp, _ = pack_pool([x[..., None] for x in ksc], bs, 9, np.random.default_rng(68), np.float32(np.nan))
+        vsp, _ = pack_pool([x[..., None] for x in vsc], bs, 9, np.random.default_rng(68), np.float32(np.nan))
+        got = orc.chunked_prefill(q, kp, vp, fmt, bt, np.asarray(lens, np.int32), 0.35, q_dtype="f16",
+                                  k_scale=np.ascontiguousarray(ksp[..., 0]), v_scale=np.ascontiguousarray(vsp[..., 0]))
+        for b, L in enumerate(lens):
+            kk = _code_values(kc[b], fmt) * ksc[b][..., None].astype(np.float64)
+            vv = _code_values(vc[b], fmt) * vsc[b][..., None].astype(np.float64)
+            mask = torch.arange(L)[None, :] <= (L - C + torch.arange(C))[:, None]
+            qq = exact(q[b], "f16").transpose(0, 1)
+            k_t = torch.from_numpy(kk).transpose(0, 1).repeat_interleave(G, 0).contiguous()
+            v_t = torch.from_numpy(vv).transpose(0, 1).repeat_interleave(G, 0).contiguous()
+            want = torch.nn.functional.scaled_dot_product_attention(
+                qq.unsqueeze(0), k_t.unsqueeze(0), v_t.unsqueeze(0), attn_mask=mask, scale=0.35)[0]
+            close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"{fmt} chunk rows vs sdpa over codes * scales, b={b}")
+
+
+# ---- per-channel scales ------------------------------------------------------------------
+#
+# The same item's other granularity: one fixed fp32 scale per (KV head, channel), given by the
+# caller, the same fp32 code steps as per token, saturating at QMAX.
+
+def pin_quantize_channels_hand_worked_fixture(orc):
+    fx = json.loads((GOLDEN / "quantize_channels_hand_worked.json").read_text())
+    x = np.asarray(fx["x"], np.float32)[None]              # [1][n_kv][d]
+    scales = np.asarray(fx["scales"], np.float32)
+    assert scales[1, 2] > 0, "the subnormal scale must survive the float32 cast"
+    for fmt, want in fx["codes"].items():
+        codes = orc.quantize_channels(x, "f32", fmt, scales)
+        want = np.asarray(want, np.uint8 if fmt == "fp8" else np.int8)
+        assert (codes[0] == want).all(), f"{fmt}: codes {codes[0].tolist()} vs {want.tolist()}"
+
+
+def pin_quantize_channels_exact_round_trip(orc):
+    # Values that are codes times their channel's power-of-two scale come back as those codes.
+    rng = np.random.default_rng(69)
+    finite = np.nonzero(np.isfinite(_fp8_values(np.arange(256, dtype=np.uint8))))[0].astype(np.uint8)
+    n_kv, d = 3, 16
+    pw = rng.integers(-6, 7, size=(n_kv, d))
+    scales = (2.0 ** pw).astype(np.float32)
+    for fmt in ("fp8", "int8"):
+        c = rng.choice(finite, size=(5, n_kv, d)) if fmt == "fp8" else rng.integers(-127, 128, (5, n_kv, d)).astype(np.int8)
+        x = (_code_values(c, fmt) * scales.astype(np.float64)).astype(np.float32)
+        codes = orc.quantize_channels(x, "f32", fmt, scales)
+        assert (_code_values(codes, fmt) == _code_values(c, fmt)).all(), f"{fmt}: codes differ"
+
+
+def pin_quantize_channels_error_bound_and_saturation(orc):
+    g = torch.Generator().manual_seed(70)
+    n_kv, d = 2, 32
+    x = stored(torch.randn(300, n_kv, d, generator=g) * 4, "bf16")
+    xv = exact(x, "bf16").numpy()
+    for fmt, qmax in (("fp8", 448.0), ("int8", 127.0)):
+        # Scales that cover about 90% of each channel's values; the rest must saturate.
+        cover = np.quantile(np.abs(xv), 0.9, axis=0)                      # [n_kv][d]
+        scales = (cover / qmax).astype(np.float32)
+        s = scales.astype(np.float64)[None]
+        codes = orc.quantize_channels(x, "bf16", fmt, scales)
+        deq = _code_values(codes, fmt) * s
+        inside = np.abs(xv) <= qmax * s * (1 - 2.0 ** -20)
+        if fmt == "int8":
+            bound = s * (0.5 + 128 * 2.0 ** -22)
+        else:
+            bound = np.maximum(np.abs(xv) * 2.0 ** -4, 2.0 ** -10 * s) * (1 + 2.0 ** -20)
+        err = np.abs(deq - xv)
+        assert (err[inside] <= np.broadcast_to(bound, err.shape)[inside]).all(), f"{fmt}: error over the bound"
+        out = np.abs(xv) > qmax * s * (1 + 2.0 ** -20)
+        assert out.sum() > 100, "the case must exercise saturation"
+        cv = _code_values(codes, fmt)
+        assert (np.abs(cv[out]) == qmax).all() and (np.sign(cv[out]) == np.sign(xv[out])).all(), \
+            f"{fmt}: values past QMAX * scale must saturate to +-QMAX"
+
+
+def pin_quantize_channels_with_the_row_scale_match_per_token(orc):
+    # One KV head whose channel scales all equal a row's per-token scale quantises that row
+    # exactly as the per-token quantiser does.
+    g = torch.Generator().manual_seed(71)
+    x = stored(torch.randn(20, 1, 24, generator=g) * 5, "f16")
+    for fmt in ("fp8", "int8"):
+        codes_t, sc = orc.quantize_rows(x, "f16", fmt)
+        for r in range(x.shape[0]):
+            codes_c = orc.quantize_channels(x[r:r + 1], "f16", fmt, np.full((1, 24), sc[r, 0], np.float32))
+            assert (codes_c[0] == codes_t[r]).all(), f"{fmt}: row {r} differs from the per-token codes"
+
+
+def pin_kv_append_quant_channel_places_codes(orc):
+    g = torch.Generator().manual_seed(72)
+    nb, n_kv, bs, d, T = 5, 2, 4, 16, 7
+    k = stored(torch.randn(T, n_kv, d, generator=g), "bf16")
+    v = stored(torch.randn(T, n_kv, d, generator=g) * 3, "bf16")
+    kch = (np.abs(np.random.default_rng(72).normal(0, 0.02, (n_kv, d))) + 1e-3).astype(np.float32)
+    vch = (np.abs(np.random.default_rng(73).normal(0, 0.05, (n_kv, d))) + 1e-3).astype(np.float32)
+    slots = np.random.default_rng(74).choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[2] = -1
+    for fmt in ("fp8", "int8"):
+        cdt = np.uint8 if fmt == "fp8" else np.int8
+        kp = np.full((nb, n_kv, bs, d), 0x11, cdt)
+        vp = kp.copy()
+        assert orc.kv_append_quant_channel(k, v, "bf16", slots, kp, vp, kch, vch, fmt) == T - 1
+        kc = orc.quantize_channels(k, "bf16", fmt, kch)
+        vc = orc.quantize_channels(v, "bf16", fmt, vch)
+        kt = kp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+        vt = vp.transpose(0, 2, 1, 3).reshape(nb * bs, n_kv, d)
+        keep = np.ones(nb * bs, bool)
+        for t, s_ in enumerate(slots):
+            if s_ < 0:
+                continue
+            keep[s_] = False
+            assert (kt[s_] == kc[t]).all() and (vt[s_] == vc[t]).all(), f"{fmt}: codes of token {t}"
+        assert (kt[keep] == 0x11).all() and (vt[keep] == 0x11).all(), f"{fmt}: untouched slots changed"
+
+
+def pin_decode_channel_quantised_matches_library_sdpa(orc):
+    ctxs, n_q, n_kv, d, bs = [1, 7, 13, 22], 8, 2, 16, 4
+    G = n_q // n_kv
+    g = torch.Generator().manual_seed(75)
+    rng = np.random.default_rng(75)
+    q = stored(torch.randn(len(ctxs), n_q, d, generator=g), "bf16")
+    kch = (rng.uniform(0.002, 0.02, (n_kv, d))).astype(np.float32)
+    vch = (rng.uniform(0.005, 0.05, (n_kv, d))).astype(np.float32)
+    for fmt in ("fp8", "int8"):
+        kc = [orc.quantize_channels(stored(torch.randn(L, n_kv, d, generator=g), "bf16"), "bf16", fmt, kch)
+              for L in ctxs]
+        vc = [orc.quantize_channels(stored(torch.randn(L, n_kv, d, generator=g) * 2, "bf16"), "bf16", fmt, vch)
+              for L in ctxs]
+        nb = sum(-(-L // bs) for L in ctxs) + 2
+        fill = np.array(0x7F if fmt == "fp8" else 99).astype(kc[0].dtype)
+        kp, bt = pack_pool(kc, bs, nb, np.random.default_rng(76), fill)
+        vp, _ = pack_pool(vc, bs, nb, np.random.default_rng(76), fill)
+        got = orc.decode(q, kp, vp, fmt, bt, np.asarray(ctxs, np.int32), 0.3, q_dtype="bf16",
+                         k_scale=kch, v_scale=vch, scale_mode="channel")
+        for b, L in enumerate(ctxs):
+            kk = _code_values(kc[b], fmt) * kch.astype(np.float64)[None]       # [L][n_kv][d]
+            vv = _code_values(vc[b], fmt) * vch.astype(np.float64)[None]
+            qq = exact(q[b], "bf16").unsqueeze(1)
+            k_t = torch.from_numpy(kk).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+            v_t = torch.from_numpy(vv).permute(1, 0, 2).repeat_interleave(G, 0).contiguous()
+            want = sdpa64(qq, k_t, v_t, 0.3)[:, 0, :]
+            close(got[b], want.numpy(), 1e-12, f"{fmt} per-channel decode vs sdpa, b={b}")
+
+
+def pin_chunked_prefill_channel_quantised_matches_library_sdpa(orc):
+    n_q, n_kv, d, bs, C = 6, 3, 8, 4, 4
+    G = n_q // n_kv
+    g = torch.Generator().manual_seed(77)
+    rng = np.random.default_rng(77)
+    lens = [6, 11]
+    q = stored(torch.randn(len(lens), C, n_q, d, generator=g), "bf16")
+    kch = rng.uniform(0.002, 0.03, (n_kv, d)).astype(np.float32)
+    vch = rng.uniform(0.002, 0.03, (n_kv, d)).astype(np.float32)
+    for fmt in ("fp8", "int8"):
+        kc = [orc.quantize_channels(stored(torch.randn(L, n_kv, d, generator=g), "bf16"), "bf16", fmt, kch)
+              for L in lens]
+        vc = [orc.quantize_channels(stored(torch.randn(L, n_kv, d, generator=g), "bf16"), "bf16", fmt, vch)
+              for L in lens]
+        fill = np.array(0x7F if fmt == "fp8" else 55).astype(kc[0].dtype)
+        kp, bt = pack_pool(kc, bs, 7, np.random.default_rng(78), fill)
+        vp, _ = pack_pool(vc, bs, 7, np.random.default_rng(78), fill)
+        got = orc.chunked_prefill(q, kp, vp, fmt, bt, np.asarray(lens, np.int32), 0.4, q_dtype="bf16",
+                                  k_scale=kch, v_scale=vch, scale_mode="channel")
+        for b, L in enumerate(lens):
+            kk = _code_values(kc[b], fmt) * kch.astype(np.float64)[None]
+            vv = _code_values(vc[b], fmt) * vch.astype(np.float64)[None]
+            mask = torch.arange(L)[None, :] <= (L - C + torch.arange(C))[:, None]
+            qq = exact(q[b], "bf16").transpose(0, 1)
+            k_t = torch.from_numpy(kk).transpose(0, 1).repeat_interleave(G, 0).contiguous()
+            v_t = torch.from_numpy(vv).transpose(0, 1).repeat_interleave(G, 0).contiguous()
+            want = torch.nn.functional.scaled_dot_product_attention(
+                qq.unsqueeze(0), k_t.unsqueeze(0), v_t.unsqueeze(0), attn_mask=mask, scale=0.4)[0]
+            close(got[b], want.transpose(0, 1).numpy(), 1e-12, f"{fmt} per-channel chunk rows vs sdpa, b={b}")
 
 
 # ---- kv_append ---------------------------------------------------------------------------

@@ -7,7 +7,9 @@ missing normalisation, an off-by-one causal mask, wrong block or offset
 arithmetic, a transposed operand, a wrong widening of stored values, a
 window off by one, and in the quantised cache a wrong largest code, wrong
 rounding, a wrong FP8 exponent bias or subnormal step, V scaled by K's scale,
-signed codes read as unsigned, scales stored at the wrong slot. All mutants
+signed codes read as unsigned, scales stored at the wrong slot, and for
+per-channel scales the wrong KV head's or the K scales for V, transposed or
+head-blind scale indexing, a subnormal scale taken as usable. All mutants
 keep every memory access in bounds.
 """
 from pathlib import Path
@@ -61,6 +63,14 @@ MUTANTS = {
                            "case ORACLE_INT8: return (double)((const uint8_t*)base)[idx];"),
     "quant_append_scale_row_offset": ("const int64_t dst_row = (blk * n_kv + g) * block_size + off;",
                                       "const int64_t dst_row = (blk * n_kv + g) * block_size + (off + 1) % block_size;"),
+    "channel_scales_of_kv_head_zero": ("keys.k_chan = k_scale + (int64_t)g * head_dim;",
+                                       "keys.k_chan = k_scale;"),
+    "channel_v_scaled_by_k_channels": ("const float* ch = is_v ? keys->v_chan : keys->k_chan;",
+                                       "const float* ch = is_v ? keys->k_chan : keys->k_chan;"),
+    "channel_append_scales_transposed": ("const int64_t sc = (int64_t)g * head_dim + c;",
+                                         "const int64_t sc = (int64_t)c * n_kv + g;"),
+    "channel_quantise_ignores_head": ("scales[(int64_t)g * d + c], fmt);", "scales[c], fmt);"),
+    "channel_subnormal_scale_kept": ("if (!(s >= 0x1p-126f)) return 0;", "if (!(s > 0.0f)) return 0;"),
     "decode_window_one_too_wide": ("(window > 0 && ctx > window) ? ctx - window : 0",
                                    "(window > 0 && ctx > window) ? ctx - window - 1 : 0"),
     "prefill_window_one_too_narrow": ("(window > 0 && i + 1 > window) ? i + 1 - window : 0",
