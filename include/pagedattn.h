@@ -283,8 +283,10 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
  * an out-of-pool block id among those read gives NaN rows. Results equal
  * pa_paged_attn_chunked_prefill with chunk_len = q_rows up to rounding (bit for
  * bit for f32 caches, which both calls serve with the same fp32 kernel and no
- * workspace). The workspace size covers any window. Supported: head_dim 64 or
- * 128; f32 within the limits given for pa_paged_attn_prefill.
+ * workspace). The workspace size covers any window; given a quantised cache
+ * description it sizes pa_paged_attn_decode_multi_quant and
+ * pa_paged_attn_chunked_prefill_quant (rows = q_rows) instead. Supported:
+ * head_dim 64 or 128; f32 within the limits given for pa_paged_attn_prefill.
  */
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache);
@@ -416,6 +418,49 @@ int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const vo
                          const float* alibi_slopes, void* out,
                                       pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream);
+
+/*
+ * paged_attn_decode_multi_quant / paged_attn_chunked_prefill_quant -- the
+ * several-rows-per-sequence calls over a quantised cache: row r of sequence b
+ * sits at position context_lens[b] - rows + r and attends to positions 0 .. that
+ * position ([AE] 1.1 causal mask aligned at the bottom right; [IW] chunked
+ * prefill and the verification of drafted tokens; [IW] INT8 / FP8 item for the
+ * values code * scale of their row).
+ *
+ *   q             [batch][rows][n_q][head_dim] in q_dtype (bf16 or f16), rows =
+ *                 q_rows or chunk_len
+ *   k_cache, v_cache, k_scale, v_scale, cache  as for pa_paged_attn_decode_quant,
+ *                 already holding the rows' own K/V (pa_kv_append_quant first)
+ *   block_table, context_lens, scale, window, alibi_slopes  as for
+ *                 pa_paged_attn_decode_multi
+ *   out           [batch][rows][n_q][head_dim], out_dtype PA_F32 or q_dtype
+ *   workspace     scratch of pa_decode_multi_workspace_bytes(batch, rows, n_q,
+ *                 max_blocks_per_seq, cache) bytes (that query takes quantised
+ *                 descriptions), or NULL as for pa_paged_attn_decode
+ * Both run the quantised-cache decode kernel with the (query head, row) pairs
+ * of a KV head as its matrix-core columns, 16 (or 8, 4, 2, 1) per workgroup
+ * slice; every slice streams the codes of the keys its rows reach, so the two
+ * calls differ only in name. Rows at negative positions are zero; a context
+ * past the block table's reach or an out-of-pool block id among those read
+ * gives NaN rows. Supported: head_dim 64 or 128, batch at most 65535, and at
+ * most 65535 slices, n_kv * G * rows / w with G = n_q / n_kv and w the largest
+ * of 16, 8, 4, 2, 1 that divides G * rows; else PA_ERR_UNSUPPORTED.
+ * chunk_len == 0 or batch == 0 is a no-op.
+ */
+int pa_paged_attn_decode_multi_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_rows, int32_t n_q,
+                                     const void* k_cache, const void* v_cache, const float* k_scale,
+                                     const float* v_scale, const pa_cache_desc* cache,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, float scale, int32_t window,
+                                     const float* alibi_slopes, void* out, pa_dtype out_dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+int pa_paged_attn_chunked_prefill_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t chunk_len,
+                                        int32_t n_q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                        const float* v_scale, const pa_cache_desc* cache,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, float scale, int32_t window,
+                                        const float* alibi_slopes, void* out, pa_dtype out_dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream);
 
 /*
  * Tuning override for the decode partition size, in tokens (a multiple of 16

@@ -31,6 +31,7 @@ from ._lib import CacheDesc, LibraryNotBuilt
 __all__ = ["kv_append", "paged_attn_decode", "paged_attn_decode_noalloc", "paged_attn_decode_append", "paged_attn_prefill",
            "paged_attn_chunked_prefill", "paged_attn_decode_multi", "kv_append_quant",
            "paged_attn_decode_quant", "paged_attn_decode_quant_append", "quant_decode_workspace_bytes",
+           "paged_attn_decode_multi_quant", "paged_attn_chunked_prefill_quant",
            "prefill_workspace_bytes", "chunked_prefill_workspace_bytes",
            "decode_workspace_bytes", "set_workspace",
            "set_decode_partition_tokens", "set_option", "get_option", "library_version", "LibraryNotBuilt", "PagedAttnError"]
@@ -503,6 +504,63 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
         _alibi_arg(alibi_slopes, n_q), _dev(out, "out"),
         _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
     return out
+
+
+def _rows_quant(fn_name: str, q, k_cache, v_cache, k_scale, v_scale, fmt, block_table, context_lens, scale,
+                out, out_dtype, workspace, stream, window, alibi_slopes):
+    L = _lib.load()
+    desc = _quant_desc(k_cache, fmt)
+    if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
+        raise ValueError("k_cache and v_cache differ")
+    _check_scales(k_cache, k_scale, v_scale)
+    if q.dim() != 4 or q.shape[3] != k_cache.shape[3]:
+        raise ValueError("q must be [B][rows][n_q][head_dim] matching the cache")
+    B, R, n_q, d = q.shape
+    if q.dtype not in (torch.bfloat16, torch.float16):
+        raise TypeError("q must be bfloat16 or float16")
+    if block_table.dim() != 2 or block_table.shape[0] != B or context_lens.shape != (B,):
+        raise ValueError("block_table must be [B][max_blocks] and context_lens [B]")
+    maxb = block_table.shape[1]
+    if out is None:
+        out = _alloc((B, R, n_q, d), out_dtype, q, stream)
+    if out.shape != q.shape or out.dtype not in _DTYPE:
+        raise ValueError("out must be [B][rows][n_q][d] in a supported dtype")
+    if workspace is None and B > 0 and R > 0:
+        need = int(L.pa_decode_multi_workspace_bytes(B, R, n_q, maxb, ctypes.byref(desc)))
+        if need:
+            workspace = _alloc(need, torch.uint8, q, stream)
+    ws_ptr, ws_bytes = _workspace_args(workspace)
+    _check(fn_name, getattr(L, fn_name)(
+        _dev(q, "q"), _DTYPE[q.dtype], B, R, n_q, _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(k_scale, "k_scale", torch.float32), _dev(v_scale, "v_scale", torch.float32),
+        ctypes.byref(desc), _dev(block_table, "block_table", torch.int32), maxb,
+        _dev(context_lens, "context_lens", torch.int32), float(scale), int(window),
+        _alibi_arg(alibi_slopes, n_q), _dev(out, "out"), _DTYPE[out.dtype], ws_ptr, ws_bytes, _stream(q, stream)))
+    return out
+
+
+def paged_attn_decode_multi_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                  k_scale: torch.Tensor, v_scale: torch.Tensor, fmt: str,
+                                  block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                  out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                                  workspace: torch.Tensor | None = None, stream=None, window: int = 0,
+                                  alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
+    """q_rows query rows per sequence, q [B][q_rows][n_q][d] (bf16 or f16), over a quantised
+    paged cache already holding the rows' own K/V; returns out [B][q_rows][n_q][d]."""
+    return _rows_quant("pa_paged_attn_decode_multi_quant", q, k_cache, v_cache, k_scale, v_scale, fmt,
+                       block_table, context_lens, scale, out, out_dtype, workspace, stream, window, alibi_slopes)
+
+
+def paged_attn_chunked_prefill_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: torch.Tensor,
+                                     k_scale: torch.Tensor, v_scale: torch.Tensor, fmt: str,
+                                     block_table: torch.Tensor, context_lens: torch.Tensor, scale: float,
+                                     out: torch.Tensor | None = None, out_dtype: torch.dtype = torch.float32,
+                                     workspace: torch.Tensor | None = None, stream=None, window: int = 0,
+                                     alibi_slopes: torch.Tensor | None = None) -> torch.Tensor:
+    """A prompt chunk q [B][chunk_len][n_q][d] (bf16 or f16) over a quantised paged cache already
+    holding the chunk's own K/V; returns out [B][chunk_len][n_q][d]."""
+    return _rows_quant("pa_paged_attn_chunked_prefill_quant", q, k_cache, v_cache, k_scale, v_scale, fmt,
+                       block_table, context_lens, scale, out, out_dtype, workspace, stream, window, alibi_slopes)
 
 
 def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

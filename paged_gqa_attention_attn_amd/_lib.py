@@ -33,6 +33,8 @@ EXPORTS = (
     "pa_kv_append_quant",
     "pa_paged_attn_decode_quant",
     "pa_paged_attn_decode_quant_append",
+    "pa_paged_attn_decode_multi_quant",
+    "pa_paged_attn_chunked_prefill_quant",
     "pa_set_decode_partition_tokens",
     "pa_set_option",
     "pa_get_option",
@@ -111,6 +113,11 @@ def load(path: Path | str = LIB_PATH) -> ctypes.CDLL:
                                                     cd, vp, i32, vp, ctypes.c_float, i32, vp, vp,
                                                     ctypes.c_int, vp, sz, vp]
     L.pa_paged_attn_decode_quant_append.restype = ctypes.c_int
+    for name in ("pa_paged_attn_decode_multi_quant", "pa_paged_attn_chunked_prefill_quant"):
+        fn = getattr(L, name)
+        fn.argtypes = [vp, ctypes.c_int, i32, i32, i32, vp, vp, vp, vp, cd, vp, i32, vp, ctypes.c_float, i32, vp,
+                       vp, ctypes.c_int, vp, sz, vp]
+        fn.restype = ctypes.c_int
     L.pa_set_decode_partition_tokens.argtypes = [i32]
     L.pa_set_decode_partition_tokens.restype = i32
     L.pa_set_option.argtypes = [i32, i32]

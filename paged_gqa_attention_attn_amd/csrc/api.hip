@@ -312,6 +312,15 @@ int check_decode_args(int32_t batch, int32_t n_q, const pa_cache_desc* cache,
     return PA_OK;
 }
 
+// Quantised-cache decode of q_rows rows: (query head, row) pairs per KV head in an
+// int, and their slices of at most 16 columns within grid y.
+bool quant_rows_fit(int32_t batch, int32_t q_rows, int32_t n_q, const pa_cache_desc* c) {
+    const int64_t pairs = (int64_t)(n_q / c->n_kv) * q_rows;
+    if (pairs > INT32_MAX / 2 || (int64_t)n_q * q_rows > INT32_MAX / 2 || batch > 65535) return false;
+    const int64_t gw = pairs % 16 == 0 ? 16 : pairs % 8 == 0 ? 8 : pairs % 4 == 0 ? 4 : pairs % 2 == 0 ? 2 : 1;
+    return (pairs / gw) * c->n_kv <= 65535;
+}
+
 // Multi-row decode plan: 4 waves per workgroup, each a contiguous run of blocks of
 // the partition (2048 tokens unless overridden), groups of 32 (row, head) pairs.
 constexpr int kMultiWaves = 4;
@@ -896,8 +905,16 @@ int pa_paged_attn_prefill(const void* q, const void* k, const void* v, pa_dtype 
 
 size_t pa_decode_multi_workspace_bytes(int32_t batch, int32_t q_rows, int32_t n_q,
                                        int32_t max_blocks_per_seq, const pa_cache_desc* cache) {
-    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq) != PA_OK || q_rows < 1) return 0;
+    if (check_decode_args(batch, n_q, cache, max_blocks_per_seq, true) != PA_OK || q_rows < 1) return 0;
     if (cache->dtype == PA_F32) return 0;   // the fp32 kernel keeps no partials
+    if (is_quant(cache->dtype)) {           // the quantised-cache decode kernel, q_rows rows
+        if (!quant_rows_fit(batch, q_rows, n_q, cache)) return 0;
+        Plan pl;
+        make_plan(batch, n_q * q_rows, max_blocks_per_seq, cache, &pl);
+        const int32_t np = mfma_parts_bound(pl.nparts_max, (int64_t)batch * cache->n_kv * pl.hsg, pl.waves_tok,
+                                            max_blocks_per_seq);
+        return partials_bytes((int64_t)batch * q_rows * n_q, np, cache->head_dim);
+    }
     const MultiPlan pl = multi_plan(batch, q_rows, n_q, max_blocks_per_seq, cache);
     if (!pl.mfma) return pl.bytes;
     const int32_t np = mfma_parts_bound(pl.nparts_max, (int64_t)batch * cache->n_kv * pl.hsg, pl.waves_tok,
@@ -1139,7 +1156,9 @@ struct FusedQuantAppend {
     float* v_scale_w;
 };
 
-int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
+// Decode of q_rows query rows per sequence (1: single-row decode, which may carry
+// a fused append) over a quantised cache; `what` names the entry point in errors.
+int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_rows, int32_t n_q,
                       const void* k_cache, const void* v_cache, const float* k_scale,
                       const float* v_scale, const pa_cache_desc* cache,
                       const int32_t* block_table, int32_t max_blocks_per_seq,
@@ -1149,6 +1168,9 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
                       const FusedQuantAppend* fa) {
     int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq, true);
     if (rc) return rc;
+    if (q_rows < 1) return fail(PA_ERR_INVALID_ARG, "q_rows %d must be positive", q_rows);
+    if (!quant_rows_fit(batch, q_rows, n_q, cache))
+        return fail(PA_ERR_UNSUPPORTED, "decode_quant: (query head, row) pairs per KV head past the grid");
     if (!is_quant(cache->dtype))
         return fail(PA_ERR_INVALID_ARG, "decode_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8");
     if (q_dtype != PA_BF16 && q_dtype != PA_F16)
@@ -1176,8 +1198,10 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
             return fail(PA_ERR_INVALID_ARG, "decode_quant_append: slot_mapping must be 8-byte aligned");
     }
 
+    // The (query head, row) pairs of a KV head are the columns, as query heads are
+    // for one row: plan as for n_q * q_rows heads.
     Plan pl;
-    make_plan(batch, n_q, span_blocks(max_blocks_per_seq, 1, window), cache, &pl);
+    make_plan(batch, n_q * q_rows, span_blocks(max_blocks_per_seq, q_rows, window), cache, &pl);
     const size_t need = plan_bytes(pl);
     std::unique_lock<std::mutex> ws_lock;   // held until the kernels are enqueued
     if (need > 0) {
@@ -1192,7 +1216,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     }
     if (validate_enabled()) {
         rc = validate_decode(batch, cache, block_table, max_blocks_per_seq, context_lens,
-                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream), 1, window);
+                             fa ? fa->slots : nullptr, static_cast<hipStream_t>(stream), q_rows, window);
         if (rc) return rc;
     }
 
@@ -1227,7 +1251,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_
     a.mfma = 1;
     fold_scale(scale, q_dtype, &a);
     a.out_f32 = out_dtype == PA_F32;
-    a.q_rows = 1;
+    a.q_rows = q_rows;
     a.window = window;
     a.alibi = alibi_slopes;
     if (fa) {
@@ -1257,9 +1281,38 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
                                const int32_t* context_lens, float scale, int32_t window,
                                const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
-    return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
+    return decode_quant_impl(q, q_dtype, batch, 1, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
                              max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out, out_dtype, workspace,
                              workspace_bytes, stream, nullptr);
+}
+
+int pa_paged_attn_decode_multi_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_rows, int32_t n_q,
+                                     const void* k_cache, const void* v_cache, const float* k_scale,
+                                     const float* v_scale, const pa_cache_desc* cache,
+                                     const int32_t* block_table, int32_t max_blocks_per_seq,
+                                     const int32_t* context_lens, float scale, int32_t window,
+                                     const float* alibi_slopes, void* out, pa_dtype out_dtype, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+    return decode_quant_impl(q, q_dtype, batch, q_rows, n_q, k_cache, v_cache, k_scale, v_scale, cache,
+                             block_table, max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out,
+                             out_dtype, workspace, workspace_bytes, stream, nullptr);
+}
+
+int pa_paged_attn_chunked_prefill_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t chunk_len,
+                                        int32_t n_q, const void* k_cache, const void* v_cache, const float* k_scale,
+                                        const float* v_scale, const pa_cache_desc* cache,
+                                        const int32_t* block_table, int32_t max_blocks_per_seq,
+                                        const int32_t* context_lens, float scale, int32_t window,
+                                        const float* alibi_slopes, void* out, pa_dtype out_dtype, void* workspace,
+                                        size_t workspace_bytes, void* stream) {
+    if (chunk_len < 0) return fail(PA_ERR_INVALID_ARG, "chunk_len %d < 0", chunk_len);
+    if (chunk_len == 0) {
+        const int rc = check_decode_args(batch, n_q, cache, max_blocks_per_seq, true);
+        return rc ? rc : PA_OK;
+    }
+    return decode_quant_impl(q, q_dtype, batch, chunk_len, n_q, k_cache, v_cache, k_scale, v_scale, cache,
+                             block_table, max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out,
+                             out_dtype, workspace, workspace_bytes, stream, nullptr);
 }
 
 int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const void* v_new, pa_dtype q_dtype,
@@ -1271,7 +1324,7 @@ int pa_paged_attn_decode_quant_append(const void* q, const void* k_new, const vo
                                       pa_dtype out_dtype, void* workspace, size_t workspace_bytes,
                                       void* stream) {
     const FusedQuantAppend fa{k_new, v_new, slot_mapping, k_cache, v_cache, k_scale, v_scale};
-    return decode_quant_impl(q, q_dtype, batch, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
+    return decode_quant_impl(q, q_dtype, batch, 1, n_q, k_cache, v_cache, k_scale, v_scale, cache, block_table,
                              max_blocks_per_seq, context_lens, scale, window, alibi_slopes, out, out_dtype, workspace,
                              workspace_bytes, stream, &fa);
 }

@@ -43,6 +43,7 @@ namespace {
 constexpr int BS = 16;
 constexpr float TAU = 8.0f;
 constexpr float LOG2E = 1.4426950408889634f;
+constexpr float M_FLOOR = -1e30f; // running-max start: finite, so 2^(s - m) of a masked s is 0
 constexpr int MAX_WAVES = 8;
 
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
@@ -142,11 +143,16 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     const int col = lane & 15;
     const int grp = lane >> 4;
 
-    const int h0 = g * p.group + hsgi * HW;
+    // MFMA column col holds (head, row) pair v = hsgi * HW + col of the KV head's
+    // G * NR pairs: new-token row v / G of the step's NR (1 for single-row decode),
+    // query head g * G + v % G. qo_row(v) is its row of q and of out.
+    const int G = p.group, NR = p.q_rows;
+    auto qo_row = [&](int v) { return ((int64_t)b * NR + v / G) * p.n_q + (int64_t)g * G + v % G; };
+    const int v_col = hsgi * HW + (col < HW ? col : 0);
     const int blk0 = part * p.waves_tok * p.blocks_per_wave + wave * p.blocks_per_wave;
     u32x4_t qreg[KK];
     {
-        const char* qrow = (const char*)p.q + (int64_t)(b * p.n_q + h0 + (col < HW ? col : 0)) * (D * 2);
+        const char* qrow = (const char*)p.q + qo_row(v_col) * (D * 2);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
@@ -163,7 +169,10 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     const bool ctx_bad = ctx_in > cap;
     const int ctx = (ctx_in < 0 || ctx_bad) ? 0 : ctx_in;
     const int nblk = (ctx + BS - 1) / BS;
-    const int first = window_first(ctx, 1, p.window);
+    const int first = window_first(ctx, NR, p.window);   // the earliest position any row sees
+    // This column's row sees positions col_lo .. col_hi (causal among the new rows).
+    const int col_hi = ctx - NR + v_col / G;
+    const int col_lo = p.window > 0 ? col_hi - p.window + 1 : 0;
     const int fb = first / BS;
     const int bpp = p.waves_tok * p.blocks_per_wave;
     const int nparts = nblk > fb ? (nblk - fb + bpp - 1) / bpp : 1;
@@ -178,7 +187,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     // ALiBi: the column's head slope in log2 units; with it, scores are formed in
     // log2 units before the max (c2 = 1), else scaled inside it.
     const bool alibi = p.alibi != nullptr;   // uniform
-    const float al2 = alibi ? p.alibi[h0 + (col < HW ? col : 0)] * LOG2E : 0.f;
+    const float al2 = alibi ? p.alibi[(int64_t)g * G + v_col % G] * LOG2E : 0.f;
     const float c2 = alibi ? 1.f : p.scale_log2;
     const bool phys_bad = __any(lane < nb && (my_phys < 0 || my_phys >= p.num_blocks));
 
@@ -252,7 +261,10 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     f32x4_t o[MT];
 #pragma unroll
     for (int t = 0; t < MT; ++t) o[t] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    float m_run = -INFINITY;
+    // Running max (log2 units) of column col. It starts finite: with several rows a
+    // block can hold no key that some column attends, and 2^(s - m) of a masked s
+    // must then be 0, not 2^(-inf + inf).
+    float m_run = M_FLOOR;
     float l_run = 0.f;
 
     wait_vmcnt<0>();
@@ -286,7 +298,8 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                     *reinterpret_cast<float*>(base + 2 * TILE + 64 + 4 * r) = new_vs;
                 }
             }
-            const bool edge = pos0 + BS > ctx || pos0 < first;   // uniform
+            // Some key of the block is outside some column's range (uniform).
+            const bool edge = pos0 + BS - 1 > ctx - NR || (p.window > 0 && pos0 < ctx - p.window);
             if (edge) {
                 // Zero the V code rows outside [first, ctx) (whole rows).
 #pragma unroll
@@ -326,8 +339,8 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             s[1] *= ks.y;
             s[2] *= ks.z;
             s[3] *= ks.w;
-            if (alibi) {   // - m_h log2(e) (ctx - 1 - j) for key j = pos0 + 4 grp + j'
-                const float b0 = al2 * (float)(pos0 + 4 * grp - (ctx - 1));
+            if (alibi) {   // - m_h log2(e) (i - j) for the column's row i and key j = pos0 + 4 grp + j'
+                const float b0 = al2 * (float)(pos0 + 4 * grp - col_hi);
 #pragma unroll
                 for (int j = 0; j < 4; ++j) s[j] = fmaf(s[j], p.scale_log2, fmaf(al2, (float)j, b0));
             }
@@ -336,7 +349,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     const int pos = pos0 + 4 * grp + j;
-                    live[j] = pos < ctx && pos >= first;
+                    live[j] = pos <= col_hi && pos >= col_lo;
                     s[j] = live[j] ? s[j] : -INFINITY;
                 }
             }
@@ -412,7 +425,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                 A = fmaf(f, aw[w], A);
             }
         }
-        const int64_t row = (int64_t)b * p.n_q + h0 + hl;
+        const int64_t row = qo_row(hsgi * HW + hl);
         if (nparts == 1) {
             float o1 = (Lsum == 0.f) ? 0.f : A * __builtin_amdgcn_rcpf(Lsum);
             if (ctx_bad) o1 = NAN;
@@ -460,7 +473,9 @@ template <class Q, class E, int D, int HW, int R> hipError_t launch_typed(const 
     hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW, R>), grid, dim3(64 * a.waves_tok), lds, s, a);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || a.nparts_max <= 1) return err;
-    return launch_decode_reduce(a, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
+    DecodeArgs m = a;
+    m.n_q = a.n_q * a.q_rows;   // the reduce kernel's rows: (b, r, h) in [B][q_rows][n_q] order
+    return launch_decode_reduce(m, std::is_same<E, BF16>::value ? Elem::BF16 : Elem::F16, D, s);
 }
 
 template <class Q, class E, int D, int R> hipError_t launch_hw(const DecodeArgs& a, hipStream_t s) {
@@ -497,7 +512,10 @@ int quant_wave_bytes(int head_dim, int hw, int ring) {
 
 hipError_t launch_decode_quant(const DecodeArgs& a, Elem q_type, QuantFmt fmt, int head_dim, hipStream_t s) {
     if (a.hs_wg != 1 || a.waves_tok < 1 || a.waves_tok > MAX_WAVES) return hipErrorInvalidValue;
-    if (a.q_rows != 1 || a.window < 0 || !a.k_scale || !a.v_scale) return hipErrorInvalidValue;
+    if (a.q_rows < 1 || a.window < 0 || !a.k_scale || !a.v_scale) return hipErrorInvalidValue;
+    // Several new rows per sequence: their pairs fill whole slices of gw columns,
+    // and no append rides along.
+    if (a.q_rows > 1 && ((a.group * a.q_rows) % a.gw != 0 || a.new_slots != nullptr)) return hipErrorInvalidValue;
     if (fmt == QuantFmt::FP8_E4M3 && q_type == Elem::BF16) return launch_dim<QFp8, BF16>(a, head_dim, s);
     if (fmt == QuantFmt::FP8_E4M3 && q_type == Elem::F16) return launch_dim<QFp8, F16>(a, head_dim, s);
     if (fmt == QuantFmt::INT8 && q_type == Elem::BF16) return launch_dim<QInt8, BF16>(a, head_dim, s);

@@ -413,6 +413,48 @@ def test_decode_quant_rejects(L, kw, code, msg):
     assert msg in _lib.last_error()
 
 
+def rows_quant(L, name, **kw):
+    a = dict(q=FAKE, q_dtype=_lib.PA_BF16, batch=2, rows=4, n_q=8, k=FAKE, v=FAKE, ks=FAKE, vs=FAKE,
+             cache=desc(dtype=FP8), bt=FAKE, maxb=4, ctx=FAKE, scale=0.125, window=0, alibi=None, out=FAKE,
+             out_dtype=_lib.PA_F32, ws=None, ws_bytes=0, stream=None)
+    a.update(kw)
+    return getattr(L, name)(a["q"], a["q_dtype"], a["batch"], a["rows"], a["n_q"], a["k"], a["v"], a["ks"],
+                            a["vs"], a["cache"], a["bt"], a["maxb"], a["ctx"], a["scale"], a["window"], a["alibi"],
+                            a["out"], a["out_dtype"], a["ws"], a["ws_bytes"], a["stream"])
+
+
+@pytest.mark.parametrize("name", ["pa_paged_attn_decode_multi_quant", "pa_paged_attn_chunked_prefill_quant"])
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(cache=desc(dtype=_lib.PA_BF16)), INVALID, "PA_FP8_E4M3"),
+    (dict(q_dtype=_lib.PA_F32), UNSUPPORTED, "q must be"),
+    (dict(out_dtype=_lib.PA_F16), UNSUPPORTED, "out_dtype"),
+    (dict(rows=-1), INVALID, "must be positive"),
+    (dict(ks=None), INVALID, "NULL"),
+    (dict(cache=desc(dtype=INT8, d=96)), UNSUPPORTED, "head_dim"),
+    (dict(n_q=7), INVALID, "multiple"),
+    (dict(scale=float("inf")), INVALID, "finite"),
+    (dict(window=-2), INVALID, "window"),
+    (dict(rows=2**24, n_q=64, cache=desc(dtype=FP8, n_kv=8)), UNSUPPORTED, "grid"),
+    (dict(maxb=8192, ws=FAKE, ws_bytes=16), INVALID, "workspace"),
+])
+def test_rows_quant_rejects(L, name, kw, code, msg):
+    if name.endswith("chunked_prefill_quant") and kw.get("rows") == -1:
+        msg = "chunk_len"
+    assert rows_quant(L, name, **kw) == code
+    assert msg in _lib.last_error()
+
+
+def test_rows_quant_empty_and_workspace_query(L):
+    assert rows_quant(L, "pa_paged_attn_chunked_prefill_quant", rows=0) == PA_OK
+    assert rows_quant(L, "pa_paged_attn_decode_multi_quant", batch=0) == PA_OK
+    # 8 KV heads x 4 rows x G = 8: 32 pairs per KV head in two slices of 16 columns, a
+    # 128-block table: (m, l, acc) for every (sequence, row, head) and partition, as the
+    # single-row quantised decode of 32 heads per KV head would need.
+    q = L.pa_decode_multi_workspace_bytes(4, 4, 64, 128, desc(nb=4096, n_kv=8, dtype=FP8))
+    one = L.pa_decode_workspace_bytes(4, 256, 128, desc(nb=4096, n_kv=8, dtype=FP8))
+    assert q == one and q > 0
+
+
 def decode_quant_append(L, **kw):
     a = dict(q=FAKE, kn=FAKE, vn=FAKE, q_dtype=_lib.PA_BF16, slots=FAKE, batch=2, n_q=8, k=FAKE, v=FAKE,
              ks=FAKE, vs=FAKE, cache=_lib.CacheDesc(64, 16, 2, 128, _lib.PA_FP8_E4M3), bt=FAKE, maxb=4,

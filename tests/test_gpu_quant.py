@@ -282,3 +282,132 @@ def test_fused_quant_step_matches_oracle_full_size(pa):
                          q_dtype=c.q_dtype, k_scale=oks, v_scale=ovs)
     stats = assert_parity(got.cpu().numpy(), want, "bf16", "fused fp8 step, all 1024 rows")
     say(f"    max_abs={stats['max_abs']:.2e}")
+
+
+# ---- several rows per sequence over the quantised cache -----------------------------------
+
+def _rows_case(fmt, q_dtype, B, R, ctx, n_q, n_kv, d, seed, free=0.2):
+    c = wl.make_quant_decode_case(fmt=fmt, q_dtype=q_dtype, batch=B, n_q=n_q, n_kv=n_kv, head_dim=d,
+                                  context_lens=ctx, free_fraction=free, seed=seed, device="cuda", name="rows")
+    g = torch.Generator(device="cuda").manual_seed(seed + 1)
+    q = torch.randn(B, R, n_q, d, generator=g, device="cuda").to(wl.TORCH_DTYPES[q_dtype])
+    return c, q
+
+
+def _oracle_rows(c, q, window=0, alibi=None, ctx=None, bt=None):
+    return oracle.chunked_prefill(stored_np(q), _np(c.k_pool), _np(c.v_pool), c.fmt,
+                                  _np(c.block_table if bt is None else bt),
+                                  _np(c.context_lens if ctx is None else ctx), c.scale, window=window,
+                                  alibi=alibi, q_dtype=c.q_dtype, k_scale=_np(c.k_scale), v_scale=_np(c.v_scale))
+
+
+ROWS = [
+    # (fmt, q dtype, batch, rows, context lengths, n_q, n_kv, head_dim)
+    ("fp8", "bf16", 2, 4, [40, 700], 8, 2, 128),
+    ("int8", "bf16", 3, 2, [2, 100, 2000], 16, 2, 128),
+    ("fp8", "f16", 2, 5, [33, 64], 4, 4, 64),
+    ("int8", "f16", 1, 8, [1500], 32, 8, 128),
+    ("fp8", "bf16", 2, 3, [300, 901], 6, 2, 128),     # 9 pairs per KV head: one column per slice
+    ("int8", "bf16", 2, 7, [7, 50], 8, 1, 64),         # a context shorter than the rows
+]
+
+
+@pytest.mark.parametrize("case", ROWS, ids=[f"{r[0]}_{r[1]}_B{r[2]}_R{r[3]}_C{'-'.join(map(str, r[4]))}_{r[5]}x{r[6]}_d{r[7]}"
+                                            for r in ROWS])
+def test_decode_multi_quant_matches_oracle(pa, case):
+    fmt, qd, B, R, ctx, n_q, n_kv, d = case
+    c, q = _rows_case(fmt, qd, B, R, ctx, n_q, n_kv, d, seed=zlib.crc32(repr(case).encode()) % 10007)
+    say(f"[quant rows] multi-row decode {case}")
+    out = nan_out(q.shape)
+    pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, fmt, c.block_table,
+                                     c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    want = _oracle_rows(c, q)
+    stats = assert_parity(out.cpu().numpy(), want, "bf16", f"{fmt} multi-row decode")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+CHUNKS = [
+    # (fmt, q dtype, batch, chunk, context lengths, n_q, n_kv, head_dim, window, alibi)
+    ("fp8", "bf16", 2, 100, [100, 433], 8, 2, 128, 0, False),
+    ("int8", "f16", 1, 257, [300], 4, 1, 64, 0, False),
+    ("fp8", "bf16", 3, 64, [64, 1000, 200], 32, 8, 128, 0, True),
+    ("int8", "bf16", 2, 90, [590, 110], 8, 2, 128, 64, False),
+    ("fp8", "f16", 1, 48, [2100], 12, 4, 128, 300, True),
+]
+
+
+@pytest.mark.parametrize("case", CHUNKS, ids=[f"{r[0]}_{r[1]}_B{r[2]}_C{r[3]}_ctx{'-'.join(map(str, r[4]))}_{r[5]}x{r[6]}"
+                                              f"_d{r[7]}_W{r[8]}{'_alibi' if r[9] else ''}" for r in CHUNKS])
+def test_chunked_prefill_quant_matches_oracle(pa, case):
+    fmt, qd, B, C, ctx, n_q, n_kv, d, window, alibi = case
+    c, q = _rows_case(fmt, qd, B, C, ctx, n_q, n_kv, d, seed=zlib.crc32(repr(case).encode()) % 10007)
+    m = (2.0 ** (-8.0 * (np.arange(n_q) + 1) / n_q)).astype(np.float32) if alibi else None
+    say(f"[quant rows] chunked prefill {case}")
+    out = nan_out(q.shape)
+    pa.paged_attn_chunked_prefill_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, fmt, c.block_table,
+                                        c.context_lens, c.scale, out=out, window=window,
+                                        alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
+    torch.cuda.synchronize()
+    want = _oracle_rows(c, q, window=window, alibi=m)
+    stats = assert_parity(out.cpu().numpy(), want, "bf16", f"{fmt} chunked prefill")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+@pytest.mark.parametrize("tokens", [256, 1024])
+def test_rows_quant_split_contexts_match_oracle(pa, tokens):
+    """Contexts split into partitions (log-sum-exp merge of per-partition partials)."""
+    c, q = _rows_case("fp8", "bf16", 2, 6, [2500, 900], 8, 2, 128, seed=tokens)
+    prev = pa.set_decode_partition_tokens(tokens)
+    try:
+        say(f"[quant rows] multi-row decode with {tokens}-token partitions")
+        out = pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "fp8",
+                                               c.block_table, c.context_lens, c.scale)
+        win = pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "fp8",
+                                               c.block_table, c.context_lens, c.scale, window=700)
+        torch.cuda.synchronize()
+    finally:
+        pa.set_decode_partition_tokens(prev)
+    assert_parity(out.cpu().numpy(), _oracle_rows(c, q), "bf16", "split multi-row decode")
+    assert_parity(win.cpu().numpy(), _oracle_rows(c, q, window=700), "bf16", "split windowed multi-row decode")
+
+
+def test_rows_quant_relabelling_and_repeat_are_bitwise(pa):
+    c, q = _rows_case("int8", "bf16", 2, 4, [1200, 77], 16, 4, 128, seed=5)
+    say("[quant rows] relabelled blocks and a repeated call, bitwise")
+    a = pa.paged_attn_chunked_prefill_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "int8", c.block_table,
+                                            c.context_lens, c.scale)
+    again = pa.paged_attn_chunked_prefill_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "int8",
+                                                c.block_table, c.context_lens, c.scale)
+    multi = pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "int8", c.block_table,
+                                             c.context_lens, c.scale)
+    perm = torch.as_tensor(np.random.default_rng(9).permutation(c.num_blocks), device="cuda")
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(c.num_blocks, device="cuda")
+    b = pa.paged_attn_chunked_prefill_quant(q, c.k_pool[inv].contiguous(), c.v_pool[inv].contiguous(),
+                                            c.k_scale[inv].contiguous(), c.v_scale[inv].contiguous(), "int8",
+                                            perm[c.block_table.long()].int(), c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert same_bits(a, again) and same_bits(a, multi) and same_bits(a, b)
+
+
+def test_rows_quant_bad_metadata_and_bf16_output(pa):
+    c, q = _rows_case("fp8", "bf16", 4, 5, [60, 60, 60, 3], 8, 2, 128, seed=11, free=0.3)
+    say("[quant rows] over-long context, out-of-pool block, context shorter than the rows; bf16 out")
+    ctx = c.context_lens.clone()
+    ctx[0] = c.block_table.shape[1] * 16 + 1
+    bt = c.block_table.clone()
+    bt[1, 2] = c.num_blocks + 5
+    out = nan_out(q.shape)
+    pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "fp8", bt, ctx, c.scale, out=out)
+    o16 = pa.paged_attn_decode_multi_quant(q, c.k_pool, c.v_pool, c.k_scale, c.v_scale, "fp8", c.block_table,
+                                           c.context_lens, c.scale, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    out = out.cpu()
+    assert torch.isnan(out[0]).all() and torch.isnan(out[1]).all()
+    assert (out[3, :2] == 0).all(), "rows at negative positions must be zero"
+    want = _oracle_rows(c, q)
+    assert_parity(out[2:].numpy(), want[2:], "bf16", "sequences next to bad metadata")
+    # bf16 output: the fp32 result's rounding (half an ulp, 2^-9 relative) on top of the tolerance.
+    got16 = o16.float().cpu().numpy()
+    assert (np.abs(got16 - want) <= 2e-3 + 2.0 ** -8 * np.abs(want)).all(), "bf16 output"
