@@ -57,9 +57,19 @@ extern "C" {
 
 /* Element types. q/k/v and the cache share one type; outputs are f32 or that type.
  * PA_FP8_E4M3 and PA_INT8 describe quantised caches only (one-byte codes plus one
- * fp32 scale per token row, see pa_kv_append_quant); every other entry point
- * rejects them with PA_ERR_UNSUPPORTED. */
-typedef enum { PA_F32 = 0, PA_BF16 = 1, PA_F16 = 2, PA_FP8_E4M3 = 3, PA_INT8 = 4 } pa_dtype;
+ * fp32 scale per token row, see pa_kv_append_quant); the _PER_CHANNEL forms hold the
+ * same codes with one fixed fp32 scale per (KV head, channel) instead. Only the
+ * quantised entry points (pa_kv_append_quant, pa_paged_attn_*_quant*) take them;
+ * every other entry point rejects them with PA_ERR_UNSUPPORTED. */
+typedef enum {
+    PA_F32 = 0,
+    PA_BF16 = 1,
+    PA_F16 = 2,
+    PA_FP8_E4M3 = 3,
+    PA_INT8 = 4,
+    PA_FP8_E4M3_PER_CHANNEL = 5,
+    PA_INT8_PER_CHANNEL = 6
+} pa_dtype;
 
 typedef enum {
     PA_OK = 0,
@@ -359,14 +369,22 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
  *   k_cache, v_cache  code pools [num_blocks][n_kv][block_size][head_dim], one
  *                 byte per element: OCP FP8 E4M3 (cache->dtype PA_FP8_E4M3) or
  *                 two's-complement INT8 (PA_INT8)
- *   k_scale, v_scale  fp32 [num_blocks][n_kv][block_size]: one scale per row
- * Every (token, KV head) row x of K and of V is quantised on its own, with every
+ *   k_scale, v_scale  fp32 [num_blocks][n_kv][block_size]: one scale per row,
+ *                 written here; for a _PER_CHANNEL cache dtype instead the fixed
+ *                 channel scales [n_kv][head_dim] (16-byte aligned), only read
+ * Per row: every (token, KV head) row x of K and of V is quantised on its own, with every
  * step one correctly rounded fp32 operation: amax = max |x_i|; scale = amax / QMAX
  * (448 for E4M3, 127 for INT8); a scale below the smallest normal float (amax = 0
  * included) is stored as 0 with all codes 0; otherwise y_i = x_i * (1 / scale) and
  * the code is the nearest E4M3 value of y_i clamped to [-448, 448] (ties to the
  * even code) or rint(y_i) clamped to [-127, 127]. The stored value of a code is
- * code * scale. Rows must be finite. num_tokens == 0 is a no-op.
+ * code * scale. Per channel ([IW]'s other granularity, read as fixed scales a
+ * caller calibrates in advance, since a cache filled one token at a time cannot
+ * take a channel's range from tokens still to come): element c of every row of
+ * KV head g with s = scale[g][c]: s below the smallest normal float stores code
+ * 0; otherwise y = x * (1 / s) and the same code rule, so values past QMAX * s
+ * saturate at +-QMAX. The stored value is code * s. Rows must be finite.
+ * num_tokens == 0 is a no-op.
  */
 int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const int64_t* slot_mapping,
                        int32_t num_tokens, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
@@ -378,13 +396,17 @@ int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const i
  * the same softmax(q K^T * scale + M) V.
  *
  *   q             [batch][n_q][head_dim] in q_dtype (bf16 or f16)
- *   k_cache, v_cache, k_scale, v_scale  as written by pa_kv_append_quant
- *   cache->dtype  PA_FP8_E4M3 or PA_INT8
+ *   k_cache, v_cache, k_scale, v_scale  as written by pa_kv_append_quant (per row),
+ *                 or the codes and the fixed channel scales [n_kv][head_dim]
+ *   cache->dtype  PA_FP8_E4M3 or PA_INT8, or their _PER_CHANNEL forms
  *   out           [batch][n_q][head_dim], out_dtype PA_F32 or q_dtype
  *   other arguments as for pa_paged_attn_decode (window, workspace sized by
  *   pa_decode_workspace_bytes with this cache description).
  * Codes are widened exactly to q's type and multiplied on the matrix cores in
  * fp32; unused slots (codes or scales, NaN included) never reach the output.
+ * Per channel, q times the K channel scales enters the bf16 matrix cores as a
+ * bf16 hi + lo pair (about 16 significant bits) and the V channel scales
+ * multiply the output once.
  */
 int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, int32_t n_q,
                                const void* k_cache, const void* v_cache, const float* k_scale,

@@ -413,13 +413,18 @@ def paged_attn_decode_multi(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
 
 # ---- quantised cache (one-byte codes + one fp32 scale per row) ------------------------------
 
-_QFMT = {"fp8": _lib.PA_FP8_E4M3, "int8": _lib.PA_INT8}
-_QCODE = {"fp8": (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8)), "int8": (torch.int8,)}
+# Quantised cache formats: codes with one scale per row ("fp8", "int8"), or with fixed
+# scales per (KV head, channel) ("fp8_per_channel", "int8_per_channel").
+_QFMT = {"fp8": _lib.PA_FP8_E4M3, "int8": _lib.PA_INT8, "fp8_per_channel": _lib.PA_FP8_E4M3_PER_CHANNEL,
+         "int8_per_channel": _lib.PA_INT8_PER_CHANNEL}
+_FP8_CODES = (torch.uint8, getattr(torch, "float8_e4m3fn", torch.uint8))
+_QCODE = {"fp8": _FP8_CODES, "int8": (torch.int8,), "fp8_per_channel": _FP8_CODES,
+          "int8_per_channel": (torch.int8,)}
 
 
 def _quant_desc(k_cache: torch.Tensor, fmt: str) -> CacheDesc:
     if fmt not in _QFMT:
-        raise ValueError(f"fmt must be 'fp8' or 'int8' (got {fmt!r})")
+        raise ValueError(f"fmt must be one of {sorted(_QFMT)} (got {fmt!r})")
     if k_cache.dim() != 4:
         raise ValueError("code pools must be [num_blocks][n_kv][block_size][head_dim]")
     if k_cache.dtype not in _QCODE[fmt]:
@@ -428,18 +433,22 @@ def _quant_desc(k_cache: torch.Tensor, fmt: str) -> CacheDesc:
     return CacheDesc(nb, bs, n_kv, d, _QFMT[fmt])
 
 
-def _check_scales(k_cache, k_scale, v_scale):
-    want = tuple(k_cache.shape[:3])
+def _check_scales(k_cache, k_scale, v_scale, fmt="fp8"):
+    per_channel = fmt.endswith("_per_channel")
+    want = (k_cache.shape[1], k_cache.shape[3]) if per_channel else tuple(k_cache.shape[:3])
+    what = "[n_kv][head_dim]" if per_channel else "[num_blocks][n_kv][block_size]"
     for name, t in (("k_scale", k_scale), ("v_scale", v_scale)):
-        if tuple(t.shape) != want:
-            raise ValueError(f"{name} must be [num_blocks][n_kv][block_size] = {list(want)}")
+        if tuple(t.shape) != tuple(want):
+            raise ValueError(f"{name} must be {what} = {list(want)}")
 
 
 def kv_append_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                     k_cache: torch.Tensor, v_cache: torch.Tensor, k_scale: torch.Tensor,
                     v_scale: torch.Tensor, fmt: str, stream=None) -> None:
-    """Quantise k/v rows [T][n_kv][d] (f32, bf16 or f16) per row into the code pools and
-    float32 scale pools at ``slot_mapping`` (int64 [T]); ``fmt`` is 'fp8' or 'int8'."""
+    """Quantise k/v rows [T][n_kv][d] (f32, bf16 or f16) into the code pools at ``slot_mapping``
+    (int64 [T]). ``fmt`` 'fp8' or 'int8': one scale per row, written to the float32 scale pools
+    [num_blocks][n_kv][block_size]; 'fp8_per_channel' or 'int8_per_channel': k_scale / v_scale
+    are the fixed float32 channel scales [n_kv][d], only read."""
     L = _lib.load()
     desc = _quant_desc(k_cache, fmt)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype or k.shape != v.shape:
@@ -448,7 +457,7 @@ def kv_append_quant(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor
         raise ValueError("k and v must be [T][n_kv][head_dim] matching the cache")
     if k.dtype not in _DTYPE or v.dtype != k.dtype:
         raise TypeError("k and v must share one of float32, bfloat16, float16")
-    _check_scales(k_cache, k_scale, v_scale)
+    _check_scales(k_cache, k_scale, v_scale, fmt)
     T = k.shape[0]
     if slot_mapping.shape != (T,):
         raise ValueError("slot_mapping must be [T]")
@@ -478,7 +487,7 @@ def paged_attn_decode_quant(q: torch.Tensor, k_cache: torch.Tensor, v_cache: tor
     desc = _quant_desc(k_cache, fmt)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache differ")
-    _check_scales(k_cache, k_scale, v_scale)
+    _check_scales(k_cache, k_scale, v_scale, fmt)
     B, n_q, d = q.shape
     if d != k_cache.shape[3]:
         raise ValueError("q head_dim differs from the cache")
@@ -512,7 +521,7 @@ def _rows_quant(fn_name: str, q, k_cache, v_cache, k_scale, v_scale, fmt, block_
     desc = _quant_desc(k_cache, fmt)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache differ")
-    _check_scales(k_cache, k_scale, v_scale)
+    _check_scales(k_cache, k_scale, v_scale, fmt)
     if q.dim() != 4 or q.shape[3] != k_cache.shape[3]:
         raise ValueError("q must be [B][rows][n_q][head_dim] matching the cache")
     B, R, n_q, d = q.shape
@@ -579,7 +588,7 @@ def paged_attn_decode_quant_append(q: torch.Tensor, k_new: torch.Tensor, v_new: 
     desc = _quant_desc(k_cache, fmt)
     if v_cache.shape != k_cache.shape or v_cache.dtype != k_cache.dtype:
         raise ValueError("k_cache and v_cache differ")
-    _check_scales(k_cache, k_scale, v_scale)
+    _check_scales(k_cache, k_scale, v_scale, fmt)
     B, n_q, d = q.shape
     if d != k_cache.shape[3]:
         raise ValueError("q head_dim differs from the cache")

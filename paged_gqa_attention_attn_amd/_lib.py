@@ -11,6 +11,7 @@ from pathlib import Path
 LIB_PATH = Path(__file__).resolve().parent / "libpagedattn.so"
 
 PA_F32, PA_BF16, PA_F16, PA_FP8_E4M3, PA_INT8 = 0, 1, 2, 3, 4
+PA_FP8_E4M3_PER_CHANNEL, PA_INT8_PER_CHANNEL = 5, 6
 PA_OK, PA_ERR_INVALID_ARG, PA_ERR_UNSUPPORTED, PA_ERR_HIP = 0, -1, -2, -3
 
 # pa_option: name -> (value, environment variable giving its initial value)

@@ -64,11 +64,20 @@ int elem_bytes(pa_dtype d) {
     case PA_F16: return 2;
     case PA_FP8_E4M3: return 1;
     case PA_INT8: return 1;
+    case PA_FP8_E4M3_PER_CHANNEL: return 1;
+    case PA_INT8_PER_CHANNEL: return 1;
     }
     return 0;
 }
 
-bool is_quant(pa_dtype d) { return d == PA_FP8_E4M3 || d == PA_INT8; }
+bool is_quant(pa_dtype d) {
+    return d == PA_FP8_E4M3 || d == PA_INT8 || d == PA_FP8_E4M3_PER_CHANNEL || d == PA_INT8_PER_CHANNEL;
+}
+// One-byte codes with fixed per-channel scales [n_kv][head_dim] instead of per-row ones.
+bool is_per_channel(pa_dtype d) { return d == PA_FP8_E4M3_PER_CHANNEL || d == PA_INT8_PER_CHANNEL; }
+pa::QuantFmt fmt_of(pa_dtype d) {
+    return d == PA_FP8_E4M3 || d == PA_FP8_E4M3_PER_CHANNEL ? pa::QuantFmt::FP8_E4M3 : pa::QuantFmt::INT8;
+}
 
 pa::Elem to_elem(pa_dtype d) { return static_cast<pa::Elem>(static_cast<int>(d)); }
 
@@ -1116,7 +1125,8 @@ int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const i
     int rc = check_cache(cache, true);
     if (rc) return rc;
     if (!is_quant(cache->dtype))
-        return fail(PA_ERR_INVALID_ARG, "kv_append_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8");
+        return fail(PA_ERR_INVALID_ARG,
+                    "kv_append_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8 (or their _PER_CHANNEL forms)");
     if (src_dtype != PA_F32 && src_dtype != PA_BF16 && src_dtype != PA_F16)
         return fail(PA_ERR_UNSUPPORTED, "kv_append_quant: k and v must be f32, bf16 or f16");
     if (num_tokens < 0) return fail(PA_ERR_INVALID_ARG, "num_tokens %d < 0", num_tokens);
@@ -1134,7 +1144,7 @@ int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const i
         if (rc) return rc;
     }
     const hipError_t e = pa::launch_kv_append_quant(
-        k, v, to_elem(src_dtype), static_cast<pa::QuantFmt>(static_cast<int>(cache->dtype)), slot_mapping,
+        k, v, to_elem(src_dtype), fmt_of(cache->dtype), is_per_channel(cache->dtype), slot_mapping,
         num_tokens, cache->n_kv, cache->head_dim, (int64_t)cache->num_blocks * cache->block_size, k_cache,
         v_cache, k_scale, v_scale, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "kv_append_quant launch");
@@ -1172,7 +1182,8 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_
     if (!quant_rows_fit(batch, q_rows, n_q, cache))
         return fail(PA_ERR_UNSUPPORTED, "decode_quant: (query head, row) pairs per KV head past the grid");
     if (!is_quant(cache->dtype))
-        return fail(PA_ERR_INVALID_ARG, "decode_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8");
+        return fail(PA_ERR_INVALID_ARG,
+                    "decode_quant: cache dtype must be PA_FP8_E4M3 or PA_INT8 (or their _PER_CHANNEL forms)");
     if (q_dtype != PA_BF16 && q_dtype != PA_F16)
         return fail(PA_ERR_UNSUPPORTED, "decode_quant: q must be bf16 or f16");
     if (out_dtype != PA_F32 && out_dtype != q_dtype)
@@ -1226,6 +1237,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_
     a.v_cache = v_cache;
     a.k_scale = k_scale;
     a.v_scale = v_scale;
+    a.chan_scales = is_per_channel(cache->dtype) ? 1 : 0;
     a.block_table = block_table;
     a.context_lens = context_lens;
     a.out = out;
@@ -1264,7 +1276,7 @@ int decode_quant_impl(const void* q, pa_dtype q_dtype, int32_t batch, int32_t q_
         a.v_scale_w = fa->v_scale_w;
     }
     const hipError_t e = pa::launch_decode_quant(a, to_elem(q_dtype),
-                                                 static_cast<pa::QuantFmt>(static_cast<int>(cache->dtype)),
+                                                 fmt_of(cache->dtype),
                                                  cache->head_dim, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "decode_quant launch");
     return PA_OK;

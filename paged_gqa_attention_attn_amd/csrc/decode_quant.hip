@@ -27,6 +27,14 @@
 //    quantised in registers exactly as the quantising append does (quant.h),
 //    patched into the LDS copy of their block, and written to the cache by one
 //    wave at the end, so the step equals the append followed by the decode.
+//  * Per-channel scales (one fixed fp32 scale per (KV head, channel), the other
+//    granularity of the same item): no scale copies. The K scales multiply q
+//    once, q * sk held as a bf16 hi + lo pair (so S^T runs on the bf16 matrix
+//    cores with about 16 significant bits of q * sk, two products per k-step);
+//    the V scales multiply the O^T rows (dims) once at the end; P is not scaled.
+//  * Several query rows per sequence (multi-row decode, chunked prefill): the
+//    (query head, row) pairs of a KV head take the columns; a row at position
+//    ctx - NR + r sees keys up to that position.
 // Rows are stored with their 16-byte chunk c at position c ^ swz(row), swz
 // chosen for one-byte rows so that both operand reads stay conflict-free.
 #include <type_traits>
@@ -82,6 +90,13 @@ template <> __device__ __forceinline__ uint2 widen4<QInt8, F16>(uint32_t w) {
     return make_uint2(__builtin_bit_cast(uint32_t, a), __builtin_bit_cast(uint32_t, b));
 }
 
+// A 16-bit element of q's type (bits in the low half) as fp32, exactly.
+template <class E> __device__ __forceinline__ float half_to_f32(uint32_t bits);
+template <> __device__ __forceinline__ float half_to_f32<BF16>(uint32_t bits) { return as_f32(bits << 16); }
+template <> __device__ __forceinline__ float half_to_f32<F16>(uint32_t bits) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits);
+}
+
 template <class E> struct Mfma16;
 template <> struct Mfma16<BF16> {
     static __device__ __forceinline__ f32x4_t qk(u32x4_t a, u32x4_t b, f32x4_t c) {
@@ -104,14 +119,14 @@ template <> struct Mfma16<F16> {
     }
 };
 
-template <int D, int HW, int R> struct QLayout {
+template <int D, int HW, int R, bool PC = false> struct QLayout {
     static constexpr int ROW = D;                     // bytes per token row (one-byte codes)
     static constexpr int CPR = ROW / 16;              // 16-byte chunks per row: 8 or 4
     static constexpr int TILE = BS * ROW;             // one (block, KV head) code tile
     static constexpr int NQ = TILE / 1024;            // 1 KB wave copies per tile
     static constexpr int SC = 256;                    // scale copy: K scales, V scales, repeat
     static constexpr int SLOTB = 2 * TILE + SC;       // one ring slot
-    static constexpr int OPS = 2 * NQ + 1;            // vector-memory operations per block
+    static constexpr int OPS = 2 * NQ + (PC ? 0 : 1); // vector-memory operations per block (no scale copy per channel)
     static constexpr int RING = R * SLOTB;            // R blocks in flight per wave
     static constexpr int PITCH = D + 4;
     static constexpr int SLOT = HW * PITCH + 2 * HW;  // merge slot floats
@@ -121,10 +136,13 @@ template <int D, int HW, int R> struct QLayout {
     static __device__ __forceinline__ int swz(int r) { return (r / (16 / CPR)) & (CPR - 1); }
 };
 
-template <class Q, class E, int D, int HW, int R>
+template <class Q, class E, int D, int HW, int R, bool PC>
 __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const DecodeArgs p) {
-    using L = QLayout<D, HW, R>;
+    using L = QLayout<D, HW, R, PC>;
     using S = typename E::storage;
+    // Matrix-core operand type: q's own, or bf16 per channel, where q arrives
+    // multiplied by the K channel scales as a bf16 hi + lo pair.
+    using M = typename std::conditional<PC, BF16, E>::type;
     constexpr int ROW = L::ROW, TILE = L::TILE, NQ = L::NQ, OPS = L::OPS;
     constexpr int KK = D / 32;    // S^T k-steps
     constexpr int MT = D / 16;    // O^T tiles
@@ -151,13 +169,33 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     const int v_col = hsgi * HW + (col < HW ? col : 0);
     const int blk0 = part * p.waves_tok * p.blocks_per_wave + wave * p.blocks_per_wave;
     u32x4_t qreg[KK];
+    u32x4_t qlo[PC ? KK : 1];   // per channel: the lo part of q * K scale
     {
         const char* qrow = (const char*)p.q + qo_row(v_col) * (D * 2);
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
             uint4 v = make_uint4(0, 0, 0, 0);
             if (col < HW) v = q_fold(*reinterpret_cast<const uint4*>(qrow + (32 * kk + 8 * grp) * 2), p.q_and, p.q_xor);
-            qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
+            if constexpr (PC) {
+                // Dims 32 kk + 8 grp + i: q_i * sk_i in fp32, then hi = bf16(x), lo = bf16(x - hi).
+                const float* sk = p.k_scale + (int64_t)g * D + 32 * kk + 8 * grp;
+                const float4 s0 = *reinterpret_cast<const float4*>(sk);
+                const float4 s1 = *reinterpret_cast<const float4*>(sk + 4);
+                const float sc[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float x0 = half_to_f32<E>(w[i] & 0xffffu) * sc[2 * i];
+                    const float x1 = half_to_f32<E>(w[i] >> 16) * sc[2 * i + 1];
+                    hi[i] = Mfma<BF16>::pack(x0, x1);
+                    lo[i] = Mfma<BF16>::pack(x0 - Mfma<BF16>::lo_of(hi[i]), x1 - Mfma<BF16>::hi_of(hi[i]));
+                }
+                qreg[kk] = u32x4_t{hi[0], hi[1], hi[2], hi[3]};
+                qlo[kk] = u32x4_t{lo[0], lo[1], lo[2], lo[3]};
+            } else {
+                qreg[kk] = u32x4_t{v.x, v.y, v.z, v.w};
+            }
         }
     }
     int my_phys = 0;
@@ -212,8 +250,17 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             xk[i] = load_f32<E>(p.k_new, e0 + i);
             xv[i] = load_f32<E>(p.v_new, e0 + i);
         }
-        new_ks = quantize_row<Q::kFp8, EPL>(xk, new_kc);
-        new_vs = quantize_row<Q::kFp8, EPL>(xv, new_vc);
+        if constexpr (PC) {
+            const int64_t c0 = (int64_t)g * D + lane * EPL;
+#pragma unroll
+            for (int i = 0; i < EPL; ++i) {
+                new_kc |= channel_code<Q::kFp8>(xk[i], p.k_scale[c0 + i]) << (8 * i);
+                new_vc |= channel_code<Q::kFp8>(xv[i], p.v_scale[c0 + i]) << (8 * i);
+            }
+        } else {
+            new_ks = quantize_row<Q::kFp8, EPL>(xk, new_kc);
+            new_vs = quantize_row<Q::kFp8, EPL>(xv, new_vc);
+        }
     }
 
     char* ring = smem + wave * L::WAVE_BYTES;
@@ -241,7 +288,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
         for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(kb + src_off[qq], dst + qq * 1024, once);
 #pragma unroll
         for (int qq = 0; qq < NQ; ++qq) copy_to_lds16(vb + src_off[qq], dst + TILE + qq * 1024, once);
-        copy_to_lds4(sbase + phys * p.n_kv * BS, dst + 2 * TILE, once);
+        if constexpr (!PC) copy_to_lds4(sbase + phys * p.n_kv * BS, dst + 2 * TILE, once);
     };
 
     uint32_t k_off[KK];   // K operand: row col, bytes 32 kk + 8 grp .. +8
@@ -293,7 +340,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
                     *reinterpret_cast<uint8_t*>(base + at) = (uint8_t)new_kc;
                     *reinterpret_cast<uint8_t*>(base + TILE + at) = (uint8_t)new_vc;
                 }
-                if (lane == 0) {
+                if (!PC && lane == 0) {
                     *reinterpret_cast<float*>(base + 2 * TILE + 4 * r) = new_ks;
                     *reinterpret_cast<float*>(base + 2 * TILE + 64 + 4 * r) = new_vs;
                 }
@@ -315,7 +362,7 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
 #pragma unroll
             for (int kk = 0; kk < KK; ++kk) {
                 const uint2 c8 = *reinterpret_cast<const uint2*>(base + k_off[kk]);
-                const uint2 lo = widen4<Q, E>(c8.x), hi = widen4<Q, E>(c8.y);
+                const uint2 lo = widen4<Q, M>(c8.x), hi = widen4<Q, M>(c8.y);
                 ka[kk] = u32x4_t{lo.x, lo.y, hi.x, hi.y};
             }
             uint2 va[MT];
@@ -325,20 +372,28 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
 #pragma unroll
                 for (int e = 0; e < 4; ++e)
                     w |= (uint32_t)*reinterpret_cast<const uint8_t*>(base + v_off[e] + ((t ^ v_sw[e]) * 16)) << (8 * e);
-                va[t] = widen4<Q, E>(w);
+                va[t] = widen4<Q, M>(w);
             }
-            const float4 ks = *reinterpret_cast<const float4*>(base + 2 * TILE + 16 * grp);
-            const float4 vs = *reinterpret_cast<const float4*>(base + 2 * TILE + 64 + 16 * grp);
+            float4 ks = make_float4(1.f, 1.f, 1.f, 1.f), vs = ks;   // per channel: scales applied outside
+            if constexpr (!PC) {
+                ks = *reinterpret_cast<const float4*>(base + 2 * TILE + 16 * grp);
+                vs = *reinterpret_cast<const float4*>(base + 2 * TILE + 64 + 16 * grp);
+            }
             lds_reads_done();
             if (i + R < nb) issue(i + R);
 
             f32x4_t s = f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KK; ++kk) s = Mfma16<E>::qk(ka[kk], qreg[kk], s);
-            s[0] *= ks.x;
-            s[1] *= ks.y;
-            s[2] *= ks.z;
-            s[3] *= ks.w;
+            for (int kk = 0; kk < KK; ++kk) {
+                s = Mfma16<M>::qk(ka[kk], qreg[kk], s);
+                if constexpr (PC) s = Mfma16<M>::qk(ka[kk], qlo[kk], s);
+            }
+            if constexpr (!PC) {
+                s[0] *= ks.x;
+                s[1] *= ks.y;
+                s[2] *= ks.z;
+                s[3] *= ks.w;
+            }
             if (alibi) {   // - m_h log2(e) (i - j) for the column's row i and key j = pos0 + 4 grp + j'
                 const float b0 = al2 * (float)(pos0 + 4 * grp - col_hi);
 #pragma unroll
@@ -368,27 +423,34 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             for (int j = 0; j < 4; ++j) {
                 const float pj = __builtin_amdgcn_exp2f(fmaf(s[j], c2, -m_run));
                 l_run += pj;
-                pr[j] = live[j] ? pj * vsc[j] : 0.f;   // V scale folded into P
+                pr[j] = live[j] ? (PC ? pj : pj * vsc[j]) : 0.f;   // per row: V scale folded into P
             }
-            const uint2 ph = make_uint2(Mfma<E>::pack(pr[0], pr[1]), Mfma<E>::pack(pr[2], pr[3]));
-            if constexpr (Mfma<E>::kSplit) {
+            const uint2 ph = make_uint2(Mfma<M>::pack(pr[0], pr[1]), Mfma<M>::pack(pr[2], pr[3]));
+            if constexpr (Mfma<M>::kSplit) {
                 // hi and lo parts stacked along k of one 16x16x32 product (twice the
                 // rate of two 16x16x16 products): k slots 8 grp + j hold key 4 grp + j % 4,
                 // part j / 4, in both operands.
-                const uint2 pl = make_uint2(Mfma<E>::pack(pr[0] - Mfma<E>::lo_of(ph.x), pr[1] - Mfma<E>::hi_of(ph.x)),
-                                            Mfma<E>::pack(pr[2] - Mfma<E>::lo_of(ph.y), pr[3] - Mfma<E>::hi_of(ph.y)));
+                const uint2 pl = make_uint2(Mfma<M>::pack(pr[0] - Mfma<M>::lo_of(ph.x), pr[1] - Mfma<M>::hi_of(ph.x)),
+                                            Mfma<M>::pack(pr[2] - Mfma<M>::lo_of(ph.y), pr[3] - Mfma<M>::hi_of(ph.y)));
                 const u32x4_t pb = u32x4_t{ph.x, ph.y, pl.x, pl.y};
 #pragma unroll
                 for (int t = 0; t < MT; ++t)
-                    o[t] = Mfma16<E>::qk(u32x4_t{va[t].x, va[t].y, va[t].x, va[t].y}, pb, o[t]);
+                    o[t] = Mfma16<M>::qk(u32x4_t{va[t].x, va[t].y, va[t].x, va[t].y}, pb, o[t]);
             } else {
 #pragma unroll
-                for (int t = 0; t < MT; ++t) o[t] = Mfma16<E>::pv(va[t], ph, o[t]);
+                for (int t = 0; t < MT; ++t) o[t] = Mfma16<M>::pv(va[t], ph, o[t]);
             }
         }
     }
 
     l_run = stride_reduce<16, false>(l_run);
+    if constexpr (PC) {   // O^T rows are dims 16 t + 4 grp + j: times their V channel scales
+#pragma unroll
+        for (int t = 0; t < MT; ++t) {
+            const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + (int64_t)g * D + 16 * t + 4 * grp);
+            o[t] *= f32x4_t{sv.x, sv.y, sv.z, sv.w};
+        }
+    }
     float* mine = reinterpret_cast<float*>(ring);
     if (col < HW) {
 #pragma unroll
@@ -455,23 +517,27 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             *kd = (uint8_t)new_kc;
             *vd = (uint8_t)new_vc;
         }
-        if (lane == 0) {
+        if (!PC && lane == 0) {
             p.k_scale_w[row] = new_ks;
             p.v_scale_w[row] = new_vs;
         }
     }
 }
 
-template <class Q, class E, int D, int HW, int R> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
-    const size_t lds = (size_t)a.waves_tok * QLayout<D, HW, R>::WAVE_BYTES;
+template <class Q, class E, int D, int HW, int R, bool PC> hipError_t launch_pc(const DecodeArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)a.waves_tok * QLayout<D, HW, R, PC>::WAVE_BYTES;
     if (lds > 160 * 1024) return hipErrorInvalidValue;
     static const hipError_t opt_in = hipFuncSetAttribute(
-        reinterpret_cast<const void*>(&decode_quant_kernel<Q, E, D, HW, R>),
+        reinterpret_cast<const void*>(&decode_quant_kernel<Q, E, D, HW, R, PC>),
         hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024);
     if (opt_in != hipSuccess) return opt_in;
     const dim3 grid(a.nparts_max, a.n_kv * a.hsg, a.batch);
-    hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW, R>), grid, dim3(64 * a.waves_tok), lds, s, a);
-    hipError_t err = hipGetLastError();
+    hipLaunchKernelGGL((decode_quant_kernel<Q, E, D, HW, R, PC>), grid, dim3(64 * a.waves_tok), lds, s, a);
+    return hipGetLastError();
+}
+
+template <class Q, class E, int D, int HW, int R> hipError_t launch_typed(const DecodeArgs& a, hipStream_t s) {
+    const hipError_t err = a.chan_scales ? launch_pc<Q, E, D, HW, R, true>(a, s) : launch_pc<Q, E, D, HW, R, false>(a, s);
     if (err != hipSuccess || a.nparts_max <= 1) return err;
     DecodeArgs m = a;
     m.n_q = a.n_q * a.q_rows;   // the reduce kernel's rows: (b, r, h) in [B][q_rows][n_q] order

@@ -60,13 +60,15 @@ hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, 
 }
 
 
-// ---- quantised cache: one-byte codes and one fp32 scale per (token, KV head) row ----
-// (the quantisation itself is in quant.h)
+// ---- quantised cache: one-byte codes, and one fp32 scale per (token, KV head) row or fixed
+// per-channel scales (the quantisation itself is in quant.h)
 
 namespace {
 
 // One wave per (token, KV head, K or V) row: lane l holds elements EPL l .. EPL l + EPL - 1.
-template <class SRC, bool FP8, int D>
+// Per row (PC false): the row's scale goes to ks / vs [slots]. Per channel (PC true):
+// ks / vs are the fixed channel scales [n_kv][D], read only.
+template <class SRC, bool FP8, int D, bool PC>
 __global__ __launch_bounds__(256) void kv_append_quant_kernel(const void* k, const void* v,
                                                               const int64_t* __restrict__ slots,
                                                               int64_t rows, int32_t n_kv, int64_t num_slots,
@@ -85,56 +87,68 @@ __global__ __launch_bounds__(256) void kv_append_quant_kernel(const void* k, con
     float x[EPL];
 #pragma unroll
     for (int i = 0; i < EPL; ++i) x[i] = load_f32<SRC>(is_v ? v : k, tg * D + lane * EPL + i);
-    uint32_t codes;
-    const float scale = quantize_row<FP8, EPL>(x, codes);
+    uint32_t codes = 0;
+    float scale = 0.f;
+    if constexpr (PC) {
+        const float* cs = (is_v ? vs : ks) + g * D + lane * EPL;
+#pragma unroll
+        for (int i = 0; i < EPL; ++i) codes |= channel_code<FP8>(x[i], cs[i]) << (8 * i);
+    } else {
+        scale = quantize_row<FP8, EPL>(x, codes);
+    }
     const int64_t row = ((slot / 16) * n_kv + g) * 16 + slot % 16;
     uint8_t* dst = (is_v ? vc : kc) + row * D + lane * EPL;
     if constexpr (EPL == 2)
         *reinterpret_cast<uint16_t*>(dst) = (uint16_t)codes;
     else
         *dst = (uint8_t)codes;
-    if (lane == 0) (is_v ? vs : ks)[row] = scale;
+    if (!PC && lane == 0) (is_v ? vs : ks)[row] = scale;
 }
 
-template <class SRC, bool FP8>
+template <class SRC, bool FP8, bool PC>
 hipError_t launch_quant_typed(const void* k, const void* v, const int64_t* slots, int64_t rows, int32_t n_kv,
                               int32_t head_dim, int64_t num_slots, void* kc, void* vc, float* ks, float* vs,
                               hipStream_t s) {
     const dim3 grid((unsigned)((rows + 3) / 4));
     if (head_dim == 128)
-        hipLaunchKernelGGL((kv_append_quant_kernel<SRC, FP8, 128>), grid, dim3(256), 0, s, k, v, slots, rows, n_kv,
-                           num_slots, static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), ks, vs);
+        hipLaunchKernelGGL((kv_append_quant_kernel<SRC, FP8, 128, PC>), grid, dim3(256), 0, s, k, v, slots, rows,
+                           n_kv, num_slots, static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), ks, vs);
     else if (head_dim == 64)
-        hipLaunchKernelGGL((kv_append_quant_kernel<SRC, FP8, 64>), grid, dim3(256), 0, s, k, v, slots, rows, n_kv,
-                           num_slots, static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), ks, vs);
+        hipLaunchKernelGGL((kv_append_quant_kernel<SRC, FP8, 64, PC>), grid, dim3(256), 0, s, k, v, slots, rows,
+                           n_kv, num_slots, static_cast<uint8_t*>(kc), static_cast<uint8_t*>(vc), ks, vs);
     else
         return hipErrorInvalidValue;
     return hipGetLastError();
 }
 
 template <class SRC>
-hipError_t launch_quant_src(bool fp8, const void* k, const void* v, const int64_t* slots, int64_t rows,
+hipError_t launch_quant_src(bool fp8, bool pc, const void* k, const void* v, const int64_t* slots, int64_t rows,
                             int32_t n_kv, int32_t head_dim, int64_t num_slots, void* kc, void* vc, float* ks,
                             float* vs, hipStream_t s) {
-    return fp8 ? launch_quant_typed<SRC, true>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s)
-               : launch_quant_typed<SRC, false>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s);
+    if (pc)
+        return fp8 ? launch_quant_typed<SRC, true, true>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s)
+                   : launch_quant_typed<SRC, false, true>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s);
+    return fp8 ? launch_quant_typed<SRC, true, false>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s)
+               : launch_quant_typed<SRC, false, false>(k, v, slots, rows, n_kv, head_dim, num_slots, kc, vc, ks, vs, s);
 }
 
 }  // namespace
 
-hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, const int64_t* slots,
-                                  int32_t num_tokens, int32_t n_kv, int32_t head_dim, int64_t num_slots,
-                                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, hipStream_t s) {
+hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, bool per_channel,
+                                  const int64_t* slots, int32_t num_tokens, int32_t n_kv, int32_t head_dim,
+                                  int64_t num_slots, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                                  hipStream_t s) {
     const int64_t rows = (int64_t)num_tokens * n_kv * 2;
     if (rows == 0) return hipSuccess;
     const bool fp8 = fmt == QuantFmt::FP8_E4M3;
+    const bool pc = per_channel;
     switch (src) {
     case Elem::F32:
-        return launch_quant_src<F32>(fp8, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
+        return launch_quant_src<F32>(fp8, pc, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
     case Elem::BF16:
-        return launch_quant_src<BF16>(fp8, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
+        return launch_quant_src<BF16>(fp8, pc, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
     case Elem::F16:
-        return launch_quant_src<F16>(fp8, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
+        return launch_quant_src<F16>(fp8, pc, k, v, slots, rows, n_kv, head_dim, num_slots, k_cache, v_cache, k_scale, v_scale, s);
     }
     return hipErrorInvalidValue;
 }

@@ -57,11 +57,14 @@ struct DecodeArgs {
     int32_t mfma;
     // Quantised cache (decode_quant.hip): per-row scales [num_blocks][n_kv][16], and
     // their writable views for a fused quantising append (k_new / v_new then hold
-    // the new rows in q's type, quantised as pa_kv_append_quant does).
+    // the new rows in q's type, quantised as pa_kv_append_quant does). With
+    // chan_scales set, k_scale / v_scale are fixed channel scales [n_kv][D] instead
+    // and the append writes codes only.
     const float* k_scale;
     const float* v_scale;
     float* k_scale_w;
     float* v_scale_w;
+    int32_t chan_scales;
 };
 
 hipError_t launch_decode(const DecodeArgs& a, Elem e, int head_dim, hipStream_t s);
@@ -76,10 +79,13 @@ hipError_t launch_decode_multi(const DecodeArgs& a, Elem e, int head_dim, hipStr
 hipError_t launch_decode_quant(const DecodeArgs& a, Elem q_type, QuantFmt fmt, int head_dim, hipStream_t s);
 // LDS bytes one wave of the quantised decode kernel takes for hw heads and a ring of `ring` blocks.
 int quant_wave_bytes(int head_dim, int hw, int ring);
-// Quantise k/v rows ([T][n_kv][D] in src) per row into codes + scales at slot_mapping.
-hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, const int64_t* slots,
-                                  int32_t num_tokens, int32_t n_kv, int32_t head_dim, int64_t num_slots,
-                                  void* k_cache, void* v_cache, float* k_scale, float* v_scale, hipStream_t s);
+// Quantise k/v rows ([T][n_kv][D] in src) into codes at slot_mapping: per row (scales
+// written to k_scale / v_scale [slots]) or, per_channel, with the fixed channel scales
+// k_scale / v_scale [n_kv][D] (read only).
+hipError_t launch_kv_append_quant(const void* k, const void* v, Elem src, QuantFmt fmt, bool per_channel,
+                                  const int64_t* slots, int32_t num_tokens, int32_t n_kv, int32_t head_dim,
+                                  int64_t num_slots, void* k_cache, void* v_cache, float* k_scale, float* v_scale,
+                                  hipStream_t s);
 
 hipError_t launch_kv_append(const void* k, const void* v, const int64_t* slots, int32_t num_tokens,
                             int32_t n_kv, int32_t row_bytes, int32_t block_size,

@@ -1,6 +1,6 @@
-// quant.h -- the per-row quantisation of the one-byte KV cache, shared by the
-// quantising append and the decode that fuses it, so that both produce the same
-// codes and scales bit for bit.
+// quant.h -- the quantisation of the one-byte KV cache (per row, or per channel
+// with fixed scales), shared by the quantising append and the decode that fuses
+// it, so that both produce the same codes and scales bit for bit.
 //
 // "LLM 推理全过程的维度变化与核心公式" (research.frankk.site), "KV Cache 的形状与增长":
 // the fp16 cache quantised to int8 / fp8 per channel or per token. Read as per-token,
@@ -46,6 +46,26 @@ template <> __device__ __forceinline__ float load_f32<F16>(const void* p, int64_
     return (float)__builtin_bit_cast(_Float16, static_cast<const uint16_t*>(p)[i]);
 }
 
+// The code of y = x / scale: the nearest E4M3 value of y clamped to [-448, 448], or
+// rint(y) clamped to [-127, 127] (one byte, two's complement).
+template <bool FP8> __device__ __forceinline__ uint32_t code_of(float y) {
+    if constexpr (FP8) {
+        return e4m3_code(fminf(fmaxf(y, -448.0f), 448.0f));
+    } else {
+        return (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f) & 0xffu;
+    }
+}
+
+// Per-channel codes (the "per channel" granularity of the same item): element x
+// of a channel whose fixed scale s the caller gives. s below the smallest normal
+// float stores code 0; otherwise inv = 1 / s, y = x * inv and code_of(y), so a
+// value past QMAX * s saturates.
+template <bool FP8> __device__ __forceinline__ uint32_t channel_code(float x, float s) {
+    if (!(s >= 0x1p-126f)) return 0;
+    const float inv = __fdiv_rn(1.0f, s);
+    return code_of<FP8>(__fmul_rn(x, inv));
+}
+
 // Quantises one row spread over a wave, EPL values per lane (lane l holds row
 // elements EPL l .. EPL l + EPL - 1). Returns the row's scale (the same in every
 // lane) and this lane's codes, element i in byte i.
@@ -62,16 +82,7 @@ __device__ __forceinline__ float quantize_row(const float (&x)[EPL], uint32_t& c
     if (scale >= 0x1p-126f) {
         const float inv = __fdiv_rn(1.0f, scale);
 #pragma unroll
-        for (int i = 0; i < EPL; ++i) {
-            const float y = __fmul_rn(x[i], inv);
-            uint32_t c;
-            if constexpr (FP8) {
-                c = e4m3_code(fminf(fmaxf(y, -448.0f), 448.0f));
-            } else {
-                c = (uint32_t)(int32_t)fminf(fmaxf(__builtin_rintf(y), -127.0f), 127.0f) & 0xffu;
-            }
-            codes |= c << (8 * i);
-        }
+        for (int i = 0; i < EPL; ++i) codes |= code_of<FP8>(__fmul_rn(x[i], inv)) << (8 * i);
     } else {
         scale = 0.f;
     }

@@ -485,11 +485,24 @@ def test_decode_quant_append_empty_batch_is_a_noop(L):
     assert decode_quant_append(L, batch=0) == PA_OK
 
 
-def test_quantised_cache_refused_elsewhere(L):
-    # The bf16/f16 entry points do not take a quantised cache description.
-    assert decode(L, cache=desc(dtype=FP8)) == UNSUPPORTED
+@pytest.mark.parametrize("dt", [FP8, INT8, _lib.PA_FP8_E4M3_PER_CHANNEL, _lib.PA_INT8_PER_CHANNEL])
+def test_quantised_cache_refused_elsewhere(L, dt):
+    # The f32/bf16/f16 entry points do not take a quantised cache description.
+    assert decode(L, cache=desc(dtype=dt)) == UNSUPPORTED
     assert "quantised" in _lib.last_error()
-    assert L.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, desc(dtype=INT8), None) == UNSUPPORTED
+    assert L.pa_kv_append(FAKE, FAKE, FAKE, 4, FAKE, FAKE, desc(dtype=dt), None) == UNSUPPORTED
+    assert chunked(L, cache=desc(dtype=dt)) == UNSUPPORTED
+    assert multi(L, cache=desc(dtype=dt)) == UNSUPPORTED
+
+
+def test_per_channel_caches_take_the_quantised_checks(L):
+    for dt in (_lib.PA_FP8_E4M3_PER_CHANNEL, _lib.PA_INT8_PER_CHANNEL):
+        assert append_quant(L, cache=desc(dtype=dt), ks=FAKE + 4) == INVALID
+        assert "aligned" in _lib.last_error()
+        assert decode_quant(L, cache=desc(dtype=dt), q_dtype=_lib.PA_F32) == UNSUPPORTED
+        assert rows_quant(L, "pa_paged_attn_decode_multi_quant", cache=desc(dtype=dt), vs=None) == INVALID
+        assert append_quant(L, cache=desc(dtype=dt), T=0) == PA_OK
+    assert append_quant(L, cache=desc(dtype=7)) != PA_OK     # past the last dtype
 
 
 def append_quant(L, **kw):

@@ -411,3 +411,150 @@ def test_rows_quant_bad_metadata_and_bf16_output(pa):
     # bf16 output: the fp32 result's rounding (half an ulp, 2^-9 relative) on top of the tolerance.
     got16 = o16.float().cpu().numpy()
     assert (np.abs(got16 - want) <= 2e-3 + 2.0 ** -8 * np.abs(want)).all(), "bf16 output"
+
+
+# ---- per-channel scales ------------------------------------------------------------------
+#
+# The same codes with one fixed fp32 scale per (KV head, channel), given by the caller. The
+# append must give the oracle's codes bit for bit (saturating past QMAX * scale, code 0 for a
+# scale below the smallest normal float); the attention calls meet the oracle over
+# code * channel scale.
+
+def _chan_scales(seed, n_kv, d, fmt, device="cuda"):
+    g = torch.Generator(device=device).manual_seed(seed)
+    qmax = wl.QUANT_QMAX[fmt]
+    k = (3.0 / qmax) * (0.5 + torch.rand((n_kv, d), generator=g, device=device))
+    v = (3.0 / qmax) * (0.5 + torch.rand((n_kv, d), generator=g, device=device))
+    return k.float().contiguous(), v.float().contiguous()
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("src", ["bf16", "f16", "f32"])
+@pytest.mark.parametrize("d", [128, 64])
+def test_append_quant_per_channel_bit_exact(pa, fmt, src, d):
+    T, n_kv, nb = 300, 2, 40
+    g = torch.Generator(device="cuda").manual_seed(zlib.crc32(f"chan{fmt}{src}{d}".encode()))
+    dt = wl.TORCH_DTYPES[src]
+    k = (torch.randn((T, n_kv, d), generator=g, device="cuda") * 2.0).to(dt)   # many past 3 * scale: saturate
+    v = (torch.randn((T, n_kv, d), generator=g, device="cuda") * 0.5).to(dt)
+    ks, vs = _chan_scales(7, n_kv, d, fmt)
+    ks[0, 3] = 0.0                 # a channel with scale 0: codes 0
+    vs[1, 5] = 1e-39               # a subnormal scale: codes 0
+    slots = torch.as_tensor(np.random.default_rng(2).permutation(nb * 16)[:T], device="cuda")
+    slots[10] = -1
+    slots[11] = nb * 16 + 3
+    code_dt = wl.QUANT_CODE_DTYPES[fmt]
+    kc = torch.full((nb, n_kv, 16, d), 0x55, dtype=torch.uint8, device="cuda").view(code_dt)
+    vc = kc.clone()
+    okc, ovc = _np(kc).copy(), _np(vc).copy()
+    ks0, vs0 = ks.clone(), vs.clone()
+    say(f"[quant append] per-channel {fmt} from {src}, d={d}, T={T}")
+    pa.kv_append_quant(k, v, slots, kc, vc, ks, vs, f"{fmt}_per_channel")
+    torch.cuda.synchronize()
+    oslots = _np(slots).copy()
+    oslots[11] = -1
+    oracle.kv_append_quant_channel(stored_np(k), stored_np(v), src, oslots, okc, ovc, _np(ks), _np(vs), fmt)
+    assert np.array_equal(_np(kc), okc), "K codes differ from the oracle"
+    assert np.array_equal(_np(vc), ovc), "V codes differ from the oracle"
+    assert same_bits(ks, ks0) and same_bits(vs, vs0), "the channel scales must only be read"
+    qmax = wl.QUANT_QMAX[fmt]
+    cv = okc.view(np.uint8) if fmt == "fp8" else okc
+    assert (np.abs(oracle.upcast(cv, fmt)) == qmax).sum() > 100, "the case must saturate some values"
+
+
+def _chan_case(fmt, q_dtype, ctx, n_q, n_kv, d, seed, free=0.25):
+    c = wl.make_quant_decode_case(fmt=fmt, q_dtype=q_dtype, batch=len(ctx), n_q=n_q, n_kv=n_kv, head_dim=d,
+                                  context_lens=ctx, free_fraction=free, seed=seed, device="cuda", name="chan")
+    ks, vs = _chan_scales(seed + 3, n_kv, d, fmt)
+    return c, ks, vs
+
+
+def _oracle_chan(c, ks, vs, q=None, rows=False, **kw):
+    args = (stored_np(c.q if q is None else q), _np(c.k_pool), _np(c.v_pool), c.fmt, _np(c.block_table),
+            _np(c.context_lens), c.scale)
+    kw.update(q_dtype=c.q_dtype, k_scale=_np(ks), v_scale=_np(vs), scale_mode="channel")
+    return oracle.chunked_prefill(*args, **kw) if rows else oracle.decode(*args, **kw)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+@pytest.mark.parametrize("name", ["gqa4_d128", "gqa4_d64_f16", "gqa8_d128", "mha_d128", "gqa2_f16", "mqa32_d64"])
+def test_decode_quant_per_channel_matches_oracle(pa, fmt, name):
+    n_q, n_kv, d, ctx, qdt = SHAPES[name]
+    c, ks, vs = _chan_case(fmt, qdt, ctx, n_q, n_kv, d, seed=zlib.crc32(f"chan{fmt}{name}".encode()) % 9973)
+    say(f"[quant decode] per-channel {fmt} {name}: ctx={ctx}")
+    out = nan_out((c.batch, n_q, d))
+    pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                               c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    stats = assert_parity(out.cpu().numpy(), _oracle_chan(c, ks, vs), qdt, f"per-channel {fmt} {name}")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_decode_quant_per_channel_split_window_alibi(pa, fmt):
+    c, ks, vs = _chan_case(fmt, "bf16", [3000, 1, 700, 2048], 16, 4, 128, seed=17)
+    m = (2.0 ** (-8.0 * (np.arange(16) + 1) / 16)).astype(np.float32)
+    prev = pa.set_decode_partition_tokens(256)
+    try:
+        say(f"[quant decode] per-channel {fmt}: 256-token partitions, window 900, ALiBi")
+        a = pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                                       c.context_lens, c.scale)
+        w = pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                                       c.context_lens, c.scale, window=900,
+                                       alibi_slopes=torch.as_tensor(m, device="cuda"))
+        torch.cuda.synchronize()
+    finally:
+        pa.set_decode_partition_tokens(prev)
+    assert_parity(a.cpu().numpy(), _oracle_chan(c, ks, vs), "bf16", "split per-channel decode")
+    assert_parity(w.cpu().numpy(), _oracle_chan(c, ks, vs, window=900, alibi=m), "bf16",
+                  "split windowed ALiBi per-channel decode")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_decode_quant_append_per_channel_equals_two_calls(pa, fmt):
+    c, ks, vs = _chan_case(fmt, "bf16", [17, 300, 1], 8, 2, 128, seed=23)
+    say(f"[quant decode] per-channel {fmt}: fused append vs append + decode, bitwise")
+    kc1, vc1 = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append_quant(c.new_k, c.new_v, c.slot_mapping, kc1, vc1, ks, vs, f"{fmt}_per_channel")
+    two = pa.paged_attn_decode_quant(c.q, kc1, vc1, ks, vs, f"{fmt}_per_channel", c.block_table, c.context_lens,
+                                     c.scale)
+    kc2, vc2 = c.k_pool.clone(), c.v_pool.clone()
+    one = pa.paged_attn_decode_quant_append(c.q, c.new_k, c.new_v, c.slot_mapping, kc2, vc2, ks, vs,
+                                            f"{fmt}_per_channel", c.block_table, c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert same_bits(kc1, kc2) and same_bits(vc1, vc2), "the fused append wrote other codes"
+    assert same_bits(one, two), "the fused step differs from append + decode"
+    want = oracle.decode(stored_np(c.q), _np(kc1), _np(vc1), fmt, _np(c.block_table), _np(c.context_lens),
+                         c.scale, q_dtype="bf16", k_scale=_np(ks), v_scale=_np(vs), scale_mode="channel")
+    assert_parity(one.cpu().numpy(), want, "bf16", "fused per-channel step")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_rows_quant_per_channel_matches_oracle(pa, fmt):
+    c, ks, vs = _chan_case(fmt, "f16", [100, 433, 40], 8, 2, 128, seed=29)
+    g = torch.Generator(device="cuda").manual_seed(29)
+    q = torch.randn(3, 37, 8, 128, generator=g, device="cuda").half()
+    say(f"[quant rows] per-channel {fmt}: chunked prefill of 37 rows and multi-row decode of 4")
+    out = pa.paged_attn_chunked_prefill_quant(q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                                              c.context_lens, c.scale, window=120)
+    q4 = q[:, -4:].contiguous()
+    out4 = pa.paged_attn_decode_multi_quant(q4, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                                            c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert_parity(out.cpu().numpy(), _oracle_chan(c, ks, vs, q=q, rows=True, window=120), "f16",
+                  "per-channel chunked prefill")
+    assert_parity(out4.cpu().numpy(), _oracle_chan(c, ks, vs, q=q4, rows=True), "f16", "per-channel multi-row")
+
+
+def test_decode_quant_per_channel_relabelling_is_bitwise(pa):
+    c, ks, vs = _chan_case("fp8", "bf16", [1200, 77], 16, 4, 128, seed=31)
+    say("[quant decode] per-channel fp8 under a relabelling of physical blocks")
+    a = pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, "fp8_per_channel", c.block_table,
+                                   c.context_lens, c.scale)
+    perm = torch.as_tensor(np.random.default_rng(4).permutation(c.num_blocks), device="cuda")
+    inv = torch.empty_like(perm)
+    inv[perm] = torch.arange(c.num_blocks, device="cuda")
+    b = pa.paged_attn_decode_quant(c.q, c.k_pool[inv].contiguous(), c.v_pool[inv].contiguous(), ks, vs,
+                                   "fp8_per_channel", perm[c.block_table.long()].int(), c.context_lens, c.scale)
+    torch.cuda.synchronize()
+    assert same_bits(a, b)
