@@ -19,8 +19,10 @@
 //    exact conversion; INT8: through fp32, exact), so the product runs on the
 //    bf16/f16 matrix cores; the K scale multiplies the 4 scores each lane holds.
 //  * The V scale folds into P (P' = P * v_scale per key; the softmax
-//    denominator keeps P), and V^T is gathered from the row-major code tile with
-//    byte reads (4 keys of one dim per lane) and widened the same way.
+//    denominator keeps P). V^T comes from the row-major code tile in dwords (4
+//    dims of one key); the dwords of a lane's 4 keys are byte-transposed in
+//    registers (8 v_perm per 64 dims), so O^T tile t = 4 h + m takes dims
+//    64 h + 4 r + m as its rows r, and widened like K.
 //  * Codes of rows outside [first, ctx) are zeroed in LDS and their P' is
 //    selected to 0: an unused slot may hold a NaN code or a NaN scale.
 //  * A decode step may carry its own append: the new token's K and V rows are
@@ -297,13 +299,18 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
         const int c = 2 * kk + (grp >> 1);
         k_off[kk] = col * ROW + ((c ^ L::swz(col)) * 16) + 8 * (grp & 1);
     }
-    uint32_t v_off[4];    // V^T gather: byte col of row 4 grp + e, chunk t (t added below)
-    int v_sw[4];
+    // V^T operand: O^T tile t = 4 h + m takes dims 64 h + 4 r + m as its rows r, so
+    // one dword of key row 4 grp + e at dims 64 h + 4 col .. +3 feeds four tiles; a
+    // 4 x 4 byte transpose of the four keys' dwords gives each tile its 4 keys.
+    constexpr int VH = D / 64;   // halves of 64 dims
+    uint32_t v_off[VH][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        v_off[e] = TILE + (4 * grp + e) * ROW + col;
-        v_sw[e] = L::swz(4 * grp + e);
-    }
+    for (int h = 0; h < VH; ++h)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int r = 4 * grp + e;
+            v_off[h][e] = TILE + r * ROW + (((4 * h + col / 4) ^ L::swz(r)) * 16) + 4 * (col % 4);
+        }
 
     f32x4_t o[MT];
 #pragma unroll
@@ -367,12 +374,19 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
             }
             uint2 va[MT];
 #pragma unroll
-            for (int t = 0; t < MT; ++t) {
-                uint32_t w = 0;
+            for (int h = 0; h < VH; ++h) {
+                uint32_t w[4];   // key 4 grp + e, dims 64 h + 4 col + m in byte m
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w |= (uint32_t)*reinterpret_cast<const uint8_t*>(base + v_off[e] + ((t ^ v_sw[e]) * 16)) << (8 * e);
-                va[t] = widen4<Q, M>(w);
+                for (int e = 0; e < 4; ++e) w[e] = *reinterpret_cast<const uint32_t*>(base + v_off[h][e]);
+                // Byte transpose: x[m] holds dim 64 h + 4 col + m of keys e = 0..3 in byte e.
+                const uint32_t lo01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+                const uint32_t hi01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+                const uint32_t lo23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+                const uint32_t hi23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+                va[4 * h + 0] = widen4<Q, M>(__builtin_amdgcn_perm(lo23, lo01, 0x05040100u));
+                va[4 * h + 1] = widen4<Q, M>(__builtin_amdgcn_perm(lo23, lo01, 0x07060302u));
+                va[4 * h + 2] = widen4<Q, M>(__builtin_amdgcn_perm(hi23, hi01, 0x05040100u));
+                va[4 * h + 3] = widen4<Q, M>(__builtin_amdgcn_perm(hi23, hi01, 0x07060302u));
             }
             float4 ks = make_float4(1.f, 1.f, 1.f, 1.f), vs = ks;   // per channel: scales applied outside
             if constexpr (!PC) {
@@ -444,18 +458,21 @@ __global__ __launch_bounds__(64 * MAX_WAVES, 2) void decode_quant_kernel(const D
     }
 
     l_run = stride_reduce<16, false>(l_run);
-    if constexpr (PC) {   // O^T rows are dims 16 t + 4 grp + j: times their V channel scales
-#pragma unroll
-        for (int t = 0; t < MT; ++t) {
-            const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + (int64_t)g * D + 16 * t + 4 * grp);
-            o[t] *= f32x4_t{sv.x, sv.y, sv.z, sv.w};
-        }
-    }
+    // o[4 h + m][j] is dim 64 h + 16 grp + 4 j + m of column col: gather the four m.
     float* mine = reinterpret_cast<float*>(ring);
     if (col < HW) {
 #pragma unroll
-        for (int t = 0; t < MT; ++t)
-            *reinterpret_cast<f32x4_t*>(mine + col * L::PITCH + 16 * t + 4 * grp) = o[t];
+        for (int h = 0; h < VH; ++h)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int dim = 64 * h + 16 * grp + 4 * j;
+                f32x4_t x = {o[4 * h][j], o[4 * h + 1][j], o[4 * h + 2][j], o[4 * h + 3][j]};
+                if constexpr (PC) {   // times the V channel scales of those dims
+                    const float4 sv = *reinterpret_cast<const float4*>(p.v_scale + (int64_t)g * D + dim);
+                    x *= f32x4_t{sv.x, sv.y, sv.z, sv.w};
+                }
+                *reinterpret_cast<f32x4_t*>(mine + col * L::PITCH + dim) = x;
+            }
         if (grp == 0) {
             mine[HW * L::PITCH + col] = phys_bad ? 0.f : m_run;
             mine[HW * L::PITCH + HW + col] = phys_bad ? NAN : l_run;
