@@ -383,7 +383,9 @@ int pa_paged_attn_chunked_prefill(const void* q, int32_t batch, int32_t chunk_le
  * take a channel's range from tokens still to come): element c of every row of
  * KV head g with s = scale[g][c]: s below the smallest normal float stores code
  * 0; otherwise y = x * (1 / s) and the same code rule, so values past QMAX * s
- * saturate at +-QMAX. The stored value is code * s. Rows must be finite.
+ * saturate at +-QMAX. The stored value is code * s. Rows must be finite. A
+ * scale per KV head, or one for the whole cache, is this form with every
+ * channel of a head (or of the cache) given the same scale.
  * num_tokens == 0 is a no-op.
  */
 int pa_kv_append_quant(const void* k, const void* v, pa_dtype src_dtype, const int64_t* slot_mapping,

@@ -558,3 +558,31 @@ def test_decode_quant_per_channel_relabelling_is_bitwise(pa):
                                    "fp8_per_channel", perm[c.block_table.long()].int(), c.context_lens, c.scale)
     torch.cuda.synchronize()
     assert same_bits(a, b)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_decode_quant_per_head_scales_meet_the_fp32_cache(pa, fmt):
+    """One scale per KV head (or per tensor) is the per-channel format with each head's row
+    constant. With power-of-two head scales every code * scale is exact in fp32, so the call
+    must meet the oracle's plain fp32-cache decode of those dequantized values."""
+    c, _, _ = _chan_case(fmt, "bf16", [1500, 37, 800, 1], 16, 4, 128, seed=41)
+    kexp = np.array([-7, -6, -8, -5], dtype=np.float64)
+    vexp = np.array([-6, -9, -7, -7], dtype=np.float64)
+    ks = torch.as_tensor(np.repeat((2.0 ** kexp)[:, None], 128, axis=1), dtype=torch.float32, device="cuda")
+    vs = torch.as_tensor(np.repeat((2.0 ** vexp)[:, None], 128, axis=1), dtype=torch.float32, device="cuda")
+    say(f"[quant decode] per-head {fmt} scales as constant per-channel rows")
+    out = nan_out((c.batch, 16, 128))
+    pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                               c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+
+    def dequant(pool, exps):
+        codes = _np(pool)
+        codes = codes.view(np.uint8) if fmt == "fp8" else codes
+        return (oracle.upcast(codes, fmt) * (2.0 ** exps)[None, :, None, None]).astype(np.float32)
+
+    q32 = c.q.float().cpu().numpy()   # bf16 values, exact in fp32
+    want = oracle.decode(q32, dequant(c.k_pool, kexp), dequant(c.v_pool, vexp), "f32", _np(c.block_table),
+                         _np(c.context_lens), c.scale)
+    stats = assert_parity(out.cpu().numpy(), want, "bf16", f"per-head {fmt}")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
