@@ -156,3 +156,19 @@ def test_bf16_output(pa):
     got = gpu_multi(pa, c, out_dtype=torch.bfloat16).float().cpu().numpy()
     want = oracle_multi(c)
     assert (np.abs(got - want) <= 2e-3 + 2.0**-8 * np.abs(want)).all()
+
+
+def test_full_size_4_rows_on_the_8b_shape_all_rows(pa):
+    """The bench's speculative-verification shape: B=32, 4 new rows per sequence, 32/8 heads,
+    d=128, contexts of 2048 including the new rows, bf16; every one of the 4096 output rows
+    against the oracle, into a NaN-filled output."""
+    from gpu_helpers import nan_out
+    c = wl.make_chunk_case(batch=32, chunk_len=4, prefix_lens=[2044] * 32, n_q=32, n_kv=8, head_dim=128,
+                           dtype="bf16", seed=1007, device="cuda")
+    say("[multi] 8B shape, 4 rows per sequence, full size, all rows")
+    kp, vp = appended(pa, c)
+    out = nan_out(tuple(c.q.shape))
+    pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    stats = assert_parity(out.cpu().numpy(), oracle_multi(c), "bf16", "multi-row 8B, all 4096 rows")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")

@@ -586,3 +586,15 @@ def test_decode_quant_per_head_scales_meet_the_fp32_cache(pa, fmt):
                          _np(c.context_lens), c.scale)
     stats = assert_parity(out.cpu().numpy(), want, "bf16", f"per-head {fmt}")
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "int8"])
+def test_full_size_8b_per_channel_all_rows(pa, fmt):
+    c, ks, vs = _chan_case(fmt, "bf16", [2048] * 32, 32, 8, 128, seed=2012)
+    say(f"[quant decode] 8B shape, per-channel {fmt}, full size, all rows")
+    out = nan_out((32, 32, 128))
+    pa.paged_attn_decode_quant(c.q, c.k_pool, c.v_pool, ks, vs, f"{fmt}_per_channel", c.block_table,
+                               c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    stats = assert_parity(out.cpu().numpy(), _oracle_chan(c, ks, vs), "bf16", f"8B per-channel {fmt}, all rows")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
