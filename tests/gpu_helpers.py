@@ -69,6 +69,24 @@ def oracle_step(case, sel=None):
     return kp, vp, out
 
 
+def oracle_pools(case, k_new=None, v_new=None):
+    """The oracle's own append of a case's new tokens (a decode case's new_k / new_v /
+    slot_mapping, or a chunk case's chunk_k / chunk_v / chunk_slots; ``k_new`` / ``v_new``
+    replace the generator's rows when a test edits them) on host copies of the
+    generator's pools. Tests that append on the GPU hand the oracle these pools, never the
+    GPU's: no oracle input comes from the HIP path. Returns (k_pool, v_pool) as stored bits."""
+    kp = stored_np(case.k_pool).copy()
+    vp = stored_np(case.v_pool).copy()
+    if hasattr(case, "chunk_k"):
+        k, v, slots = case.chunk_k, case.chunk_v, case.chunk_slots
+    else:
+        k, v, slots = case.new_k, case.new_v, case.slot_mapping
+    k = k if k_new is None else k_new
+    v = v if v_new is None else v_new
+    oracle.kv_append(stored_np(k), stored_np(v), slots.cpu().numpy(), kp, vp)
+    return kp, vp
+
+
 def nan_out(shape, dtype=torch.float32, device="cuda") -> torch.Tensor:
     """An output buffer filled with NaN, so that any element a kernel never writes
     fails the parity check (torch.empty may hand back finite leftovers)."""

@@ -18,7 +18,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, nan_out, same_bits, say, stored_np
+from gpu_helpers import assert_parity, nan_out, oracle_pools, same_bits, say, stored_np
 from oracle_pins import alibi_slopes
 from paged_gqa_attention_attn_amd import workloads as wl
 
@@ -95,7 +95,7 @@ def test_decode_alibi_matches_oracle(pa, decode_kernel, name, kind, window):
     got = pa.paged_attn_decode(c.q, kp, vp, c.block_table, c.context_lens, c.scale, window=window,
                                alibi_slopes=_dev(m))
     torch.cuda.synchronize()
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), c.dtype,
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), c.dtype,
                          c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                          window=window, alibi=m)
     stats = assert_parity(got.cpu().numpy(), want, c.dtype, f"decode {name} {kind} W={window}")
@@ -115,7 +115,7 @@ def test_decode_alibi_partition_sizes(pa, decode_kernel, tokens):
         torch.cuda.synchronize()
     finally:
         pa.set_decode_partition_tokens(prev)
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), c.dtype,
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), c.dtype,
                          c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                          alibi=m)
     assert_parity(got.cpu().numpy(), want, c.dtype, f"partition {tokens}")
@@ -148,7 +148,7 @@ def test_decode_alibi_full_size_all_rows(pa):
     pa.paged_attn_decode_append(c.q, c.new_k, c.new_v, c.slot_mapping, kp, vp, c.block_table,
                                 c.context_lens, c.scale, alibi_slopes=_dev(m), out=got)
     torch.cuda.synchronize()
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16", _np(c.block_table),
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), "bf16", _np(c.block_table),
                          _np(c.context_lens), c.scale, alibi=m)
     stats = assert_parity(got.cpu().numpy(), want, "bf16", "8B alibi, all 1024 rows")
     say(f"    max_abs={stats['max_abs']:.2e}")
@@ -180,7 +180,7 @@ def test_decode_multi_alibi_matches_oracle(pa, decode_kernel, shape):
     got = pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, c.scale, window=W,
                                      alibi_slopes=_dev(m))
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), dt,
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), dt,
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                                   window=W, alibi=m)
     stats = assert_parity(got.cpu().numpy(), want, dt, f"multi W={W}")
@@ -210,7 +210,7 @@ def test_chunked_prefill_alibi_matches_oracle(pa, shape):
     got = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale,
                                         window=W, alibi_slopes=_dev(m))
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), dt,
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), dt,
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                                   window=W, alibi=m)
     stats = assert_parity(got.cpu().numpy(), want, dt, f"chunked W={W}")

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, same_bits, say, stored_np
+from gpu_helpers import assert_parity, oracle_pools, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -107,7 +107,10 @@ def test_chunked_prefill_v_beyond_f16_matches_oracle(pa, where):
     got = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
     torch.cuda.synchronize()
     got = got.cpu().numpy()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+    okp, ovp = oracle_pools(c, v_new=cv)      # the same edits on the oracle's own pools
+    if where == "prefix":
+        ovp[int(c.block_table[0, 5]), 0, 3, 11] = stored_np(torch.tensor([70144.0], dtype=torch.bfloat16))[0]
+    want = oracle.chunked_prefill(stored_np(c.q), okp, ovp, "bf16",
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale)
     assert np.isfinite(got).all()
     big = np.zeros(got.shape, bool)
@@ -153,7 +156,7 @@ def test_short_context_and_bad_metadata(pa):
     out = out.cpu()
     assert (out[0, :13] == 0).all(), "rows at negative positions must be zero"
     assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
-    want = oracle.chunked_prefill(stored_np(c.q[:2]), stored_np(kp), stored_np(vp), "bf16",
+    want = oracle.chunked_prefill(stored_np(c.q[:2]), *oracle_pools(c), "bf16",
                                   c.block_table[:2].cpu().numpy(), ctx[:2].cpu().numpy(), c.scale)
     assert_parity(out[0, 13:].numpy(), want[0, 13:], "bf16", "rows of the short sequence")
     assert_parity(out[1].numpy(), want[1], "bf16", "sequence next to bad metadata")
@@ -184,8 +187,25 @@ def test_chunked_prefill_past_the_copy_cap_keeps_the_bf16_product(pa, option):
     option("prefill_stage_v", 0)
     unstaged = pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale)
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), "bf16",
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale)
     stats = assert_parity(got.cpu().numpy(), want, "bf16", "chunked prefill, 9000-block table")
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
     assert same_bits(got, unstaged)
+
+
+def test_chunked_prefill_bench_shape_all_rows(pa):
+    """The bench's chunked prefill at full size: 2 sequences, a 1024-token chunk over a
+    3072-token paged prefix, 32/8 heads, d=128, bf16 (f16 copy of V); all 65536 (row, head)
+    outputs against the oracle, into a NaN-filled output."""
+    from gpu_helpers import nan_out
+    c = wl.make_chunk_case(batch=2, chunk_len=1024, prefix_lens=[3072, 3072], n_q=32, n_kv=8, head_dim=128,
+                           dtype="bf16", free_fraction=0.2, seed=3, device="cuda")
+    say("[chunk] bench shape 2 x 1024 over 3072, full size, all rows")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    pa.kv_append(c.chunk_k, c.chunk_v, c.chunk_slots, kp, vp)
+    out = nan_out(tuple(c.q.shape))
+    pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out)
+    torch.cuda.synchronize()
+    stats = assert_parity(out.cpu().numpy(), oracle_chunk(c), "bf16", "chunked prefill 2 x 1024 over 3072, all rows")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")

@@ -17,7 +17,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, nan_out, same_bits, say, stored_np
+from gpu_helpers import assert_parity, nan_out, oracle_pools, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import _lib
 from paged_gqa_attention_attn_amd import workloads as wl
 
@@ -115,13 +115,13 @@ def test_side_stream_calls_match_the_oracle(pa):
     pa.kv_append(ch.chunk_k, ch.chunk_v, ch.chunk_slots, ckp, cvp, stream=side)
     chunk = pa.paged_attn_chunked_prefill(ch.q, ckp, cvp, ch.block_table, ch.context_lens, ch.scale, stream=side)
     side.synchronize()
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16", c.block_table.cpu().numpy(),
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), "bf16", c.block_table.cpu().numpy(),
                          c.context_lens.cpu().numpy(), c.scale)
     for o in outs:
         assert_parity(o.cpu().numpy(), want, "bf16", "side-stream decode")
     assert_parity(pre.cpu().numpy(), oracle.prefill(stored_np(q), stored_np(k), stored_np(v), "bf16", True, 0.1),
                   "bf16", "side-stream prefill")
-    wc = oracle.chunked_prefill(stored_np(ch.q), stored_np(ckp), stored_np(cvp), "bf16",
+    wc = oracle.chunked_prefill(stored_np(ch.q), *oracle_pools(ch), "bf16",
                                 ch.block_table.cpu().numpy(), ch.context_lens.cpu().numpy(), ch.scale)
     assert_parity(chunk.cpu().numpy(), wc, "bf16", "side-stream chunked prefill")
     assert np.isfinite(chunk.cpu().numpy()).all()

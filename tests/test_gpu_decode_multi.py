@@ -10,7 +10,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, same_bits, say, stored_np
+from gpu_helpers import assert_parity, oracle_pools, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -143,7 +143,7 @@ def test_short_context_and_bad_metadata(pa):
     out = out.cpu()
     assert (out[0, :2] == 0).all()
     assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
-    want = oracle.chunked_prefill(stored_np(c.q[:2]), stored_np(kp), stored_np(vp), "bf16",
+    want = oracle.chunked_prefill(stored_np(c.q[:2]), *oracle_pools(c), "bf16",
                                   c.block_table[:2].cpu().numpy(), ctx[:2].cpu().numpy(), c.scale)
     assert_parity(out[0, 2:].numpy(), want[0, 2:], "bf16", "rows of the short sequence")
     assert_parity(out[1].numpy(), want[1], "bf16", "sequence next to bad metadata")

@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, nan_out, same_bits, say, stored_np
+from gpu_helpers import assert_parity, nan_out, oracle_pools, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -111,7 +111,7 @@ def test_chunked_prefill_f32(pa, shape):
     pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out, window=window,
                                   alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), "f32", c.block_table.cpu().numpy(),
                                   c.context_lens.cpu().numpy(), c.scale, window=window, alibi=m)
     stats = assert_parity(out.cpu().numpy(), want, "f32", "f32 chunked prefill")
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
@@ -150,7 +150,7 @@ def test_chunked_prefill_f32_short_context_and_bad_metadata(pa):
     out = out.cpu()
     assert (out[0, :13] == 0).all(), "rows at negative positions must be zero"
     assert torch.isnan(out[2]).all() and torch.isnan(out[3]).all()
-    want = oracle.chunked_prefill(stored_np(c.q[:2]), stored_np(kp), stored_np(vp), "f32",
+    want = oracle.chunked_prefill(stored_np(c.q[:2]), *oracle_pools(c), "f32",
                                   c.block_table[:2].cpu().numpy(), ctx[:2].cpu().numpy(), c.scale)
     assert_parity(out[0, 13:].numpy(), want[0, 13:], "f32", "rows of the short sequence")
     assert_parity(out[1].numpy(), want[1], "f32", "sequence next to bad metadata")
@@ -180,7 +180,7 @@ def test_decode_multi_f32(pa, shape):
     pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, c.scale, out=out, window=window,
                                alibi_slopes=None if m is None else torch.as_tensor(m, device="cuda"))
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), "f32", c.block_table.cpu().numpy(),
                                   c.context_lens.cpu().numpy(), c.scale, window=window, alibi=m)
     stats = assert_parity(out.cpu().numpy(), want, "f32", "f32 multi-row decode")
     say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
@@ -197,7 +197,7 @@ def test_decode_multi_f32_one_row_matches_decode(pa):
     out = nan_out(q.shape)
     pa.paged_attn_decode_multi(q, kp, vp, c.block_table, c.context_lens, c.scale, out=out)
     torch.cuda.synchronize()
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), "f32", c.block_table.cpu().numpy(),
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), "f32", c.block_table.cpu().numpy(),
                          c.context_lens.cpu().numpy(), c.scale)
     assert_parity(out.reshape(3, 8, 128).cpu().numpy(), want, "f32", "one-row f32 multi-row decode")
 

@@ -524,7 +524,10 @@ def test_decode_quant_append_per_channel_equals_two_calls(pa, fmt):
     torch.cuda.synchronize()
     assert same_bits(kc1, kc2) and same_bits(vc1, vc2), "the fused append wrote other codes"
     assert same_bits(one, two), "the fused step differs from append + decode"
-    want = oracle.decode(stored_np(c.q), _np(kc1), _np(vc1), fmt, _np(c.block_table), _np(c.context_lens),
+    okc, ovc = _np(c.k_pool).copy(), _np(c.v_pool).copy()   # the oracle's own append
+    oracle.kv_append_quant_channel(stored_np(c.new_k), stored_np(c.new_v), c.q_dtype, _np(c.slot_mapping),
+                                   okc, ovc, _np(ks), _np(vs), fmt)
+    want = oracle.decode(stored_np(c.q), okc, ovc, fmt, _np(c.block_table), _np(c.context_lens),
                          c.scale, q_dtype="bf16", k_scale=_np(ks), v_scale=_np(vs), scale_mode="channel")
     assert_parity(one.cpu().numpy(), want, "bf16", "fused per-channel step")
 

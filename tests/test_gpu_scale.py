@@ -16,7 +16,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, nan_out, say, stored_np
+from gpu_helpers import assert_parity, nan_out, oracle_pools, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -75,13 +75,13 @@ def test_decode(pa, decode_kernel, name, alibi, scale):
         torch.cuda.synchronize()
     finally:
         pa.set_decode_partition_tokens(prev)
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), dt, c.block_table.cpu().numpy(),
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), dt, c.block_table.cpu().numpy(),
                          c.context_lens.cpu().numpy(), scale, alibi=m)
     stats = assert_parity(out.cpu().numpy(), want, dt, f"decode {name} scale={scale}")
     say(f"    max_abs={stats['max_abs']:.2e}")
     if scale == 0.0 and not alibi:
         # The plain mean of each sequence's V rows, gathered here through the block table.
-        vals = oracle.upcast(stored_np(vp), dt)
+        vals = oracle.upcast(oracle_pools(c)[1], dt)
         bt = c.block_table.cpu().numpy()
         for b, n in enumerate(ctx):
             rows = np.stack([vals[bt[b, t // 16], :, t % 16, :] for t in range(n)])   # [n][n_kv][d]
@@ -117,7 +117,7 @@ def test_decode_multi(pa, rows, n_q, scale):
     out = nan_out(c.q.shape)
     pa.paged_attn_decode_multi(c.q, kp, vp, c.block_table, c.context_lens, scale, out=out)
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), "bf16",
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), scale)
     assert_parity(out.cpu().numpy(), want, "bf16", f"multi rows={rows} scale={scale}")
 
@@ -160,6 +160,6 @@ def test_chunked_prefill(pa, alibi, scale):
     pa.paged_attn_chunked_prefill(c.q, kp, vp, c.block_table, c.context_lens, scale, out=out,
                                   alibi_slopes=None if m is None else _dev(m))
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), "bf16",
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), "bf16",
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), scale, alibi=m)
     assert_parity(out.cpu().numpy(), want, "bf16", f"chunked scale={scale}")

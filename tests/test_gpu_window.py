@@ -13,7 +13,7 @@ import pytest
 import torch
 
 import oracle
-from gpu_helpers import assert_parity, same_bits, say, stored_np
+from gpu_helpers import assert_parity, oracle_pools, same_bits, say, stored_np
 from paged_gqa_attention_attn_amd import workloads as wl
 
 pytestmark = pytest.mark.gpu
@@ -77,7 +77,7 @@ def test_decode_window_matches_oracle(pa, decode_kernel, name, window):
     kp, vp = _appended(pa, c)
     got = pa.paged_attn_decode(c.q, kp, vp, c.block_table, c.context_lens, c.scale, window=window)
     torch.cuda.synchronize()
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), c.dtype,
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), c.dtype,
                          c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                          window=window)
     stats = assert_parity(got.cpu().numpy(), want, c.dtype, f"decode {name} W={window}")
@@ -100,7 +100,7 @@ def test_decode_window_partition_sizes(pa, decode_kernel, tokens):
         torch.cuda.synchronize()
     finally:
         pa.set_decode_partition_tokens(prev)
-    want = oracle.decode(stored_np(c.q), stored_np(kp), stored_np(vp), c.dtype,
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), c.dtype,
                          c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                          window=3000)
     assert_parity(got.cpu().numpy(), want, c.dtype, f"partition {tokens}")
@@ -155,7 +155,7 @@ def test_decode_multi_window_matches_oracle(pa, shape):
     bt = _poison_before(c.block_table, c.context_lens, R, W)
     again = pa.paged_attn_decode_multi(c.q, kp, vp, bt, c.context_lens, c.scale, window=W)
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), dt,
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), dt,
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                                   window=W)
     stats = assert_parity(got.cpu().numpy(), want, dt, f"multi W={W}")
@@ -190,7 +190,7 @@ def test_chunked_prefill_window_matches_oracle(pa, shape):
     bt = _poison_before(c.block_table, c.context_lens, C, W)
     again = pa.paged_attn_chunked_prefill(c.q, kp, vp, bt, c.context_lens, c.scale, window=W)
     torch.cuda.synchronize()
-    want = oracle.chunked_prefill(stored_np(c.q), stored_np(kp), stored_np(vp), dt,
+    want = oracle.chunked_prefill(stored_np(c.q), *oracle_pools(c), dt,
                                   c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale,
                                   window=W)
     stats = assert_parity(got.cpu().numpy(), want, dt, f"chunked W={W}")
@@ -240,3 +240,26 @@ def test_window_rejections_reach_python(pa):
     kv = torch.zeros(1, 8, 2, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(pa.PagedAttnError, match="causal"):
         pa.paged_attn_prefill(q, kv, kv, False, 0.1, window=4)
+
+
+def test_window_bench_shape_all_rows(pa):
+    """The bench's sliding-window step at full size (B=32, 32/8 heads, d=128, bf16, contexts of
+    16384, W=4096, the new token appended in the same launch): every row against the oracle,
+    into a NaN-filled output, and every row again after poisoning the entries before the window."""
+    from gpu_helpers import nan_out
+    c = wl.make_window_decode_case(device="cuda")
+    W = wl.WINDOW_TOKENS
+    say(f"[window] 8B shape, ctx 16384, W={W}, fused step, full size, all rows")
+    kp, vp = c.k_pool.clone(), c.v_pool.clone()
+    out = nan_out((c.batch, c.n_q, c.head_dim))
+    pa.paged_attn_decode_append(c.q, c.new_k, c.new_v, c.slot_mapping, kp, vp, c.block_table,
+                                c.context_lens, c.scale, out=out, window=W)
+    torch.cuda.synchronize()
+    want = oracle.decode(stored_np(c.q), *oracle_pools(c), c.dtype,
+                         c.block_table.cpu().numpy(), c.context_lens.cpu().numpy(), c.scale, window=W)
+    stats = assert_parity(out.cpu().numpy(), want, c.dtype, "window 8B shape, all 1024 rows")
+    say(f"    max_abs={stats['max_abs']:.2e} rel={stats['rel']:.2e}")
+    bt = _poison_before(c.block_table, c.context_lens, 1, W)
+    again = pa.paged_attn_decode(c.q, kp, vp, bt, c.context_lens, c.scale, window=W)
+    torch.cuda.synchronize()
+    assert same_bits(out, again), "the fused step and the plain decode after it must agree bit for bit"
