@@ -84,7 +84,8 @@ typedef enum {
  * so element (block, kv_head, offset, c) sits at
  *   ((block * n_kv + kv_head) * block_size + offset) * head_dim + c.
  * Supported: block_size 16; head_dim 64 or 128; dtype f32, bf16 or f16 (and,
- * for the quantised entry points, PA_FP8_E4M3 or PA_INT8, one byte per element).
+ * for the quantised entry points, PA_FP8_E4M3 or PA_INT8 or their _PER_CHANNEL
+ * forms, one byte per element).
  */
 typedef struct {
     int32_t num_blocks;
