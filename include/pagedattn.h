@@ -305,7 +305,7 @@ int pa_paged_attn_decode_multi(const void* q, int32_t batch, int32_t q_rows, int
                                const void* k_cache, const void* v_cache, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, float scale, int32_t window,
-                         const float* alibi_slopes, void* out,
+                               const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -416,7 +416,7 @@ int pa_paged_attn_decode_quant(const void* q, pa_dtype q_dtype, int32_t batch, i
                                const float* v_scale, const pa_cache_desc* cache,
                                const int32_t* block_table, int32_t max_blocks_per_seq,
                                const int32_t* context_lens, float scale, int32_t window,
-                         const float* alibi_slopes, void* out,
+                               const float* alibi_slopes, void* out,
                                pa_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
